@@ -1,0 +1,37 @@
+"""CPU oracle (numpy, float64) for sliding-window attention over a two-pool
+paged KV cache.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library or its Python binding.  It
+shares no code with the HIP path.
+
+Parity status of each function (what pins it, see tests/test_oracle_pins.py):
+  codecs.*            pinned: torch's dtype casts over every bf16 input pattern
+  pool_config         pinned: the MiMo-V2-Flash worked example on the SWA note
+  translate_loc       pinned: sentinel/tombstone invariants + page-level rebuild
+  window_table        pinned: page-level rebuild (slot = page * P + offset)
+  kv_store            pinned: round trip and untouched-row invariants
+  attention           pinned: full-causal reduction, plain-softmax reduction,
+                      pure-Python brute force, W=0 and identical-key closed
+                      forms, GQA expansion, pair-count ratio ~ 2W/T.
+  The sink formula, the 1/sqrt(D) scale and the GQA head map are readings of
+  ours (the pages do not spell them out): pinned only through the special cases
+  above, i.e. parity unpinned by the pages themselves for those three readings.
+"""
+
+from . import codecs, swa_oracle  # noqa: F401
+from .swa_oracle import (  # noqa: F401
+    NoSpaceError,
+    OracleError,
+    attend,
+    attention,
+    decode,
+    extend,
+    kv_bytes_per_token,
+    kv_store,
+    pool_config,
+    scored_pairs,
+    translate_loc,
+    window_range,
+    window_table,
+)

@@ -1,0 +1,297 @@
+"""Plain, slow CPU oracle of sliding-window attention (SWA) over a two-pool paged
+KV cache, in float64 with numpy.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the CPU-baseline leg
+of the benchmark may import it; the HIP library never does, and the two share
+no code, headers, tables or helpers.
+
+Sources (three web pages; every function names the passage it follows):
+  [SWA]   zdszero.github.io/swa.html — SWA design note (sections: 问题 Problem,
+          设计 Design, 抽象 Abstraction, 实现 Implementation, 双池与映射表
+          Two pools and the mapping table, 显存怎么分 Memory split, 运行时
+          Runtime, Attention backend).
+  [POOLS] pinghaoyang.com.cn, "SGLang 源码完全拆解(十五): 内存池与显存管理"
+          (sections: 一重映射 request-slot pool, 二重映射 KV storage pool,
+          三重映射 page allocator, alloc_extend, 双池 + 映射表
+          SWATokenToKVPoolAllocator, 谁在往页里写 who writes into the pages).
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * window: the configured W excludes the current token, so query i sees keys
+    [max(0, i-W), i]; W = -1 means full attention ([SWA] 实现, per-layer
+    sliding_window_size; FlashInfer path truncating to W+1 in Attention backend).
+  * decode query position: i = seq_len - 1 (the current token's K/V is stored
+    before attention).
+  * sink: one extra logit sigma_h per q head in the softmax denominator, in the
+    scaled-logit domain, with no value row ([SWA] 设计: weight "leaks" to the
+    sink).  No sink is sigma = -inf.
+  * softmax scale: 1/sqrt(D) unless the caller passes another.
+  * GQA: q head h reads kv head floor(h / G), G = Hq / Hkv.
+  * an in-window tombstone (mapping 0 on an SWA layer) is a contract violation
+    and raises.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import codecs
+
+
+class OracleError(ValueError):
+    """A contract violation detected by the oracle (bad index, tombstone...)."""
+
+
+class NoSpaceError(OracleError):
+    """The SWA pool cannot hold a single request (startup error on the pages)."""
+
+
+# ---------------------------------------------------------------------------
+# a1 — pool sizing.  [SWA] 显存怎么分 (--swa-full-tokens-ratio): with F and S
+# the per-token, per-layer KV bytes of a full and of an SWA layer,
+#   cell = F * L_full + r * S * L_swa,  N_full = floor(avail / cell),
+#   N_swa = r * N_full,  both rounded down to a page;  N_swa <= W + P is a
+# startup error.
+# ---------------------------------------------------------------------------
+
+
+def kv_bytes_per_token(kv_heads: int, head_dim: int, v_head_dim: int, dtype_size: int) -> int:
+    """F or S of the cell formula: num_kv_heads * (head_dim + v_head_dim) * dtype_size."""
+    return kv_heads * (head_dim + v_head_dim) * dtype_size
+
+
+def pool_config(avail_bytes, ratio, page_size, window, n_full_layers, full_bytes_per_token,
+                n_swa_layers, swa_bytes_per_token):
+    """Return (cell_bytes, N_full, N_swa) for the two pools; raise NoSpaceError
+    when N_swa <= W + P ([SWA] 显存怎么分)."""
+    if page_size <= 0 or ratio < 0:
+        raise OracleError("page_size must be positive and ratio non-negative")
+    cell = full_bytes_per_token * n_full_layers + ratio * swa_bytes_per_token * n_swa_layers
+    n_full = math.floor(avail_bytes / cell)
+    n_full = (n_full // page_size) * page_size
+    n_swa = math.floor(ratio * n_full)
+    n_swa = (n_swa // page_size) * page_size
+    if n_swa <= window + page_size:
+        raise NoSpaceError(f"SWA pool of {n_swa} tokens cannot hold W + P = {window + page_size}")
+    return cell, n_full, n_swa
+
+
+# ---------------------------------------------------------------------------
+# a2 — translate_loc.  [SWA] 双池与映射表 and Attention backend; [POOLS]
+# 双池 + 映射表: the SWA index of a token is full_to_swa[full]; the table has
+# size + page_size entries followed by one trailing -1, so -1 translates to -1;
+# 0 means "no SWA slot" (tombstone / padding).
+# ---------------------------------------------------------------------------
+
+
+def translate_loc(full_loc, full_to_swa):
+    """swa_loc[n] = full_to_swa[full_loc[n]], with -1 -> the trailing -1 entry.
+
+    Any index outside [-1, len-2] is an error (the oracle does not clamp)."""
+    m = np.asarray(full_to_swa, dtype=np.int64)
+    x = np.asarray(full_loc, dtype=np.int64)
+    if m.ndim != 1 or m.size < 2 or m[-1] != -1:
+        raise OracleError("mapping table must end with the -1 sentinel")
+    out = np.empty_like(x)
+    for n, f in enumerate(x.tolist()):
+        if f == -1:
+            out[n] = m[m.size - 1]
+        elif 0 <= f < m.size - 1:
+            out[n] = m[f]
+        else:
+            raise OracleError(f"full loc {f} outside the mapping table")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a3 — window gather.  [SWA] Attention backend: backends translate the window's
+# full indices once per batch (FlashInfer keeps W+1 positions per request);
+# [POOLS] 一重映射: req_to_token[row, pos] holds the full slot of each position.
+# ---------------------------------------------------------------------------
+
+
+def window_range(seq_len: int, prefix_len: int, window: int):
+    """Positions [lo, hi] whose K/V the new queries of a request can see.
+
+    The new queries are positions prefix_len .. seq_len-1; query i sees
+    [max(0, i-W), i], so together they see [max(0, prefix_len - W), seq_len-1].
+    Decode is prefix_len = seq_len - 1.  W = -1 is full attention (lo = 0)."""
+    hi = seq_len - 1
+    lo = 0 if window < 0 else max(0, prefix_len - window)
+    return lo, hi
+
+
+def window_table(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, prefix_lens=None):
+    """Per request, the slots of positions window_range(...), concatenated.
+
+    Returns (table int64, indptr int64 of length B+1).  With full_to_swa None
+    the slots are the full-pool slots (full layers need no translation)."""
+    r2t = np.asarray(req_to_token)
+    rows = np.asarray(req_pool_idx, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    b_count = lens.size
+    pre = lens - 1 if prefix_lens is None else np.asarray(prefix_lens, dtype=np.int64)
+    table, indptr = [], [0]
+    for b in range(b_count):
+        lo, hi = window_range(int(lens[b]), int(pre[b]), window)
+        for j in range(lo, hi + 1):
+            full = int(r2t[rows[b], j])
+            slot = full if full_to_swa is None else int(translate_loc([full], full_to_swa)[0])
+            table.append(slot)
+        indptr.append(len(table))
+    return np.asarray(table, dtype=np.int64), np.asarray(indptr, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# a4 — kv_store.  [SWA] Attention backend (KVWriteLoc: SWA layers receive an
+# already translated swa_loc, the pool does not translate); [POOLS] 谁在往页里写
+# and 二重映射 (per-layer k_buffer / v_buffer of shape (size + page, heads,
+# dim); fp8 pools hold bytes).
+# ---------------------------------------------------------------------------
+
+
+def kv_store(pool_k, pool_v, loc, k_new, v_new, in_dtype: str, pool_dtype: str):
+    """Return copies of the pools with row loc[n] set to enc(k_new[n]) / enc(v_new[n]).
+
+    k_new / v_new hold storage bits of `in_dtype` with shape (n, Hkv, D); the
+    pools hold storage bits of `pool_dtype` with shape (rows, Hkv, D).  Values
+    are decoded exactly and re-encoded with the oracle codecs (a byte copy
+    when the two dtypes agree).  Duplicate locs are a contract violation."""
+    loc = np.asarray(loc, dtype=np.int64)
+    if np.unique(loc).size != loc.size:
+        raise OracleError("duplicate store locations")
+    rows = pool_k.shape[0]
+    if loc.size and (loc.min() < 0 or loc.max() >= rows):
+        raise OracleError("store location outside the pool")
+    out_k, out_v = pool_k.copy(), pool_v.copy()
+    for n, slot in enumerate(loc.tolist()):
+        out_k[slot] = codecs.encode_store(codecs.decode_store(k_new[n], in_dtype), pool_dtype)
+        out_v[slot] = codecs.encode_store(codecs.decode_store(v_new[n], in_dtype), pool_dtype)
+    return out_k, out_v
+
+
+# ---------------------------------------------------------------------------
+# a5 / a6 / a7 — attention.  [SWA] opening paragraph (each query attends only
+# to the most recent window), 实现 (sliding_window_size excludes the current
+# token, -1 = full) and 设计 (learnable per-head sink).
+# ---------------------------------------------------------------------------
+
+
+def attend(q, keys, values, sink, scale):
+    """Output of one query head:
+
+        s_j = scale * (q . k_j)
+        m   = max(max_j s_j, sigma)
+        o   = sum_j e^{s_j - m} v_j / (sum_j e^{s_j - m} + e^{sigma - m})
+
+    sink None means sigma = -inf (plain softmax over the window)."""
+    s = scale * (keys @ q)
+    sigma = -math.inf if sink is None else float(sink)
+    m = max(float(s.max()), sigma)
+    w = np.exp(s - m)
+    denom = w.sum() + (0.0 if sink is None else math.exp(sigma - m))
+    return (w @ values) / denom
+
+
+def _gather_kv(pool_k, pool_v, slots, pool_dtype, k_scale, v_scale):
+    k = codecs.decode_store(pool_k[slots], pool_dtype) * k_scale
+    v = codecs.decode_store(pool_v[slots], pool_dtype) * v_scale
+    return k, v
+
+
+def _slots_for(r2t_row, lo, hi, full_to_swa):
+    full = np.asarray(r2t_row[lo:hi + 1], dtype=np.int64)
+    if full_to_swa is None:
+        return full
+    slots = translate_loc(full, full_to_swa)
+    if np.any(slots == 0):
+        raise OracleError("in-window tombstone: a window position has no SWA slot")
+    if np.any(slots < 0):
+        raise OracleError("window position translated to the -1 sentinel")
+    return slots
+
+
+def attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx, seq_lens,
+              full_to_swa, window, sinks=None, scale=None, prefix_lens=None, qo_indptr=None,
+              k_scale=1.0, v_scale=1.0, only=None):
+    """Windowed attention of the new queries of every request (decode or extend).
+
+    q: storage bits (q_dtype) of shape (total_new, Hq, D); request b owns rows
+    qo_indptr[b] .. qo_indptr[b+1]-1, holding positions prefix_lens[b] .. seq_lens[b]-1.
+    Decode is prefix_lens = seq_lens - 1 with one row per request (the defaults).
+    pool_k / pool_v: storage bits of shape (rows, Hkv, D).  full_to_swa None means
+    the pool is the full pool.  Returns float64 (total_new, Hq, D), unrounded.
+
+    `only`, if given, is a list of (row, head) pairs to compute; other entries
+    are left NaN (for sampled checks at full size)."""
+    qf = codecs.decode_store(q, q_dtype)
+    total_new, hq, d = qf.shape
+    hkv = pool_k.shape[1]
+    if hq % hkv:
+        raise OracleError("q heads must be a multiple of kv heads")
+    group = hq // hkv
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    b_count = lens.size
+    pre = lens - 1 if prefix_lens is None else np.asarray(prefix_lens, dtype=np.int64)
+    indptr = np.arange(b_count + 1) if qo_indptr is None else np.asarray(qo_indptr, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    r2t = np.asarray(req_to_token)
+    rows = np.asarray(req_pool_idx, dtype=np.int64)
+    out = np.full((total_new, hq, d), np.nan)
+    wanted = None if only is None else {}
+    if only is not None:
+        for r, h in only:
+            wanted.setdefault(int(r), []).append(int(h))
+    for b in range(b_count):
+        if indptr[b + 1] - indptr[b] != lens[b] - pre[b]:
+            raise OracleError("qo_indptr disagrees with seq_lens - prefix_lens")
+        for t in range(int(indptr[b + 1] - indptr[b])):
+            row = int(indptr[b] + t)
+            if wanted is not None and row not in wanted:
+                continue
+            i = int(pre[b]) + t
+            lo = 0 if window < 0 else max(0, i - window)
+            slots = _slots_for(r2t[rows[b]], lo, i, full_to_swa)
+            k, v = _gather_kv(pool_k, pool_v, slots, pool_dtype, k_scale, v_scale)
+            heads = range(hq) if wanted is None else wanted[row]
+            for h in heads:
+                g = h // group
+                sink = None if sinks is None else sinks[h]
+                out[row, h] = attend(qf[row, h], k[:, g, :], v[:, g, :], sink, scale)
+    return out
+
+
+def decode(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx, seq_lens,
+           full_to_swa, window, sinks=None, scale=None, k_scale=1.0, v_scale=1.0, only=None):
+    """Decode: one query per request at position seq_len-1 (see attention)."""
+    return attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx,
+                     seq_lens, full_to_swa, window, sinks, scale, None, None, k_scale, v_scale, only)
+
+
+def extend(q, q_dtype, qo_indptr, prefix_lens, pool_k, pool_v, pool_dtype, req_to_token,
+           req_pool_idx, seq_lens, full_to_swa, window, sinks=None, scale=None,
+           k_scale=1.0, v_scale=1.0, only=None):
+    """Extend / chunked prefill: queries prefix_len .. seq_len-1 per request,
+    each over [max(0, i-W), i], against a pool that already holds the chunk's
+    K/V (see attention)."""
+    return attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx,
+                     seq_lens, full_to_swa, window, sinks, scale, prefix_lens, qo_indptr,
+                     k_scale, v_scale, only)
+
+
+# ---------------------------------------------------------------------------
+# Cost model.  [SWA] 问题: causal full attention scores about T^2/2 pairs, SWA
+# a fixed window per query; the ratio is about 2W/T.
+# ---------------------------------------------------------------------------
+
+
+def scored_pairs(seq_len: int, window: int) -> int:
+    """Number of (query, key) pairs the oracle scores for one request of length
+    T when every position is a query (prefill), counted by walking the windows."""
+    total = 0
+    for i in range(seq_len):
+        lo = 0 if window < 0 else max(0, i - window)
+        total += i - lo + 1
+    return total

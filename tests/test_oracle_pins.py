@@ -1,0 +1,519 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Every check here is independent of the oracle's own code path: textbook matrix
+attention, pure-Python loops, closed forms, library casts, page-level rebuilds
+of the index tables, and figures printed on the pages (tests/golden).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import codecs
+from oracle import swa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# codecs against torch's casts (library routines)
+# ---------------------------------------------------------------------------
+
+ALL_BF16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+def test_bf16_decode_matches_torch_on_every_pattern():
+    ours = codecs.bf16_bits_to_f64(ALL_BF16)
+    ref = torch.from_numpy(ALL_BF16.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_bf16_encode_matches_torch():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-38).astype(np.float32),  # subnormal range
+        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+        # exact ties: bf16 values plus half an ulp (odd and even mantissas)
+        (codecs.bf16_bits_to_f64(np.arange(0x3F80, 0x3FA0, dtype=np.uint16)) * (1 + 2.0 ** -8)).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38], dtype=np.float32),
+    ])
+    ours = codecs.f64_to_bf16_bits(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = codecs.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+    assert codecs.e4m3_to_f64(np.array([0x7E]))[0] == 448.0
+
+
+def test_e4m3_encode_matches_torch_on_every_bf16_input():
+    vals = codecs.bf16_bits_to_f64(ALL_BF16)
+    ours = codecs.f64_to_e4m3(vals)
+    ref = torch.from_numpy(ALL_BF16.view(np.int16)).view(torch.bfloat16).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+    finite_in_range = np.isfinite(vals) & (np.abs(vals) <= 464.0)
+    assert np.array_equal(ours[finite_in_range], ref[finite_in_range])
+    # reading: saturate-to-finite beyond the largest finite value, NaN -> 0x7F
+    big = np.isfinite(vals) & (np.abs(vals) > 448.0) | np.isinf(vals)
+    assert np.all(codecs.e4m3_to_f64(ours[big]) == np.sign(vals[big]) * 448.0)
+    assert np.all(ours[np.isnan(vals)] == 0x7F)
+
+
+def test_e4m3_encode_fp32_inputs_match_torch():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(100000), rng.standard_normal(20000) * 1e-3,
+                        rng.uniform(-460, 460, 20000)]).astype(np.float32)
+    ours = codecs.f64_to_e4m3(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# pool sizing: the MiMo-V2-Flash worked example printed on the SWA note
+# ---------------------------------------------------------------------------
+
+
+def test_pool_config_reproduces_mimo_example():
+    g = golden()["mimo_pool_split"]
+    F = 1000  # bytes per token per full layer; S = 2F
+    S = int(F * g["swa_bytes_over_full_bytes"])
+    avail = 10 ** 12
+    cells = {}
+    for case in g["cases"]:
+        cell, n_full, n_swa = O.pool_config(avail, case["ratio"], 1, 128, g["layers_full"], F,
+                                            g["layers_swa"], S)
+        assert round(cell / F, 1) == case["cell_over_F"]
+        cells[case["ratio"]] = (cell, n_full, n_swa)
+        if "swa_share_of_kv_memory_approx" in case:
+            share = n_swa * S * g["layers_swa"] / (n_swa * S * g["layers_swa"] + n_full * F * g["layers_full"])
+            assert round(share, 2) == case["swa_share_of_kv_memory_approx"]
+    gain = cells[0.05][1] / cells[0.8][1]
+    assert round(gain, 1) == g["cases"][1]["full_capacity_gain_vs_ratio_0.8_approx"]
+
+
+def test_pool_config_page_rounding_and_nospace():
+    # rounding down to a page on both pools
+    cell, n_full, n_swa = O.pool_config(10 ** 9, 0.1, 64, 128, 9, 2048, 39, 4096)
+    assert n_full % 64 == 0 and n_swa % 64 == 0
+    assert n_full <= 10 ** 9 / cell < n_full + 64
+    # the long-context mixed configuration: 32 requests x 32K tokens fill the full pool
+    F = O.kv_bytes_per_token(4, 128, 128, 2)
+    S = O.kv_bytes_per_token(8, 128, 128, 2)
+    assert (F, S) == (2048, 4096)
+    cell = F * 9 + 0.1 * S * 39
+    _, n_full, n_swa = O.pool_config(math.ceil(cell * 1048576), 0.1, 64, 128, 9, F, 39, S)
+    assert n_full == 1048576 and n_swa == 104832
+    # startup error when the SWA pool cannot hold W + P tokens
+    with pytest.raises(O.NoSpaceError):
+        O.pool_config(192 * 4096 * 10, 0.01, 64, 128, 0, 0, 10, 4096)
+
+
+# ---------------------------------------------------------------------------
+# index translation against page-level rebuilds (slot = page * P + offset)
+# ---------------------------------------------------------------------------
+
+
+def test_page_math_examples():
+    for ex in golden()["page_math"]["examples"]:
+        assert ex["page"] * ex["page_size"] + ex["offset"] == ex["slot"]
+        assert ex["slot"] // ex["page_size"] == ex["page"]
+
+
+def make_two_pool(rng, seq_lens, P, window, margin, n_full_pages=None, n_swa_pages=None):
+    """A page-consistent two-pool cache described at page level.
+
+    Returns the token-level tables plus the page-level truth used to rebuild
+    expected slots: full_pages[b][p] and swa_pages[b][p] (0 when tombstoned)."""
+    B = len(seq_lens)
+    need = [-(-t // P) for t in seq_lens]
+    n_full_pages = n_full_pages or sum(need) + 3
+    n_swa_pages = n_swa_pages or sum(need) + 3
+    fperm = rng.permutation(np.arange(1, n_full_pages + 1))
+    sperm = rng.permutation(np.arange(1, n_swa_pages + 1))
+    stride = max(seq_lens) + 5
+    r2t = np.zeros((B + 1, stride), dtype=np.int32)
+    mapping = np.zeros((n_full_pages + 1) * P + 1, dtype=np.int64)
+    mapping[-1] = -1
+    full_pages, swa_pages = [], []
+    fi = si = 0
+    for b, t in enumerate(seq_lens):
+        fp = fperm[fi:fi + need[b]]
+        fi += need[b]
+        keep_from = max(0, (t - 1 - window - margin)) // P if window >= 0 else 0
+        sp = np.zeros(need[b], dtype=np.int64)
+        for p in range(keep_from, need[b]):
+            sp[p] = sperm[si]
+            si += 1
+        full_pages.append(fp)
+        swa_pages.append(sp)
+        for j in range(t):
+            p, k = divmod(j, P)
+            r2t[b + 1, j] = fp[p] * P + k
+            mapping[fp[p] * P + k] = 0 if sp[p] == 0 else sp[p] * P + k
+    return r2t, np.arange(1, B + 1, dtype=np.int32), np.asarray(seq_lens, np.int32), mapping, full_pages, swa_pages
+
+
+def test_translate_loc_invariants_and_page_rebuild():
+    rng = np.random.default_rng(3)
+    P = 4
+    r2t, rows, lens, mapping, fpages, spages = make_two_pool(rng, [37, 9, 50], P, 6, 2)
+    assert mapping[-1] == -1
+    out = O.translate_loc(np.array([-1, 0, 0, -1]), mapping)
+    assert out.tolist() == [-1, 0, 0, -1]
+    for b, t in enumerate(lens):
+        full = r2t[b + 1, :t]
+        got = O.translate_loc(full, mapping)
+        want = [0 if spages[b][j // P] == 0 else spages[b][j // P] * P + j % P for j in range(t)]
+        assert got.tolist() == want
+    with pytest.raises(O.OracleError):
+        O.translate_loc(np.array([mapping.size - 1]), mapping)
+    with pytest.raises(O.OracleError):
+        O.translate_loc(np.array([-2]), mapping)
+
+
+@pytest.mark.parametrize("window", [0, 3, 6, 100, -1])
+def test_window_table_page_rebuild(window):
+    rng = np.random.default_rng(4)
+    P = 4
+    lens = [37, 1, 9, 50]
+    r2t, rows, lens_a, mapping, fpages, spages = make_two_pool(rng, lens, P, max(window, 0), 3)
+    for use_map in (True, False):
+        if window < 0 and use_map:
+            continue
+        table, indptr = O.window_table(r2t, rows, lens_a, mapping if use_map else None, window)
+        assert indptr[0] == 0 and indptr.size == len(lens) + 1
+        for b, t in enumerate(lens):
+            i = t - 1
+            lo = 0 if window < 0 else max(0, i - window)
+            pages = spages[b] if use_map else fpages[b]
+            want = [pages[j // P] * P + j % P for j in range(lo, i + 1)]
+            assert table[indptr[b]:indptr[b + 1]].tolist() == want
+            assert indptr[b + 1] - indptr[b] == (t if window < 0 else min(t, window + 1))
+
+
+def test_window_table_extend_ranges():
+    rng = np.random.default_rng(5)
+    P = 8
+    lens = [40, 24]
+    pre = [30, 0]
+    r2t, rows, lens_a, mapping, fpages, spages = make_two_pool(rng, lens, P, 5, 1)
+    table, indptr = O.window_table(r2t, rows, lens_a, mapping, 5, prefix_lens=np.array(pre))
+    assert (indptr[1] - indptr[0]) == 40 - 25
+    assert (indptr[2] - indptr[1]) == 24
+
+
+# ---------------------------------------------------------------------------
+# kv_store: round trip and untouched rows
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("in_dtype,pool_dtype", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "e4m3"),
+                                                 ("f32", "e4m3"), ("f32", "bf16")])
+def test_kv_store_round_trip(in_dtype, pool_dtype):
+    rng = np.random.default_rng(6)
+    rows, H, D, n = 40, 2, 8, 7
+    x = rng.standard_normal((n, H, D)) * 3
+    k_new = codecs.encode_store(x, in_dtype)
+    v_new = codecs.encode_store(-x, in_dtype)
+    empty = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[pool_dtype]
+    pool_k = np.full((rows, H, D), 0x55, dtype=empty)
+    pool_v = np.full((rows, H, D), 0x66, dtype=empty)
+    loc = rng.choice(np.arange(1, rows), n, replace=False)
+    nk, nv = O.kv_store(pool_k, pool_v, loc, k_new, v_new, in_dtype, pool_dtype)
+    other = np.setdiff1d(np.arange(rows), loc)
+    assert np.array_equal(nk[other], pool_k[other]) and np.array_equal(nv[other], pool_v[other])
+    src = codecs.decode_store(k_new, in_dtype)
+    got = codecs.decode_store(nk[loc], pool_dtype)
+    if in_dtype == pool_dtype:
+        assert np.array_equal(nk[loc].view(np.uint8), k_new.view(np.uint8))
+        assert np.array_equal(nv[loc].view(np.uint8), v_new.view(np.uint8))
+    else:
+        # the stored value is a nearest representable value of the target format
+        table = codecs.E4M3_VALUES[np.isfinite(codecs.E4M3_VALUES)] if pool_dtype == "e4m3" else None
+        if table is not None:
+            best = np.min(np.abs(src[..., None] - table), axis=-1)
+            assert np.allclose(np.abs(src - got), best, rtol=0, atol=0)
+        else:
+            assert np.all(np.abs(src - got) <= np.abs(src) * 2.0 ** -8)
+    with pytest.raises(O.OracleError):
+        O.kv_store(pool_k, pool_v, np.array([3, 3]), k_new[:2], v_new[:2], in_dtype, pool_dtype)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+
+def dense_case(rng, T, Hq, Hkv, D, window, P=1, margin=0, qdt="f32", kvdt="f32", sinks=True, evict=False):
+    """One request whose every position is a query (prefix 0), on a shuffled
+    two-pool cache; returns arguments for O.extend plus the dense logical K/V.
+    With evict=True, pages before the last window (+ margin) are tombstoned,
+    which only a decode of the last position may read around."""
+    keep = max(window, 0) if evict else T
+    r2t, rows, lens, mapping, fpages, spages = make_two_pool(rng, [T], P, keep, margin)
+    n_rows = mapping.size
+    q = codecs.encode_store(rng.standard_normal((T, Hq, D)), qdt)
+    kd = codecs.encode_store(rng.standard_normal((T, Hkv, D)), kvdt)
+    vd = codecs.encode_store(rng.standard_normal((T, Hkv, D)), kvdt)
+    empty = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[kvdt]
+    nan_bits = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F)}[kvdt]
+    pool_k = np.full((n_rows, Hkv, D), nan_bits, dtype=empty)
+    pool_v = np.full((n_rows, Hkv, D), nan_bits, dtype=empty)
+    use_map = window >= 0
+    for j in range(T):
+        full = r2t[1, j]
+        slot = mapping[full] if use_map else full
+        if slot > 0:
+            pool_k[slot] = kd[j]
+            pool_v[slot] = vd[j]
+    s = rng.standard_normal(Hq) if sinks else None
+    args = dict(q=q, q_dtype=qdt, qo_indptr=np.array([0, T]), prefix_lens=np.array([0]), pool_k=pool_k,
+                pool_v=pool_v, pool_dtype=kvdt, req_to_token=r2t, req_pool_idx=rows, seq_lens=lens,
+                full_to_swa=mapping if use_map else None, window=window, sinks=s)
+    return args, codecs.decode_store(q, qdt), codecs.decode_store(kd, kvdt), codecs.decode_store(vd, kvdt)
+
+
+def textbook_causal(q, k, v, scale):
+    """Full causal attention as matrices: softmax(QK^T * scale + triangular mask) V."""
+    T, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.empty_like(q)
+    mask = np.triu(np.ones((T, T), dtype=bool), 1)
+    for h in range(Hq):
+        s = scale * q[:, h, :] @ k[:, h // G, :].T
+        s[mask] = -np.inf
+        out[:, h, :] = scipy.special.softmax(s, axis=1) @ v[:, h // G, :]
+    return out
+
+
+@pytest.mark.parametrize("window", [-1, 40, 41, 1000])
+def test_window_at_least_T_is_full_causal(window):
+    rng = np.random.default_rng(7)
+    T, Hq, Hkv, D = 40, 4, 2, 16
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, window, P=4, sinks=False)
+    got = O.extend(**args)
+    want = textbook_causal(q, k, v, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_sink_minus_inf_is_plain_softmax():
+    rng = np.random.default_rng(8)
+    T, Hq, Hkv, D, W = 30, 4, 4, 8, 5
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, W, P=2, margin=3, sinks=False)
+    no_sink = O.extend(**args)
+    args["sinks"] = np.full(Hq, -np.inf)
+    with_inf = O.extend(**args)
+    assert np.array_equal(no_sink, with_inf)
+    scale = 1 / math.sqrt(D)
+    for i in range(T):
+        lo = max(0, i - W)
+        for h in range(Hq):
+            p = scipy.special.softmax(scale * k[lo:i + 1, h, :] @ q[i, h, :])
+            np.testing.assert_allclose(no_sink[i, h], p @ v[lo:i + 1, h, :], rtol=1e-12, atol=1e-14)
+
+
+def brute_force(q, k, v, sinks, window, scale):
+    """Pure-Python loops with math.exp, one (query, head) at a time."""
+    T, Hq, D = len(q), len(q[0]), len(q[0][0])
+    G = Hq // len(k[0])
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(T)]
+    for i in range(T):
+        lo = 0 if window < 0 else max(0, i - window)
+        for h in range(Hq):
+            g = h // G
+            scores = []
+            for j in range(lo, i + 1):
+                scores.append(scale * sum(q[i][h][d] * k[j][g][d] for d in range(D)))
+            sig = -math.inf if sinks is None else sinks[h]
+            m = max(max(scores), sig)
+            ws = [math.exp(s - m) for s in scores]
+            den = sum(ws) + (0.0 if sinks is None else math.exp(sig - m))
+            for d in range(D):
+                out[i][h][d] = sum(w * v[lo + n][g][d] for n, w in enumerate(ws)) / den
+    return np.array(out)
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+@pytest.mark.parametrize("window", [0, 1, 2, 8])
+@pytest.mark.parametrize("sinks", [True, False])
+def test_brute_force_tiny(T, window, sinks):
+    rng = np.random.default_rng(100 * T + 10 * window + sinks)
+    Hq, Hkv, D = 4, 2, 4
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, window, P=1, sinks=sinks)
+    got = O.extend(**args)
+    want = brute_force(q.tolist(), k.tolist(), v.tolist(), None if args["sinks"] is None else list(args["sinks"]),
+                       window, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_window_zero_closed_form():
+    rng = np.random.default_rng(9)
+    T, Hq, Hkv, D = 12, 2, 2, 8
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, 0, P=2)
+    got = O.extend(**args)
+    s = np.einsum("thd,thd->th", q, k) / math.sqrt(D)
+    sig = 1 / (1 + np.exp(-(s - args["sinks"][None, :])))
+    np.testing.assert_allclose(got, v * sig[:, :, None], rtol=1e-12, atol=1e-15)
+    args["sinks"] = None
+    got = O.extend(**args)
+    assert np.array_equal(got, v)  # exactly v_i: a single key with weight 1
+
+
+def test_identical_keys_closed_form():
+    rng = np.random.default_rng(10)
+    T, Hq, Hkv, D, W = 20, 2, 1, 8, 6
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, W, P=4, margin=2)
+    krow = rng.standard_normal(D).astype(np.float32).astype(np.float64)
+    pool_k = args["pool_k"].copy()
+    used = np.isfinite(pool_k[:, 0, 0])
+    pool_k[used] = krow.astype(np.float32)
+    args["pool_k"] = pool_k
+    got = O.extend(**args)
+    for i in range(T):
+        lo = max(0, i - W)
+        n = i - lo + 1
+        for h in range(Hq):
+            s = float(q[i, h] @ krow) / math.sqrt(D)
+            want = v[lo:i + 1, 0].mean(axis=0) * n / (n + math.exp(args["sinks"][h] - s))
+            np.testing.assert_allclose(got[i, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_gqa_equals_expanded_heads():
+    """G q heads sharing one kv head equal G copies of that kv head with G = 1."""
+    rng = np.random.default_rng(11)
+    T, Hq, Hkv, D, W = 16, 8, 2, 8, 5
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, W, P=2, margin=1)
+    got = O.extend(**args)
+    G = Hq // Hkv
+    args["pool_k"] = np.repeat(args["pool_k"], G, axis=1)
+    args["pool_v"] = np.repeat(args["pool_v"], G, axis=1)
+    assert np.array_equal(O.extend(**args), got)
+
+
+def test_decode_matches_last_extend_row_and_dequant_scale():
+    rng = np.random.default_rng(12)
+    T, Hq, Hkv, D, W = 25, 4, 2, 8, 7
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, W, P=4, margin=4, kvdt="e4m3", qdt="bf16")
+    full = O.extend(**args)
+    dec = O.decode(args["q"][T - 1:T], "bf16", args["pool_k"], args["pool_v"], "e4m3", args["req_to_token"],
+                   args["req_pool_idx"], args["seq_lens"], args["full_to_swa"], W, args["sinks"])
+    assert np.array_equal(dec[0], full[T - 1])
+    # k_scale multiplies every logit; v_scale multiplies the output linearly
+    d2 = O.decode(args["q"][T - 1:T], "bf16", args["pool_k"], args["pool_v"], "e4m3", args["req_to_token"],
+                  args["req_pool_idx"], args["seq_lens"], args["full_to_swa"], W, args["sinks"], v_scale=2.0)
+    np.testing.assert_allclose(d2, 2 * dec, rtol=1e-14)
+    d3 = O.decode(args["q"][T - 1:T], "bf16", args["pool_k"], args["pool_v"], "e4m3", args["req_to_token"],
+                  args["req_pool_idx"], args["seq_lens"], args["full_to_swa"], W, args["sinks"],
+                  scale=2 / math.sqrt(D))
+    d4 = O.decode(args["q"][T - 1:T], "bf16", args["pool_k"], args["pool_v"], "e4m3", args["req_to_token"],
+                  args["req_pool_idx"], args["seq_lens"], args["full_to_swa"], W, args["sinks"], k_scale=2.0)
+    np.testing.assert_allclose(d3, d4, rtol=1e-13)
+
+
+def test_in_window_tombstone_raises():
+    rng = np.random.default_rng(13)
+    args, *_ = dense_case(rng, 20, 2, 2, 4, 4, P=2, margin=0, evict=True)
+    dec = [args[k] for k in ("pool_k", "pool_v", "pool_dtype", "req_to_token", "req_pool_idx", "seq_lens",
+                             "full_to_swa")]
+    q_last = args["q"][19:20]
+    out = O.decode(q_last, "f32", *dec, 4, args["sinks"])
+    assert np.isfinite(out).all()
+    with pytest.raises(O.OracleError):
+        O.decode(q_last, "f32", *dec, 12, args["sinks"])  # reaches into evicted pages
+    with pytest.raises(O.OracleError):
+        O.extend(**args)  # early queries of a prefill see evicted pages
+
+
+def test_pair_count_ratio_matches_page_claim():
+    g = golden()["swa_cost_ratio"]
+    T, W = g["T"], g["W"]
+    swa = O.scored_pairs(T, W)
+    full = O.scored_pairs(T, -1)
+    assert full == T * (T + 1) // 2
+    assert swa == T * (W + 1) - W * (W + 1) // 2
+    ratio = swa / full
+    assert ratio < g["fraction_below"]
+    assert abs(ratio / (2 * W / T) - 1) < 0.01  # about 2W/T
+    assert O.scored_pairs(10, 20) == O.scored_pairs(10, -1)
+
+
+def test_layout_invariance_of_oracle():
+    """The same logical K/V stored under another slot permutation gives the same output."""
+    rng = np.random.default_rng(14)
+    args1, q, k, v = dense_case(np.random.default_rng(15), 30, 4, 2, 8, 6, P=2, margin=2)
+    args2, *_ = dense_case(np.random.default_rng(16), 30, 4, 2, 8, 6, P=2, margin=2)
+    args2["q"], args2["sinks"] = args1["q"], args1["sinks"]
+    # rebuild pool 2 from the logical values of case 1
+    for name, arr in (("pool_k", k), ("pool_v", v)):
+        pool = np.full_like(args2[name], np.nan)
+        for j in range(30):
+            slot = args2["full_to_swa"][args2["req_to_token"][1, j]]
+            if slot > 0:
+                pool[slot] = arr[j].astype(np.float32)
+        args2[name] = pool
+    assert np.array_equal(O.extend(**args1), O.extend(**args2))
+    del rng
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each plausible error in the attention oracle trips a pin
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("mutation", ["drop_sink", "no_scale", "scaled_output"])
+def test_pins_catch_planted_mistakes(monkeypatch, mutation):
+    original = O.attend
+
+    def mutant(q, keys, values, sink, scale):
+        if mutation == "drop_sink":
+            return original(q, keys, values, None, scale)
+        if mutation == "no_scale":
+            return original(q, keys, values, sink, 1.0)
+        return original(q, keys, values, sink, scale) * 1.01
+
+    monkeypatch.setattr(O, "attend", mutant)
+    rng = np.random.default_rng(17)
+    args, q, k, v = dense_case(rng, 5, 4, 2, 4, 2, P=1, sinks=True)
+    got = O.extend(**args)
+    want = brute_force(q.tolist(), k.tolist(), v.tolist(), list(args["sinks"]), 2, 1 / math.sqrt(4))
+    assert not np.allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_pins_catch_off_by_one_window(monkeypatch):
+    real_attention = O.attention
+
+    def shifted(*a, **kw):
+        kw = dict(kw)
+        if "window" in kw:
+            kw["window"] = kw["window"] - 1
+        return real_attention(*a, **kw)
+
+    rng = np.random.default_rng(18)
+    args, q, k, v = dense_case(rng, 8, 2, 2, 4, 2, P=1, sinks=True)
+    want = brute_force(q.tolist(), k.tolist(), v.tolist(), list(args["sinks"]), 2, 0.5)
+    a = dict(args)
+    args_pos = (a.pop("q"), a.pop("q_dtype"), a.pop("pool_k"), a.pop("pool_v"), a.pop("pool_dtype"),
+                a.pop("req_to_token"), a.pop("req_pool_idx"), a.pop("seq_lens"), a.pop("full_to_swa"))
+    got = shifted(*args_pos, window=a["window"], sinks=a["sinks"], prefix_lens=a["prefix_lens"],
+                  qo_indptr=a["qo_indptr"])
+    assert not np.allclose(got, want, rtol=1e-9, atol=1e-12)
+    good = real_attention(*args_pos, window=a["window"], sinks=a["sinks"], prefix_lens=a["prefix_lens"],
+                          qo_indptr=a["qo_indptr"])
+    np.testing.assert_allclose(good, want, rtol=1e-12, atol=1e-14)
