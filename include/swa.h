@@ -1,0 +1,213 @@
+/*
+ * swa.h — C ABI of libswa: sliding-window attention (SWA) over a two-pool paged
+ * KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  The operations are the ones three web pages describe:
+ *   [SWA]   zdszero.github.io/swa.html — SWA design note
+ *   [POOLS] pinghaoyang.com.cn, "SGLang 源码完全拆解(十五): 内存池与显存管理"
+ *   [PR]    prhub.com.cn digest of sglang pull request 34602
+ * Each declaration below names the section it follows.
+ *
+ * Conventions shared by every call.
+ *   - Pointers are DEVICE pointers owned by the caller unless marked [host].
+ *     No call allocates or frees device memory, and none synchronises the
+ *     device except swa_validate, which is a debugging aid.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream).  Argument errors are detected on the host, before anything is
+ *     enqueued, and returned synchronously; a failed launch returns SWA_E_HIP.
+ *   - Kernels never fault on bad index data.  A slot, loc or position outside
+ *     its table or pool is replaced by 0, the padding row / page 0 sink of every
+ *     pool and table ([POOLS] 一重映射 and 二重映射: row 0 of req_to_token and
+ *     slot 0 of each KV buffer absorb padded reads and writes); a store to a loc
+ *     outside the pool is dropped.  swa_validate reports such data.
+ *   - The library is stateless and thread-safe; calls that share output
+ *     buffers on different streams race, as any two kernels would.
+ *   - Every index is an element index, never a byte offset; slot offsets are
+ *     computed in 64-bit arithmetic, so pools may exceed 2^31 rows x bytes
+ *     ([PR] 实现拆解: the kernel-facing row bound of int32 index buffers).
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Negative values are errors. */
+typedef enum swa_status {
+  SWA_OK = 0,
+  SWA_E_ARG = -1,       /* null pointer, negative size, inconsistent arguments */
+  SWA_E_DTYPE = -2,     /* unsupported dtype or dtype combination */
+  SWA_E_SHAPE = -3,     /* unsupported head_dim / head counts / group size */
+  SWA_E_NOSPACE = -4,   /* pool sizing: the SWA pool cannot hold one request */
+  SWA_E_WORKSPACE = -5, /* workspace missing or smaller than required */
+  SWA_E_HIP = -6        /* the HIP runtime reported an error (launch / query) */
+} swa_status_t;
+
+/* Element types.  fp8 pools hold raw bytes ([POOLS] 二重映射: fp8 KV caches
+ * are stored as uint8 and re-interpreted on read); the format is OCP e4m3fn. */
+typedef enum swa_dtype {
+  SWA_F32 = 0,
+  SWA_BF16 = 1,
+  SWA_FP8_E4M3 = 2
+} swa_dtype_t;
+
+/* One layer's dense K and V views of a pool ([POOLS] 二重映射: per-layer
+ * k_buffer / v_buffer of shape (size + page_size, head_num, head_dim);
+ * [SWA] 双池与映射表: the full pool and the SWA pool are two ordinary pools).
+ * k and v are row-major (rows, kv_heads, head_dim) arrays of `dtype`;
+ * row 0 is the padding sink.  k_scale / v_scale dequantise fp8 (value = code
+ * * scale); they are ignored for f32 / bf16 and must be 1 there. */
+typedef struct swa_kv_layer {
+  void *k;
+  void *v;
+  int64_t rows;      /* = N + page_size */
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t dtype;     /* swa_dtype_t */
+  float k_scale;
+  float v_scale;
+} swa_kv_layer_t;
+
+/* The batch's index structures.
+ *   req_to_token  int32 (r2t_rows, r2t_stride): full-pool slot of each position
+ *                 of each request row; row 0 is padding ([POOLS] 一重映射).
+ *   req_pool_idx  int32 (batch): the req_to_token row of each request.
+ *   seq_lens      int32 (batch): tokens of each request INCLUDING the ones
+ *                 being computed (decode: the current token is stored first).
+ *   full_to_swa   int64 (map_len): SWA slot of each full slot, 0 = no SWA slot
+ *                 (tombstone), last entry -1 so that -1 translates to -1
+ *                 ([SWA] 双池与映射表; [POOLS] 双池 + 映射表).  map_len is
+ *                 full pool size + page_size + 1.  NULL for full layers.
+ *   page_size     pages of both pools; kernels translate per token, so it is
+ *                 used only for validation. */
+typedef struct swa_index {
+  const int32_t *req_to_token;
+  int64_t r2t_rows;
+  int64_t r2t_stride;
+  const int32_t *req_pool_idx;
+  const int32_t *seq_lens;
+  const int64_t *full_to_swa;
+  int64_t map_len;
+  int32_t batch;
+  int32_t page_size;
+} swa_index_t;
+
+/* ---------------------------------------------------------------------------
+ * Pool sizing — [SWA] 显存怎么分 (--swa-full-tokens-ratio).  All [host].
+ *   cell   = full_bytes_per_token * n_full_layers
+ *          + ratio * swa_bytes_per_token * n_swa_layers
+ *   N_full = floor(avail_bytes / cell), N_swa = floor(ratio * N_full), both
+ *   rounded down to page_size.  *_bytes_per_token is num_kv_heads *
+ *   (head_dim + v_head_dim) * dtype_size of one layer.
+ * Returns SWA_E_NOSPACE when N_swa <= window + page_size (the startup error on
+ * the page), SWA_E_ARG for non-positive page_size, negative sizes or ratio, or
+ * null outputs.  Outputs are written on SWA_OK and on SWA_E_NOSPACE. */
+swa_status_t swa_pool_config(int64_t avail_bytes, double ratio, int32_t page_size, int32_t window,
+                             int32_t n_full_layers, int64_t full_bytes_per_token,
+                             int32_t n_swa_layers, int64_t swa_bytes_per_token,
+                             int64_t *n_full_tokens, int64_t *n_swa_tokens);
+
+/* ---------------------------------------------------------------------------
+ * translate_loc — [SWA] Attention backend (translate_loc_from_full_to_swa is
+ * full_to_swa[idx]) and 双池与映射表 (the -1 sentinel).
+ *   swa_loc[i] = full_to_swa[full_loc[i]]  for 0 <= full_loc[i] < map_len - 1
+ *              = full_to_swa[map_len - 1] (= -1) for full_loc[i] == -1
+ *              = 0 for any other value.
+ * full_loc, swa_loc: int64 (n); may not alias.  n == 0 is a no-op. */
+swa_status_t swa_translate_loc(const int64_t *full_loc, int64_t n, const int64_t *full_to_swa,
+                               int64_t map_len, int64_t *swa_loc, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * translate_window — the fused index translation + window gather, done once
+ * per batch and shared by every SWA layer ([SWA] Attention backend: backends
+ * build the window's translated indices once per batch; FlashInfer keeps W+1
+ * positions, which is why W excludes the current token, [SWA] 实现).
+ * For request b with row r = req_pool_idx[b], L = seq_lens[b],
+ * p = prefix_lens ? prefix_lens[b] : L - 1 (decode):
+ *   positions lo .. L-1, lo = (window < 0) ? 0 : max(0, p - window)
+ *   slot_table[table_indptr[b] + k] = T(req_to_token[r][lo + k])
+ * with T = full_to_swa (0 for an index outside the table, -1 -> -1) when
+ * idx->full_to_swa is set, identity otherwise.
+ * table_indptr: int32 (batch + 1), written by the kernel (exclusive prefix sum
+ * of the counts L - lo, clamped at 0).  Entries past table_capacity are not
+ * written; the caller sizes the table (decode: batch * (window + 1)). */
+swa_status_t swa_translate_window(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens,
+                                  int32_t *slot_table, int32_t *table_indptr,
+                                  int64_t table_capacity, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_store — scatter new K/V rows into a pool ([SWA] Attention backend: SWA
+ * layers receive an already translated swa_loc and the pool never translates;
+ * [POOLS] 谁在往页里写 (KVWriteLoc) and 二重映射).
+ *   layer->k[loc[i]] = cvt(k_new[i]), layer->v[loc[i]] = cvt(v_new[i])
+ * k_new, v_new: (n, kv_heads, head_dim) of in_dtype.  loc: int64 (n), physical
+ * rows of THIS pool; rows outside [0, rows) are skipped.  Conversions:
+ * same dtype -> byte copy; f32 -> bf16 and f32/bf16 -> e4m3 round to nearest
+ * even, e4m3 saturates to +-448 and maps NaN to 0x7F.  Duplicate locs (other
+ * than the padding row 0) race; swa_validate reports them. */
+swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64_t n,
+                          const void *k_new, const void *v_new, int32_t in_dtype,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode planning [host]: number of key splits per (request, kv head) and the
+ * workspace swa_decode needs.  max_seq_len is a host-side upper bound of
+ * seq_lens (a performance hint: any split count gives correct results).
+ * SWA layers (window >= 0) use one split and no workspace. */
+swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                             int32_t window, int64_t max_seq_len, int32_t *num_splits,
+                             size_t *workspace_bytes);
+
+/* ---------------------------------------------------------------------------
+ * decode — one query per request at position i = seq_lens[b] - 1 ([SWA]
+ * opening paragraph: each query sees the most recent window; 实现: W excludes
+ * the current token, -1 = full; 设计: learnable per-head sink):
+ *   keys j in [max(0, i - W), i] (all of [0, i] for window = -1)
+ *   s_j = sm_scale * q_h . k_j, with kv head g = h / (q_heads / kv_heads)
+ *   m   = max(max_j s_j, sink_h)
+ *   o_h = sum_j e^{s_j - m} v_j / (sum_j e^{s_j - m} + e^{sink_h - m})
+ * sinks NULL means no sink (sink_h = -inf).
+ * Keys come from the window table when table_indptr is given (SWA layers: the
+ * output of swa_translate_window with the same window), otherwise from
+ * req_to_token directly (full layers, or single-pool windowed attention).
+ * q: (batch, q_heads, head_dim) of q_dtype; out: same shape of out_dtype
+ * (SWA_F32, or SWA_BF16 = the f32 result rounded to nearest even).
+ * Supported: head_dim 128; q_dtype f32 with f32 K/V; q_dtype bf16 with bf16 or
+ * e4m3 K/V; q_heads / kv_heads in {1, 2, 4, 8, 16}.
+ * num_splits and workspace come from swa_decode_plan for the same shape. */
+swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
+                        void *out, int32_t out_dtype, int32_t num_splits, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * extend — windowed-causal prefill of a chunk over a cached prefix ([SWA]
+ * 运行时: chunked prefill; same formula as decode).  Request b owns query rows
+ * qo_indptr[b] .. qo_indptr[b+1]-1 holding positions prefix_lens[b] ..
+ * seq_lens[b]-1; query i sees keys [max(0, i - W), i].  The chunk's own K/V
+ * must already be in the pool (swa_kv_store first).
+ * q, out: (total_q, q_heads, head_dim).  total_q (host) is the row count of q
+ * and out, i.e. qo_indptr[batch].  Keys come from the window table built by
+ * swa_translate_window(prefix_lens) when table_indptr is given, else from
+ * req_to_token directly.  Supported: head_dim 128, bf16 q with bf16 K/V,
+ * q_heads / kv_heads in {1, 2, 4, 8, 16}. */
+swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
+                        const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
+                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
+                        void *out, int32_t out_dtype, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *swa_status_string(swa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

@@ -1,0 +1,230 @@
+// C ABI of libswa: argument checks on the host, then kernel launches on the
+// caller's stream.  Every check runs before any HIP call, so argument errors
+// never touch the device.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+constexpr int32_t kHeadDim = 128;
+// gfx950 (MI355X) has 256 compute units; split planning targets ~8
+// workgroups per CU for long full-attention contexts.
+constexpr int64_t kTargetWorkgroups = 2048;
+constexpr int64_t kMinKeysPerSplit = 512;
+constexpr int32_t kMaxSplits = 1024;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_group(int32_t q_heads, int32_t kv_heads) {
+  if (kv_heads <= 0 || q_heads <= 0 || q_heads % kv_heads) return false;
+  const int32_t g = q_heads / kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+}
+
+swa_status_t from_hip(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_E_HIP; }
+
+swa_status_t check_layer(const swa_kv_layer_t *layer) {
+  if (!layer || !layer->k || !layer->v) return SWA_E_ARG;
+  if (layer->rows < 1 || layer->kv_heads < 1 || layer->head_dim < 1) return SWA_E_ARG;
+  if (layer->dtype != SWA_F32 && layer->dtype != SWA_BF16 && layer->dtype != SWA_FP8_E4M3) return SWA_E_DTYPE;
+  if (!aligned16(layer->k) || !aligned16(layer->v)) return SWA_E_ARG;
+  if (layer->dtype == SWA_FP8_E4M3) {
+    if (!(layer->k_scale > 0.f) || !(layer->v_scale > 0.f) || !std::isfinite(layer->k_scale) ||
+        !std::isfinite(layer->v_scale))
+      return SWA_E_ARG;
+  }
+  return SWA_OK;
+}
+
+swa_status_t check_index(const swa_index_t *idx, bool need_r2t) {
+  if (!idx || idx->batch < 0) return SWA_E_ARG;
+  if (idx->batch == 0) return SWA_OK;
+  if (!idx->seq_lens) return SWA_E_ARG;
+  if (need_r2t) {
+    if (!idx->req_to_token || !idx->req_pool_idx || idx->r2t_rows < 1 || idx->r2t_stride < 1) return SWA_E_ARG;
+  }
+  if (idx->full_to_swa && idx->map_len < 2) return SWA_E_ARG;
+  return SWA_OK;
+}
+
+// Slots pass through int32 window tables, so a pool addressed through them
+// must have fewer than 2^31 rows.
+constexpr int64_t kMaxRows = INT32_MAX;
+
+}  // namespace
+
+extern "C" {
+
+swa_status_t swa_pool_config(int64_t avail_bytes, double ratio, int32_t page_size, int32_t window,
+                             int32_t n_full_layers, int64_t full_bytes_per_token, int32_t n_swa_layers,
+                             int64_t swa_bytes_per_token, int64_t *n_full_tokens, int64_t *n_swa_tokens) {
+  if (!n_full_tokens || !n_swa_tokens) return SWA_E_ARG;
+  if (page_size <= 0 || avail_bytes < 0 || !(ratio >= 0.0) || !std::isfinite(ratio) || window < -1 ||
+      n_full_layers < 0 || n_swa_layers < 0 || full_bytes_per_token < 0 || swa_bytes_per_token < 0)
+    return SWA_E_ARG;
+  const double cell = static_cast<double>(full_bytes_per_token) * n_full_layers +
+                      ratio * static_cast<double>(swa_bytes_per_token) * n_swa_layers;
+  if (!(cell > 0.0)) return SWA_E_ARG;
+  int64_t n_full = static_cast<int64_t>(std::floor(static_cast<double>(avail_bytes) / cell));
+  n_full = n_full / page_size * page_size;
+  int64_t n_swa = static_cast<int64_t>(std::floor(ratio * static_cast<double>(n_full)));
+  n_swa = n_swa / page_size * page_size;
+  *n_full_tokens = n_full;
+  *n_swa_tokens = n_swa;
+  if (n_swa <= static_cast<int64_t>(window) + page_size) return SWA_E_NOSPACE;
+  return SWA_OK;
+}
+
+swa_status_t swa_translate_loc(const int64_t *full_loc, int64_t n, const int64_t *full_to_swa, int64_t map_len,
+                               int64_t *swa_loc, hipStream_t stream) {
+  if (n < 0) return SWA_E_ARG;
+  if (n == 0) return SWA_OK;
+  if (!full_loc || !full_to_swa || !swa_loc || map_len < 2) return SWA_E_ARG;
+  if (full_loc == swa_loc) return SWA_E_ARG;
+  return from_hip(swa::launch_translate_loc(full_loc, n, full_to_swa, map_len, swa_loc, stream));
+}
+
+swa_status_t swa_translate_window(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens,
+                                  int32_t *slot_table, int32_t *table_indptr, int64_t table_capacity,
+                                  hipStream_t stream) {
+  swa_status_t st = check_index(idx, true);
+  if (st != SWA_OK) return st;
+  if (window < -1 || table_capacity < 0 || !table_indptr) return SWA_E_ARG;
+  if (table_capacity > 0 && !slot_table) return SWA_E_ARG;
+  return from_hip(swa::launch_translate_window(*idx, window, prefix_lens, slot_table, table_indptr, table_capacity,
+                                               stream));
+}
+
+swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64_t n, const void *k_new,
+                          const void *v_new, int32_t in_dtype, hipStream_t stream) {
+  swa_status_t st = check_layer(layer);
+  if (st != SWA_OK) return st;
+  if (n < 0) return SWA_E_ARG;
+  const int32_t out = layer->dtype;
+  const bool pair_ok = (in_dtype == out && in_dtype != SWA_FP8_E4M3) || (in_dtype == SWA_F32 && out == SWA_BF16) ||
+                       (in_dtype == SWA_BF16 && out == SWA_FP8_E4M3) || (in_dtype == SWA_F32 && out == SWA_FP8_E4M3);
+  if (!pair_ok) return SWA_E_DTYPE;
+  if ((static_cast<int64_t>(layer->kv_heads) * layer->head_dim) % 8) return SWA_E_SHAPE;
+  if (n == 0) return SWA_OK;
+  if (!loc || !k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return SWA_E_ARG;
+  return from_hip(swa::launch_kv_store(*layer, loc, n, k_new, v_new, in_dtype, stream));
+}
+
+swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim, int32_t window,
+                             int64_t max_seq_len, int32_t *num_splits, size_t *workspace_bytes) {
+  if (!num_splits || !workspace_bytes) return SWA_E_ARG;
+  if (batch < 0 || window < -1 || max_seq_len < 0) return SWA_E_ARG;
+  if (head_dim != kHeadDim) return SWA_E_SHAPE;
+  if (!valid_group(q_heads, kv_heads)) return SWA_E_SHAPE;
+  int64_t splits = 1;
+  if (window < 0 && batch > 0) {
+    const int64_t by_fill = (kTargetWorkgroups + static_cast<int64_t>(batch) * kv_heads - 1) /
+                            (static_cast<int64_t>(batch) * kv_heads);
+    const int64_t by_len = (max_seq_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
+    splits = by_fill < by_len ? by_fill : by_len;
+    if (splits < 1) splits = 1;
+    if (splits > kMaxSplits) splits = kMaxSplits;
+  }
+  *num_splits = static_cast<int32_t>(splits);
+  *workspace_bytes = splits > 1 ? static_cast<size_t>(batch) * q_heads * splits * (2 + kHeadDim) * sizeof(float) : 0;
+  return SWA_OK;
+}
+
+swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                        int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  swa_status_t st = check_layer(layer);
+  if (st != SWA_OK) return st;
+  st = check_index(idx, table_indptr == nullptr);
+  if (st != SWA_OK) return st;
+  if (!q || !out || window < -1 || num_splits < 1 || num_splits > kMaxSplits) return SWA_E_ARG;
+  if (!std::isfinite(sm_scale)) return SWA_E_ARG;
+  if (table_indptr && (!slot_table || table_capacity < 0)) return SWA_E_ARG;
+  if (layer->head_dim != kHeadDim) return SWA_E_SHAPE;
+  if (!valid_group(q_heads, layer->kv_heads)) return SWA_E_SHAPE;
+  if (layer->rows > kMaxRows) return SWA_E_SHAPE;
+  const bool f32_path = q_dtype == SWA_F32 && layer->dtype == SWA_F32;
+  const bool mfma_path = q_dtype == SWA_BF16 && (layer->dtype == SWA_BF16 || layer->dtype == SWA_FP8_E4M3);
+  if (!f32_path && !mfma_path) return SWA_E_DTYPE;
+  if (out_dtype != SWA_F32 && out_dtype != SWA_BF16) return SWA_E_DTYPE;
+  if (!aligned16(q) || !aligned16(out)) return SWA_E_ARG;
+  if (num_splits > 1) {
+    const size_t need = static_cast<size_t>(idx->batch) * q_heads * num_splits * (2 + kHeadDim) * sizeof(float);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SWA_E_WORKSPACE;
+  }
+  swa::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.q_heads = q_heads;
+  a.layer = *layer;
+  a.idx = *idx;
+  a.table = slot_table;
+  a.indptr = table_indptr;
+  a.capacity = table_capacity;
+  a.window = window;
+  a.sinks = sinks;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.num_splits = num_splits;
+  a.ws = static_cast<float *>(workspace);
+  return from_hip(swa::launch_decode(a, stream));
+}
+
+swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
+                        const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
+                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                        int32_t out_dtype, hipStream_t stream) {
+  swa_status_t st = check_layer(layer);
+  if (st != SWA_OK) return st;
+  st = check_index(idx, true);
+  if (st != SWA_OK) return st;
+  if (total_q < 0 || window < -1 || !std::isfinite(sm_scale)) return SWA_E_ARG;
+  if (idx->batch > 0 && (!qo_indptr || !prefix_lens)) return SWA_E_ARG;
+  if (total_q > 0 && (!q || !out)) return SWA_E_ARG;
+  if (table_indptr && (!slot_table || table_capacity < 0)) return SWA_E_ARG;
+  if (layer->head_dim != kHeadDim) return SWA_E_SHAPE;
+  if (!valid_group(q_heads, layer->kv_heads)) return SWA_E_SHAPE;
+  if (layer->rows > kMaxRows || total_q > INT32_MAX) return SWA_E_SHAPE;
+  if (q_dtype != SWA_BF16 || layer->dtype != SWA_BF16) return SWA_E_DTYPE;
+  if (out_dtype != SWA_F32 && out_dtype != SWA_BF16) return SWA_E_DTYPE;
+  if (total_q > 0 && (!aligned16(q) || !aligned16(out))) return SWA_E_ARG;
+  swa::ExtendArgs a{};
+  a.q = q;
+  a.q_heads = q_heads;
+  a.qo_indptr = qo_indptr;
+  a.prefix_lens = prefix_lens;
+  a.total_q = total_q;
+  a.layer = *layer;
+  a.idx = *idx;
+  a.table = slot_table;
+  a.indptr = table_indptr;
+  a.capacity = table_capacity;
+  a.window = window;
+  a.sinks = sinks;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return from_hip(swa::launch_extend(a, stream));
+}
+
+const char *swa_status_string(swa_status_t status) {
+  switch (status) {
+    case SWA_OK: return "ok";
+    case SWA_E_ARG: return "invalid argument";
+    case SWA_E_DTYPE: return "unsupported dtype";
+    case SWA_E_SHAPE: return "unsupported shape";
+    case SWA_E_NOSPACE: return "SWA pool cannot hold window + page";
+    case SWA_E_WORKSPACE: return "workspace missing or too small";
+    case SWA_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

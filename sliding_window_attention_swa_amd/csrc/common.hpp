@@ -1,0 +1,110 @@
+// Internal helpers shared by the HIP kernels of libswa (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swa.h"
+
+namespace swa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;   // MFMA bf16 operand
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;    // 16x16 MFMA accumulator
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;  // packed conversion result
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Finite stand-in for -inf as a running maximum: exp2(x - kNegBig) stays 0 for
+// x = -inf and exp2(kNegBig - kNegBig) = 1, so empty ranges never produce NaN.
+constexpr float kNegBig = -1.0e30f;
+
+// bf16 <-> f32.  bf16 is the upper half of an IEEE binary32 word.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN -> quiet NaN 0x7FC0.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+
+// OCP e4m3fn encoder: round to nearest even, saturate finite overflow (and inf)
+// to +-448, NaN -> 0x7F.  Normal range: the binary32 word is rounded at the
+// 20-bit boundary (3 mantissa bits kept) and re-biased (127 - 7 = 120);
+// below 2^-6 the value is a multiple of 2^-9 and rintf gives the RNE count.
+__device__ __forceinline__ uint8_t f32_to_e4m3_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7F;
+  uint32_t code;
+  if (a < 0x3C800000u) {  // |f| < 2^-6: subnormal codes 0..8
+    code = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));
+  } else {
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return static_cast<uint8_t>(sign | code);
+}
+
+// 64-bit row offset of (slot, head) in a (rows, heads, dim) array, in elements.
+__device__ __forceinline__ int64_t row_elem(int64_t slot, int32_t heads, int32_t head, int32_t dim) {
+  return (slot * heads + head) * static_cast<int64_t>(dim);
+}
+
+}  // namespace swa
+
+// Launchers implemented in the .hip translation units (host side, internal).
+namespace swa {
+hipError_t launch_translate_loc(const int64_t *full_loc, int64_t n, const int64_t *map, int64_t map_len,
+                                int64_t *out, hipStream_t stream);
+hipError_t launch_translate_window(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
+                                   int32_t *table, int32_t *indptr, int64_t capacity, hipStream_t stream);
+hipError_t launch_kv_store(const swa_kv_layer_t &layer, const int64_t *loc, int64_t n, const void *k_new,
+                           const void *v_new, int32_t in_dtype, hipStream_t stream);
+
+struct DecodeArgs {
+  const void *q;
+  int32_t q_dtype;
+  int32_t q_heads;
+  swa_kv_layer_t layer;
+  swa_index_t idx;
+  const int32_t *table;
+  const int32_t *indptr;
+  int64_t capacity;
+  int32_t window;
+  const float *sinks;
+  float sm_scale;
+  void *out;
+  int32_t out_dtype;
+  int32_t num_splits;
+  float *ws;  // partials: m, l (batch*q_heads*num_splits each), acc (... * head_dim)
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+struct ExtendArgs {
+  const void *q;
+  int32_t q_heads;
+  const int32_t *qo_indptr;
+  const int32_t *prefix_lens;
+  int64_t total_q;
+  swa_kv_layer_t layer;
+  swa_index_t idx;
+  const int32_t *table;
+  const int32_t *indptr;
+  int64_t capacity;
+  int32_t window;
+  const float *sinks;
+  float sm_scale;
+  void *out;
+  int32_t out_dtype;
+};
+hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream);
+}  // namespace swa

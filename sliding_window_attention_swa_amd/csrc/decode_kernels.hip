@@ -1,0 +1,600 @@
+// Windowed decode attention over a paged pool (one query per request).
+//
+// What is computed (SWA note, zdszero.github.io/swa.html: opening paragraph —
+// each query attends to the most recent window; section 实现 — the configured
+// window excludes the current token and -1 means full attention; section 设计 —
+// a learnable per-head sink logit):
+//   query position i = seq_len - 1, keys j in [max(0, i - W), i]
+//   s_j = sm_scale * q_h . k_j       (kv head g = h / G)
+//   o_h = sum_j e^{s_j - m} v_j / (sum_j e^{s_j - m} + e^{sink_h - m})
+//
+// Work decomposition (MI355X-specific, not the pages' kernels):
+//   * one workgroup per (key split, kv head, request); the G query heads that
+//     share a kv head are computed together, so each K/V row is read from HBM
+//     exactly once per layer;
+//   * inside the workgroup the keys are dealt to NW wavefronts in 16-key
+//     blocks; each wavefront keeps a running (max, sum, acc) per head
+//     (online softmax in base 2) and the wavefronts are merged through LDS;
+//   * with several splits (full layers over long contexts) each workgroup
+//     writes its (max, sum, acc) partial and a merge kernel combines them; the
+//     sink enters exactly once, in the final merge.
+//
+// bf16 / e4m3 K/V path: S^T = K Q^T and O^T = V^T P^T on the CDNA4 matrix
+// cores (v_mfma_f32_16x16x32_bf16).  With keys as the M dimension of the
+// first product, its accumulator layout (lane = head column, 4 keys per lane)
+// is exactly the B-operand layout the second product needs for P^T, so P
+// never leaves registers.  The head dimension is permuted identically in Q and
+// K (lane group q covers dims 32q..32q+31) so each lane reads 64 contiguous
+// bytes of a K row.  V is staged through LDS (padded rows, conflict-free
+// transposed reads) because the key index must be the per-lane contraction
+// index of the second product.  e4m3 bytes are widened to bf16 exactly with
+// v_cvt_scalef32_pk_bf16_fp8; the per-tensor scales are folded into the logit
+// scale and the output.
+//
+// f32 path: plain VALU, one key row per wavefront step, two dims per lane.
+#include "common.hpp"
+
+namespace swa {
+namespace {
+
+constexpr int kD = 128;           // head_dim handled by these kernels
+constexpr int kMaxG = 16;         // q heads per kv head (MFMA N = 16)
+constexpr int kVRow = kD + 4;     // LDS V row: 264 bytes, 2-dword skew per row
+
+struct DecodeParams {
+  const void *q;
+  const void *k;
+  const void *v;
+  int64_t rows;
+  int32_t kv_heads;
+  int32_t q_heads;
+  int32_t group;
+  float k_scale;
+  float v_scale;
+  const int32_t *r2t;
+  int64_t r2t_rows;
+  int64_t r2t_stride;
+  const int32_t *req_idx;
+  const int32_t *seq_lens;
+  const int32_t *table;
+  const int32_t *indptr;
+  int64_t capacity;
+  int32_t window;
+  const float *sinks;
+  float scale2;  // sm_scale * k_scale * log2(e)
+  void *out;
+  int32_t num_splits;
+  float *ws_m;
+  float *ws_l;
+  float *ws_acc;
+};
+
+// Keys of request b for this layer, as [first, first + n) of either the window
+// table (table mode) or positions of the request row (req_to_token mode).
+struct KeySource {
+  const int32_t *src;  // slot of key k is src[k]
+  int32_t n;
+};
+
+__device__ __forceinline__ KeySource key_source(const DecodeParams &p, int32_t b) {
+  KeySource ks{p.table, 0};
+  if (p.indptr) {
+    int64_t lo = p.indptr[b];
+    int64_t hi = p.indptr[b + 1];
+    if (lo < 0) lo = 0;
+    if (hi > p.capacity) hi = p.capacity;
+    ks.src = p.table + lo;
+    ks.n = hi > lo ? static_cast<int32_t>(hi - lo) : 0;
+    return ks;
+  }
+  int32_t L = p.seq_lens[b];
+  if (L > p.r2t_stride) L = static_cast<int32_t>(p.r2t_stride);
+  if (L <= 0) {
+    ks.src = p.r2t;
+    return ks;
+  }
+  const int32_t i = L - 1;
+  int32_t lo = p.window < 0 ? 0 : i - p.window;
+  if (lo < 0) lo = 0;
+  int64_t row = p.req_idx[b];
+  if (row < 0 || row >= p.r2t_rows) row = 0;
+  ks.src = p.r2t + row * p.r2t_stride + lo;
+  ks.n = L - lo;
+  return ks;
+}
+
+__device__ __forceinline__ int64_t safe_slot(int32_t s, int64_t rows) {
+  return (s < 0 || s >= rows) ? 0 : static_cast<int64_t>(s);
+}
+
+__device__ __forceinline__ float wave_max_q(float x) {  // over the 4 lane groups (lanes l, l^16, l^32, l^48)
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_q(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float wave_sum_all(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Split of request keys handled by workgroup `s`: a multiple of 16 keys.
+__device__ __forceinline__ void split_range(int32_t n, int32_t s, int32_t splits, int32_t *k0, int32_t *k1) {
+  int32_t per = (n + splits - 1) / splits;
+  per = (per + 15) & ~15;
+  int32_t a = s * per;
+  int32_t e = a + per;
+  if (a > n) a = n;
+  if (e > n) e = n;
+  *k0 = a;
+  *k1 = e;
+}
+
+// --------------------------------------------------------------------------
+// Shared epilogue: combine NW wavefront partials held in LDS and either write
+// the final output (one split) or this split's partial to the workspace.
+// red_m / red_l: [NW][kMaxG] (base-2 logit domain); red_acc: [NW][G][kD].
+// --------------------------------------------------------------------------
+template <int NW, bool OUT_BF16>
+__device__ void merge_waves_and_store(const DecodeParams &p, const float *red_m, const float *red_l,
+                                      const float *red_acc, int32_t b, int32_t g, int32_t s) {
+  const int32_t G = p.group;
+  const bool final = p.num_splits == 1;
+  // each thread produces 4 consecutive dims of one head
+  for (int32_t t = threadIdx.x; t < G * (kD / 4); t += NW * 64) {
+    const int32_t hh = t / (kD / 4);
+    const int32_t d4 = (t % (kD / 4)) * 4;
+    const int32_t h = g * G + hh;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * kMaxG + hh]);
+    float sig2 = -INFINITY;
+    if (final && p.sinks) {
+      sig2 = p.sinks[h] * kLog2e;
+      M = fmaxf(M, sig2);
+    }
+    float L = 0.f;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = exp2f(red_m[w * kMaxG + hh] - M);
+      L += red_l[w * kMaxG + hh] * a;
+      const float4 v = *reinterpret_cast<const float4 *>(red_acc + (w * G + hh) * kD + d4);
+      o0 += v.x * a;
+      o1 += v.y * a;
+      o2 += v.z * a;
+      o3 += v.w * a;
+    }
+    if (final) {
+      if (p.sinks) L += exp2f(sig2 - M);
+      const float inv = L > 0.f ? p.v_scale / L : 0.f;
+      o0 *= inv;
+      o1 *= inv;
+      o2 *= inv;
+      o3 *= inv;
+      const int64_t off = (static_cast<int64_t>(b) * p.q_heads + h) * kD + d4;
+      if (OUT_BF16) {
+        uint2 pk = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + off) = pk;
+      } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + off) = make_float4(o0, o1, o2, o3);
+      }
+    } else {
+      const int64_t pi = (static_cast<int64_t>(b) * p.q_heads + h) * p.num_splits + s;
+      if (d4 == 0) {
+        p.ws_m[pi] = M;
+        p.ws_l[pi] = L;
+      }
+      *reinterpret_cast<float4 *>(p.ws_acc + pi * kD + d4) = make_float4(o0, o1, o2, o3);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// MFMA path (bf16 q; bf16 or e4m3 K/V)
+// --------------------------------------------------------------------------
+template <typename KV>
+struct KvLoad;
+
+template <>
+struct KvLoad<uint16_t> {  // bf16 rows: 64 bytes per lane = 4 x 16 B
+  static constexpr int kVecs = 4;
+  __device__ static void to_bf16(const uint4 *raw, bf16x8_t *ops) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) __builtin_memcpy(&ops[c], &raw[c], 16);
+  }
+};
+
+template <>
+struct KvLoad<uint8_t> {  // e4m3 rows: 32 bytes per lane = 2 x 16 B, widened exactly
+  static constexpr int kVecs = 2;
+  __device__ static void to_bf16(const uint4 *raw, bf16x8_t *ops) {
+    uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * c], 1.0f, false);
+      bf16x2_t bq = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * c], 1.0f, true);
+      bf16x2_t cc = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * c + 1], 1.0f, false);
+      bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * c + 1], 1.0f, true);
+      uint32_t u[4];
+      __builtin_memcpy(&u[0], &a, 4);
+      __builtin_memcpy(&u[1], &bq, 4);
+      __builtin_memcpy(&u[2], &cc, 4);
+      __builtin_memcpy(&u[3], &d, 4);
+      __builtin_memcpy(&ops[c], u, 16);
+    }
+  }
+};
+
+// Raw registers of one 16-key block for this lane (key = lane % 16, dims 32q..32q+31).
+template <typename KV>
+struct BlockRegs {
+  uint4 k[KvLoad<KV>::kVecs];
+  uint4 v[KvLoad<KV>::kVecs];
+};
+
+template <typename KV>
+__device__ __forceinline__ void load_block(const DecodeParams &p, const KeySource &ks, int32_t key, bool valid,
+                                           int32_t g, int32_t lq, BlockRegs<KV> &r) {
+#pragma unroll
+  for (int c = 0; c < KvLoad<KV>::kVecs; ++c) {
+    r.k[c] = make_uint4(0, 0, 0, 0);
+    r.v[c] = make_uint4(0, 0, 0, 0);
+  }
+  if (!valid) return;
+  const int64_t slot = safe_slot(ks.src[key], p.rows);
+  const int64_t off = row_elem(slot, p.kv_heads, g, kD) + 32 * lq;
+  const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.k) + off);
+  const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.v) + off);
+#pragma unroll
+  for (int c = 0; c < KvLoad<KV>::kVecs; ++c) {
+    r.k[c] = kp[c];
+    r.v[c] = vp[c];
+  }
+}
+
+template <typename KV, int NW, bool OUT_BF16>
+__global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeParams p) {
+  // LDS: per-wave V tile [32 keys][kVRow] bf16, reused for the merge.
+  constexpr int kTileBytes = NW * 32 * kVRow * 2;
+  constexpr int kRedBytes = NW * kMaxG * kD * 4;
+  constexpr int kLdsBytes = kTileBytes > kRedBytes ? kTileBytes : kRedBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ float red_m[NW * kMaxG];
+  __shared__ float red_l[NW * kMaxG];
+
+  const int32_t s = blockIdx.x;
+  const int32_t g = blockIdx.y;
+  const int32_t b = blockIdx.z;
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;  // key row (A operand) / head column (B operand, accumulators)
+  const int32_t lq = lane >> 4;  // lane group
+  const int32_t G = p.group;
+
+  const KeySource ks = key_source(p, b);
+  int32_t k0, k1;
+  split_range(ks.n, s, p.num_splits, &k0, &k1);
+  const int32_t nblk = (k1 - k0 + 15) >> 4;
+
+  // Q^T operand: head g*G + kr, dims 32*lq .. 32*lq+31 (zeros for padding heads).
+  bf16x8_t qop[4];
+  {
+    uint4 raw[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    if (kr < G) {
+      const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
+                                                        (static_cast<int64_t>(b) * p.q_heads + g * G + kr) * kD +
+                                                        32 * lq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw[c] = qp[c];
+    }
+    KvLoad<uint16_t>::to_bf16(raw, qop);
+  }
+
+  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * 32 * kVRow;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig;
+  float l_run = 0.f;
+
+  // Pairs of this wave's blocks: (w + 2u*NW, w + (2u+1)*NW).
+  const int32_t npair = (nblk > w) ? ((nblk - w + NW - 1) / NW + 1) / 2 : 0;
+  BlockRegs<KV> cur0, cur1, nxt0, nxt1;
+  auto issue = [&](int32_t u, BlockRegs<KV> &r0, BlockRegs<KV> &r1) {
+    const int32_t t0 = w + 2 * u * NW;
+    const int32_t t1 = t0 + NW;
+    const int32_t key0 = k0 + 16 * t0 + kr;
+    const int32_t key1 = k0 + 16 * t1 + kr;
+    load_block<KV>(p, ks, key0, t0 < nblk && key0 < k1, g, lq, r0);
+    load_block<KV>(p, ks, key1, t1 < nblk && key1 < k1, g, lq, r1);
+  };
+  if (npair > 0) issue(0, cur0, cur1);
+
+  for (int32_t u = 0; u < npair; ++u) {
+    if (u + 1 < npair) issue(u + 1, nxt0, nxt1);
+    const int32_t t0 = w + 2 * u * NW;
+    const int32_t t1 = t0 + NW;
+
+    // ---- V rows -> LDS (bf16), this lane's key row, dims 32lq..32lq+31
+    {
+      bf16x8_t v0[4], v1[4];
+      KvLoad<KV>::to_bf16(cur0.v, v0);
+      KvLoad<KV>::to_bf16(cur1.v, v1);
+      uint2 *d0 = reinterpret_cast<uint2 *>(vt + kr * kVRow + 32 * lq);
+      uint2 *d1 = reinterpret_cast<uint2 *>(vt + (16 + kr) * kVRow + 32 * lq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint2 a[2], bb[2];
+        __builtin_memcpy(a, &v0[c], 16);
+        __builtin_memcpy(bb, &v1[c], 16);
+        d0[2 * c] = a[0];
+        d0[2 * c + 1] = a[1];
+        d1[2 * c] = bb[0];
+        d1[2 * c + 1] = bb[1];
+      }
+    }
+
+    // ---- S^T = K Q^T for both blocks: lane holds keys 4lq..4lq+3 of head kr
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8_t ka[4], kb[4];
+      KvLoad<KV>::to_bf16(cur0.k, ka);
+      KvLoad<KV>::to_bf16(cur1.k, kb);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qop[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c], qop[c], s1, 0, 0, 0);
+      }
+    }
+    float sc[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t ka = k0 + 16 * t0 + 4 * lq + r;
+      const int32_t kb = k0 + 16 * t1 + 4 * lq + r;
+      sc[r] = (t0 < nblk && ka < k1) ? s0[r] * p.scale2 : -INFINITY;
+      sc[4 + r] = (t1 < nblk && kb < k1) ? s1[r] * p.scale2 : -INFINITY;
+    }
+    float mb = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sc[e]);
+    mb = wave_max_q(mb);
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float ps = 0.f;
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = exp2f(sc[e] - m_new);
+      ps += pv[e];
+    }
+    l_run = l_run * alpha + ps;
+    bf16x8_t pop;
+    {
+      uint32_t u4[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                        pack_bf16x2(pv[6], pv[7])};
+      __builtin_memcpy(&pop, u4, 16);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+
+    // V tile written by this wave only: wait for the LDS writes to land.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- O^T += V^T P^T: lane reads dim 16n + kr for keys {4lq..4lq+3} of each block
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const uint16_t *col = vt + 16 * n + kr;
+      uint16_t e8[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        e8[e] = col[(4 * lq + e) * kVRow];
+        e8[4 + e] = col[(16 + 4 * lq + e) * kVRow];
+      }
+      bf16x8_t vop;
+      __builtin_memcpy(&vop, e8, 16);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[n], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+
+    if (u + 1 < npair) {
+      cur0 = nxt0;
+      cur1 = nxt1;
+    }
+  }
+  l_run = wave_sum_q(l_run);
+
+  // ---- merge the NW wavefronts through LDS
+  __syncthreads();  // every wave is done with its V tile
+  float *red_acc = reinterpret_cast<float *>(lds);
+  if (kr < G) {
+    if (lq == 0) {
+      red_m[w * kMaxG + kr] = m_run;
+      red_l[w * kMaxG + kr] = l_run;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      float4 v = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+      *reinterpret_cast<float4 *>(red_acc + (w * G + kr) * kD + 16 * n + 4 * lq) = v;
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<NW, OUT_BF16>(p, red_m, red_l, red_acc, b, g, s);
+}
+
+// --------------------------------------------------------------------------
+// f32 VALU path (f32 q, f32 K/V): lane l owns dims 2l, 2l+1.
+// --------------------------------------------------------------------------
+template <int NW, bool OUT_BF16>
+__global__ void __launch_bounds__(NW * 64) decode_f32_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float red_acc[NW * kMaxG * kD];
+  __shared__ float red_m[NW * kMaxG];
+  __shared__ float red_l[NW * kMaxG];
+  const int32_t s = blockIdx.x;
+  const int32_t g = blockIdx.y;
+  const int32_t b = blockIdx.z;
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t G = p.group;
+
+  const KeySource ks = key_source(p, b);
+  int32_t k0, k1;
+  split_range(ks.n, s, p.num_splits, &k0, &k1);
+
+  float2 qv[kMaxG];
+  float m_run[kMaxG], l_run[kMaxG];
+  float2 acc[kMaxG];
+#pragma unroll
+  for (int hh = 0; hh < kMaxG; ++hh) {
+    qv[hh] = make_float2(0.f, 0.f);
+    if (hh < G)
+      qv[hh] = *reinterpret_cast<const float2 *>(static_cast<const float *>(p.q) +
+                                                 (static_cast<int64_t>(b) * p.q_heads + g * G + hh) * kD + 2 * lane);
+    m_run[hh] = kNegBig;
+    l_run[hh] = 0.f;
+    acc[hh] = make_float2(0.f, 0.f);
+  }
+  const float *K = static_cast<const float *>(p.k);
+  const float *V = static_cast<const float *>(p.v);
+  for (int32_t key = k0 + w; key < k1; key += NW) {
+    const int64_t slot = safe_slot(ks.src[key], p.rows);
+    const int64_t off = row_elem(slot, p.kv_heads, g, kD) + 2 * lane;
+    const float2 kx = *reinterpret_cast<const float2 *>(K + off);
+    const float2 vx = *reinterpret_cast<const float2 *>(V + off);
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh) {
+      if (hh >= G) break;
+      const float sc = wave_sum_all(fmaf(qv[hh].x, kx.x, qv[hh].y * kx.y)) * p.scale2;
+      const float m_new = fmaxf(m_run[hh], sc);
+      const float alpha = exp2f(m_run[hh] - m_new);
+      const float pj = exp2f(sc - m_new);
+      m_run[hh] = m_new;
+      l_run[hh] = l_run[hh] * alpha + pj;
+      acc[hh].x = fmaf(pj, vx.x, acc[hh].x * alpha);
+      acc[hh].y = fmaf(pj, vx.y, acc[hh].y * alpha);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < kMaxG; ++hh) {
+    if (hh >= G) break;
+    if (lane == 0) {
+      red_m[w * kMaxG + hh] = m_run[hh];
+      red_l[w * kMaxG + hh] = l_run[hh];
+    }
+    *reinterpret_cast<float2 *>(red_acc + (w * G + hh) * kD + 2 * lane) = acc[hh];
+  }
+  __syncthreads();
+  merge_waves_and_store<NW, OUT_BF16>(p, red_m, red_l, red_acc, b, g, s);
+}
+
+// --------------------------------------------------------------------------
+// Split merge: one workgroup of 128 threads (one per dim) per (request, q head).
+//   M = max(max_s m_s, sink), L = sum_s l_s 2^{m_s - M} + 2^{sink - M}
+//   o = v_scale * sum_s acc_s 2^{m_s - M} / L
+// --------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(kD) decode_merge_kernel(DecodeParams p) {
+  const int32_t h = blockIdx.x;
+  const int32_t b = blockIdx.y;
+  const int32_t d = threadIdx.x;
+  const int64_t base = (static_cast<int64_t>(b) * p.q_heads + h) * p.num_splits;
+  float M = kNegBig;
+  for (int32_t s = 0; s < p.num_splits; ++s) M = fmaxf(M, p.ws_m[base + s]);
+  float sig2 = -INFINITY;
+  if (p.sinks) {
+    sig2 = p.sinks[h] * kLog2e;
+    M = fmaxf(M, sig2);
+  }
+  float L = p.sinks ? exp2f(sig2 - M) : 0.f;
+  float o = 0.f;
+  for (int32_t s = 0; s < p.num_splits; ++s) {
+    const float a = exp2f(p.ws_m[base + s] - M);
+    L += p.ws_l[base + s] * a;
+    o += p.ws_acc[(base + s) * kD + d] * a;
+  }
+  o = L > 0.f ? o * (p.v_scale / L) : 0.f;
+  const int64_t off = (static_cast<int64_t>(b) * p.q_heads + h) * kD + d;
+  if (OUT_BF16)
+    static_cast<uint16_t *>(p.out)[off] = f32_to_bf16_rne(o);
+  else
+    static_cast<float *>(p.out)[off] = o;
+}
+
+template <typename KV, int NW>
+hipError_t launch_mfma(const DecodeParams &p, dim3 grid, bool out_bf16, hipStream_t stream) {
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, NW, true>), grid, dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, NW, false>), grid, dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+constexpr int kDecodeWaves = 4;
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (a.idx.batch == 0) return hipSuccess;
+  DecodeParams p{};
+  p.q = a.q;
+  p.k = a.layer.k;
+  p.v = a.layer.v;
+  p.rows = a.layer.rows;
+  p.kv_heads = a.layer.kv_heads;
+  p.q_heads = a.q_heads;
+  p.group = a.q_heads / a.layer.kv_heads;
+  const bool fp8 = a.layer.dtype == SWA_FP8_E4M3;
+  p.k_scale = fp8 ? a.layer.k_scale : 1.f;
+  p.v_scale = fp8 ? a.layer.v_scale : 1.f;
+  p.r2t = a.idx.req_to_token;
+  p.r2t_rows = a.idx.r2t_rows;
+  p.r2t_stride = a.idx.r2t_stride;
+  p.req_idx = a.idx.req_pool_idx;
+  p.seq_lens = a.idx.seq_lens;
+  p.table = a.table;
+  p.indptr = a.indptr;
+  p.capacity = a.capacity;
+  p.window = a.window;
+  p.sinks = a.sinks;
+  p.scale2 = a.sm_scale * p.k_scale * kLog2e;
+  p.out = a.out;
+  p.num_splits = a.num_splits;
+  if (a.num_splits > 1) {
+    const int64_t parts = static_cast<int64_t>(a.idx.batch) * a.q_heads * a.num_splits;
+    p.ws_m = a.ws;
+    p.ws_l = a.ws + parts;
+    p.ws_acc = a.ws + 2 * parts;
+  }
+  const bool out_bf16 = a.out_dtype == SWA_BF16;
+  const dim3 grid(static_cast<uint32_t>(a.num_splits), static_cast<uint32_t>(a.layer.kv_heads),
+                  static_cast<uint32_t>(a.idx.batch));
+  hipError_t e;
+  if (a.layer.dtype == SWA_F32) {
+    if (out_bf16)
+      hipLaunchKernelGGL((decode_f32_kernel<kDecodeWaves, true>), grid, dim3(kDecodeWaves * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_f32_kernel<kDecodeWaves, false>), grid, dim3(kDecodeWaves * 64), 0, stream, p);
+    e = hipGetLastError();
+  } else if (a.layer.dtype == SWA_BF16) {
+    e = launch_mfma<uint16_t, kDecodeWaves>(p, grid, out_bf16, stream);
+  } else {
+    e = launch_mfma<uint8_t, kDecodeWaves>(p, grid, out_bf16, stream);
+  }
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const dim3 mgrid(static_cast<uint32_t>(a.q_heads), static_cast<uint32_t>(a.idx.batch));
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_merge_kernel<true>), mgrid, dim3(kD), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<false>), mgrid, dim3(kD), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -1,0 +1,109 @@
+// Index translation kernels: flat full -> SWA loc translation and the fused
+// window gather (req_to_token -> full slot -> full_to_swa -> SWA slot).
+//
+// SWA note (zdszero.github.io/swa.html), sections 双池与映射表 and Attention
+// backend: the full index is the primary address; the SWA slot of a token is
+// full_to_swa[full], 0 meaning "no SWA slot" and a trailing -1 making -1
+// translate to -1; backends translate the window once per batch.  SGLang
+// memory-pool article (pinghaoyang.com.cn), section 一重映射: req_to_token
+// rows hold each position's full slot, row 0 is padding.
+#include "common.hpp"
+
+namespace swa {
+namespace {
+
+__device__ __forceinline__ int64_t map_full(const int64_t *__restrict__ map, int64_t map_len, int64_t full) {
+  if (full == -1) return map[map_len - 1];
+  if (full < 0 || full >= map_len - 1) return 0;
+  return map[full];
+}
+
+__global__ void __launch_bounds__(256) translate_loc_kernel(const int64_t *__restrict__ full_loc, int64_t n,
+                                                            const int64_t *__restrict__ map, int64_t map_len,
+                                                            int64_t *__restrict__ out) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (; i < n; i += step) out[i] = map_full(map, map_len, full_loc[i]);
+}
+
+// Number of window entries of request b: positions lo .. L-1.
+__device__ __forceinline__ int32_t window_count(const int32_t *__restrict__ seq_lens,
+                                                const int32_t *__restrict__ prefix_lens, int32_t window,
+                                                int64_t stride, int32_t b, int32_t *lo_out) {
+  int32_t L = seq_lens[b];
+  if (L < 0) L = 0;
+  if (L > stride) L = static_cast<int32_t>(stride);
+  int32_t p = prefix_lens ? prefix_lens[b] : L - 1;
+  if (p > L) p = L;
+  int32_t lo = window < 0 ? 0 : p - window;
+  if (lo < 0) lo = 0;
+  if (lo_out) *lo_out = lo;
+  int32_t c = L - lo;
+  return c > 0 ? c : 0;
+}
+
+// One workgroup per request.  The workgroup first sums the counts of the
+// requests before it (an exclusive prefix sum done redundantly per request,
+// which avoids a separate scan launch and any host read of device lengths),
+// then gathers and translates its window with coalesced int32 reads.
+__global__ void __launch_bounds__(256) translate_window_kernel(
+    const int32_t *__restrict__ r2t, int64_t r2t_rows, int64_t r2t_stride, const int32_t *__restrict__ req_idx,
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ prefix_lens,
+    const int64_t *__restrict__ map, int64_t map_len, int32_t batch, int32_t window, int32_t *__restrict__ table,
+    int32_t *__restrict__ indptr, int64_t capacity) {
+  __shared__ int64_t partial[256];
+  const int32_t b = blockIdx.x;
+  if (batch == 0) {  // empty batch: the prefix sum is the single 0
+    if (threadIdx.x == 0) indptr[0] = 0;
+    return;
+  }
+  int64_t acc = 0;
+  for (int32_t t = threadIdx.x; t < b; t += blockDim.x)
+    acc += window_count(seq_lens, prefix_lens, window, r2t_stride, t, nullptr);
+  partial[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) partial[threadIdx.x] += partial[threadIdx.x + s];
+    __syncthreads();
+  }
+  const int64_t base = partial[0];
+  int32_t lo = 0;
+  const int32_t count = window_count(seq_lens, prefix_lens, window, r2t_stride, b, &lo);
+  if (threadIdx.x == 0) {
+    indptr[b] = static_cast<int32_t>(base);
+    if (b == batch - 1) indptr[batch] = static_cast<int32_t>(base + count);
+  }
+  int64_t row = req_idx[b];
+  if (row < 0 || row >= r2t_rows) row = 0;
+  const int32_t *__restrict__ src = r2t + row * r2t_stride + lo;
+  for (int32_t k = threadIdx.x; k < count; k += blockDim.x) {
+    const int64_t dst = base + k;
+    if (dst >= capacity) break;
+    int64_t full = src[k];
+    int64_t slot = map ? map_full(map, map_len, full) : full;
+    table[dst] = static_cast<int32_t>(slot);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_translate_loc(const int64_t *full_loc, int64_t n, const int64_t *map, int64_t map_len,
+                                int64_t *out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(translate_loc_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, full_loc, n,
+                     map, map_len, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_translate_window(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
+                                   int32_t *table, int32_t *indptr, int64_t capacity, hipStream_t stream) {
+  const uint32_t grid = idx.batch > 0 ? static_cast<uint32_t>(idx.batch) : 1u;
+  hipLaunchKernelGGL(translate_window_kernel, dim3(grid), dim3(256), 0, stream,
+                     idx.req_to_token, idx.r2t_rows, idx.r2t_stride, idx.req_pool_idx, idx.seq_lens, prefix_lens,
+                     idx.full_to_swa, idx.map_len, idx.batch, window, table, indptr, capacity);
+  return hipGetLastError();
+}
+
+}  // namespace swa

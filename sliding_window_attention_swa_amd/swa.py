@@ -1,0 +1,235 @@
+"""Thin Python binding of libswa (ctypes).  Argument marshalling only: every
+step of the path runs in the library's HIP kernels.  PyTorch supplies device
+memory and streams.
+
+The function names are the C names (include/swa.h).  Tensors must be
+contiguous CUDA (HIP) tensors of the documented dtypes; the binding checks
+device, dtype and contiguity, converts them to pointers and raises SwaError on
+a non-zero status.  There is no fallback: if libswa.so is missing the import
+of this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+
+SWA_OK, SWA_E_ARG, SWA_E_DTYPE, SWA_E_SHAPE, SWA_E_NOSPACE, SWA_E_WORKSPACE, SWA_E_HIP = 0, -1, -2, -3, -4, -5, -6
+SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
+
+# every symbol include/swa.h declares
+EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
+           "swa_decode", "swa_extend", "swa_status_string")
+
+
+class SwaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m sliding_window_attention_swa_amd.build`")
+    return ctypes.CDLL(_LIB_PATH)
+
+
+lib = _load()
+
+
+class KvLayerStruct(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
+class IndexStruct(ctypes.Structure):
+    _fields_ = [("req_to_token", ctypes.c_void_p), ("r2t_rows", ctypes.c_int64), ("r2t_stride", ctypes.c_int64),
+                ("req_pool_idx", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("full_to_swa", ctypes.c_void_p),
+                ("map_len", ctypes.c_int64), ("batch", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+_i32, _i64, _f32, _f64, _p, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p,
+                                   ctypes.c_size_t)
+_sig = {
+    "swa_pool_config": (_i32, [_i64, _f64, _i32, _i32, _i32, _i64, _i32, _i64, ctypes.POINTER(_i64),
+                               ctypes.POINTER(_i64)]),
+    "swa_translate_loc": (_i32, [_p, _i64, _p, _i64, _p, _p]),
+    "swa_translate_window": (_i32, [ctypes.POINTER(IndexStruct), _i32, _p, _p, _p, _i64, _p]),
+    "swa_kv_store": (_i32, [ctypes.POINTER(KvLayerStruct), _p, _i64, _p, _p, _i32, _p]),
+    "swa_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_sz)]),
+    "swa_decode": (_i32, [_p, _i32, _i32, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct), _p, _p, _i64,
+                          _i32, _p, _f32, _p, _i32, _i32, _p, _sz, _p]),
+    "swa_extend": (_i32, [_p, _i32, _i32, _p, _p, _i64, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct),
+                          _p, _p, _i64, _i32, _p, _f32, _p, _i32, _p]),
+    "swa_status_string": (ctypes.c_char_p, [_i32]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def status_string(status: int) -> str:
+    return lib.swa_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != SWA_OK:
+        raise SwaError(status, what)
+
+
+_TORCH_DTYPE = {SWA_F32: torch.float32, SWA_BF16: torch.bfloat16, SWA_FP8_E4M3: torch.uint8}
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SWA_F32
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return SWA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclass
+class KvLayer:
+    """One layer's K and V views of a pool: (rows, kv_heads, head_dim) tensors."""
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    def struct(self) -> KvLayerStruct:
+        if self.k.shape != self.v.shape or self.k.dim() != 3 or self.k.dtype != self.v.dtype:
+            raise ValueError("k and v must be (rows, kv_heads, head_dim) tensors of one dtype")
+        return KvLayerStruct(_ptr(self.k, name="k"), _ptr(self.v, name="v"), self.k.shape[0], self.k.shape[1],
+                             self.k.shape[2], dtype_code(self.k), self.k_scale, self.v_scale)
+
+
+@dataclass
+class IndexTables:
+    """The batch's req_to_token / req_pool_idx / seq_lens / full_to_swa tensors."""
+    req_to_token: torch.Tensor
+    req_pool_idx: torch.Tensor
+    seq_lens: torch.Tensor
+    full_to_swa: Optional[torch.Tensor] = None
+    page_size: int = 1
+
+    def struct(self, with_map: bool = True) -> IndexStruct:
+        m = self.full_to_swa if with_map else None
+        return IndexStruct(_ptr(self.req_to_token, torch.int32, "req_to_token"), self.req_to_token.shape[0],
+                           self.req_to_token.shape[1], _ptr(self.req_pool_idx, torch.int32, "req_pool_idx"),
+                           _ptr(self.seq_lens, torch.int32, "seq_lens"), _ptr(m, torch.int64, "full_to_swa"),
+                           0 if m is None else m.numel(), self.seq_lens.numel(), self.page_size)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+
+def swa_pool_config(avail_bytes: int, ratio: float, page_size: int, window: int, n_full_layers: int,
+                    full_bytes_per_token: int, n_swa_layers: int, swa_bytes_per_token: int):
+    """Returns (status, n_full_tokens, n_swa_tokens); raises on argument errors
+    (SWA_E_NOSPACE is returned, not raised, so callers can report the sizes)."""
+    nf, ns = _i64(), _i64()
+    st = lib.swa_pool_config(avail_bytes, ratio, page_size, window, n_full_layers, full_bytes_per_token, n_swa_layers,
+                             swa_bytes_per_token, ctypes.byref(nf), ctypes.byref(ns))
+    if st not in (SWA_OK, SWA_E_NOSPACE):
+        _check(st, "swa_pool_config")
+    return st, nf.value, ns.value
+
+
+def swa_translate_loc(full_loc: torch.Tensor, full_to_swa: torch.Tensor, swa_loc: torch.Tensor, stream=None):
+    if full_loc.numel() != swa_loc.numel():
+        raise ValueError("full_loc and swa_loc must have the same length")
+    _check(lib.swa_translate_loc(_ptr(full_loc, torch.int64, "full_loc"), full_loc.numel(),
+                                 _ptr(full_to_swa, torch.int64, "full_to_swa"), full_to_swa.numel(),
+                                 _ptr(swa_loc, torch.int64, "swa_loc"), _stream(stream)), "swa_translate_loc")
+
+
+def swa_translate_window(index: IndexTables, window: int, slot_table: torch.Tensor, table_indptr: torch.Tensor,
+                         prefix_lens: Optional[torch.Tensor] = None, use_map: bool = True, stream=None):
+    if table_indptr.numel() < index.seq_lens.numel() + 1:
+        raise ValueError("table_indptr needs batch + 1 entries")
+    s = index.struct(with_map=use_map)
+    _check(lib.swa_translate_window(ctypes.byref(s), window, _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                                    _ptr(slot_table, torch.int32, "slot_table"),
+                                    _ptr(table_indptr, torch.int32, "table_indptr"), slot_table.numel(),
+                                    _stream(stream)), "swa_translate_window")
+
+
+def swa_kv_store(layer: KvLayer, loc: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+    if k_new.shape != v_new.shape or k_new.shape[0] != loc.numel():
+        raise ValueError("k_new / v_new must be (n, kv_heads, head_dim) with n = len(loc)")
+    if k_new.numel() and tuple(k_new.shape[1:]) != tuple(layer.k.shape[1:]):
+        raise ValueError("new rows must match the pool's (kv_heads, head_dim)")
+    s = layer.struct()
+    _check(lib.swa_kv_store(ctypes.byref(s), _ptr(loc, torch.int64, "loc"), loc.numel(), _ptr(k_new, name="k_new"),
+                            _ptr(v_new, name="v_new"), dtype_code(k_new), _stream(stream)), "swa_kv_store")
+
+
+def swa_decode_plan(batch: int, q_heads: int, kv_heads: int, head_dim: int, window: int, max_seq_len: int):
+    ns, ws = _i32(), _sz()
+    _check(lib.swa_decode_plan(batch, q_heads, kv_heads, head_dim, window, max_seq_len, ctypes.byref(ns),
+                               ctypes.byref(ws)), "swa_decode_plan")
+    return ns.value, ws.value
+
+
+def swa_decode(q: torch.Tensor, layer: KvLayer, index: IndexTables, window: int, out: torch.Tensor,
+               sinks: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+               slot_table: Optional[torch.Tensor] = None, table_indptr: Optional[torch.Tensor] = None,
+               num_splits: int = 1, workspace: Optional[torch.Tensor] = None, use_map: bool = True, stream=None):
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be (batch, q_heads, head_dim)")
+    scale = sm_scale if sm_scale is not None else q.shape[2] ** -0.5
+    ls, ix = layer.struct(), index.struct(with_map=use_map)
+    _check(lib.swa_decode(_ptr(q, name="q"), dtype_code(q), q.shape[1], ctypes.byref(ls), ctypes.byref(ix),
+                          _ptr(slot_table, torch.int32, "slot_table"), _ptr(table_indptr, torch.int32, "table_indptr"),
+                          0 if slot_table is None else slot_table.numel(), window,
+                          _ptr(sinks, torch.float32, "sinks"), scale, _ptr(out, name="out"), dtype_code(out),
+                          num_splits, _ptr(workspace, name="workspace"),
+                          0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)),
+           "swa_decode")
+
+
+def swa_extend(q: torch.Tensor, qo_indptr: torch.Tensor, prefix_lens: torch.Tensor, layer: KvLayer,
+               index: IndexTables, window: int, out: torch.Tensor, sinks: Optional[torch.Tensor] = None,
+               sm_scale: Optional[float] = None, slot_table: Optional[torch.Tensor] = None,
+               table_indptr: Optional[torch.Tensor] = None, use_map: bool = True, stream=None):
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be (total_q, q_heads, head_dim)")
+    scale = sm_scale if sm_scale is not None else q.shape[2] ** -0.5
+    ls, ix = layer.struct(), index.struct(with_map=use_map)
+    _check(lib.swa_extend(_ptr(q, name="q"), dtype_code(q), q.shape[1], _ptr(qo_indptr, torch.int32, "qo_indptr"),
+                          _ptr(prefix_lens, torch.int32, "prefix_lens"), q.shape[0], ctypes.byref(ls),
+                          ctypes.byref(ix), _ptr(slot_table, torch.int32, "slot_table"),
+                          _ptr(table_indptr, torch.int32, "table_indptr"),
+                          0 if slot_table is None else slot_table.numel(), window,
+                          _ptr(sinks, torch.float32, "sinks"), scale, _ptr(out, name="out"), dtype_code(out),
+                          _stream(stream)), "swa_extend")

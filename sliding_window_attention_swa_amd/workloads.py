@@ -1,0 +1,386 @@
+"""Seeded synthetic inputs for the five workloads (and scaled-down variants).
+
+This module only draws random numbers and lays out index structures: page
+permutations, req_to_token rows, full_to_swa entries, pool contents.  It holds
+none of the attention / translation / store arithmetic, and it serves both the
+HIP path (tests, benchmark) and the CPU oracle.
+
+Recipe (shared by every workload):
+  * independent streams from numpy.random.SeedSequence(seed).spawn(8), used in
+    this order: lengths, full pages, SWA pages, Q, K, V, sinks, new K/V;
+  * values are float32 N(0, 1) draws rounded to the storage dtype by torch's
+    dtype casts (bf16 round-to-nearest-even; e4m3fn: nearest, ties to even);
+  * request b lives in req_to_token row b + 1 (row 0 is padding); its
+    positions fill pages taken in order from a seeded permutation of the full
+    pool's pages 1..N_full/P (page 0 is padding); SWA pages come the same way
+    from a permutation of 1..N_swa/P, only for pages that are still live;
+  * a position j on full page f (offset k) maps to SWA slot s * P + k when its
+    page is live on SWA page s, else to 0 (tombstone);
+  * every pool row that no position references, and page 0, holds NaN (e4m3:
+    the NaN code 0x7F), so any stray read shows up in the output.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F)}
+NP_STORE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}
+
+
+def to_store(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 draws -> storage bits of dtype via torch's casts."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "f32":
+        return t.numpy().copy()
+    if dtype == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if dtype == "e4m3":
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    raise ValueError(dtype)
+
+
+class SparsePool:
+    """A pool of shape (rows, heads, dim) given by its referenced rows; every
+    other row reads as NaN.  Indexing with an integer array returns those rows.
+    Used where a dense host copy of a large pool would be wasteful."""
+
+    def __init__(self, rows: int, heads: int, dim: int, dtype: str, used_rows: np.ndarray, values: np.ndarray):
+        self.shape = (rows, heads, dim)
+        self.dtype = dtype
+        order = np.argsort(used_rows, kind="stable")
+        self.used_rows = np.asarray(used_rows, dtype=np.int64)[order]
+        self.values = values[order]
+
+        self.overlay = {}  # rows written after construction (slot -> row values)
+
+    def __getitem__(self, slots):
+        scalar = np.ndim(slots) == 0
+        slots = np.atleast_1d(np.asarray(slots, dtype=np.int64))
+        out = np.full(slots.shape + self.shape[1:], NAN_BITS[self.dtype], dtype=NP_STORE[self.dtype])
+        if len(self.used_rows):
+            pos = np.searchsorted(self.used_rows, slots)
+            pos_c = np.minimum(pos, len(self.used_rows) - 1)
+            hit = (pos < len(self.used_rows)) & (self.used_rows[pos_c] == slots)
+            out[hit] = self.values[pos_c[hit]]
+        for n, sl in enumerate(slots.tolist()):
+            if sl in self.overlay:
+                out[n] = self.overlay[sl]
+        return out[0] if scalar else out
+
+    def __setitem__(self, slot, row):
+        self.overlay[int(slot)] = np.asarray(row, dtype=NP_STORE[self.dtype]).reshape(self.shape[1:])
+
+    def copy(self) -> "SparsePool":
+        c = SparsePool.__new__(SparsePool)
+        c.shape, c.dtype, c.used_rows, c.values = self.shape, self.dtype, self.used_rows, self.values
+        c.overlay = dict(self.overlay)
+        return c
+
+    def written_rows(self) -> np.ndarray:
+        """Every row that holds a value (initial rows and overlay), sorted."""
+        return np.union1d(self.used_rows, np.fromiter(self.overlay.keys(), dtype=np.int64))
+
+    def dense(self) -> np.ndarray:
+        out = np.full(self.shape, NAN_BITS[self.dtype], dtype=NP_STORE[self.dtype])
+        out[self.used_rows] = self.values
+        for sl, row in self.overlay.items():
+            out[sl] = row
+        return out
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    window: int
+    page_size: int
+    q_dtype: str
+    kv_dtype: str
+    seq_lens: np.ndarray                 # int32 (B,)
+    req_to_token: np.ndarray             # int32 (B + 1, stride)
+    req_pool_idx: np.ndarray             # int32 (B,)
+    full_to_swa: Optional[np.ndarray]    # int64 (N_full + P + 1,) or None (single pool / full layer)
+    n_full: int
+    n_swa: int
+    pool_k: SparsePool
+    pool_v: SparsePool
+    q: np.ndarray                        # storage bits (total_q, Hq, D)
+    sinks: Optional[np.ndarray]          # float32 (Hq,) or None
+    prefix_lens: Optional[np.ndarray] = None   # extend: int32 (B,)
+    qo_indptr: Optional[np.ndarray] = None     # extend: int32 (B + 1,)
+    new_full_loc: Optional[np.ndarray] = None  # store: int64 full locs of the new tokens
+    new_k: Optional[np.ndarray] = None         # store: (n, Hkv, D) bits of new_dtype
+    new_v: Optional[np.ndarray] = None
+    new_dtype: str = "bf16"
+    ratio: float = 0.8
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def pool_rows(self) -> int:
+        return self.pool_k.shape[0]
+
+
+def _streams(seed: int):
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(8)]
+
+
+def _layout(seq_lens, P, n_full, n_swa, live_from_pos, rng_full, rng_swa, stride=None):
+    """req_to_token rows and the page-consistent full_to_swa table.
+
+    live_from_pos[b]: positions >= this value (rounded down to its page) keep
+    an SWA page; earlier pages are tombstoned."""
+    B = len(seq_lens)
+    stride = stride or int(max(seq_lens))
+    full_pages = rng_full.permutation(np.arange(1, n_full // P + 1, dtype=np.int64))
+    swa_pages = rng_swa.permutation(np.arange(1, n_swa // P + 1, dtype=np.int64)) if n_swa else None
+    r2t = np.zeros((B + 1, stride), dtype=np.int32)
+    mapping = np.zeros(n_full + P + 1, dtype=np.int64)
+    mapping[-1] = -1
+    fi = si = 0
+    swa_rows = []  # (b, position) -> swa slot for referenced positions
+    for b, T in enumerate(seq_lens):
+        T = int(T)
+        npg = -(-T // P)
+        fp = full_pages[fi:fi + npg]
+        fi += npg
+        if fi > len(full_pages):
+            raise ValueError("full pool too small for the requests")
+        pos = np.arange(T)
+        full = fp[pos // P] * P + pos % P
+        r2t[b + 1, :T] = full
+        if swa_pages is not None:
+            first_live = max(0, int(live_from_pos[b])) // P
+            live = np.arange(first_live, npg)
+            sp = swa_pages[si:si + len(live)]
+            si += len(live)
+            if si > len(swa_pages):
+                raise ValueError("SWA pool too small for the live windows")
+            page_to_swa = np.zeros(npg, dtype=np.int64)
+            page_to_swa[live] = sp
+            mapped = page_to_swa[pos // P]
+            slots = np.where(mapped > 0, mapped * P + pos % P, 0)
+            mapping[full] = slots
+            swa_rows.append(slots)
+        else:
+            swa_rows.append(full)
+    return r2t, mapping, swa_rows
+
+
+def _fill_pool(rows, H, D, dtype, slot_lists, rng_k, rng_v):
+    """Pool rows referenced by any position get N(0,1) values (drawn in
+    request / position order); returns two SparsePools."""
+    used = np.concatenate([s[s > 0] for s in slot_lists]) if slot_lists else np.zeros(0, np.int64)
+    if np.unique(used).size != used.size:
+        raise ValueError("two positions share a pool row")
+    kv = to_store(rng_k.standard_normal((used.size, H, D), dtype=np.float32), dtype)
+    vv = to_store(rng_v.standard_normal((used.size, H, D), dtype=np.float32), dtype)
+    return SparsePool(rows, H, D, dtype, used, kv), SparsePool(rows, H, D, dtype, used, vv)
+
+
+def round_up(x: int, m: int) -> int:
+    return -(-x // m) * m
+
+
+def decode_workload(name, seed, seq_lens, q_heads, kv_heads, window, page_size, q_dtype, kv_dtype, sinks=True,
+                    ratio=0.8, live_margin=0, with_store=False, head_dim=128, slack_pages=2, swa_tokens=None):
+    """A batch of decode requests against one SWA layer (window >= 0) of a two-pool
+    cache, or against a single full pool (window < 0: positions read from
+    req_to_token directly, no SWA pool)."""
+    r_len, r_full, r_swa, r_q, r_k, r_v, r_s, r_new = _streams(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    B, P = len(seq_lens), page_size
+    n_full = round_up(int(sum(round_up(int(t), P) for t in seq_lens)) + slack_pages * P, P)
+    use_swa = window >= 0
+    if use_swa:
+        live_from = np.maximum(seq_lens - 1 - window - live_margin, 0)
+        need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(seq_lens, live_from)))
+        n_swa = swa_tokens or max(round_up(int(math.floor(ratio * n_full)), P), round_up(need + slack_pages * P, P))
+        n_swa = n_swa // P * P
+    else:
+        live_from = np.zeros(B, np.int64)
+        n_swa = 0
+    r2t, mapping, slot_lists = _layout(seq_lens, P, n_full, n_swa, live_from, r_full, r_swa)
+    rows = (n_swa if use_swa else n_full) + P
+    pk, pv = _fill_pool(rows, kv_heads, head_dim, kv_dtype, slot_lists, r_k, r_v)
+    q = to_store(r_q.standard_normal((B, q_heads, head_dim), dtype=np.float32), q_dtype)
+    s = r_s.standard_normal(q_heads).astype(np.float32) if sinks else None
+    wl = Workload(name, B, q_heads, kv_heads, head_dim, window, P, q_dtype, kv_dtype, seq_lens.astype(np.int32), r2t,
+                  np.arange(1, B + 1, dtype=np.int32), mapping if use_swa else None, n_full, n_swa, pk, pv, q, s,
+                  ratio=ratio)
+    if with_store:
+        # the current token (position T-1) gets new K/V, stored before attention
+        wl.new_full_loc = r2t[np.arange(1, B + 1), seq_lens - 1].astype(np.int64)
+        wl.new_k = to_store(r_new.standard_normal((B, kv_heads, head_dim), dtype=np.float32), "bf16")
+        wl.new_v = to_store(r_new.standard_normal((B, kv_heads, head_dim), dtype=np.float32), "bf16")
+        wl.new_dtype = "bf16"
+    return wl
+
+
+def extend_workload(name, seed, prefix_lens, chunk_lens, q_heads, kv_heads, window, page_size, sinks=True,
+                    ratio=0.8, head_dim=128, slack_pages=2):
+    """Chunked prefill: each request has a cached prefix whose pages before
+    prefix - W are tombstoned on the SWA side, plus a chunk of new tokens whose
+    K/V are provided as new_k / new_v (to be stored at translate(new_full_loc))."""
+    r_len, r_full, r_swa, r_q, r_k, r_v, r_s, r_new = _streams(seed)
+    prefix = np.asarray(prefix_lens, dtype=np.int64)
+    chunk = np.asarray(chunk_lens, dtype=np.int64)
+    seq = prefix + chunk
+    B, P = len(seq), page_size
+    n_full = round_up(int(sum(round_up(int(t), P) for t in seq)) + slack_pages * P, P)
+    live_from = np.maximum(prefix - window, 0) if window >= 0 else np.zeros(B, np.int64)
+    need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(seq, live_from)))
+    n_swa = max(round_up(int(math.floor(ratio * n_full)), P), round_up(need + slack_pages * P, P))
+    r2t, mapping, slot_lists = _layout(seq, P, n_full, n_swa, live_from, r_full, r_swa)
+    rows = n_swa + P
+    # pool holds the live prefix window only; chunk rows start as NaN and are stored
+    prefix_slots = [s[:int(p)] for s, p in zip(slot_lists, prefix)]
+    pk, pv = _fill_pool(rows, kv_heads, head_dim, "bf16", prefix_slots, r_k, r_v)
+    total = int(chunk.sum())
+    q = to_store(r_q.standard_normal((total, q_heads, head_dim), dtype=np.float32), "bf16")
+    s = r_s.standard_normal(q_heads).astype(np.float32) if sinks else None
+    qo = np.zeros(B + 1, dtype=np.int32)
+    qo[1:] = np.cumsum(chunk)
+    new_loc = np.concatenate([r2t[b + 1, int(prefix[b]):int(seq[b])] for b in range(B)]).astype(np.int64)
+    wl = Workload(name, B, q_heads, kv_heads, head_dim, window, P, "bf16", "bf16", seq.astype(np.int32), r2t,
+                  np.arange(1, B + 1, dtype=np.int32), mapping, n_full, n_swa, pk, pv, q, s,
+                  prefix_lens=prefix.astype(np.int32), qo_indptr=qo, ratio=ratio)
+    wl.new_full_loc = new_loc
+    wl.new_k = to_store(r_new.standard_normal((total, kv_heads, head_dim), dtype=np.float32), "bf16")
+    wl.new_v = to_store(r_new.standard_normal((total, kv_heads, head_dim), dtype=np.float32), "bf16")
+    return wl
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at their stated sizes
+# ---------------------------------------------------------------------------
+
+SEED_BASE = 20261202
+
+
+def c1_decode_f32(seed=SEED_BASE + 1) -> Workload:
+    """Single SWA layer decode: 1 request, T = 512, W = 128, 8 q / 8 kv heads,
+    D = 128, f32, P = 1; positions < T - W - 128 evicted (mapping 0)."""
+    T, W = 512, 128
+    # live_from = i - W - margin = T - W - 128 with i = T - 1
+    return decode_workload("c1_decode_f32_T512", seed, [T], 8, 8, W, 1, "f32", "f32", ratio=0.5, live_margin=127,
+                           slack_pages=512, swa_tokens=512)
+
+
+def c2_decode_bf16(seed=SEED_BASE + 2, batch=64, q_heads=64, kv_heads=8) -> Workload:
+    """Batched SWA decode: B = 64, T ~ U[1024, 8192], W = 128, 64 q / 8 kv heads,
+    D = 128, bf16, P = 16, out-of-window pages tombstoned, ratio 0.8."""
+    lens = np.random.default_rng(np.random.SeedSequence(seed).spawn(8)[0]).integers(1024, 8193, size=batch)
+    return decode_workload("c2_decode_bf16_B64", seed, lens, q_heads, kv_heads, 128, 16, "bf16", "bf16", ratio=0.8,
+                           with_store=True)
+
+
+def c3_extend_bf16(seed=SEED_BASE + 3, batch=4, prefix=8192, chunk=2048) -> Workload:
+    """Chunked-prefill extend: B = 4, prefix 8K + chunk 2K, W = 128, 64 q / 8 kv
+    heads, D = 128, bf16, P = 64; the chunk's K/V are stored first."""
+    return extend_workload("c3_extend_bf16_B4_8K+2K", seed, [prefix] * batch, [chunk] * batch, 64, 8, 128, 64)
+
+
+def c5_lengths(seed, batch):
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(8)[0])
+    return np.clip(np.round(np.exp(rng.normal(math.log(16384), 1.0, size=batch))), 512, 65536).astype(np.int64)
+
+
+def c5_decode_fp8(seed=SEED_BASE + 5, batch=256, ratio=0.02) -> Workload:
+    """fp8 KV decode: B = 256, lognormal lengths (median 16K, sigma 1, clipped to
+    [512, 64K]), W = 128, 64 q / 8 kv heads, D = 128, e4m3 K/V (scale 1), bf16 q,
+    P = 64, plus a store of one new token per request.  SWA ratio 0.02: every
+    live window fits, and a 0.8 pool (~11 GB per layer) would only add NaN rows."""
+    lens = c5_lengths(seed, batch)
+    return decode_workload("c5_decode_fp8_B256", seed, lens, 64, 8, 128, 64, "bf16", "e4m3", ratio=ratio,
+                           with_store=True)
+
+
+# ---------------------------------------------------------------------------
+# Long-context mixed-layer decode step (48 layers) — index structures on the
+# host, per-layer K/V drawn on the device from per-layer seeds.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class MixedStep:
+    batch: int
+    seq_len: int
+    q_heads: int
+    head_dim: int
+    page_size: int
+    layers: List[dict]            # {"id", "kind": "full"|"swa", "window", "kv_heads", "seed"}
+    req_to_token: np.ndarray
+    req_pool_idx: np.ndarray
+    seq_lens: np.ndarray
+    full_to_swa: np.ndarray
+    n_full: int
+    n_swa: int
+    swa_slots: np.ndarray         # SWA slots referenced by live windows (to receive values)
+    seed: int
+    ratio: float
+    cell_bytes: float = 0.0
+
+
+def c4_mixed_step(seed=SEED_BASE + 4, batch=32, seq_len=32768, n_layers=48, full_every=5, n_full_layers=9,
+                  ratio=0.1) -> MixedStep:
+    """B = 32, T = 32K; 48 layers: 9 full (W = -1, 4 kv heads) at ids 0, 5, ..,
+    40 and 39 SWA (W = 128, 8 kv heads); 64 q heads, D = 128, bf16, P = 64; SWA
+    pool at ratio 0.1 of the full pool (cell formula); SWA pages live for the
+    window plus one eviction interval (128 tokens); no sink."""
+    P, W, D = 64, 128, 128
+    r_len, r_full, r_swa, *_ = _streams(seed)
+    lens = np.full(batch, seq_len, dtype=np.int64)
+    n_full = batch * seq_len
+    F, S = 4 * (D + D) * 2, 8 * (D + D) * 2
+    n_swa = int(math.floor(ratio * n_full)) // P * P
+    live_from = lens - 1 - W - 128
+    r2t, mapping, slot_lists = _layout(lens, P, n_full, n_swa, live_from, r_full, r_swa)
+    full_ids = [full_every * i for i in range(n_full_layers)]
+    layers = []
+    children = np.random.SeedSequence(seed).spawn(8 + n_layers)[8:]
+    for lid in range(n_layers):
+        kind = "full" if lid in full_ids else "swa"
+        layers.append({"id": lid, "kind": kind, "window": -1 if kind == "full" else W,
+                       "kv_heads": 4 if kind == "full" else 8,
+                       "seed": int(children[lid].generate_state(1)[0])})
+    swa_slots = np.concatenate([s[s > 0] for s in slot_lists])
+    return MixedStep(batch, seq_len, 64, D, P, layers, r2t, np.arange(1, batch + 1, dtype=np.int32),
+                     lens.astype(np.int32), mapping, n_full, n_swa, swa_slots, seed, ratio,
+                     F * n_full_layers + ratio * S * (n_layers - n_full_layers))
+
+
+def c4_layer_tensors(step: MixedStep, layer: dict, device="cuda"):
+    """Per-layer device tensors of the mixed step, drawn from the layer's seed
+    with torch's generator on `device`: Q (B, Hq, D) bf16 and the layer's K/V
+    pool (rows, Hkv, D) bf16.  Full layers reference every full-pool row; SWA
+    layers hold values at the live window slots and NaN elsewhere."""
+    g = torch.Generator(device=device)
+    g.manual_seed(layer["seed"])
+    H, D = layer["kv_heads"], step.head_dim
+    q = torch.randn((step.batch, step.q_heads, D), generator=g, device=device).to(torch.bfloat16)
+    if layer["kind"] == "full":
+        rows = step.n_full + step.page_size
+        k = torch.empty((rows, H, D), dtype=torch.bfloat16, device=device)
+        v = torch.empty((rows, H, D), dtype=torch.bfloat16, device=device)
+        for t, name in ((k, "k"), (v, "v")):
+            chunk = 1 << 18
+            for r0 in range(0, rows, chunk):
+                r1 = min(rows, r0 + chunk)
+                t[r0:r1] = torch.randn((r1 - r0, H, D), generator=g, device=device).to(torch.bfloat16)
+            t[:step.page_size] = float("nan")  # page 0 is the padding sink
+        return q, k, v
+    rows = step.n_swa + step.page_size
+    k = torch.full((rows, H, D), float("nan"), dtype=torch.bfloat16, device=device)
+    v = torch.full((rows, H, D), float("nan"), dtype=torch.bfloat16, device=device)
+    idx = torch.from_numpy(step.swa_slots).to(device)
+    k[idx] = torch.randn((idx.numel(), H, D), generator=g, device=device).to(torch.bfloat16)
+    v[idx] = torch.randn((idx.numel(), H, D), generator=g, device=device).to(torch.bfloat16)
+    return q, k, v

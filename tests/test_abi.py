@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+
+@pytest.fixture(scope="module")
+def swa():
+    from sliding_window_attention_swa_amd import swa as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(swa):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(swa.lib, n), f"{n} declared in swa.h but not exported"
+    assert set(names) == set(swa.EXPORTS)
+
+
+def test_status_strings(swa):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert swa.status_string(code) not in ("", "unknown status")
+    assert swa.status_string(-99) == "unknown status"
+
+
+def test_pool_config_matches_cell_formula(swa):
+    from oracle import swa_oracle as O
+    for avail, ratio, P, W, Lf, F, Ls, S in [(36_077_256_295, 0.1, 64, 128, 9, 2048, 39, 4096),
+                                             (10 ** 11, 0.8, 16, 128, 9, 1000, 39, 2000),
+                                             (10 ** 10, 0.05, 1, 128, 9, 1000, 39, 2000),
+                                             (5 * 10 ** 9, 0.3, 64, 4095, 0, 0, 10, 4096)]:
+        st, nf, ns = swa.swa_pool_config(avail, ratio, P, W, Lf, F, Ls, S)
+        _, onf, ons = O.pool_config(avail, ratio, P, W, Lf, F, Ls, S)
+        assert st == 0 and (nf, ns) == (onf, ons)
+    st, nf, ns = swa.swa_pool_config(192 * 4096 * 10, 0.01, 64, 128, 0, 0, 10, 4096)
+    assert st == swa.SWA_E_NOSPACE
+    with pytest.raises(swa.SwaError):
+        swa.swa_pool_config(10 ** 9, 0.5, 0, 128, 9, 1000, 39, 2000)  # page_size 0
+    with pytest.raises(swa.SwaError):
+        swa.swa_pool_config(10 ** 9, -0.5, 64, 128, 9, 1000, 39, 2000)
+
+
+def test_decode_plan(swa):
+    ns, ws = swa.swa_decode_plan(64, 64, 8, 128, 128, 8192)
+    assert ns == 1 and ws == 0  # SWA layers: one split, no workspace
+    ns, ws = swa.swa_decode_plan(32, 64, 4, 128, -1, 32768)
+    assert ns > 1 and ws == 32 * 64 * ns * (2 + 128) * 4
+    ns, _ = swa.swa_decode_plan(1, 8, 8, 128, -1, 100)
+    assert ns == 1
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_decode_plan(4, 64, 8, 64, 128, 100)
+    assert e.value.status == swa.SWA_E_SHAPE
+    with pytest.raises(swa.SwaError) as e:
+        swa.swa_decode_plan(4, 24, 8, 128, 128, 100)  # group 3
+    assert e.value.status == swa.SWA_E_SHAPE
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def layer(swa, dtype=1, head_dim=128, kv_heads=8, rows=1024, k=FAKE, v=FAKE, scale=1.0):
+    return swa.KvLayerStruct(k, v, rows, kv_heads, head_dim, dtype, scale, scale)
+
+
+def index(swa, batch=2, map_ptr=FAKE):
+    return swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, map_ptr, 50 if map_ptr else 0, batch, 16)
+
+
+def decode(swa, ly, ix, q_dtype=1, q_heads=64, out_dtype=0, splits=1, ws=None, ws_bytes=0, window=128,
+           table=FAKE, indptr=FAKE, q=FAKE, out=FAKE):
+    return swa.lib.swa_decode(q, q_dtype, q_heads, ctypes.byref(ly), ctypes.byref(ix), table, indptr, 1000, window,
+                              None, 0.088, out, out_dtype, splits, ws, ws_bytes, None)
+
+
+def test_decode_argument_errors(swa):
+    E = swa
+    ly, ix = layer(swa), index(swa)
+    assert decode(swa, layer(swa, head_dim=64), ix) == E.SWA_E_SHAPE
+    assert decode(swa, ly, ix, q_heads=24) == E.SWA_E_SHAPE
+    assert decode(swa, ly, ix, q_heads=64 * 4) == E.SWA_E_SHAPE  # group 32
+    assert decode(swa, ly, ix, q_dtype=0) == E.SWA_E_DTYPE        # f32 q with bf16 K/V
+    assert decode(swa, layer(swa, dtype=0), ix, q_dtype=1) == E.SWA_E_DTYPE
+    assert decode(swa, ly, ix, out_dtype=2) == E.SWA_E_DTYPE
+    assert decode(swa, layer(swa, dtype=7), ix) == E.SWA_E_DTYPE
+    assert decode(swa, ly, ix, q=None) == E.SWA_E_ARG
+    assert decode(swa, ly, ix, out=FAKE + 4) == E.SWA_E_ARG        # misaligned
+    assert decode(swa, ly, ix, window=-2) == E.SWA_E_ARG
+    assert decode(swa, ly, ix, splits=0) == E.SWA_E_ARG
+    assert decode(swa, ly, ix, splits=4) == E.SWA_E_WORKSPACE
+    assert decode(swa, ly, ix, splits=4, ws=FAKE, ws_bytes=100) == E.SWA_E_WORKSPACE
+    assert decode(swa, ly, ix, table=None) == E.SWA_E_ARG          # indptr without table
+    assert decode(swa, layer(swa, k=None), ix) == E.SWA_E_ARG
+    assert decode(swa, layer(swa, rows=0), ix) == E.SWA_E_ARG
+    assert decode(swa, layer(swa, dtype=2, scale=0.0), ix) == E.SWA_E_ARG  # fp8 scale must be > 0
+    assert decode(swa, layer(swa, rows=1 << 31), ix) == E.SWA_E_SHAPE       # slots must fit int32
+    bad_ix = swa.IndexStruct(FAKE, 3, 100, FAKE, None, FAKE, 50, 2, 16)     # no seq_lens
+    assert decode(swa, ly, bad_ix) == E.SWA_E_ARG
+    bad_ix = swa.IndexStruct(None, 3, 100, FAKE, FAKE, None, 0, 2, 16)      # full layer, no req_to_token
+    assert decode(swa, ly, bad_ix, table=None, indptr=None, window=-1) == E.SWA_E_ARG
+
+
+def test_extend_argument_errors(swa):
+    E = swa
+    ly, ix = layer(swa), index(swa)
+
+    def ext(ly=ly, ix=ix, q_dtype=1, out_dtype=0, total=100, qo=FAKE, pre=FAKE, window=128):
+        return swa.lib.swa_extend(FAKE, q_dtype, 64, qo, pre, total, ctypes.byref(ly), ctypes.byref(ix), FAKE, FAKE,
+                                  1000, window, None, 0.088, FAKE, out_dtype, None)
+
+    assert ext(ly=layer(swa, dtype=2)) == E.SWA_E_DTYPE   # extend takes bf16 K/V
+    assert ext(q_dtype=0) == E.SWA_E_DTYPE
+    assert ext(ly=layer(swa, head_dim=256)) == E.SWA_E_SHAPE
+    assert ext(qo=None) == E.SWA_E_ARG
+    assert ext(pre=None) == E.SWA_E_ARG
+    assert ext(total=-1) == E.SWA_E_ARG
+    assert ext(total=1 << 31) == E.SWA_E_SHAPE
+    assert ext(window=-3) == E.SWA_E_ARG
+
+
+def test_store_and_translate_argument_errors(swa):
+    E = swa
+    lib = swa.lib
+    ly = layer(swa)
+    # dtype pairs: e4m3 input and bf16 -> f32 are not supported
+    assert lib.swa_kv_store(ctypes.byref(layer(swa, dtype=1)), FAKE, 4, FAKE, FAKE, 2, None) == E.SWA_E_DTYPE
+    assert lib.swa_kv_store(ctypes.byref(layer(swa, dtype=0)), FAKE, 4, FAKE, FAKE, 1, None) == E.SWA_E_DTYPE
+    assert lib.swa_kv_store(ctypes.byref(layer(swa, kv_heads=1, head_dim=4)), FAKE, 4, FAKE, FAKE, 1,
+                            None) == E.SWA_E_SHAPE
+    assert lib.swa_kv_store(ctypes.byref(ly), FAKE, -1, FAKE, FAKE, 1, None) == E.SWA_E_ARG
+    assert lib.swa_kv_store(ctypes.byref(ly), None, 4, FAKE, FAKE, 1, None) == E.SWA_E_ARG
+    assert lib.swa_kv_store(ctypes.byref(ly), FAKE, 4, FAKE + 8, FAKE, 1, None) == E.SWA_E_ARG
+    assert lib.swa_kv_store(None, FAKE, 4, FAKE, FAKE, 1, None) == E.SWA_E_ARG
+    assert lib.swa_kv_store(ctypes.byref(ly), FAKE, 0, FAKE, FAKE, 1, None) == E.SWA_OK  # empty: no launch
+    assert lib.swa_translate_loc(FAKE, -1, FAKE, 10, FAKE + 64, None) == E.SWA_E_ARG
+    assert lib.swa_translate_loc(FAKE, 5, FAKE, 1, FAKE + 64, None) == E.SWA_E_ARG
+    assert lib.swa_translate_loc(FAKE, 5, FAKE, 10, FAKE, None) == E.SWA_E_ARG     # aliasing
+    assert lib.swa_translate_loc(None, 0, None, 0, None, None) == E.SWA_OK         # empty: no launch
+    ix = index(swa)
+    assert lib.swa_translate_window(ctypes.byref(ix), -2, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window(ctypes.byref(ix), 128, None, None, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window(ctypes.byref(ix), 128, None, FAKE, None, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window(None, 128, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+
+
+def test_binding_rejects_host_tensors(swa):
+    import torch
+    a = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        swa.swa_translate_loc(a, torch.zeros(10, dtype=torch.int64), torch.zeros(4, dtype=torch.int64))
+

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Bit-exact for index translation and stores; attention
+within max|err| / RMS(oracle) of 1e-5 (f32), 2e-2 (bf16 K/V), 6e-2 (e4m3 K/V),
+checked on the kernel's f32 output; the bf16 output must equal the f32 output
+rounded to nearest even, bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs
+from oracle import swa_oracle as O
+from sliding_window_attention_swa_amd import workloads as WL
+
+from gpu_path import (TOL, DeviceWorkload, bits_to_device, check, device_to_bits, oracle_decode, oracle_extend,
+                      run_decode, run_extend, run_store, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sliding_window_attention_swa_amd import swa  # noqa: F401  (fails loudly if libswa.so is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def bf16_of(t: torch.Tensor) -> np.ndarray:
+    return device_to_bits(t.float().to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------------------
+# index translation and stores: bit-exact
+# ---------------------------------------------------------------------------
+
+
+def test_translate_loc_bit_exact():
+    from sliding_window_attention_swa_amd import swa
+    wl = WL.decode_workload("tl", 11, [300, 40, 1000], 4, 2, 128, 16, "bf16", "bf16")
+    rng = np.random.default_rng(0)
+    full = wl.req_to_token[1:, :].ravel()
+    full = np.concatenate([full[full > 0], [-1, 0, 0, -1]])
+    rng.shuffle(full)
+    full = full.astype(np.int64)
+    say(f"translate_loc n={full.size}")
+    m = torch.from_numpy(wl.full_to_swa).cuda()
+    out = torch.empty(full.size, dtype=torch.int64, device="cuda")
+    swa.swa_translate_loc(torch.from_numpy(full).cuda(), m, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), O.translate_loc(full, wl.full_to_swa))
+    # indices outside the table become 0 (the padding row), never an out-of-bounds read
+    bad = torch.tensor([-5, wl.full_to_swa.size - 1, wl.full_to_swa.size + 7, 1 << 40], dtype=torch.int64).cuda()
+    out = torch.empty_like(bad)
+    swa.swa_translate_loc(bad, m, out)
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("window", [128, 0, 7, -1])
+@pytest.mark.parametrize("extend", [False, True])
+def test_translate_window_bit_exact(window, extend):
+    from sliding_window_attention_swa_amd import swa
+    say(f"translate_window window={window} extend={extend}")
+    if extend:
+        wl = WL.extend_workload("tw", 12, [0, 5, 300, 1000], [20, 1, 70, 300], 4, 2, window, 16)
+        pre = wl.prefix_lens
+    else:
+        wl = WL.decode_workload("tw", 12, [1, 2, 129, 130, 700], 4, 2, max(window, 0) if window >= 0 else 128, 16,
+                                "bf16", "bf16")
+        pre = None
+    dw = DeviceWorkload(wl)
+    for use_map in (True, False):
+        if window < 0 and use_map and not extend:
+            continue
+        table_ref, indptr_ref = O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens,
+                                               wl.full_to_swa if use_map else None, window, prefix_lens=pre)
+        table = torch.full((table_ref.size + 5,), -77, dtype=torch.int32, device="cuda")
+        indptr = torch.empty(wl.batch + 1, dtype=torch.int32, device="cuda")
+        swa.swa_translate_window(dw.index, window, table, indptr, prefix_lens=dw.prefix, use_map=use_map)
+        torch.cuda.synchronize()
+        t = table.cpu().numpy()
+        assert np.array_equal(indptr.cpu().numpy(), indptr_ref)
+        assert np.array_equal(t[:table_ref.size], table_ref)
+        assert np.all(t[table_ref.size:] == -77)  # nothing written past the windows
+
+
+def test_translate_window_capacity_and_empty_batch():
+    from sliding_window_attention_swa_amd import swa
+    wl = WL.decode_workload("cap", 13, [50, 300], 4, 2, 128, 16, "bf16", "bf16")
+    dw = DeviceWorkload(wl)
+    table = torch.full((60,), -5, dtype=torch.int32, device="cuda")  # smaller than 50 + 129 entries
+    guard = torch.full((64,), -5, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(3, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(dw.index, 128, table, indptr)
+    torch.cuda.synchronize()
+    ref, ref_ptr = O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, 128)
+    assert np.array_equal(indptr.cpu().numpy(), ref_ptr)
+    assert np.array_equal(table.cpu().numpy(), ref[:60])
+    assert np.all(guard.cpu().numpy() == -5)
+    # empty batch: indptr = [0]
+    empty = swa.IndexTables(dw.r2t, dw.rows[:0], dw.lens[:0], dw.map, 16)
+    ip = torch.full((1,), 9, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(empty, 128, table, ip)
+    torch.cuda.synchronize()
+    assert ip.item() == 0
+
+
+STORE_PAIRS = [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"), ("bf16", "e4m3"), ("f32", "e4m3")]
+
+
+@pytest.mark.parametrize("in_dtype,pool_dtype", STORE_PAIRS)
+def test_kv_store_bit_exact(in_dtype, pool_dtype):
+    from sliding_window_attention_swa_amd import swa
+    say(f"kv_store {in_dtype}->{pool_dtype}")
+    rng = np.random.default_rng(14)
+    rows, H, D, n = 1000, 8, 128, 300
+    base = WL.SparsePool(rows, H, D, pool_dtype, np.arange(0), np.zeros((0, H, D), WL.NP_STORE[pool_dtype]))
+    loc = rng.choice(np.arange(1, rows), n, replace=False).astype(np.int64)
+    x = rng.standard_normal((n, H, D)).astype(np.float32) * rng.choice([1e-3, 1, 30], (n, 1, 1)).astype(np.float32)
+    kn = WL.to_store(x, in_dtype)
+    vn = WL.to_store(-2 * x, in_dtype)
+    from gpu_path import pool_to_device
+    k, v = pool_to_device(base), pool_to_device(base)
+    swa.swa_kv_store(swa.KvLayer(k, v), torch.from_numpy(loc).cuda(), bits_to_device(kn, in_dtype),
+                     bits_to_device(vn, in_dtype))
+    torch.cuda.synchronize()
+    ek, ev = O.kv_store(base, base, loc, kn, vn, in_dtype, pool_dtype)
+    gk, gv = device_to_bits(k), device_to_bits(v)
+    for got, exp in ((gk, ek.dense()), (gv, ev.dense())):
+        assert np.array_equal(got.view(np.uint8)[1:], exp.view(np.uint8)[1:])
+
+
+def test_kv_store_e4m3_every_bf16_pattern():
+    """All 65,536 bf16 bit patterns (NaN, inf, subnormals, overflow) through the
+    store kernel's e4m3 encoder, against the oracle's table-search encoder."""
+    from sliding_window_attention_swa_amd import swa
+    H, D = 8, 128
+    n = 65536 // (H * D)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(n, H, D)
+    rows = n + 8
+    loc = np.arange(1, n + 1, dtype=np.int64)
+    k = torch.zeros((rows, H, D), dtype=torch.uint8, device="cuda")
+    v = torch.zeros((rows, H, D), dtype=torch.uint8, device="cuda")
+    kb = bits_to_device(bits, "bf16")
+    swa.swa_kv_store(swa.KvLayer(k, v), torch.from_numpy(loc).cuda(), kb, kb)
+    torch.cuda.synchronize()
+    want = codecs.f64_to_e4m3(codecs.bf16_bits_to_f64(bits))
+    got = k.cpu().numpy()[1:n + 1]
+    assert np.array_equal(got, want)
+    assert np.array_equal(v.cpu().numpy()[1:n + 1], want)
+
+
+def test_kv_store_skips_out_of_pool_locs():
+    from sliding_window_attention_swa_amd import swa
+    H, D, rows = 2, 128, 16
+    k = torch.zeros((rows, H, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((rows, H, D), dtype=torch.bfloat16, device="cuda")
+    loc = torch.tensor([3, -1, rows, 1 << 40], dtype=torch.int64, device="cuda")
+    new = torch.ones((4, H, D), dtype=torch.bfloat16, device="cuda")
+    swa.swa_kv_store(swa.KvLayer(k, v), loc, new, new)
+    torch.cuda.synchronize()
+    written = (k.float().abs().sum(dim=(1, 2)) > 0).cpu().numpy()
+    assert written.tolist() == [i == 3 for i in range(rows)]
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = {
+    # name: (seq_lens, q_heads, kv_heads, window, page, q_dtype, kv_dtype, sinks)
+    "f32_g1": ([1, 100, 700], 4, 4, 128, 1, "f32", "f32", True),
+    "f32_g4_w3": ([1, 5, 64, 300], 8, 2, 3, 4, "f32", "f32", True),
+    "bf16_g8": ([1, 2, 129, 130, 1000], 16, 2, 128, 16, "bf16", "bf16", True),
+    "bf16_g8_nosink": ([1, 17, 200, 2000], 16, 2, 128, 16, "bf16", "bf16", False),
+    "bf16_g1": ([3, 150, 999], 4, 4, 128, 16, "bf16", "bf16", True),
+    "bf16_g2": ([3, 150, 999], 8, 4, 128, 16, "bf16", "bf16", True),
+    "bf16_g4": ([3, 150, 999], 8, 2, 128, 8, "bf16", "bf16", True),
+    "bf16_g16": ([3, 150, 999], 32, 2, 128, 16, "bf16", "bf16", True),
+    "bf16_w0": ([1, 9, 500], 16, 2, 0, 16, "bf16", "bf16", True),
+    "bf16_w1": ([1, 9, 500], 16, 2, 1, 16, "bf16", "bf16", True),
+    "bf16_w300_p64": ([1, 299, 300, 301, 302, 1500], 16, 2, 300, 64, "bf16", "bf16", True),
+    "e4m3_g8": ([1, 2, 129, 130, 1000], 16, 2, 128, 16, "bf16", "e4m3", True),
+    "e4m3_g16_nosink": ([5, 600], 32, 2, 128, 64, "bf16", "e4m3", False),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_decode_small(name):
+    lens, hq, hkv, w, P, qd, kvd, sinks = DECODE_CASES[name]
+    say(f"decode {name}")
+    wl = WL.decode_workload(name, 100 + len(name), lens, hq, hkv, w, P, qd, kvd, sinks=sinks, with_store=True,
+                            live_margin=5)
+    if kvd == "f32":
+        wl.new_k = WL.to_store(codecs.bf16_bits_to_f64(wl.new_k), "f32")
+        wl.new_v = WL.to_store(codecs.bf16_bits_to_f64(wl.new_v), "f32")
+        wl.new_dtype = "f32"
+    dw = DeviceWorkload(wl)
+    run_store(dw, wl.new_dtype)
+    out = run_decode(dw, "f32")
+    ref = oracle_decode(wl)
+    check(out, ref, TOL[kvd], name)
+    out_bf = run_decode(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
+FULL_CASES = {
+    "bf16_full_g16": ([1, 37, 600, 3000], 16, 1, "bf16", "bf16"),
+    "bf16_full_g8": ([1, 129, 2500], 16, 2, "bf16", "bf16"),
+    "e4m3_full_g8": ([2, 777, 2000], 16, 2, "bf16", "e4m3"),
+    "f32_full_g2": ([1, 64, 900], 4, 2, "f32", "f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_CASES))
+@pytest.mark.parametrize("splits", [None, 1, 3, 8])
+def test_decode_full_layer_splits(name, splits):
+    """W = -1 (full layer): keys straight from req_to_token, split-K partials
+    merged with the sink added once."""
+    lens, hq, hkv, qd, kvd = FULL_CASES[name]
+    say(f"decode full {name} splits={splits}")
+    wl = WL.decode_workload(name, 7 + len(name), lens, hq, hkv, -1, 16, qd, kvd, sinks=True)
+    dw = DeviceWorkload(wl)
+    out = run_decode(dw, "f32", num_splits=splits)
+    ref = oracle_decode(wl)
+    check(out, ref, TOL[kvd], f"{name} splits={splits}")
+    out_bf = run_decode(dw, "bf16", num_splits=splits)
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
+def relabel_swa_pages(wl: WL.Workload, seed: int) -> WL.Workload:
+    """Same logical K/V under another SWA page permutation."""
+    import copy
+    rng = np.random.default_rng(seed)
+    P = wl.page_size
+    npages = wl.n_swa // P
+    perm = np.concatenate([[0], rng.permutation(np.arange(1, npages + 1))])
+    w2 = copy.copy(wl)
+    m = wl.full_to_swa.copy()
+    live = m > 0
+    m[live] = perm[m[live] // P] * P + m[live] % P
+    w2.full_to_swa = m
+    rows = lambda r: perm[r // P] * P + r % P  # noqa: E731
+    w2.pool_k = WL.SparsePool(*wl.pool_k.shape, wl.kv_dtype, rows(wl.pool_k.used_rows), wl.pool_k.values)
+    w2.pool_v = WL.SparsePool(*wl.pool_v.shape, wl.kv_dtype, rows(wl.pool_v.used_rows), wl.pool_v.values)
+    return w2
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "e4m3"])
+def test_decode_layout_invariance(kvd):
+    say(f"layout invariance {kvd}")
+    wl = WL.decode_workload("inv", 21, [1, 130, 700, 2000], 16, 2, 128, 16, "bf16", kvd)
+    a = run_decode(DeviceWorkload(wl), "f32")
+    b = run_decode(DeviceWorkload(relabel_swa_pages(wl, 5)), "f32")
+    assert torch.equal(a, b)
+
+
+def test_decode_c1_full_size():
+    wl = WL.c1_decode_f32()
+    say("decode c1 (1 x 512, f32)")
+    out = run_decode(DeviceWorkload(wl), "f32")
+    check(out, oracle_decode(wl), TOL["f32"], "c1")
+
+
+def test_decode_c2_full_size():
+    wl = WL.c2_decode_bf16()
+    say("decode c2 (64 requests, bf16, with store)")
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_decode(dw, "f32")
+    check(out, oracle_decode(wl), TOL["bf16"], "c2")
+
+
+def test_decode_c5_full_size():
+    wl = WL.c5_decode_fp8()
+    say("decode c5 (256 requests, e4m3 K/V, with store)")
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_decode(dw, "f32")
+    check(out, oracle_decode(wl), TOL["e4m3"], "c5")
+    # the stored rows are the oracle's encoding of the new tokens, bit for bit
+    loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+    want = codecs.f64_to_e4m3(codecs.bf16_bits_to_f64(wl.new_k))
+    assert np.array_equal(dw.k[torch.from_numpy(loc).cuda()].cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+# extend
+# ---------------------------------------------------------------------------
+
+EXTEND_CASES = {
+    # name: (prefix, chunk, q_heads, kv_heads, window, page, sinks)
+    "g8_w128": ([0, 5, 300], [33, 100, 70], 16, 2, 128, 16, True),
+    "g8_w128_nosink": ([200, 0], [17, 250], 16, 2, 128, 16, False),
+    "g8_full": ([0, 40], [50, 17], 16, 2, -1, 8, True),
+    "g8_w0": ([10, 0], [20, 5], 16, 2, 0, 4, True),
+    "g8_w16": ([100, 3], [64, 33], 16, 2, 16, 16, True),
+    "g8_w300": ([50, 700], [400, 31], 16, 2, 300, 64, True),
+    "g1": ([20, 300], [40, 90], 2, 2, 128, 16, True),
+    "g2": ([20, 300], [40, 90], 4, 2, 128, 16, True),
+    "g4": ([20, 300], [40, 90], 8, 2, 128, 16, True),
+    "g16": ([20, 300], [40, 90], 32, 2, 128, 16, True),
+}
+
+
+@pytest.mark.parametrize("name", list(EXTEND_CASES))
+def test_extend_small(name):
+    pre, chunk, hq, hkv, w, P, sinks = EXTEND_CASES[name]
+    say(f"extend {name}")
+    wl = WL.extend_workload(name, 300 + len(name), pre, chunk, hq, hkv, w, P, sinks=sinks)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_extend(dw, "f32")
+    check(out, oracle_extend(wl), TOL["bf16"], name)
+    out_bf = run_extend(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
+def test_extend_c3_full_size_sampled():
+    wl = WL.c3_extend_bf16()
+    say("extend c3 (4 x (8K prefix + 2K chunk), bf16) — sampled rows")
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_extend(dw, "f32")
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(wl.q.shape[0] - 40, wl.q.shape[0]),
+                                     rng.choice(wl.q.shape[0], 300, replace=False)]))
+    only = [(int(r), h) for r in rows for h in range(wl.q_heads)]
+    ref = oracle_extend(wl, only=only)
+    check(out, ref, TOL["bf16"], "c3 sampled")
