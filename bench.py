@@ -1,0 +1,295 @@
+"""Benchmark of the sliding-window attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+
+Default workload (c2): batched SWA decode, B = 64 requests with context lengths
+uniform in [1K, 8K], W = 128, 64 q / 8 kv heads, head_dim 128, bf16, page 16,
+two-pool cache with out-of-window pages tombstoned.  One step is one decode
+step of that batch through a stack of 32 SWA layers, each with its own K/V
+pool (so the 256 MB Infinity Cache cannot serve repeats):
+    translate_loc (new tokens' full locs -> SWA slots)    once per step
+    translate_window (req_to_token -> full -> SWA slots)  once per step
+    per layer: kv_store (new token K/V) + swa_decode
+The step is captured once as a HIP graph and replayed; inputs are resident in
+HBM before timing starts.  The JSON line reports algorithmic HBM bytes per
+second of the whole step, the dominant kernel's roofline (swa_decode, timed
+live with HIP events over back-to-back launches), and the CPU oracle timed on
+the host for a bounded sample of the same work.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "SWA decode HBM GB/s & tokens/s; windowed prefill TFLOP/s (% of MI355X peak)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name: str, kernel_files, per_launch_units: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when absent or taken on another version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != source_sha(*kernel_files):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# device setup helpers (torch for memory only)
+# ---------------------------------------------------------------------------
+
+
+def dev_from_bits(torch, bits, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    if dtype == "e4m3":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).cuda()
+
+
+def randn_store(torch, shape, gen, dtype):
+    x = torch.randn(shape, generator=gen, device="cuda")
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    if dtype == "e4m3":
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return x
+
+
+def nan_pool(torch, rows, H, D, dtype):
+    if dtype == "bf16":
+        t = torch.empty((rows, H, D), dtype=torch.bfloat16, device="cuda")
+        t.view(torch.int16).fill_(0x7FC0)
+    elif dtype == "e4m3":
+        t = torch.full((rows, H, D), 0x7F, dtype=torch.uint8, device="cuda")
+    else:
+        t = torch.full((rows, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    return t
+
+
+class DecodeBench:
+    """A decode batch of one workload replicated over `layers` SWA layers."""
+
+    def __init__(self, torch, swa, wl, layers, out_dtype="bf16", seed=7):
+        self.torch, self.swa, self.wl, self.L = torch, swa, wl, layers
+        B, Hq, Hkv, D = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
+        self.r2t = torch.from_numpy(wl.req_to_token).cuda()
+        self.rows = torch.from_numpy(wl.req_pool_idx).cuda()
+        self.lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).cuda()
+        self.map = torch.from_numpy(wl.full_to_swa).cuda()
+        self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, wl.page_size)
+        self.has_store = wl.new_full_loc is not None
+        if self.has_store:
+            self.full_loc = torch.from_numpy(wl.new_full_loc).cuda()
+            self.swa_loc = torch.empty_like(self.full_loc)
+        self.cap = B * (wl.window + 1)
+        self.table = torch.empty(self.cap, dtype=torch.int32, device="cuda")
+        self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+        used = torch.from_numpy(wl.pool_k.used_rows).cuda()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.layers = []
+        for _ in range(layers):
+            k = nan_pool(torch, wl.pool_rows, Hkv, D, wl.kv_dtype)
+            v = nan_pool(torch, wl.pool_rows, Hkv, D, wl.kv_dtype)
+            k[used] = randn_store(torch, (used.numel(), Hkv, D), g, wl.kv_dtype)
+            v[used] = randn_store(torch, (used.numel(), Hkv, D), g, wl.kv_dtype)
+            self.layers.append(dict(
+                kv=swa.KvLayer(k, v),
+                q=randn_store(torch, (B, Hq, D), g, wl.q_dtype),
+                new_k=randn_store(torch, (B, Hkv, D), g, "bf16" if wl.kv_dtype != "f32" else "f32"),
+                new_v=randn_store(torch, (B, Hkv, D), g, "bf16" if wl.kv_dtype != "f32" else "f32"),
+                out=torch.empty((B, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
+                                device="cuda"),
+            ))
+        self.sinks = torch.from_numpy(wl.sinks).cuda() if wl.sinks is not None else None
+        # algorithmic bytes (window only): K/V rows, Q, O, window table
+        n_keys = np.minimum(wl.seq_lens.astype(np.int64), wl.window + 1)
+        kv_b = {"bf16": 2, "e4m3": 1, "f32": 4}[wl.kv_dtype]
+        q_b = {"bf16": 2, "f32": 4}[wl.q_dtype]
+        o_b = 2 if out_dtype == "bf16" else 4
+        self.decode_bytes = int(n_keys.sum() * Hkv * D * kv_b * 2 + B * Hq * D * (q_b + o_b) + n_keys.sum() * 4
+                                + (B + 1) * 4)
+        new_b = 2 if wl.kv_dtype != "f32" else 4
+        self.store_bytes = B * Hkv * D * 2 * (new_b + kv_b) + B * 8 if self.has_store else 0
+        self.translate_bytes = (B * 8 * 3 if self.has_store else 0) + int(n_keys.sum()) * (4 + 8 + 4) + B * 12
+        self.step_bytes = self.translate_bytes + layers * (self.store_bytes + self.decode_bytes)
+        self.flops_decode = int(n_keys.sum()) * Hq * D * 4
+
+    def step(self):
+        swa, wl = self.swa, self.wl
+        if self.has_store:
+            swa.swa_translate_loc(self.full_loc, self.map, self.swa_loc)
+        swa.swa_translate_window(self.index, wl.window, self.table, self.indptr)
+        for ly in self.layers:
+            if self.has_store:
+                swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
+            swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                           slot_table=self.table, table_indptr=self.indptr)
+
+    def dominant(self):
+        """Back-to-back decode launches only (one per layer)."""
+        swa, wl = self.swa, self.wl
+        for ly in self.layers:
+            swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                           slot_table=self.table, table_indptr=self.indptr)
+
+
+def graph_of(torch, fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager run on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, g, n):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(n):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n  # ms per replay
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, single-threaded, on a bounded sample
+# ---------------------------------------------------------------------------
+
+
+def cpu_baseline_decode(wl, budget_s=12.0):
+    from threadpoolctl import threadpool_limits
+    from oracle import swa_oracle as O
+    B = wl.batch
+    done_req = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        pk, pv = wl.pool_k, wl.pool_v
+        if wl.new_full_loc is not None:
+            swa_loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+            pk, pv = O.kv_store(pk, pv, swa_loc, wl.new_k, wl.new_v, wl.new_dtype, wl.kv_dtype)
+        O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window)
+        b = 0
+        while time.perf_counter() - t0 < budget_s:
+            only = [(b, h) for h in range(wl.q_heads)]
+            O.decode(wl.q, wl.q_dtype, pk, pv, wl.kv_dtype, wl.req_to_token, wl.req_pool_idx, wl.seq_lens,
+                     wl.full_to_swa, wl.window, wl.sinks, only=only)
+            b = (b + 1) % B
+            done_req += 1
+    return time.perf_counter() - t0, done_req
+
+
+# ---------------------------------------------------------------------------
+
+
+def run_decode_workload(args, torch, swa, W):
+    name = args.workload
+    if name == "c2":
+        wl, layers = W.c2_decode_bf16(), 32
+        desc = "batched SWA decode B=64, T~U[1K,8K], W=128, 64q/8kv, D=128, bf16, page 16"
+    elif name == "c5":
+        wl, layers = W.c5_decode_fp8(), 16
+        desc = "fp8 KV decode B=256, T~lognormal(16K), W=128, 64q/8kv, D=128, e4m3 K/V, bf16 q, page 64"
+    else:
+        wl, layers = W.c1_decode_f32(), 8
+        desc = "single SWA decode T=512, W=128, 8q/8kv, D=128, f32, page 1"
+    out_dtype = "f32" if wl.q_dtype == "f32" else "bf16"
+    log(f"[bench] {name}: building {layers} layers")
+    bench = DecodeBench(torch, swa, wl, layers, out_dtype)
+    g_step = graph_of(torch, bench.step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    ms = time_replays(torch, g_step, args.steps)
+    log(f"[bench] step {ms:.4f} ms")
+    g_dec = graph_of(torch, bench.dominant)
+    dec_reps = max(10, args.steps // 2)
+    ms_dec = time_replays(torch, g_dec, dec_reps) / layers
+    log(f"[bench] swa_decode {ms_dec * 1e3:.2f} us per launch")
+    value = bench.step_bytes / (ms * 1e-3) / 1e9
+    achieved = bench.decode_bytes / (ms_dec * 1e-3) / 1e9
+    traffic = traffic_from_profile(f"swa_decode_{name}", ["decode_kernels.hip", "common.hpp"], 1)
+    res = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype={"c5": "bf16 q / e4m3 kv", "c1": "f32"}.get(name, "bf16"), data="synthetic",
+        config={"workload": desc, "global_batch": int(wl.batch), "layers_per_step": layers, "window": wl.window,
+                "max_seq_len": int(wl.seq_lens.max()), "parallelism": "none (1 GPU)"},
+        tokens_per_s=round(wl.batch / (ms * 1e-3), 1),
+        layer_tokens_per_s=round(wl.batch * layers / (ms * 1e-3), 1),
+        frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
+        roofline=dict(kernel="swa_decode", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                      unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                      bytes_per_launch=bench.decode_bytes, us_per_launch=round(ms_dec * 1e3, 3)),
+    )
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        secs, nreq = cpu_baseline_decode(wl)
+        per_req_bytes = bench.decode_bytes / wl.batch
+        res["cpu_baseline"] = dict(value=round(nreq * per_req_bytes / secs / 1e9, 6), unit="GB/s", cores=1,
+                                   kind="oracle",
+                                   sample=f"one layer: translate + store + window table for all {wl.batch} requests, "
+                                          f"then decode of {nreq} requests x {wl.q_heads} heads ({secs:.1f} s)")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+    import torch
+    from sliding_window_attention_swa_amd import swa
+    from sliding_window_attention_swa_amd import workloads as W
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    res = run_decode_workload(args, torch, swa, W)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

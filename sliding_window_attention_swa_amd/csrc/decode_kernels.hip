@@ -140,18 +140,17 @@ __device__ __forceinline__ void split_range(int32_t n, int32_t s, int32_t splits
 // the final output (one split) or this split's partial to the workspace.
 // red_m / red_l: [NW][kMaxG] (base-2 logit domain); red_acc: [NW][G][kD].
 // --------------------------------------------------------------------------
-template <int NW, bool OUT_BF16>
-__device__ void merge_waves_and_store(const DecodeParams &p, const float *red_m, const float *red_l,
+template <bool OUT_BF16>
+__device__ void merge_waves_and_store(const DecodeParams &p, int NW, const float *red_m, const float *red_l,
                                       const float *red_acc, int32_t b, int32_t g, int32_t s) {
   const int32_t G = p.group;
   const bool final = p.num_splits == 1;
   // each thread produces 4 consecutive dims of one head
-  for (int32_t t = threadIdx.x; t < G * (kD / 4); t += NW * 64) {
+  for (int32_t t = threadIdx.x; t < G * (kD / 4); t += blockDim.x) {
     const int32_t hh = t / (kD / 4);
     const int32_t d4 = (t % (kD / 4)) * 4;
     const int32_t h = g * G + hh;
     float M = kNegBig;
-#pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * kMaxG + hh]);
     float sig2 = -INFINITY;
     if (final && p.sinks) {
@@ -160,7 +159,6 @@ __device__ void merge_waves_and_store(const DecodeParams &p, const float *red_m,
     }
     float L = 0.f;
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-#pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float a = exp2f(red_m[w * kMaxG + hh] - M);
       L += red_l[w * kMaxG + hh] * a;
@@ -427,7 +425,184 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  merge_waves_and_store<NW, OUT_BF16>(p, red_m, red_l, red_acc, b, g, s);
+  merge_waves_and_store<OUT_BF16>(p, NW, red_m, red_l, red_acc, b, g, s);
+}
+
+// --------------------------------------------------------------------------
+// Window kernel (SWA layers, one split).  The window's 16-key blocks are dealt
+// to 4 wavefronts, at most MAXB blocks each (3 at W = 128), and every K/V row
+// of the window is requested before any arithmetic starts: the registers of a
+// CU (512 KB) hold far more bytes in flight than its LDS, so the whole batch is
+// resident in one round and the kernel is one dependent chain deep:
+//   slot table -> K/V rows -> MFMA -> wavefront merge -> output.
+// (Plain loads: measured on MI355X, non-temporal loads made this gather ~50%
+// slower.)
+// --------------------------------------------------------------------------
+constexpr int kWinWaves = 4;
+
+template <typename KV, int MAXB, bool OUT_BF16>
+__global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kWinWaves * MAXB * 16 * kVRow * 2 >
+                                                                    kWinWaves * kMaxG * kD * 4
+                                                                ? kWinWaves * MAXB * 16 * kVRow * 2
+                                                                : kWinWaves * kMaxG * kD * 4];
+  __shared__ float red_m[kWinWaves * kMaxG];
+  __shared__ float red_l[kWinWaves * kMaxG];
+  const int32_t g = blockIdx.y;
+  const int32_t b = blockIdx.z;
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  const int32_t G = p.group;
+  constexpr int kVec = KvLoad<KV>::kVecs;
+
+  // ---- key source (window table or req_to_token row).  A window holds at
+  // most W + 1 keys: only the last W + 1 entries are used.
+  const KeySource ks = key_source(p, b);
+  const int32_t n = ks.n < p.window + 1 ? ks.n : p.window + 1;
+  const int32_t *src = ks.src + (ks.n - n);
+  const int32_t nblk = (n + 15) >> 4;  // <= kWinWaves * MAXB for this instantiation
+
+  // Q^T operand rows (head g*G + kr, dims 32lq..32lq+31).  Lanes of padding
+  // heads (kr >= G) read a real head: their columns are never stored.
+  const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
+                                                    (static_cast<int64_t>(b) * p.q_heads + g * G +
+                                                     (kr < G ? kr : 0)) * kD + 32 * lq);
+  uint4 qraw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig;
+  float l_run = 0.f;
+  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * MAXB * 16 * kVRow;
+
+  if (w < nblk) {  // wave-uniform: this wavefront owns at least one block
+    // All loads are unconditional (no control flow between them, so none of
+    // them waits for another): keys past the end re-read the wavefront's first
+    // key, and their scores are masked to -inf below.  The phases are fenced
+    // with scheduling barriers so that the compiler cannot pull arithmetic into
+    // the load phase (its in-order vmcnt waits would make later rows wait for
+    // earlier ones).
+    int32_t sl[MAXB];
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) {
+      const int32_t key = 16 * (w + kWinWaves * u) + kr;
+      sl[u] = src[key < n ? key : 16 * w];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // every K row first, then every V row: the scores only wait for K
+    int64_t off[MAXB];
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) off[u] = row_elem(safe_slot(sl[u], p.rows), p.kv_heads, g, kD) + 32 * lq;
+    uint4 kraw[MAXB][kVec], vraw[MAXB][kVec];
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) {
+      const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.k) + off[u]);
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) kraw[u][c] = kp[c];
+    }
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) {
+      const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.v) + off[u]);
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) vraw[u][c] = vp[c];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t qop[4];
+    KvLoad<uint16_t>::to_bf16(qraw, qop);
+
+    // ---- S^T = K Q^T for every block (lane: keys 4lq..4lq+3 of head kr)
+    float sc[MAXB][4];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) {
+      const int32_t t = w + kWinWaves * u;
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+      bf16x8_t kk[4];
+      KvLoad<KV>::to_bf16(kraw[u], kk);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c], qop[c], sacc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[u][r] = (16 * t + 4 * lq + r < n) ? sacc[r] * p.scale2 : -INFINITY;
+        mb = fmaxf(mb, sc[u][r]);
+      }
+    }
+    // ---- one softmax over the wavefront's keys (no rescaling needed)
+    m_run = fmaxf(kNegBig, wave_max_q(mb));
+    constexpr int kPairs = (MAXB + 1) / 2;
+    bf16x8_t pop[kPairs];
+#pragma unroll
+    for (int u2 = 0; u2 < kPairs; ++u2) {
+      float pv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = exp2f(sc[2 * u2][r] - m_run);
+        pv[4 + r] = (2 * u2 + 1 < MAXB) ? exp2f(sc[(2 * u2 + 1) < MAXB ? 2 * u2 + 1 : 0][r] - m_run) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l_run += pv[e];
+      uint32_t u4[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                        pack_bf16x2(pv[6], pv[7])};
+      __builtin_memcpy(&pop[u2], u4, 16);
+    }
+    // ---- V rows -> LDS (bf16, 264-byte rows), block u at rows 16u..16u+15
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) {
+      bf16x8_t vv[4];
+      KvLoad<KV>::to_bf16(vraw[u], vv);
+      uint2 *d = reinterpret_cast<uint2 *>(vt + (u * 16 + kr) * kVRow + 32 * lq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint2 a2[2];
+        __builtin_memcpy(a2, &vv[c], 16);
+        d[2 * c] = a2[0];
+        d[2 * c + 1] = a2[1];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1)
+#pragma unroll
+    for (int u2 = 0; u2 < kPairs; ++u2) {
+      const bool second = 2 * u2 + 1 < MAXB;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint16_t *col = vt + (2 * u2 * 16) * kVRow + 16 * c + kr;
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          e8[e] = col[(4 * lq + e) * kVRow];
+          e8[4 + e] = second ? col[(16 + 4 * lq + e) * kVRow] : static_cast<uint16_t>(0);
+        }
+        bf16x8_t vop;
+        __builtin_memcpy(&vop, e8, 16);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[u2], acc[c], 0, 0, 0);
+      }
+    }
+  }
+  l_run = wave_sum_q(l_run);
+
+  __syncthreads();  // all V tiles consumed: the LDS is reused for the merge
+  float *red_acc = reinterpret_cast<float *>(lds);
+  if (kr < G) {
+    if (lq == 0) {
+      red_m[w * kMaxG + kr] = m_run;
+      red_l[w * kMaxG + kr] = l_run;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float4 v = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+      *reinterpret_cast<float4 *>(red_acc + (w * G + kr) * kD + 16 * c + 4 * lq) = v;
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<OUT_BF16>(p, kWinWaves, red_m, red_l, red_acc, b, g, 0);
 }
 
 // --------------------------------------------------------------------------
@@ -492,7 +667,7 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(DecodeParams p) {
     *reinterpret_cast<float2 *>(red_acc + (w * G + hh) * kD + 2 * lane) = acc[hh];
   }
   __syncthreads();
-  merge_waves_and_store<NW, OUT_BF16>(p, red_m, red_l, red_acc, b, g, s);
+  merge_waves_and_store<OUT_BF16>(p, NW, red_m, red_l, red_acc, b, g, s);
 }
 
 // --------------------------------------------------------------------------
@@ -526,6 +701,26 @@ __global__ void __launch_bounds__(kD) decode_merge_kernel(DecodeParams p) {
     static_cast<uint16_t *>(p.out)[off] = f32_to_bf16_rne(o);
   else
     static_cast<float *>(p.out)[off] = o;
+}
+
+template <typename KV, int MAXB>
+hipError_t launch_window_b(const DecodeParams &p, dim3 grid, bool out_bf16, hipStream_t stream) {
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, true>), grid, dim3(kWinWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, false>), grid, dim3(kWinWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Blocks per wavefront for a window of W + 1 keys over kWinWaves wavefronts.
+template <typename KV>
+hipError_t launch_window(const DecodeParams &p, dim3 grid, int window, bool out_bf16, hipStream_t stream) {
+  const int blocks = (window + 1 + 15) / 16;
+  const int maxb = (blocks + kWinWaves - 1) / kWinWaves;
+  if (maxb <= 1) return launch_window_b<KV, 1>(p, grid, out_bf16, stream);
+  if (maxb == 2) return launch_window_b<KV, 2>(p, grid, out_bf16, stream);
+  if (maxb == 3) return launch_window_b<KV, 3>(p, grid, out_bf16, stream);
+  return launch_window_b<KV, 4>(p, grid, out_bf16, stream);
 }
 
 template <typename KV, int NW>
@@ -583,6 +778,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((decode_f32_kernel<kDecodeWaves, false>), grid, dim3(kDecodeWaves * 64), 0, stream, p);
     e = hipGetLastError();
+  } else if (a.num_splits == 1 && a.window >= 0 && a.window < 16 * kWinWaves * 4) {
+    // SWA layer: the whole window in flight at once (up to 4 blocks per wavefront)
+    e = a.layer.dtype == SWA_BF16 ? launch_window<uint16_t>(p, grid, a.window, out_bf16, stream)
+                                  : launch_window<uint8_t>(p, grid, a.window, out_bf16, stream);
   } else if (a.layer.dtype == SWA_BF16) {
     e = launch_mfma<uint16_t, kDecodeWaves>(p, grid, out_bf16, stream);
   } else {
