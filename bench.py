@@ -2,6 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
 
+Other workloads (one JSON line each, same fields): c1 single f32 decode; c3
+chunked-prefill extend (store + extend over 4 layers); c4 the 48-layer mixed
+decode step (39 SWA + 9 full layers); c5 fp8-KV decode with store.
+
 Default workload (c2): batched SWA decode, B = 64 requests with context lengths
 uniform in [1K, 8K], W = 128, 64 q / 8 kv heads, head_dim 128, bf16, page 16,
 two-pool cache with out-of-window pages tombstoned.  One step is one decode
@@ -268,12 +272,220 @@ def run_decode_workload(args, torch, swa, W):
     return res
 
 
+# ---------------------------------------------------------------------------
+# c3: chunked-prefill extend
+# ---------------------------------------------------------------------------
+
+
+class ExtendBench:
+    """The c3 extend batch replicated over `layers` SWA layers."""
+
+    def __init__(self, torch, swa, wl, layers, seed=11):
+        self.torch, self.swa, self.wl = torch, swa, wl
+        B, Hq, Hkv, D = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
+        self.r2t = torch.from_numpy(wl.req_to_token).cuda()
+        self.rows = torch.from_numpy(wl.req_pool_idx).cuda()
+        self.lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).cuda()
+        self.map = torch.from_numpy(wl.full_to_swa).cuda()
+        self.prefix = torch.from_numpy(wl.prefix_lens).cuda()
+        self.qo = torch.from_numpy(wl.qo_indptr).cuda()
+        self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, wl.page_size)
+        self.full_loc = torch.from_numpy(wl.new_full_loc).cuda()
+        self.swa_loc = torch.empty_like(self.full_loc)
+        lo = np.maximum(wl.prefix_lens.astype(np.int64) - wl.window, 0)
+        self.n_keys = (wl.seq_lens.astype(np.int64) - lo)
+        self.cap = int(self.n_keys.sum())
+        self.table = torch.empty(self.cap, dtype=torch.int32, device="cuda")
+        self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+        used = torch.from_numpy(wl.pool_k.used_rows).cuda()
+        total_q = wl.q.shape[0]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.layers = []
+        for _ in range(layers):
+            k = nan_pool(torch, wl.pool_rows, Hkv, D, "bf16")
+            v = nan_pool(torch, wl.pool_rows, Hkv, D, "bf16")
+            k[used] = randn_store(torch, (used.numel(), Hkv, D), g, "bf16")
+            v[used] = randn_store(torch, (used.numel(), Hkv, D), g, "bf16")
+            self.layers.append(dict(kv=swa.KvLayer(k, v), q=randn_store(torch, (total_q, Hq, D), g, "bf16"),
+                                    new_k=randn_store(torch, (total_q, Hkv, D), g, "bf16"),
+                                    new_v=randn_store(torch, (total_q, Hkv, D), g, "bf16"),
+                                    out=torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device="cuda")))
+        self.sinks = torch.from_numpy(wl.sinks).cuda()
+        # algorithmic bytes and band-only FLOPs of one extend launch
+        self.extend_bytes = int(total_q * Hq * D * 2 * 2 + self.n_keys.sum() * Hkv * D * 2 * 2 + self.cap * 4
+                                + (B + 1) * 4 * 2 + B * 4 * 2)
+        pairs = 0
+        for b in range(B):
+            i = np.arange(int(wl.prefix_lens[b]), int(wl.seq_lens[b]))
+            pairs += int(np.sum(i - np.maximum(i - wl.window, 0) + 1))
+        self.extend_flops = pairs * Hq * D * 4
+        self.store_bytes = total_q * Hkv * D * 2 * 2 * 2 + total_q * 8
+        self.step_bytes = total_q * 8 * 3 + self.cap * 16 + layers * (self.store_bytes + self.extend_bytes)
+        self.step_flops = layers * self.extend_flops
+
+    def step(self):
+        swa, wl = self.swa, self.wl
+        swa.swa_translate_loc(self.full_loc, self.map, self.swa_loc)
+        swa.swa_translate_window(self.index, wl.window, self.table, self.indptr, prefix_lens=self.prefix)
+        for ly in self.layers:
+            swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
+            swa.swa_extend(ly["q"], self.qo, self.prefix, ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                           slot_table=self.table, table_indptr=self.indptr)
+
+    def dominant(self):
+        swa, wl = self.swa, self.wl
+        for ly in self.layers:
+            swa.swa_extend(ly["q"], self.qo, self.prefix, ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                           slot_table=self.table, table_indptr=self.indptr)
+
+
+def cpu_baseline_extend(wl, budget_s=12.0):
+    from threadpoolctl import threadpool_limits
+    from oracle import swa_oracle as O
+    rows_done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        swa_loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+        pk, pv = O.kv_store(wl.pool_k, wl.pool_v, swa_loc, wl.new_k, wl.new_v, "bf16", "bf16")
+        O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window,
+                       prefix_lens=wl.prefix_lens)
+        r = 0
+        while time.perf_counter() - t0 < budget_s:
+            only = [(r, h) for h in range(wl.q_heads)]
+            O.extend(wl.q, "bf16", wl.qo_indptr, wl.prefix_lens, pk, pv, "bf16", wl.req_to_token, wl.req_pool_idx,
+                     wl.seq_lens, wl.full_to_swa, wl.window, wl.sinks, only=only)
+            r = (r + 997) % wl.q.shape[0]
+            rows_done += 1
+    return time.perf_counter() - t0, rows_done
+
+
+def run_extend_workload(args, torch, swa, W):
+    wl, layers = W.c3_extend_bf16(), 4
+    log(f"[bench] c3: building {layers} layers")
+    bench = ExtendBench(torch, swa, wl, layers)
+    g_step = graph_of(torch, bench.step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    ms = time_replays(torch, g_step, args.steps)
+    g_dom = graph_of(torch, bench.dominant)
+    ms_ext = time_replays(torch, g_dom, max(5, args.steps)) / layers
+    log(f"[bench] step {ms:.4f} ms, extend {ms_ext * 1e3:.2f} us")
+    value = bench.step_bytes / (ms * 1e-3) / 1e9
+    achieved = bench.extend_bytes / (ms_ext * 1e-3) / 1e9
+    tflops = bench.extend_flops / (ms_ext * 1e-3) / 1e12
+    res = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic",
+        config={"workload": "chunked-prefill extend B=4, prefix 8K + chunk 2K, W=128, 64q/8kv, D=128, bf16, page 64",
+                "global_batch": int(wl.batch), "new_tokens": int(wl.q.shape[0]), "layers_per_step": layers,
+                "window": wl.window, "parallelism": "none (1 GPU)"},
+        tokens_per_s=round(wl.q.shape[0] / (ms * 1e-3) * layers / layers, 1),
+        extend_tflops=round(tflops, 2), extend_frac_of_mfma_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
+        extend_attainable_tflops=round(min(BF16_PEAK_TFLOPS, bench.extend_flops / bench.extend_bytes * HBM_PEAK_GBS
+                                           / 1e3), 1),
+        roofline=dict(kernel="swa_extend", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=traffic_from_profile("swa_extend_c3", ["extend_kernels.hip", "common.hpp"], 1),
+                      bytes_per_launch=bench.extend_bytes, flops_per_launch=bench.extend_flops,
+                      us_per_launch=round(ms_ext * 1e3, 3)),
+    )
+    if not args.no_cpu_baseline:
+        secs, rows = cpu_baseline_extend(wl)
+        per_row_flops = bench.extend_flops / wl.q.shape[0]
+        res["cpu_baseline"] = dict(value=round(rows * per_row_flops / secs / 1e12, 9), unit="TFLOP/s", cores=1,
+                                   kind="oracle", sample=f"translate + store + window table, then {rows} query rows x "
+                                                         f"{wl.q_heads} heads ({secs:.1f} s)")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# c4: 48-layer mixed decode step (39 SWA + 9 full layers)
+# ---------------------------------------------------------------------------
+
+
+class MixedBench:
+    def __init__(self, torch, swa, W):
+        self.torch, self.swa = torch, swa
+        st = self.st = W.c4_mixed_step()
+        B, Hq, D = st.batch, st.q_heads, st.head_dim
+        self.r2t = torch.from_numpy(st.req_to_token).cuda()
+        self.rows = torch.from_numpy(st.req_pool_idx).cuda()
+        self.lens = torch.from_numpy(st.seq_lens).cuda()
+        self.map = torch.from_numpy(st.full_to_swa).cuda()
+        self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, st.page_size)
+        self.table = torch.empty(B * 129, dtype=torch.int32, device="cuda")
+        self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+        self.layers = []
+        self.splits, ws_bytes = swa.swa_decode_plan(B, Hq, 4, D, -1, st.seq_len)
+        self.ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+        for ly in st.layers:
+            q, k, v = W.c4_layer_tensors(st, ly)
+            self.layers.append(dict(meta=ly, q=q, kv=swa.KvLayer(k, v),
+                                    out=torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")))
+        T, W1 = st.seq_len, 129
+        self.full_bytes = B * T * 4 * D * 2 * 2 + B * Hq * D * 4 + B * T * 4
+        self.swa_bytes = B * W1 * 8 * D * 2 * 2 + B * Hq * D * 4 + B * W1 * 4
+        self.step_bytes = 9 * self.full_bytes + 39 * self.swa_bytes + B * W1 * 16
+        self.full_flops = B * T * Hq * D * 4
+
+    def layer_call(self, ly):
+        swa, m = self.swa, ly["meta"]
+        if m["kind"] == "full":
+            swa.swa_decode(ly["q"], ly["kv"], self.index, -1, ly["out"], num_splits=self.splits, workspace=self.ws,
+                           use_map=False)
+        else:
+            swa.swa_decode(ly["q"], ly["kv"], self.index, 128, ly["out"], slot_table=self.table,
+                           table_indptr=self.indptr)
+
+    def step(self):
+        self.swa.swa_translate_window(self.index, 128, self.table, self.indptr)
+        for ly in self.layers:
+            self.layer_call(ly)
+
+    def dominant(self):
+        for ly in self.layers:
+            if ly["meta"]["kind"] == "full":
+                self.layer_call(ly)
+
+
+def run_mixed_workload(args, torch, swa, W):
+    log("[bench] c4: building 48 layers")
+    bench = MixedBench(torch, swa, W)
+    g_step = graph_of(torch, bench.step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    ms = time_replays(torch, g_step, args.steps)
+    g_dom = graph_of(torch, bench.dominant)
+    ms_full = time_replays(torch, g_dom, max(3, args.steps // 2)) / 9
+    log(f"[bench] step {ms:.3f} ms, full-layer decode {ms_full * 1e3:.1f} us")
+    value = bench.step_bytes / (ms * 1e-3) / 1e9
+    achieved = bench.full_bytes / (ms_full * 1e-3) / 1e9
+    st = bench.st
+    res = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic",
+        config={"workload": "mixed 48-layer decode step B=32, T=32K, 39 SWA (W=128, 8kv) + 9 full (4kv) layers, "
+                            "64q, D=128, bf16, page 64, SWA ratio 0.1", "global_batch": st.batch,
+                "seq_len": st.seq_len, "layers": 48, "parallelism": "none (1 GPU)"},
+        tokens_per_s=round(st.batch / (ms * 1e-3), 1),
+        roofline=dict(kernel="swa_decode full layer (split-K + merge)", bound="hbm", achieved=round(achieved, 1),
+                      peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=traffic_from_profile("swa_decode_full_c4", ["decode_kernels.hip", "common.hpp"], 1),
+                      bytes_per_launch=bench.full_bytes, us_per_launch=round(ms_full * 1e3, 2),
+                      splits=bench.splits),
+    )
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -287,7 +499,12 @@ def main():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
     torch.cuda.set_device(0)
-    res = run_decode_workload(args, torch, swa, W)
+    if args.workload == "c3":
+        res = run_extend_workload(args, torch, swa, W)
+    elif args.workload == "c4":
+        res = run_mixed_workload(args, torch, swa, W)
+    else:
+        res = run_decode_workload(args, torch, swa, W)
     print(json.dumps(res), flush=True)
 
 

@@ -34,6 +34,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16_rne(lo)) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
 }
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+// For finite inputs it equals pack_bf16x2; NaN payloads are the hardware's.
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  f32x2v_t x = {lo, hi};
+  bf16x2v_t r = __builtin_convertvector(x, bf16x2v_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane r supplies the LDS
+// address of 4 consecutive 16-bit elements (row r of a 16 x 4 block M);
+// lane i receives M[i/4 + 4e][i%4] for e = 0..3.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t *lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t *)(const_cast<uint16_t *>(lds_ptr)));
+}
+
 // OCP e4m3fn encoder: round to nearest even, saturate finite overflow (and inf)
 // to +-448, NaN -> 0x7F.  Normal range: the binary32 word is rounded at the
 // 20-bit boundary (3 mantissa bits kept) and re-biased (127 - 7 = 120);

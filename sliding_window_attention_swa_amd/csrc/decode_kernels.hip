@@ -459,11 +459,23 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
 
   // ---- key source (window table or req_to_token row).  A window holds at
   // most W + 1 keys: only the last W + 1 entries are used.
-  const KeySource ks = key_source(p, b);
-  const int32_t n = ks.n < p.window + 1 ? ks.n : p.window + 1;
-  const int32_t *src = ks.src + (ks.n - n);
-  const int32_t nblk = (n + 15) >> 4;  // <= kWinWaves * MAXB for this instantiation
-
+  // In table mode the slots are first read speculatively at the offset a full
+  // window per request would have (b * (W + 1)), at the same time as the
+  // table offsets, which removes one dependent memory hop; they are re-read in
+  // the rare case the offsets disagree (a short request earlier in the batch).
+  int32_t sl[MAXB];
+  int64_t spec_base = 0;
+  if (p.indptr && p.capacity > 0) {
+    spec_base = static_cast<int64_t>(b) * (p.window + 1);
+#pragma unroll
+    for (int u = 0; u < MAXB; ++u) {
+      // keys past the window re-read its last entry (one row, cached)
+      const int32_t key = 16 * (w + kWinWaves * u) + kr;
+      int64_t idx = spec_base + (key < p.window ? key : p.window);
+      idx = idx < p.capacity ? idx : p.capacity - 1;
+      sl[u] = p.table[idx < 0 ? 0 : idx];
+    }
+  }
   // Q^T operand rows (head g*G + kr, dims 32lq..32lq+31).  Lanes of padding
   // heads (kr >= G) read a real head: their columns are never stored.
   const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
@@ -474,6 +486,12 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
   __builtin_amdgcn_sched_barrier(0);
 
+  const KeySource ks = key_source(p, b);
+  const int32_t n = ks.n < p.window + 1 ? ks.n : p.window + 1;
+  const int32_t *src = ks.src + (ks.n - n);
+  const int32_t nblk = (n + 15) >> 4;  // <= kWinWaves * MAXB for this instantiation
+  const bool spec_ok = p.indptr && p.capacity > 0 && src == p.table + spec_base;
+
   f32x4_t acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -482,17 +500,17 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * MAXB * 16 * kVRow;
 
   if (w < nblk) {  // wave-uniform: this wavefront owns at least one block
-    // All loads are unconditional (no control flow between them, so none of
-    // them waits for another): keys past the end re-read the wavefront's first
-    // key, and their scores are masked to -inf below.  The phases are fenced
-    // with scheduling barriers so that the compiler cannot pull arithmetic into
-    // the load phase (its in-order vmcnt waits would make later rows wait for
-    // earlier ones).
-    int32_t sl[MAXB];
+    // All row loads are unconditional (no control flow between them, so none
+    // of them waits for another); rows of keys past the end are masked out
+    // below.  The phases are fenced with scheduling barriers so that the
+    // compiler cannot pull arithmetic into the load phase (its in-order vmcnt
+    // waits would make later rows wait for earlier ones).
+    if (!spec_ok) {
 #pragma unroll
-    for (int u = 0; u < MAXB; ++u) {
-      const int32_t key = 16 * (w + kWinWaves * u) + kr;
-      sl[u] = src[key < n ? key : 16 * w];
+      for (int u = 0; u < MAXB; ++u) {
+        const int32_t key = 16 * (w + kWinWaves * u) + kr;
+        sl[u] = src[key < n ? key : 16 * w];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // every K row first, then every V row: the scores only wait for K
@@ -554,6 +572,10 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     // ---- V rows -> LDS (bf16, 264-byte rows), block u at rows 16u..16u+15
 #pragma unroll
     for (int u = 0; u < MAXB; ++u) {
+      if (16 * (w + kWinWaves * u) + kr >= n) {  // key past the end: its row may be anything
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) vraw[u][c] = make_uint4(0, 0, 0, 0);
+      }
       bf16x8_t vv[4];
       KvLoad<KV>::to_bf16(vraw[u], vv);
       uint2 *d = reinterpret_cast<uint2 *>(vt + (u * 16 + kr) * kVRow + 32 * lq);

@@ -15,7 +15,9 @@
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32
 //     accumulation; P is rounded to bf16 for the second product and never leaves
 //     registers (the first product's accumulator layout is the second's B
-//     operand layout); online softmax in base 2 over chunks of up to 9 blocks;
+//     operand layout); the V^T operand is read from a row-major LDS tile with
+//     gfx950's transposing ds_read_b64_tr_b16; online softmax in base 2 over
+//     chunks of up to 9 blocks, masks computed only on band-edge blocks;
 //   * tiles are numbered (request, kv head, query tile) and dealt to the 8 XCDs
 //     in contiguous runs, so the 9 tiles that share a K/V block run on one XCD
 //     and hit its L2.
@@ -29,7 +31,7 @@ constexpr int kNW = 4;       // wavefronts per workgroup
 constexpr int kTQ = 16;      // queries per tile
 constexpr int kKB = 9;       // key blocks (of 16) per chunk
 constexpr int kKRow = kD + 8;  // LDS K row: 272 bytes (16-byte aligned rows, 4-bank skew)
-constexpr int kVRow = kD + 4;  // LDS V row: 264 bytes (2-dword skew: conflict-free column reads)
+constexpr int kVRow = kD + 16;  // LDS V row: 288 bytes (8-bank skew: conflict-free transposed reads)
 
 struct ExtendParams {
   const uint16_t *q;
@@ -74,8 +76,125 @@ __device__ __forceinline__ int32_t new_count(const ExtendParams &p, int32_t b) {
   return n > 0 ? n : 0;
 }
 
+// Steady-state tile: 16 valid queries, band [i0 - W, i0 + 15] not clipped at
+// position 0, W = 16 * (NB - 1).  Then the band is exactly NB blocks of 16
+// keys (key offset k from i0 - W): block 0 is the band's lower edge (query kr
+// sees k >= kr), block NB-1 the diagonal (k <= W + kr), the rest are inside
+// the band for every query.  Compile-time structure, no per-key position math.
+template <int NB, int MB>
+__device__ __forceinline__ void tile_fast(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile,
+                                          const bf16x8_t (&qop)[MB][4], const int32_t *key_slots, int32_t g,
+                                          f32x4_t (&acc)[MB][8], float (&m_run)[MB], float (&l_run)[MB]) {
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  // ---- stage the NB blocks (16 threads per 256-byte row); all loads first
+  {
+    const int32_t piece = threadIdx.x & 15;
+    int32_t slot[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) slot[i] = key_slots[(threadIdx.x >> 4) + 16 * i];
+    int64_t off[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t sl = (slot[i] < 0 || slot[i] >= p.rows) ? 0 : static_cast<int64_t>(slot[i]);
+      off[i] = row_elem(sl, p.kv_heads, g, kD) + 8 * piece;
+    }
+    uint4 kreg[NB], vreg[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) kreg[i] = *reinterpret_cast<const uint4 *>(p.k + off[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) vreg[i] = *reinterpret_cast<const uint4 *>(p.v + off[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int32_t key = (threadIdx.x >> 4) + 16 * i;
+      *reinterpret_cast<uint4 *>(ktile + key * kKRow + 8 * piece) = kreg[i];
+      *reinterpret_cast<uint4 *>(vtile + key * kVRow + 8 * piece) = vreg[i];
+    }
+  }
+  __syncthreads();
+  // ---- S^T = K Q^T
+  f32x4_t sacc[MB][NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+    bf16x8_t kop[4];
+    const uint16_t *kp = ktile + (kb * 16 + kr) * kKRow + 32 * lq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 8 * c, 16);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      sacc[m][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sacc[m][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c], qop[m][c], sacc[m][kb], 0, 0, 0);
+    }
+  }
+  // ---- band edges: block 0 keeps k >= kr, block NB-1 keeps k <= W + kr
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int32_t k = 4 * lq + r;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (NB == 1) {
+        sacc[m][0][r] = (k == kr) ? sacc[m][0][r] : -INFINITY;
+      } else {
+        sacc[m][0][r] = (k >= kr) ? sacc[m][0][r] : -INFINITY;
+        sacc[m][NB - 1][r] = (k <= kr) ? sacc[m][NB - 1][r] : -INFINITY;
+      }
+    }
+  }
+  // ---- softmax (one chunk: no rescaling of acc needed)
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][kb][r]);
+    const float m_new = wave_max_q(mx) * p.scale2;  // finite: every query sees its own key
+    m_run[m] = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][kb][r], p.scale2, -m_new));
+        sacc[m][kb][r] = e;
+        ps += e;
+      }
+    l_run[m] = ps;
+  }
+  // ---- O^T = V^T P^T over block pairs; V^T via transposing LDS reads
+  const uint16_t *vrow = vtile + (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
+#pragma unroll
+  for (int u = 0; u < (NB + 1) / 2; ++u) {
+    constexpr int kLast = NB - 1;
+    const bool second = 2 * u + 1 < NB;  // compile-time after unrolling
+    const int kb1 = second ? 2 * u + 1 : kLast;
+    bf16x8_t pop[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][2 * u][0], sacc[m][2 * u][1]),
+                        pack_bf16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
+                        second ? pack_bf16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
+                        second ? pack_bf16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
+      __builtin_memcpy(&pop[m], u4, 16);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const i16x4_t lo = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * n);
+      i16x4_t hi = {0, 0, 0, 0};
+      if (second) hi = lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * n);
+      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], acc[m][n], 0, 0, 0);
+    }
+  }
+}
+
 template <int MB, bool OUT_BF16>
-__global__ void __launch_bounds__(kNW * 64) extend_kernel(ExtendParams p) {
+__global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
 
@@ -116,8 +235,8 @@ __global__ void __launch_bounds__(kNW * 64) extend_kernel(ExtendParams p) {
 
   // key position -> slot
   const int32_t *src = nullptr;
-  int64_t src_lo = 0, src_hi = 0;  // valid index range into src
-  int32_t pos_base = 0;            // position of src[0]
+  int64_t src_hi = 0;  // valid index range into src: [0, src_hi)
+  int32_t pos_base = 0;  // position of src[0]
   if (p.indptr) {
     int64_t lo = p.indptr[b], hi = p.indptr[b + 1];
     if (lo < 0) lo = 0;
@@ -133,19 +252,20 @@ __global__ void __launch_bounds__(kNW * 64) extend_kernel(ExtendParams p) {
     src_hi = p.r2t_stride;
   }
 
-  // ---- Q^T operands: query kr of the tile, heads w*MB + m, dims 32lq..32lq+31
+  // ---- Q^T operands: query kr of the tile, heads w*MB + m, dims 32lq..32lq+31.
+  // Rows past the request (last partial tile) and padding heads read a real
+  // row; their columns are never stored.
+  const bool qvalid = (qt * kTQ + kr) < n_new && static_cast<int64_t>(row0) + kr < p.total_q;
+  const int64_t qrow = qvalid ? static_cast<int64_t>(row0) + kr : static_cast<int64_t>(row0);
   bf16x8_t qop[MB][4];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    const int64_t qrow = static_cast<int64_t>(row0) + kr;
-    const bool ok = hh < G && (qt * kTQ + kr) < n_new && qrow < p.total_q;
-    uint4 raw[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    if (ok) {
-      const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + (qrow * p.q_heads + g * G + hh) * kD + 32 * lq);
+    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + (qrow * p.q_heads + g * G + (hh < G ? hh : 0)) * kD +
+                                                      32 * lq);
+    uint4 raw[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) raw[c] = qp[c];
-    }
+    for (int c = 0; c < 4; ++c) raw[c] = qp[c];
 #pragma unroll
     for (int c = 0; c < 4; ++c) __builtin_memcpy(&qop[m][c], &raw[c], 16);
   }
@@ -163,38 +283,57 @@ __global__ void __launch_bounds__(kNW * 64) extend_kernel(ExtendParams p) {
   }
   const int32_t qpos = i0 + kr;  // position of the query in this lane's column
 
+  // steady-state tile (see tile_fast): W = 128, 16 valid queries, band inside
+  // the request and inside its key source
+  const bool fast = W == 16 * (kKB - 1) && i0 - W >= 0 && qt * kTQ + kTQ <= n_new && i_last == i0 + kTQ - 1 &&
+                    static_cast<int64_t>(kj0) - pos_base >= 0 &&
+                    static_cast<int64_t>(kj0) - pos_base + 16 * kKB <= src_hi;
+  if (fast) {
+    tile_fast<kKB, MB>(p, ktile, vtile, qop, src + (kj0 - pos_base), g, acc, m_run, l_run);
+  } else
   for (int32_t c0 = 0; c0 < nkeys; c0 += kKB * 16) {
     const int32_t nbk = min(kKB, (nkeys - c0 + 15) / 16);
     const int32_t chunk_pos = kj0 + c0;  // position of key 0 of the chunk
 
-    // ---- stage K and V rows of the chunk in LDS (16 threads per 256-byte row)
+    // ---- stage K and V rows of the chunk in LDS (16 threads per 256-byte row).
+    // Every thread issues all its loads before writing any (no control flow
+    // between loads); keys past the band re-read the chunk's first key and are
+    // zeroed when written to LDS.
     __syncthreads();  // previous chunk fully consumed
     {
-      uint4 kreg[kKB], vreg[kKB];
       const int32_t piece = threadIdx.x & 15;
+      int32_t slot[kKB];
+      if (src_hi > 0) {  // workgroup-uniform
 #pragma unroll
-      for (int i = 0; i < kKB; ++i) {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-        const int32_t key = (threadIdx.x >> 4) + 16 * i;
-        if (i < nbk && c0 + key < nkeys) {
-          const int64_t si = static_cast<int64_t>(chunk_pos + key) - pos_base;
-          int32_t slot = (si >= src_lo && si < src_hi) ? src[si] : 0;
-          const int64_t sl = (slot < 0 || slot >= p.rows) ? 0 : static_cast<int64_t>(slot);
-          const int64_t off = row_elem(sl, p.kv_heads, g, kD) + 8 * piece;
-          kreg[i] = *reinterpret_cast<const uint4 *>(p.k + off);
-          vreg[i] = *reinterpret_cast<const uint4 *>(p.v + off);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kKB; ++i) {
-        if (i < nbk) {
+        for (int i = 0; i < kKB; ++i) {
           const int32_t key = (threadIdx.x >> 4) + 16 * i;
-          *reinterpret_cast<uint4 *>(ktile + key * kKRow + 8 * piece) = kreg[i];
-          uint2 *vd = reinterpret_cast<uint2 *>(vtile + key * kVRow + 8 * piece);
-          vd[0] = make_uint2(vreg[i].x, vreg[i].y);
-          vd[1] = make_uint2(vreg[i].z, vreg[i].w);
+          const bool kv_ok = i < nbk && c0 + key < nkeys;
+          const int64_t si = static_cast<int64_t>(chunk_pos + (kv_ok ? key : 0)) - pos_base;
+          slot[i] = src[si >= 0 && si < src_hi ? si : 0];
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kKB; ++i) slot[i] = 0;
+      }
+      int64_t off[kKB];
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) {
+        const int64_t sl = (slot[i] < 0 || slot[i] >= p.rows) ? 0 : static_cast<int64_t>(slot[i]);
+        off[i] = row_elem(sl, p.kv_heads, g, kD) + 8 * piece;
+      }
+      uint4 kreg[kKB], vreg[kKB];
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) kreg[i] = *reinterpret_cast<const uint4 *>(p.k + off[i]);
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) vreg[i] = *reinterpret_cast<const uint4 *>(p.v + off[i]);
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) {
+        const int32_t key = (threadIdx.x >> 4) + 16 * i;
+        const bool kv_ok = i < nbk && c0 + key < nkeys;
+        const uint4 kz = kv_ok ? kreg[i] : make_uint4(0, 0, 0, 0);
+        const uint4 vz = kv_ok ? vreg[i] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(ktile + key * kKRow + 8 * piece) = kz;
+        *reinterpret_cast<uint4 *>(vtile + key * kVRow + 8 * piece) = vz;
       }
     }
     __syncthreads();
@@ -218,72 +357,84 @@ __global__ void __launch_bounds__(kNW * 64) extend_kernel(ExtendParams p) {
       }
     }
 
-    // ---- mask, online softmax, P^T operands
-    bf16x8_t pop[MB][(kKB + 1) / 2];
+    // ---- mask: only blocks that touch the band's edges or the chunk end need
+    // a per-key test (a block is inside the band for every query of the tile
+    // when its last key <= i0 and its first key >= i_last - W).
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+      const int32_t j0 = chunk_pos + kb * 16;
+      const bool interior = kb < nbk && c0 + kb * 16 + 15 < nkeys && j0 + 15 <= i0 && (W < 0 || j0 >= i_last - W);
+      if (!interior) {  // workgroup-uniform
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t j = j0 + 4 * lq + r;
+          const bool ok = kb < nbk && (c0 + kb * 16 + 4 * lq + r) < nkeys && j <= qpos && (W < 0 || j >= qpos - W);
+#pragma unroll
+          for (int m = 0; m < MB; ++m) sacc[m][kb][r] = ok ? sacc[m][kb][r] : -INFINITY;
+        }
+      }
+    }
+    // ---- online softmax in base 2; the running max is kept in the scaled
+    // domain, scores are scaled inside the exponent (one fma per score)
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int32_t j = chunk_pos + kb * 16 + 4 * lq + r;
-          const bool ok = kb < nbk && (c0 + kb * 16 + 4 * lq + r) < nkeys && j <= qpos && (W < 0 || j >= qpos - W);
-          const float sv = ok ? sacc[m][kb][r] * p.scale2 : -INFINITY;
-          sacc[m][kb][r] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      }
-      mx = wave_max_q(mx);
-      const float m_new = fmaxf(m_run[m], mx);
-      const float alpha = exp2f(m_run[m] - m_new);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][kb][r]);
+      const float m_new = fmaxf(m_run[m], wave_max_q(mx) * p.scale2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[m] - m_new);
       m_run[m] = m_new;
       float ps = 0.f;
 #pragma unroll
-      for (int u = 0; u < (kKB + 1) / 2; ++u) {
-        float pv[8];
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pv[r] = exp2f(sacc[m][2 * u][r] - m_new);
-          pv[4 + r] = (2 * u + 1 < kKB) ? exp2f(sacc[m][(2 * u + 1) < kKB ? 2 * u + 1 : 0][r] - m_new) : 0.f;
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][kb][r], p.scale2, -m_new));
+          sacc[m][kb][r] = e;
+          ps += e;
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ps += pv[e];
-        uint32_t u4[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                          pack_bf16x2(pv[6], pv[7])};
-        __builtin_memcpy(&pop[m][u], u4, 16);
-      }
       l_run[m] = l_run[m] * alpha + ps;
+      if (c0 > 0) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) acc[m][n] *= alpha;
+        for (int n = 0; n < 8; ++n) acc[m][n] *= alpha;
+      }
     }
 
-    // ---- O^T += V^T P^T over block pairs (2u, 2u+1)
+    // ---- O^T += V^T P^T over block pairs (2u, 2u+1).  The V^T operand comes
+    // straight from the row-major tile with transposing LDS reads: lane (kr, lq)
+    // gets V[4lq + e][16n + kr], e = 0..3, of each block of the pair.
+    const uint16_t *vrow = vtile + (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
 #pragma unroll
     for (int u = 0; u < (kKB + 1) / 2; ++u) {
       if (2 * u < nbk) {
         const bool second = 2 * u + 1 < nbk;
+        bf16x8_t pop[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          const int kb1 = (2 * u + 1) < kKB ? 2 * u + 1 : 2 * u;
+          uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][2 * u][0], sacc[m][2 * u][1]),
+                            pack_bf16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
+                            second ? pack_bf16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
+                            second ? pack_bf16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
+          __builtin_memcpy(&pop[m], u4, 16);
+        }
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const uint16_t *col = vtile + 16 * n + kr;
-          uint16_t e8[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            e8[e] = col[(32 * u + 4 * lq + e) * kVRow];
-            e8[4 + e] = second ? col[(32 * u + 16 + 4 * lq + e) * kVRow] : static_cast<uint16_t>(0);
-          }
-          bf16x8_t vop;
-          __builtin_memcpy(&vop, e8, 16);
+          i16x4_t lo = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * n);
+          i16x4_t hi = {0, 0, 0, 0};
+          if (second) hi = lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * n);
+          bf16x8_t vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int m = 0; m < MB; ++m)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m][u], acc[m][n], 0, 0, 0);
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], acc[m][n], 0, 0, 0);
         }
       }
     }
   }
 
   // ---- finalize: sink once, normalise, store
-  const bool qvalid = (qt * kTQ + kr) < n_new && static_cast<int64_t>(row0) + kr < p.total_q;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
@@ -308,7 +459,7 @@ __global__ void __launch_bounds__(kNW * 64) extend_kernel(ExtendParams p) {
                   o3 = acc[m][n][3] * inv;
       if (OUT_BF16) {
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + obase + 16 * n) =
-            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            make_uint2(pack_bf16x2_hw(o0, o1), pack_bf16x2_hw(o2, o3));
       } else {
         *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + obase + 16 * n) = make_float4(o0, o1, o2, o3);
       }
