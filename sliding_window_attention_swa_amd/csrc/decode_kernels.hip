@@ -256,176 +256,219 @@ __device__ __forceinline__ void load_block(const DecodeParams &p, const KeySourc
   }
 }
 
-template <typename KV, int NW, bool OUT_BF16>
-__global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeParams p) {
-  // LDS: per-wave V tile [32 keys][kVRow] bf16, reused for the merge.
-  constexpr int kTileBytes = NW * 32 * kVRow * 2;
-  constexpr int kRedBytes = NW * kMaxG * kD * 4;
-  constexpr int kLdsBytes = kTileBytes > kRedBytes ? kTileBytes : kRedBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float red_m[NW * kMaxG];
-  __shared__ float red_l[NW * kMaxG];
+// Streaming kernel (long key ranges: full layers, split-K).  Each wavefront
+// walks the blocks w, w+4, w+8, ... of its workgroup's key range (the four
+// wavefronts read neighbouring blocks at the same time), two blocks per round,
+// in a two-stage software pipeline: the slots of round r+2 and the K/V rows of
+// round r+1 are in flight while round r is computed.  All loads are
+// unconditional (keys past the range re-read the range's first key and are
+// masked).  V goes through a per-wavefront LDS tile and is read back with the
+// transposing ds_read_b64_tr_b16, so P^T and V^T never need register shuffles.
+constexpr int kStreamWaves = 4;
+constexpr int kSVRow = kD + 16;  // LDS V row: 288 bytes (transposed reads are conflict-free)
+
+template <typename KV>
+struct StreamRound {
+  uint4 k[2][KvLoad<KV>::kVecs];
+  uint4 v[2][KvLoad<KV>::kVecs];
+};
+
+template <typename KV>
+__device__ __forceinline__ void stream_issue(const DecodeParams &p, const int32_t (&sl)[2], int32_t g, int32_t lq,
+                                             StreamRound<KV> &r) {
+  constexpr int kVec = KvLoad<KV>::kVecs;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t off = row_elem(safe_slot(sl[u], p.rows), p.kv_heads, g, kD) + 32 * lq;
+    const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.k) + off);
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) r.k[u][c] = kp[c];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t off = row_elem(safe_slot(sl[u], p.rows), p.kv_heads, g, kD) + 32 * lq;
+    const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.v) + off);
+#pragma unroll
+    for (int c = 0; c < kVec; ++c) r.v[u][c] = vp[c];
+  }
+}
+
+template <typename KV>
+__device__ __forceinline__ void stream_compute(const DecodeParams &p, const StreamRound<KV> &r, int32_t key_base0,
+                                               int32_t key_base1, int32_t k1, const bf16x8_t (&qop)[4], uint16_t *vt,
+                                               int32_t kr, int32_t lq, f32x4_t (&acc)[8], float &m_run,
+                                               float &l_run) {
+  // S^T for the two blocks (lane: keys 4lq..4lq+3 of head kr)
+  float sc[2][4];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x8_t kk[4];
+    KvLoad<KV>::to_bf16(r.k[u], kk);
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c], qop[c], sacc, 0, 0, 0);
+    const int32_t kb = u == 0 ? key_base0 : key_base1;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      sc[u][rr] = (kb + 4 * lq + rr < k1) ? sacc[rr] : -INFINITY;
+      mb = fmaxf(mb, sc[u][rr]);
+    }
+  }
+  // V rows -> LDS (bf16): block u at rows 16u..16u+15, lane's row kr, dims 32lq..
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x8_t vv[4];
+    KvLoad<KV>::to_bf16(r.v[u], vv);
+    const bool ok = (u == 0 ? key_base0 : key_base1) + kr < k1;
+    uint4 *d = reinterpret_cast<uint4 *>(vt + (u * 16 + kr) * kSVRow + 32 * lq);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 x;
+      __builtin_memcpy(&x, &vv[c], 16);
+      d[c] = ok ? x : make_uint4(0, 0, 0, 0);  // rows past the range may hold anything
+    }
+  }
+  // online softmax (base 2, scale folded into the exponent)
+  const float m_new = fmaxf(m_run, wave_max_q(mb) * p.scale2);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  m_run = m_new;
+  float pv[8];
+  float ps = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    pv[rr] = __builtin_amdgcn_exp2f(fmaf(sc[0][rr], p.scale2, -m_new));
+    pv[4 + rr] = __builtin_amdgcn_exp2f(fmaf(sc[1][rr], p.scale2, -m_new));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ps += pv[e];
+  l_run = l_run * alpha + ps;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+  bf16x8_t pop;
+  {
+    uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
+                      pack_bf16x2_hw(pv[6], pv[7])};
+    __builtin_memcpy(&pop, u4, 16);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
+  __builtin_amdgcn_wave_barrier();
+  const uint16_t *vrow = vt + (4 * lq + (kr >> 2)) * kSVRow + 4 * (kr & 3);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const i16x4_t lo = lds_read_tr16(vrow + 16 * c);
+    const i16x4_t hi = lds_read_tr16(vrow + 16 * kSVRow + 16 * c);
+    const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[c], 0, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next round rewrites the tile
+}
+
+// One workgroup per (key split, group of up to 4 kv heads, request): wavefront
+// w handles kv head 4 * blockIdx.y + w over the whole split, so the four
+// wavefronts together read whole token rows (all kv heads of a slot are
+// contiguous) and each page of the paged pool is visited once per split.
+// A wavefront owns its heads completely: it writes its split partial (or,
+// with one split, the final output with the sink) without any LDS merge.
+template <typename KV, bool OUT_BF16>
+__global__ void __launch_bounds__(kStreamWaves * 64, 2) decode_stream_kernel(DecodeParams p) {
+  constexpr int NW = kStreamWaves;
+  __shared__ __attribute__((aligned(16))) uint16_t vtiles[NW * 32 * kSVRow];
 
   const int32_t s = blockIdx.x;
-  const int32_t g = blockIdx.y;
   const int32_t b = blockIdx.z;
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
-  const int32_t kr = lane & 15;  // key row (A operand) / head column (B operand, accumulators)
-  const int32_t lq = lane >> 4;  // lane group
+  const int32_t g = blockIdx.y * NW + w;
+  if (g >= p.kv_heads) return;  // wave-uniform; no workgroup barrier below
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
   const int32_t G = p.group;
 
   const KeySource ks = key_source(p, b);
   int32_t k0, k1;
   split_range(ks.n, s, p.num_splits, &k0, &k1);
   const int32_t nblk = (k1 - k0 + 15) >> 4;
+  const int32_t nround = (nblk + 1) / 2;
 
-  // Q^T operand: head g*G + kr, dims 32*lq .. 32*lq+31 (zeros for padding heads).
-  bf16x8_t qop[4];
-  {
-    uint4 raw[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    if (kr < G) {
-      const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
-                                                        (static_cast<int64_t>(b) * p.q_heads + g * G + kr) * kD +
-                                                        32 * lq);
+  const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
+                                                    (static_cast<int64_t>(b) * p.q_heads + g * G +
+                                                     (kr < G ? kr : 0)) * kD + 32 * lq);
+  uint4 qraw[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) raw[c] = qp[c];
-    }
-    KvLoad<uint16_t>::to_bf16(raw, qop);
-  }
+  for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
 
-  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * 32 * kVRow;
   f32x4_t acc[8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig;
   float l_run = 0.f;
+  uint16_t *vt = vtiles + w * 32 * kSVRow;
 
-  // Pairs of this wave's blocks: (w + 2u*NW, w + (2u+1)*NW).
-  const int32_t npair = (nblk > w) ? ((nblk - w + NW - 1) / NW + 1) / 2 : 0;
-  BlockRegs<KV> cur0, cur1, nxt0, nxt1;
-  auto issue = [&](int32_t u, BlockRegs<KV> &r0, BlockRegs<KV> &r1) {
-    const int32_t t0 = w + 2 * u * NW;
-    const int32_t t1 = t0 + NW;
-    const int32_t key0 = k0 + 16 * t0 + kr;
-    const int32_t key1 = k0 + 16 * t1 + kr;
-    load_block<KV>(p, ks, key0, t0 < nblk && key0 < k1, g, lq, r0);
-    load_block<KV>(p, ks, key1, t1 < nblk && key1 < k1, g, lq, r1);
-  };
-  if (npair > 0) issue(0, cur0, cur1);
-
-  for (int32_t u = 0; u < npair; ++u) {
-    if (u + 1 < npair) issue(u + 1, nxt0, nxt1);
-    const int32_t t0 = w + 2 * u * NW;
-    const int32_t t1 = t0 + NW;
-
-    // ---- V rows -> LDS (bf16), this lane's key row, dims 32lq..32lq+31
-    {
-      bf16x8_t v0[4], v1[4];
-      KvLoad<KV>::to_bf16(cur0.v, v0);
-      KvLoad<KV>::to_bf16(cur1.v, v1);
-      uint2 *d0 = reinterpret_cast<uint2 *>(vt + kr * kVRow + 32 * lq);
-      uint2 *d1 = reinterpret_cast<uint2 *>(vt + (16 + kr) * kVRow + 32 * lq);
+  if (nround > 0) {
+    auto key_of = [&](int32_t j) { return k0 + 16 * j; };
+    auto slots_of = [&](int32_t round, int32_t (&sl)[2]) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint2 a[2], bb[2];
-        __builtin_memcpy(a, &v0[c], 16);
-        __builtin_memcpy(bb, &v1[c], 16);
-        d0[2 * c] = a[0];
-        d0[2 * c + 1] = a[1];
-        d1[2 * c] = bb[0];
-        d1[2 * c + 1] = bb[1];
+      for (int u = 0; u < 2; ++u) {
+        const int32_t key = key_of(2 * round + u) + kr;
+        sl[u] = ks.src[key < k1 ? key : k0];
       }
-    }
-
-    // ---- S^T = K Q^T for both blocks: lane holds keys 4lq..4lq+3 of head kr
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      bf16x8_t ka[4], kb[4];
-      KvLoad<KV>::to_bf16(cur0.k, ka);
-      KvLoad<KV>::to_bf16(cur1.k, kb);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qop[c], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[c], qop[c], s1, 0, 0, 0);
-      }
-    }
-    float sc[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int32_t ka = k0 + 16 * t0 + 4 * lq + r;
-      const int32_t kb = k0 + 16 * t1 + 4 * lq + r;
-      sc[r] = (t0 < nblk && ka < k1) ? s0[r] * p.scale2 : -INFINITY;
-      sc[4 + r] = (t1 < nblk && kb < k1) ? s1[r] * p.scale2 : -INFINITY;
-    }
-    float mb = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sc[e]);
-    mb = wave_max_q(mb);
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float ps = 0.f;
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = exp2f(sc[e] - m_new);
-      ps += pv[e];
-    }
-    l_run = l_run * alpha + ps;
-    bf16x8_t pop;
-    {
-      uint32_t u4[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                        pack_bf16x2(pv[6], pv[7])};
-      __builtin_memcpy(&pop, u4, 16);
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-
-    // V tile written by this wave only: wait for the LDS writes to land.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- O^T += V^T P^T: lane reads dim 16n + kr for keys {4lq..4lq+3} of each block
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint16_t *col = vt + 16 * n + kr;
-      uint16_t e8[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        e8[e] = col[(4 * lq + e) * kVRow];
-        e8[4 + e] = col[(16 + 4 * lq + e) * kVRow];
-      }
-      bf16x8_t vop;
-      __builtin_memcpy(&vop, e8, 16);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[n], 0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-
-    if (u + 1 < npair) {
-      cur0 = nxt0;
-      cur1 = nxt1;
+    };
+    bf16x8_t qop[4];
+    KvLoad<uint16_t>::to_bf16(qraw, qop);
+    int32_t slA[2], slB[2];
+    StreamRound<KV> A, B;
+    slots_of(0, slA);
+    if (nround > 1) slots_of(1, slB);
+    __builtin_amdgcn_sched_barrier(0);
+    stream_issue<KV>(p, slA, g, lq, A);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int32_t r = 0; r < nround; r += 2) {
+      if (r + 1 < nround) stream_issue<KV>(p, slB, g, lq, B);
+      if (r + 2 < nround) slots_of(r + 2, slA);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_compute<KV>(p, A, key_of(2 * r), key_of(2 * r + 1), k1, qop, vt, kr, lq, acc, m_run, l_run);
+      if (r + 1 >= nround) break;
+      if (r + 2 < nround) stream_issue<KV>(p, slA, g, lq, A);
+      if (r + 3 < nround) slots_of(r + 3, slB);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_compute<KV>(p, B, key_of(2 * r + 2), key_of(2 * r + 3), k1, qop, vt, kr, lq, acc, m_run, l_run);
     }
   }
   l_run = wave_sum_q(l_run);
-
-  // ---- merge the NW wavefronts through LDS
-  __syncthreads();  // every wave is done with its V tile
-  float *red_acc = reinterpret_cast<float *>(lds);
-  if (kr < G) {
+  if (kr >= G) return;
+  const int32_t h = g * G + kr;
+  if (p.num_splits == 1) {
+    float M = m_run, L = l_run, a = 1.f;
+    if (p.sinks) {
+      const float sig2 = p.sinks[h] * kLog2e;
+      const float Mn = fmaxf(M, sig2);
+      a = __builtin_amdgcn_exp2f(M - Mn);
+      L = L * a + __builtin_amdgcn_exp2f(sig2 - Mn);
+    }
+    const float inv = L > 0.f ? a * p.v_scale / L : 0.f;
+    const int64_t off = (static_cast<int64_t>(b) * p.q_heads + h) * kD + 4 * lq;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float o0 = acc[c][0] * inv, o1 = acc[c][1] * inv, o2 = acc[c][2] * inv, o3 = acc[c][3] * inv;
+      if (OUT_BF16)
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + off + 16 * c) =
+            make_uint2(pack_bf16x2_hw(o0, o1), pack_bf16x2_hw(o2, o3));
+      else
+        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + off + 16 * c) = make_float4(o0, o1, o2, o3);
+    }
+  } else {
+    const int64_t pi = (static_cast<int64_t>(b) * p.q_heads + h) * p.num_splits + s;
     if (lq == 0) {
-      red_m[w * kMaxG + kr] = m_run;
-      red_l[w * kMaxG + kr] = l_run;
+      p.ws_m[pi] = m_run;
+      p.ws_l[pi] = l_run;
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      float4 v = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-      *reinterpret_cast<float4 *>(red_acc + (w * G + kr) * kD + 16 * n + 4 * lq) = v;
-    }
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<float4 *>(p.ws_acc + pi * kD + 16 * c + 4 * lq) =
+          make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
   }
-  __syncthreads();
-  merge_waves_and_store<OUT_BF16>(p, NW, red_m, red_l, red_acc, b, g, s);
 }
 
 // --------------------------------------------------------------------------
@@ -745,12 +788,14 @@ hipError_t launch_window(const DecodeParams &p, dim3 grid, int window, bool out_
   return launch_window_b<KV, 4>(p, grid, out_bf16, stream);
 }
 
-template <typename KV, int NW>
-hipError_t launch_mfma(const DecodeParams &p, dim3 grid, bool out_bf16, hipStream_t stream) {
+template <typename KV>
+hipError_t launch_stream(const DecodeParams &p, dim3 grid0, bool out_bf16, hipStream_t stream) {
+  // grid: (splits, groups of kStreamWaves kv heads, requests)
+  const dim3 grid(grid0.x, (p.kv_heads + kStreamWaves - 1) / kStreamWaves, grid0.z);
   if (out_bf16)
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, NW, true>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_stream_kernel<KV, true>), grid, dim3(kStreamWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, NW, false>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_stream_kernel<KV, false>), grid, dim3(kStreamWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -805,9 +850,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     e = a.layer.dtype == SWA_BF16 ? launch_window<uint16_t>(p, grid, a.window, out_bf16, stream)
                                   : launch_window<uint8_t>(p, grid, a.window, out_bf16, stream);
   } else if (a.layer.dtype == SWA_BF16) {
-    e = launch_mfma<uint16_t, kDecodeWaves>(p, grid, out_bf16, stream);
+    e = launch_stream<uint16_t>(p, grid, out_bf16, stream);
   } else {
-    e = launch_mfma<uint8_t, kDecodeWaves>(p, grid, out_bf16, stream);
+    e = launch_stream<uint8_t>(p, grid, out_bf16, stream);
   }
   if (e != hipSuccess || a.num_splits == 1) return e;
   const dim3 mgrid(static_cast<uint32_t>(a.q_heads), static_cast<uint32_t>(a.idx.batch));
