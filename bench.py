@@ -192,6 +192,21 @@ def time_replays(torch, g, n):
     return start.elapsed_time(end) / n  # ms per replay
 
 
+def replay_percentiles(torch, g, n, per_replay):
+    """p10 / p50 / p90 of one replay's duration (ms), each replay bracketed by
+    its own pair of events on the stream the graph is replayed on, divided by
+    the `per_replay` launches it holds."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)]) / per_replay
+    return {k: round(float(np.percentile(d, q)) * 1e3, 3) for k, q in (("p10_us", 10), ("p50_us", 50), ("p90_us", 90))}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, single-threaded, on a bounded sample
 # ---------------------------------------------------------------------------
@@ -244,6 +259,7 @@ def run_decode_workload(args, torch, swa, W):
     g_dec = graph_of(torch, bench.dominant)
     dec_reps = max(10, args.steps // 2)
     ms_dec = time_replays(torch, g_dec, dec_reps) / layers
+    pct = replay_percentiles(torch, g_dec, dec_reps, layers)
     log(f"[bench] swa_decode {ms_dec * 1e3:.2f} us per launch")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     achieved = bench.decode_bytes / (ms_dec * 1e-3) / 1e9
@@ -259,7 +275,7 @@ def run_decode_workload(args, torch, swa, W):
         frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
         roofline=dict(kernel="swa_decode", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                       unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                      bytes_per_launch=bench.decode_bytes, us_per_launch=round(ms_dec * 1e3, 3)),
+                      bytes_per_launch=bench.decode_bytes, us_per_launch=round(ms_dec * 1e3, 3), **pct),
     )
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -370,6 +386,7 @@ def run_extend_workload(args, torch, swa, W):
     ms = time_replays(torch, g_step, args.steps)
     g_dom = graph_of(torch, bench.dominant)
     ms_ext = time_replays(torch, g_dom, max(5, args.steps)) / layers
+    pct = replay_percentiles(torch, g_dom, max(5, args.steps), layers)
     log(f"[bench] step {ms:.4f} ms, extend {ms_ext * 1e3:.2f} us")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     achieved = bench.extend_bytes / (ms_ext * 1e-3) / 1e9
@@ -389,7 +406,7 @@ def run_extend_workload(args, torch, swa, W):
                       frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=traffic_from_profile("swa_extend_c3", ["extend_kernels.hip", "common.hpp"], 1),
                       bytes_per_launch=bench.extend_bytes, flops_per_launch=bench.extend_flops,
-                      us_per_launch=round(ms_ext * 1e3, 3)),
+                      us_per_launch=round(ms_ext * 1e3, 3), **pct),
     )
     if not args.no_cpu_baseline:
         secs, rows = cpu_baseline_extend(wl)
@@ -459,6 +476,7 @@ def run_mixed_workload(args, torch, swa, W):
     ms = time_replays(torch, g_step, args.steps)
     g_dom = graph_of(torch, bench.dominant)
     ms_full = time_replays(torch, g_dom, max(3, args.steps // 2)) / 9
+    pct = replay_percentiles(torch, g_dom, max(3, args.steps // 2), 9)
     log(f"[bench] step {ms:.3f} ms, full-layer decode {ms_full * 1e3:.1f} us")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     achieved = bench.full_bytes / (ms_full * 1e-3) / 1e9
@@ -475,9 +493,23 @@ def run_mixed_workload(args, torch, swa, W):
                       peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=traffic_from_profile("swa_decode_full_c4", ["decode_kernels.hip", "common.hpp"], 1),
                       bytes_per_launch=bench.full_bytes, us_per_launch=round(ms_full * 1e3, 2),
-                      splits=bench.splits),
+                      splits=bench.splits, **pct),
     )
     return res
+
+
+def copy_probe(torch, reps=5):
+    """A plain elementwise kernel of known traffic (1 GiB read + 1 GiB written
+    per launch), run so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can
+    be scaled to bytes: factor = known bytes / counter bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return {"copy_probe": "torch.neg float32", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+            "launches": reps}
 
 
 def main():
@@ -487,6 +519,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a copy kernel of known size (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -499,6 +533,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        print(json.dumps(copy_probe(torch)), flush=True)
+        return
     if args.workload == "c3":
         res = run_extend_workload(args, torch, swa, W)
     elif args.workload == "c4":

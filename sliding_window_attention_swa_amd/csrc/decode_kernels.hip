@@ -9,15 +9,18 @@
 //   o_h = sum_j e^{s_j - m} v_j / (sum_j e^{s_j - m} + e^{sink_h - m})
 //
 // Work decomposition (MI355X-specific, not the pages' kernels):
-//   * one workgroup per (key split, kv head, request); the G query heads that
-//     share a kv head are computed together, so each K/V row is read from HBM
-//     exactly once per layer;
-//   * inside the workgroup the keys are dealt to NW wavefronts in 16-key
-//     blocks; each wavefront keeps a running (max, sum, acc) per head
-//     (online softmax in base 2) and the wavefronts are merged through LDS;
-//   * with several splits (full layers over long contexts) each workgroup
-//     writes its (max, sum, acc) partial and a merge kernel combines them; the
-//     sink enters exactly once, in the final merge.
+//   * the G query heads that share a kv head are always computed together, so
+//     each K/V row is read from HBM exactly once per layer;
+//   * window layers (one split): one workgroup per (kv head, request); its
+//     four wavefronts take 16-key blocks of the window, all loads in flight
+//     at once, and are merged through LDS;
+//   * full layers (split-K): one workgroup per (key split, four kv heads,
+//     request), one wavefront per kv head streaming its split with a two-deep
+//     load pipeline, so a workgroup reads whole token rows page by page; each
+//     wavefront writes its (max, sum, acc) partial and a merge kernel
+//     combines the splits;
+//   * online softmax in base 2; the sink enters exactly once, where the final
+//     normalisation happens.
 //
 // bf16 / e4m3 K/V path: S^T = K Q^T and O^T = V^T P^T on the CDNA4 matrix
 // cores (v_mfma_f32_16x16x32_bf16).  With keys as the M dimension of the
@@ -31,7 +34,7 @@
 // v_cvt_scalef32_pk_bf16_fp8; the per-tensor scales are folded into the logit
 // scale and the output.
 //
-// f32 path: plain VALU, one key row per wavefront step, two dims per lane.
+// f32 path: plain VALU; 16 keys per wavefront step, 4 lanes per key row.
 #include "common.hpp"
 
 namespace swa {
@@ -671,68 +674,170 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
 }
 
 // --------------------------------------------------------------------------
-// f32 VALU path (f32 q, f32 K/V): lane l owns dims 2l, 2l+1.
+// f32 VALU path (f32 q, f32 K/V).  A wavefront takes 16 keys at a time:
+// lane (key kr = lane / 4, quarter c = lane % 4) holds dims 32c..32c+31 of
+// that key's K and V rows, so a score needs 32 FMAs and a 4-lane sum.  The
+// chunk's probabilities and V rows go through this wavefront's LDS slice and
+// lane l then accumulates dims 2l, 2l+1 of every head.  The rows of the next
+// chunk are loaded (unconditionally: keys past the split re-read its first
+// row and get probability 0) while the current one is computed.
 // --------------------------------------------------------------------------
-template <int NW, bool OUT_BF16>
-__global__ void __launch_bounds__(NW * 64) decode_f32_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) float red_acc[NW * kMaxG * kD];
+constexpr int kF32Waves = 4;
+constexpr int kF32Chunk = 16;
+
+struct F32Rows {
+  float4 k[8], v[8];
+};
+
+__device__ __forceinline__ void f32_issue(const DecodeParams &p, int32_t slot, int32_t g, int32_t c, F32Rows &r) {
+  const int64_t off = row_elem(safe_slot(slot, p.rows), p.kv_heads, g, kD) + 32 * c;
+  const float4 *kp = reinterpret_cast<const float4 *>(static_cast<const float *>(p.k) + off);
+  const float4 *vp = reinterpret_cast<const float4 *>(static_cast<const float *>(p.v) + off);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.k[i] = kp[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.v[i] = vp[i];
+}
+
+template <int G, bool OUT_BF16>
+__global__ void __launch_bounds__(kF32Waves * 64) decode_f32_kernel(DecodeParams p) {
+  constexpr int NW = kF32Waves;
+  __shared__ __attribute__((aligned(16))) float q_lds[kMaxG * kD];
+  // per-wavefront V chunk during the loop; the cross-wavefront partials after it
+  __shared__ __attribute__((aligned(16))) float big[NW * kMaxG * kD];
+  __shared__ float p_lds[NW * kF32Chunk * kMaxG];
   __shared__ float red_m[NW * kMaxG];
   __shared__ float red_l[NW * kMaxG];
+  static_assert(NW * kF32Chunk * kD <= NW * kMaxG * kD, "V chunk must fit the partials buffer");
+
   const int32_t s = blockIdx.x;
   const int32_t g = blockIdx.y;
   const int32_t b = blockIdx.z;
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
-  const int32_t G = p.group;
+  const int32_t kr = lane >> 2;
+  const int32_t c = lane & 3;
 
   const KeySource ks = key_source(p, b);
   int32_t k0, k1;
   split_range(ks.n, s, p.num_splits, &k0, &k1);
 
-  float2 qv[kMaxG];
-  float m_run[kMaxG], l_run[kMaxG];
-  float2 acc[kMaxG];
+  float m_run[G], l_run[G];
+  float2 acc[G];
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh) {
-    qv[hh] = make_float2(0.f, 0.f);
-    if (hh < G)
-      qv[hh] = *reinterpret_cast<const float2 *>(static_cast<const float *>(p.q) +
-                                                 (static_cast<int64_t>(b) * p.q_heads + g * G + hh) * kD + 2 * lane);
+  for (int hh = 0; hh < G; ++hh) {
     m_run[hh] = kNegBig;
     l_run[hh] = 0.f;
     acc[hh] = make_float2(0.f, 0.f);
   }
-  const float *K = static_cast<const float *>(p.k);
-  const float *V = static_cast<const float *>(p.v);
-  for (int32_t key = k0 + w; key < k1; key += NW) {
-    const int64_t slot = safe_slot(ks.src[key], p.rows);
-    const int64_t off = row_elem(slot, p.kv_heads, g, kD) + 2 * lane;
-    const float2 kx = *reinterpret_cast<const float2 *>(K + off);
-    const float2 vx = *reinterpret_cast<const float2 *>(V + off);
+  float *vc = big + w * kF32Chunk * kD;
+  float *pc = p_lds + w * kF32Chunk * kMaxG;
+
+  auto chunk_base = [&](int32_t j) { return k0 + kF32Chunk * (w + NW * j); };
+  auto slot_of = [&](int32_t j) {
+    const int32_t key = chunk_base(j) + kr;
+    return ks.src[key < k1 ? key : k0];
+  };
+
+  // Slots run two chunks ahead of the rows, rows one chunk ahead of the
+  // arithmetic; the query rows are fetched while the first slots are in flight.
+  const bool any = chunk_base(0) < k1;  // wavefront-uniform; implies k0 < k1
+  int32_t sl0 = 0, sl1 = 0;
+  if (any) {
+    sl0 = slot_of(0);
+    sl1 = slot_of(1);
+  }
+  constexpr int kQVec = (G * kD / 4 + NW * 64 - 1) / (NW * 64);
+  float4 qr[kQVec];
+  const float4 *qsrc = reinterpret_cast<const float4 *>(static_cast<const float *>(p.q) +
+                                                        (static_cast<int64_t>(b) * p.q_heads + g * G) * kD);
 #pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
-      if (hh >= G) break;
-      const float sc = wave_sum_all(fmaf(qv[hh].x, kx.x, qv[hh].y * kx.y)) * p.scale2;
-      const float m_new = fmaxf(m_run[hh], sc);
-      const float alpha = exp2f(m_run[hh] - m_new);
-      const float pj = exp2f(sc - m_new);
-      m_run[hh] = m_new;
-      l_run[hh] = l_run[hh] * alpha + pj;
-      acc[hh].x = fmaf(pj, vx.x, acc[hh].x * alpha);
-      acc[hh].y = fmaf(pj, vx.y, acc[hh].y * alpha);
+  for (int i = 0; i < kQVec; ++i) {
+    const int32_t t = threadIdx.x + i * NW * 64;
+    if (t < G * kD / 4) qr[i] = qsrc[t];
+  }
+  F32Rows cur, nxt;
+  if (any) f32_issue(p, sl0, g, c, cur);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kQVec; ++i) {
+    const int32_t t = threadIdx.x + i * NW * 64;
+    if (t < G * kD / 4) reinterpret_cast<float4 *>(q_lds)[t] = qr[i];
+  }
+  __syncthreads();
+
+  if (any) {
+    for (int32_t j = 0; chunk_base(j) < k1; ++j) {
+      const bool more = chunk_base(j + 1) < k1;  // wavefront-uniform
+      if (more) {
+        f32_issue(p, sl1, g, c, nxt);
+        sl1 = slot_of(j + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const bool valid = chunk_base(j) + kr < k1;
+      // V chunk to LDS (row kr, dims 32c..32c+31)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) reinterpret_cast<float4 *>(vc + kr * kD + 32 * c)[i] = cur.v[i];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float4 *qh = reinterpret_cast<const float4 *>(q_lds + hh * kD + 32 * c);
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 qv = qh[i];
+          d0 = fmaf(qv.x, cur.k[i].x, d0);
+          d1 = fmaf(qv.y, cur.k[i].y, d1);
+          d0 = fmaf(qv.z, cur.k[i].z, d0);
+          d1 = fmaf(qv.w, cur.k[i].w, d1);
+        }
+        float dot = d0 + d1;
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        const float sc = valid ? dot * p.scale2 : -INFINITY;
+        float cm = sc;
+#pragma unroll
+        for (int o = 4; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+        const float m_new = fmaxf(m_run[hh], cm);
+        const float alpha = exp2f(m_run[hh] - m_new);
+        const float pj = exp2f(sc - m_new);
+        float ps = pj;
+#pragma unroll
+        for (int o = 4; o < 64; o <<= 1) ps += __shfl_xor(ps, o);
+        m_run[hh] = m_new;
+        l_run[hh] = l_run[hh] * alpha + ps;
+        acc[hh].x *= alpha;
+        acc[hh].y *= alpha;
+        if (c == 0) pc[kr * kMaxG + hh] = pj;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows and probabilities are in LDS
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+      for (int32_t r = 0; r < kF32Chunk; ++r) {
+        const float2 v2 = reinterpret_cast<const float2 *>(vc + r * kD)[lane];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float pr = pc[r * kMaxG + hh];
+          acc[hh].x = fmaf(pr, v2.x, acc[hh].x);
+          acc[hh].y = fmaf(pr, v2.y, acc[hh].y);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next chunk overwrites the slice
+      __builtin_amdgcn_wave_barrier();
+      if (!more) break;
+      cur = nxt;
     }
   }
+  __syncthreads();  // every wavefront is done with its V slice before `big` holds partials
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh) {
-    if (hh >= G) break;
+  for (int hh = 0; hh < G; ++hh) {
     if (lane == 0) {
       red_m[w * kMaxG + hh] = m_run[hh];
       red_l[w * kMaxG + hh] = l_run[hh];
     }
-    *reinterpret_cast<float2 *>(red_acc + (w * G + hh) * kD + 2 * lane) = acc[hh];
+    reinterpret_cast<float2 *>(big + (w * G + hh) * kD)[lane] = acc[hh];
   }
   __syncthreads();
-  merge_waves_and_store<OUT_BF16>(p, NW, red_m, red_l, red_acc, b, g, s);
+  merge_waves_and_store<OUT_BF16>(p, NW, red_m, red_l, big, b, g, s);
 }
 
 // --------------------------------------------------------------------------
@@ -768,6 +873,20 @@ __global__ void __launch_bounds__(kD) decode_merge_kernel(DecodeParams p) {
     static_cast<float *>(p.out)[off] = o;
 }
 
+template <bool OUT_BF16>
+hipError_t launch_f32(const DecodeParams &p, dim3 grid, hipStream_t stream) {
+  const dim3 block(kF32Waves * 64);
+  switch (p.group) {  // validated on the host: 1, 2, 4, 8 or 16
+    case 1: hipLaunchKernelGGL((decode_f32_kernel<1, OUT_BF16>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_f32_kernel<2, OUT_BF16>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_f32_kernel<4, OUT_BF16>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_f32_kernel<8, OUT_BF16>), grid, block, 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((decode_f32_kernel<16, OUT_BF16>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename KV, int MAXB>
 hipError_t launch_window_b(const DecodeParams &p, dim3 grid, bool out_bf16, hipStream_t stream) {
   if (out_bf16)
@@ -800,8 +919,6 @@ hipError_t launch_stream(const DecodeParams &p, dim3 grid0, bool out_bf16, hipSt
 }
 
 }  // namespace
-
-constexpr int kDecodeWaves = 4;
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.idx.batch == 0) return hipSuccess;
@@ -840,11 +957,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
                   static_cast<uint32_t>(a.idx.batch));
   hipError_t e;
   if (a.layer.dtype == SWA_F32) {
-    if (out_bf16)
-      hipLaunchKernelGGL((decode_f32_kernel<kDecodeWaves, true>), grid, dim3(kDecodeWaves * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_f32_kernel<kDecodeWaves, false>), grid, dim3(kDecodeWaves * 64), 0, stream, p);
-    e = hipGetLastError();
+    e = out_bf16 ? launch_f32<true>(p, grid, stream) : launch_f32<false>(p, grid, stream);
   } else if (a.num_splits == 1 && a.window >= 0 && a.window < 16 * kWinWaves * 4) {
     // SWA layer: the whole window in flight at once (up to 4 blocks per wavefront)
     e = a.layer.dtype == SWA_BF16 ? launch_window<uint16_t>(p, grid, a.window, out_bf16, stream)

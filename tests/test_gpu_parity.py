@@ -173,6 +173,8 @@ DECODE_CASES = {
     # name: (seq_lens, q_heads, kv_heads, window, page, q_dtype, kv_dtype, sinks)
     "f32_g1": ([1, 100, 700], 4, 4, 128, 1, "f32", "f32", True),
     "f32_g4_w3": ([1, 5, 64, 300], 8, 2, 3, 4, "f32", "f32", True),
+    "f32_g8": ([1, 33, 129, 400], 16, 2, 128, 16, "f32", "f32", True),
+    "f32_g16_w20": ([2, 19, 250], 32, 2, 20, 4, "f32", "f32", False),
     "bf16_g8": ([1, 2, 129, 130, 1000], 16, 2, 128, 16, "bf16", "bf16", True),
     "bf16_g8_nosink": ([1, 17, 200, 2000], 16, 2, 128, 16, "bf16", "bf16", False),
     "bf16_g1": ([3, 150, 999], 4, 4, 128, 16, "bf16", "bf16", True),
@@ -211,6 +213,7 @@ FULL_CASES = {
     "bf16_full_g8": ([1, 129, 2500], 16, 2, "bf16", "bf16"),
     "e4m3_full_g8": ([2, 777, 2000], 16, 2, "bf16", "e4m3"),
     "f32_full_g2": ([1, 64, 900], 4, 2, "f32", "f32"),
+    "f32_full_g16": ([3, 200, 1100], 32, 2, "f32", "f32"),
 }
 
 
