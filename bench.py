@@ -263,7 +263,7 @@ def run_decode_workload(args, torch, swa, W):
     log(f"[bench] swa_decode {ms_dec * 1e3:.2f} us per launch")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     achieved = bench.decode_bytes / (ms_dec * 1e-3) / 1e9
-    traffic = traffic_from_profile(f"swa_decode_{name}", ["decode_kernels.hip", "common.hpp"], 1)
+    traffic = traffic_from_profile(f"swa_decode_{name}", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1)
     res = dict(
         metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
@@ -404,7 +404,7 @@ def run_extend_workload(args, torch, swa, W):
                                            / 1e3), 1),
         roofline=dict(kernel="swa_extend", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4),
-                      traffic=traffic_from_profile("swa_extend_c3", ["extend_kernels.hip", "common.hpp"], 1),
+                      traffic=traffic_from_profile("swa_extend_c3", ["extend_kernels.hip", "common.hpp", "api.cpp"], 1),
                       bytes_per_launch=bench.extend_bytes, flops_per_launch=bench.extend_flops,
                       us_per_launch=round(ms_ext * 1e3, 3), **pct),
     )
@@ -491,7 +491,7 @@ def run_mixed_workload(args, torch, swa, W):
         tokens_per_s=round(st.batch / (ms * 1e-3), 1),
         roofline=dict(kernel="swa_decode full layer (split-K + merge)", bound="hbm", achieved=round(achieved, 1),
                       peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                      traffic=traffic_from_profile("swa_decode_full_c4", ["decode_kernels.hip", "common.hpp"], 1),
+                      traffic=traffic_from_profile("swa_decode_full_c4", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1),
                       bytes_per_launch=bench.full_bytes, us_per_launch=round(ms_full * 1e3, 2),
                       splits=bench.splits, **pct),
     )

@@ -10,9 +10,11 @@
 namespace {
 
 constexpr int32_t kHeadDim = 128;
-// gfx950 (MI355X) has 256 compute units; split planning targets ~8
-// workgroups per CU for long full-attention contexts.
-constexpr int64_t kTargetWorkgroups = 2048;
+// gfx950 (MI355X) has 256 compute units.  A full-layer split is streamed by
+// one wavefront per (request, kv head, split); planning targets about four such
+// streams per CU: more streams only add outstanding requests to a path whose
+// limit is address translation and DRAM, not issue slots.
+constexpr int64_t kTargetStreams = 1024;
 constexpr int64_t kMinKeysPerSplit = 512;
 constexpr int32_t kMaxSplits = 1024;
 
@@ -121,7 +123,7 @@ swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, i
   if (!valid_group(q_heads, kv_heads)) return SWA_E_SHAPE;
   int64_t splits = 1;
   if (window < 0 && batch > 0) {
-    const int64_t by_fill = (kTargetWorkgroups + static_cast<int64_t>(batch) * kv_heads - 1) /
+    const int64_t by_fill = (kTargetStreams + static_cast<int64_t>(batch) * kv_heads - 1) /
                             (static_cast<int64_t>(batch) * kv_heads);
     const int64_t by_len = (max_seq_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
     splits = by_fill < by_len ? by_fill : by_len;

@@ -375,7 +375,7 @@ __device__ __forceinline__ void stream_compute(const DecodeParams &p, const Stre
 // A wavefront owns its heads completely: it writes its split partial (or,
 // with one split, the final output with the sink) without any LDS merge.
 template <typename KV, bool OUT_BF16>
-__global__ void __launch_bounds__(kStreamWaves * 64, 2) decode_stream_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kStreamWaves * 64, 1) decode_stream_kernel(DecodeParams p) {
   constexpr int NW = kStreamWaves;
   __shared__ __attribute__((aligned(16))) uint16_t vtiles[NW * 32 * kSVRow];
 
