@@ -203,6 +203,48 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
                         int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
                         void *out, int32_t out_dtype, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Validation (debugging aid; SYNCHRONOUS: waits for `stream`).  Counts the
+ * index data that the kernels above silently absorb, per the contracts of
+ * [SWA] 双池与映射表 and 运行时 (a live window never holds a tombstone: eviction
+ * frees only positions that left the window) and [POOLS] 一重映射, 二重映射
+ * and 释放 (indices stay inside their tables; a slot is handed out once, page
+ * 0 being the shared sink of padded writes).
+ *
+ * Window part (idx->batch requests): request b is bad when req_pool_idx[b]
+ * is outside [0, r2t_rows), seq_lens[b] outside [0, r2t_stride] or, with
+ * prefix_lens, prefix_lens[b] outside [0, seq_lens[b]]; its positions are then
+ * skipped.  Otherwise every position of its window (the ones swa_translate_
+ * window would emit for the same window and prefix_lens) is classified:
+ *   full_out_of_range  with a map: req_to_token entry outside [-1, map_len-1)
+ *   tombstones         SWA slot 0 (with a map) / full slot 0 (without)
+ *   sentinels          SWA slot -1 (with a map)
+ *   slot_out_of_range  any other slot outside [0, pool_rows)
+ * Store part (n_store locs, may be 0 / NULL): locs outside [0, pool_rows), and
+ * repeats of a loc outside page 0 (each occurrence after the first counts).
+ * pool_rows: rows of the pool the window and the locs address (the SWA pool
+ * with a map, the full pool without).
+ * workspace: device, at least swa_validate_workspace_bytes(pool_rows) bytes,
+ * 16-byte aligned; its contents are overwritten.  report: [host].
+ * Returns SWA_E_ARG for null / negative arguments or page_size < 1. */
+typedef struct swa_validate_report {
+  int64_t bad_requests;
+  int64_t positions;
+  int64_t full_out_of_range;
+  int64_t tombstones;
+  int64_t sentinels;
+  int64_t slot_out_of_range;
+  int64_t store_locs;
+  int64_t store_out_of_range;
+  int64_t store_duplicates;
+} swa_validate_report_t;
+
+size_t swa_validate_workspace_bytes(int64_t pool_rows);
+
+swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
+                          const int64_t *store_loc, int64_t n_store, void *workspace, size_t workspace_bytes,
+                          swa_validate_report_t *report, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *swa_status_string(swa_status_t status);
 

@@ -11,6 +11,7 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   translate_loc       pinned: sentinel/tombstone invariants + page-level rebuild
   window_table        pinned: page-level rebuild (slot = page * P + offset)
   kv_store            pinned: round trip and untouched-row invariants
+  validate            pinned: hand-counted violations of a hand-built batch
   attention           pinned: full-causal reduction, plain-softmax reduction,
                       pure-Python brute force, W=0 and identical-key closed
                       forms, GQA expansion, pair-count ratio ~ 2W/T.
@@ -32,6 +33,7 @@ from .swa_oracle import (  # noqa: F401
     pool_config,
     scored_pairs,
     translate_loc,
+    validate,
     window_range,
     window_table,
 )

@@ -282,6 +282,71 @@ def extend(q, q_dtype, qo_indptr, prefix_lens, pool_k, pool_v, pool_dtype, req_t
 
 
 # ---------------------------------------------------------------------------
+# Index-data contracts, counted rather than raised.  [SWA] 双池与映射表 and
+# 运行时: a live window never holds a tombstone (eviction frees only positions
+# that left the window) and the mapping ends in the -1 sentinel that a -1 loc
+# reads; [POOLS] 一重映射 and 二重映射: indices stay inside their tables and
+# page 0 is the shared sink of padded writes; 释放: a slot is handed out once.
+# ---------------------------------------------------------------------------
+
+VALIDATE_FIELDS = ("bad_requests", "positions", "full_out_of_range", "tombstones", "sentinels",
+                   "slot_out_of_range", "store_locs", "store_out_of_range", "store_duplicates")
+
+
+def validate(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, pool_rows, page_size,
+             prefix_lens=None, store_loc=None):
+    """Counts of violations in a batch's index data.
+
+    A request is bad when its req_to_token row, its length or its prefix lies
+    outside its table; its window is then skipped.  Each window position (the
+    positions window_range gives) is classified once: a full slot outside the
+    mapping (with a mapping), a tombstone (slot 0), the sentinel (slot -1) or
+    another slot outside [0, pool_rows).  Store locations: outside
+    [0, pool_rows), or a repeat of a location outside page 0."""
+    r2t = np.asarray(req_to_token)
+    n_rows, stride = r2t.shape
+    c = dict.fromkeys(VALIDATE_FIELDS, 0)
+    for b in range(len(seq_lens)):
+        row, n = int(req_pool_idx[b]), int(seq_lens[b])
+        pre = n - 1 if prefix_lens is None else int(prefix_lens[b])
+        if not (0 <= row < n_rows) or not (0 <= n <= stride) or (prefix_lens is not None and not 0 <= pre <= n):
+            c["bad_requests"] += 1
+            continue
+        if n == 0:
+            continue
+        lo = 0 if window < 0 else max(0, pre - window)
+        for j in range(lo, n):
+            c["positions"] += 1
+            full = int(r2t[row, j])
+            if full_to_swa is not None:
+                if not -1 <= full < len(full_to_swa) - 1:
+                    c["full_out_of_range"] += 1
+                    continue
+                slot = int(full_to_swa[full])  # full = -1 reads the trailing sentinel entry
+                if slot == 0:
+                    c["tombstones"] += 1
+                elif slot == -1:
+                    c["sentinels"] += 1
+                elif not 0 <= slot < pool_rows:
+                    c["slot_out_of_range"] += 1
+            elif full == 0:
+                c["tombstones"] += 1
+            elif not 0 <= full < pool_rows:
+                c["slot_out_of_range"] += 1
+    if store_loc is not None:
+        seen = set()
+        for x in (int(v) for v in store_loc):
+            c["store_locs"] += 1
+            if not 0 <= x < pool_rows:
+                c["store_out_of_range"] += 1
+            elif x >= page_size:
+                if x in seen:
+                    c["store_duplicates"] += 1
+                seen.add(x)
+    return c
+
+
+# ---------------------------------------------------------------------------
 # Cost model.  [SWA] 问题: causal full attention scores about T^2/2 pairs, SWA
 # a fixed window per query; the ratio is about 2W/T.
 # ---------------------------------------------------------------------------

@@ -29,7 +29,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["api.cpp", "index_kernels.hip", "store_kernels.hip", "decode_kernels.hip", "extend_kernels.hip"]
+SOURCES = ["api.cpp", "index_kernels.hip", "store_kernels.hip", "decode_kernels.hip", "extend_kernels.hip",
+           "validate_kernels.hip"]
 
 
 def hipcc() -> str:

@@ -216,6 +216,44 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
   return from_hip(swa::launch_extend(a, stream));
 }
 
+// Workspace of swa_validate: 16 int64 counters, then one bit per pool row.
+constexpr int64_t kValidateCounterBytes = 16 * sizeof(int64_t);
+
+size_t swa_validate_workspace_bytes(int64_t pool_rows) {
+  if (pool_rows < 0) return 0;
+  return static_cast<size_t>(kValidateCounterBytes + (pool_rows + 31) / 32 * 4);
+}
+
+swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
+                          const int64_t *store_loc, int64_t n_store, void *workspace, size_t workspace_bytes,
+                          swa_validate_report_t *report, hipStream_t stream) {
+  if (!report || !idx || idx->batch < 0 || window < -1 || pool_rows < 0 || n_store < 0) return SWA_E_ARG;
+  if (idx->page_size < 1) return SWA_E_ARG;
+  swa_status_t st = check_index(idx, true);
+  if (st != SWA_OK) return st;
+  if (n_store > 0 && !store_loc) return SWA_E_ARG;
+  if (!workspace || !aligned16(workspace)) return SWA_E_WORKSPACE;
+  const size_t need = n_store > 0 ? swa_validate_workspace_bytes(pool_rows) : kValidateCounterBytes;
+  if (workspace_bytes < need) return SWA_E_WORKSPACE;
+  hipError_t e = swa::launch_validate(*idx, window, prefix_lens, pool_rows, store_loc, n_store, workspace,
+                                      kValidateCounterBytes, stream);
+  if (e != hipSuccess) return SWA_E_HIP;
+  int64_t c[16];
+  e = hipMemcpyAsync(c, workspace, sizeof(c), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return SWA_E_HIP;
+  report->bad_requests = c[0];
+  report->positions = c[1];
+  report->full_out_of_range = c[2];
+  report->tombstones = c[3];
+  report->sentinels = c[4];
+  report->slot_out_of_range = c[5];
+  report->store_locs = c[6];
+  report->store_out_of_range = c[7];
+  report->store_duplicates = c[8];
+  return SWA_OK;
+}
+
 const char *swa_status_string(swa_status_t status) {
   switch (status) {
     case SWA_OK: return "ok";

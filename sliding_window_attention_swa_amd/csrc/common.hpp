@@ -110,6 +110,10 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
+                           const int64_t *store_loc, int64_t n_store, void *workspace, int64_t counters_bytes,
+                           hipStream_t stream);
+
 struct ExtendArgs {
   const void *q;
   int32_t q_heads;

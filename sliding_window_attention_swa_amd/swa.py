@@ -25,7 +25,7 @@ SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/swa.h declares
 EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
-           "swa_decode", "swa_extend", "swa_status_string")
+           "swa_decode", "swa_extend", "swa_validate_workspace_bytes", "swa_validate", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -55,6 +55,14 @@ class IndexStruct(ctypes.Structure):
                 ("map_len", ctypes.c_int64), ("batch", ctypes.c_int32), ("page_size", ctypes.c_int32)]
 
 
+VALIDATE_FIELDS = ("bad_requests", "positions", "full_out_of_range", "tombstones", "sentinels", "slot_out_of_range",
+                   "store_locs", "store_out_of_range", "store_duplicates")
+
+
+class ValidateReportStruct(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int64) for f in VALIDATE_FIELDS]
+
+
 _i32, _i64, _f32, _f64, _p, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p,
                                    ctypes.c_size_t)
 _sig = {
@@ -68,6 +76,9 @@ _sig = {
                           _i32, _p, _f32, _p, _i32, _i32, _p, _sz, _p]),
     "swa_extend": (_i32, [_p, _i32, _i32, _p, _p, _i64, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct),
                           _p, _p, _i64, _i32, _p, _f32, _p, _i32, _p]),
+    "swa_validate_workspace_bytes": (_sz, [_i64]),
+    "swa_validate": (_i32, [ctypes.POINTER(IndexStruct), _i32, _p, _i64, _p, _i64, _p, _sz,
+                            ctypes.POINTER(ValidateReportStruct), _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -233,3 +244,20 @@ def swa_extend(q: torch.Tensor, qo_indptr: torch.Tensor, prefix_lens: torch.Tens
                           0 if slot_table is None else slot_table.numel(), window,
                           _ptr(sinks, torch.float32, "sinks"), scale, _ptr(out, name="out"), dtype_code(out),
                           _stream(stream)), "swa_extend")
+
+
+def swa_validate(index: IndexTables, window: int, pool_rows: int, prefix_lens: Optional[torch.Tensor] = None,
+                 store_loc: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 use_map: bool = True, stream=None) -> dict:
+    """Counts of contract violations in the batch's index data (synchronous).
+    The workspace is allocated here when not given."""
+    if workspace is None:
+        nbytes = lib.swa_validate_workspace_bytes(pool_rows)
+        workspace = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.int32, device=index.seq_lens.device)
+    rep = ValidateReportStruct()
+    ix = index.struct(with_map=use_map)
+    _check(lib.swa_validate(ctypes.byref(ix), window, _ptr(prefix_lens, torch.int32, "prefix_lens"), pool_rows,
+                            _ptr(store_loc, torch.int64, "store_loc"), 0 if store_loc is None else store_loc.numel(),
+                            _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                            ctypes.byref(rep), _stream(stream)), "swa_validate")
+    return {f: getattr(rep, f) for f in VALIDATE_FIELDS}

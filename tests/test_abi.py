@@ -163,3 +163,27 @@ def test_binding_rejects_host_tensors(swa):
     with pytest.raises(ValueError):
         swa.swa_translate_loc(a, torch.zeros(10, dtype=torch.int64), torch.zeros(4, dtype=torch.int64))
 
+
+
+def test_validate_argument_errors(swa):
+    lib, E = swa.lib, swa
+    ix = index(swa)
+    rep = swa.ValidateReportStruct()
+    need = lib.swa_validate_workspace_bytes(1000)
+    assert need == 128 + (1000 + 31) // 32 * 4
+    assert lib.swa_validate_workspace_bytes(-1) == 0
+
+    def val(ix=ix, window=128, pre=None, rows=1000, loc=FAKE, n=8, ws=FAKE, ws_bytes=need, report=rep):
+        return lib.swa_validate(ctypes.byref(ix), window, pre, rows, loc, n, ws, ws_bytes,
+                                None if report is None else ctypes.byref(report), None)
+
+    assert val(report=None) == E.SWA_E_ARG
+    assert val(window=-2) == E.SWA_E_ARG
+    assert val(rows=-1) == E.SWA_E_ARG
+    assert val(n=-1) == E.SWA_E_ARG
+    assert val(loc=None) == E.SWA_E_ARG                       # locs counted but not given
+    assert val(ws=None) == E.SWA_E_WORKSPACE
+    assert val(ws=FAKE + 8) == E.SWA_E_WORKSPACE              # misaligned
+    assert val(ws_bytes=need - 4) == E.SWA_E_WORKSPACE
+    no_page = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, FAKE, 50, 2, 0)
+    assert val(ix=no_page) == E.SWA_E_ARG

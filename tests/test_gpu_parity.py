@@ -289,6 +289,128 @@ def test_decode_c5_full_size():
     assert np.array_equal(dw.k[torch.from_numpy(loc).cuda()].cpu().numpy(), want)
 
 
+def _c4_oracle_layer(st, ly, q, k, v, reqs):
+    """Oracle output of one C4 layer for the requests `reqs` (all q heads),
+    from host copies of only the pool rows those requests reference."""
+    r2t, rows = st.req_to_token, st.req_pool_idx
+    T = int(st.seq_lens[0])
+    if ly["kind"] == "full":
+        used = np.concatenate([r2t[rows[b], :T] for b in reqs]).astype(np.int64)
+        mapping, window = None, -1
+    else:
+        used = np.concatenate([O.translate_loc(r2t[rows[b], T - 129:T], st.full_to_swa) for b in reqs])
+        mapping, window = st.full_to_swa, 128
+    used = np.unique(used)
+    idx = torch.from_numpy(used).cuda()
+    H, D = k.shape[1], k.shape[2]
+    pk = WL.SparsePool(k.shape[0], H, D, "bf16", used, device_to_bits(k[idx]))
+    pv = WL.SparsePool(v.shape[0], H, D, "bf16", used, device_to_bits(v[idx]))
+    only = [(int(b), h) for b in reqs for h in range(st.q_heads)]
+    return O.decode(device_to_bits(q), "bf16", pk, pv, "bf16", r2t, rows, st.seq_lens, mapping, window, None,
+                    only=only)
+
+
+def test_mixed_step_c4_full_size_sampled():
+    """C4 at full size: the first full layer (W = -1, 4 kv heads, 32K keys,
+    split-K as planned for the step) and the first SWA layer (W = 128, 8 kv
+    heads, keys through the step's shared window table), against the oracle
+    on sampled requests (every q head)."""
+    from sliding_window_attention_swa_amd import swa
+    st = WL.c4_mixed_step()
+    B, Hq, D, T = st.batch, st.q_heads, st.head_dim, int(st.seq_lens[0])
+    say("mixed step c4 (B=32, T=32K): one full and one SWA layer — sampled requests")
+    index = swa.IndexTables(torch.from_numpy(st.req_to_token).cuda(), torch.from_numpy(st.req_pool_idx).cuda(),
+                            torch.from_numpy(st.seq_lens).cuda(), torch.from_numpy(st.full_to_swa).cuda(),
+                            st.page_size)
+    table = torch.empty(B * 129, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(index, 128, table, indptr)
+    reqs = [0, 13, 31]
+    full = next(ly for ly in st.layers if ly["kind"] == "full")
+    swl = next(ly for ly in st.layers if ly["kind"] == "swa")
+    for ly in (full, swl):
+        q, k, v = WL.c4_layer_tensors(st, ly)
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        if ly["kind"] == "full":
+            splits, ws_bytes = swa.swa_decode_plan(B, Hq, ly["kv_heads"], D, -1, T)
+            assert splits > 1
+            ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+            swa.swa_decode(q, swa.KvLayer(k, v), index, -1, out, num_splits=splits, workspace=ws, use_map=False)
+        else:
+            swa.swa_decode(q, swa.KvLayer(k, v), index, 128, out, slot_table=table, table_indptr=indptr)
+        torch.cuda.synchronize()
+        ref = _c4_oracle_layer(st, ly, q, k, v, reqs)
+        check(out, ref, TOL["bf16"], f"c4 layer {ly['id']} ({ly['kind']})")
+        del q, k, v
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# validate (debug report): counts equal the oracle's, exactly
+# ---------------------------------------------------------------------------
+
+def _index(r2t, rows, lens, mapping, page):
+    from sliding_window_attention_swa_amd import swa
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return swa.IndexTables(dev(r2t), dev(rows), dev(lens), None if mapping is None else dev(mapping), page)
+
+
+def test_validate_hand_built_batch():
+    from sliding_window_attention_swa_amd import swa
+    from test_oracle_pins import EXTEND_PREFIX, HAND_COUNTS, hand_built_batch
+    mapping, r2t, rows, lens, store = hand_built_batch()
+    say("validate hand-built batch (decode / extend / full layer)")
+    ix = _index(r2t, rows, lens, mapping, 2)
+    got = swa.swa_validate(ix, 2, 6, store_loc=torch.from_numpy(store).cuda())
+    assert got == HAND_COUNTS["decode"]
+    got = swa.swa_validate(ix, 2, 6, prefix_lens=torch.from_numpy(EXTEND_PREFIX).cuda())
+    assert got == HAND_COUNTS["extend"]
+    got = swa.swa_validate(ix, -1, 10, use_map=False)
+    assert got == HAND_COUNTS["full"]
+
+
+def test_validate_planted_violations():
+    """A generated decode batch, then tombstones, sentinels, stray indices, a
+    bad request and repeated store locations planted into its index data."""
+    from sliding_window_attention_swa_amd import swa
+    wl = WL.decode_workload("validate", 31, [1, 20, 77, 300, 301, 5], 8, 2, 16, 4, "bf16", "bf16",
+                            with_store=True, live_margin=3)
+    rng = np.random.default_rng(9)
+    r2t, mapping = wl.req_to_token.copy(), wl.full_to_swa.copy()
+    rows, lens = wl.req_pool_idx.copy(), wl.seq_lens.astype(np.int32).copy()
+    pool_rows, P = wl.pool_k.shape[0], wl.page_size
+    loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+    say("validate: clean batch, then planted violations")
+    clean = swa.swa_validate(_index(r2t, rows, lens, mapping, P), wl.window, pool_rows,
+                             store_loc=torch.from_numpy(loc).cuda())
+    assert clean == O.validate(r2t, rows, lens, mapping, wl.window, pool_rows, P, store_loc=loc)
+    assert clean["tombstones"] == clean["sentinels"] == clean["store_duplicates"] == 0
+    # plant: window positions of request 3 (300 tokens) -> tombstone / sentinel / past the pool
+    r3 = rows[3]
+    fulls = r2t[r3, 300 - 17:300]
+    mapping[fulls[0]] = 0
+    mapping[fulls[1]] = -1
+    mapping[fulls[2]] = pool_rows + 7
+    r2t[r3, 300 - 5] = len(mapping) + 100     # past the mapping
+    r2t[rows[4], 301 - 2] = -1                  # reads the sentinel
+    rows[5] = r2t.shape[0] + 3                  # no such row
+    bad_loc = np.concatenate([loc, loc[:3], [pool_rows, -5, 0, 0, 1]]).astype(np.int64)
+    rng.shuffle(bad_loc)
+    ix = _index(r2t, rows, lens, mapping, P)
+    got = swa.swa_validate(ix, wl.window, pool_rows, store_loc=torch.from_numpy(bad_loc).cuda())
+    want = O.validate(r2t, rows, lens, mapping, wl.window, pool_rows, P, store_loc=bad_loc)
+    assert got == want
+    assert want["tombstones"] >= 1 and want["sentinels"] >= 2 and want["slot_out_of_range"] >= 1
+    assert want["full_out_of_range"] == 1 and want["bad_requests"] == 1
+    # the same data as an extend batch (prefix lengths) and as a full layer
+    pre = np.maximum(lens - 40, 0).astype(np.int32)
+    got = swa.swa_validate(ix, wl.window, pool_rows, prefix_lens=torch.from_numpy(pre).cuda())
+    assert got == O.validate(r2t, rows, lens, mapping, wl.window, pool_rows, P, prefix_lens=pre)
+    n_full_rows = len(mapping) - 1
+    got = swa.swa_validate(ix, -1, n_full_rows, use_map=False)
+    assert got == O.validate(r2t, rows, lens, None, -1, n_full_rows, P)
+
+
 # ---------------------------------------------------------------------------
 # extend
 # ---------------------------------------------------------------------------

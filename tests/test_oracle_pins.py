@@ -16,6 +16,7 @@ import torch
 
 from oracle import codecs
 from oracle import swa_oracle as O
+from sliding_window_attention_swa_amd import workloads as WL
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
 
@@ -517,3 +518,55 @@ def test_pins_catch_off_by_one_window(monkeypatch):
     good = real_attention(*args_pos, window=a["window"], sinks=a["sinks"], prefix_lens=a["prefix_lens"],
                           qo_indptr=a["qo_indptr"])
     np.testing.assert_allclose(good, want, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# validate: a hand-built batch whose violations are counted by hand
+# (page 2; full pool 8 rows + page 0 -> mapping of 11 entries ending in -1;
+# SWA pool 6 rows).
+# ---------------------------------------------------------------------------
+
+def hand_built_batch():
+    mapping = np.zeros(11, dtype=np.int64)
+    mapping[-1] = -1
+    mapping[[2, 3, 4, 5, 6, 7, 8]] = [2, 3, 4, 0, -1, 9, 5]  # 5: tombstone, 6: planted -1, 7: slot past the pool
+    r2t = np.zeros((4, 6), dtype=np.int32)
+    r2t[1] = [2, 3, 4, 5, 6, 7]
+    r2t[2] = [2, 3, 99, 8, -1, 4]  # 99: past the mapping; -1 reads the sentinel
+    r2t[3] = 8
+    rows = np.array([1, 2, 7, 3, 0, 1], dtype=np.int32)  # 7: no such row
+    lens = np.array([6, 5, 3, 7, 3, 2], dtype=np.int32)  # 7: longer than a row
+    store = np.array([2, 3, 3, 0, 0, 1, 7, -1, 5, 5, 5], dtype=np.int64)
+    return mapping, r2t, rows, lens, store
+
+
+HAND_COUNTS = {
+    # decode, W = 2, with the mapping (SWA pool of 6 rows)
+    "decode": dict(bad_requests=2, positions=11, full_out_of_range=1, tombstones=4, sentinels=2,
+                   slot_out_of_range=1, store_locs=11, store_out_of_range=2, store_duplicates=3),
+    # extend, W = 2, prefixes [4, 5, 0, 0, 1, 3] (the last one exceeds its length)
+    "extend": dict(bad_requests=3, positions=9, full_out_of_range=0, tombstones=4, sentinels=2,
+                   slot_out_of_range=1, store_locs=0, store_out_of_range=0, store_duplicates=0),
+    # full layer (no mapping), W = -1, full pool of 10 rows
+    "full": dict(bad_requests=2, positions=16, full_out_of_range=0, tombstones=3, sentinels=0,
+                 slot_out_of_range=2, store_locs=0, store_out_of_range=0, store_duplicates=0),
+}
+EXTEND_PREFIX = np.array([4, 5, 0, 0, 1, 3], dtype=np.int32)
+
+
+def test_validate_hand_counted():
+    mapping, r2t, rows, lens, store = hand_built_batch()
+    assert O.validate(r2t, rows, lens, mapping, 2, 6, 2, store_loc=store) == HAND_COUNTS["decode"]
+    assert O.validate(r2t, rows, lens, mapping, 2, 6, 2, prefix_lens=EXTEND_PREFIX) == HAND_COUNTS["extend"]
+    assert O.validate(r2t, rows, lens, None, -1, 10, 2) == HAND_COUNTS["full"]
+
+
+def test_validate_clean_workload_counts_nothing():
+    """A generated batch keeps every contract: only positions and locs count."""
+    wl = WL.decode_workload("clean", 5, [1, 40, 300], 8, 2, 16, 4, "bf16", "bf16", with_store=True, live_margin=3)
+    loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+    c = O.validate(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window, wl.pool_k.shape[0],
+                   wl.page_size, store_loc=loc)
+    assert c["positions"] == sum(min(n, wl.window + 1) for n in wl.seq_lens)
+    assert c["store_locs"] == loc.size
+    assert sum(v for k, v in c.items() if k not in ("positions", "store_locs")) == 0
