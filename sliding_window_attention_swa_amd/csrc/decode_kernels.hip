@@ -27,12 +27,13 @@
 // first product, its accumulator layout (lane = head column, 4 keys per lane)
 // is exactly the B-operand layout the second product needs for P^T, so P
 // never leaves registers.  The head dimension is permuted identically in Q and
-// K (lane group q covers dims 32q..32q+31) so each lane reads 64 contiguous
-// bytes of a K row.  V is staged through LDS (padded rows, conflict-free
-// transposed reads) because the key index must be the per-lane contraction
-// index of the second product.  e4m3 bytes are widened to bf16 exactly with
-// v_cvt_scalef32_pk_bf16_fp8; the per-tensor scales are folded into the logit
-// scale and the output.
+// K so that each load instruction reads whole runs of K rows (the four lane
+// groups of a key read neighbouring 16-byte pieces).  V is staged through LDS
+// (whole rows per load instruction, padded LDS rows, conflict-free transposed
+// reads with ds_read_b64_tr_b16) because the key index must be the per-lane
+// contraction index of the second product.  e4m3 bytes are widened to bf16
+// exactly with v_cvt_scalef32_pk_bf16_fp8; the per-tensor scales are folded
+// into the logit scale and the output.
 //
 // f32 path: plain VALU; 16 keys per wavefront step, 4 lanes per key row.
 #include "common.hpp"
@@ -42,7 +43,6 @@ namespace {
 
 constexpr int kD = 128;           // head_dim handled by these kernels
 constexpr int kMaxG = 16;         // q heads per kv head (MFMA N = 16)
-constexpr int kVRow = kD + 4;     // LDS V row: 264 bytes, 2-dword skew per row
 
 struct DecodeParams {
   const void *q;
@@ -203,8 +203,7 @@ template <typename KV>
 struct KvLoad;
 
 template <>
-struct KvLoad<uint16_t> {  // bf16 rows: 64 bytes per lane = 4 x 16 B
-  static constexpr int kVecs = 4;
+struct KvLoad<uint16_t> {  // bf16: the four 16-B K loads are the four contraction blocks
   __device__ static void to_bf16(const uint4 *raw, bf16x8_t *ops) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) __builtin_memcpy(&ops[c], &raw[c], 16);
@@ -212,8 +211,7 @@ struct KvLoad<uint16_t> {  // bf16 rows: 64 bytes per lane = 4 x 16 B
 };
 
 template <>
-struct KvLoad<uint8_t> {  // e4m3 rows: 32 bytes per lane = 2 x 16 B, widened exactly
-  static constexpr int kVecs = 2;
+struct KvLoad<uint8_t> {  // e4m3: each 16-B K load widens (exactly) to two contraction blocks
   __device__ static void to_bf16(const uint4 *raw, bf16x8_t *ops) {
     uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
 #pragma unroll
@@ -232,30 +230,118 @@ struct KvLoad<uint8_t> {  // e4m3 rows: 32 bytes per lane = 2 x 16 B, widened ex
   }
 };
 
-// Raw registers of one 16-key block for this lane (key = lane % 16, dims 32q..32q+31).
+// Global-load layouts.  K rows feed S^T = K Q^T straight from registers: for
+// contraction block c (32 dims) lane (key kr, group lq) holds 8 dims of key kr
+// (an MFMA operand needs them in one lane).  Which 8 dims is our choice (Q is
+// permuted identically); it is made so that in every load instruction the
+// four lane groups of one key read one contiguous run of its row, i.e. the
+// loads are row-coalesced.  V rows only pass through LDS, so they are read
+// 16 B per lane with each row covered by neighbouring lanes (16 lanes per
+// bf16 row, 8 per e4m3 row): every instruction reads whole rows.
 template <typename KV>
-struct BlockRegs {
-  uint4 k[KvLoad<KV>::kVecs];
-  uint4 v[KvLoad<KV>::kVecs];
+struct Layout;
+
+template <>
+struct Layout<uint16_t> {
+  static constexpr int kKLoads = 4;  // 16-B K loads per key per lane
+  static constexpr int kVLoads = 4;  // 16-B V loads per 16-key block per lane
+  __device__ static int k_off(int c, int lq) { return 32 * c + 8 * lq; }   // element offset of K load c
+  __device__ static int qk_dim(int c, int lq) { return 32 * c + 8 * lq; }  // dims of contraction block c
+  __device__ static int v_key(int j, int lane) { return 4 * j + (lane >> 4); }
+  __device__ static int v_off(int lane) { return 8 * (lane & 15); }
 };
 
+template <>
+struct Layout<uint8_t> {
+  static constexpr int kKLoads = 2;  // one 16-B load = 16 dims = two contraction blocks
+  static constexpr int kVLoads = 2;
+  __device__ static int k_off(int c, int lq) { return 64 * c + 16 * lq; }
+  __device__ static int qk_dim(int c, int lq) { return 64 * (c >> 1) + 16 * lq + 8 * (c & 1); }
+  __device__ static int v_key(int j, int lane) { return 8 * j + (lane >> 3); }
+  __device__ static int v_off(int lane) { return 16 * (lane & 7); }
+};
+
+constexpr int kSVRow = kD + 16;  // LDS V row: 288 bytes (transposed reads are conflict-free)
+
+// Q^T operand of head h for lane group lq, in the contraction order of Layout<KV>.
 template <typename KV>
-__device__ __forceinline__ void load_block(const DecodeParams &p, const KeySource &ks, int32_t key, bool valid,
-                                           int32_t g, int32_t lq, BlockRegs<KV> &r) {
+__device__ __forceinline__ void load_q(const DecodeParams &p, int32_t b, int32_t h, int32_t lq, uint4 (&qraw)[4]) {
+  const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + (static_cast<int64_t>(b) * p.q_heads + h) * kD;
 #pragma unroll
-  for (int c = 0; c < KvLoad<KV>::kVecs; ++c) {
-    r.k[c] = make_uint4(0, 0, 0, 0);
-    r.v[c] = make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < 4; ++c) qraw[c] = *reinterpret_cast<const uint4 *>(qrow + Layout<KV>::qk_dim(c, lq));
+}
+
+// The K loads of one key row (slot) for lane group lq.
+template <typename KV>
+__device__ __forceinline__ void load_k(const DecodeParams &p, int32_t slot, int32_t g, int32_t lq,
+                                       uint4 (&raw)[Layout<KV>::kKLoads]) {
+  const KV *row = static_cast<const KV *>(p.k) + row_elem(safe_slot(slot, p.rows), p.kv_heads, g, kD);
+#pragma unroll
+  for (int c = 0; c < Layout<KV>::kKLoads; ++c)
+    raw[c] = *reinterpret_cast<const uint4 *>(row + Layout<KV>::k_off(c, lq));
+}
+
+// The V loads of one 16-key block whose slots are held by lanes 0..15 (lane
+// kr holds the slot of key kr in `slot`).
+template <typename KV>
+__device__ __forceinline__ void load_v(const DecodeParams &p, int32_t slot, int32_t g, int32_t lane,
+                                       uint4 (&raw)[Layout<KV>::kVLoads]) {
+#pragma unroll
+  for (int j = 0; j < Layout<KV>::kVLoads; ++j) {
+    const int32_t s = __shfl(slot, Layout<KV>::v_key(j, lane));
+    const KV *row = static_cast<const KV *>(p.v) + row_elem(safe_slot(s, p.rows), p.kv_heads, g, kD);
+    raw[j] = *reinterpret_cast<const uint4 *>(row + Layout<KV>::v_off(lane));
   }
-  if (!valid) return;
-  const int64_t slot = safe_slot(ks.src[key], p.rows);
-  const int64_t off = row_elem(slot, p.kv_heads, g, kD) + 32 * lq;
-  const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.k) + off);
-  const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.v) + off);
+}
+
+// 16 e4m3 bytes -> 16 bf16 (exact).
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4 &x, uint4 (&out)[2]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t u[8];
 #pragma unroll
-  for (int c = 0; c < KvLoad<KV>::kVecs; ++c) {
-    r.k[c] = kp[c];
-    r.v[c] = vp[c];
+  for (int i = 0; i < 4; ++i) {
+    bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+    bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+    __builtin_memcpy(&u[2 * i], &a, 4);
+    __builtin_memcpy(&u[2 * i + 1], &c, 4);
+  }
+  out[0] = make_uint4(u[0], u[1], u[2], u[3]);
+  out[1] = make_uint4(u[4], u[5], u[6], u[7]);
+}
+
+// One block's V rows into its 16-row LDS tile (bf16, kSVRow stride); rows of
+// keys at or past k_end are written as zeros (their slots may hold anything).
+template <typename KV>
+__device__ __forceinline__ void v_to_lds(const uint4 (&raw)[Layout<KV>::kVLoads], uint16_t *tile, int32_t lane,
+                                         int32_t key_base, int32_t k_end) {
+#pragma unroll
+  for (int j = 0; j < Layout<KV>::kVLoads; ++j) {
+    const int32_t key = Layout<KV>::v_key(j, lane);
+    const bool ok = key_base + key < k_end;
+    uint4 *d = reinterpret_cast<uint4 *>(tile + key * kSVRow + Layout<KV>::v_off(lane));
+    if constexpr (sizeof(KV) == 2) {
+      d[0] = ok ? raw[j] : make_uint4(0, 0, 0, 0);
+    } else {
+      uint4 w2[2];
+      fp8x16_to_bf16(raw[j], w2);
+      d[0] = ok ? w2[0] : make_uint4(0, 0, 0, 0);
+      d[1] = ok ? w2[1] : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T for a pair of 16-key blocks whose rows start at `pair` in the
+// LDS tile (the second block absent when !SECOND); pop holds P^T of the pair.
+template <bool SECOND>
+__device__ __forceinline__ void pv_pair(const uint16_t *pair, int32_t kr, int32_t lq, const bf16x8_t &pop,
+                                        f32x4_t (&acc)[8]) {
+  const uint16_t *vrow = pair + (4 * lq + (kr >> 2)) * kSVRow + 4 * (kr & 3);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const i16x4_t lo = lds_read_tr16(vrow + 16 * c);
+    const i16x4_t hi = SECOND ? lds_read_tr16(vrow + 16 * kSVRow + 16 * c) : i16x4_t{0, 0, 0, 0};
+    const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[c], 0, 0, 0);
   }
 }
 
@@ -268,39 +354,28 @@ __device__ __forceinline__ void load_block(const DecodeParams &p, const KeySourc
 // masked).  V goes through a per-wavefront LDS tile and is read back with the
 // transposing ds_read_b64_tr_b16, so P^T and V^T never need register shuffles.
 constexpr int kStreamWaves = 4;
-constexpr int kSVRow = kD + 16;  // LDS V row: 288 bytes (transposed reads are conflict-free)
 
 template <typename KV>
 struct StreamRound {
-  uint4 k[2][KvLoad<KV>::kVecs];
-  uint4 v[2][KvLoad<KV>::kVecs];
+  uint4 k[2][Layout<KV>::kKLoads];
+  uint4 v[2][Layout<KV>::kVLoads];
 };
 
 template <typename KV>
-__device__ __forceinline__ void stream_issue(const DecodeParams &p, const int32_t (&sl)[2], int32_t g, int32_t lq,
+__device__ __forceinline__ void stream_issue(const DecodeParams &p, const int32_t (&sl)[2], int32_t g, int32_t lane,
                                              StreamRound<KV> &r) {
-  constexpr int kVec = KvLoad<KV>::kVecs;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t off = row_elem(safe_slot(sl[u], p.rows), p.kv_heads, g, kD) + 32 * lq;
-    const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.k) + off);
+  for (int u = 0; u < 2; ++u) load_k<KV>(p, sl[u], g, lane >> 4, r.k[u]);
 #pragma unroll
-    for (int c = 0; c < kVec; ++c) r.k[u][c] = kp[c];
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t off = row_elem(safe_slot(sl[u], p.rows), p.kv_heads, g, kD) + 32 * lq;
-    const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.v) + off);
-#pragma unroll
-    for (int c = 0; c < kVec; ++c) r.v[u][c] = vp[c];
-  }
+  for (int u = 0; u < 2; ++u) load_v<KV>(p, sl[u], g, lane, r.v[u]);
 }
 
 template <typename KV>
 __device__ __forceinline__ void stream_compute(const DecodeParams &p, const StreamRound<KV> &r, int32_t key_base0,
                                                int32_t key_base1, int32_t k1, const bf16x8_t (&qop)[4], uint16_t *vt,
-                                               int32_t kr, int32_t lq, f32x4_t (&acc)[8], float &m_run,
-                                               float &l_run) {
+                                               int32_t lane, f32x4_t (&acc)[8], float &m_run, float &l_run) {
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
   // S^T for the two blocks (lane: keys 4lq..4lq+3 of head kr)
   float sc[2][4];
   float mb = -INFINITY;
@@ -318,20 +393,9 @@ __device__ __forceinline__ void stream_compute(const DecodeParams &p, const Stre
       mb = fmaxf(mb, sc[u][rr]);
     }
   }
-  // V rows -> LDS (bf16): block u at rows 16u..16u+15, lane's row kr, dims 32lq..
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    bf16x8_t vv[4];
-    KvLoad<KV>::to_bf16(r.v[u], vv);
-    const bool ok = (u == 0 ? key_base0 : key_base1) + kr < k1;
-    uint4 *d = reinterpret_cast<uint4 *>(vt + (u * 16 + kr) * kSVRow + 32 * lq);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 x;
-      __builtin_memcpy(&x, &vv[c], 16);
-      d[c] = ok ? x : make_uint4(0, 0, 0, 0);  // rows past the range may hold anything
-    }
-  }
+  // V rows -> LDS (bf16): block u at rows 16u..16u+15
+  v_to_lds<KV>(r.v[0], vt, lane, key_base0, k1);
+  v_to_lds<KV>(r.v[1], vt + 16 * kSVRow, lane, key_base1, k1);
   // online softmax (base 2, scale folded into the exponent)
   const float m_new = fmaxf(m_run, wave_max_q(mb) * p.scale2);
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -356,14 +420,7 @@ __device__ __forceinline__ void stream_compute(const DecodeParams &p, const Stre
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
   __builtin_amdgcn_wave_barrier();
-  const uint16_t *vrow = vt + (4 * lq + (kr >> 2)) * kSVRow + 4 * (kr & 3);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const i16x4_t lo = lds_read_tr16(vrow + 16 * c);
-    const i16x4_t hi = lds_read_tr16(vrow + 16 * kSVRow + 16 * c);
-    const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[c], 0, 0, 0);
-  }
+  pv_pair<true>(vt, kr, lq, pop, acc);
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next round rewrites the tile
 }
@@ -395,12 +452,8 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 1) decode_stream_kernel(Dec
   const int32_t nblk = (k1 - k0 + 15) >> 4;
   const int32_t nround = (nblk + 1) / 2;
 
-  const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
-                                                    (static_cast<int64_t>(b) * p.q_heads + g * G +
-                                                     (kr < G ? kr : 0)) * kD + 32 * lq);
   uint4 qraw[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
+  load_q<KV>(p, b, g * G + (kr < G ? kr : 0), lq, qraw);
 
   f32x4_t acc[8];
 #pragma unroll
@@ -425,18 +478,18 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 1) decode_stream_kernel(Dec
     slots_of(0, slA);
     if (nround > 1) slots_of(1, slB);
     __builtin_amdgcn_sched_barrier(0);
-    stream_issue<KV>(p, slA, g, lq, A);
+    stream_issue<KV>(p, slA, g, lane, A);
     __builtin_amdgcn_sched_barrier(0);
     for (int32_t r = 0; r < nround; r += 2) {
-      if (r + 1 < nround) stream_issue<KV>(p, slB, g, lq, B);
+      if (r + 1 < nround) stream_issue<KV>(p, slB, g, lane, B);
       if (r + 2 < nround) slots_of(r + 2, slA);
       __builtin_amdgcn_sched_barrier(0);
-      stream_compute<KV>(p, A, key_of(2 * r), key_of(2 * r + 1), k1, qop, vt, kr, lq, acc, m_run, l_run);
+      stream_compute<KV>(p, A, key_of(2 * r), key_of(2 * r + 1), k1, qop, vt, lane, acc, m_run, l_run);
       if (r + 1 >= nround) break;
-      if (r + 2 < nround) stream_issue<KV>(p, slA, g, lq, A);
+      if (r + 2 < nround) stream_issue<KV>(p, slA, g, lane, A);
       if (r + 3 < nround) slots_of(r + 3, slB);
       __builtin_amdgcn_sched_barrier(0);
-      stream_compute<KV>(p, B, key_of(2 * r + 2), key_of(2 * r + 3), k1, qop, vt, kr, lq, acc, m_run, l_run);
+      stream_compute<KV>(p, B, key_of(2 * r + 2), key_of(2 * r + 3), k1, qop, vt, lane, acc, m_run, l_run);
     }
   }
   l_run = wave_sum_q(l_run);
@@ -488,10 +541,10 @@ constexpr int kWinWaves = 4;
 
 template <typename KV, int MAXB, bool OUT_BF16>
 __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kWinWaves * MAXB * 16 * kVRow * 2 >
-                                                                    kWinWaves * kMaxG * kD * 4
-                                                                ? kWinWaves * MAXB * 16 * kVRow * 2
-                                                                : kWinWaves * kMaxG * kD * 4];
+  // each wavefront stages one pair of blocks (32 V rows) at a time
+  constexpr int kTileBytes = kWinWaves * 32 * kSVRow * 2;
+  constexpr int kRedBytes = kWinWaves * kMaxG * kD * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
   __shared__ float red_m[kWinWaves * kMaxG];
   __shared__ float red_l[kWinWaves * kMaxG];
   const int32_t g = blockIdx.y;
@@ -501,7 +554,8 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
   const int32_t G = p.group;
-  constexpr int kVec = KvLoad<KV>::kVecs;
+  constexpr int kKL = Layout<KV>::kKLoads;
+  constexpr int kVL = Layout<KV>::kVLoads;
 
   // ---- key source (window table or req_to_token row).  A window holds at
   // most W + 1 keys: only the last W + 1 entries are used.
@@ -522,14 +576,10 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
       sl[u] = p.table[idx < 0 ? 0 : idx];
     }
   }
-  // Q^T operand rows (head g*G + kr, dims 32lq..32lq+31).  Lanes of padding
-  // heads (kr >= G) read a real head: their columns are never stored.
-  const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) +
-                                                    (static_cast<int64_t>(b) * p.q_heads + g * G +
-                                                     (kr < G ? kr : 0)) * kD + 32 * lq);
+  // Q^T operand (head g*G + kr).  Lanes of padding heads (kr >= G) read a
+  // real head: their columns are never stored.
   uint4 qraw[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
+  load_q<KV>(p, b, g * G + (kr < G ? kr : 0), lq, qraw);
   __builtin_amdgcn_sched_barrier(0);
 
   const KeySource ks = key_source(p, b);
@@ -543,7 +593,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig;
   float l_run = 0.f;
-  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * MAXB * 16 * kVRow;
+  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * 32 * kSVRow;
 
   if (w < nblk) {  // wave-uniform: this wavefront owns at least one block
     // All row loads are unconditional (no control flow between them, so none
@@ -560,22 +610,11 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     }
     __builtin_amdgcn_sched_barrier(0);
     // every K row first, then every V row: the scores only wait for K
-    int64_t off[MAXB];
+    uint4 kraw[MAXB][kKL], vraw[MAXB][kVL];
 #pragma unroll
-    for (int u = 0; u < MAXB; ++u) off[u] = row_elem(safe_slot(sl[u], p.rows), p.kv_heads, g, kD) + 32 * lq;
-    uint4 kraw[MAXB][kVec], vraw[MAXB][kVec];
+    for (int u = 0; u < MAXB; ++u) load_k<KV>(p, sl[u], g, lq, kraw[u]);
 #pragma unroll
-    for (int u = 0; u < MAXB; ++u) {
-      const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.k) + off[u]);
-#pragma unroll
-      for (int c = 0; c < kVec; ++c) kraw[u][c] = kp[c];
-    }
-#pragma unroll
-    for (int u = 0; u < MAXB; ++u) {
-      const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const KV *>(p.v) + off[u]);
-#pragma unroll
-      for (int c = 0; c < kVec; ++c) vraw[u][c] = vp[c];
-    }
+    for (int u = 0; u < MAXB; ++u) load_v<KV>(p, sl[u], g, lane, vraw[u]);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t qop[4];
     KvLoad<uint16_t>::to_bf16(qraw, qop);
@@ -606,52 +645,32 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
       float pv[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[r] = exp2f(sc[2 * u2][r] - m_run);
-        pv[4 + r] = (2 * u2 + 1 < MAXB) ? exp2f(sc[(2 * u2 + 1) < MAXB ? 2 * u2 + 1 : 0][r] - m_run) : 0.f;
+        pv[r] = __builtin_amdgcn_exp2f(sc[2 * u2][r] - m_run);
+        pv[4 + r] =
+            (2 * u2 + 1 < MAXB) ? __builtin_amdgcn_exp2f(sc[(2 * u2 + 1) < MAXB ? 2 * u2 + 1 : 0][r] - m_run) : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) l_run += pv[e];
-      uint32_t u4[4] = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                        pack_bf16x2(pv[6], pv[7])};
+      uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
+                        pack_bf16x2_hw(pv[6], pv[7])};
       __builtin_memcpy(&pop[u2], u4, 16);
     }
-    // ---- V rows -> LDS (bf16, 264-byte rows), block u at rows 16u..16u+15
-#pragma unroll
-    for (int u = 0; u < MAXB; ++u) {
-      if (16 * (w + kWinWaves * u) + kr >= n) {  // key past the end: its row may be anything
-#pragma unroll
-        for (int c = 0; c < kVec; ++c) vraw[u][c] = make_uint4(0, 0, 0, 0);
-      }
-      bf16x8_t vv[4];
-      KvLoad<KV>::to_bf16(vraw[u], vv);
-      uint2 *d = reinterpret_cast<uint2 *>(vt + (u * 16 + kr) * kVRow + 32 * lq);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint2 a2[2];
-        __builtin_memcpy(a2, &vv[c], 16);
-        d[2 * c] = a2[0];
-        d[2 * c + 1] = a2[1];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
-    __builtin_amdgcn_wave_barrier();
-    // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1)
+    // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1), each pair's V rows
+    // staged in this wave's 32-row LDS tile
 #pragma unroll
     for (int u2 = 0; u2 < kPairs; ++u2) {
-      const bool second = 2 * u2 + 1 < MAXB;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint16_t *col = vt + (2 * u2 * 16) * kVRow + 16 * c + kr;
-        uint16_t e8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          e8[e] = col[(4 * lq + e) * kVRow];
-          e8[4 + e] = second ? col[(16 + 4 * lq + e) * kVRow] : static_cast<uint16_t>(0);
-        }
-        bf16x8_t vop;
-        __builtin_memcpy(&vop, e8, 16);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[u2], acc[c], 0, 0, 0);
-      }
+      const int32_t u0 = 2 * u2;
+      v_to_lds<KV>(vraw[u0], vt, lane, 16 * (w + kWinWaves * u0), n);
+      if (u0 + 1 < MAXB)
+        v_to_lds<KV>(vraw[u0 + 1 < MAXB ? u0 + 1 : u0], vt + 16 * kSVRow, lane, 16 * (w + kWinWaves * (u0 + 1)), n);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+      if (u0 + 1 < MAXB)
+        pv_pair<true>(vt, kr, lq, pop[u2], acc);
+      else
+        pv_pair<false>(vt, kr, lq, pop[u2], acc);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the tile is rewritten
     }
   }
   l_run = wave_sum_q(l_run);
