@@ -27,6 +27,10 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # Packed fp32 VALU ops stay off: all fp32 math is emitted as scalar-lane ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # No implicit fma contraction: only explicit fmaf() fuses, so every
+    # instantiation of a kernel (e.g. f32 and bf16 output) computes the same
+    # f32 values and the bf16 output is exactly the f32 output rounded.
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["api.cpp", "index_kernels.hip", "store_kernels.hip", "decode_kernels.hip", "extend_kernels.hip",

@@ -7,29 +7,36 @@
 // the pool and the chunk's queries read the prefix's last window plus the chunk.
 //
 // MI355X design (not the pages' kernels):
-//   * one workgroup = 16 consecutive queries x the G query heads of one kv head
-//     (GQA packed into the M side), so each K/V row staged in LDS serves G heads;
-//   * the key range of a tile is only the band [i0 - W, i0 + 15]: blocks of 16
-//     keys entirely outside the band are never loaded or multiplied (at W = 128:
-//     9 blocks, two of them partially masked);
+//   * a tile = 16 consecutive queries x the G query heads of one kv head (GQA
+//     packed into the M side), so each K/V row staged in LDS serves G heads;
+//     the key range of a tile is only its band [i0 - W, i0 + 15];
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32
 //     accumulation; P is rounded to bf16 for the second product and never leaves
 //     registers (the first product's accumulator layout is the second's B
 //     operand layout); the V^T operand is read from a row-major LDS tile with
-//     gfx950's transposing ds_read_b64_tr_b16; online softmax in base 2 over
-//     chunks of up to 9 blocks, masks computed only on band-edge blocks;
-//   * tiles are numbered (request, kv head, query tile) and dealt to the 8 XCDs
-//     in contiguous runs, so the 9 tiles that share a K/V block run on one XCD
-//     and hit its L2.
+//     gfx950's transposing ds_read_b64_tr_b16; online softmax in base 2;
+//   * one workgroup walks a run of consecutive tiles of one (request, kv
+//     head).  At W = 128 a full tile's band is exactly 9 blocks of 16 keys and
+//     the next tile's band is the same minus its first block plus one new
+//     block, so the band lives in a 9-slot LDS ring: while a tile is computed,
+//     the next tile's queries and its one new K/V block are already in flight
+//     (and the slots of the block after that), so a tile costs its arithmetic,
+//     not a memory round trip.  Other tiles (other windows, band clipped at
+//     position 0, partial tiles) take a general path that stages the band in
+//     chunks of 9 blocks;
+//   * runs are numbered (request, kv head, run) and dealt to the 8 XCDs in
+//     contiguous ranges, so neighbouring runs, which share band blocks, hit the
+//     same L2.
 #include "common.hpp"
 
 namespace swa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kNW = 4;       // wavefronts per workgroup
-constexpr int kTQ = 16;      // queries per tile
-constexpr int kKB = 9;       // key blocks (of 16) per chunk
+constexpr int kNW = 4;         // wavefronts per workgroup
+constexpr int kTQ = 16;        // queries per tile
+constexpr int kKB = 9;         // key blocks (of 16) per chunk / ring slots
+constexpr int kBand = 16 * kKB;  // keys of a full band at W = 128
 constexpr int kKRow = kD + 8;  // LDS K row: 272 bytes (16-byte aligned rows, 4-bank skew)
 constexpr int kVRow = kD + 16;  // LDS V row: 288 bytes (8-bank skew: conflict-free transposed reads)
 
@@ -57,6 +64,7 @@ struct ExtendParams {
   const float *sinks;
   float scale2;
   void *out;
+  int32_t run_tiles;  // tiles per workgroup run
 };
 
 __device__ __forceinline__ float wave_max_q(float x) {
@@ -70,270 +78,262 @@ __device__ __forceinline__ float wave_sum_q(float x) {
   return x;
 }
 
-// Queries of request b: count and first position.
+// Workgroup barrier for LDS data only.  __syncthreads() also fences global
+// memory, i.e. waits for every outstanding global load and store of the wave;
+// the ring's barriers must not wait for the next tile's prefetches or this
+// tile's output stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Queries of request b.
 __device__ __forceinline__ int32_t new_count(const ExtendParams &p, int32_t b) {
   int32_t n = p.qo_indptr[b + 1] - p.qo_indptr[b];
   return n > 0 ? n : 0;
 }
 
-// Steady-state tile: 16 valid queries, band [i0 - W, i0 + 15] not clipped at
-// position 0, W = 16 * (NB - 1).  Then the band is exactly NB blocks of 16
-// keys (key offset k from i0 - W): block 0 is the band's lower edge (query kr
-// sees k >= kr), block NB-1 the diagonal (k <= W + kr), the rest are inside
-// the band for every query.  Compile-time structure, no per-key position math.
-template <int NB, int MB>
-__device__ __forceinline__ void tile_fast(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile,
-                                          const bf16x8_t (&qop)[MB][4], const int32_t *key_slots, int32_t g,
-                                          f32x4_t (&acc)[MB][8], float (&m_run)[MB], float (&l_run)[MB]) {
+// Key position -> pool slot for one request: src[pos - pos_base], 0 <= . < hi.
+struct KeySrc {
+  const int32_t *src;
+  int64_t hi;
+  int32_t pos_base;
+};
+
+__device__ __forceinline__ KeySrc key_src(const ExtendParams &p, int32_t b, int32_t prefix) {
+  KeySrc ks;
+  if (p.indptr) {
+    int64_t lo = p.indptr[b], hi = p.indptr[b + 1];
+    if (lo < 0) lo = 0;
+    if (hi > p.capacity) hi = p.capacity;
+    ks.src = p.table + lo;
+    ks.hi = hi > lo ? hi - lo : 0;
+    int32_t base = p.window < 0 ? 0 : prefix - p.window;
+    ks.pos_base = base < 0 ? 0 : base;
+  } else {
+    int64_t row = p.req_idx[b];
+    if (row < 0 || row >= p.r2t_rows) row = 0;
+    ks.src = p.r2t + row * p.r2t_stride;
+    ks.hi = p.r2t_stride;
+    ks.pos_base = 0;
+  }
+  return ks;
+}
+
+// Slot of key position `pos` (a position outside the source reads entry 0;
+// callers only use such slots for rows they mask or zero).
+__device__ __forceinline__ int32_t slot_at(const KeySrc &ks, int64_t pos) {
+  if (ks.hi <= 0) return 0;
+  const int64_t si = pos - ks.pos_base;
+  return ks.src[si >= 0 && si < ks.hi ? si : 0];
+}
+
+struct Tile {
+  int32_t row0;    // first q row of the tile
+  int32_t i0;      // position of its first query
+  int32_t i_last;  // position of its last valid query
+  int32_t kj0;     // first key position of its band
+  int32_t nkeys;   // keys in the band
+  bool steady;     // W = 128, 16 valid queries, band inside position 0.. and the key source
+};
+
+__device__ __forceinline__ Tile tile_at(const ExtendParams &p, const KeySrc &ks, int32_t qo0, int32_t qt,
+                                        int32_t prefix, int32_t n_new, int32_t seq) {
+  Tile t;
+  const int32_t W = p.window;
+  t.row0 = qo0 + qt * kTQ;
+  t.i0 = prefix + qt * kTQ;
+  int32_t il = t.i0 + kTQ - 1;
+  if (il > prefix + n_new - 1) il = prefix + n_new - 1;
+  if (il > seq - 1) il = seq - 1;
+  t.i_last = il;
+  int32_t kj0 = W < 0 ? 0 : t.i0 - W;
+  t.kj0 = kj0 < 0 ? 0 : kj0;
+  t.nkeys = il >= t.kj0 ? il - t.kj0 + 1 : 0;
+  t.steady = W == kBand - 16 && t.i0 - W >= 0 && qt * kTQ + kTQ <= n_new && il == t.i0 + kTQ - 1 &&
+             static_cast<int64_t>(t.row0) + kTQ <= p.total_q && static_cast<int64_t>(t.kj0) - ks.pos_base >= 0 &&
+             static_cast<int64_t>(t.kj0) - ks.pos_base + kBand <= ks.hi;
+  return t;
+}
+
+// Slot of a key position known to lie inside the key source (steady tiles).
+__device__ __forceinline__ int32_t slot_in(const KeySrc &ks, int32_t pos) { return ks.src[pos - ks.pos_base]; }
+
+// Q^T operands of this lane: query row `qrow`, heads w*MB + m, dims 32lq..32lq+31
+// (padding heads read a real head; their columns are never stored).
+template <int MB>
+__device__ __forceinline__ void load_q(const ExtendParams &p, int64_t qrow, int32_t g, int32_t w, int32_t lq,
+                                       uint4 (&raw)[MB][4]) {
+  const int32_t G = p.group;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int32_t hh = w * MB + m;
+    const uint4 *qp =
+        reinterpret_cast<const uint4 *>(p.q + (qrow * p.q_heads + g * G + (hh < G ? hh : 0)) * kD + 32 * lq);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[m][c] = qp[c];
+  }
+}
+
+// This thread's 16-byte piece of one K row and one V row (16 threads per row).
+__device__ __forceinline__ void fetch_piece(const ExtendParams &p, int32_t slot, int32_t g, uint4 &k, uint4 &v) {
+  const int64_t sl = (slot < 0 || slot >= p.rows) ? 0 : static_cast<int64_t>(slot);
+  const int64_t off = row_elem(sl, p.kv_heads, g, kD) + 8 * (threadIdx.x & 15);
+  k = *reinterpret_cast<const uint4 *>(p.k + off);
+  v = *reinterpret_cast<const uint4 *>(p.v + off);
+}
+
+__device__ __forceinline__ void put_piece(uint16_t *ktile, uint16_t *vtile, int32_t row, const uint4 &k,
+                                          const uint4 &v) {
+  const int32_t piece = threadIdx.x & 15;
+  *reinterpret_cast<uint4 *>(ktile + row * kKRow + 8 * piece) = k;
+  *reinterpret_cast<uint4 *>(vtile + row * kVRow + 8 * piece) = v;
+}
+
+// Steady tiles read the band from the ring: band block j lives in ring slot
+// (q0 + j) mod 9.  Block 0 is the band's lower edge (query kr sees key offsets
+// k >= kr), block 8 the diagonal (k <= kr), the rest are inside the band for
+// every query.
+__device__ __forceinline__ int32_t ring_slot(int32_t q0, int j) { return q0 + j < kKB ? q0 + j : q0 + j - kKB; }
+
+// Scores and softmax numerators of a steady tile (sacc ends up holding
+// 2^(s - m) per key; m_run / l_run the tile's max and sum).
+template <int MB>
+__device__ __forceinline__ void ring_scores(const ExtendParams &p, const uint16_t *ktile, int32_t q0,
+                                            const bf16x8_t (&qop)[MB][4], f32x4_t (&sacc)[MB][kKB],
+                                            float (&m_run)[MB], float (&l_run)[MB]) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
-  // ---- stage the NB blocks (16 threads per 256-byte row); all loads first
-  {
-    const int32_t piece = threadIdx.x & 15;
-    int32_t slot[NB];
+  int32_t slot[kKB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) slot[i] = key_slots[(threadIdx.x >> 4) + 16 * i];
-    int64_t off[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int64_t sl = (slot[i] < 0 || slot[i] >= p.rows) ? 0 : static_cast<int64_t>(slot[i]);
-      off[i] = row_elem(sl, p.kv_heads, g, kD) + 8 * piece;
-    }
-    uint4 kreg[NB], vreg[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) kreg[i] = *reinterpret_cast<const uint4 *>(p.k + off[i]);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) vreg[i] = *reinterpret_cast<const uint4 *>(p.v + off[i]);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int32_t key = (threadIdx.x >> 4) + 16 * i;
-      *reinterpret_cast<uint4 *>(ktile + key * kKRow + 8 * piece) = kreg[i];
-      *reinterpret_cast<uint4 *>(vtile + key * kVRow + 8 * piece) = vreg[i];
-    }
-  }
-  __syncthreads();
+  for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
   // ---- S^T = K Q^T
-  f32x4_t sacc[MB][NB];
 #pragma unroll
-  for (int kb = 0; kb < NB; ++kb) {
+  for (int j = 0; j < kKB; ++j) {
     bf16x8_t kop[4];
-    const uint16_t *kp = ktile + (kb * 16 + kr) * kKRow + 32 * lq;
+    const uint16_t *kp = ktile + (slot[j] * 16 + kr) * kKRow + 32 * lq;
 #pragma unroll
     for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 8 * c, 16);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      sacc[m][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sacc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        sacc[m][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c], qop[m][c], sacc[m][kb], 0, 0, 0);
+        sacc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c], qop[m][c], sacc[m][j], 0, 0, 0);
     }
   }
-  // ---- band edges: block 0 keeps k >= kr, block NB-1 keeps k <= W + kr
+  // ---- band edges
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int32_t k = 4 * lq + r;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      if (NB == 1) {
-        sacc[m][0][r] = (k == kr) ? sacc[m][0][r] : -INFINITY;
-      } else {
-        sacc[m][0][r] = (k >= kr) ? sacc[m][0][r] : -INFINITY;
-        sacc[m][NB - 1][r] = (k <= kr) ? sacc[m][NB - 1][r] : -INFINITY;
-      }
+      sacc[m][0][r] = (k >= kr) ? sacc[m][0][r] : -INFINITY;
+      sacc[m][kKB - 1][r] = (k <= kr) ? sacc[m][kKB - 1][r] : -INFINITY;
     }
   }
-  // ---- softmax (one chunk: no rescaling of acc needed)
+  // ---- softmax (the whole band at once: no rescaling)
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int j = 0; j < kKB; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][kb][r]);
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][j][r]);
     const float m_new = wave_max_q(mx) * p.scale2;  // finite: every query sees its own key
     m_run[m] = m_new;
     float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int j = 0; j < kKB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][kb][r], p.scale2, -m_new));
-        sacc[m][kb][r] = e;
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][j][r], p.scale2, -m_new));
+        sacc[m][j][r] = e;
         ps += e;
       }
     l_run[m] = ps;
   }
-  // ---- O^T = V^T P^T over block pairs; V^T via transposing LDS reads
-  const uint16_t *vrow = vtile + (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
+}
+
+// O^T = V^T P^T of a steady tile over block pairs (2u, 2u+1) of its band.
+// acc is written, not accumulated into: the first pair starts from zero, so
+// acc holds no registers while the scores are computed.
+template <int MB>
+__device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const f32x4_t (&sacc)[MB][kKB],
+                                        f32x4_t (&acc)[MB][8]) {
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  int32_t slot[kKB];
 #pragma unroll
-  for (int u = 0; u < (NB + 1) / 2; ++u) {
-    constexpr int kLast = NB - 1;
-    const bool second = 2 * u + 1 < NB;  // compile-time after unrolling
-    const int kb1 = second ? 2 * u + 1 : kLast;
+  for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
+  const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
+#pragma unroll
+  for (int u = 0; u < (kKB + 1) / 2; ++u) {
+    const bool second = 2 * u + 1 < kKB;  // compile-time after unrolling
+    const int ja = 2 * u;
+    const int jb = second ? 2 * u + 1 : 2 * u;
     bf16x8_t pop[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][2 * u][0], sacc[m][2 * u][1]),
-                        pack_bf16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
-                        second ? pack_bf16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
-                        second ? pack_bf16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
+      uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][ja][0], sacc[m][ja][1]), pack_bf16x2_hw(sacc[m][ja][2], sacc[m][ja][3]),
+                        second ? pack_bf16x2_hw(sacc[m][jb][0], sacc[m][jb][1]) : 0u,
+                        second ? pack_bf16x2_hw(sacc[m][jb][2], sacc[m][jb][3]) : 0u};
       __builtin_memcpy(&pop[m], u4, 16);
     }
+    const uint16_t *va = vtile + slot[ja] * 16 * kVRow + voff;
+    const uint16_t *vb = vtile + slot[jb] * 16 * kVRow + voff;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const i16x4_t lo = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * n);
-      i16x4_t hi = {0, 0, 0, 0};
-      if (second) hi = lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * n);
+      const i16x4_t lo = lds_read_tr16(va + 16 * n);
+      const i16x4_t hi = second ? lds_read_tr16(vb + 16 * n) : i16x4_t{0, 0, 0, 0};
       const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int m = 0; m < MB; ++m)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], acc[m][n], 0, 0, 0);
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], u == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[m][n],
+                                                            0, 0, 0);
     }
   }
 }
 
-template <int MB, bool OUT_BF16>
-__global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
-
-  // ---- which tile: XCD-contiguous numbering of (request, kv head, query tile)
-  const int32_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
-  int32_t t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  int32_t b = 0;
-  int32_t ntile = 0;
-  for (; b < p.batch; ++b) {
-    ntile = (new_count(p, b) + kTQ - 1) / kTQ;
-    const int32_t tb = ntile * p.kv_heads;
-    if (t < tb) break;
-    t -= tb;
-  }
-  if (b >= p.batch) return;
-  const int32_t g = t / ntile;
-  const int32_t qt = t % ntile;
-
+// General tile: the band staged in chunks of up to 9 blocks, online softmax
+// across chunks, per-key masks on blocks that touch the band's edges.
+template <int MB>
+__device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile &tl, const bf16x8_t (&qop)[MB][4],
+                             int32_t g, uint16_t *ktile, uint16_t *vtile, f32x4_t (&acc)[MB][8], float (&m_run)[MB],
+                             float (&l_run)[MB]) {
   const int32_t lane = threadIdx.x & 63;
-  const int32_t w = threadIdx.x >> 6;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
-  const int32_t G = p.group;
   const int32_t W = p.window;
+  const int32_t qpos = tl.i0 + kr;  // position of the query in this lane's column
+  for (int32_t c0 = 0; c0 < tl.nkeys; c0 += kKB * 16) {
+    const int32_t nbk = min(kKB, (tl.nkeys - c0 + 15) / 16);
+    const int32_t chunk_pos = tl.kj0 + c0;  // position of key 0 of the chunk
 
-  const int32_t n_new = new_count(p, b);
-  int32_t seq = p.seq_lens[b];
-  if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
-  const int32_t prefix = p.prefix_lens[b];
-  const int32_t row0 = p.qo_indptr[b] + qt * kTQ;      // first q row of the tile
-  const int32_t i0 = prefix + qt * kTQ;                 // its position
-  int32_t i_last = i0 + kTQ - 1;                        // last position of the tile
-  if (i_last > prefix + n_new - 1) i_last = prefix + n_new - 1;
-  if (i_last > seq - 1) i_last = seq - 1;
-  int32_t kj0 = W < 0 ? 0 : i0 - W;                     // first key position of the band
-  if (kj0 < 0) kj0 = 0;
-  const int32_t nkeys = i_last >= kj0 ? i_last - kj0 + 1 : 0;
-
-  // key position -> slot
-  const int32_t *src = nullptr;
-  int64_t src_hi = 0;  // valid index range into src: [0, src_hi)
-  int32_t pos_base = 0;  // position of src[0]
-  if (p.indptr) {
-    int64_t lo = p.indptr[b], hi = p.indptr[b + 1];
-    if (lo < 0) lo = 0;
-    if (hi > p.capacity) hi = p.capacity;
-    src = p.table + lo;
-    src_hi = hi > lo ? hi - lo : 0;
-    pos_base = W < 0 ? 0 : prefix - W;
-    if (pos_base < 0) pos_base = 0;
-  } else {
-    int64_t row = p.req_idx[b];
-    if (row < 0 || row >= p.r2t_rows) row = 0;
-    src = p.r2t + row * p.r2t_stride;
-    src_hi = p.r2t_stride;
-  }
-
-  // ---- Q^T operands: query kr of the tile, heads w*MB + m, dims 32lq..32lq+31.
-  // Rows past the request (last partial tile) and padding heads read a real
-  // row; their columns are never stored.
-  const bool qvalid = (qt * kTQ + kr) < n_new && static_cast<int64_t>(row0) + kr < p.total_q;
-  const int64_t qrow = qvalid ? static_cast<int64_t>(row0) + kr : static_cast<int64_t>(row0);
-  bf16x8_t qop[MB][4];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int32_t hh = w * MB + m;
-    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + (qrow * p.q_heads + g * G + (hh < G ? hh : 0)) * kD +
-                                                      32 * lq);
-    uint4 raw[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = qp[c];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) __builtin_memcpy(&qop[m][c], &raw[c], 16);
-  }
-
-  f32x4_t acc[MB][8];
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[MB], l_run[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    m_run[m] = kNegBig;
-    l_run[m] = 0.f;
-  }
-  const int32_t qpos = i0 + kr;  // position of the query in this lane's column
-
-  // steady-state tile (see tile_fast): W = 128, 16 valid queries, band inside
-  // the request and inside its key source
-  const bool fast = W == 16 * (kKB - 1) && i0 - W >= 0 && qt * kTQ + kTQ <= n_new && i_last == i0 + kTQ - 1 &&
-                    static_cast<int64_t>(kj0) - pos_base >= 0 &&
-                    static_cast<int64_t>(kj0) - pos_base + 16 * kKB <= src_hi;
-  if (fast) {
-    tile_fast<kKB, MB>(p, ktile, vtile, qop, src + (kj0 - pos_base), g, acc, m_run, l_run);
-  } else
-  for (int32_t c0 = 0; c0 < nkeys; c0 += kKB * 16) {
-    const int32_t nbk = min(kKB, (nkeys - c0 + 15) / 16);
-    const int32_t chunk_pos = kj0 + c0;  // position of key 0 of the chunk
-
-    // ---- stage K and V rows of the chunk in LDS (16 threads per 256-byte row).
-    // Every thread issues all its loads before writing any (no control flow
-    // between loads); keys past the band re-read the chunk's first key and are
-    // zeroed when written to LDS.
-    __syncthreads();  // previous chunk fully consumed
+    // ---- stage K and V rows of the chunk in LDS (16 threads per 256-byte
+    // row).  Every thread issues all its loads before writing any; keys past
+    // the band re-read the chunk's first key and are zeroed when written.
+    __syncthreads();  // previous chunk (or tile) fully consumed
     {
-      const int32_t piece = threadIdx.x & 15;
       int32_t slot[kKB];
-      if (src_hi > 0) {  // workgroup-uniform
-#pragma unroll
-        for (int i = 0; i < kKB; ++i) {
-          const int32_t key = (threadIdx.x >> 4) + 16 * i;
-          const bool kv_ok = i < nbk && c0 + key < nkeys;
-          const int64_t si = static_cast<int64_t>(chunk_pos + (kv_ok ? key : 0)) - pos_base;
-          slot[i] = src[si >= 0 && si < src_hi ? si : 0];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kKB; ++i) slot[i] = 0;
-      }
-      int64_t off[kKB];
-#pragma unroll
-      for (int i = 0; i < kKB; ++i) {
-        const int64_t sl = (slot[i] < 0 || slot[i] >= p.rows) ? 0 : static_cast<int64_t>(slot[i]);
-        off[i] = row_elem(sl, p.kv_heads, g, kD) + 8 * piece;
-      }
-      uint4 kreg[kKB], vreg[kKB];
-#pragma unroll
-      for (int i = 0; i < kKB; ++i) kreg[i] = *reinterpret_cast<const uint4 *>(p.k + off[i]);
-#pragma unroll
-      for (int i = 0; i < kKB; ++i) vreg[i] = *reinterpret_cast<const uint4 *>(p.v + off[i]);
 #pragma unroll
       for (int i = 0; i < kKB; ++i) {
         const int32_t key = (threadIdx.x >> 4) + 16 * i;
-        const bool kv_ok = i < nbk && c0 + key < nkeys;
-        const uint4 kz = kv_ok ? kreg[i] : make_uint4(0, 0, 0, 0);
-        const uint4 vz = kv_ok ? vreg[i] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(ktile + key * kKRow + 8 * piece) = kz;
-        *reinterpret_cast<uint4 *>(vtile + key * kVRow + 8 * piece) = vz;
+        const bool kv_ok = i < nbk && c0 + key < tl.nkeys;
+        slot[i] = slot_at(ks, chunk_pos + (kv_ok ? key : 0));
+      }
+      uint4 kreg[kKB], vreg[kKB];
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) fetch_piece(p, slot[i], g, kreg[i], vreg[i]);
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) {
+        const int32_t key = (threadIdx.x >> 4) + 16 * i;
+        const bool kv_ok = i < nbk && c0 + key < tl.nkeys;
+        put_piece(ktile, vtile, key, kv_ok ? kreg[i] : make_uint4(0, 0, 0, 0),
+                  kv_ok ? vreg[i] : make_uint4(0, 0, 0, 0));
       }
     }
     __syncthreads();
@@ -363,12 +363,13 @@ __global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       const int32_t j0 = chunk_pos + kb * 16;
-      const bool interior = kb < nbk && c0 + kb * 16 + 15 < nkeys && j0 + 15 <= i0 && (W < 0 || j0 >= i_last - W);
+      const bool interior =
+          kb < nbk && c0 + kb * 16 + 15 < tl.nkeys && j0 + 15 <= tl.i0 && (W < 0 || j0 >= tl.i_last - W);
       if (!interior) {  // workgroup-uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t j = j0 + 4 * lq + r;
-          const bool ok = kb < nbk && (c0 + kb * 16 + 4 * lq + r) < nkeys && j <= qpos && (W < 0 || j >= qpos - W);
+          const bool ok = kb < nbk && (c0 + kb * 16 + 4 * lq + r) < tl.nkeys && j <= qpos && (W < 0 || j >= qpos - W);
 #pragma unroll
           for (int m = 0; m < MB; ++m) sacc[m][kb][r] = ok ? sacc[m][kb][r] : -INFINITY;
         }
@@ -402,9 +403,8 @@ __global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
       }
     }
 
-    // ---- O^T += V^T P^T over block pairs (2u, 2u+1).  The V^T operand comes
-    // straight from the row-major tile with transposing LDS reads: lane (kr, lq)
-    // gets V[4lq + e][16n + kr], e = 0..3, of each block of the pair.
+    // ---- O^T += V^T P^T over block pairs (2u, 2u+1): lane (kr, lq) gets
+    // V[4lq + e][16n + kr], e = 0..3, of each block of the pair.
     const uint16_t *vrow = vtile + (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
 #pragma unroll
     for (int u = 0; u < (kKB + 1) / 2; ++u) {
@@ -433,8 +433,18 @@ __global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
       }
     }
   }
+}
 
-  // ---- finalize: sink once, normalise, store
+// Sink once, normalise, store this lane's query row of every head of the wave.
+template <int MB, bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const ExtendParams &p, f32x4_t (&acc)[MB][8], const float (&m_run)[MB],
+                                           const float (&l_run)[MB], const float (&sink2)[MB], int32_t g,
+                                           int32_t row0, bool qvalid) {
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  const int32_t G = p.group;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
@@ -443,15 +453,14 @@ __global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
     const int32_t h = g * G + hh;
     float M = m_run[m];
     float L = l;
+    float a = 1.f;
     if (p.sinks) {
-      const float sig2 = p.sinks[h] * kLog2e;
+      const float sig2 = sink2[m];
       const float Mn = fmaxf(M, sig2);
-      L = L * exp2f(M - Mn) + exp2f(sig2 - Mn);
-      const float a = exp2f(M - Mn);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) acc[m][n] *= a;
+      a = __builtin_amdgcn_exp2f(M - Mn);
+      L = L * a + __builtin_amdgcn_exp2f(sig2 - Mn);
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = L > 0.f ? a / L : 0.f;
     const int64_t obase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + h) * kD + 4 * lq;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
@@ -467,6 +476,306 @@ __global__ void __launch_bounds__(kNW * 64, 2) extend_kernel(ExtendParams p) {
   }
 }
 
+// A finished tile's normalised output for this lane, packed for its stores.
+template <int MB, bool OUT_BF16>
+struct TileOut;
+template <int MB>
+struct TileOut<MB, true> {
+  uint2 v[MB][8];
+};
+template <int MB>
+struct TileOut<MB, false> {
+  float4 v[MB][8];
+};
+
+template <int MB, bool OUT_BF16>
+__device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t (&acc)[MB][8],
+                                            const float (&m_run)[MB], const float (&l_run)[MB],
+                                            const float (&sink2)[MB], TileOut<MB, OUT_BF16> &o) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const float M = m_run[m];
+    float L = wave_sum_q(l_run[m]);
+    float a = 1.f;
+    if (p.sinks) {
+      const float Mn = fmaxf(M, sink2[m]);
+      a = __builtin_amdgcn_exp2f(M - Mn);
+      L = L * a + __builtin_amdgcn_exp2f(sink2[m] - Mn);
+    }
+    const float inv = L > 0.f ? a / L : 0.f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const float o0 = acc[m][n][0] * inv, o1 = acc[m][n][1] * inv, o2 = acc[m][n][2] * inv,
+                  o3 = acc[m][n][3] * inv;
+      if constexpr (OUT_BF16)
+        o.v[m][n] = make_uint2(pack_bf16x2_hw(o0, o1), pack_bf16x2_hw(o2, o3));
+      else
+        o.v[m][n] = make_float4(o0, o1, o2, o3);
+    }
+  }
+}
+
+template <int MB, bool OUT_BF16>
+__device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<MB, OUT_BF16> &o, int32_t g,
+                                           int32_t row0) {
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int32_t hh = w * MB + m;
+    if (hh >= p.group) continue;
+    const int64_t obase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + g * p.group + hh) * kD + 4 * lq;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if constexpr (OUT_BF16)
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + obase + 16 * n) = o.v[m][n];
+      else
+        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + obase + 16 * n) = o.v[m][n];
+    }
+  }
+}
+
+template <int MB>
+__device__ __forceinline__ void q_operands(const uint4 (&raw)[MB][4], bf16x8_t (&qop)[MB][4]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) __builtin_memcpy(&qop[m][c], &raw[m][c], 16);
+}
+
+// The tiles [qt_begin, qt_end) of request b, kv head g ("a run") are done in
+// two passes: the steady tiles through the ring (run_steady), then the other
+// tiles (band clipped at position 0, partial tiles, other windows) through the
+// general path (run_general).  Tiles are independent; the kernel runs all
+// first passes of its runs, then all second passes, which keeps the two
+// paths' registers apart.
+template <int MB, bool OUT_BF16>
+__device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
+                                          int32_t g, int32_t qt_begin, int32_t qt_end) {
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  const int32_t row = threadIdx.x >> 4;  // K/V row this thread stages within a block
+
+  // Everything the tile loop needs from memory about the request (and the
+  // sinks of this wave's heads) is read once here: a load inside the loop
+  // would make the wave wait for all of its older memory operations, i.e. the
+  // previous tile's output stores and the prefetches.
+  const int32_t n_new = new_count(p, b);
+  const int32_t qo0 = p.qo_indptr[b];
+  int32_t seq = p.seq_lens[b];
+  if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
+  const int32_t prefix = p.prefix_lens[b];
+  const KeySrc ks = key_src(p, b, prefix);
+  float sink2[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int32_t hh = w * MB + m;
+    sink2[m] = (p.sinks && hh < p.group) ? p.sinks[g * p.group + hh] * kLog2e : 0.f;
+  }
+
+  // gfx950 counts global loads and stores on one counter and they may retire
+  // out of order, so waiting for any load while stores are outstanding waits
+  // for the stores too.  A steady tile therefore waits for memory at one point
+  // only, its top, where everything it needs arrives together (issued one tile
+  // earlier); the previous tile's output is stored right after that wait
+  // (bf16 output), so its stores have a whole tile to drain before the next.
+  int32_t qt = qt_begin;
+  while (qt < qt_end) {
+    Tile tl = tile_at(p, ks, qo0, qt, prefix, n_new, seq);
+    if (!tl.steady) {
+      ++qt;
+      continue;
+    }
+    // ---- a stretch of steady tiles starts: fill the ring with the whole band
+    // of its first tile (slots 0..8), all 18 loads in flight before the first
+    // LDS write waits for one.
+    uint4 qraw[MB][4];
+    load_q<MB>(p, static_cast<int64_t>(tl.row0) + kr, g, w, lq, qraw);
+    bool next_steady = qt + 1 < qt_end && tile_at(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
+    int32_t nslot;  // slot of this thread's row of the next tile's band block 8
+    {
+      int32_t sl[kKB];
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) sl[i] = slot_in(ks, tl.kj0 + 16 * i + row);
+      // (a position that is not needed re-reads one inside this band: no branch)
+      nslot = slot_in(ks, next_steady ? tl.kj0 + kBand + row : tl.kj0 + row);
+      lds_barrier();  // other waves may still read an earlier band
+      uint4 kreg[kKB], vreg[kKB];
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) fetch_piece(p, sl[i], g, kreg[i], vreg[i]);
+#pragma unroll
+      for (int i = 0; i < kKB; ++i) put_piece(ktile, vtile, 16 * i + row, kreg[i], vreg[i]);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * kKB, 0);  // the 18 global loads first,
+      __builtin_amdgcn_sched_group_barrier(0x200, 2 * kKB, 0);  // then the 18 LDS writes
+      lds_barrier();
+    }
+    // ---- stream: this tile, then the next while it is steady.  Each tile
+    // waits for memory only at its top, where the block, slots and queries
+    // issued one tile earlier arrive together.
+    int32_t q0 = 0;  // ring slot of band block 0
+    bool first = true;
+    bool have_o = false;
+    int32_t pend_row0 = 0;
+    TileOut<MB, OUT_BF16> pend;
+    uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
+    for (;;) {
+      if (!first) {
+        lds_barrier();  // every wave is done with the previous tile: its band block 0 slot is free
+        put_piece(ktile, vtile, ring_slot(q0, kKB - 1) * 16 + row, nk, nv);  // this tile's band block 8
+        lds_barrier();
+      }
+      first = false;
+      if (have_o) {  // the previous tile's output (bf16): its stores drain during this tile
+        write_tile<MB, OUT_BF16>(p, pend, g, pend_row0);
+        have_o = false;
+      }
+      // ---- in flight during this tile: the next tile's band block 8, the
+      // slots of the one after, and the next tile's queries
+      uint4 qn[MB][4];
+      if (next_steady) {
+        fetch_piece(p, nslot, g, nk, nv);
+        const bool next2 = qt + 2 < qt_end && tile_at(p, ks, qo0, qt + 2, prefix, n_new, seq).steady;
+        nslot = slot_in(ks, next2 ? tl.kj0 + 16 + kBand + row : tl.kj0 + row);
+        load_q<MB>(p, static_cast<int64_t>(tl.row0) + kTQ + kr, g, w, lq, qn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4_t acc[MB][8];  // written by ring_pv
+      float m_run[MB], l_run[MB];
+      f32x4_t sacc[MB][kKB];
+      {
+        bf16x8_t qop[MB][4];
+        q_operands<MB>(qraw, qop);
+        ring_scores<MB>(p, ktile, q0, qop, sacc, m_run, l_run);
+      }
+      ring_pv<MB>(vtile, q0, sacc, acc);
+      if constexpr (OUT_BF16) {
+        finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, pend);
+        pend_row0 = tl.row0;
+        have_o = true;
+      } else {
+        TileOut<MB, OUT_BF16> o;
+        finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
+        write_tile<MB, OUT_BF16>(p, o, g, tl.row0);
+      }
+      ++qt;
+      if (!next_steady) break;
+      tl = tile_at(p, ks, qo0, qt, prefix, n_new, seq);
+      next_steady = qt + 1 < qt_end && tile_at(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
+      q0 = q0 + 1 < kKB ? q0 + 1 : 0;
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qraw[m][c] = qn[m][c];
+    }
+    if (have_o) write_tile<MB, OUT_BF16>(p, pend, g, pend_row0);
+  }
+}
+
+template <int MB, bool OUT_BF16>
+__device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
+                                           int32_t g, int32_t qt_begin, int32_t qt_end) {
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+
+  // Everything the tile loop needs from memory about the request (and the
+  // sinks of this wave's heads) is read once here: a load inside the loop
+  // would make the wave wait for all of its older memory operations, i.e. the
+  // previous tile's output stores and the prefetches.
+  const int32_t n_new = new_count(p, b);
+  const int32_t qo0 = p.qo_indptr[b];
+  int32_t seq = p.seq_lens[b];
+  if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
+  const int32_t prefix = p.prefix_lens[b];
+  const KeySrc ks = key_src(p, b, prefix);
+  float sink2[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int32_t hh = w * MB + m;
+    sink2[m] = (p.sinks && hh < p.group) ? p.sinks[g * p.group + hh] * kLog2e : 0.f;
+  }
+
+  for (int32_t qt = qt_begin; qt < qt_end; ++qt) {
+    const Tile tl = tile_at(p, ks, qo0, qt, prefix, n_new, seq);
+    if (tl.steady) continue;
+    const bool qvalid = (qt * kTQ + kr) < n_new && static_cast<int64_t>(tl.row0) + kr < p.total_q;
+    f32x4_t acc[MB][8];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[MB], l_run[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      m_run[m] = kNegBig;
+      l_run[m] = 0.f;
+    }
+    // rows past the request (last partial tile) read a real row; never stored
+    uint4 qr[MB][4];
+    load_q<MB>(p, qvalid ? static_cast<int64_t>(tl.row0) + kr : static_cast<int64_t>(tl.row0), g, w, lq, qr);
+    bf16x8_t qop[MB][4];
+    q_operands<MB>(qr, qop);
+    tile_general<MB>(p, ks, tl, qop, g, ktile, vtile, acc, m_run, l_run);
+    store_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, g, tl.row0, qvalid);
+  }
+}
+
+// Run r of the numbering (request, kv head, run of T tiles); b = -1 past the end.
+struct Run {
+  int32_t b, g, qt_begin, qt_end;
+};
+
+__device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t r) {
+  int32_t t = r, b = 0, ntile = 0, nrun = 0;
+  for (; b < p.batch; ++b) {
+    ntile = (new_count(p, b) + kTQ - 1) / kTQ;
+    nrun = (ntile + T - 1) / T;
+    const int32_t tb = nrun * p.kv_heads;
+    if (t < tb) break;
+    t -= tb;
+  }
+  Run run{-1, 0, 0, 0};
+  if (b >= p.batch) return run;
+  run.b = b;
+  run.g = t / nrun;
+  run.qt_begin = (t % nrun) * T;
+  run.qt_end = run.qt_begin + T < ntile ? run.qt_begin + T : ntile;
+  return run;
+}
+
+// Persistent grid (about two workgroups per CU): the runs, numbered
+// (request, kv head, run), are split into 8 contiguous ranges, one per XCD
+// (workgroup i runs on XCD i % 8), so neighbouring runs, which share band
+// blocks, meet in one L2; the workgroups of an XCD stride through its range.
+template <int MB, bool OUT_BF16>
+__global__ void __launch_bounds__(kNW * 64, MB >= 4 ? 1 : 2) extend_kernel(ExtendParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
+  const int32_t T = p.run_tiles;
+  int32_t total = 0;
+  for (int32_t b = 0; b < p.batch; ++b) total += (new_count(p, b) + kTQ * T - 1) / (kTQ * T) * p.kv_heads;
+  const int32_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
+  const int32_t x = blockIdx.x % 8;
+  const int32_t r_lo = static_cast<int32_t>(static_cast<int64_t>(total) * x / 8);
+  const int32_t r_hi = static_cast<int32_t>(static_cast<int64_t>(total) * (x + 1) / 8);
+  const int32_t r0 = r_lo + static_cast<int32_t>(blockIdx.x / 8);
+  for (int32_t r = r0; r < r_hi; r += per_xcd) {
+    const Run run = run_of(p, T, r);
+    if (run.b < 0) break;
+    run_steady<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+  }
+  for (int32_t r = r0; r < r_hi; r += per_xcd) {
+    const Run run = run_of(p, T, r);
+    if (run.b < 0) break;
+    run_general<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+  }
+}
+
 template <int MB>
 hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStream_t stream) {
   if (out_bf16)
@@ -475,6 +784,10 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
     hipLaunchKernelGGL((extend_kernel<MB, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
+
+// Workgroups of the persistent grid: two per CU of the 256 on MI355X (the LDS
+// ring allows two).
+constexpr int64_t kResidentGroups = 512;
 
 }  // namespace
 
@@ -504,15 +817,25 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   p.sinks = a.sinks;
   p.scale2 = a.sm_scale * kLog2e;
   p.out = a.out;
-  // Upper bound of the tile count: every request adds at most one partial tile.
-  int64_t tiles = ((a.total_q + kTQ - 1) / kTQ + a.idx.batch) * a.layer.kv_heads;
-  tiles = (tiles + 7) / 8 * 8;
-  if (tiles > 0x7FFFFFF8LL) return hipErrorInvalidValue;
-  const bool out_bf16 = a.out_dtype == SWA_BF16;
+  // Tiles: every request adds at most one partial tile.  Runs of T tiles, about
+  // one run per workgroup of the persistent grid (each run fills its ring once,
+  // so fewer, longer runs are cheaper; more runs than workgroups would leave
+  // some workgroups a second run while others idle).
   const int32_t mb = p.group >= 16 ? 4 : (p.group >= 8 ? 2 : 1);
-  if (mb == 4) return launch_mb<4>(p, static_cast<uint32_t>(tiles), out_bf16, stream);
-  if (mb == 2) return launch_mb<2>(p, static_cast<uint32_t>(tiles), out_bf16, stream);
-  return launch_mb<1>(p, static_cast<uint32_t>(tiles), out_bf16, stream);
+  const int64_t resident = mb == 4 ? kResidentGroups / 2 : kResidentGroups;  // G = 16: one per CU
+  const int64_t tiles = ((a.total_q + kTQ - 1) / kTQ + a.idx.batch) * a.layer.kv_heads;
+  int64_t T = tiles / resident;
+  if (T < 1) T = 1;
+  if (T > 64) T = 64;
+  p.run_tiles = static_cast<int32_t>(T);
+  int64_t grid = (tiles + T - 1) / T + static_cast<int64_t>(a.idx.batch) * a.layer.kv_heads;
+  if (grid > resident) grid = resident;
+  grid = (grid + 7) / 8 * 8;
+  const uint32_t runs = static_cast<uint32_t>(grid);
+  const bool out_bf16 = a.out_dtype == SWA_BF16;
+  if (mb == 4) return launch_mb<4>(p, static_cast<uint32_t>(runs), out_bf16, stream);
+  if (mb == 2) return launch_mb<2>(p, static_cast<uint32_t>(runs), out_bf16, stream);
+  return launch_mb<1>(p, static_cast<uint32_t>(runs), out_bf16, stream);
 }
 
 }  // namespace swa

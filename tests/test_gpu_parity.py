@@ -443,6 +443,24 @@ def test_extend_small(name):
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
+def test_extend_tile_runs_sampled():
+    """Enough tiles that every workgroup walks a run of several tiles (band
+    blocks rotating through the LDS ring), mixed with band-clipped and
+    partial tiles in the same runs."""
+    say("extend tile runs (3 requests, 64q/8kv) — sampled rows")
+    wl = WL.extend_workload("runs", 77, [300, 129, 16], [1500, 700, 1000], 64, 8, 128, 16, sinks=True)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_extend(dw, "f32")
+    total = wl.q.shape[0]
+    rows = np.unique(np.concatenate([np.arange(0, total, 3), np.arange(total - 20, total),
+                                     np.arange(1480, 1530), np.arange(2180, 2230)]))
+    only = [(int(r), h) for r in rows for h in range(wl.q_heads)]
+    check(out, oracle_extend(wl, only=only), TOL["bf16"], "runs sampled")
+    out_bf = run_extend(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
 def test_extend_c3_full_size_sampled():
     wl = WL.c3_extend_bf16()
     say("extend c3 (4 x (8K prefix + 2K chunk), bf16) — sampled rows")
