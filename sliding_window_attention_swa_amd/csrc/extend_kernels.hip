@@ -160,8 +160,11 @@ __device__ __forceinline__ Tile tile_at(const ExtendParams &p, const KeySrc &ks,
 // Slot of a key position known to lie inside the key source (steady tiles).
 __device__ __forceinline__ int32_t slot_in(const KeySrc &ks, int32_t pos) { return ks.src[pos - ks.pos_base]; }
 
-// Q^T operands of this lane: query row `qrow`, heads w*MB + m, dims 32lq..32lq+31
-// (padding heads read a real head; their columns are never stored).
+// Q^T operands of this lane: query row `qrow`, heads w*MB + m.  Contraction
+// block c takes dims 32c + 8lq .. +7 from lane group lq (K operands are read
+// from LDS in the same order), so each load instruction reads 64 contiguous
+// bytes of every query row.  Padding heads read a real head; their columns
+// are never stored.
 template <int MB>
 __device__ __forceinline__ void load_q(const ExtendParams &p, int64_t qrow, int32_t g, int32_t w, int32_t lq,
                                        uint4 (&raw)[MB][4]) {
@@ -169,10 +172,9 @@ __device__ __forceinline__ void load_q(const ExtendParams &p, int64_t qrow, int3
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    const uint4 *qp =
-        reinterpret_cast<const uint4 *>(p.q + (qrow * p.q_heads + g * G + (hh < G ? hh : 0)) * kD + 32 * lq);
+    const uint16_t *qp = p.q + (qrow * p.q_heads + g * G + (hh < G ? hh : 0)) * kD + 8 * lq;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) raw[m][c] = qp[c];
+    for (int c = 0; c < 4; ++c) raw[m][c] = *reinterpret_cast<const uint4 *>(qp + 32 * c);
   }
 }
 
@@ -213,9 +215,9 @@ __device__ __forceinline__ void ring_scores(const ExtendParams &p, const uint16_
 #pragma unroll
   for (int j = 0; j < kKB; ++j) {
     bf16x8_t kop[4];
-    const uint16_t *kp = ktile + (slot[j] * 16 + kr) * kKRow + 32 * lq;
+    const uint16_t *kp = ktile + (slot[j] * 16 + kr) * kKRow + 8 * lq;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 8 * c, 16);
+    for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 32 * c, 16);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       sacc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -346,9 +348,9 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
       for (int m = 0; m < MB; ++m) sacc[m][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       if (kb < nbk) {
         bf16x8_t kop[4];
-        const uint16_t *kp = ktile + (kb * 16 + kr) * kKRow + 32 * lq;
+        const uint16_t *kp = ktile + (kb * 16 + kr) * kKRow + 8 * lq;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 8 * c, 16);
+        for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 32 * c, 16);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
