@@ -13,7 +13,8 @@ step of that batch through a stack of 32 SWA layers, each with its own K/V
 pool (so the 256 MB Infinity Cache cannot serve repeats):
     translate_loc (new tokens' full locs -> SWA slots)    once per step
     translate_window (req_to_token -> full -> SWA slots)  once per step
-    per layer: kv_store (new token K/V) + swa_decode
+    per layer: swa_decode_store (the new token's K/V store fused into the
+               windowed decode; equal to kv_store followed by swa_decode)
 The step is captured once as a HIP graph and replayed; inputs are resident in
 HBM before timing starts.  The JSON line reports algorithmic HBM bytes per
 second of the whole step, the dominant kernel's roofline (swa_decode, timed
@@ -143,7 +144,16 @@ class DecodeBench:
         self.decode_bytes = int(n_keys.sum() * Hkv * D * kv_b * 2 + B * Hq * D * (q_b + o_b) + n_keys.sum() * 4
                                 + (B + 1) * 4)
         new_b = 2 if wl.kv_dtype != "f32" else 4
-        self.store_bytes = B * Hkv * D * 2 * (new_b + kv_b) + B * 8 if self.has_store else 0
+        # The new token's store is fused into the decode launch (swa_decode_store):
+        # its K/V are read once, as the window's last row (counted in
+        # decode_bytes), and written once to the pool (counted here).
+        # (bf16 pools only: the e4m3 variant needs more registers, which costs
+        # a workgroup per CU, more than the separate store launch costs)
+        self.fused = self.has_store and wl.kv_dtype == "bf16" and 0 <= wl.window <= 255
+        if self.fused:
+            self.store_bytes = B * Hkv * D * kv_b * 2 + B * 8
+        else:
+            self.store_bytes = B * Hkv * D * 2 * (new_b + kv_b) + B * 8 if self.has_store else 0
         self.translate_bytes = (B * 8 * 3 if self.has_store else 0) + int(n_keys.sum()) * (4 + 8 + 4) + B * 12
         self.step_bytes = self.translate_bytes + layers * (self.store_bytes + self.decode_bytes)
         self.flops_decode = int(n_keys.sum()) * Hq * D * 4
@@ -154,17 +164,31 @@ class DecodeBench:
             swa.swa_translate_loc(self.full_loc, self.map, self.swa_loc)
         swa.swa_translate_window(self.index, wl.window, self.table, self.indptr)
         for ly in self.layers:
-            if self.has_store:
-                swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
-            swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                           slot_table=self.table, table_indptr=self.indptr)
+            self.layer_call(ly)
+
+    def layer_call(self, ly):
+        swa, wl = self.swa, self.wl
+        if self.fused:
+            swa.swa_decode_store(ly["q"], ly["kv"], self.index, wl.window, ly["out"], self.swa_loc, ly["new_k"],
+                                 ly["new_v"], sinks=self.sinks, slot_table=self.table, table_indptr=self.indptr)
+            return
+        if self.has_store:
+            swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
+        swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                       slot_table=self.table, table_indptr=self.indptr)
 
     def dominant(self):
-        """Back-to-back decode launches only (one per layer)."""
+        """Back-to-back decode launches only (one per layer; with the store fused
+        in when the step fuses it)."""
         swa, wl = self.swa, self.wl
         for ly in self.layers:
-            swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                           slot_table=self.table, table_indptr=self.indptr)
+            if self.fused:
+                swa.swa_decode_store(ly["q"], ly["kv"], self.index, wl.window, ly["out"], self.swa_loc,
+                                     ly["new_k"], ly["new_v"], sinks=self.sinks, slot_table=self.table,
+                                     table_indptr=self.indptr)
+            else:
+                swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                               slot_table=self.table, table_indptr=self.indptr)
 
 
 def graph_of(torch, fn):
@@ -262,7 +286,8 @@ def run_decode_workload(args, torch, swa, W):
     pct = replay_percentiles(torch, g_dec, dec_reps, layers)
     log(f"[bench] swa_decode {ms_dec * 1e3:.2f} us per launch")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
-    achieved = bench.decode_bytes / (ms_dec * 1e-3) / 1e9
+    dom_bytes = bench.decode_bytes + (bench.store_bytes if bench.fused else 0)
+    achieved = dom_bytes / (ms_dec * 1e-3) / 1e9
     traffic = traffic_from_profile(f"swa_decode_{name}", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1)
     res = dict(
         metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -273,9 +298,10 @@ def run_decode_workload(args, torch, swa, W):
         tokens_per_s=round(wl.batch / (ms * 1e-3), 1),
         layer_tokens_per_s=round(wl.batch * layers / (ms * 1e-3), 1),
         frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
-        roofline=dict(kernel="swa_decode", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+        roofline=dict(kernel="swa_decode_store (store fused)" if bench.fused else "swa_decode", bound="hbm",
+                      achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                       unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                      bytes_per_launch=bench.decode_bytes, us_per_launch=round(ms_dec * 1e3, 3), **pct),
+                      bytes_per_launch=dom_bytes, us_per_launch=round(ms_dec * 1e3, 3), **pct),
     )
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

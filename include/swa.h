@@ -187,6 +187,26 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * decode with the current token's store fused in — the same result as
+ *   swa_kv_store(layer, loc, batch, k_new, v_new, new_dtype);
+ *   swa_decode(..., num_splits = 1, ...);
+ * in one launch ([SWA] Attention backend: the new token's K/V are written to
+ * the layer's pool right before its attention; [POOLS] 谁在往页里写).
+ * loc (batch): the pool slot of each request's current token, i.e. of
+ * position seq_lens[b] - 1, which its window's last entry resolves to (SWA
+ * layers: the translated swa_loc); a loc outside [0, rows) is not stored.
+ * k_new, v_new: bf16 (batch, kv_heads, head_dim), 16-byte aligned.  The
+ * current token is attended from these rows converted to the pool format
+ * exactly as stored.  Supported: windowed layers with 0 <= window <= 255,
+ * bf16 q, bf16 or e4m3 pools, new_dtype SWA_BF16; other cases return
+ * SWA_E_DTYPE / SWA_E_SHAPE (use the two calls). */
+swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                              const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                              int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
+                              const int64_t *loc, const void *k_new, const void *v_new, int32_t new_dtype,
+                              void *out, int32_t out_dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * extend — windowed-causal prefill of a chunk over a cached prefix ([SWA]
  * 运行时: chunked prefill; same formula as decode).  Request b owns query rows
  * qo_indptr[b] .. qo_indptr[b+1]-1 holding positions prefix_lens[b] ..

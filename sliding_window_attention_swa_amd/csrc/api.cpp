@@ -135,11 +135,16 @@ swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, i
   return SWA_OK;
 }
 
-swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
-                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
-                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
-                        int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by swa_decode and swa_decode_store (loc == null: no store).
+swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                         const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                         int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                         int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                         const int64_t *loc, const void *k_new, const void *v_new, hipStream_t stream) {
   swa_status_t st = check_layer(layer);
   if (st != SWA_OK) return st;
   st = check_index(idx, table_indptr == nullptr);
@@ -159,6 +164,11 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
     const size_t need = static_cast<size_t>(idx->batch) * q_heads * num_splits * (2 + kHeadDim) * sizeof(float);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SWA_E_WORKSPACE;
   }
+  if (loc) {
+    if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return SWA_E_ARG;
+    if (!mfma_path) return SWA_E_DTYPE;
+    if (window < 0 || window > swa::kMaxFusedWindow || num_splits != 1) return SWA_E_SHAPE;
+  }
   swa::DecodeArgs a{};
   a.q = q;
   a.q_dtype = q_dtype;
@@ -175,7 +185,35 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
   a.out_dtype = out_dtype;
   a.num_splits = num_splits;
   a.ws = static_cast<float *>(workspace);
+  a.new_loc = loc;
+  a.k_new = k_new;
+  a.v_new = v_new;
   return from_hip(swa::launch_decode(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                        int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return decode_impl(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity, window, sinks,
+                     sm_scale, out, out_dtype, num_splits, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                     stream);
+}
+
+swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                              const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                              int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
+                              const int64_t *loc, const void *k_new, const void *v_new, int32_t new_dtype,
+                              void *out, int32_t out_dtype, hipStream_t stream) {
+  if (!loc) return SWA_E_ARG;
+  if (new_dtype != SWA_BF16) return SWA_E_DTYPE;
+  return decode_impl(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity, window, sinks,
+                     sm_scale, out, out_dtype, 1, nullptr, 0, loc, k_new, v_new, stream);
 }
 
 swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,

@@ -107,7 +107,14 @@ struct DecodeArgs {
   int32_t out_dtype;
   int32_t num_splits;
   float *ws;  // partials: m, l (batch*q_heads*num_splits each), acc (... * head_dim)
+  // fused store of the current token (null: none): bf16 (batch, kv_heads,
+  // head_dim) rows written to pool slot new_loc[b]
+  const void *k_new;
+  const void *v_new;
+  const int64_t *new_loc;
 };
+// Largest window the one-split window kernel (and so the fused store) handles.
+constexpr int32_t kMaxFusedWindow = 255;
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,

@@ -70,6 +70,11 @@ struct DecodeParams {
   float *ws_m;
   float *ws_l;
   float *ws_acc;
+  // fused store of the current token (window kernel only): bf16 rows
+  // (batch, kv_heads, head_dim) and their pool slots
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  const int64_t *new_loc;
 };
 
 // Keys of request b for this layer, as [first, first + n) of either the window
@@ -309,6 +314,40 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 &x, uint4 (&out)[2]) 
   out[1] = make_uint4(u[4], u[5], u[6], u[7]);
 }
 
+// Component-wise select (a ternary on the vector struct goes through memory).
+__device__ __forceinline__ uint4 sel4(bool c, const uint4 &a, const uint4 &b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// 16 bf16 -> 16 e4m3 bytes (nearest even, saturating; the pool encoding).
+__device__ __forceinline__ uint4 bf16x16_to_fp8(const uint4 &lo, const uint4 &hi) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint16_t h = static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16));
+    o[e >> 2] |= static_cast<uint32_t>(f32_to_e4m3_rne(bf16_to_f32(h))) << ((e & 3) * 8);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// This lane's pieces of the new token's K / V head rows in the pool format,
+// from their raw bf16 pieces (loaded per Layout<KV>: bf16 pieces as they are,
+// each e4m3 piece from two bf16 pieces).
+template <typename KV>
+__device__ __forceinline__ void new_pieces(const uint4 (&kn_raw)[4], const uint4 (&vn_raw)[2],
+                                           uint4 (&knew)[Layout<KV>::kKLoads], uint4 &vnew) {
+  if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) knew[c] = kn_raw[c];
+    vnew = vn_raw[0];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) knew[c] = bf16x16_to_fp8(kn_raw[2 * c], kn_raw[2 * c + 1]);
+    vnew = bf16x16_to_fp8(vn_raw[0], vn_raw[1]);
+  }
+}
+
 // One block's V rows into its 16-row LDS tile (bf16, kSVRow stride); rows of
 // keys at or past k_end are written as zeros (their slots may hold anything).
 template <typename KV>
@@ -539,7 +578,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 1) decode_stream_kernel(Dec
 // --------------------------------------------------------------------------
 constexpr int kWinWaves = 4;
 
-template <typename KV, int MAXB, bool OUT_BF16>
+template <typename KV, int MAXB, bool OUT_BF16, bool FUSED>
 __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodeParams p) {
   // each wavefront stages one pair of blocks (32 V rows) at a time
   constexpr int kTileBytes = kWinWaves * 32 * kSVRow * 2;
@@ -580,6 +619,29 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   // real head: their columns are never stored.
   uint4 qraw[4];
   load_q<KV>(p, b, g * G + (kr < G ? kr : 0), lq, qraw);
+  // Fused store: the current token (window key n - 1) is attended from the new
+  // rows, converted to the pool format exactly as they are stored at the end.
+  // A lane's piece depends only on its lane position (lanes of a group read the
+  // same addresses); the raw bf16 pieces are loaded by every lane, without a
+  // branch, and converted only by the wavefront that owns key n - 1.
+  uint4 kn_raw[4], vn_raw[2];
+  if constexpr (FUSED) {
+    const uint16_t *krow = p.k_new + (static_cast<int64_t>(b) * p.kv_heads + g) * kD;
+    const uint16_t *vrow_new = p.v_new + (static_cast<int64_t>(b) * p.kv_heads + g) * kD;
+    if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kn_raw[c] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq));
+      vn_raw[0] = *reinterpret_cast<const uint4 *>(vrow_new + Layout<KV>::v_off(lane));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        kn_raw[2 * c] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq));
+        kn_raw[2 * c + 1] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq) + 8);
+      }
+      vn_raw[0] = *reinterpret_cast<const uint4 *>(vrow_new + Layout<KV>::v_off(lane));
+      vn_raw[1] = *reinterpret_cast<const uint4 *>(vrow_new + Layout<KV>::v_off(lane) + 8);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   const KeySource ks = key_source(p, b);
@@ -587,6 +649,8 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   const int32_t *src = ks.src + (ks.n - n);
   const int32_t nblk = (n + 15) >> 4;  // <= kWinWaves * MAXB for this instantiation
   const bool spec_ok = p.indptr && p.capacity > 0 && src == p.table + spec_base;
+  const int32_t owner = ((n > 0 ? n - 1 : 0) >> 4) % kWinWaves;  // wavefront holding key n - 1
+  uint4 knew[kKL], vnew;  // (fused store) the new rows in the pool format, owner wave only
 
   f32x4_t acc[8];
 #pragma unroll
@@ -616,6 +680,21 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
 #pragma unroll
     for (int u = 0; u < MAXB; ++u) load_v<KV>(p, sl[u], g, lane, vraw[u]);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FUSED) {
+      if (w == owner) {  // wave-uniform
+        new_pieces<KV>(kn_raw, vn_raw, knew, vnew);
+        const int32_t last = n - 1;
+#pragma unroll
+        for (int u = 0; u < MAXB; ++u) {
+          const int32_t kb = 16 * (w + kWinWaves * u);
+#pragma unroll
+          for (int c = 0; c < kKL; ++c) kraw[u][c] = sel4(kb + kr == last, knew[c], kraw[u][c]);
+#pragma unroll
+          for (int j = 0; j < kVL; ++j)
+            vraw[u][j] = sel4(kb + Layout<KV>::v_key(j, lane) == last, vnew, vraw[u][j]);
+        }
+      }
+    }
     bf16x8_t qop[4];
     KvLoad<uint16_t>::to_bf16(qraw, qop);
 
@@ -689,6 +768,20 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     }
   }
   __syncthreads();
+  if constexpr (FUSED) {
+    // the owner wavefront stores this kv head's slice of the new row; after every load
+    // (a wait for a load issued after a store would also wait for the store)
+    const int64_t loc = p.new_loc[b];
+    if (w == owner && n > 0 && loc >= 0 && loc < p.rows) {
+      KV *kdst = static_cast<KV *>(const_cast<void *>(p.k)) + row_elem(loc, p.kv_heads, g, kD);
+      KV *vdst = static_cast<KV *>(const_cast<void *>(p.v)) + row_elem(loc, p.kv_heads, g, kD);
+      if (kr == 0) {
+#pragma unroll
+        for (int c = 0; c < kKL; ++c) *reinterpret_cast<uint4 *>(kdst + Layout<KV>::k_off(c, lq)) = knew[c];
+      }
+      if (Layout<KV>::v_key(0, lane) == 0) *reinterpret_cast<uint4 *>(vdst + Layout<KV>::v_off(lane)) = vnew;
+    }
+  }
   merge_waves_and_store<OUT_BF16>(p, kWinWaves, red_m, red_l, red_acc, b, g, 0);
 }
 
@@ -908,10 +1001,18 @@ hipError_t launch_f32(const DecodeParams &p, dim3 grid, hipStream_t stream) {
 
 template <typename KV, int MAXB>
 hipError_t launch_window_b(const DecodeParams &p, dim3 grid, bool out_bf16, hipStream_t stream) {
-  if (out_bf16)
-    hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, true>), grid, dim3(kWinWaves * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, false>), grid, dim3(kWinWaves * 64), 0, stream, p);
+  const dim3 block(kWinWaves * 64);
+  if (p.new_loc) {
+    if (out_bf16)
+      hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, true, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, false, true>), grid, block, 0, stream, p);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, true, false>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_window_kernel<KV, MAXB, false, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -971,13 +1072,19 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     p.ws_l = a.ws + parts;
     p.ws_acc = a.ws + 2 * parts;
   }
+  p.k_new = static_cast<const uint16_t *>(a.k_new);
+  p.v_new = static_cast<const uint16_t *>(a.v_new);
+  p.new_loc = a.new_loc;
   const bool out_bf16 = a.out_dtype == SWA_BF16;
   const dim3 grid(static_cast<uint32_t>(a.num_splits), static_cast<uint32_t>(a.layer.kv_heads),
                   static_cast<uint32_t>(a.idx.batch));
+  const bool window_path = a.num_splits == 1 && a.window >= 0 && a.window < 16 * kWinWaves * 4;
+  // the fused store exists in the window kernel only (bf16 / e4m3 pools)
+  if (a.new_loc && (!window_path || a.layer.dtype == SWA_F32)) return hipErrorInvalidValue;
   hipError_t e;
   if (a.layer.dtype == SWA_F32) {
     e = out_bf16 ? launch_f32<true>(p, grid, stream) : launch_f32<false>(p, grid, stream);
-  } else if (a.num_splits == 1 && a.window >= 0 && a.window < 16 * kWinWaves * 4) {
+  } else if (window_path) {
     // SWA layer: the whole window in flight at once (up to 4 blocks per wavefront)
     e = a.layer.dtype == SWA_BF16 ? launch_window<uint16_t>(p, grid, a.window, out_bf16, stream)
                                   : launch_window<uint8_t>(p, grid, a.window, out_bf16, stream);

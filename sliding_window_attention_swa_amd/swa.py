@@ -25,7 +25,8 @@ SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/swa.h declares
 EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
-           "swa_decode", "swa_extend", "swa_validate_workspace_bytes", "swa_validate", "swa_status_string")
+           "swa_decode", "swa_decode_store", "swa_extend", "swa_validate_workspace_bytes", "swa_validate",
+           "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -74,6 +75,8 @@ _sig = {
     "swa_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_sz)]),
     "swa_decode": (_i32, [_p, _i32, _i32, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct), _p, _p, _i64,
                           _i32, _p, _f32, _p, _i32, _i32, _p, _sz, _p]),
+    "swa_decode_store": (_i32, [_p, _i32, _i32, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct), _p, _p,
+                                _i64, _i32, _p, _f32, _p, _p, _p, _i32, _p, _i32, _p]),
     "swa_extend": (_i32, [_p, _i32, _i32, _p, _p, _i64, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct),
                           _p, _p, _i64, _i32, _p, _f32, _p, _i32, _p]),
     "swa_validate_workspace_bytes": (_sz, [_i64]),
@@ -227,6 +230,29 @@ def swa_decode(q: torch.Tensor, layer: KvLayer, index: IndexTables, window: int,
                           num_splits, _ptr(workspace, name="workspace"),
                           0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)),
            "swa_decode")
+
+
+def swa_decode_store(q: torch.Tensor, layer: KvLayer, index: IndexTables, window: int, out: torch.Tensor,
+                     loc: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                     sinks: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                     slot_table: Optional[torch.Tensor] = None, table_indptr: Optional[torch.Tensor] = None,
+                     use_map: bool = True, stream=None):
+    """swa_kv_store(layer, loc, k_new, v_new) then swa_decode(...) in one launch."""
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be (batch, q_heads, head_dim)")
+    if k_new.shape != v_new.shape or k_new.shape[0] != loc.numel() or loc.numel() != q.shape[0]:
+        raise ValueError("k_new / v_new must be (batch, kv_heads, head_dim) with one loc per request")
+    if tuple(k_new.shape[1:]) != tuple(layer.k.shape[1:]):
+        raise ValueError("new rows must match the pool's (kv_heads, head_dim)")
+    scale = sm_scale if sm_scale is not None else q.shape[2] ** -0.5
+    ls, ix = layer.struct(), index.struct(with_map=use_map)
+    _check(lib.swa_decode_store(_ptr(q, name="q"), dtype_code(q), q.shape[1], ctypes.byref(ls), ctypes.byref(ix),
+                                _ptr(slot_table, torch.int32, "slot_table"),
+                                _ptr(table_indptr, torch.int32, "table_indptr"),
+                                0 if slot_table is None else slot_table.numel(), window,
+                                _ptr(sinks, torch.float32, "sinks"), scale, _ptr(loc, torch.int64, "loc"),
+                                _ptr(k_new, name="k_new"), _ptr(v_new, name="v_new"), dtype_code(k_new),
+                                _ptr(out, name="out"), dtype_code(out), _stream(stream)), "swa_decode_store")
 
 
 def swa_extend(q: torch.Tensor, qo_indptr: torch.Tensor, prefix_lens: torch.Tensor, layer: KvLayer,

@@ -96,6 +96,25 @@ def run_store(dw: DeviceWorkload, in_dtype="bf16"):
     return loc
 
 
+def run_decode_store(dw: DeviceWorkload, out_dtype="f32"):
+    """The fused call: the new tokens' store and the decode in one launch."""
+    from sliding_window_attention_swa_amd import swa
+    wl = dw.wl
+    B = wl.batch
+    full = torch.from_numpy(wl.new_full_loc).cuda()
+    loc = torch.empty_like(full)
+    swa.swa_translate_loc(full, dw.map, loc)
+    table = torch.empty(max(B * (wl.window + 1), 1), dtype=torch.int32, device="cuda")
+    indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(dw.index, wl.window, table, indptr)
+    out = torch.empty((B, wl.q_heads, wl.head_dim), dtype=TORCH_STORE[out_dtype], device="cuda")
+    swa.swa_decode_store(dw.q, dw.layer, dw.index, wl.window, out, loc, bits_to_device(wl.new_k, wl.new_dtype),
+                         bits_to_device(wl.new_v, wl.new_dtype), sinks=dw.sinks, slot_table=table,
+                         table_indptr=indptr)
+    torch.cuda.synchronize()
+    return out
+
+
 def run_decode(dw: DeviceWorkload, out_dtype="f32", num_splits=None, use_table=True, max_seq=None):
     from sliding_window_attention_swa_amd import swa
     wl = dw.wl

@@ -187,3 +187,20 @@ def test_validate_argument_errors(swa):
     assert val(ws_bytes=need - 4) == E.SWA_E_WORKSPACE
     no_page = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, FAKE, 50, 2, 0)
     assert val(ix=no_page) == E.SWA_E_ARG
+
+
+def test_decode_store_argument_errors(swa):
+    lib, E = swa.lib, swa
+    ly, ix = layer(swa), index(swa)
+
+    def fused(window=128, loc=FAKE, new_dtype=1, q_dtype=1, kn=FAKE, ly=ly):
+        return lib.swa_decode_store(FAKE, q_dtype, 64, ctypes.byref(ly), ctypes.byref(ix), FAKE, FAKE, 1000, window,
+                                    None, 0.088, loc, kn, FAKE, new_dtype, FAKE, 0, None)
+
+    assert fused(loc=None) == E.SWA_E_ARG
+    assert fused(kn=None) == E.SWA_E_ARG
+    assert fused(kn=FAKE + 8) == E.SWA_E_ARG            # misaligned new rows
+    assert fused(new_dtype=0) == E.SWA_E_DTYPE          # f32 new rows: use the two calls
+    assert fused(window=-1) == E.SWA_E_SHAPE            # full layers: split-K, no fused store
+    assert fused(window=300) == E.SWA_E_SHAPE           # beyond the one-split window kernel
+    assert fused(q_dtype=0, ly=layer(swa, dtype=0)) == E.SWA_E_DTYPE

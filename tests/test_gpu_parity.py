@@ -13,7 +13,7 @@ from oracle import swa_oracle as O
 from sliding_window_attention_swa_amd import workloads as WL
 
 from gpu_path import (TOL, DeviceWorkload, bits_to_device, check, device_to_bits, oracle_decode, oracle_extend,
-                      run_decode, run_extend, run_store, say)
+                      run_decode, run_decode_store, run_extend, run_store, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -206,6 +206,31 @@ def test_decode_small(name):
     check(out, ref, TOL[kvd], name)
     out_bf = run_decode(dw, "bf16")
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
+FUSED_CASES = ["bf16_g8", "bf16_g8_nosink", "bf16_g1", "bf16_g2", "bf16_g4", "bf16_g16", "bf16_w0", "bf16_w1",
+               "e4m3_g8", "e4m3_g16_nosink"]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_decode_store_fused(name):
+    """swa_decode_store = swa_kv_store + swa_decode: the same pools and the same
+    output bits as the two calls, and within tolerance of the oracle."""
+    lens, hq, hkv, w, P, qd, kvd, sinks = DECODE_CASES[name]
+    say(f"decode+store fused {name}")
+    wl = WL.decode_workload(name, 100 + len(name), lens, hq, hkv, w, P, qd, kvd, sinks=sinks, with_store=True,
+                            live_margin=5)
+    two = DeviceWorkload(wl)
+    run_store(two)
+    want = run_decode(two, "f32")
+    one = DeviceWorkload(wl)
+    got = run_decode_store(one, "f32")
+    assert np.array_equal(got.cpu().numpy(), want.cpu().numpy())
+    for a, b in ((one.layer.k, two.layer.k), (one.layer.v, two.layer.v)):
+        assert np.array_equal(device_to_bits(a).view(np.uint8), device_to_bits(b).view(np.uint8))
+    check(got, oracle_decode(wl), TOL[kvd], f"fused {name}")
+    fused_bf = run_decode_store(DeviceWorkload(wl), "bf16")
+    assert np.array_equal(device_to_bits(fused_bf), bf16_of(got))
 
 
 FULL_CASES = {
