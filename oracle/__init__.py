@@ -12,6 +12,8 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   window_table        pinned: page-level rebuild (slot = page * P + offset)
   kv_store            pinned: round trip and untouched-row invariants
   validate            pinned: hand-counted violations of a hand-built batch
+  evict               pinned: hand-worked ranges (both modes, interval, protected
+                      prefix), idempotence, and the next window has no tombstone
   attention           pinned: full-causal reduction, plain-softmax reduction,
                       pure-Python brute force, W=0 and identical-key closed
                       forms, GQA expansion, pair-count ratio ~ 2W/T.
@@ -27,6 +29,8 @@ from .swa_oracle import (  # noqa: F401
     attend,
     attention,
     decode,
+    evict,
+    evict_range,
     extend,
     kv_bytes_per_token,
     kv_store,

@@ -282,6 +282,60 @@ def extend(q, q_dtype, qo_indptr, prefix_lens, pool_k, pool_v, pool_dtype, req_t
 
 
 # ---------------------------------------------------------------------------
+# f1 — SWA eviction.  [SWA] 运行时 (free_swa_out_of_window_slots): per request,
+# the SWA KV of positions that left the window is returned to the SWA pool:
+# lower bound the larger of the request's evicted length and its protected
+# (radix-managed) prefix, upper bound pre_len - W (chunk cache) or
+# pre_len - max(W, page) (radix cache), aligned down to a page; in decode the
+# release waits until at least `interval` (128 by default) tokens have left the
+# window.  [SWA] 双池与映射表: free_swa releases only mapping values > 0 and then
+# zeroes them, so a repeated release frees nothing twice.
+# ---------------------------------------------------------------------------
+
+RADIX = 1  # mode: radix cache (upper bound pre_len - max(W, P)); 0 = chunk cache
+
+
+def evict_range(pre_len, evicted, protected, window, page_size, mode, interval):
+    """(lo, hi) of the positions to release for one request; hi <= lo means none."""
+    bound = pre_len - (max(window, page_size) if mode == RADIX else window)
+    hi = (bound // page_size) * page_size if bound > 0 else 0
+    lo = max(evicted, protected)
+    if interval > 0 and hi - evicted < interval:
+        return lo, lo
+    return lo, hi
+
+
+def evict(req_to_token, req_pool_idx, full_to_swa, pre_lens, evicted_lens, window, page_size, mode=0,
+          interval=0, protected_lens=None):
+    """Release the out-of-window SWA slots of every request.
+
+    Returns (mapping, evicted_lens, freed_pages): a new mapping with the released
+    entries set to 0, the advanced evicted lengths (a request with nothing to
+    release keeps its value), and the released SWA pages in request order, then
+    position order.  A page is reported at the first released position of the
+    range and at every released position that starts a page (slot // page)."""
+    r2t = np.asarray(req_to_token)
+    m = np.array(full_to_swa, dtype=np.int64, copy=True)
+    ev = np.array(evicted_lens, dtype=np.int64, copy=True)
+    pages = []
+    for b in range(len(pre_lens)):
+        prot = 0 if protected_lens is None else int(protected_lens[b])
+        lo, hi = evict_range(int(pre_lens[b]), int(ev[b]), prot, window, page_size, mode, interval)
+        if hi <= lo:
+            continue
+        row = int(req_pool_idx[b])
+        for j in range(lo, hi):
+            full = int(r2t[row, j])
+            slot = int(m[full])
+            if slot > 0:
+                if j == lo or j % page_size == 0:
+                    pages.append(slot // page_size)
+                m[full] = 0
+        ev[b] = hi
+    return m, ev, np.asarray(pages, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
 # Index-data contracts, counted rather than raised.  [SWA] 双池与映射表 and
 # 运行时: a live window never holds a tombstone (eviction frees only positions
 # that left the window) and the mapping ends in the -1 sentinel that a -1 loc

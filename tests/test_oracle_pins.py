@@ -570,3 +570,67 @@ def test_validate_clean_workload_counts_nothing():
     assert c["positions"] == sum(min(n, wl.window + 1) for n in wl.seq_lens)
     assert c["store_locs"] == loc.size
     assert sum(v for k, v in c.items() if k not in ("positions", "store_locs")) == 0
+
+
+# ---------------------------------------------------------------------------
+# evict: hand-worked ranges and a hand-built release, then properties that
+# tie it to the attention path ([SWA] 运行时, 双池与映射表)
+# ---------------------------------------------------------------------------
+
+def test_evict_range_hand_worked():
+    # chunk cache: pre_len - W, aligned down to the page
+    assert O.evict_range(1000, 0, 0, 128, 16, 0, 0) == (0, 864)
+    # radix cache: pre_len - max(W, P)
+    assert O.evict_range(1000, 0, 0, 128, 64, O.RADIX, 0) == (0, 832)
+    assert O.evict_range(1000, 0, 0, 16, 64, O.RADIX, 0) == (0, 896)     # max(16, 64) = 64
+    # protected prefix raises the lower bound; evicted length too
+    assert O.evict_range(1000, 100, 300, 128, 16, 0, 0) == (300, 864)
+    # nothing left of the window yet
+    assert O.evict_range(100, 0, 0, 128, 16, 0, 0)[1] == 0
+    # decode interval: wait until 128 tokens have left the window
+    assert O.evict_range(1000, 800, 0, 128, 16, 0, 128) == (800, 800)     # 864 - 800 = 64 < 128
+    assert O.evict_range(1056, 800, 0, 128, 16, 0, 128) == (800, 928)    # 928 - 800 = 128
+
+
+def test_evict_hand_built():
+    # page 4, window 4; one request (row 1) of 20 positions on full pages 3,1,4,2,5
+    # mapped to SWA pages 7,2,9,4,6 (in-page offsets kept); pre_len 19 -> bound 15 -> 12
+    P = 4
+    full_pages, swa_pages = [3, 1, 4, 2, 5], [7, 2, 9, 4, 6]
+    r2t = np.zeros((2, 20), dtype=np.int32)
+    mapping = np.zeros(6 * P + P + 1, dtype=np.int64)
+    mapping[-1] = -1
+    for j in range(20):
+        f = full_pages[j // P] * P + j % P
+        r2t[1, j] = f
+        mapping[f] = swa_pages[j // P] * P + j % P
+    m, ev, pages = O.evict(r2t, [1], mapping, [19], [0], 4, P)
+    assert pages.tolist() == [7, 2, 9]
+    assert ev.tolist() == [12]
+    released = set(r2t[1, :12].tolist())
+    for f in range(mapping.size):
+        assert m[f] == (0 if f in released else mapping[f])
+    # a second release frees nothing and changes nothing
+    m2, ev2, pages2 = O.evict(r2t, [1], m, [19], ev, 4, P)
+    assert pages2.size == 0 and np.array_equal(m2, m) and ev2.tolist() == [12]
+
+
+def test_evict_keeps_the_next_window_and_its_attention():
+    """After releasing everything left of the current token's window, that
+    window has no tombstone and decode gives the very same output."""
+    wl = WL.decode_workload("evict", 9, [1, 40, 300, 1000, 129], 8, 2, 128, 16, "bf16", "bf16", sinks=True,
+                            live_margin=200)
+    before = O.decode(wl.q, "bf16", wl.pool_k, wl.pool_v, "bf16", wl.req_to_token, wl.req_pool_idx, wl.seq_lens,
+                      wl.full_to_swa, wl.window, wl.sinks)
+    pre = wl.seq_lens.astype(np.int64) - 1
+    m, ev, pages = O.evict(wl.req_to_token, wl.req_pool_idx, wl.full_to_swa, pre, np.zeros(5, np.int64), 128, 16)
+    assert pages.size > 0 and np.all(pages > 0)
+    assert np.unique(pages).size == pages.size                     # each page released once
+    after = O.decode(wl.q, "bf16", wl.pool_k, wl.pool_v, "bf16", wl.req_to_token, wl.req_pool_idx, wl.seq_lens,
+                     m, wl.window, wl.sinks)                      # raises on an in-window tombstone
+    assert np.array_equal(before, after)
+    # every released page was mapped before and is mapped nowhere now
+    swa_pages_before = set((wl.full_to_swa[wl.full_to_swa > 0] // 16).tolist())
+    swa_pages_after = set((m[m > 0] // 16).tolist())
+    assert set(pages.tolist()) <= swa_pages_before
+    assert not set(pages.tolist()) & swa_pages_after
