@@ -1,10 +1,11 @@
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|evict]
 
 Other workloads (one JSON line each, same fields): c1 single f32 decode; c3
 chunked-prefill extend (store + extend over 4 layers); c4 the 48-layer mixed
-decode step (39 SWA + 9 full layers); c5 fp8-KV decode with store.
+decode step (39 SWA + 9 full layers); c5 fp8-KV decode with store; evict the
+SWA eviction of the c5 batch right after its prefill.
 
 Default workload (c2): batched SWA decode, B = 64 requests with context lengths
 uniform in [1K, 8K], W = 128, 64 q / 8 kv heads, head_dim 128, bf16, page 16,
@@ -524,6 +525,127 @@ def run_mixed_workload(args, torch, swa, W):
     return res
 
 
+# ---------------------------------------------------------------------------
+# evict: SWA eviction of a batch right after its prefill
+# ---------------------------------------------------------------------------
+
+
+class EvictBench:
+    """The after-prefill eviction batch on `copies` distinct copies of its index
+    tables (req_to_token, mapping, evicted lengths), so that back-to-back calls
+    are not served from the 256 MB Infinity Cache.  A call consumes its copy's
+    mapping; restore() puts the pristine mapping back (outside the timed
+    events)."""
+
+    def __init__(self, torch, swa, eb, copies=16):
+        self.torch, self.swa, self.eb, self.copies = torch, swa, eb, copies
+        B, P = eb.batch, eb.page_size
+        rows = torch.from_numpy(eb.req_pool_idx).cuda()
+        lens = torch.from_numpy(eb.seq_lens).cuda()
+        self.pre = torch.from_numpy(eb.pre_lens).cuda()
+        self.map0 = torch.from_numpy(eb.full_to_swa).cuda()
+        self.ev0 = torch.from_numpy(eb.evicted_lens).cuda()
+        self.index = [swa.IndexTables(torch.from_numpy(eb.req_to_token).cuda(), rows, lens, None, P)
+                      for _ in range(copies)]
+        self.maps = [torch.empty_like(self.map0) for _ in range(copies)]
+        self.evs = [torch.empty_like(self.ev0) for _ in range(copies)]
+        cap = B * (eb.req_to_token.shape[1] // P + 2)  # at most one report per page plus the first
+        self.pages = [torch.empty(cap, dtype=torch.int64, device="cuda") for _ in range(copies)]
+        self.count = [torch.zeros(1, dtype=torch.int64, device="cuda") for _ in range(copies)]
+        need = swa.lib.swa_evict_workspace_bytes(B, eb.req_to_token.shape[1], P)
+        self.ws = torch.empty(need // 4, dtype=torch.int32, device="cuda")
+        self.restore()
+
+    def released(self):
+        """Positions and pages the last call on copy 0 released (from its
+        advanced evicted lengths and its page count)."""
+        moved = (self.evs[0].long() - self.ev0.long()).clamp_min(0)
+        return int(moved.sum().item()), int(self.count[0].item())
+
+    def restore(self):
+        for m, e in zip(self.maps, self.evs):
+            m.copy_(self.map0)
+            e.copy_(self.ev0)
+
+    def calls(self):
+        for i in range(self.copies):
+            self.swa.swa_evict(self.index[i], self.maps[i], self.pre, self.evs[i], self.eb.window, self.pages[i],
+                               self.count[i], interval=128, workspace=self.ws)
+
+
+def cpu_baseline_evict(eb, budget_s=12.0):
+    from oracle import swa_oracle as O
+    reps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        O.evict(eb.req_to_token, eb.req_pool_idx, eb.full_to_swa, eb.pre_lens, eb.evicted_lens, eb.window,
+                eb.page_size, interval=128)
+        reps += 1
+    return time.perf_counter() - t0, reps
+
+
+def run_evict_workload(args, torch, swa, W):
+    eb = W.evict_after_prefill()
+    log("[bench] evict: building 16 copies of the index tables")
+    bench = EvictBench(torch, swa, eb)
+    g = graph_of(torch, bench.calls)
+    for _ in range(max(1, args.warmup // bench.copies)):
+        bench.restore()
+        g.replay()
+    n_rep = max(1, -(-args.steps // bench.copies))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep)]
+    torch.cuda.synchronize()
+    for r in range(n_rep):
+        bench.restore()  # untimed: the calls consume their copies' mappings
+        starts[r].record()
+        g.replay()
+        ends[r].record()
+    torch.cuda.synchronize()
+    per_call = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) / bench.copies  # ms
+    ms = float(per_call.mean())
+    positions, pages = bench.released()
+    # a further replay finds every request's interval gate shut: the per-step cost
+    # of calling the eviction when nothing is due (skipped in profiling runs, whose
+    # per-kernel averages should cover the releasing calls only)
+    noop = None if args.skip_noop else time_replays(torch, g, 20) / bench.copies
+    # algorithmic bytes of one call: per released position its req_to_token
+    # entry (4 B) and its mapping entry read and cleared (8 + 8 B); per released
+    # page one int64 report; per request req_pool_idx, pre_lens and evicted_lens
+    # read (12 B) and evicted_lens written (4 B); the count (8 B).
+    nbytes = positions * 20 + pages * 8 + eb.batch * 16 + 8
+    value = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] evict {ms * 1e3:.2f} us per call, {positions} positions, {pages} pages; "
+        f"no-op call {'-' if noop is None else f'{noop * 1e3:.2f}'} us")
+    traffic = traffic_from_profile("swa_evict_after_prefill", ["evict_kernels.hip", "common.hpp", "api.cpp"], 1)
+    res = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=n_rep * bench.copies,
+        warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="int64", data="synthetic",
+        config={"workload": "SWA eviction right after prefill: B=256, lognormal lengths (median 16K, clipped to "
+                            "[512, 64K]), W=128, page 64, decode interval 128, every position mapped",
+                "global_batch": int(eb.batch), "window": eb.window, "page_size": eb.page_size,
+                "released_positions": int(positions), "released_pages": pages,
+                "parallelism": "none (1 GPU)"},
+        timed="back-to-back calls on 16 distinct copies of the index tables, replayed as one graph; the "
+              "mappings are restored between replays, outside the timed events",
+        positions_per_s=round(positions / (ms * 1e-3), 1),
+        noop_call_us=None if noop is None else round(noop * 1e3, 3),
+        roofline=dict(kernel="swa_evict (scan + apply)", bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS,
+                      unit="GB/s", frac=round(value / HBM_PEAK_GBS, 4), traffic=traffic, bytes_per_launch=nbytes,
+                      us_per_launch=round(ms * 1e3, 3),
+                      p10_us=round(float(np.percentile(per_call, 10)) * 1e3, 3),
+                      p50_us=round(float(np.percentile(per_call, 50)) * 1e3, 3),
+                      p90_us=round(float(np.percentile(per_call, 90)) * 1e3, 3)),
+    )
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        secs, reps = cpu_baseline_evict(eb)
+        res["cpu_baseline"] = dict(value=round(reps * nbytes / secs / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
+                                   sample=f"the whole batch, {reps} times ({secs:.1f} s)")
+    return res
+
+
 def copy_probe(torch, reps=5):
     """A plain elementwise kernel of known traffic (1 GiB read + 1 GiB written
     per launch), run so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can
@@ -543,8 +665,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "evict"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-noop", action="store_true",
+                    help="evict: skip timing the calls that release nothing (for profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a copy kernel of known size (counter calibration)")
     args = ap.parse_args()
@@ -566,6 +690,8 @@ def main():
         res = run_extend_workload(args, torch, swa, W)
     elif args.workload == "c4":
         res = run_mixed_workload(args, torch, swa, W)
+    elif args.workload == "evict":
+        res = run_evict_workload(args, torch, swa, W)
     else:
         res = run_decode_workload(args, torch, swa, W)
     print(json.dumps(res), flush=True)

@@ -224,6 +224,45 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
                         void *out, int32_t out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * SWA eviction — release the SWA KV of positions that left each request's
+ * window ([SWA] 运行时: free_swa_out_of_window_slots; 双池与映射表: free_swa).
+ * For request b (row req_pool_idx[b] of req_to_token) the released positions
+ * are [lo, hi) with
+ *   lo = max(evicted_lens[b], protected_lens[b])        (protected_lens NULL: 0)
+ *   hi = floor_page(pre_lens[b] - W)            mode 0, chunk cache
+ *   hi = floor_page(pre_lens[b] - max(W, P))    mode 1, radix cache
+ * (floor_page rounds down to a multiple of idx->page_size; a negative bound is
+ * 0), and nothing when interval > 0 and hi - evicted_lens[b] < interval (the
+ * decode eviction interval, 128 on the page).  For each released position whose
+ * full slot f has full_to_swa[f] > 0, that SWA slot is released and
+ * full_to_swa[f] is set to 0; entries that are already 0 release nothing, so a
+ * repeated call frees nothing twice.  A request that releases a range gets
+ * evicted_lens[b] = hi.
+ *   full_to_swa  the mapping (map_len = idx->map_len entries), modified in
+ *                place; idx->full_to_swa is not used.
+ *   freed_pages  int64 (freed_capacity): the released SWA pages (slot / P), in
+ *                request order, then position order; a page is reported at the
+ *                first released position of a range and at every released
+ *                position that starts a page.  Entries past the capacity are
+ *                not written; *freed_count (device int64) receives the full
+ *                number, so the caller can detect a short buffer.
+ *   pre_lens, evicted_lens, protected_lens  device int32 [batch]
+ *                (evicted_lens read and updated in place).
+ *   workspace    device, swa_evict_workspace_bytes(batch, r2t_stride, page)
+ *                bytes, 4-aligned; overwritten.
+ * Ranges of different requests must not share full slots (a shared prefix is
+ * protected).  Positions or slots outside their tables release nothing.
+ * Errors: SWA_E_ARG (null or inconsistent arguments, window < 0, mode not 0/1,
+ * interval < 0), SWA_E_WORKSPACE (workspace missing, short or misaligned),
+ * SWA_E_SHAPE (req_to_token rows longer than 65,535 x 1,024 positions). */
+size_t swa_evict_workspace_bytes(int32_t batch, int64_t r2t_stride, int32_t page_size);
+
+swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32_t *pre_lens,
+                       const int32_t *protected_lens, int32_t *evicted_lens, int32_t window, int32_t mode,
+                       int32_t interval, int64_t *freed_pages, int64_t freed_capacity, int64_t *freed_count,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Validation (debugging aid; SYNCHRONOUS: waits for `stream`).  Counts the
  * index data that the kernels above silently absorb, per the contracts of
  * [SWA] 双池与映射表 and 运行时 (a live window never holds a tombstone: eviction

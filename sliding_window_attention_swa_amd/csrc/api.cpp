@@ -254,6 +254,34 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
   return from_hip(swa::launch_extend(a, stream));
 }
 
+size_t swa_evict_workspace_bytes(int32_t batch, int64_t r2t_stride, int32_t page_size) {
+  if (batch <= 0 || r2t_stride < 1 || page_size < 1) return 0;
+  return static_cast<size_t>(batch) * static_cast<size_t>(3 + swa::evict_chunks(r2t_stride, page_size)) *
+         sizeof(int32_t);
+}
+
+swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32_t *pre_lens,
+                       const int32_t *protected_lens, int32_t *evicted_lens, int32_t window, int32_t mode,
+                       int32_t interval, int64_t *freed_pages, int64_t freed_capacity, int64_t *freed_count,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!idx || idx->batch < 0 || !full_to_swa || !freed_count) return SWA_E_ARG;
+  swa_status_t st = check_index(idx, true);
+  if (st != SWA_OK) return st;
+  if (idx->map_len < 2 || idx->page_size < 1 || window < 0 || (mode != 0 && mode != 1) || interval < 0 ||
+      freed_capacity < 0)
+    return SWA_E_ARG;
+  if (idx->batch > 0 && (!pre_lens || !evicted_lens)) return SWA_E_ARG;
+  if (freed_capacity > 0 && !freed_pages) return SWA_E_ARG;
+  if (idx->batch > 0 && swa::evict_chunks(idx->r2t_stride, idx->page_size) > 65535) return SWA_E_SHAPE;
+  if (idx->batch > 0 &&
+      (!workspace || workspace_bytes < swa_evict_workspace_bytes(idx->batch, idx->r2t_stride, idx->page_size) ||
+       (reinterpret_cast<uintptr_t>(workspace) & 3u)))
+    return SWA_E_WORKSPACE;
+  return from_hip(swa::launch_evict(*idx, full_to_swa, pre_lens, protected_lens, evicted_lens, window, mode,
+                                    interval, freed_pages, freed_capacity, freed_count,
+                                    static_cast<int32_t *>(workspace), stream));
+}
+
 // Workspace of swa_validate: 16 int64 counters, then one bit per pool row.
 constexpr int64_t kValidateCounterBytes = 16 * sizeof(int64_t);
 

@@ -121,6 +121,22 @@ hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t
                            const int64_t *store_loc, int64_t n_store, void *workspace, int64_t counters_bytes,
                            hipStream_t stream);
 
+// Eviction works on chunks of positions that start at page boundaries: the
+// smallest multiple of the page size that is at least 1024 positions.
+__host__ __device__ inline int64_t evict_chunk(int32_t page) {
+  return (1024 + static_cast<int64_t>(page) - 1) / page * page;
+}
+__host__ __device__ inline int64_t evict_chunks(int64_t r2t_stride, int32_t page) {
+  const int64_t c = evict_chunk(page);
+  return (r2t_stride + c - 1) / c;
+}
+
+// workspace: int32 [batch] counts, [batch][2] ranges, [batch][evict_chunks] bases
+hipError_t launch_evict(const swa_index_t &idx, int64_t *full_to_swa, const int32_t *pre_lens,
+                        const int32_t *protected_lens, int32_t *evicted_lens, int32_t window, int32_t radix,
+                        int32_t interval, int64_t *freed_pages, int64_t capacity, int64_t *freed_count,
+                        int32_t *workspace, hipStream_t stream);
+
 struct ExtendArgs {
   const void *q;
   int32_t q_heads;

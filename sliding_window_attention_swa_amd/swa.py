@@ -26,6 +26,7 @@ SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 # every symbol include/swa.h declares
 EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
            "swa_decode", "swa_decode_store", "swa_extend", "swa_validate_workspace_bytes", "swa_validate",
+           "swa_evict_workspace_bytes", "swa_evict",
            "swa_status_string")
 
 
@@ -82,6 +83,8 @@ _sig = {
     "swa_validate_workspace_bytes": (_sz, [_i64]),
     "swa_validate": (_i32, [ctypes.POINTER(IndexStruct), _i32, _p, _i64, _p, _i64, _p, _sz,
                             ctypes.POINTER(ValidateReportStruct), _p]),
+    "swa_evict_workspace_bytes": (_sz, [_i32, _i64, _i32]),
+    "swa_evict": (_i32, [ctypes.POINTER(IndexStruct), _p, _p, _p, _p, _i32, _i32, _i32, _p, _i64, _p, _p, _sz, _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -287,3 +290,22 @@ def swa_validate(index: IndexTables, window: int, pool_rows: int, prefix_lens: O
                             _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
                             ctypes.byref(rep), _stream(stream)), "swa_validate")
     return {f: getattr(rep, f) for f in VALIDATE_FIELDS}
+
+
+def swa_evict(index: IndexTables, full_to_swa: torch.Tensor, pre_lens: torch.Tensor, evicted_lens: torch.Tensor,
+              window: int, freed_pages: torch.Tensor, freed_count: torch.Tensor, mode: int = 0, interval: int = 0,
+              protected_lens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Release out-of-window SWA slots (mapping and evicted_lens updated in
+    place; released pages into freed_pages, their number into freed_count)."""
+    B = index.seq_lens.numel()
+    if workspace is None:
+        need = lib.swa_evict_workspace_bytes(B, index.req_to_token.shape[1], index.page_size)
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.int32, device=full_to_swa.device)
+    ix = index.struct(with_map=False)
+    ix.map_len = full_to_swa.numel()
+    _check(lib.swa_evict(ctypes.byref(ix), _ptr(full_to_swa, torch.int64, "full_to_swa"),
+                         _ptr(pre_lens, torch.int32, "pre_lens"), _ptr(protected_lens, torch.int32, "protected_lens"),
+                         _ptr(evicted_lens, torch.int32, "evicted_lens"), window, mode, interval,
+                         _ptr(freed_pages, torch.int64, "freed_pages"), freed_pages.numel(),
+                         _ptr(freed_count, torch.int64, "freed_count"), _ptr(workspace, torch.int32, "workspace"),
+                         workspace.numel() * 4, _stream(stream)), "swa_evict")

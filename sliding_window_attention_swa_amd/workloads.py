@@ -384,3 +384,48 @@ def c4_layer_tensors(step: MixedStep, layer: dict, device="cuda"):
     k[idx] = torch.randn((idx.numel(), H, D), generator=g, device=device).to(torch.bfloat16)
     v[idx] = torch.randn((idx.numel(), H, D), generator=g, device=device).to(torch.bfloat16)
     return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# SWA eviction: index structures only (eviction touches no K/V)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class EvictBatch:
+    name: str
+    batch: int
+    page_size: int
+    window: int
+    seq_lens: np.ndarray          # int32 (B,)
+    pre_lens: np.ndarray          # int32 (B,): seq_len - 1, the decode position
+    evicted_lens: np.ndarray      # int32 (B,)
+    req_to_token: np.ndarray      # int32 (B + 1, stride), row 0 padding
+    req_pool_idx: np.ndarray      # int32 (B,)
+    full_to_swa: np.ndarray       # int64 (n_full + P + 1,), trailing -1 sentinel
+    n_full: int
+    n_swa: int
+
+
+def evict_batch(name, seed, seq_lens, page_size, window, live_from=None, evicted_lens=None) -> EvictBatch:
+    """A batch whose positions >= live_from (rounded down to a page; default 0,
+    i.e. every position) still hold SWA slots, laid out by the same recipe as
+    the decode workloads."""
+    _, r_full, r_swa, *_ = _streams(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    B, P = len(seq_lens), page_size
+    live_from = np.zeros(B, np.int64) if live_from is None else np.asarray(live_from, np.int64)
+    n_full = round_up(int(sum(round_up(int(t), P) for t in seq_lens)) + 2 * P, P)
+    need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(seq_lens, live_from)))
+    n_swa = round_up(need + 2 * P, P)
+    r2t, mapping, _ = _layout(seq_lens, P, n_full, n_swa, live_from, r_full, r_swa)
+    ev = np.zeros(B, np.int32) if evicted_lens is None else np.asarray(evicted_lens, np.int32)
+    return EvictBatch(name, B, P, window, seq_lens.astype(np.int32), (seq_lens - 1).astype(np.int32), ev, r2t,
+                      np.arange(1, B + 1, dtype=np.int32), mapping, n_full, n_swa)
+
+
+def evict_after_prefill(seed=SEED_BASE + 5, batch=256) -> EvictBatch:
+    """The fp8 decode batch (B = 256, lognormal lengths, median 16K, clipped to
+    [512, 64K], W = 128, P = 64) right after its prefill: every position still
+    holds an SWA slot and nothing has been evicted, so the first decode step's
+    eviction releases every page before the window."""
+    return evict_batch("evict_after_prefill_B256", seed, c5_lengths(seed, batch), 64, 128)

@@ -204,3 +204,36 @@ def test_decode_store_argument_errors(swa):
     assert fused(window=-1) == E.SWA_E_SHAPE            # full layers: split-K, no fused store
     assert fused(window=300) == E.SWA_E_SHAPE           # beyond the one-split window kernel
     assert fused(q_dtype=0, ly=layer(swa, dtype=0)) == E.SWA_E_DTYPE
+
+
+def test_evict_argument_errors(swa):
+    lib, E = swa.lib, swa
+    ix = index(swa)
+    # int32 counts, ranges (2) and one base per chunk of >= 1024 positions starting at page boundaries
+    assert lib.swa_evict_workspace_bytes(5, 4096, 16) == 5 * (3 + 4) * 4
+    assert lib.swa_evict_workspace_bytes(2, 100, 3) == 2 * (3 + 1) * 4      # chunk 1026
+    assert lib.swa_evict_workspace_bytes(1, 2049, 2048) == 1 * (3 + 2) * 4  # chunk 2048
+    assert lib.swa_evict_workspace_bytes(0, 4096, 16) == 0
+    need = lib.swa_evict_workspace_bytes(2, 100, 16)
+
+    def ev(ix=ix, mp=FAKE, pre=FAKE, evd=FAKE, window=128, mode=0, interval=0, pages=FAKE, cap=10, count=FAKE,
+           ws=FAKE, ws_bytes=need):
+        return lib.swa_evict(ctypes.byref(ix), mp, pre, None, evd, window, mode, interval, pages, cap, count, ws,
+                             ws_bytes, None)
+
+    assert ev(mp=None) == E.SWA_E_ARG
+    assert ev(count=None) == E.SWA_E_ARG
+    assert ev(pre=None) == E.SWA_E_ARG
+    assert ev(evd=None) == E.SWA_E_ARG
+    assert ev(window=-1) == E.SWA_E_ARG                 # full layers release nothing
+    assert ev(mode=2) == E.SWA_E_ARG
+    assert ev(interval=-1) == E.SWA_E_ARG
+    assert ev(cap=-1) == E.SWA_E_ARG
+    assert ev(pages=None) == E.SWA_E_ARG                # a capacity with no buffer
+    assert ev(ws=None) == E.SWA_E_WORKSPACE
+    assert ev(ws_bytes=need - 4) == E.SWA_E_WORKSPACE
+    assert ev(ws=FAKE + 2) == E.SWA_E_WORKSPACE         # misaligned
+    short_map = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, None, 1, 2, 16)
+    assert ev(ix=short_map) == E.SWA_E_ARG              # a mapping needs its sentinel entry
+    long_rows = swa.IndexStruct(FAKE, 3, 65536 * 1024 + 1, FAKE, FAKE, None, 50, 2, 16)
+    assert ev(ix=long_rows, ws_bytes=1 << 40) == E.SWA_E_SHAPE

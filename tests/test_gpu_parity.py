@@ -498,3 +498,107 @@ def test_extend_c3_full_size_sampled():
     only = [(int(r), h) for r in rows for h in range(wl.q_heads)]
     ref = oracle_extend(wl, only=only)
     check(out, ref, TOL["bf16"], "c3 sampled")
+
+
+# ---------------------------------------------------------------------------
+# SWA eviction (mapping maintenance): bit-exact against the oracle
+# ---------------------------------------------------------------------------
+
+EVICT_CASES = {
+    # name: (lens, page, mode, interval, evicted, protected, live_from)
+    "chunk": ([1, 40, 300, 1000, 2049, 129], 16, 0, 0, None, None, None),
+    "radix_p64": ([1, 40, 300, 1000, 2049, 129], 64, 1, 0, None, None, None),
+    "interval": ([1, 40, 300, 1000, 2049, 129], 16, 0, 128, [0, 0, 96, 800, 1760, 0], None, None),
+    "protected": ([1, 40, 300, 1000, 2049, 129], 16, 0, 0, [0, 0, 16, 0, 512, 0], [0, 30, 100, 900, 0, 0], None),
+    # stale evicted lengths over spans already tombstoned: only mapped slots are released
+    "tombstoned": ([3000, 5000, 700, 4097], 16, 0, 0, None, None, [1000, 4500, 0, 2050]),
+    "page1": ([513, 2, 1500], 1, 0, 128, [0, 0, 1000], None, [100, 0, 0]),
+    "page3_radix": ([1000, 3001], 3, 1, 0, [7, 0], [0, 10], None),
+}
+
+
+def _evict_gpu(eb, mapping, ev, prot, mode, interval, cap):
+    """One swa_evict call on device copies of the batch; returns host copies of
+    (mapping, evicted_lens, freed_pages, freed_count)."""
+    from sliding_window_attention_swa_amd import swa
+    ix = swa.IndexTables(torch.from_numpy(eb.req_to_token).cuda(), torch.from_numpy(eb.req_pool_idx).cuda(),
+                         torch.from_numpy(eb.seq_lens).cuda(), None, eb.page_size)
+    m = torch.from_numpy(np.array(mapping, dtype=np.int64)).cuda()
+    evd = torch.from_numpy(np.asarray(ev, dtype=np.int32)).cuda()
+    pages = torch.full((max(cap, 1),), -9, dtype=torch.int64, device="cuda")
+    count = torch.full((1,), -9, dtype=torch.int64, device="cuda")
+    prot_d = None if prot is None else torch.from_numpy(np.asarray(prot, np.int32)).cuda()
+    swa.swa_evict(ix, m, torch.from_numpy(eb.pre_lens).cuda(), evd, eb.window, pages[:cap] if cap else pages[:0],
+                  count, mode=mode, interval=interval, protected_lens=prot_d)
+    torch.cuda.synchronize()
+    return m.cpu().numpy(), evd.cpu().numpy(), pages.cpu().numpy()[:cap], int(count.item())
+
+
+def _check_evict(eb, ev, prot, mode, interval):
+    want_m, want_ev, want_pages = O.evict(eb.req_to_token, eb.req_pool_idx, eb.full_to_swa, eb.pre_lens, ev,
+                                          eb.window, eb.page_size, mode=mode, interval=interval,
+                                          protected_lens=prot)
+    assert want_pages.size > 0
+    m, evd, pages, count = _evict_gpu(eb, eb.full_to_swa, ev, prot, mode, interval, want_pages.size + 5)
+    assert np.array_equal(m, want_m)
+    assert np.array_equal(evd, want_ev)
+    assert count == want_pages.size
+    assert np.array_equal(pages[:count], want_pages) and np.all(pages[count:] == -9)
+    return m, evd, want_m, want_pages
+
+
+@pytest.mark.parametrize("name", list(EVICT_CASES))
+def test_evict_bit_exact(name):
+    lens, P, mode, interval, ev, prot, live = EVICT_CASES[name]
+    say(f"evict {name}")
+    eb = WL.evict_batch("ev" + name, 41, lens, P, 128, live_from=live)
+    ev = np.zeros(len(lens), np.int32) if ev is None else np.asarray(ev, np.int32)
+    m, evd, want_m, want_pages = _check_evict(eb, ev, prot, mode, interval)
+    # releasing again frees nothing and changes nothing
+    m2, evd2, pages2, count2 = _evict_gpu(eb, m, evd, prot, mode, interval, 4)
+    assert count2 == 0 and np.array_equal(m2, m) and np.array_equal(evd2, evd) and np.all(pages2 == -9)
+    # a short page buffer: its prefix is written, the count is the full number
+    m3, _, pages3, count3 = _evict_gpu(eb, eb.full_to_swa, ev, prot, mode, interval, 3)
+    assert count3 == want_pages.size and np.array_equal(pages3, want_pages[:3]) and np.array_equal(m3, want_m)
+    # no page buffer at all
+    _, _, _, count4 = _evict_gpu(eb, eb.full_to_swa, ev, prot, mode, interval, 0)
+    assert count4 == want_pages.size
+
+
+def test_evict_empty_batch():
+    from sliding_window_attention_swa_amd import swa
+    say("evict empty batch")
+    r2t = torch.zeros((1, 16), dtype=torch.int32, device="cuda")
+    e = torch.zeros(0, dtype=torch.int32, device="cuda")
+    ix = swa.IndexTables(r2t, e, e, None, 16)
+    m = torch.tensor([0, 5, -1], dtype=torch.int64, device="cuda")
+    count = torch.full((1,), -9, dtype=torch.int64, device="cuda")
+    swa.swa_evict(ix, m, e, e, 128, torch.empty(0, dtype=torch.int64, device="cuda"), count)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 0 and m.tolist() == [0, 5, -1]
+
+
+def test_evict_after_prefill_full_size():
+    """The benchmark's eviction batch at its full size (B = 256, lognormal
+    lengths up to 64K, P = 64, decode interval 128), compared in full."""
+    say("evict after prefill, full size")
+    eb = WL.evict_after_prefill()
+    _check_evict(eb, eb.evicted_lens, None, 0, 128)
+
+
+def test_evict_then_decode_unchanged():
+    """Releasing everything left of the current token's window changes neither
+    the window tables nor the decode output, bit for bit."""
+    wl = WL.decode_workload("evdec", 43, [1, 40, 300, 1000, 129, 4000], 16, 2, 128, 16, "bf16", "bf16",
+                            sinks=True, live_margin=100000)
+    dw = DeviceWorkload(wl)
+    say("evict then decode")
+    before = run_decode(dw, "f32").cpu().numpy()
+    eb = WL.EvictBatch("evdec", wl.batch, 16, 128, wl.seq_lens, (wl.seq_lens - 1).astype(np.int32),
+                       np.zeros(wl.batch, np.int32), wl.req_to_token, wl.req_pool_idx, wl.full_to_swa, wl.n_full,
+                       wl.n_swa)
+    m, _, _, count = _evict_gpu(eb, wl.full_to_swa, eb.evicted_lens, None, 0, 0, 4096)
+    assert count > 0 and np.count_nonzero(m == 0) > np.count_nonzero(wl.full_to_swa == 0)
+    dw.map.copy_(torch.from_numpy(m).cuda())
+    after = run_decode(dw, "f32").cpu().numpy()
+    assert np.array_equal(before, after)
