@@ -254,7 +254,7 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
  * protected).  Positions or slots outside their tables release nothing.
  * Errors: SWA_E_ARG (null or inconsistent arguments, window < 0, mode not 0/1,
  * interval < 0), SWA_E_WORKSPACE (workspace missing, short or misaligned),
- * SWA_E_SHAPE (req_to_token rows longer than 65,535 x 1,024 positions). */
+ * SWA_E_SHAPE (req_to_token rows longer than 65,535 x 2,048 positions). */
 size_t swa_evict_workspace_bytes(int32_t batch, int64_t r2t_stride, int32_t page_size);
 
 swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32_t *pre_lens,

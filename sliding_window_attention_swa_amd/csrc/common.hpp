@@ -122,9 +122,15 @@ hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t
                            hipStream_t stream);
 
 // Eviction works on chunks of positions that start at page boundaries: the
-// smallest multiple of the page size that is at least 1024 positions.
+// smallest multiple of the page size that is at least one apply pass (256
+// threads x kEvictApplyPerThread positions).
+#ifndef SWA_EVICT_APPLY_PER_THREAD
+#define SWA_EVICT_APPLY_PER_THREAD 8
+#endif
+constexpr int kEvictApplyPerThread = SWA_EVICT_APPLY_PER_THREAD;
 __host__ __device__ inline int64_t evict_chunk(int32_t page) {
-  return (1024 + static_cast<int64_t>(page) - 1) / page * page;
+  const int64_t pass = 256 * kEvictApplyPerThread;
+  return (pass + static_cast<int64_t>(page) - 1) / page * page;
 }
 __host__ __device__ inline int64_t evict_chunks(int64_t r2t_stride, int32_t page) {
   const int64_t c = evict_chunk(page);

@@ -16,7 +16,7 @@
 //          range), counts the reports, records for every chunk of the range the
 //          number of reports before it, stores the range and advances the
 //          evicted length;
-//   apply: one workgroup per (request, chunk of about 1024 positions) clears
+//   apply: one workgroup per (request, chunk of about 2048 positions) clears
 //          the chunk's mapping entries and writes its reports at
 //          (reports of earlier requests) + (reports of earlier chunks) + rank.
 // The report order (request, then position) is therefore deterministic, and
@@ -27,8 +27,9 @@ namespace swa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = 4;
-constexpr int kBatch = kThreads * kPerThread;  // positions (or candidates) per pass
+constexpr int kPerThread = 4;                  // scan: candidates per thread and pass
+constexpr int kBatch = kThreads * kPerThread;
+constexpr int kApplyPerThread = kEvictApplyPerThread;  // apply: positions per thread and pass
 
 struct EvictParams {
   const int32_t *r2t;
@@ -156,63 +157,92 @@ __global__ void __launch_bounds__(kThreads) evict_scan_kernel(EvictParams p) {
   }
 }
 
-// Sum of one value per thread over the workgroup.
-__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t *red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
-}
-
-// Reports of requests [0, b), and (block (0, 0) only) the total.
-__device__ int64_t reports_before(const EvictParams &p, int32_t b, int64_t *red) {
-  int64_t before = 0;
-  for (int32_t i = threadIdx.x; i < b; i += kThreads) before += p.counts[i];
-  return block_sum(before, red);
-}
-
+// Apply: one workgroup per (request, chunk).  Three memory phases: the
+// independent per-block values (range, chunk base, request row, the earlier
+// requests' counts), then the chunk's req_to_token entries, then their mapping
+// entries; one barrier ranks the reports and sums the counts together.
 __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
-  __shared__ int32_t cnt[kPerThread * 4];
+  __shared__ int32_t cnt[kApplyPerThread * 4];
   __shared__ int64_t red[4];
   const int32_t b = blockIdx.x;
   const int32_t k = blockIdx.y;
-  if (b == 0 && k == 0) {
-    const int64_t total = reports_before(p, p.batch, red);
-    if (threadIdx.x == 0) *p.freed_count = total;
-  }
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const bool first_block = b == 0 && k == 0;  // also reports the total
+
   const int64_t lo = p.range[2 * b];
   const int64_t hi = p.range[2 * b + 1];
+  const int64_t row = p.req_idx[b];
+  const int64_t base = p.base[static_cast<int64_t>(b) * p.nchunk + k];  // read only for a live chunk
+  int64_t before = 0;  // reports of requests [0, b) (block (0, 0): of all requests)
+  const int32_t upto = first_block ? p.batch : b;
+  for (int32_t i = threadIdx.x; i < upto; i += kThreads) before += p.counts[i];
+
   const int64_t c_lo = k * p.chunk > lo ? k * p.chunk : lo;
   int64_t c_hi = (k + 1) * p.chunk < hi ? (k + 1) * p.chunk : hi;
   if (c_hi > p.r2t_stride) c_hi = p.r2t_stride;
-  if (c_lo >= c_hi) return;  // workgroup-uniform
-  const int64_t row = p.req_idx[b];
-  int64_t out = -1;  // output offset of the chunk's first report, computed once needed
+  const bool live = c_lo < c_hi;
+  if (!live && !first_block) return;  // workgroup-uniform
+  constexpr int64_t kPass = kThreads * kApplyPerThread;
+  // block (0, 0) makes one pass even with nothing of its own, to write the total
+  const int64_t n_pass = live ? (c_hi - c_lo + kPass - 1) / kPass : 1;
+  const bool rows_ok = row >= 0 && row < p.r2t_rows;
+
   int64_t run = 0;
-  for (int64_t j0 = c_lo; j0 < c_hi; j0 += kBatch) {  // workgroup-uniform trip count
-    int64_t full[kPerThread], slot[kPerThread];
-    bool flag[kPerThread];
+  for (int64_t ps = 0; ps < n_pass; ++ps) {  // workgroup-uniform trip count
+    const int64_t j0 = c_lo + ps * kPass;
+    int32_t full[kApplyPerThread];
+    int64_t slot[kApplyPerThread];
+    bool flag[kApplyPerThread];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
+    for (int i = 0; i < kApplyPerThread; ++i) {
       const int64_t j = j0 + i * kThreads + threadIdx.x;
-      full[i] = -1;
-      slot[i] = 0;
-      if (j < c_hi) load_position(p, row, j, full[i], slot[i]);
+      full[i] = (rows_ok && j < c_hi) ? p.r2t[row * p.r2t_stride + j] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kApplyPerThread; ++i) {
+      const bool ok = full[i] >= 0 && full[i] < p.map_len - 1;
+      slot[i] = ok ? p.map[full[i]] : 0;
+      const int64_t j = j0 + i * kThreads + threadIdx.x;
       flag[i] = slot[i] > 0 && (j == lo || j % p.page == 0);
     }
-    int32_t rank[kPerThread], n;
-    block_ranks(flag, rank, n, cnt);
-    if (n > 0 && out < 0) out = reports_before(p, b, red) + p.base[static_cast<int64_t>(b) * p.nchunk + k];
+    // ranks of the reports in position order, and (first pass) the counts' sum,
+    // behind one barrier
+    uint64_t mask[kApplyPerThread];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
+    for (int i = 0; i < kApplyPerThread; ++i) {
+      mask[i] = __ballot(flag[i]);
+      if (lane == 0) cnt[i * 4 + w] = __popcll(mask[i]);
+    }
+    if (ps == 0) {
+      for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o);
+      if (lane == 0) red[w] = before;
+    }
+    __syncthreads();
+    if (ps == 0) {
+      before = red[0] + red[1] + red[2] + red[3];
+      if (first_block) {
+        if (threadIdx.x == 0) *p.freed_count = before;
+        before = 0;
+      }
+    }
+    const int64_t out = before + base + run;
+    int32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < kApplyPerThread; ++i) {
+      int32_t r = acc;
+      for (int v = 0; v < 4; ++v) {
+        r += v < w ? cnt[i * 4 + v] : 0;
+        acc += cnt[i * 4 + v];
+      }
       if (flag[i]) {
-        const int64_t at = out + run + rank[i];
+        const int64_t at = out + r + __popcll(mask[i] & ((1ull << lane) - 1ull));
         if (at < p.capacity) p.freed_pages[at] = slot[i] / p.page;
       }
       if (slot[i] > 0) p.map[full[i]] = 0;
     }
-    run += n;
+    run += acc;
+    if (ps + 1 < n_pass) __syncthreads();  // cnt is reused by the next pass
   }
 }
 

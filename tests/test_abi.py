@@ -209,10 +209,10 @@ def test_decode_store_argument_errors(swa):
 def test_evict_argument_errors(swa):
     lib, E = swa.lib, swa
     ix = index(swa)
-    # int32 counts, ranges (2) and one base per chunk of >= 1024 positions starting at page boundaries
-    assert lib.swa_evict_workspace_bytes(5, 4096, 16) == 5 * (3 + 4) * 4
-    assert lib.swa_evict_workspace_bytes(2, 100, 3) == 2 * (3 + 1) * 4      # chunk 1026
-    assert lib.swa_evict_workspace_bytes(1, 2049, 2048) == 1 * (3 + 2) * 4  # chunk 2048
+    # int32 counts, ranges (2) and one base per chunk of >= 2048 positions starting at page boundaries
+    assert lib.swa_evict_workspace_bytes(5, 4096, 16) == 5 * (3 + 2) * 4
+    assert lib.swa_evict_workspace_bytes(2, 100, 3) == 2 * (3 + 1) * 4      # chunk 2049
+    assert lib.swa_evict_workspace_bytes(1, 4097, 4096) == 1 * (3 + 2) * 4  # chunk 4096
     assert lib.swa_evict_workspace_bytes(0, 4096, 16) == 0
     need = lib.swa_evict_workspace_bytes(2, 100, 16)
 
@@ -235,5 +235,5 @@ def test_evict_argument_errors(swa):
     assert ev(ws=FAKE + 2) == E.SWA_E_WORKSPACE         # misaligned
     short_map = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, None, 1, 2, 16)
     assert ev(ix=short_map) == E.SWA_E_ARG              # a mapping needs its sentinel entry
-    long_rows = swa.IndexStruct(FAKE, 3, 65536 * 1024 + 1, FAKE, FAKE, None, 50, 2, 16)
+    long_rows = swa.IndexStruct(FAKE, 3, 65535 * 2048 + 1, FAKE, FAKE, None, 50, 2, 16)
     assert ev(ix=long_rows, ws_bytes=1 << 40) == E.SWA_E_SHAPE
