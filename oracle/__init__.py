@@ -14,6 +14,10 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   validate            pinned: hand-counted violations of a hand-built batch
   evict               pinned: hand-worked ranges (both modes, interval, protected
                       prefix), idempotence, and the next window has no tombstone
+  alloc_extend,       pinned: a hand-worked batch (all three parts, no prefix,
+  alloc_decode,       a one-token chunk), a token-by-token allocator written
+  alloc_paired,       independently, page size 1 = slicing the free list,
+  pages_needed        decode = extend of one token, paired offsets and mapping
   attention           pinned: full-causal reduction, plain-softmax reduction,
                       pure-Python brute force, W=0 and identical-key closed
                       forms, GQA expansion, pair-count ratio ~ 2W/T.
@@ -26,6 +30,9 @@ from . import codecs, swa_oracle  # noqa: F401
 from .swa_oracle import (  # noqa: F401
     NoSpaceError,
     OracleError,
+    alloc_decode,
+    alloc_extend,
+    alloc_paired,
     attend,
     attention,
     decode,
@@ -34,6 +41,8 @@ from .swa_oracle import (  # noqa: F401
     extend,
     kv_bytes_per_token,
     kv_store,
+    pages_bound,
+    pages_needed,
     pool_config,
     scored_pairs,
     translate_loc,

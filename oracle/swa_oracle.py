@@ -336,6 +336,115 @@ def evict(req_to_token, req_pool_idx, full_to_swa, pre_lens, evicted_lens, windo
 
 
 # ---------------------------------------------------------------------------
+# Paired allocation.  [POOLS] 三重映射 (a paged allocator hands out pages from
+# the head of its free list; page 0 is never free), alloc_extend (per request:
+# where its outputs start and where its new pages start in the free list, then
+# three parts: the rest of the half-full page from last_loc + 1, whole new
+# pages, the tail page), alloc_decode (one token per request), 扩容与不足
+# (the optimistic bound extend_tokens // P + bs + 1, else the exact count;
+# not enough pages -> nothing is allocated), and 双池 + 映射表 together with
+# [SWA] 双池与映射表 (both allocators allocate the same count, the SWA side's
+# last_loc is the mapping of the full one -- the trailing -1 turns a -1 into
+# -1 -- and the mapping is written afterwards).
+# ---------------------------------------------------------------------------
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def pages_needed(pre_lens, seq_lens, page_size) -> int:
+    """Exact number of new pages: sum over requests of ceil(seq/P) - ceil(pre/P)
+    ([POOLS] alloc_extend, the page-count formula)."""
+    return int(sum(_ceil_div(int(s), page_size) - _ceil_div(int(p), page_size)
+                   for p, s in zip(pre_lens, seq_lens)))
+
+
+def pages_bound(extend_num_tokens, batch, page_size) -> int:
+    """The optimistic upper bound of [POOLS] 扩容与不足."""
+    return int(extend_num_tokens) // page_size + int(batch) + 1
+
+
+def alloc_extend(pre_lens, seq_lens, last_loc, free_pages, page_size):
+    """One pool's allocation of the slots of positions [pre_len, seq_len) of
+    every request.  Returns (out, pages_taken) with out in request order, or
+    None when the free list is too short.  Follows [POOLS] alloc_extend."""
+    P = page_size
+    free_pages = np.asarray(free_pages, dtype=np.int64)
+    if pages_needed(pre_lens, seq_lens, P) > free_pages.size:
+        return None
+    out = []
+    new_page_start = 0  # running prefix sum of the earlier requests' new pages
+    for pre, seq, last in zip(pre_lens, seq_lens, last_loc):
+        pre, seq, last = int(pre), int(seq), int(last)
+        own_pages = _ceil_div(seq, P) - _ceil_div(pre, P)
+        # part 1: the rest of the page the prefix ends in, continuing from last_loc
+        n1 = min(seq, _ceil_div(pre, P) * P) - pre
+        out.extend(last + 1 + k for k in range(n1))
+        if pre + n1 < seq:
+            # part 2: whole new pages
+            n2 = (seq // P) * P - _ceil_div(pre, P) * P
+            for off in range(n2):
+                page = int(free_pages[new_page_start + off // P])
+                out.append(page * P + off % P)
+            # part 3: the tail, at the start of the last new page
+            n3 = seq - (seq // P) * P
+            if n3 > 0:
+                page = int(free_pages[new_page_start + own_pages - 1])
+                out.extend(page * P + k for k in range(n3))
+        new_page_start += own_pages
+    return np.asarray(out, dtype=np.int64), new_page_start
+
+
+def alloc_decode(seq_lens, last_loc, free_pages, page_size):
+    """One new token per request (pre_len = seq_len - 1): last_loc + 1 while it
+    stays in its page, else the start of the next free page.  Returns
+    (out, pages_taken) or None.  Follows [POOLS] alloc_decode."""
+    P = page_size
+    free_pages = np.asarray(free_pages, dtype=np.int64)
+    pre_lens = [int(s) - 1 for s in seq_lens]
+    if pages_needed(pre_lens, seq_lens, P) > free_pages.size:
+        return None
+    out = []
+    new_page_start = 0
+    for seq, last in zip(seq_lens, last_loc):
+        seq, pre = int(seq), int(seq) - 1
+        own = _ceil_div(seq, P) - _ceil_div(pre, P)
+        if own == 0:
+            out.append(int(last) + 1)
+        else:
+            out.append(int(free_pages[new_page_start]) * P)
+        new_page_start += own
+    return np.asarray(out, dtype=np.int64), new_page_start
+
+
+def alloc_paired(pre_lens, seq_lens, last_loc, full_free, swa_free, full_to_swa, page_size, decode=False):
+    """SWATokenToKVPoolAllocator: the same allocation on the full and the SWA
+    pool, the SWA side continuing from full_to_swa[last_loc] (index -1 reads the
+    trailing -1), then full_to_swa[full_out] = swa_out.  Returns (full_out,
+    swa_out, mapping, pages_taken) or None if either free list is too short.
+    With swa_free None (one pool) only the full allocation is made."""
+    m = np.array(full_to_swa, dtype=np.int64, copy=True) if full_to_swa is not None else None
+    if decode:
+        full = alloc_decode(seq_lens, last_loc, full_free, page_size)
+    else:
+        full = alloc_extend(pre_lens, seq_lens, last_loc, full_free, page_size)
+    if full is None:
+        return None
+    if swa_free is None:
+        return full[0], None, m, full[1]
+    swa_last = [int(m[int(x)]) for x in last_loc]  # Python's m[-1] is the sentinel
+    if decode:
+        swa = alloc_decode(seq_lens, swa_last, swa_free, page_size)
+    else:
+        swa = alloc_extend(pre_lens, seq_lens, swa_last, swa_free, page_size)
+    if swa is None:
+        return None
+    m[full[0]] = swa[0]
+    return full[0], swa[0], m, full[1]
+
+
+# ---------------------------------------------------------------------------
 # Index-data contracts, counted rather than raised.  [SWA] 双池与映射表 and
 # 运行时: a live window never holds a tombstone (eviction frees only positions
 # that left the window) and the mapping ends in the -1 sentinel that a -1 loc

@@ -634,3 +634,129 @@ def test_evict_keeps_the_next_window_and_its_attention():
     swa_pages_after = set((m[m > 0] // 16).tolist())
     assert set(pages.tolist()) <= swa_pages_before
     assert not set(pages.tolist()) & swa_pages_after
+
+
+# ---------------------------------------------------------------------------
+# paired allocation ([POOLS] 三重映射, alloc_extend, alloc_decode, 扩容与不足,
+# 双池 + 映射表): slot = page * P + offset
+# ---------------------------------------------------------------------------
+
+# A batch worked by hand with P = 4 and free list [5, 3, 8, 1, 6, 2, 7]:
+#   req 0: prefix 6, seq 15, last_loc 29 (page 7, offset 1 = (6-1) % 4).
+#          part 1 fills positions 6, 7 -> 30, 31; it needs ceil(15/4) - ceil(6/4) = 2
+#          new pages (5 and 3): positions 8..11 -> 20..23 (page 5), then the tail
+#          12..14 -> 12, 13, 14 at the start of its last new page (3).
+#   req 1: no prefix (last_loc -1), seq 5: pages 8 and 1 -> 32..35 and 4.
+#   req 2: prefix 8 (page aligned, no part 1), seq 9: one page (6) -> 24.
+#   req 3: prefix 3, seq 4: the token stays in the half-full page: 38 + 1 = 39.
+HAND_ALLOC = dict(pre=[6, 0, 8, 3], seq=[15, 5, 9, 4], last=[29, -1, 11, 38], free=[5, 3, 8, 1, 6, 2, 7], P=4,
+                  out=[30, 31, 20, 21, 22, 23, 12, 13, 14, 32, 33, 34, 35, 4, 24, 39], pages=5)
+
+
+def test_alloc_extend_hand_worked():
+    h = HAND_ALLOC
+    out, taken = O.alloc_extend(h["pre"], h["seq"], h["last"], h["free"], h["P"])
+    assert out.tolist() == h["out"] and taken == h["pages"]
+    assert O.pages_needed(h["pre"], h["seq"], h["P"]) == h["pages"]
+    # one page fewer on the free list: nothing is allocated
+    assert O.alloc_extend(h["pre"], h["seq"], h["last"], h["free"][:4], h["P"]) is None
+
+
+def _token_by_token(pre_lens, seq_lens, last_loc, free, P):
+    """An allocator that walks every new position in order and takes the next
+    free page whenever a position starts a page; a position in the page the
+    prefix ends in uses that page (the page of last_loc)."""
+    out, nxt = [], 0
+    for pre, seq, last in zip(pre_lens, seq_lens, last_loc):
+        page = last // P if pre % P else None
+        for j in range(pre, seq):
+            if j % P == 0:
+                page = free[nxt]
+                nxt += 1
+            out.append(page * P + j % P)
+    return out, nxt
+
+
+def _alloc_case(rng, B, P, max_len=300):
+    pre = rng.integers(0, max_len, B)
+    pre[rng.random(B) < 0.3] = 0
+    seq = pre + rng.integers(0, max_len, B)
+    # last_loc: a slot of some used page, at the in-page offset of position pre - 1
+    last = np.where(pre > 0, (rng.integers(1000, 2000, B)) * P + (pre - 1) % P, -1)
+    free = rng.permutation(np.arange(1, 1000))
+    return pre, seq, last, free
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 16, 64])
+def test_alloc_extend_equals_token_by_token(P):
+    rng = np.random.default_rng(300 + P)
+    for _ in range(20):
+        pre, seq, last, free = _alloc_case(rng, int(rng.integers(1, 9)), P)
+        if O.pages_needed(pre, seq, P) > free.size:
+            continue
+        want, taken = _token_by_token(pre.tolist(), seq.tolist(), last.tolist(), free.tolist(), P)
+        out, n = O.alloc_extend(pre, seq, last, free, P)
+        assert out.tolist() == want and n == taken
+        assert np.unique(out).size == out.size and not np.any((out >= 0) & (out < P))   # distinct, never page 0
+        pos = np.concatenate([np.arange(p, s) for p, s in zip(pre, seq)])
+        assert np.array_equal(out % P, pos % P)                                         # in-page offsets
+        assert O.pages_bound(int((seq - pre).sum()), len(pre), P) >= n
+
+
+def test_alloc_page_size_one_slices_the_free_list():
+    rng = np.random.default_rng(311)
+    pre, seq, last, free = _alloc_case(rng, 6, 1)
+    n = int((seq - pre).sum())
+    out, taken = O.alloc_extend(pre, seq, last, free, 1)
+    assert out.tolist() == free[:n].tolist() and taken == n
+
+
+@pytest.mark.parametrize("P", [1, 4, 64])
+def test_alloc_decode_is_extend_of_one_token(P):
+    rng = np.random.default_rng(320 + P)
+    seq = rng.integers(1, 500, 40)
+    seq[:4] = [1, P, P + 1, 2 * P]
+    last = np.where(seq > 1, rng.integers(1000, 2000, 40) * P + (seq - 2) % P, -1)
+    free = rng.permutation(np.arange(1, 500))
+    dec, n_dec = O.alloc_decode(seq, last, free, P)
+    ext, n_ext = O.alloc_extend(seq - 1, seq, last, free, P)
+    assert dec.tolist() == ext.tolist() and n_dec == n_ext == int(np.sum((seq - 1) % P == 0))
+
+
+def test_alloc_paired_offsets_mapping_and_sentinel():
+    P = 16
+    rng = np.random.default_rng(330)
+    B = 6
+    pre = np.array([0, 5, 16, 31, 100, 0])
+    seq = pre + np.array([40, 11, 1, 33, 0, 16])
+    n_full = 64 * P
+    mapping = np.zeros(n_full + P + 1, np.int64)
+    mapping[-1] = -1
+    # existing prefixes: full page fp <-> SWA page sp, same offsets
+    last = np.full(B, -1)
+    for b in range(B):
+        if pre[b]:
+            fp, sp = 40 + b, 20 + b
+            last[b] = fp * P + (pre[b] - 1) % P
+            mapping[fp * P:(fp + 1) * P] = sp * P + np.arange(P)
+    full_free = rng.permutation(np.arange(1, 40))
+    swa_free = rng.permutation(np.arange(1, 20))
+    full, swa, m, taken = O.alloc_paired(pre, seq, last, full_free, swa_free, mapping, P)
+    assert full.size == swa.size == int((seq - pre).sum())
+    assert np.array_equal(full % P, swa % P)
+    assert np.array_equal(m[full], swa)
+    untouched = np.ones(m.size, bool)
+    untouched[full] = False
+    assert np.array_equal(m[untouched], mapping[untouched]) and m[-1] == -1
+    # the SWA side continued from the mapped last_loc, e.g. request 1's first token
+    assert swa[40] == mapping[last[1]] + 1
+    # either free list too short: nothing
+    need = O.pages_needed(pre, seq, P)
+    assert O.alloc_paired(pre, seq, last, full_free, swa_free[:need - 1], mapping, P) is None
+
+
+def test_alloc_pins_catch_floor_for_ceil(monkeypatch):
+    monkeypatch.setattr(O, "_ceil_div", lambda a, b: a // b)
+    h = HAND_ALLOC
+    got = O.alloc_extend(h["pre"], h["seq"], h["last"], h["free"], h["P"])
+    assert got is None or got[0].tolist() != h["out"]
