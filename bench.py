@@ -1,11 +1,12 @@
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|evict]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|evict|alloc]
 
 Other workloads (one JSON line each, same fields): c1 single f32 decode; c3
 chunked-prefill extend (store + extend over 4 layers); c4 the 48-layer mixed
 decode step (39 SWA + 9 full layers); c5 fp8-KV decode with store; evict the
-SWA eviction of the c5 batch right after its prefill.
+SWA eviction of the c5 batch right after its prefill; alloc the paired
+allocation of a prefill chunk (and of a decode step) for the c5 batch.
 
 Default workload (c2): batched SWA decode, B = 64 requests with context lengths
 uniform in [1K, 8K], W = 128, 64 q / 8 kv heads, head_dim 128, bf16, page 16,
@@ -646,6 +647,98 @@ def run_evict_workload(args, torch, swa, W):
     return res
 
 
+# ---------------------------------------------------------------------------
+# alloc: paired allocation for the c5 batch (a prefill chunk, a decode step)
+# ---------------------------------------------------------------------------
+
+
+class AllocBench:
+    """One allocation call on device copies of an allocation state.  The call
+    only writes outputs and mapping entries whose values do not depend on what
+    the previous call wrote, so replays repeat the same work."""
+
+    def __init__(self, torch, swa, ab, decode):
+        self.torch, self.swa, self.ab, self.decode = torch, swa, ab, decode
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.pre, self.seq, self.last = dev(ab.pre_lens), dev(ab.seq_lens), dev(ab.last_loc)
+        self.map = dev(ab.full_to_swa)
+        self.free_full, self.free_swa = dev(ab.free_full), dev(ab.free_swa)
+        self.n = ab.batch if decode else int((ab.seq_lens.astype(np.int64) - ab.pre_lens).sum())
+        self.out_full = torch.empty(self.n, dtype=torch.int64, device="cuda")
+        self.out_swa = torch.empty(self.n, dtype=torch.int64, device="cuda")
+        self.new_pages = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.pages = swa.swa_alloc_pages_needed(None if decode else ab.pre_lens, ab.seq_lens, ab.page_size)
+        # algorithmic bytes: per request its lengths and last_loc (16 B, decode 12 B) and
+        # the mapped last_loc (8 B); per new position both slots written (16 B) and its
+        # mapping entry written (8 B); per new page one entry read from each free list
+        self.bytes = ab.batch * ((12 if decode else 16) + 8) + self.n * 24 + self.pages * 16 + 8
+
+    def call(self):
+        ab, swa = self.ab, self.swa
+        if self.decode:
+            ok = swa.swa_alloc_decode(self.seq, self.last, ab.page_size, self.free_full, self.out_full,
+                                      free_swa=self.free_swa, full_to_swa=self.map, out_swa=self.out_swa,
+                                      new_pages=self.new_pages, seq_lens_host=ab.seq_lens)
+        else:
+            ok = swa.swa_alloc_extend(self.pre, self.seq, self.last, ab.page_size, self.free_full, self.out_full,
+                                      free_swa=self.free_swa, full_to_swa=self.map, out_swa=self.out_swa,
+                                      new_pages=self.new_pages, pre_lens_host=ab.pre_lens, seq_lens_host=ab.seq_lens)
+        if not ok:
+            raise RuntimeError("allocation refused: free lists too short")
+
+
+def cpu_baseline_alloc(ab, decode, budget_s=12.0):
+    from oracle import swa_oracle as O
+    reps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        O.alloc_paired(ab.pre_lens, ab.seq_lens, ab.last_loc, ab.free_full, ab.free_swa, ab.full_to_swa,
+                       ab.page_size, decode=decode)
+        reps += 1
+    return time.perf_counter() - t0, reps
+
+
+def run_alloc_workload(args, torch, swa, W):
+    log("[bench] alloc: building the prefill-chunk and decode-step states")
+    ext = AllocBench(torch, swa, W.alloc_prefill_chunk(), decode=False)
+    dec = AllocBench(torch, swa, W.alloc_decode_step(), decode=True)
+    reps = 32  # calls per graph replay
+    g_ext = graph_of(torch, lambda: [ext.call() for _ in range(reps)])
+    g_dec = graph_of(torch, lambda: [dec.call() for _ in range(reps)])
+    for _ in range(max(1, args.warmup // reps)):
+        g_ext.replay()
+        g_dec.replay()
+    n_rep = max(1, -(-args.steps // reps))
+    ms = time_replays(torch, g_ext, n_rep) / reps
+    pct = replay_percentiles(torch, g_ext, n_rep, reps)
+    ms_dec = time_replays(torch, g_dec, n_rep) / reps
+    value = ext.bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] alloc_extend {ms * 1e3:.2f} us ({ext.n} positions, {ext.pages} pages per pool); "
+        f"alloc_decode {ms_dec * 1e3:.2f} us ({dec.n} requests, {dec.pages} pages)")
+    traffic = traffic_from_profile("swa_alloc_prefill_chunk", ["alloc_kernels.hip", "common.hpp", "api.cpp"], 1)
+    res = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=n_rep * reps, warmup=args.warmup,
+        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="int64",
+        data="synthetic",
+        config={"workload": "paired allocation (full and SWA pool, mapping written) of one 2048-position prefill "
+                            "chunk for each of 256 requests with lognormal lengths (median 16K), page 64",
+                "global_batch": int(ext.ab.batch), "page_size": ext.ab.page_size, "new_positions": ext.n,
+                "new_pages_per_pool": int(ext.pages), "parallelism": "none (1 GPU)"},
+        positions_per_s=round(ext.n / (ms * 1e-3), 1),
+        decode_step_us=round(ms_dec * 1e3, 3),
+        decode_step="alloc_decode of one position for each of the same 256 requests",
+        roofline=dict(kernel="alloc_extend", bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(value / HBM_PEAK_GBS, 4), traffic=traffic, bytes_per_launch=ext.bytes,
+                      us_per_launch=round(ms * 1e3, 3), **pct),
+    )
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        secs, n = cpu_baseline_alloc(ext.ab, False)
+        res["cpu_baseline"] = dict(value=round(n * ext.bytes / secs / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
+                                   sample=f"the whole prefill-chunk allocation, {n} times ({secs:.1f} s)")
+    return res
+
+
 def copy_probe(torch, reps=5):
     """A plain elementwise kernel of known traffic (1 GiB read + 1 GiB written
     per launch), run so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can
@@ -665,7 +758,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "evict"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "evict", "alloc"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-noop", action="store_true",
                     help="evict: skip timing the calls that release nothing (for profiling runs)")
@@ -692,6 +785,8 @@ def main():
         res = run_mixed_workload(args, torch, swa, W)
     elif args.workload == "evict":
         res = run_evict_workload(args, torch, swa, W)
+    elif args.workload == "alloc":
+        res = run_alloc_workload(args, torch, swa, W)
     else:
         res = run_decode_workload(args, torch, swa, W)
     print(json.dumps(res), flush=True)

@@ -43,7 +43,9 @@ typedef enum swa_status {
   SWA_E_ARG = -1,       /* null pointer, negative size, inconsistent arguments */
   SWA_E_DTYPE = -2,     /* unsupported dtype or dtype combination */
   SWA_E_SHAPE = -3,     /* unsupported head_dim / head counts / group size */
-  SWA_E_NOSPACE = -4,   /* pool sizing: the SWA pool cannot hold one request */
+  SWA_E_NOSPACE = -4,   /* pool sizing: the SWA pool cannot hold one request;
+                           allocation: a free list is (or cannot be shown to be)
+                           too short */
   SWA_E_WORKSPACE = -5, /* workspace missing or smaller than required */
   SWA_E_HIP = -6        /* the HIP runtime reported an error (launch / query) */
 } swa_status_t;
@@ -261,6 +263,70 @@ swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32
                        const int32_t *protected_lens, int32_t *evicted_lens, int32_t window, int32_t mode,
                        int32_t interval, int64_t *freed_pages, int64_t freed_capacity, int64_t *freed_count,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Paired allocation ([POOLS] 三重映射, alloc_extend, alloc_decode, 扩容与不足
+ * and SWATokenToKVPoolAllocator; [SWA] 双池与映射表: alloc, alloc_extend and
+ * alloc_decode take the same number of slots from both allocators, then write
+ * the mapping).
+ *
+ * A paged allocator's free list is an array of page numbers handed out from
+ * its head; page 0 is never on it.  The caller passes each list from its
+ * current head and advances the head by the number of pages taken (*new_pages,
+ * or swa_alloc_pages_needed on host copies of the lengths); freeing is the
+ * caller's (pages released by swa_evict go back on the SWA list).
+ *
+ * For request b (page size P, pre = pre_lens[b], seq = seq_lens[b]) the new
+ * positions [pre, seq) get, in order and packed after the earlier requests'
+ * new positions in out_full / out_swa:
+ *   - positions before ceil_P(pre) (the rest of the page the prefix ends in):
+ *     last + 1, last + 2, ..., where last is last_loc[b] on the full side and
+ *     full_to_swa[last_loc[b]] on the SWA side (-1, no prefix, stays -1);
+ *   - position p >= ceil_P(pre): page * P + p mod P, with page the request's
+ *     ((p - ceil_P(pre)) / P)-th new page; the request's new pages are
+ *     ceil(seq/P) - ceil(pre/P) consecutive entries of each free list, after
+ *     the earlier requests' new pages.
+ * Then full_to_swa[full slot] = SWA slot for every new position.  With
+ * swa_list NULL only the full pool is allocated (one-pool cache) and
+ * full_to_swa is not used.
+ *
+ * Before anything is launched the host proves that the free lists are long
+ * enough, as the pages do: first with the bound extend_num_tokens / P + batch
+ * + 1 (decode: batch); if that does not fit, with the exact count from the host
+ * copies of the lengths; if those are NULL or the count does not fit, the call
+ * returns SWA_E_NOSPACE and changes nothing.  The kernels never read past a
+ * free list (a page beyond it would read as page 0) and never write more than
+ * extend_num_tokens (decode: batch) outputs.
+ *   pre_lens, seq_lens  device int32 [batch]; last_loc device int64 [batch]:
+ *                the full slot of position pre - 1 (decode: seq - 2), or -1.
+ *   full, swa_list  [host] structs naming device int64 free lists.
+ *   full_to_swa  the mapping (map_len entries, trailing -1), written in place.
+ *   extend_num_tokens  [host] sum of seq - pre, the length of the outputs.
+ *   pre_lens_host, seq_lens_host  [host] optional copies for the exact count.
+ *   out_full, out_swa  device int64 (out_swa may be NULL).
+ *   new_pages  optional device int64: the pages taken from each list.
+ * Errors: SWA_E_ARG, SWA_E_NOSPACE. */
+typedef struct swa_free_list {
+  const int64_t *pages; /* device int64 page numbers, taken from index 0 on */
+  int64_t count;        /* entries available */
+} swa_free_list_t;
+
+/* [host] The exact number of new pages: sum of ceil(seq/P) - ceil(pre/P) over
+ * host arrays (pre_lens NULL: decode, pre = seq - 1).  -1 on bad arguments. */
+int64_t swa_alloc_pages_needed(const int32_t *pre_lens, const int32_t *seq_lens, int32_t batch, int32_t page_size);
+
+swa_status_t swa_alloc_extend(int32_t batch, int32_t page_size, const int32_t *pre_lens, const int32_t *seq_lens,
+                              const int64_t *last_loc, const swa_free_list_t *full, const swa_free_list_t *swa_list,
+                              int64_t *full_to_swa, int64_t map_len, int64_t extend_num_tokens,
+                              const int32_t *pre_lens_host, const int32_t *seq_lens_host, int64_t *out_full,
+                              int64_t *out_swa, int64_t *new_pages, hipStream_t stream);
+
+/* One new token per request (pre = seq - 1): last + 1 while it stays in its
+ * page, else the start of the next free page ([POOLS] alloc_decode). */
+swa_status_t swa_alloc_decode(int32_t batch, int32_t page_size, const int32_t *seq_lens, const int64_t *last_loc,
+                              const swa_free_list_t *full, const swa_free_list_t *swa_list, int64_t *full_to_swa,
+                              int64_t map_len, const int32_t *seq_lens_host, int64_t *out_full, int64_t *out_swa,
+                              int64_t *new_pages, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Validation (debugging aid; SYNCHRONOUS: waits for `stream`).  Counts the

@@ -34,7 +34,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["api.cpp", "index_kernels.hip", "store_kernels.hip", "decode_kernels.hip", "extend_kernels.hip",
-           "validate_kernels.hip", "evict_kernels.hip"]
+           "validate_kernels.hip", "evict_kernels.hip", "alloc_kernels.hip"]
 
 
 def hipcc() -> str:

@@ -254,6 +254,89 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
   return from_hip(swa::launch_extend(a, stream));
 }
 
+int64_t swa_alloc_pages_needed(const int32_t *pre_lens, const int32_t *seq_lens, int32_t batch, int32_t page_size) {
+  if (batch < 0 || page_size < 1 || (batch > 0 && !seq_lens)) return -1;
+  int64_t n = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    int64_t seq = seq_lens[b];
+    int64_t pre = pre_lens ? pre_lens[b] : seq - 1;
+    if (pre < 0) pre = 0;
+    if (seq < pre) seq = pre;
+    n += (seq + page_size - 1) / page_size - (pre + page_size - 1) / page_size;
+  }
+  return n;
+}
+
+namespace {
+
+// The sufficiency check that must pass before an allocation kernel reads a
+// free list: the optimistic bound first, then (with host copies of the
+// lengths) the exact count.
+swa_status_t alloc_fits(int32_t batch, int32_t page, int64_t bound, const int32_t *pre_host,
+                        const int32_t *seq_host, int64_t avail) {
+  if (bound <= avail) return SWA_OK;
+  if (!seq_host) return SWA_E_NOSPACE;
+  const int64_t exact = swa_alloc_pages_needed(pre_host, seq_host, batch, page);
+  return exact <= avail ? SWA_OK : SWA_E_NOSPACE;
+}
+
+swa_status_t alloc_impl(bool decode, int32_t batch, int32_t page_size, const int32_t *pre_lens,
+                        const int32_t *seq_lens, const int64_t *last_loc, const swa_free_list_t *full,
+                        const swa_free_list_t *swa_list, int64_t *full_to_swa, int64_t map_len, int64_t n_tokens,
+                        const int32_t *pre_host, const int32_t *seq_host, int64_t *out_full, int64_t *out_swa,
+                        int64_t *new_pages, hipStream_t stream) {
+  if (batch < 0 || page_size < 1 || n_tokens < 0 || !full || full->count < 0) return SWA_E_ARG;
+  if (batch > 0 && (!seq_lens || !last_loc || (!decode && !pre_lens))) return SWA_E_ARG;
+  if (full->count > 0 && !full->pages) return SWA_E_ARG;
+  if (n_tokens > 0 && !out_full) return SWA_E_ARG;
+  if (swa_list) {
+    if (swa_list->count < 0 || (swa_list->count > 0 && !swa_list->pages)) return SWA_E_ARG;
+    if (!full_to_swa || map_len < 2) return SWA_E_ARG;
+  }
+  int64_t avail = full->count;
+  if (swa_list && swa_list->count < avail) avail = swa_list->count;
+  const int64_t bound = decode ? batch : n_tokens / page_size + batch + 1;
+  const swa_status_t fits = alloc_fits(batch, page_size, bound, decode ? nullptr : pre_host, seq_host, avail);
+  if (fits != SWA_OK) return fits;
+  swa::AllocArgs a{};
+  a.batch = batch;
+  a.page_size = page_size;
+  a.decode = decode;
+  a.pre_lens = decode ? nullptr : pre_lens;
+  a.seq_lens = seq_lens;
+  a.last_loc = last_loc;
+  a.free_full = full->pages;
+  a.n_free_full = full->count;
+  a.free_swa = swa_list ? swa_list->pages : nullptr;
+  a.n_free_swa = swa_list ? swa_list->count : 0;
+  a.full_to_swa = swa_list ? full_to_swa : nullptr;
+  a.map_len = swa_list ? map_len : 0;
+  a.out_full = out_full;
+  a.out_swa = swa_list ? out_swa : nullptr;
+  a.capacity = n_tokens;
+  a.new_pages = new_pages;
+  return from_hip(swa::launch_alloc(a, stream));
+}
+
+}  // namespace
+
+swa_status_t swa_alloc_extend(int32_t batch, int32_t page_size, const int32_t *pre_lens, const int32_t *seq_lens,
+                              const int64_t *last_loc, const swa_free_list_t *full, const swa_free_list_t *swa_list,
+                              int64_t *full_to_swa, int64_t map_len, int64_t extend_num_tokens,
+                              const int32_t *pre_lens_host, const int32_t *seq_lens_host, int64_t *out_full,
+                              int64_t *out_swa, int64_t *new_pages, hipStream_t stream) {
+  return alloc_impl(false, batch, page_size, pre_lens, seq_lens, last_loc, full, swa_list, full_to_swa, map_len,
+                    extend_num_tokens, pre_lens_host, seq_lens_host, out_full, out_swa, new_pages, stream);
+}
+
+swa_status_t swa_alloc_decode(int32_t batch, int32_t page_size, const int32_t *seq_lens, const int64_t *last_loc,
+                              const swa_free_list_t *full, const swa_free_list_t *swa_list, int64_t *full_to_swa,
+                              int64_t map_len, const int32_t *seq_lens_host, int64_t *out_full, int64_t *out_swa,
+                              int64_t *new_pages, hipStream_t stream) {
+  return alloc_impl(true, batch, page_size, nullptr, seq_lens, last_loc, full, swa_list, full_to_swa, map_len, batch,
+                    nullptr, seq_lens_host, out_full, out_swa, new_pages, stream);
+}
+
 size_t swa_evict_workspace_bytes(int32_t batch, int64_t r2t_stride, int32_t page_size) {
   if (batch <= 0 || r2t_stride < 1 || page_size < 1) return 0;
   return static_cast<size_t>(batch) * static_cast<size_t>(3 + swa::evict_chunks(r2t_stride, page_size)) *

@@ -143,6 +143,27 @@ hipError_t launch_evict(const swa_index_t &idx, int64_t *full_to_swa, const int3
                         int32_t interval, int64_t *freed_pages, int64_t capacity, int64_t *freed_count,
                         int32_t *workspace, hipStream_t stream);
 
+struct AllocArgs {
+  int32_t batch;
+  int32_t page_size;
+  bool decode;              // one new token per request (pre = seq - 1; pre_lens unused)
+  const int32_t *pre_lens;  // device
+  const int32_t *seq_lens;  // device
+  const int64_t *last_loc;  // device: full slot of position pre - 1, or -1
+  const int64_t *free_full;
+  int64_t n_free_full;
+  const int64_t *free_swa;  // null: one pool
+  int64_t n_free_swa;
+  int64_t *full_to_swa;
+  int64_t map_len;
+  int64_t *out_full;
+  int64_t *out_swa;
+  int64_t capacity;
+  int64_t *new_pages;
+};
+
+hipError_t launch_alloc(const AllocArgs &a, hipStream_t stream);
+
 struct ExtendArgs {
   const void *q;
   int32_t q_heads;

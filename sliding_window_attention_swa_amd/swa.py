@@ -16,6 +16,7 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
@@ -26,8 +27,8 @@ SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 # every symbol include/swa.h declares
 EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
            "swa_decode", "swa_decode_store", "swa_extend", "swa_validate_workspace_bytes", "swa_validate",
-           "swa_evict_workspace_bytes", "swa_evict",
-           "swa_status_string")
+           "swa_evict_workspace_bytes", "swa_evict", "swa_alloc_pages_needed", "swa_alloc_extend",
+           "swa_alloc_decode", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -55,6 +56,10 @@ class IndexStruct(ctypes.Structure):
     _fields_ = [("req_to_token", ctypes.c_void_p), ("r2t_rows", ctypes.c_int64), ("r2t_stride", ctypes.c_int64),
                 ("req_pool_idx", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("full_to_swa", ctypes.c_void_p),
                 ("map_len", ctypes.c_int64), ("batch", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+class FreeListStruct(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("count", ctypes.c_int64)]
 
 
 VALIDATE_FIELDS = ("bad_requests", "positions", "full_out_of_range", "tombstones", "sentinels", "slot_out_of_range",
@@ -85,6 +90,11 @@ _sig = {
                             ctypes.POINTER(ValidateReportStruct), _p]),
     "swa_evict_workspace_bytes": (_sz, [_i32, _i64, _i32]),
     "swa_evict": (_i32, [ctypes.POINTER(IndexStruct), _p, _p, _p, _p, _i32, _i32, _i32, _p, _i64, _p, _p, _sz, _p]),
+    "swa_alloc_pages_needed": (_i64, [_p, _p, _i32, _i32]),
+    "swa_alloc_extend": (_i32, [_i32, _i32, _p, _p, _p, ctypes.POINTER(FreeListStruct), ctypes.POINTER(FreeListStruct),
+                                _p, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "swa_alloc_decode": (_i32, [_i32, _i32, _p, _p, ctypes.POINTER(FreeListStruct), ctypes.POINTER(FreeListStruct),
+                                _p, _i64, _p, _p, _p, _p, _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -309,3 +319,79 @@ def swa_evict(index: IndexTables, full_to_swa: torch.Tensor, pre_lens: torch.Ten
                          _ptr(freed_pages, torch.int64, "freed_pages"), freed_pages.numel(),
                          _ptr(freed_count, torch.int64, "freed_count"), _ptr(workspace, torch.int32, "workspace"),
                          workspace.numel() * 4, _stream(stream)), "swa_evict")
+
+
+def _host_i32(a) -> Optional[np.ndarray]:
+    """A host copy of lengths as a contiguous int32 numpy array (kept alive by the caller)."""
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError("host lengths must be on the host")
+        a = a.numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _free_list(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    return FreeListStruct(_ptr(t, torch.int64, name) if t.numel() else None, t.numel())
+
+
+def swa_alloc_pages_needed(pre_lens_host, seq_lens_host, page_size: int) -> int:
+    """Exact new-page count from host lengths (pre_lens_host None: decode)."""
+    pre, seq = _host_i32(pre_lens_host), _host_i32(seq_lens_host)
+    n = lib.swa_alloc_pages_needed(None if pre is None else pre.ctypes.data, seq.ctypes.data, seq.size, page_size)
+    if n < 0:
+        raise SwaError(SWA_E_ARG, "swa_alloc_pages_needed")
+    return n
+
+
+def swa_alloc_extend(pre_lens: torch.Tensor, seq_lens: torch.Tensor, last_loc: torch.Tensor, page_size: int,
+                     free_full: torch.Tensor, out_full: torch.Tensor, free_swa: Optional[torch.Tensor] = None,
+                     full_to_swa: Optional[torch.Tensor] = None, out_swa: Optional[torch.Tensor] = None,
+                     new_pages: Optional[torch.Tensor] = None, pre_lens_host=None, seq_lens_host=None,
+                     stream=None) -> bool:
+    """Allocate the new positions [pre, seq) of every request (free lists
+    passed from their heads).  Returns False, changing nothing, when the free
+    lists are not provably long enough."""
+    pre_h, seq_h = _host_i32(pre_lens_host), _host_i32(seq_lens_host)
+    ff, fs = _free_list(free_full, "free_full"), _free_list(free_swa, "free_swa")
+    if out_swa is not None and out_swa.numel() < out_full.numel():
+        raise ValueError("out_swa must be as long as out_full")
+    st = lib.swa_alloc_extend(seq_lens.numel(), page_size, _ptr(pre_lens, torch.int32, "pre_lens"),
+                              _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(last_loc, torch.int64, "last_loc"),
+                              ctypes.byref(ff), None if fs is None else ctypes.byref(fs),
+                              _ptr(full_to_swa, torch.int64, "full_to_swa"),
+                              0 if full_to_swa is None else full_to_swa.numel(), out_full.numel(),
+                              None if pre_h is None else pre_h.ctypes.data,
+                              None if seq_h is None else seq_h.ctypes.data, _ptr(out_full, torch.int64, "out_full"),
+                              _ptr(out_swa, torch.int64, "out_swa"), _ptr(new_pages, torch.int64, "new_pages"),
+                              _stream(stream))
+    if st == SWA_E_NOSPACE:
+        return False
+    _check(st, "swa_alloc_extend")
+    return True
+
+
+def swa_alloc_decode(seq_lens: torch.Tensor, last_loc: torch.Tensor, page_size: int, free_full: torch.Tensor,
+                     out_full: torch.Tensor, free_swa: Optional[torch.Tensor] = None,
+                     full_to_swa: Optional[torch.Tensor] = None, out_swa: Optional[torch.Tensor] = None,
+                     new_pages: Optional[torch.Tensor] = None, seq_lens_host=None, stream=None) -> bool:
+    """One new token per request; returns False, changing nothing, when the
+    free lists are not provably long enough."""
+    seq_h = _host_i32(seq_lens_host)
+    ff, fs = _free_list(free_full, "free_full"), _free_list(free_swa, "free_swa")
+    if out_full.numel() < seq_lens.numel() or (out_swa is not None and out_swa.numel() < seq_lens.numel()):
+        raise ValueError("out_full and out_swa need one entry per request")
+    st = lib.swa_alloc_decode(seq_lens.numel(), page_size, _ptr(seq_lens, torch.int32, "seq_lens"),
+                              _ptr(last_loc, torch.int64, "last_loc"), ctypes.byref(ff),
+                              None if fs is None else ctypes.byref(fs), _ptr(full_to_swa, torch.int64, "full_to_swa"),
+                              0 if full_to_swa is None else full_to_swa.numel(),
+                              None if seq_h is None else seq_h.ctypes.data, _ptr(out_full, torch.int64, "out_full"),
+                              _ptr(out_swa, torch.int64, "out_swa"), _ptr(new_pages, torch.int64, "new_pages"),
+                              _stream(stream))
+    if st == SWA_E_NOSPACE:
+        return False
+    _check(st, "swa_alloc_decode")
+    return True

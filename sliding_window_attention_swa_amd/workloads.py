@@ -429,3 +429,62 @@ def evict_after_prefill(seed=SEED_BASE + 5, batch=256) -> EvictBatch:
     holds an SWA slot and nothing has been evicted, so the first decode step's
     eviction releases every page before the window."""
     return evict_batch("evict_after_prefill_B256", seed, c5_lengths(seed, batch), 64, 128)
+
+
+# ---------------------------------------------------------------------------
+# Allocation: index structures and free lists only
+# ---------------------------------------------------------------------------
+
+@dataclass
+class AllocBatch:
+    name: str
+    batch: int
+    page_size: int
+    pre_lens: np.ndarray          # int32 (B,): positions already held
+    seq_lens: np.ndarray          # int32 (B,): positions after the allocation
+    last_loc: np.ndarray          # int64 (B,): full slot of position pre - 1, or -1
+    req_to_token: np.ndarray      # int32 (B + 1, stride)
+    req_pool_idx: np.ndarray      # int32 (B,)
+    full_to_swa: np.ndarray       # int64 (n_full + P + 1,)
+    free_full: np.ndarray         # int64 full pages not in use, in a seeded order
+    free_swa: np.ndarray          # int64 SWA pages not in use, in a seeded order
+    n_full: int
+    n_swa: int
+
+
+def alloc_batch(name, seed, pre_lens, seq_lens, page_size, window=128, margin=128, slack_pages=4) -> AllocBatch:
+    """Requests holding pre_lens positions (laid out like the decode workloads:
+    SWA pages only from pre - window - margin on) that will grow to seq_lens;
+    both pools get room for the growth plus slack_pages, and every page not in
+    use goes on a free list in a seeded order."""
+    _, r_full, r_swa, _, _, _, _, r_free = _streams(seed)
+    pre = np.asarray(pre_lens, dtype=np.int64)
+    seq = np.asarray(seq_lens, dtype=np.int64)
+    B, P = len(pre), page_size
+    grow = int(sum(-(-int(s) // P) - -(-int(p) // P) for p, s in zip(pre, seq))) * P
+    n_full = round_up(int(sum(round_up(int(t), P) for t in pre)) + grow + slack_pages * P, P)
+    live_from = np.maximum(pre - window - margin, 0)
+    need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(pre, live_from)))
+    n_swa = round_up(need + grow + slack_pages * P, P)
+    r2t, mapping, _ = _layout(pre, P, n_full, n_swa, live_from, r_full, r_swa, stride=max(int(seq.max()), 1))
+    used_full = np.unique(r2t[1:][r2t[1:] > 0] // P) if pre.sum() else np.zeros(0, np.int64)
+    used_swa = np.unique(mapping[:-1][mapping[:-1] > 0] // P)
+    free_full = r_free.permutation(np.setdiff1d(np.arange(1, n_full // P + 1), used_full)).astype(np.int64)
+    free_swa = r_free.permutation(np.setdiff1d(np.arange(1, n_swa // P + 1), used_swa)).astype(np.int64)
+    rows = np.arange(1, B + 1)
+    last = np.where(pre > 0, r2t[rows, np.maximum(pre - 1, 0)], -1).astype(np.int64)
+    return AllocBatch(name, B, P, pre.astype(np.int32), seq.astype(np.int32), last, r2t, rows.astype(np.int32),
+                      mapping, free_full, free_swa, n_full, n_swa)
+
+
+def alloc_prefill_chunk(seed=SEED_BASE + 5, batch=256, chunk=2048) -> AllocBatch:
+    """The fp8 decode batch (B = 256, lognormal lengths, P = 64) taking one more
+    prefill chunk of 2048 positions per request."""
+    pre = c5_lengths(seed, batch)
+    return alloc_batch("alloc_chunk2048_B256", seed, pre, pre + chunk, 64)
+
+
+def alloc_decode_step(seed=SEED_BASE + 5, batch=256) -> AllocBatch:
+    """The fp8 decode batch's next decode step: one new position per request."""
+    pre = c5_lengths(seed, batch)
+    return alloc_batch("alloc_decode_B256", seed, pre, pre + 1, 64)

@@ -237,3 +237,55 @@ def test_evict_argument_errors(swa):
     assert ev(ix=short_map) == E.SWA_E_ARG              # a mapping needs its sentinel entry
     long_rows = swa.IndexStruct(FAKE, 3, 65535 * 2048 + 1, FAKE, FAKE, None, 50, 2, 16)
     assert ev(ix=long_rows, ws_bytes=1 << 40) == E.SWA_E_SHAPE
+
+
+def test_alloc_pages_needed_on_host(swa):
+    lib = swa.lib
+    pre = np.array([6, 0, 8, 3], np.int32)
+    seq = np.array([15, 5, 9, 4], np.int32)
+    # ceil(15/4)-ceil(6/4) + ceil(5/4) + ceil(9/4)-ceil(8/4) + ceil(4/4)-ceil(3/4) = 2 + 2 + 1 + 0
+    assert lib.swa_alloc_pages_needed(pre.ctypes.data, seq.ctypes.data, 4, 4) == 5
+    dec = np.array([1, 4, 5, 9, 2], np.int32)   # decode: a page opens where seq - 1 is a multiple of 4
+    assert lib.swa_alloc_pages_needed(None, dec.ctypes.data, 5, 4) == 3
+    assert lib.swa_alloc_pages_needed(None, None, 2, 4) == -1
+    assert lib.swa_alloc_pages_needed(None, dec.ctypes.data, 5, 0) == -1
+
+
+def test_alloc_argument_errors_and_no_space(swa):
+    lib, E = swa.lib, swa
+    full = swa.FreeListStruct(FAKE, 100)
+    sl = swa.FreeListStruct(FAKE, 100)
+
+    def ext(batch=2, page=16, pre=FAKE, seq=FAKE, last=FAKE, fl=full, sw=sl, mp=FAKE, map_len=50, n=64,
+            pre_h=None, seq_h=None, out=FAKE):
+        return lib.swa_alloc_extend(batch, page, pre, seq, last, None if fl is None else ctypes.byref(fl),
+                                    None if sw is None else ctypes.byref(sw), mp, map_len, n, pre_h, seq_h, out, FAKE,
+                                    None, None)
+
+    assert ext(page=0) == E.SWA_E_ARG
+    assert ext(batch=-1) == E.SWA_E_ARG
+    assert ext(n=-1) == E.SWA_E_ARG
+    assert ext(fl=None) == E.SWA_E_ARG
+    assert ext(pre=None) == E.SWA_E_ARG
+    assert ext(last=None) == E.SWA_E_ARG
+    assert ext(out=None) == E.SWA_E_ARG
+    assert ext(mp=None) == E.SWA_E_ARG                       # two pools need the mapping
+    assert ext(map_len=1) == E.SWA_E_ARG
+    assert ext(fl=swa.FreeListStruct(None, 5)) == E.SWA_E_ARG
+    # the bound 64/16 + 2 + 1 = 7 pages is not provable against a 6-page list and no host lengths are given
+    assert ext(sw=swa.FreeListStruct(FAKE, 6)) == E.SWA_E_NOSPACE
+    # the exact count (host copies) needs 9 pages: still too many
+    pre_h = np.array([0, 20], np.int32)
+    seq_h = np.array([64, 84], np.int32)
+    assert ext(sw=swa.FreeListStruct(FAKE, 6), pre_h=pre_h.ctypes.data, seq_h=seq_h.ctypes.data) == E.SWA_E_NOSPACE
+
+    def dec(batch=2, fl=full, sw=sl, seq_h=None, out=FAKE, mp=FAKE):
+        return lib.swa_alloc_decode(batch, 16, FAKE, FAKE, ctypes.byref(fl), None if sw is None else ctypes.byref(sw),
+                                    mp, 50, seq_h, out, None, None, None)
+
+    assert dec(out=None) == E.SWA_E_ARG
+    assert dec(mp=None) == E.SWA_E_ARG
+    assert dec(fl=swa.FreeListStruct(FAKE, -1)) == E.SWA_E_ARG
+    assert dec(sw=swa.FreeListStruct(FAKE, 1)) == E.SWA_E_NOSPACE           # bound: 2 pages
+    two = np.array([17, 33], np.int32)                                      # both open a page
+    assert dec(sw=swa.FreeListStruct(FAKE, 1), seq_h=two.ctypes.data) == E.SWA_E_NOSPACE

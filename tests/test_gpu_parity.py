@@ -602,3 +602,152 @@ def test_evict_then_decode_unchanged():
     dw.map.copy_(torch.from_numpy(m).cuda())
     after = run_decode(dw, "f32").cpu().numpy()
     assert np.array_equal(before, after)
+
+
+# ---------------------------------------------------------------------------
+# paired allocation: bit-exact against the oracle
+# ---------------------------------------------------------------------------
+
+ALLOC_CASES = {
+    # name: (pre_lens, seq_lens, page)
+    "mixed_p16": ([0, 5, 16, 31, 100, 0, 700, 17], [40, 16, 17, 64, 100, 1, 3000, 4113], 16),
+    "p1": ([0, 3, 9, 50], [7, 3, 300, 51], 1),
+    "p64_chunks": ([8192, 8000, 8191, 1], [10240, 10048, 10239, 2049], 64),
+    "p3_ragged": ([2, 0, 11], [2000, 5, 12], 3),
+}
+
+
+def _alloc_gpu(ab, decode, two_pools=True, host_lens=True, with_swa_out=True, free_full=None, free_swa=None):
+    from sliding_window_attention_swa_amd import swa
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    n = ab.batch if decode else int((ab.seq_lens.astype(np.int64) - ab.pre_lens).sum())
+    out_full = torch.full((max(n, 1),), -9, dtype=torch.int64, device="cuda")[:n]
+    out_swa = torch.full((max(n, 1),), -9, dtype=torch.int64, device="cuda")[:n] if with_swa_out else None
+    new_pages = torch.full((1,), -9, dtype=torch.int64, device="cuda")
+    m = dev(ab.full_to_swa) if two_pools else None
+    ff = dev(ab.free_full if free_full is None else free_full)
+    fs = dev(ab.free_swa if free_swa is None else free_swa) if two_pools else None
+    if decode:
+        ok = swa.swa_alloc_decode(dev(ab.seq_lens), dev(ab.last_loc), ab.page_size, ff, out_full, free_swa=fs,
+                                  full_to_swa=m, out_swa=out_swa, new_pages=new_pages,
+                                  seq_lens_host=ab.seq_lens if host_lens else None)
+    else:
+        ok = swa.swa_alloc_extend(dev(ab.pre_lens), dev(ab.seq_lens), dev(ab.last_loc), ab.page_size, ff, out_full,
+                                  free_swa=fs, full_to_swa=m, out_swa=out_swa, new_pages=new_pages,
+                                  pre_lens_host=ab.pre_lens if host_lens else None,
+                                  seq_lens_host=ab.seq_lens if host_lens else None)
+    torch.cuda.synchronize()
+    return (ok, out_full.cpu().numpy(), None if out_swa is None else out_swa.cpu().numpy(),
+            None if m is None else m.cpu().numpy(), int(new_pages.item()))
+
+
+def _check_alloc(ab, decode, two_pools=True, with_swa_out=True):
+    want = O.alloc_paired(ab.pre_lens, ab.seq_lens, ab.last_loc, ab.free_full, ab.free_swa if two_pools else None,
+                          ab.full_to_swa, ab.page_size, decode=decode)
+    assert want is not None
+    ok, full, swa_out, m, pages = _alloc_gpu(ab, decode, two_pools, with_swa_out=with_swa_out)
+    assert ok
+    assert np.array_equal(full, want[0])
+    assert pages == want[3]
+    if two_pools:
+        assert np.array_equal(m, want[2])
+        if with_swa_out:
+            assert np.array_equal(swa_out, want[1])
+    return want
+
+
+@pytest.mark.parametrize("name", list(ALLOC_CASES))
+@pytest.mark.parametrize("two_pools", [True, False])
+def test_alloc_extend_bit_exact(name, two_pools):
+    pre, seq, P = ALLOC_CASES[name]
+    say(f"alloc_extend {name} two_pools={two_pools}")
+    ab = WL.alloc_batch("al" + name, 51, pre, seq, P)
+    _check_alloc(ab, decode=False, two_pools=two_pools)
+
+
+@pytest.mark.parametrize("P", [1, 16, 64])
+def test_alloc_decode_bit_exact(P):
+    say(f"alloc_decode P={P}")
+    rng = np.random.default_rng(60 + P)
+    pre = rng.integers(1, 3 * P + 40, 300)   # 300 requests: two workgroups
+    pre[:6] = [P, 2 * P, 1, P - 1 if P > 1 else 1, 5 * P, 7]
+    ab = WL.alloc_batch(f"ald{P}", 52, pre, pre + 1, P)
+    want = _check_alloc(ab, decode=True)
+    assert want[3] == int(np.sum(pre % P == 0))
+    _check_alloc(ab, decode=True, with_swa_out=False)
+
+
+def test_alloc_prefill_chunk_full_size():
+    """The benchmark's extend allocation: 256 requests of lognormal length take
+    a 2048-position chunk each (P = 64); the bound cannot prove the fit, the
+    exact count from the host lengths can."""
+    say("alloc prefill chunk, full size")
+    ab = WL.alloc_prefill_chunk()
+    _check_alloc(ab, decode=False)
+
+
+def test_alloc_decode_step_full_size():
+    say("alloc decode step, full size")
+    _check_alloc(WL.alloc_decode_step(), decode=True)
+
+
+def test_alloc_no_space_changes_nothing():
+    say("alloc no space")
+    ab = WL.alloc_batch("alns", 53, [0, 20, 64], [100, 84, 130], 16)
+    need = O.pages_needed(ab.pre_lens, ab.seq_lens, 16)
+    # one page short on the SWA list: not allocated, outputs and mapping untouched
+    ok, full, swa_out, m, pages = _alloc_gpu(ab, False, free_swa=ab.free_swa[:need - 1])
+    assert not ok and np.all(full == -9) and np.all(swa_out == -9) and pages == -9
+    assert np.array_equal(m, ab.full_to_swa)
+    # exactly enough (16 pages), proven only by the exact count: the bound is 230 // 16 + 3 + 1 = 18
+    want = O.alloc_paired(ab.pre_lens, ab.seq_lens, ab.last_loc, ab.free_full[:need], ab.free_swa[:need],
+                          ab.full_to_swa, 16)
+    ok, full, swa_out, m, pages = _alloc_gpu(ab, False, free_full=ab.free_full[:need], free_swa=ab.free_swa[:need])
+    assert ok and np.array_equal(full, want[0]) and np.array_equal(swa_out, want[1]) and np.array_equal(m, want[2])
+    # without host lengths the same call cannot be proven and is refused
+    ok, *_ = _alloc_gpu(ab, False, host_lens=False, free_full=ab.free_full[:need], free_swa=ab.free_swa[:need])
+    assert not ok
+
+
+def test_alloc_empty_batch():
+    from sliding_window_attention_swa_amd import swa
+    say("alloc empty batch")
+    e32 = torch.zeros(0, dtype=torch.int32, device="cuda")
+    e64 = torch.zeros(0, dtype=torch.int64, device="cuda")
+    pages = torch.full((1,), -9, dtype=torch.int64, device="cuda")
+    free = torch.arange(1, 5, dtype=torch.int64, device="cuda")
+    assert swa.swa_alloc_extend(e32, e32, e64, 16, free, e64, new_pages=pages)
+    torch.cuda.synchronize()
+    assert int(pages.item()) == 0
+
+
+def test_alloc_then_translate_and_window():
+    """The allocation's mapping is the one the path reads: translate_loc of the
+    new full slots gives the new SWA slots, and after writing the new positions
+    into req_to_token the window tables of the grown requests hold them."""
+    from sliding_window_attention_swa_amd import swa
+    say("alloc then translate")
+    ab = WL.alloc_batch("alrt", 54, [0, 5, 300, 1000], [200, 6, 301, 1100], 16)
+    ok, full, swa_out, m, _ = _alloc_gpu(ab, False)
+    assert ok
+    loc = torch.empty(full.size, dtype=torch.int64, device="cuda")
+    swa.swa_translate_loc(torch.from_numpy(full).cuda(), torch.from_numpy(m).cuda(), loc)
+    torch.cuda.synchronize()
+    assert np.array_equal(loc.cpu().numpy(), swa_out)
+    r2t = ab.req_to_token.copy()
+    at = 0
+    for b in range(ab.batch):
+        n = int(ab.seq_lens[b] - ab.pre_lens[b])
+        r2t[ab.req_pool_idx[b], ab.pre_lens[b]:ab.seq_lens[b]] = full[at:at + n]
+        at += n
+    want = O.window_table(r2t, ab.req_pool_idx, ab.seq_lens, m, 128)
+    ix = swa.IndexTables(torch.from_numpy(r2t).cuda(), torch.from_numpy(ab.req_pool_idx).cuda(),
+                         torch.from_numpy(ab.seq_lens).cuda(), torch.from_numpy(m).cuda(), 16)
+    table = torch.empty(ab.batch * 129, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(ab.batch + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(ix, 128, table, indptr)
+    torch.cuda.synchronize()
+    got_ptr = indptr.cpu().numpy()
+    assert np.array_equal(got_ptr, want[1])
+    assert np.array_equal(table.cpu().numpy()[:got_ptr[-1]], want[0])
+    assert np.all(want[0] > 0)   # every slot of the grown windows is live
