@@ -14,6 +14,11 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   validate            pinned: hand-counted violations of a hand-built batch
   evict               pinned: hand-worked ranges (both modes, interval, protected
                       prefix), idempotence, and the next window has no tombstone
+  unified_*,          pinned: the envelope formula equals view base + kernel id
+  envelope_offset     row for row, a byte-exact cross-check of the strided
+                      views against rows placed by the envelope formula, the
+                      tail pad bound, tombstone clamping, a planted
+                      multiplier-1 mistake, and layout-invariant attention
   alloc_extend,       pinned: a hand-worked batch (all three parts, no prefix,
   alloc_decode,       a one-token chunk), a token-by-token allocator written
   alloc_paired,       independently, page size 1 = slicing the free list,
@@ -46,6 +51,12 @@ from .swa_oracle import (  # noqa: F401
     pool_config,
     scored_pairs,
     translate_loc,
+    unified_geometry,
+    unified_kernel_ids,
+    unified_mapping,
+    unified_view_base,
+    unified_views,
+    envelope_offset,
     validate,
     window_range,
     window_table,

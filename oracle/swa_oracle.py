@@ -445,6 +445,83 @@ def alloc_paired(pre_lens, seq_lens, last_loc, full_free, swa_free, full_to_swa,
 
 
 # ---------------------------------------------------------------------------
+# Unified pool.  [PR] (prhub.com.cn digest of sglang pull request 34602),
+# 功能与动机 and 实现拆解: one raw byte buffer stores every layer's K/V in
+# page-major envelopes [L0_K*ps | L0_V*ps | L1_K*ps | ...], i.e. 2L equally
+# wide row blocks per page; layer l's K is block 2l and its V block 2l + 1.
+# Per-layer dense views start at their block and address rows by the
+# kernel-facing id kernel_id(t) = v2p[t // ps] * (ps * 2L) + t % ps, a
+# tombstoned page (-1) clamped to 0, the page-0 sink; the last view reaches
+# (2L - 1) * ps rows past the last envelope, so one envelope of tail padding
+# follows the buffer; kernel-facing rows must stay below 2^31.
+# ---------------------------------------------------------------------------
+
+
+def unified_geometry(layer_num, kv_heads, head_dim, itemsize, page_size, num_pages):
+    """Sizes of one sub-pool: row bytes, row blocks per page, envelope bytes,
+    kernel-facing rows, envelope bytes in all, and the tail pad."""
+    row_bytes = kv_heads * head_dim * itemsize
+    blocks = 2 * layer_num
+    page_bytes = page_size * blocks * row_bytes
+    return dict(row_bytes=row_bytes, blocks=blocks, page_bytes=page_bytes, n_rows=num_pages * blocks * page_size,
+                total_bytes=num_pages * page_bytes, tail_pad=page_bytes)
+
+
+def envelope_offset(anchor, phys_page, layer, kv, offset, layer_num, row_bytes, page_size):
+    """Byte offset of one row in the page-major envelope: page phys_page, block
+    2 * layer + kv (kv 0 = K, 1 = V), in-page offset `offset`."""
+    return anchor + ((phys_page * 2 * layer_num + 2 * layer + kv) * page_size + offset) * row_bytes
+
+
+def unified_view_base(anchor, layer, kv, row_bytes, page_size):
+    """Start byte of layer `layer`'s K (kv 0) or V (kv 1) dense view: its block
+    in page 0's envelope."""
+    return anchor + (2 * layer + kv) * page_size * row_bytes
+
+
+def unified_kernel_ids(virt, v2p, page_size, multiplier):
+    """translate_kv_loc_for_kernel: kernel_id = v2p[t // ps] * (ps * multiplier)
+    + t % ps, then clamped at 0.  Virtual ids must be >= 0 and inside the page
+    table."""
+    virt = np.asarray(virt, dtype=np.int64)
+    v2p = np.asarray(v2p, dtype=np.int64)
+    pages = virt // page_size
+    if virt.size and (virt.min() < 0 or pages.max() >= v2p.size):
+        raise OracleError("virtual id outside the page table")
+    ids = v2p[pages] * (page_size * multiplier) + virt % page_size
+    return np.maximum(ids, 0)
+
+
+def unified_mapping(v2p, page_size, multiplier):
+    """The per-virtual-token kernel ids as a mapping table (tombstones 0, a
+    trailing -1), so that window attention over a unified view is the same
+    computation as over a two-pool SWA layer."""
+    n_virt = len(v2p) * page_size
+    m = unified_kernel_ids(np.arange(n_virt), v2p, page_size, multiplier)
+    return np.concatenate([m, [-1]]).astype(np.int64)
+
+
+def unified_views(raw, anchor, layer_num, kv_heads, head_dim, store_dtype, page_size, num_pages):
+    """The per-layer dense views, built as numpy strided views over the raw
+    byte buffer (the buffer must hold the tail pad).  store_dtype: numpy dtype
+    of the stored elements (np.uint16 for bf16 bits, np.uint8 for e4m3,
+    np.float32).  Returns ([K_0, ...], [V_0, ...]), each (n_rows, H, D)."""
+    itemsize = np.dtype(store_dtype).itemsize
+    g = unified_geometry(layer_num, kv_heads, head_dim, itemsize, page_size, num_pages)
+    ks, vs = [], []
+    for layer in range(layer_num):
+        for kv, out in ((0, ks), (1, vs)):
+            base = unified_view_base(anchor, layer, kv, g["row_bytes"], page_size)
+            end = base + g["n_rows"] * g["row_bytes"]
+            if end > raw.size:
+                raise OracleError(f"view of layer {layer} ends at byte {end}; the buffer holds {raw.size}")
+            out.append(np.lib.stride_tricks.as_strided(
+                raw[base:].view(store_dtype), shape=(g["n_rows"], kv_heads, head_dim),
+                strides=(g["row_bytes"], head_dim * itemsize, itemsize), writeable=False))
+    return ks, vs
+
+
+# ---------------------------------------------------------------------------
 # Index-data contracts, counted rather than raised.  [SWA] 双池与映射表 and
 # 运行时: a live window never holds a tombstone (eviction frees only positions
 # that left the window) and the mapping ends in the -1 sentinel that a -1 loc

@@ -760,3 +760,123 @@ def test_alloc_pins_catch_floor_for_ceil(monkeypatch):
     h = HAND_ALLOC
     got = O.alloc_extend(h["pre"], h["seq"], h["last"], h["free"], h["P"])
     assert got is None or got[0].tolist() != h["out"]
+
+
+# ---------------------------------------------------------------------------
+# unified pool ([PR] 实现拆解: page-major envelope, dense per-layer views,
+# kernel-facing ids)
+# ---------------------------------------------------------------------------
+
+def _envelope_raw(rng, layer_num, H, D, P, num_pages, anchor=0, pad=True):
+    """A raw byte buffer whose every envelope row holds its own random bytes,
+    placed row by row with the envelope formula; returns (raw, rows) with
+    rows[(page, layer, kv, off)] the bytes placed there."""
+    g = O.unified_geometry(layer_num, H, D, 2, P, num_pages)
+    raw = np.zeros(anchor + g["total_bytes"] + (g["tail_pad"] if pad else 0), dtype=np.uint8)
+    rows = {}
+    for page in range(num_pages):
+        for layer in range(layer_num):
+            for kv in (0, 1):
+                for off in range(P):
+                    at = O.envelope_offset(anchor, page, layer, kv, off, layer_num, g["row_bytes"], P)
+                    row = rng.integers(0, 256, g["row_bytes"], dtype=np.uint8)
+                    raw[at:at + g["row_bytes"]] = row
+                    rows[(page, layer, kv, off)] = row
+    return raw, rows, g
+
+
+def test_unified_view_addressing_equals_envelope():
+    L, H, D, P, pages, anchor = 3, 2, 8, 4, 5, 96
+    row_bytes = H * D * 2
+    v2p = np.array([0, 3, 1, 4, 2])            # virtual page -> physical page
+    for t in range(len(v2p) * P):
+        kid = int(O.unified_kernel_ids([t], v2p, P, 2 * L)[0])
+        for layer in range(L):
+            for kv in (0, 1):
+                via_view = O.unified_view_base(anchor, layer, kv, row_bytes, P) + kid * row_bytes
+                assert via_view == O.envelope_offset(anchor, v2p[t // P], layer, kv, t % P, L, row_bytes, P)
+
+
+def test_unified_strided_views_match_placed_rows_byte_for_byte():
+    rng = np.random.default_rng(400)
+    L, H, D, P, pages, anchor = 3, 2, 8, 4, 6, 64
+    raw, rows, g = _envelope_raw(rng, L, H, D, P, pages, anchor)
+    ks, vs = O.unified_views(raw, anchor, L, H, D, np.uint16, P, pages)
+    v2p = rng.permutation(pages)
+    for t in range(pages * P):
+        kid = int(O.unified_kernel_ids([t], v2p, P, 2 * L)[0])
+        for layer in range(L):
+            for kv, views in ((0, ks), (1, vs)):
+                got = np.ascontiguousarray(views[layer][kid]).view(np.uint8).ravel()
+                assert np.array_equal(got, rows[(int(v2p[t // P]), layer, kv, t % P)])
+
+
+def test_unified_tail_pad_is_one_envelope_and_needed():
+    rng = np.random.default_rng(401)
+    L, H, D, P, pages = 2, 1, 4, 4, 3
+    raw, _, g = _envelope_raw(rng, L, H, D, P, pages, pad=False)
+    with pytest.raises(O.OracleError):
+        O.unified_views(raw, 0, L, H, D, np.uint16, P, pages)     # the last views run past the envelopes
+    last_end = O.unified_view_base(0, L - 1, 1, g["row_bytes"], P) + g["n_rows"] * g["row_bytes"]
+    assert last_end == g["total_bytes"] + (2 * L - 1) * P * g["row_bytes"] <= g["total_bytes"] + g["tail_pad"]
+    raw2, _, _ = _envelope_raw(rng, L, H, D, P, pages, pad=True)
+    O.unified_views(raw2, 0, L, H, D, np.uint16, P, pages)
+
+
+def test_unified_tombstone_clamps_to_the_sink():
+    v2p = np.array([2, -1, 0, 1])
+    ids = O.unified_kernel_ids(np.arange(16), v2p, 4, 6)
+    assert ids[4:8].tolist() == [0, 0, 0, 0]                    # page 1 tombstoned
+    assert ids[:4].tolist() == [48, 49, 50, 51]                   # 2 * (4 * 6) + offset
+    m = O.unified_mapping(v2p, 4, 6)
+    assert m.size == 17 and m[-1] == -1 and np.array_equal(m[:-1], ids)
+
+
+def test_unified_pins_catch_multiplier_one():
+    rng = np.random.default_rng(402)
+    L, H, D, P, pages = 2, 1, 4, 4, 4
+    raw, rows, _ = _envelope_raw(rng, L, H, D, P, pages)
+    ks, _ = O.unified_views(raw, 0, L, H, D, np.uint16, P, pages)
+    v2p = np.arange(pages)
+    wrong = 0
+    for t in range(pages * P):
+        kid = int(O.unified_kernel_ids([t], v2p, P, 1)[0])     # physical ids written into dense rows
+        got = np.ascontiguousarray(ks[1][kid]).view(np.uint8).ravel()
+        wrong += not np.array_equal(got, rows[(t // P, 1, 0, t % P)])
+    assert wrong > 0
+
+
+def test_unified_attention_equals_two_pool_attention():
+    """The same logical K/V laid out in a two-pool SWA layer and in a unified
+    envelope give exactly the same window attention."""
+    rng = np.random.default_rng(403)
+    L, H, D, P, W = 2, 2, 8, 4, 5
+    lens = np.array([9, 14, 3])
+    n_vpages = 1 + sum(-(-int(t) // P) for t in lens)
+    vpages = 1 + rng.permutation(n_vpages - 1)               # virtual pages of the requests, page 0 padding
+    r2t = np.zeros((4, 16), np.int32)
+    at = 0
+    for b, t in enumerate(lens):
+        npg = -(-int(t) // P)
+        for j in range(int(t)):
+            r2t[b + 1, j] = vpages[at + j // P] * P + j % P
+        at += npg
+    v2p = np.concatenate([[0], 1 + rng.permutation(n_vpages - 1)])   # virtual -> physical page
+    raw, _, g = _envelope_raw(rng, L, H, D, P, n_vpages)
+    # keep the stored bits finite bf16 values: clear the exponent's top bit of every element
+    raw_bits = raw.view(np.uint16)
+    raw_bits &= np.uint16(0xBFFF)
+    ks, vs = O.unified_views(raw, 0, L, H, D, np.uint16, P, n_vpages)
+    m_unified = O.unified_mapping(v2p, P, 2 * L)
+    # two-pool form: an SWA pool whose slot s = virtual id holds the same rows
+    q = codecs.f64_to_bf16_bits(rng.standard_normal((3, 4, D)))
+    sinks = rng.standard_normal(4)
+    n_virt = n_vpages * P
+    identity = np.concatenate([np.arange(n_virt), [-1]]).astype(np.int64)
+    for layer in range(L):
+        kid = m_unified[:-1]
+        pool_k = np.asarray(ks[layer])[kid]
+        pool_v = np.asarray(vs[layer])[kid]
+        a = O.decode(q, "bf16", ks[layer], vs[layer], "bf16", r2t, np.arange(1, 4), lens, m_unified, W, sinks)
+        b = O.decode(q, "bf16", pool_k, pool_v, "bf16", r2t, np.arange(1, 4), lens, identity, W, sinks)
+        assert np.array_equal(a, b)
