@@ -1,12 +1,13 @@
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|evict|alloc]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|evict|alloc|unified]
 
 Other workloads (one JSON line each, same fields): c1 single f32 decode; c3
 chunked-prefill extend (store + extend over 4 layers); c4 the 48-layer mixed
 decode step (39 SWA + 9 full layers); c5 fp8-KV decode with store; evict the
 SWA eviction of the c5 batch right after its prefill; alloc the paired
-allocation of a prefill chunk (and of a decode step) for the c5 batch.
+allocation of a prefill chunk (and of a decode step) for the c5 batch;
+unified the c2 decode step over one unified sub-pool of 32 layers.
 
 Default workload (c2): batched SWA decode, B = 64 requests with context lengths
 uniform in [1K, 8K], W = 128, 64 q / 8 kv heads, head_dim 128, bf16, page 16,
@@ -527,6 +528,125 @@ def run_mixed_workload(args, torch, swa, W):
 
 
 # ---------------------------------------------------------------------------
+# unified: the c2 decode batch over one unified sub-pool of 32 layers
+# ---------------------------------------------------------------------------
+
+
+class UnifiedBench:
+    """The c2 decode step with its 32 SWA layers in one raw buffer of page-major
+    envelopes, read through the library's dense per-layer views."""
+
+    def __init__(self, torch, swa, ub, seed=9):
+        self.torch, self.swa, self.ub = torch, swa, ub
+        B, Hq, Hkv, D, L, P = ub.batch, ub.q_heads, ub.kv_heads, ub.head_dim, ub.layers, ub.page_size
+        self.mult = 2 * L
+        self.raw_bytes = swa.swa_unified_pool_bytes(L, Hkv, D, torch.bfloat16, P, ub.n_phys)
+        self.raw = torch.empty(self.raw_bytes, dtype=torch.uint8, device="cuda")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        flat = self.raw.view(torch.bfloat16)
+        chunk = 1 << 26
+        for at in range(0, flat.numel(), chunk):
+            n = min(chunk, flat.numel() - at)
+            flat[at:at + n] = torch.randn(n, generator=g, device="cuda").to(torch.bfloat16)
+        self.views = swa.swa_unified_layer_views(self.raw, 0, L, Hkv, D, torch.bfloat16, P, ub.n_phys)
+        self.v2p = torch.from_numpy(ub.v2p).cuda()
+        self.index = swa.IndexTables(torch.from_numpy(ub.req_to_token).cuda(), torch.from_numpy(ub.req_pool_idx).cuda(),
+                                     torch.from_numpy(ub.seq_lens).cuda(), None, P)
+        virt = ub.req_to_token[ub.req_pool_idx, ub.seq_lens - 1].astype(np.int64)   # each request's current token
+        self.new_virt = torch.from_numpy(virt).cuda()
+        self.new_ids = torch.empty_like(self.new_virt)
+        self.table = torch.empty(B * (ub.window + 1), dtype=torch.int32, device="cuda")
+        self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+        self.sinks = torch.from_numpy(ub.sinks).cuda()
+        self.layers = [dict(q=randn_store(torch, (B, Hq, D), g, "bf16"),
+                            new_k=randn_store(torch, (B, Hkv, D), g, "bf16"),
+                            new_v=randn_store(torch, (B, Hkv, D), g, "bf16"),
+                            out=torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")) for _ in range(L)]
+        # algorithmic bytes, as for the two-pool decode step (window only), the
+        # kernel-id translation reading one page-table entry per position
+        n_keys = np.minimum(ub.seq_lens.astype(np.int64), ub.window + 1)
+        self.decode_bytes = int(n_keys.sum() * Hkv * D * 2 * 2 + B * Hq * D * 4 + n_keys.sum() * 4 + (B + 1) * 4)
+        self.store_bytes = B * Hkv * D * 2 * 2 + B * 8
+        self.translate_bytes = B * 8 * 3 + int(n_keys.sum()) * (4 + 8 + 4) + B * 12
+        self.step_bytes = self.translate_bytes + L * (self.store_bytes + self.decode_bytes)
+
+    def step(self):
+        swa, ub = self.swa, self.ub
+        swa.swa_translate_kernel_ids(self.new_virt, self.v2p, ub.page_size, self.mult, self.new_ids)
+        swa.swa_translate_window_unified(self.index, self.v2p, self.mult, ub.window, self.table, self.indptr)
+        self.dominant()
+
+    def dominant(self):
+        swa, ub = self.swa, self.ub
+        for view, ly in zip(self.views, self.layers):
+            swa.swa_decode_store(ly["q"], view, self.index, ub.window, ly["out"], self.new_ids, ly["new_k"],
+                                 ly["new_v"], sinks=self.sinks, slot_table=self.table, table_indptr=self.indptr,
+                                 use_map=False)
+
+
+def cpu_baseline_unified(bench, budget_s=12.0):
+    """The oracle over the first layer's view (read back to the host once), on
+    as many requests as fit the budget."""
+    from threadpoolctl import threadpool_limits
+    from oracle import swa_oracle as O
+    ub = bench.ub
+    raw = bench.raw.cpu().numpy()
+    ks, vs = O.unified_views(raw, 0, ub.layers, ub.kv_heads, ub.head_dim, np.uint16, ub.page_size, ub.n_phys)
+    m = O.unified_mapping(ub.v2p, ub.page_size, bench.mult)
+    q = bench.layers[0]["q"].view(bench.torch.int16).cpu().numpy().view(np.uint16)
+    done, b = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while time.perf_counter() - t0 < budget_s:
+            O.decode(q, "bf16", ks[0], vs[0], "bf16", ub.req_to_token, ub.req_pool_idx, ub.seq_lens, m, ub.window,
+                     ub.sinks, only=[(b, h) for h in range(ub.q_heads)])
+            b = (b + 1) % ub.batch
+            done += 1
+    return time.perf_counter() - t0, done
+
+
+def run_unified_workload(args, torch, swa, W):
+    ub = W.unified_c2_decode()
+    log(f"[bench] unified: building one sub-pool of {ub.layers} layers")
+    bench = UnifiedBench(torch, swa, ub)
+    g_step = graph_of(torch, bench.step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    ms = time_replays(torch, g_step, args.steps)
+    g_dec = graph_of(torch, bench.dominant)
+    dec_reps = max(10, args.steps // 2)
+    ms_dec = time_replays(torch, g_dec, dec_reps) / ub.layers
+    pct = replay_percentiles(torch, g_dec, dec_reps, ub.layers)
+    value = bench.step_bytes / (ms * 1e-3) / 1e9
+    dom_bytes = bench.decode_bytes + bench.store_bytes
+    achieved = dom_bytes / (ms_dec * 1e-3) / 1e9
+    log(f"[bench] unified step {ms:.4f} ms; swa_decode_store {ms_dec * 1e3:.2f} us per layer")
+    traffic = traffic_from_profile("swa_decode_unified_c2", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1)
+    res = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic",
+        config={"workload": "batched SWA decode B=64, T~U[1K,8K], W=128, 64q/8kv, D=128, bf16, page 16, over one "
+                            "unified sub-pool of 32 layers (page-major envelopes, dense per-layer views)",
+                "global_batch": int(ub.batch), "layers_per_step": ub.layers, "window": ub.window,
+                "pool_bytes": int(bench.raw_bytes), "parallelism": "none (1 GPU)"},
+        tokens_per_s=round(ub.batch / (ms * 1e-3), 1),
+        roofline=dict(kernel="swa_decode_store (store fused) over unified views", bound="hbm",
+                      achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=traffic, bytes_per_launch=dom_bytes, us_per_launch=round(ms_dec * 1e3, 3), **pct),
+    )
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        secs, nreq = cpu_baseline_unified(bench)
+        res["cpu_baseline"] = dict(value=round(nreq * bench.decode_bytes / ub.batch / secs / 1e9, 6), unit="GB/s",
+                                   cores=1, kind="oracle",
+                                   sample=f"one layer's decode of {nreq} requests x {ub.q_heads} heads over the "
+                                          f"unified view ({secs:.1f} s)")
+    return res
+
+
+# ---------------------------------------------------------------------------
 # evict: SWA eviction of a batch right after its prefill
 # ---------------------------------------------------------------------------
 
@@ -758,7 +878,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "evict", "alloc"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "evict", "alloc", "unified"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-noop", action="store_true",
                     help="evict: skip timing the calls that release nothing (for profiling runs)")
@@ -787,6 +907,8 @@ def main():
         res = run_evict_workload(args, torch, swa, W)
     elif args.workload == "alloc":
         res = run_alloc_workload(args, torch, swa, W)
+    elif args.workload == "unified":
+        res = run_unified_workload(args, torch, swa, W)
     else:
         res = run_decode_workload(args, torch, swa, W)
     print(json.dumps(res), flush=True)

@@ -265,6 +265,52 @@ swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Unified pool ([PR] 功能与动机 and 实现拆解, steps 1-3: build_mha_views,
+ * view_tail_pad_bytes, _assert_kernel_id_bound, translate_kv_loc_for_kernel).
+ * One raw byte buffer holds a sub-pool of L layers as page-major envelopes
+ * [L0_K*P | L0_V*P | L1_K*P | L1_V*P | ...]: page p is 2L row blocks of P rows,
+ * a row being kv_heads * head_dim elements.  Layer l's K view starts at block
+ * 2l of page 0 and its V view at block 2l + 1; both are ordinary dense
+ * (n_rows, kv_heads, head_dim) layers with n_rows = num_pages * 2L * P, so
+ * row kernel_id(t) = v2p[t / P] * (P * 2L) + t % P of the view is the row of
+ * virtual token t, and every kernel of this library runs on them unchanged.
+ * The last view reaches (2L - 1) * P rows past the last envelope: the buffer
+ * must hold one envelope of tail pad after the envelopes. */
+
+/* [host] Bytes a sub-pool needs from its anchor on: num_pages envelopes plus
+ * the tail pad.  -1 on bad arguments. */
+int64_t swa_unified_pool_bytes(int32_t layer_num, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                               int32_t page_size, int64_t num_pages);
+
+/* [host] Fill views[0 .. layer_num) (host array) with the per-layer K/V views
+ * of the sub-pool at raw + anchor_bytes (device buffer of raw_bytes bytes).
+ * No device work.  Errors: SWA_E_ARG (null / misaligned: raw and anchor must
+ * be 16-byte aligned), SWA_E_DTYPE, SWA_E_SHAPE (rows not a multiple of 16
+ * bytes, the views would run past the buffer (tail pad missing), or
+ * n_rows >= 2^31, the bound of int32 index buffers). */
+swa_status_t swa_unified_layer_views(void *raw, int64_t raw_bytes, int64_t anchor_bytes, int32_t layer_num,
+                                     int32_t kv_heads, int32_t head_dim, int32_t dtype, int32_t page_size,
+                                     int64_t num_pages, float k_scale, float v_scale, swa_kv_layer_t *views);
+
+/* Virtual token ids -> kernel-facing ids: out[i] = v2p[t / P] * (P *
+ * multiplier) + t % P for t = virt[i], with multiplier = 2L, the row blocks
+ * per page; a tombstoned page (v2p = -1) and an id outside the page table
+ * (t < 0 or t / P >= n_pages) give 0, the sink row.  virt / out: device
+ * int64 [n] (may be the same buffer); v2p: device int64 [n_pages]. */
+swa_status_t swa_translate_kernel_ids(const int64_t *virt, int64_t n, const int64_t *v2p, int64_t n_pages,
+                                      int32_t page_size, int32_t multiplier, int64_t *out, hipStream_t stream);
+
+/* swa_translate_window on a unified pool: req_to_token holds virtual ids and
+ * each window position's slot is its kernel-facing id (as above), written to
+ * the int32 slot table; idx->full_to_swa is not used.  Errors as
+ * swa_translate_window, plus SWA_E_SHAPE when a kernel-facing id could reach
+ * 2^31. */
+swa_status_t swa_translate_window_unified(const swa_index_t *idx, const int64_t *v2p, int64_t n_pages,
+                                          int32_t multiplier, int32_t window, const int32_t *prefix_lens,
+                                          int32_t *slot_table, int32_t *table_indptr, int64_t table_capacity,
+                                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Paired allocation ([POOLS] 三重映射, alloc_extend, alloc_decode, 扩容与不足
  * and SWATokenToKVPoolAllocator; [SWA] 双池与映射表: alloc, alloc_extend and
  * alloc_decode take the same number of slots from both allocators, then write

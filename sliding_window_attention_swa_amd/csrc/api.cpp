@@ -254,6 +254,88 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
   return from_hip(swa::launch_extend(a, stream));
 }
 
+namespace {
+
+int64_t dtype_bytes(int32_t dtype) {
+  return dtype == SWA_F32 ? 4 : dtype == SWA_BF16 ? 2 : dtype == SWA_FP8_E4M3 ? 1 : 0;
+}
+
+// Geometry of one unified sub-pool, or false on bad or oversized arguments:
+// bytes of one row, of one page envelope (2L row blocks), and kernel-facing rows.
+bool unified_geometry(int32_t layer_num, int32_t kv_heads, int32_t head_dim, int32_t dtype, int32_t page_size,
+                      int64_t num_pages, int64_t &row_bytes, int64_t &page_bytes, int64_t &n_rows) {
+  const int64_t item = dtype_bytes(dtype);
+  if (!item || layer_num < 1 || kv_heads < 1 || head_dim < 1 || page_size < 1 || num_pages < 1) return false;
+  if (layer_num > 4096 || kv_heads > 4096 || head_dim > 4096 || page_size > (1 << 20) || num_pages > (1ll << 40))
+    return false;
+  row_bytes = static_cast<int64_t>(kv_heads) * head_dim * item;
+  const int64_t blocks = 2ll * layer_num;
+  page_bytes = page_size * blocks * row_bytes;
+  if (num_pages > INT64_MAX / 2 / page_bytes) return false;
+  n_rows = num_pages * blocks * page_size;
+  return true;
+}
+
+}  // namespace
+
+int64_t swa_unified_pool_bytes(int32_t layer_num, int32_t kv_heads, int32_t head_dim, int32_t dtype,
+                               int32_t page_size, int64_t num_pages) {
+  int64_t row_bytes, page_bytes, n_rows;
+  if (!unified_geometry(layer_num, kv_heads, head_dim, dtype, page_size, num_pages, row_bytes, page_bytes, n_rows))
+    return -1;
+  return num_pages * page_bytes + page_bytes;  // the envelopes, then one envelope of tail pad
+}
+
+swa_status_t swa_unified_layer_views(void *raw, int64_t raw_bytes, int64_t anchor_bytes, int32_t layer_num,
+                                     int32_t kv_heads, int32_t head_dim, int32_t dtype, int32_t page_size,
+                                     int64_t num_pages, float k_scale, float v_scale, swa_kv_layer_t *views) {
+  if (!raw || !views || raw_bytes < 0 || anchor_bytes < 0 || (anchor_bytes & 15)) return SWA_E_ARG;
+  if (!aligned16(raw)) return SWA_E_ARG;
+  if (dtype_bytes(dtype) == 0) return SWA_E_DTYPE;
+  int64_t row_bytes, page_bytes, n_rows;
+  if (!unified_geometry(layer_num, kv_heads, head_dim, dtype, page_size, num_pages, row_bytes, page_bytes, n_rows))
+    return SWA_E_ARG;
+  if (row_bytes & 15) return SWA_E_SHAPE;     // rows must keep 16-byte alignment
+  if (n_rows > kMaxRows) return SWA_E_SHAPE;  // kernel-facing ids travel through int32 tables
+  // the last view (layer L-1's V) ends (2L - 1) * P rows past the last envelope
+  if (anchor_bytes > raw_bytes || raw_bytes - anchor_bytes < num_pages * page_bytes + page_bytes) return SWA_E_SHAPE;
+  char *base = static_cast<char *>(raw) + anchor_bytes;
+  for (int32_t l = 0; l < layer_num; ++l) {
+    swa_kv_layer_t &v = views[l];
+    v.k = base + (2ll * l) * page_size * row_bytes;
+    v.v = base + (2ll * l + 1) * page_size * row_bytes;
+    v.rows = n_rows;
+    v.kv_heads = kv_heads;
+    v.head_dim = head_dim;
+    v.dtype = dtype;
+    v.k_scale = k_scale;
+    v.v_scale = v_scale;
+  }
+  return SWA_OK;
+}
+
+swa_status_t swa_translate_kernel_ids(const int64_t *virt, int64_t n, const int64_t *v2p, int64_t n_pages,
+                                      int32_t page_size, int32_t multiplier, int64_t *out, hipStream_t stream) {
+  if (n < 0 || n_pages < 1 || !v2p || page_size < 1 || multiplier < 1) return SWA_E_ARG;
+  if (n > 0 && (!virt || !out)) return SWA_E_ARG;
+  return from_hip(swa::launch_translate_ids(virt, n, v2p, n_pages, page_size, multiplier, out, stream));
+}
+
+swa_status_t swa_translate_window_unified(const swa_index_t *idx, const int64_t *v2p, int64_t n_pages,
+                                          int32_t multiplier, int32_t window, const int32_t *prefix_lens,
+                                          int32_t *slot_table, int32_t *table_indptr, int64_t table_capacity,
+                                          hipStream_t stream) {
+  swa_status_t st = check_index(idx, true);
+  if (st != SWA_OK) return st;
+  if (!v2p || n_pages < 1 || multiplier < 1 || idx->page_size < 1) return SWA_E_ARG;
+  if (window < -1 || table_capacity < 0 || !table_indptr) return SWA_E_ARG;
+  if (table_capacity > 0 && !slot_table) return SWA_E_ARG;
+  // every kernel-facing id must fit the int32 table
+  if (n_pages > kMaxRows / idx->page_size / multiplier) return SWA_E_SHAPE;
+  return from_hip(swa::launch_translate_window_unified(*idx, v2p, n_pages, multiplier, window, prefix_lens,
+                                                       slot_table, table_indptr, table_capacity, stream));
+}
+
 int64_t swa_alloc_pages_needed(const int32_t *pre_lens, const int32_t *seq_lens, int32_t batch, int32_t page_size) {
   if (batch < 0 || page_size < 1 || (batch > 0 && !seq_lens)) return -1;
   int64_t n = 0;

@@ -143,6 +143,12 @@ hipError_t launch_evict(const swa_index_t &idx, int64_t *full_to_swa, const int3
                         int32_t interval, int64_t *freed_pages, int64_t capacity, int64_t *freed_count,
                         int32_t *workspace, hipStream_t stream);
 
+hipError_t launch_translate_window_unified(const swa_index_t &idx, const int64_t *v2p, int64_t n_pages,
+                                           int32_t multiplier, int32_t window, const int32_t *prefix_lens,
+                                           int32_t *table, int32_t *indptr, int64_t capacity, hipStream_t stream);
+hipError_t launch_translate_ids(const int64_t *virt, int64_t n, const int64_t *v2p, int64_t n_pages,
+                                int32_t page_size, int32_t multiplier, int64_t *out, hipStream_t stream);
+
 struct AllocArgs {
   int32_t batch;
   int32_t page_size;

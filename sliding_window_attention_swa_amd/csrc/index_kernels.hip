@@ -1,5 +1,7 @@
 // Index translation kernels: flat full -> SWA loc translation and the fused
-// window gather (req_to_token -> full slot -> full_to_swa -> SWA slot).
+// window gather (req_to_token -> full slot -> full_to_swa -> SWA slot), and
+// their unified-pool forms (virtual id -> kernel-facing row through a page
+// table).
 //
 // SWA note (zdszero.github.io/swa.html), sections 双池与映射表 and Attention
 // backend: the full index is the primary address; the SWA slot of a token is
@@ -26,6 +28,41 @@ __global__ void __launch_bounds__(256) translate_loc_kernel(const int64_t *__res
   for (; i < n; i += step) out[i] = map_full(map, map_len, full_loc[i]);
 }
 
+// Unified pool (prhub.com.cn digest of sglang pull request 34602, 实现拆解:
+// translate_kv_loc_for_kernel): a virtual id t addresses row
+// v2p[t / P] * (P * multiplier) + t % P of a dense per-layer view, multiplier
+// being the row blocks per page (2 x layers); a tombstoned page (-1) lands on
+// row 0, the sink.  Ids outside the page table read row 0 as well.
+struct PageTable {
+  const int64_t *__restrict__ v2p;
+  int64_t n_pages;
+  int32_t page;
+  int64_t stride;  // page * multiplier
+  __device__ __forceinline__ int64_t operator()(int64_t virt) const {
+    if (virt < 0) return 0;
+    const int64_t pg = virt / page;
+    if (pg >= n_pages) return 0;
+    const int64_t id = v2p[pg] * stride + virt % page;
+    return id > 0 ? id : 0;
+  }
+};
+
+// The two-pool translation (or none: a full layer reads req_to_token directly).
+struct MapTable {
+  const int64_t *__restrict__ map;
+  int64_t map_len;
+  __device__ __forceinline__ int64_t operator()(int64_t full) const {
+    return map ? map_full(map, map_len, full) : full;
+  }
+};
+
+__global__ void __launch_bounds__(256) translate_ids_kernel(const int64_t *__restrict__ virt, int64_t n,
+                                                            PageTable tr, int64_t *__restrict__ out) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (; i < n; i += step) out[i] = tr(virt[i]);
+}
+
 // Number of window entries of request b: positions lo .. L-1.
 __device__ __forceinline__ int32_t window_count(const int32_t *__restrict__ seq_lens,
                                                 const int32_t *__restrict__ prefix_lens, int32_t window,
@@ -46,11 +83,11 @@ __device__ __forceinline__ int32_t window_count(const int32_t *__restrict__ seq_
 // requests before it (an exclusive prefix sum done redundantly per request,
 // which avoids a separate scan launch and any host read of device lengths),
 // then gathers and translates its window with coalesced int32 reads.
+template <typename Translate>
 __global__ void __launch_bounds__(256) translate_window_kernel(
     const int32_t *__restrict__ r2t, int64_t r2t_rows, int64_t r2t_stride, const int32_t *__restrict__ req_idx,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ prefix_lens,
-    const int64_t *__restrict__ map, int64_t map_len, int32_t batch, int32_t window, int32_t *__restrict__ table,
-    int32_t *__restrict__ indptr, int64_t capacity) {
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ prefix_lens, Translate tr, int32_t batch,
+    int32_t window, int32_t *__restrict__ table, int32_t *__restrict__ indptr, int64_t capacity) {
   __shared__ int64_t partial[256];
   const int32_t b = blockIdx.x;
   if (batch == 0) {  // empty batch: the prefix sum is the single 0
@@ -79,9 +116,7 @@ __global__ void __launch_bounds__(256) translate_window_kernel(
   for (int32_t k = threadIdx.x; k < count; k += blockDim.x) {
     const int64_t dst = base + k;
     if (dst >= capacity) break;
-    int64_t full = src[k];
-    int64_t slot = map ? map_full(map, map_len, full) : full;
-    table[dst] = static_cast<int32_t>(slot);
+    table[dst] = static_cast<int32_t>(tr(src[k]));
   }
 }
 
@@ -100,9 +135,31 @@ hipError_t launch_translate_loc(const int64_t *full_loc, int64_t n, const int64_
 hipError_t launch_translate_window(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
                                    int32_t *table, int32_t *indptr, int64_t capacity, hipStream_t stream) {
   const uint32_t grid = idx.batch > 0 ? static_cast<uint32_t>(idx.batch) : 1u;
-  hipLaunchKernelGGL(translate_window_kernel, dim3(grid), dim3(256), 0, stream,
-                     idx.req_to_token, idx.r2t_rows, idx.r2t_stride, idx.req_pool_idx, idx.seq_lens, prefix_lens,
-                     idx.full_to_swa, idx.map_len, idx.batch, window, table, indptr, capacity);
+  hipLaunchKernelGGL(translate_window_kernel<MapTable>, dim3(grid), dim3(256), 0, stream, idx.req_to_token,
+                     idx.r2t_rows, idx.r2t_stride, idx.req_pool_idx, idx.seq_lens, prefix_lens,
+                     MapTable{idx.full_to_swa, idx.map_len}, idx.batch, window, table, indptr, capacity);
+  return hipGetLastError();
+}
+
+hipError_t launch_translate_window_unified(const swa_index_t &idx, const int64_t *v2p, int64_t n_pages,
+                                           int32_t multiplier, int32_t window, const int32_t *prefix_lens,
+                                           int32_t *table, int32_t *indptr, int64_t capacity, hipStream_t stream) {
+  const uint32_t grid = idx.batch > 0 ? static_cast<uint32_t>(idx.batch) : 1u;
+  const PageTable tr{v2p, n_pages, idx.page_size, static_cast<int64_t>(idx.page_size) * multiplier};
+  hipLaunchKernelGGL(translate_window_kernel<PageTable>, dim3(grid), dim3(256), 0, stream, idx.req_to_token,
+                     idx.r2t_rows, idx.r2t_stride, idx.req_pool_idx, idx.seq_lens, prefix_lens, tr, idx.batch,
+                     window, table, indptr, capacity);
+  return hipGetLastError();
+}
+
+hipError_t launch_translate_ids(const int64_t *virt, int64_t n, const int64_t *v2p, int64_t n_pages,
+                                int32_t page_size, int32_t multiplier, int64_t *out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const PageTable tr{v2p, n_pages, page_size, static_cast<int64_t>(page_size) * multiplier};
+  hipLaunchKernelGGL(translate_ids_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, virt, n, tr,
+                     out);
   return hipGetLastError();
 }
 

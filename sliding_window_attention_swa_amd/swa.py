@@ -28,7 +28,8 @@ SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
            "swa_decode", "swa_decode_store", "swa_extend", "swa_validate_workspace_bytes", "swa_validate",
            "swa_evict_workspace_bytes", "swa_evict", "swa_alloc_pages_needed", "swa_alloc_extend",
-           "swa_alloc_decode", "swa_status_string")
+           "swa_alloc_decode", "swa_unified_pool_bytes", "swa_unified_layer_views", "swa_translate_kernel_ids",
+           "swa_translate_window_unified", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -95,6 +96,12 @@ _sig = {
                                 _p, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "swa_alloc_decode": (_i32, [_i32, _i32, _p, _p, ctypes.POINTER(FreeListStruct), ctypes.POINTER(FreeListStruct),
                                 _p, _i64, _p, _p, _p, _p, _p]),
+    "swa_unified_pool_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i64]),
+    "swa_unified_layer_views": (_i32, [_p, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32,
+                                       ctypes.POINTER(KvLayerStruct)]),
+    "swa_translate_kernel_ids": (_i32, [_p, _i64, _p, _i64, _i32, _i32, _p, _p]),
+    "swa_translate_window_unified": (_i32, [ctypes.POINTER(IndexStruct), _p, _i64, _i32, _i32, _p, _p, _p, _i64,
+                                            _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -214,9 +221,9 @@ def swa_translate_window(index: IndexTables, window: int, slot_table: torch.Tens
 def swa_kv_store(layer: KvLayer, loc: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
     if k_new.shape != v_new.shape or k_new.shape[0] != loc.numel():
         raise ValueError("k_new / v_new must be (n, kv_heads, head_dim) with n = len(loc)")
-    if k_new.numel() and tuple(k_new.shape[1:]) != tuple(layer.k.shape[1:]):
-        raise ValueError("new rows must match the pool's (kv_heads, head_dim)")
     s = layer.struct()
+    if k_new.numel() and tuple(k_new.shape[1:]) != (s.kv_heads, s.head_dim):
+        raise ValueError("new rows must match the pool's (kv_heads, head_dim)")
     _check(lib.swa_kv_store(ctypes.byref(s), _ptr(loc, torch.int64, "loc"), loc.numel(), _ptr(k_new, name="k_new"),
                             _ptr(v_new, name="v_new"), dtype_code(k_new), _stream(stream)), "swa_kv_store")
 
@@ -255,10 +262,10 @@ def swa_decode_store(q: torch.Tensor, layer: KvLayer, index: IndexTables, window
         raise ValueError("q and out must be (batch, q_heads, head_dim)")
     if k_new.shape != v_new.shape or k_new.shape[0] != loc.numel() or loc.numel() != q.shape[0]:
         raise ValueError("k_new / v_new must be (batch, kv_heads, head_dim) with one loc per request")
-    if tuple(k_new.shape[1:]) != tuple(layer.k.shape[1:]):
+    ls, ix = layer.struct(), index.struct(with_map=use_map)
+    if tuple(k_new.shape[1:]) != (ls.kv_heads, ls.head_dim):
         raise ValueError("new rows must match the pool's (kv_heads, head_dim)")
     scale = sm_scale if sm_scale is not None else q.shape[2] ** -0.5
-    ls, ix = layer.struct(), index.struct(with_map=use_map)
     _check(lib.swa_decode_store(_ptr(q, name="q"), dtype_code(q), q.shape[1], ctypes.byref(ls), ctypes.byref(ix),
                                 _ptr(slot_table, torch.int32, "slot_table"),
                                 _ptr(table_indptr, torch.int32, "table_indptr"),
@@ -395,3 +402,63 @@ def swa_alloc_decode(seq_lens: torch.Tensor, last_loc: torch.Tensor, page_size: 
         return False
     _check(st, "swa_alloc_decode")
     return True
+
+
+# ---------------------------------------------------------------------------
+# unified pool
+# ---------------------------------------------------------------------------
+
+_DTYPE_CODE = {torch.float32: SWA_F32, torch.bfloat16: SWA_BF16, torch.uint8: SWA_FP8_E4M3,
+               torch.float8_e4m3fn: SWA_FP8_E4M3}
+
+
+def swa_unified_pool_bytes(layer_num: int, kv_heads: int, head_dim: int, dtype: torch.dtype, page_size: int,
+                           num_pages: int) -> int:
+    n = lib.swa_unified_pool_bytes(layer_num, kv_heads, head_dim, _DTYPE_CODE[dtype], page_size, num_pages)
+    if n < 0:
+        raise SwaError(SWA_E_ARG, "swa_unified_pool_bytes")
+    return n
+
+
+@dataclass
+class RawKvLayer:
+    """A layer view the library computed over a raw buffer (kept alive here)."""
+    raw: torch.Tensor
+    view: KvLayerStruct
+
+    def struct(self) -> KvLayerStruct:
+        return self.view
+
+
+def swa_unified_layer_views(raw: torch.Tensor, anchor_bytes: int, layer_num: int, kv_heads: int, head_dim: int,
+                            dtype: torch.dtype, page_size: int, num_pages: int, k_scale: float = 1.0,
+                            v_scale: float = 1.0):
+    """Per-layer K/V views of a unified sub-pool in `raw` (a uint8 device tensor)."""
+    views = (KvLayerStruct * layer_num)()
+    _check(lib.swa_unified_layer_views(_ptr(raw, torch.uint8, "raw"), raw.numel(), anchor_bytes, layer_num, kv_heads,
+                                       head_dim, _DTYPE_CODE[dtype], page_size, num_pages, k_scale, v_scale, views),
+           "swa_unified_layer_views")
+    return [RawKvLayer(raw, KvLayerStruct(v.k, v.v, v.rows, v.kv_heads, v.head_dim, v.dtype, v.k_scale, v.v_scale))
+            for v in views]
+
+
+def swa_translate_kernel_ids(virt: torch.Tensor, v2p: torch.Tensor, page_size: int, multiplier: int,
+                             out: torch.Tensor, stream=None):
+    if virt.numel() != out.numel():
+        raise ValueError("virt and out must have the same length")
+    _check(lib.swa_translate_kernel_ids(_ptr(virt, torch.int64, "virt"), virt.numel(), _ptr(v2p, torch.int64, "v2p"),
+                                        v2p.numel(), page_size, multiplier, _ptr(out, torch.int64, "out"),
+                                        _stream(stream)), "swa_translate_kernel_ids")
+
+
+def swa_translate_window_unified(index: IndexTables, v2p: torch.Tensor, multiplier: int, window: int,
+                                 slot_table: torch.Tensor, table_indptr: torch.Tensor,
+                                 prefix_lens: Optional[torch.Tensor] = None, stream=None):
+    if table_indptr.numel() < index.seq_lens.numel() + 1:
+        raise ValueError("table_indptr needs batch + 1 entries")
+    ix = index.struct(with_map=False)
+    _check(lib.swa_translate_window_unified(ctypes.byref(ix), _ptr(v2p, torch.int64, "v2p"), v2p.numel(), multiplier,
+                                            window, _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                                            _ptr(slot_table, torch.int32, "slot_table"),
+                                            _ptr(table_indptr, torch.int32, "table_indptr"), slot_table.numel(),
+                                            _stream(stream)), "swa_translate_window_unified")

@@ -488,3 +488,78 @@ def alloc_decode_step(seed=SEED_BASE + 5, batch=256) -> AllocBatch:
     """The fp8 decode batch's next decode step: one new position per request."""
     pre = c5_lengths(seed, batch)
     return alloc_batch("alloc_decode_B256", seed, pre, pre + 1, 64)
+
+
+# ---------------------------------------------------------------------------
+# Unified pool: virtual ids, a page table, and per-layer rows per live token
+# (where the rows sit in the raw buffer is the layout under test, so it is
+# not decided here)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class UnifiedBatch:
+    name: str
+    batch: int
+    layers: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    window: int
+    page_size: int
+    kv_dtype: str
+    seq_lens: np.ndarray          # int32 (B,)
+    req_to_token: np.ndarray      # int32 (B + 1, stride): virtual ids
+    req_pool_idx: np.ndarray      # int32 (B,)
+    v2p: np.ndarray               # int64 (virtual pages,): physical page, -1 tombstoned, v2p[0] = 0
+    n_phys: int                   # physical pages of the sub-pool (page 0 included)
+    live_tokens: np.ndarray       # int64: virtual ids whose page is live, ascending
+    k_rows: Optional[np.ndarray]  # (layers, n_live, kv_heads, head_dim) storage bits, or None
+    v_rows: Optional[np.ndarray]
+    q: np.ndarray                 # (B, q_heads, head_dim) bf16 bits
+    sinks: Optional[np.ndarray]
+    new_k: np.ndarray             # (layers, B, kv_heads, head_dim) bf16 bits: the current token's K/V
+    new_v: np.ndarray
+
+
+def unified_batch(name, seed, seq_lens, layers, q_heads, kv_heads, window, page_size, kv_dtype="bf16", sinks=True,
+                  live_margin=128, slack_pages=2, head_dim=128, with_rows=True) -> UnifiedBatch:
+    """Decode requests over one unified SWA sub-pool of `layers` layers: virtual
+    pages laid out like the two-pool decode workloads (the full-page
+    permutation gives the virtual pages, the SWA-page permutation the physical
+    pages of live pages; pages before seq - 1 - window - live_margin are
+    tombstoned)."""
+    r_len, r_full, r_swa, r_q, r_k, r_v, r_s, r_new = _streams(seed)
+    seq = np.asarray(seq_lens, dtype=np.int64)
+    B, P = len(seq), page_size
+    n_virt = round_up(int(sum(round_up(int(t), P) for t in seq)) + slack_pages * P, P)
+    live_from = np.maximum(seq - 1 - window - live_margin, 0)
+    need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(seq, live_from)))
+    n_phys_tokens = round_up(need + slack_pages * P, P)
+    r2t, mapping, _ = _layout(seq, P, n_virt, n_phys_tokens, live_from, r_full, r_swa)
+    vp = np.arange(n_virt // P + 1)
+    v2p = np.where(mapping[vp * P] > 0, mapping[vp * P] // P, -1).astype(np.int64)
+    v2p[0] = 0
+    live = np.nonzero(np.repeat(v2p > 0, P))[0].astype(np.int64)
+    live = live[np.isin(live, r2t[1:][r2t[1:] > 0])]
+    k_rows = v_rows = None
+    if with_rows:
+        k_rows = to_store(r_k.standard_normal((layers, live.size, kv_heads, head_dim), dtype=np.float32), kv_dtype)
+        v_rows = to_store(r_v.standard_normal((layers, live.size, kv_heads, head_dim), dtype=np.float32), kv_dtype)
+    q = to_store(r_q.standard_normal((B, q_heads, head_dim), dtype=np.float32), "bf16")
+    s = r_s.standard_normal(q_heads).astype(np.float32) if sinks else None
+    new_k = to_store(r_new.standard_normal((layers, B, kv_heads, head_dim), dtype=np.float32), "bf16")
+    new_v = to_store(r_new.standard_normal((layers, B, kv_heads, head_dim), dtype=np.float32), "bf16")
+    return UnifiedBatch(name, B, layers, q_heads, kv_heads, head_dim, window, P, kv_dtype, seq.astype(np.int32), r2t,
+                        np.arange(1, B + 1, dtype=np.int32), v2p, n_phys_tokens // P + 1, live, k_rows, v_rows, q, s,
+                        new_k, new_v)
+
+
+def unified_c2_decode(seed=SEED_BASE + 2, layers=32) -> UnifiedBatch:
+    """The batched SWA decode batch (B = 64, T ~ U[1024, 8192], W = 128, 64 q /
+    8 kv heads, D = 128, bf16, P = 16, pages before the window tombstoned) over
+    one unified sub-pool holding `layers` SWA layers; rows are left to the
+    caller (the benchmark fills the buffer on the device)."""
+    lens = np.random.default_rng(np.random.SeedSequence(seed).spawn(8)[0]).integers(1024, 8193, size=64)
+    return unified_batch("unified_c2_B64_L%d" % layers, seed, lens, layers, 64, 8, 128, 16, live_margin=0,
+                         with_rows=False)
+

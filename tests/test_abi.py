@@ -289,3 +289,52 @@ def test_alloc_argument_errors_and_no_space(swa):
     assert dec(sw=swa.FreeListStruct(FAKE, 1)) == E.SWA_E_NOSPACE           # bound: 2 pages
     two = np.array([17, 33], np.int32)                                      # both open a page
     assert dec(sw=swa.FreeListStruct(FAKE, 1), seq_h=two.ctypes.data) == E.SWA_E_NOSPACE
+
+
+def test_unified_views_on_host_match_the_oracle_builder(swa):
+    """swa_unified_layer_views is host arithmetic only: its view pointers must
+    start where the oracle's strided builder starts each layer's block."""
+    from oracle import swa_oracle as O
+    lib, E = swa.lib, swa
+    L, H, D, P, pages, anchor = 5, 8, 128, 16, 37, 4096
+    g = O.unified_geometry(L, H, D, 2, P, pages)
+    need = lib.swa_unified_pool_bytes(L, H, D, swa.SWA_BF16, P, pages)
+    assert need == g["total_bytes"] + g["tail_pad"]
+    views = (swa.KvLayerStruct * L)()
+    raw = 1 << 20   # never dereferenced
+    assert lib.swa_unified_layer_views(raw, anchor + need, anchor, L, H, D, swa.SWA_BF16, P, pages, 1.0, 1.0,
+                                       views) == E.SWA_OK
+    for layer in range(L):
+        assert views[layer].k == raw + O.unified_view_base(anchor, layer, 0, g["row_bytes"], P)
+        assert views[layer].v == raw + O.unified_view_base(anchor, layer, 1, g["row_bytes"], P)
+        assert views[layer].rows == g["n_rows"] and views[layer].kv_heads == H and views[layer].dtype == swa.SWA_BF16
+    # one byte short of the tail pad: the last views would run past the buffer
+    assert lib.swa_unified_layer_views(raw, anchor + need - 1, anchor, L, H, D, swa.SWA_BF16, P, pages, 1.0, 1.0,
+                                       views) == E.SWA_E_SHAPE
+    assert lib.swa_unified_layer_views(raw, 1 << 40, 8, L, H, D, swa.SWA_BF16, P, pages, 1.0, 1.0,
+                                       views) == E.SWA_E_ARG       # anchor not 16-aligned
+    assert lib.swa_unified_layer_views(raw, 1 << 40, 0, L, H, D, 7, P, pages, 1.0, 1.0, views) == E.SWA_E_DTYPE
+    # kernel-facing rows reach 2^31: refused (int32 index buffers)
+    big = (1 << 31) // (2 * L * P) + 1
+    assert lib.swa_unified_layer_views(raw, 1 << 62, 0, L, H, D, swa.SWA_BF16, P, big, 1.0, 1.0,
+                                       views) == E.SWA_E_SHAPE
+    assert lib.swa_unified_pool_bytes(0, H, D, swa.SWA_BF16, P, pages) == -1
+
+
+def test_unified_translate_argument_errors(swa):
+    lib, E = swa.lib, swa
+    assert lib.swa_translate_kernel_ids(FAKE, 10, FAKE, 4, 0, 2, FAKE, None) == E.SWA_E_ARG
+    assert lib.swa_translate_kernel_ids(FAKE, 10, FAKE, 4, 16, 0, FAKE, None) == E.SWA_E_ARG
+    assert lib.swa_translate_kernel_ids(FAKE, 10, None, 4, 16, 2, FAKE, None) == E.SWA_E_ARG
+    assert lib.swa_translate_kernel_ids(None, 10, FAKE, 4, 16, 2, FAKE, None) == E.SWA_E_ARG
+    ix = index(swa, map_ptr=None)
+
+    def win(v2p=FAKE, n_pages=100, mult=64, window=128, table=FAKE, cap=1000):
+        return lib.swa_translate_window_unified(ctypes.byref(ix), v2p, n_pages, mult, window, None, table, FAKE, cap,
+                                                None)
+
+    assert win(v2p=None) == E.SWA_E_ARG
+    assert win(mult=0) == E.SWA_E_ARG
+    assert win(window=-2) == E.SWA_E_ARG
+    assert win(table=None) == E.SWA_E_ARG
+    assert win(n_pages=(1 << 31) // (16 * 64) + 1) == E.SWA_E_SHAPE     # ids would pass 2^31

@@ -751,3 +751,135 @@ def test_alloc_then_translate_and_window():
     assert np.array_equal(got_ptr, want[1])
     assert np.array_equal(table.cpu().numpy()[:got_ptr[-1]], want[0])
     assert np.all(want[0] > 0)   # every slot of the grown windows is live
+
+
+# ---------------------------------------------------------------------------
+# unified pool: same kernels over dense per-layer views of one raw buffer
+# ---------------------------------------------------------------------------
+
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+def _unified_raw(ub, anchor=256):
+    """The raw byte buffer of a unified batch: NaN everywhere (so stray reads
+    show), each live token's rows placed by the oracle's envelope formula."""
+    itemsize = 2
+    g = O.unified_geometry(ub.layers, ub.kv_heads, ub.head_dim, itemsize, ub.page_size, ub.n_phys)
+    raw = np.empty(anchor + g["total_bytes"] + g["tail_pad"], dtype=np.uint8)
+    raw.view(np.uint16)[:] = NAN_BF16
+    P = ub.page_size
+    for i, t in enumerate(ub.live_tokens):
+        page, off = int(ub.v2p[t // P]), int(t % P)
+        for layer in range(ub.layers):
+            for kv, rows in ((0, ub.k_rows), (1, ub.v_rows)):
+                at = O.envelope_offset(anchor, page, layer, kv, off, ub.layers, g["row_bytes"], P)
+                raw[at:at + g["row_bytes"]] = rows[layer, i].reshape(-1).view(np.uint8)
+    return raw, g
+
+
+def test_unified_kernel_ids_bit_exact():
+    from sliding_window_attention_swa_amd import swa
+    say("unified kernel ids")
+    ub = WL.unified_batch("uk", 61, [1, 40, 300, 1000, 129], 3, 8, 2, 128, 16, with_rows=False)
+    virt = np.arange(ub.v2p.size * ub.page_size, dtype=np.int64)
+    want = O.unified_kernel_ids(virt, ub.v2p, ub.page_size, 2 * ub.layers)
+    out = torch.empty(virt.size, dtype=torch.int64, device="cuda")
+    d_virt = torch.from_numpy(virt).cuda()
+    swa.swa_translate_kernel_ids(d_virt, torch.from_numpy(ub.v2p).cuda(), ub.page_size, 2 * ub.layers, out)
+    # in place, and ids outside the page table (negative, past the last page) read the sink row 0
+    odd = torch.tensor([-1, -100, virt.size, virt.size + 17, 5], dtype=torch.int64, device="cuda")
+    swa.swa_translate_kernel_ids(odd, torch.from_numpy(ub.v2p).cuda(), ub.page_size, 2 * ub.layers, odd)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want)
+    assert odd.cpu().tolist() == [0, 0, 0, 0, int(want[5])]
+
+
+@pytest.mark.parametrize("P", [1, 16, 64])
+def test_unified_window_table_bit_exact(P):
+    from sliding_window_attention_swa_amd import swa
+    say(f"unified window table P={P}")
+    ub = WL.unified_batch(f"uw{P}", 62, [1, 40, 300, 1000, 129, 4000], 4, 8, 2, 128, P, with_rows=False)
+    mult = 2 * ub.layers
+    want = O.window_table(ub.req_to_token, ub.req_pool_idx, ub.seq_lens, O.unified_mapping(ub.v2p, P, mult), 128)
+    ix = swa.IndexTables(torch.from_numpy(ub.req_to_token).cuda(), torch.from_numpy(ub.req_pool_idx).cuda(),
+                         torch.from_numpy(ub.seq_lens).cuda(), None, P)
+    table = torch.empty(int(want[1][-1]) + 7, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(ub.batch + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window_unified(ix, torch.from_numpy(ub.v2p).cuda(), mult, 128, table, indptr)
+    torch.cuda.synchronize()
+    assert np.array_equal(indptr.cpu().numpy(), want[1])
+    assert np.array_equal(table.cpu().numpy()[:want[1][-1]], want[0])
+
+
+def test_unified_store_places_rows_byte_exact():
+    """kv_store through the library's views at kernel-facing ids writes each
+    row exactly where the oracle's envelope formula puts it."""
+    from sliding_window_attention_swa_amd import swa
+    say("unified store")
+    ub = WL.unified_batch("us", 63, [40, 300, 129, 17], 3, 8, 2, 128, 16, with_rows=False)
+    anchor = 512
+    g = O.unified_geometry(ub.layers, ub.kv_heads, ub.head_dim, 2, 16, ub.n_phys)
+    raw = torch.zeros(anchor + g["total_bytes"] + g["tail_pad"], dtype=torch.uint8, device="cuda")
+    views = swa.swa_unified_layer_views(raw, anchor, ub.layers, ub.kv_heads, ub.head_dim, torch.bfloat16, 16,
+                                        ub.n_phys)
+    virt = ub.req_to_token[ub.req_pool_idx, ub.seq_lens - 1].astype(np.int64)   # each request's current token
+    ids = torch.empty(ub.batch, dtype=torch.int64, device="cuda")
+    swa.swa_translate_kernel_ids(torch.from_numpy(virt).cuda(), torch.from_numpy(ub.v2p).cuda(), 16, 2 * ub.layers,
+                                 ids)
+    for layer in range(ub.layers):
+        swa.swa_kv_store(views[layer], ids, bits_to_device(ub.new_k[layer], "bf16"),
+                         bits_to_device(ub.new_v[layer], "bf16"))
+    torch.cuda.synchronize()
+    want = np.zeros(raw.numel(), dtype=np.uint8)
+    for b, t in enumerate(virt):
+        page, off = int(ub.v2p[t // 16]), int(t % 16)
+        for layer in range(ub.layers):
+            for kv, rows in ((0, ub.new_k), (1, ub.new_v)):
+                at = O.envelope_offset(anchor, page, layer, kv, off, ub.layers, g["row_bytes"], 16)
+                want[at:at + g["row_bytes"]] = rows[layer, b].reshape(-1).view(np.uint8)
+    assert np.array_equal(raw.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_unified_decode_matches_oracle_and_two_pool(P):
+    from sliding_window_attention_swa_amd import swa
+    say(f"unified decode P={P}")
+    ub = WL.unified_batch(f"ud{P}", 64, [1, 40, 300, 1000, 129, 2049], 3, 16, 2, 128, P)
+    mult = 2 * ub.layers
+    raw_h, g = _unified_raw(ub)
+    raw = torch.from_numpy(raw_h).cuda()
+    views = swa.swa_unified_layer_views(raw, 256, ub.layers, ub.kv_heads, ub.head_dim, torch.bfloat16, P, ub.n_phys)
+    ks, vs = O.unified_views(raw_h, 256, ub.layers, ub.kv_heads, ub.head_dim, np.uint16, P, ub.n_phys)
+    m_unified = O.unified_mapping(ub.v2p, P, mult)
+    d_r2t = torch.from_numpy(ub.req_to_token).cuda()
+    d_rows = torch.from_numpy(ub.req_pool_idx).cuda()
+    d_lens = torch.from_numpy(ub.seq_lens).cuda()
+    ix = swa.IndexTables(d_r2t, d_rows, d_lens, None, P)
+    cap = ub.batch * 129
+    table = torch.empty(cap, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(ub.batch + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window_unified(ix, torch.from_numpy(ub.v2p).cuda(), mult, 128, table, indptr)
+    q = bits_to_device(ub.q, "bf16")
+    sinks = torch.from_numpy(ub.sinks).cuda()
+    # the two-pool form of the same data: pool row s = virtual id s (identity mapping, tombstones 0)
+    kid = m_unified[:-1]
+    ident = np.where(kid > 0, np.arange(kid.size), 0).astype(np.int64)
+    ident = np.concatenate([ident, [-1]])
+    ix2 = swa.IndexTables(d_r2t, d_rows, d_lens, torch.from_numpy(ident).cuda(), P)
+    table2 = torch.empty(cap, dtype=torch.int32, device="cuda")
+    indptr2 = torch.empty(ub.batch + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(ix2, 128, table2, indptr2)
+    for layer in range(ub.layers):
+        out = torch.empty((ub.batch, ub.q_heads, ub.head_dim), dtype=torch.float32, device="cuda")
+        swa.swa_decode(q, views[layer], ix, 128, out, sinks=sinks, slot_table=table, table_indptr=indptr,
+                       num_splits=1, use_map=False)
+        pool_k = bits_to_device(np.asarray(ks[layer])[kid], "bf16")
+        pool_v = bits_to_device(np.asarray(vs[layer])[kid], "bf16")
+        out2 = torch.empty_like(out)
+        swa.swa_decode(q, swa.KvLayer(pool_k, pool_v), ix2, 128, out2, sinks=sinks, slot_table=table2,
+                       table_indptr=indptr2, num_splits=1)
+        torch.cuda.synchronize()
+        want = O.decode(ub.q, "bf16", ks[layer], vs[layer], "bf16", ub.req_to_token, ub.req_pool_idx, ub.seq_lens,
+                        m_unified, 128, ub.sinks)
+        check(out, want, TOL["bf16"], f"unified decode layer {layer}")
+        assert torch.equal(out, out2)
