@@ -23,6 +23,13 @@ Parity status of each function (what pins it, see tests/test_oracle_pins.py):
   alloc_decode,       a one-token chunk), a token-by-token allocator written
   alloc_paired,       independently, page size 1 = slicing the free list,
   pages_needed        decode = extend of one token, paired offsets and mapping
+  first_key (chunked  pinned: chunk >= T is causal attention, chunk 1 is the
+  local attention)    W = 0 closed form, a masked-matrix brute force, the
+                      block-diagonal pair count
+  ring_*              pinned: the window's positions never share a ring row
+                      while they span at most R (brute force), a planted
+                      too-small ring collides, ring attention equals two-pool
+                      attention on the same rows
   attention           pinned: full-causal reduction, plain-softmax reduction,
                       pure-Python brute force, W=0 and identical-key closed
                       forms, GQA expansion, pair-count ratio ~ 2W/T.
@@ -46,8 +53,13 @@ from .swa_oracle import (  # noqa: F401
     extend,
     kv_bytes_per_token,
     kv_store,
+    first_key,
     pages_bound,
     pages_needed,
+    ring_capacity,
+    ring_req_to_token,
+    ring_rows,
+    ring_slot,
     pool_config,
     scored_pairs,
     translate_loc,

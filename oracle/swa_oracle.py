@@ -111,18 +111,33 @@ def translate_loc(full_loc, full_to_swa):
 # ---------------------------------------------------------------------------
 
 
-def window_range(seq_len: int, prefix_len: int, window: int):
+def first_key(i: int, window: int, chunk: int = 0) -> int:
+    """First key position query i sees: i - W for a sliding window (W >= 0),
+    the start of i's chunk for chunked local attention (chunk C > 0: [SWA] 设计,
+    Llama4's chunked local layers -- chunks of C positions from position 0, a
+    query sees its own chunk up to itself), the larger of the two when both
+    are given, and never below 0."""
+    lo = 0
+    if window >= 0:
+        lo = max(lo, i - window)
+    if chunk > 0:
+        lo = max(lo, (i // chunk) * chunk)
+    return lo
+
+
+def window_range(seq_len: int, prefix_len: int, window: int, chunk: int = 0):
     """Positions [lo, hi] whose K/V the new queries of a request can see.
 
     The new queries are positions prefix_len .. seq_len-1; query i sees
-    [max(0, i-W), i], so together they see [max(0, prefix_len - W), seq_len-1].
-    Decode is prefix_len = seq_len - 1.  W = -1 is full attention (lo = 0)."""
+    [first_key(i), i], so together they see [first_key(prefix_len), seq_len-1]
+    (first_key never decreases with i).  Decode is prefix_len = seq_len - 1.
+    W = -1 and chunk = 0 is full attention (lo = 0)."""
     hi = seq_len - 1
-    lo = 0 if window < 0 else max(0, prefix_len - window)
+    lo = first_key(prefix_len, window, chunk)
     return lo, hi
 
 
-def window_table(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, prefix_lens=None):
+def window_table(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, prefix_lens=None, chunk=0):
     """Per request, the slots of positions window_range(...), concatenated.
 
     Returns (table int64, indptr int64 of length B+1).  With full_to_swa None
@@ -134,7 +149,7 @@ def window_table(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, pref
     pre = lens - 1 if prefix_lens is None else np.asarray(prefix_lens, dtype=np.int64)
     table, indptr = [], [0]
     for b in range(b_count):
-        lo, hi = window_range(int(lens[b]), int(pre[b]), window)
+        lo, hi = window_range(int(lens[b]), int(pre[b]), window, chunk)
         for j in range(lo, hi + 1):
             full = int(r2t[rows[b], j])
             slot = full if full_to_swa is None else int(translate_loc([full], full_to_swa)[0])
@@ -214,7 +229,7 @@ def _slots_for(r2t_row, lo, hi, full_to_swa):
 
 def attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx, seq_lens,
               full_to_swa, window, sinks=None, scale=None, prefix_lens=None, qo_indptr=None,
-              k_scale=1.0, v_scale=1.0, only=None):
+              k_scale=1.0, v_scale=1.0, only=None, chunk=0):
     """Windowed attention of the new queries of every request (decode or extend).
 
     q: storage bits (q_dtype) of shape (total_new, Hq, D); request b owns rows
@@ -252,7 +267,7 @@ def attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx
             if wanted is not None and row not in wanted:
                 continue
             i = int(pre[b]) + t
-            lo = 0 if window < 0 else max(0, i - window)
+            lo = first_key(i, window, chunk)
             slots = _slots_for(r2t[rows[b]], lo, i, full_to_swa)
             k, v = _gather_kv(pool_k, pool_v, slots, pool_dtype, k_scale, v_scale)
             heads = range(hq) if wanted is None else wanted[row]
@@ -264,21 +279,55 @@ def attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx
 
 
 def decode(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx, seq_lens,
-           full_to_swa, window, sinks=None, scale=None, k_scale=1.0, v_scale=1.0, only=None):
+           full_to_swa, window, sinks=None, scale=None, k_scale=1.0, v_scale=1.0, only=None, chunk=0):
     """Decode: one query per request at position seq_len-1 (see attention)."""
     return attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx,
-                     seq_lens, full_to_swa, window, sinks, scale, None, None, k_scale, v_scale, only)
+                     seq_lens, full_to_swa, window, sinks, scale, None, None, k_scale, v_scale, only, chunk)
 
 
 def extend(q, q_dtype, qo_indptr, prefix_lens, pool_k, pool_v, pool_dtype, req_to_token,
            req_pool_idx, seq_lens, full_to_swa, window, sinks=None, scale=None,
-           k_scale=1.0, v_scale=1.0, only=None):
+           k_scale=1.0, v_scale=1.0, only=None, chunk=0):
     """Extend / chunked prefill: queries prefix_len .. seq_len-1 per request,
-    each over [max(0, i-W), i], against a pool that already holds the chunk's
+    each over [first_key(i), i], against a pool that already holds the chunk's
     K/V (see attention)."""
     return attention(q, q_dtype, pool_k, pool_v, pool_dtype, req_to_token, req_pool_idx,
                      seq_lens, full_to_swa, window, sinks, scale, prefix_lens, qo_indptr,
-                     k_scale, v_scale, only)
+                     k_scale, v_scale, only, chunk)
+
+
+# ---------------------------------------------------------------------------
+# Per-request SWA ring.  [POOLS] SWATokenToKVPoolAllocator ("为什么滑窗可以
+# 按请求记账"): with a ring, each request slot owns a fixed SWA capacity of the
+# ring size rounded up to a page, total capacity = request slots x that cost,
+# and the paged SWA indices go unused.  Reading: slot r owns rows
+# [r*R, (r+1)*R) and position j lives at row r*R + j mod R, so a request's
+# positions overwrite their own ring and no mapping or eviction is needed; it
+# is valid while the positions a step reads or writes span at most R.
+# ---------------------------------------------------------------------------
+
+
+def ring_rows(ring_size: int, page_size: int) -> int:
+    """R: the ring size rounded up to a whole page (_swa_ring_cost)."""
+    return -(-ring_size // page_size) * page_size
+
+
+def ring_capacity(request_slots: int, ring_size: int, page_size: int) -> int:
+    """The SWA pool's capacity in ring mode: every request slot's ring."""
+    return request_slots * ring_rows(ring_size, page_size)
+
+
+def ring_slot(row: int, pos: int, R: int) -> int:
+    return row * R + pos % R
+
+
+def ring_req_to_token(n_rows: int, stride: int, R: int):
+    """The table of ring slots: entry [r, j] = ring_slot(r, j, R), int64.
+    Attention over a ring is attention with these slots read directly
+    (full_to_swa None)."""
+    r = np.arange(n_rows, dtype=np.int64)[:, None]
+    j = np.arange(stride, dtype=np.int64)[None, :]
+    return r * R + j % R
 
 
 # ---------------------------------------------------------------------------

@@ -880,3 +880,112 @@ def test_unified_attention_equals_two_pool_attention():
         a = O.decode(q, "bf16", ks[layer], vs[layer], "bf16", r2t, np.arange(1, 4), lens, m_unified, W, sinks)
         b = O.decode(q, "bf16", pool_k, pool_v, "bf16", r2t, np.arange(1, 4), lens, identity, W, sinks)
         assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# chunked local attention ([SWA] 设计: Llama4's chunked local layers) and the
+# per-request SWA ring ([POOLS] SWATokenToKVPoolAllocator)
+# ---------------------------------------------------------------------------
+
+def masked_matrix(q, k, v, scale, window=-1, chunk=0, sinks=None):
+    """Attention as matrices: query i may see key j iff j <= i, j >= i - W
+    (W >= 0) and j lies in i's chunk (j // C == i // C, C > 0); a sink adds a
+    logit column with no value."""
+    T, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    ok = j <= i
+    if window >= 0:
+        ok &= j >= i - window
+    if chunk > 0:
+        ok &= (j // chunk) == (i // chunk)
+    out = np.empty_like(q)
+    for h in range(Hq):
+        s = scale * q[:, h, :] @ k[:, h // G, :].T
+        s = np.where(ok, s, -np.inf)
+        if sinks is not None:
+            s = np.concatenate([s, np.full((T, 1), sinks[h])], axis=1)
+        p = scipy.special.softmax(s, axis=1)
+        out[:, h, :] = p[:, :T] @ v[:, h // G, :]
+    return out
+
+
+@pytest.mark.parametrize("chunk", [40, 41, 1000])
+def test_chunk_at_least_T_is_full_causal(chunk):
+    rng = np.random.default_rng(500)
+    T, Hq, Hkv, D = 40, 4, 2, 16
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, -1, P=4, sinks=False)
+    got = O.extend(**args, chunk=chunk)
+    np.testing.assert_allclose(got, textbook_causal(q, k, v, 1 / math.sqrt(D)), rtol=1e-12, atol=1e-13)
+
+
+def test_chunk_one_is_the_window_zero_closed_form():
+    rng = np.random.default_rng(501)
+    T, Hq, Hkv, D = 12, 2, 2, 8
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, -1, P=2)
+    got = O.extend(**args, chunk=1)
+    s = np.einsum("thd,thd->th", q, k) / math.sqrt(D)
+    sig = 1 / (1 + np.exp(-(s - args["sinks"][None, :])))
+    np.testing.assert_allclose(got, v * sig[:, :, None], rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("chunk", [4, 7, 16])
+@pytest.mark.parametrize("window", [-1, 3, 10])
+def test_chunked_local_matches_the_block_mask(chunk, window):
+    rng = np.random.default_rng(510 + chunk + window)
+    T, Hq, Hkv, D = 37, 4, 2, 8
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, window, P=4)
+    got = O.extend(**args, chunk=chunk)
+    want = masked_matrix(q, k, v, 1 / math.sqrt(D), window, chunk, args["sinks"])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_chunked_local_pair_count():
+    # without a window, a chunk of n positions scores n (n + 1) / 2 pairs
+    for T, C in ((100, 8), (64, 64), (1000, 96), (7, 3)):
+        pairs = sum(i - O.first_key(i, -1, C) + 1 for i in range(T))
+        sizes = [C] * (T // C) + ([T % C] if T % C else [])
+        assert pairs == sum(n * (n + 1) // 2 for n in sizes)
+
+
+def test_ring_rows_and_capacity():
+    assert O.ring_rows(129, 16) == 144 and O.ring_rows(128, 16) == 128 and O.ring_rows(5, 1) == 5
+    assert O.ring_capacity(8, 129, 16) == 8 * 144
+
+
+@pytest.mark.parametrize("W,n_new,P", [(128, 1, 16), (20, 9, 4), (0, 1, 1), (7, 33, 8)])
+def test_ring_positions_of_one_step_never_share_a_row(W, n_new, P):
+    """The positions one step reads or writes (the window of its first new
+    query through its last) span W + n_new; a ring of that size rounded to a
+    page keeps them on distinct rows, and rows of different requests never
+    meet.  One row fewer collides."""
+    span = W + n_new
+    R = O.ring_rows(span, P)
+    for row in (1, 2, 5):
+        for start in range(0, 3 * R):
+            slots = [O.ring_slot(row, j, R) for j in range(start, start + span)]
+            assert len(set(slots)) == span
+            assert all(row * R <= s < (row + 1) * R for s in slots)
+    if span > 1:
+        short = span - 1
+        slots = [O.ring_slot(1, j, short) for j in range(span)]
+        assert len(set(slots)) < span
+
+
+def test_ring_attention_equals_two_pool_attention():
+    rng = np.random.default_rng(520)
+    T, Hq, Hkv, D, W = 30, 4, 2, 8, 6
+    args, q, k, v = dense_case(rng, T, Hq, Hkv, D, W, P=2, margin=1)
+    R = O.ring_rows(T, 4)          # extend of every position: the ring holds them all
+    rows = args["req_pool_idx"]
+    ring = O.ring_req_to_token(args["req_to_token"].shape[0], args["req_to_token"].shape[1], R)
+    n_rows = ring.max() + 1
+    pk = np.full((n_rows, Hkv, D), np.nan, dtype=np.float32)
+    pv = np.full((n_rows, Hkv, D), np.nan, dtype=np.float32)
+    for j in range(T):
+        pk[ring[rows[0], j]] = codecs.encode_store(k[j], "f32")
+        pv[ring[rows[0], j]] = codecs.encode_store(v[j], "f32")
+    want = O.extend(**args)
+    ring_args = dict(args, pool_k=pk, pool_v=pv, req_to_token=ring, full_to_swa=None)
+    assert np.array_equal(O.extend(**ring_args), want)
