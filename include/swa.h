@@ -226,6 +226,53 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
                         void *out, int32_t out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Attention variants.
+ *
+ * Chunked local attention ([SWA] 设计: Llama4's chunked local layers).  With a
+ * chunk size C > 0, positions form chunks of C from position 0 and query i
+ * sees only the earlier positions of its own chunk and itself: keys
+ * [max(first, C * floor(i / C)), i], where first is i - W for a window W >= 0
+ * and 0 for W = -1.  swa_translate_window_chunked builds the slot table of
+ * those keys (for extend: from the first new query's first key on);
+ * swa_extend_chunked is swa_extend with the chunk bound in its masks and
+ * reads the table built with the same W and C.  Decode needs no variant: a
+ * decode reads exactly the keys its table lists, so swa_decode with the
+ * chunked table (window = C - 1 when C <= 256, else -1 with a split plan for
+ * C keys) is chunked local decode.  C = 0 is the plain window.
+ */
+swa_status_t swa_translate_window_chunked(const swa_index_t *idx, int32_t window, int32_t chunk,
+                                          const int32_t *prefix_lens, int32_t *slot_table, int32_t *table_indptr,
+                                          int64_t table_capacity, hipStream_t stream);
+
+swa_status_t swa_extend_chunked(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
+                                const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
+                                const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                                int64_t table_capacity, int32_t window, int32_t chunk, const float *sinks,
+                                float sm_scale, void *out, int32_t out_dtype, hipStream_t stream);
+
+/* Per-request SWA ring ([POOLS] SWATokenToKVPoolAllocator, per-request SWA
+ * ring: each request slot owns the ring size rounded up to a page, the SWA
+ * capacity is request slots x that, the paged SWA indices go unused).  Request
+ * slot r (req_pool_idx) owns pool rows [r * R, (r + 1) * R) and position j lives
+ * at row r * R + j mod R, with R = ring_rows (the rounded ring size): no
+ * mapping, no eviction.  Valid while the positions one call reads or writes
+ * span at most R (decode: W + 1; extend: W + the chunk).
+ * swa_translate_window_ring writes the window's ring rows as the slot table
+ * (req_to_token is not read; idx->r2t_rows bounds the request slots,
+ * idx->r2t_stride the positions); swa_ring_locs writes the ring rows of the
+ * new positions [prefix_lens[b], seq_lens[b]) of every request packed in
+ * request order (prefix_lens NULL: decode, one position seq_lens[b] - 1 per
+ * request) for swa_kv_store / swa_decode_store; at most n_out are written.
+ * The layer views the ring pool, rows = request slots x R.  Errors: SWA_E_ARG,
+ * SWA_E_SHAPE (ring rows of all slots reach 2^31). */
+swa_status_t swa_translate_window_ring(const swa_index_t *idx, int64_t ring_rows, int32_t window, int32_t chunk,
+                                       const int32_t *prefix_lens, int32_t *slot_table, int32_t *table_indptr,
+                                       int64_t table_capacity, hipStream_t stream);
+
+swa_status_t swa_ring_locs(const swa_index_t *idx, int64_t ring_rows, const int32_t *prefix_lens, int64_t *out,
+                           int64_t n_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * SWA eviction — release the SWA KV of positions that left each request's
  * window ([SWA] 运行时: free_swa_out_of_window_slots; 双池与映射表: free_swa).
  * For request b (row req_pool_idx[b] of req_to_token) the released positions

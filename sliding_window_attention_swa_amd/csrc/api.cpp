@@ -96,8 +96,42 @@ swa_status_t swa_translate_window(const swa_index_t *idx, int32_t window, const 
   if (st != SWA_OK) return st;
   if (window < -1 || table_capacity < 0 || !table_indptr) return SWA_E_ARG;
   if (table_capacity > 0 && !slot_table) return SWA_E_ARG;
-  return from_hip(swa::launch_translate_window(*idx, window, prefix_lens, slot_table, table_indptr, table_capacity,
-                                               stream));
+  return from_hip(swa::launch_translate_window(*idx, window, 0, prefix_lens, slot_table, table_indptr,
+                                               table_capacity, stream));
+}
+
+swa_status_t swa_translate_window_chunked(const swa_index_t *idx, int32_t window, int32_t chunk,
+                                          const int32_t *prefix_lens, int32_t *slot_table, int32_t *table_indptr,
+                                          int64_t table_capacity, hipStream_t stream) {
+  swa_status_t st = check_index(idx, true);
+  if (st != SWA_OK) return st;
+  if (window < -1 || chunk < 0 || table_capacity < 0 || !table_indptr) return SWA_E_ARG;
+  if (table_capacity > 0 && !slot_table) return SWA_E_ARG;
+  return from_hip(swa::launch_translate_window(*idx, window, chunk, prefix_lens, slot_table, table_indptr,
+                                               table_capacity, stream));
+}
+
+swa_status_t swa_translate_window_ring(const swa_index_t *idx, int64_t ring_rows, int32_t window, int32_t chunk,
+                                       const int32_t *prefix_lens, int32_t *slot_table, int32_t *table_indptr,
+                                       int64_t table_capacity, hipStream_t stream) {
+  swa_status_t st = check_index(idx, false);
+  if (st != SWA_OK) return st;
+  if (ring_rows < 1 || window < -1 || chunk < 0 || table_capacity < 0 || !table_indptr) return SWA_E_ARG;
+  if (idx->r2t_rows < 1 || idx->r2t_stride < 1 || (idx->batch > 0 && !idx->req_pool_idx)) return SWA_E_ARG;
+  if (table_capacity > 0 && !slot_table) return SWA_E_ARG;
+  if (ring_rows > kMaxRows / idx->r2t_rows) return SWA_E_SHAPE;  // ring rows travel through int32 tables
+  return from_hip(swa::launch_translate_window_ring(*idx, ring_rows, window, chunk, prefix_lens, slot_table,
+                                                    table_indptr, table_capacity, stream));
+}
+
+swa_status_t swa_ring_locs(const swa_index_t *idx, int64_t ring_rows, const int32_t *prefix_lens, int64_t *out,
+                           int64_t n_out, hipStream_t stream) {
+  swa_status_t st = check_index(idx, false);
+  if (st != SWA_OK) return st;
+  if (ring_rows < 1 || n_out < 0 || (n_out > 0 && !out)) return SWA_E_ARG;
+  if (idx->r2t_rows < 1 || (idx->batch > 0 && !idx->req_pool_idx)) return SWA_E_ARG;
+  if (ring_rows > INT64_MAX / idx->r2t_rows) return SWA_E_SHAPE;
+  return from_hip(swa::launch_ring_locs(*idx, ring_rows, prefix_lens, out, n_out, stream));
 }
 
 swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64_t n, const void *k_new,
@@ -216,16 +250,18 @@ swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, c
                      sm_scale, out, out_dtype, 1, nullptr, 0, loc, k_new, v_new, stream);
 }
 
-swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
-                        const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
-                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
-                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
-                        int32_t out_dtype, hipStream_t stream) {
+namespace {
+
+swa_status_t extend_impl(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
+                         const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
+                         const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                         int64_t table_capacity, int32_t window, int32_t chunk, const float *sinks, float sm_scale,
+                         void *out, int32_t out_dtype, hipStream_t stream) {
   swa_status_t st = check_layer(layer);
   if (st != SWA_OK) return st;
   st = check_index(idx, true);
   if (st != SWA_OK) return st;
-  if (total_q < 0 || window < -1 || !std::isfinite(sm_scale)) return SWA_E_ARG;
+  if (total_q < 0 || window < -1 || chunk < 0 || !std::isfinite(sm_scale)) return SWA_E_ARG;
   if (idx->batch > 0 && (!qo_indptr || !prefix_lens)) return SWA_E_ARG;
   if (total_q > 0 && (!q || !out)) return SWA_E_ARG;
   if (table_indptr && (!slot_table || table_capacity < 0)) return SWA_E_ARG;
@@ -247,11 +283,32 @@ swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const i
   a.indptr = table_indptr;
   a.capacity = table_capacity;
   a.window = window;
+  a.chunk = chunk;
   a.sinks = sinks;
   a.sm_scale = sm_scale;
   a.out = out;
   a.out_dtype = out_dtype;
   return from_hip(swa::launch_extend(a, stream));
+}
+
+}  // namespace
+
+swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
+                        const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
+                        const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                        int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                        int32_t out_dtype, hipStream_t stream) {
+  return extend_impl(q, q_dtype, q_heads, qo_indptr, prefix_lens, total_q, layer, idx, slot_table, table_indptr,
+                     table_capacity, window, 0, sinks, sm_scale, out, out_dtype, stream);
+}
+
+swa_status_t swa_extend_chunked(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
+                                const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
+                                const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                                int64_t table_capacity, int32_t window, int32_t chunk, const float *sinks,
+                                float sm_scale, void *out, int32_t out_dtype, hipStream_t stream) {
+  return extend_impl(q, q_dtype, q_heads, qo_indptr, prefix_lens, total_q, layer, idx, slot_table, table_indptr,
+                     table_capacity, window, chunk, sinks, sm_scale, out, out_dtype, stream);
 }
 
 namespace {

@@ -46,6 +46,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return u;
 }
 
+// Sum of the two bf16 values of a packed pair, in f32.  The softmax weights
+// that enter P.V are rounded to bf16; summing the same rounded weights for the
+// normaliser makes the output an exact convex combination of V rows (plus the
+// sink), so the rounding only perturbs relative weights: a query with few keys,
+// whose output is as large as a V row, then carries no more error than one
+// with many.
+__device__ __forceinline__ float bf16x2_sum(uint32_t u) {
+  return __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane r supplies the LDS
 // address of 4 consecutive 16-bit elements (row r of a 16 x 4 block M);
 // lane i receives M[i/4 + 4e][i%4] for e = 0..3.
@@ -86,8 +96,13 @@ __device__ __forceinline__ int64_t row_elem(int64_t slot, int32_t heads, int32_t
 namespace swa {
 hipError_t launch_translate_loc(const int64_t *full_loc, int64_t n, const int64_t *map, int64_t map_len,
                                 int64_t *out, hipStream_t stream);
-hipError_t launch_translate_window(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
+hipError_t launch_translate_window(const swa_index_t &idx, int32_t window, int32_t chunk, const int32_t *prefix_lens,
                                    int32_t *table, int32_t *indptr, int64_t capacity, hipStream_t stream);
+hipError_t launch_translate_window_ring(const swa_index_t &idx, int64_t ring_rows, int32_t window, int32_t chunk,
+                                        const int32_t *prefix_lens, int32_t *table, int32_t *indptr,
+                                        int64_t capacity, hipStream_t stream);
+hipError_t launch_ring_locs(const swa_index_t &idx, int64_t ring_rows, const int32_t *prefix_lens, int64_t *out,
+                            int64_t capacity, hipStream_t stream);
 hipError_t launch_kv_store(const swa_kv_layer_t &layer, const int64_t *loc, int64_t n, const void *k_new,
                            const void *v_new, int32_t in_dtype, hipStream_t stream);
 
@@ -171,6 +186,7 @@ struct AllocArgs {
 hipError_t launch_alloc(const AllocArgs &a, hipStream_t stream);
 
 struct ExtendArgs {
+  int32_t chunk;  // chunked local attention: chunk size, 0 = none
   const void *q;
   int32_t q_heads;
   const int32_t *qo_indptr;

@@ -440,21 +440,19 @@ __device__ __forceinline__ void stream_compute(const DecodeParams &p, const Stre
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   m_run = m_new;
   float pv[8];
-  float ps = 0.f;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     pv[rr] = __builtin_amdgcn_exp2f(fmaf(sc[0][rr], p.scale2, -m_new));
     pv[4 + rr] = __builtin_amdgcn_exp2f(fmaf(sc[1][rr], p.scale2, -m_new));
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ps += pv[e];
-  l_run = l_run * alpha + ps;
-#pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] *= alpha;
   bf16x8_t pop;
   {
     uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
                       pack_bf16x2_hw(pv[6], pv[7])};
+    // the normaliser sums the rounded weights that enter P.V
+    l_run = l_run * alpha + ((bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3])));
     __builtin_memcpy(&pop, u4, 16);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
@@ -728,10 +726,10 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
         pv[4 + r] =
             (2 * u2 + 1 < MAXB) ? __builtin_amdgcn_exp2f(sc[(2 * u2 + 1) < MAXB ? 2 * u2 + 1 : 0][r] - m_run) : 0.f;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) l_run += pv[e];
       uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
                         pack_bf16x2_hw(pv[6], pv[7])};
+      // the normaliser sums the rounded weights that enter P.V
+      l_run += (bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3]));
       __builtin_memcpy(&pop[u2], u4, 16);
     }
     // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1), each pair's V rows

@@ -65,7 +65,20 @@ struct ExtendParams {
   float scale2;
   void *out;
   int32_t run_tiles;  // tiles per workgroup run
+  int32_t chunk;      // chunked local attention: chunk size, 0 = none
 };
+
+// First key position query i sees: i - W (W >= 0), the start of i's chunk of C
+// positions (chunked local attention, SWA note section 设计: Llama4's chunked
+// local layers; C > 0), the later of the two, never below 0.  It never
+// decreases with i, so a tile's first query has the tile's first key and its
+// last query the latest first key.
+__device__ __forceinline__ int32_t first_key(int32_t i, int32_t window, int32_t chunk) {
+  int32_t lo = 0;
+  if (window >= 0 && i - window > lo) lo = i - window;
+  if (chunk > 0 && i > 0 && i - i % chunk > lo) lo = i - i % chunk;
+  return lo;
+}
 
 __device__ __forceinline__ float wave_max_q(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -101,6 +114,7 @@ struct KeySrc {
   int32_t pos_base;
 };
 
+template <bool CHUNKED>
 __device__ __forceinline__ KeySrc key_src(const ExtendParams &p, int32_t b, int32_t prefix) {
   KeySrc ks;
   if (p.indptr) {
@@ -109,8 +123,12 @@ __device__ __forceinline__ KeySrc key_src(const ExtendParams &p, int32_t b, int3
     if (hi > p.capacity) hi = p.capacity;
     ks.src = p.table + lo;
     ks.hi = hi > lo ? hi - lo : 0;
-    int32_t base = p.window < 0 ? 0 : prefix - p.window;
-    ks.pos_base = base < 0 ? 0 : base;
+    if constexpr (CHUNKED) {
+      ks.pos_base = first_key(prefix, p.window, p.chunk);
+    } else {
+      int32_t base = p.window < 0 ? 0 : prefix - p.window;
+      ks.pos_base = base < 0 ? 0 : base;
+    }
   } else {
     int64_t row = p.req_idx[b];
     if (row < 0 || row >= p.r2t_rows) row = 0;
@@ -138,6 +156,7 @@ struct Tile {
   bool steady;     // W = 128, 16 valid queries, band inside position 0.. and the key source
 };
 
+template <bool CHUNKED>
 __device__ __forceinline__ Tile tile_at(const ExtendParams &p, const KeySrc &ks, int32_t qo0, int32_t qt,
                                         int32_t prefix, int32_t n_new, int32_t seq) {
   Tile t;
@@ -150,8 +169,9 @@ __device__ __forceinline__ Tile tile_at(const ExtendParams &p, const KeySrc &ks,
   t.i_last = il;
   int32_t kj0 = W < 0 ? 0 : t.i0 - W;
   t.kj0 = kj0 < 0 ? 0 : kj0;
+  if constexpr (CHUNKED) t.kj0 = first_key(t.i0, W, p.chunk);
   t.nkeys = il >= t.kj0 ? il - t.kj0 + 1 : 0;
-  t.steady = W == kBand - 16 && t.i0 - W >= 0 && qt * kTQ + kTQ <= n_new && il == t.i0 + kTQ - 1 &&
+  t.steady = !CHUNKED && W == kBand - 16 && t.i0 - W >= 0 && qt * kTQ + kTQ <= n_new && il == t.i0 + kTQ - 1 &&
              static_cast<int64_t>(t.row0) + kTQ <= p.total_q && static_cast<int64_t>(t.kj0) - ks.pos_base >= 0 &&
              static_cast<int64_t>(t.kj0) - ks.pos_base + kBand <= ks.hi;
   return t;
@@ -200,11 +220,12 @@ __device__ __forceinline__ void put_piece(uint16_t *ktile, uint16_t *vtile, int3
 __device__ __forceinline__ int32_t ring_slot(int32_t q0, int j) { return q0 + j < kKB ? q0 + j : q0 + j - kKB; }
 
 // Scores and softmax numerators of a steady tile (sacc ends up holding
-// 2^(s - m) per key; m_run / l_run the tile's max and sum).
+// 2^(s - m) per key; m_run the tile's max; the sum is taken in ring_pv, over
+// the rounded weights).
 template <int MB>
 __device__ __forceinline__ void ring_scores(const ExtendParams &p, const uint16_t *ktile, int32_t q0,
                                             const bf16x8_t (&qop)[MB][4], f32x4_t (&sacc)[MB][kKB],
-                                            float (&m_run)[MB], float (&l_run)[MB]) {
+                                            float (&m_run)[MB]) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
@@ -246,25 +267,20 @@ __device__ __forceinline__ void ring_scores(const ExtendParams &p, const uint16_
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][j][r]);
     const float m_new = wave_max_q(mx) * p.scale2;  // finite: every query sees its own key
     m_run[m] = m_new;
-    float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < kKB; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][j][r], p.scale2, -m_new));
-        sacc[m][j][r] = e;
-        ps += e;
-      }
-    l_run[m] = ps;
+      for (int r = 0; r < 4; ++r) sacc[m][j][r] = __builtin_amdgcn_exp2f(fmaf(sacc[m][j][r], p.scale2, -m_new));
   }
 }
 
 // O^T = V^T P^T of a steady tile over block pairs (2u, 2u+1) of its band.
 // acc is written, not accumulated into: the first pair starts from zero, so
 // acc holds no registers while the scores are computed.
+// l_run receives the sum of the bf16-rounded weights that enter the product.
 template <int MB>
 __device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const f32x4_t (&sacc)[MB][kKB],
-                                        f32x4_t (&acc)[MB][8]) {
+                                        f32x4_t (&acc)[MB][8], float (&l_run)[MB]) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
@@ -283,6 +299,8 @@ __device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const
       uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][ja][0], sacc[m][ja][1]), pack_bf16x2_hw(sacc[m][ja][2], sacc[m][ja][3]),
                         second ? pack_bf16x2_hw(sacc[m][jb][0], sacc[m][jb][1]) : 0u,
                         second ? pack_bf16x2_hw(sacc[m][jb][2], sacc[m][jb][3]) : 0u};
+      const float ps = (bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3]));
+      l_run[m] = u == 0 ? ps : l_run[m] + ps;
       __builtin_memcpy(&pop[m], u4, 16);
     }
     const uint16_t *va = vtile + slot[ja] * 16 * kVRow + voff;
@@ -302,7 +320,7 @@ __device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const
 
 // General tile: the band staged in chunks of up to 9 blocks, online softmax
 // across chunks, per-key masks on blocks that touch the band's edges.
-template <int MB>
+template <int MB, bool CHUNKED>
 __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile &tl, const bf16x8_t (&qop)[MB][4],
                              int32_t g, uint16_t *ktile, uint16_t *vtile, f32x4_t (&acc)[MB][8], float (&m_run)[MB],
                              float (&l_run)[MB]) {
@@ -311,6 +329,10 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
   const int32_t lq = lane >> 4;
   const int32_t W = p.window;
   const int32_t qpos = tl.i0 + kr;  // position of the query in this lane's column
+  // chunked local attention: the start of this lane's query's chunk and of the
+  // tile's last query's chunk (the latest chunk start of the tile)
+  const int32_t q_chunk0 = CHUNKED ? qpos - qpos % p.chunk : 0;
+  const int32_t tile_chunk0 = CHUNKED ? tl.i_last - tl.i_last % p.chunk : 0;
   for (int32_t c0 = 0; c0 < tl.nkeys; c0 += kKB * 16) {
     const int32_t nbk = min(kKB, (tl.nkeys - c0 + 15) / 16);
     const int32_t chunk_pos = tl.kj0 + c0;  // position of key 0 of the chunk
@@ -361,17 +383,20 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
 
     // ---- mask: only blocks that touch the band's edges or the chunk end need
     // a per-key test (a block is inside the band for every query of the tile
-    // when its last key <= i0 and its first key >= i_last - W).
+    // when its last key <= i0 and its first key >= i_last - W and, with chunks,
+    // >= the start of i_last's chunk).
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       const int32_t j0 = chunk_pos + kb * 16;
       const bool interior =
-          kb < nbk && c0 + kb * 16 + 15 < tl.nkeys && j0 + 15 <= tl.i0 && (W < 0 || j0 >= tl.i_last - W);
+          kb < nbk && c0 + kb * 16 + 15 < tl.nkeys && j0 + 15 <= tl.i0 && (W < 0 || j0 >= tl.i_last - W) &&
+          (!CHUNKED || j0 >= tile_chunk0);
       if (!interior) {  // workgroup-uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t j = j0 + 4 * lq + r;
-          const bool ok = kb < nbk && (c0 + kb * 16 + 4 * lq + r) < tl.nkeys && j <= qpos && (W < 0 || j >= qpos - W);
+          const bool ok = kb < nbk && (c0 + kb * 16 + 4 * lq + r) < tl.nkeys && j <= qpos &&
+                          (W < 0 || j >= qpos - W) && (!CHUNKED || j >= q_chunk0);
 #pragma unroll
           for (int m = 0; m < MB; ++m) sacc[m][kb][r] = ok ? sacc[m][kb][r] : -INFINITY;
         }
@@ -389,16 +414,11 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
       const float m_new = fmaxf(m_run[m], wave_max_q(mx) * p.scale2);
       const float alpha = __builtin_amdgcn_exp2f(m_run[m] - m_new);
       m_run[m] = m_new;
-      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][kb][r], p.scale2, -m_new));
-          sacc[m][kb][r] = e;
-          ps += e;
-        }
-      l_run[m] = l_run[m] * alpha + ps;
+        for (int r = 0; r < 4; ++r) sacc[m][kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[m][kb][r], p.scale2, -m_new));
+      l_run[m] *= alpha;  // the chunk's rounded weights are added below, as they are packed
       if (c0 > 0) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[m][n] *= alpha;
@@ -420,6 +440,7 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
                             pack_bf16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
                             second ? pack_bf16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
                             second ? pack_bf16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
+          l_run[m] += (bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3]));
           __builtin_memcpy(&pop[m], u4, 16);
         }
 #pragma unroll
@@ -571,7 +592,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
   int32_t seq = p.seq_lens[b];
   if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
   const int32_t prefix = p.prefix_lens[b];
-  const KeySrc ks = key_src(p, b, prefix);
+  const KeySrc ks = key_src<false>(p, b, prefix);
   float sink2[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -587,7 +608,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
   // (bf16 output), so its stores have a whole tile to drain before the next.
   int32_t qt = qt_begin;
   while (qt < qt_end) {
-    Tile tl = tile_at(p, ks, qo0, qt, prefix, n_new, seq);
+    Tile tl = tile_at<false>(p, ks, qo0, qt, prefix, n_new, seq);
     if (!tl.steady) {
       ++qt;
       continue;
@@ -597,7 +618,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
     // LDS write waits for one.
     uint4 qraw[MB][4];
     load_q<MB>(p, static_cast<int64_t>(tl.row0) + kr, g, w, lq, qraw);
-    bool next_steady = qt + 1 < qt_end && tile_at(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
+    bool next_steady = qt + 1 < qt_end && tile_at<false>(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
     int32_t nslot;  // slot of this thread's row of the next tile's band block 8
     {
       int32_t sl[kKB];
@@ -640,7 +661,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
       uint4 qn[MB][4];
       if (next_steady) {
         fetch_piece(p, nslot, g, nk, nv);
-        const bool next2 = qt + 2 < qt_end && tile_at(p, ks, qo0, qt + 2, prefix, n_new, seq).steady;
+        const bool next2 = qt + 2 < qt_end && tile_at<false>(p, ks, qo0, qt + 2, prefix, n_new, seq).steady;
         nslot = slot_in(ks, next2 ? tl.kj0 + 16 + kBand + row : tl.kj0 + row);
         load_q<MB>(p, static_cast<int64_t>(tl.row0) + kTQ + kr, g, w, lq, qn);
       }
@@ -651,9 +672,9 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
       {
         bf16x8_t qop[MB][4];
         q_operands<MB>(qraw, qop);
-        ring_scores<MB>(p, ktile, q0, qop, sacc, m_run, l_run);
+        ring_scores<MB>(p, ktile, q0, qop, sacc, m_run);
       }
-      ring_pv<MB>(vtile, q0, sacc, acc);
+      ring_pv<MB>(vtile, q0, sacc, acc, l_run);
       if constexpr (OUT_BF16) {
         finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, pend);
         pend_row0 = tl.row0;
@@ -665,8 +686,8 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
       }
       ++qt;
       if (!next_steady) break;
-      tl = tile_at(p, ks, qo0, qt, prefix, n_new, seq);
-      next_steady = qt + 1 < qt_end && tile_at(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
+      tl = tile_at<false>(p, ks, qo0, qt, prefix, n_new, seq);
+      next_steady = qt + 1 < qt_end && tile_at<false>(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
       q0 = q0 + 1 < kKB ? q0 + 1 : 0;
 #pragma unroll
       for (int m = 0; m < MB; ++m)
@@ -677,7 +698,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
   }
 }
 
-template <int MB, bool OUT_BF16>
+template <int MB, bool OUT_BF16, bool CHUNKED>
 __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
                                            int32_t g, int32_t qt_begin, int32_t qt_end) {
   const int32_t lane = threadIdx.x & 63;
@@ -694,7 +715,7 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
   int32_t seq = p.seq_lens[b];
   if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
   const int32_t prefix = p.prefix_lens[b];
-  const KeySrc ks = key_src(p, b, prefix);
+  const KeySrc ks = key_src<CHUNKED>(p, b, prefix);
   float sink2[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -703,7 +724,7 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
   }
 
   for (int32_t qt = qt_begin; qt < qt_end; ++qt) {
-    const Tile tl = tile_at(p, ks, qo0, qt, prefix, n_new, seq);
+    const Tile tl = tile_at<CHUNKED>(p, ks, qo0, qt, prefix, n_new, seq);
     if (tl.steady) continue;
     const bool qvalid = (qt * kTQ + kr) < n_new && static_cast<int64_t>(tl.row0) + kr < p.total_q;
     f32x4_t acc[MB][8];
@@ -722,7 +743,7 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
     load_q<MB>(p, qvalid ? static_cast<int64_t>(tl.row0) + kr : static_cast<int64_t>(tl.row0), g, w, lq, qr);
     bf16x8_t qop[MB][4];
     q_operands<MB>(qr, qop);
-    tile_general<MB>(p, ks, tl, qop, g, ktile, vtile, acc, m_run, l_run);
+    tile_general<MB, CHUNKED>(p, ks, tl, qop, g, ktile, vtile, acc, m_run, l_run);
     store_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, g, tl.row0, qvalid);
   }
 }
@@ -754,7 +775,9 @@ __device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t 
 // (request, kv head, run), are split into 8 contiguous ranges, one per XCD
 // (workgroup i runs on XCD i % 8), so neighbouring runs, which share band
 // blocks, meet in one L2; the workgroups of an XCD stride through its range.
-template <int MB, bool OUT_BF16>
+// CHUNKED: chunked local attention (p.chunk > 0), a separate instantiation so
+// the window-only code carries none of it.
+template <int MB, bool OUT_BF16, bool CHUNKED>
 __global__ void __launch_bounds__(kNW * 64, MB >= 4 ? 1 : 2) extend_kernel(ExtendParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
@@ -766,24 +789,32 @@ __global__ void __launch_bounds__(kNW * 64, MB >= 4 ? 1 : 2) extend_kernel(Exten
   const int32_t r_lo = static_cast<int32_t>(static_cast<int64_t>(total) * x / 8);
   const int32_t r_hi = static_cast<int32_t>(static_cast<int64_t>(total) * (x + 1) / 8);
   const int32_t r0 = r_lo + static_cast<int32_t>(blockIdx.x / 8);
-  for (int32_t r = r0; r < r_hi; r += per_xcd) {
-    const Run run = run_of(p, T, r);
-    if (run.b < 0) break;
-    run_steady<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+  if constexpr (!CHUNKED) {  // steady tiles exist only without chunks
+    for (int32_t r = r0; r < r_hi; r += per_xcd) {
+      const Run run = run_of(p, T, r);
+      if (run.b < 0) break;
+      run_steady<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+    }
   }
   for (int32_t r = r0; r < r_hi; r += per_xcd) {
     const Run run = run_of(p, T, r);
     if (run.b < 0) break;
-    run_general<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+    run_general<MB, OUT_BF16, CHUNKED>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
   }
 }
 
 template <int MB>
 hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStream_t stream) {
-  if (out_bf16)
-    hipLaunchKernelGGL((extend_kernel<MB, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((extend_kernel<MB, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  if (p.chunk > 0) {
+    if (out_bf16)
+      hipLaunchKernelGGL((extend_kernel<MB, true, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((extend_kernel<MB, false, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  } else if (out_bf16) {
+    hipLaunchKernelGGL((extend_kernel<MB, true, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((extend_kernel<MB, false, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -816,6 +847,7 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   p.indptr = a.indptr;
   p.capacity = a.capacity;
   p.window = a.window;
+  p.chunk = a.chunk;
   p.sinks = a.sinks;
   p.scale2 = a.sm_scale * kLog2e;
   p.out = a.out;

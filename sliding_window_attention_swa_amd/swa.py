@@ -29,7 +29,8 @@ EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_
            "swa_decode", "swa_decode_store", "swa_extend", "swa_validate_workspace_bytes", "swa_validate",
            "swa_evict_workspace_bytes", "swa_evict", "swa_alloc_pages_needed", "swa_alloc_extend",
            "swa_alloc_decode", "swa_unified_pool_bytes", "swa_unified_layer_views", "swa_translate_kernel_ids",
-           "swa_translate_window_unified", "swa_status_string")
+           "swa_translate_window_unified", "swa_translate_window_chunked", "swa_extend_chunked",
+           "swa_translate_window_ring", "swa_ring_locs", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -102,6 +103,11 @@ _sig = {
     "swa_translate_kernel_ids": (_i32, [_p, _i64, _p, _i64, _i32, _i32, _p, _p]),
     "swa_translate_window_unified": (_i32, [ctypes.POINTER(IndexStruct), _p, _i64, _i32, _i32, _p, _p, _p, _i64,
                                             _p]),
+    "swa_translate_window_chunked": (_i32, [ctypes.POINTER(IndexStruct), _i32, _i32, _p, _p, _p, _i64, _p]),
+    "swa_extend_chunked": (_i32, [_p, _i32, _i32, _p, _p, _i64, ctypes.POINTER(KvLayerStruct),
+                                  ctypes.POINTER(IndexStruct), _p, _p, _i64, _i32, _i32, _p, _f32, _p, _i32, _p]),
+    "swa_translate_window_ring": (_i32, [ctypes.POINTER(IndexStruct), _i64, _i32, _i32, _p, _p, _p, _i64, _p]),
+    "swa_ring_locs": (_i32, [ctypes.POINTER(IndexStruct), _i64, _p, _p, _i64, _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -462,3 +468,69 @@ def swa_translate_window_unified(index: IndexTables, v2p: torch.Tensor, multipli
                                             _ptr(slot_table, torch.int32, "slot_table"),
                                             _ptr(table_indptr, torch.int32, "table_indptr"), slot_table.numel(),
                                             _stream(stream)), "swa_translate_window_unified")
+
+
+# ---------------------------------------------------------------------------
+# attention variants: chunked local attention, per-request SWA ring
+# ---------------------------------------------------------------------------
+
+
+def swa_translate_window_chunked(index: IndexTables, window: int, chunk: int, slot_table: torch.Tensor,
+                                 table_indptr: torch.Tensor, prefix_lens: Optional[torch.Tensor] = None,
+                                 use_map: bool = True, stream=None):
+    if table_indptr.numel() < index.seq_lens.numel() + 1:
+        raise ValueError("table_indptr needs batch + 1 entries")
+    ix = index.struct(with_map=use_map)
+    _check(lib.swa_translate_window_chunked(ctypes.byref(ix), window, chunk,
+                                            _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                                            _ptr(slot_table, torch.int32, "slot_table"),
+                                            _ptr(table_indptr, torch.int32, "table_indptr"), slot_table.numel(),
+                                            _stream(stream)), "swa_translate_window_chunked")
+
+
+def swa_extend_chunked(q: torch.Tensor, qo_indptr: torch.Tensor, prefix_lens: torch.Tensor, layer: KvLayer,
+                       index: IndexTables, window: int, chunk: int, out: torch.Tensor,
+                       sinks: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                       slot_table: Optional[torch.Tensor] = None, table_indptr: Optional[torch.Tensor] = None,
+                       use_map: bool = True, stream=None):
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be (total_q, q_heads, head_dim)")
+    scale = sm_scale if sm_scale is not None else q.shape[2] ** -0.5
+    ls, ix = layer.struct(), index.struct(with_map=use_map)
+    _check(lib.swa_extend_chunked(_ptr(q, name="q"), dtype_code(q), q.shape[1],
+                                  _ptr(qo_indptr, torch.int32, "qo_indptr"), _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                                  q.shape[0], ctypes.byref(ls), ctypes.byref(ix),
+                                  _ptr(slot_table, torch.int32, "slot_table"),
+                                  _ptr(table_indptr, torch.int32, "table_indptr"),
+                                  0 if slot_table is None else slot_table.numel(), window, chunk,
+                                  _ptr(sinks, torch.float32, "sinks"), scale, _ptr(out, name="out"), dtype_code(out),
+                                  _stream(stream)), "swa_extend_chunked")
+
+
+def _ring_index(req_pool_idx: torch.Tensor, seq_lens: torch.Tensor, request_slots: int, max_len: int) -> IndexStruct:
+    return IndexStruct(None, request_slots, max_len, _ptr(req_pool_idx, torch.int32, "req_pool_idx"),
+                       _ptr(seq_lens, torch.int32, "seq_lens"), None, 0, seq_lens.numel(), 1)
+
+
+def swa_translate_window_ring(req_pool_idx: torch.Tensor, seq_lens: torch.Tensor, request_slots: int, max_len: int,
+                              ring_rows: int, window: int, slot_table: torch.Tensor, table_indptr: torch.Tensor,
+                              chunk: int = 0, prefix_lens: Optional[torch.Tensor] = None, stream=None):
+    """Window slot table of a per-request SWA ring (request slot r, position j
+    -> r * ring_rows + j mod ring_rows)."""
+    if table_indptr.numel() < seq_lens.numel() + 1:
+        raise ValueError("table_indptr needs batch + 1 entries")
+    ix = _ring_index(req_pool_idx, seq_lens, request_slots, max_len)
+    _check(lib.swa_translate_window_ring(ctypes.byref(ix), ring_rows, window, chunk,
+                                         _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                                         _ptr(slot_table, torch.int32, "slot_table"),
+                                         _ptr(table_indptr, torch.int32, "table_indptr"), slot_table.numel(),
+                                         _stream(stream)), "swa_translate_window_ring")
+
+
+def swa_ring_locs(req_pool_idx: torch.Tensor, seq_lens: torch.Tensor, request_slots: int, ring_rows: int,
+                  out: torch.Tensor, prefix_lens: Optional[torch.Tensor] = None, stream=None):
+    """Ring rows of the new positions (prefix_lens None: one decode position
+    per request)."""
+    ix = _ring_index(req_pool_idx, seq_lens, request_slots, 1)
+    _check(lib.swa_ring_locs(ctypes.byref(ix), ring_rows, _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                             _ptr(out, torch.int64, "out"), out.numel(), _stream(stream)), "swa_ring_locs")

@@ -191,15 +191,17 @@ def round_up(x: int, m: int) -> int:
 
 
 def decode_workload(name, seed, seq_lens, q_heads, kv_heads, window, page_size, q_dtype, kv_dtype, sinks=True,
-                    ratio=0.8, live_margin=0, with_store=False, head_dim=128, slack_pages=2, swa_tokens=None):
+                    ratio=0.8, live_margin=0, with_store=False, head_dim=128, slack_pages=2, swa_tokens=None,
+                    two_pools=True):
     """A batch of decode requests against one SWA layer (window >= 0) of a two-pool
-    cache, or against a single full pool (window < 0: positions read from
-    req_to_token directly, no SWA pool)."""
+    cache, or against a single full pool (window < 0, or two_pools=False: the
+    windowed single-pool mode; positions read from req_to_token directly, no
+    SWA pool)."""
     r_len, r_full, r_swa, r_q, r_k, r_v, r_s, r_new = _streams(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     B, P = len(seq_lens), page_size
     n_full = round_up(int(sum(round_up(int(t), P) for t in seq_lens)) + slack_pages * P, P)
-    use_swa = window >= 0
+    use_swa = window >= 0 and two_pools
     if use_swa:
         live_from = np.maximum(seq_lens - 1 - window - live_margin, 0)
         need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(seq_lens, live_from)))
@@ -226,21 +228,25 @@ def decode_workload(name, seed, seq_lens, q_heads, kv_heads, window, page_size, 
 
 
 def extend_workload(name, seed, prefix_lens, chunk_lens, q_heads, kv_heads, window, page_size, sinks=True,
-                    ratio=0.8, head_dim=128, slack_pages=2):
+                    ratio=0.8, head_dim=128, slack_pages=2, two_pools=True, live_from=None):
     """Chunked prefill: each request has a cached prefix whose pages before
-    prefix - W are tombstoned on the SWA side, plus a chunk of new tokens whose
-    K/V are provided as new_k / new_v (to be stored at translate(new_full_loc))."""
+    prefix - W (or live_from) are tombstoned on the SWA side, plus a chunk of
+    new tokens whose K/V are provided as new_k / new_v (to be stored at
+    translate(new_full_loc)).  two_pools=False: one full pool, no mapping (the
+    windowed single-pool mode)."""
     r_len, r_full, r_swa, r_q, r_k, r_v, r_s, r_new = _streams(seed)
     prefix = np.asarray(prefix_lens, dtype=np.int64)
     chunk = np.asarray(chunk_lens, dtype=np.int64)
     seq = prefix + chunk
     B, P = len(seq), page_size
     n_full = round_up(int(sum(round_up(int(t), P) for t in seq)) + slack_pages * P, P)
-    live_from = np.maximum(prefix - window, 0) if window >= 0 else np.zeros(B, np.int64)
+    if live_from is None:
+        live_from = np.maximum(prefix - window, 0) if window >= 0 else np.zeros(B, np.int64)
+    live_from = np.asarray(live_from, dtype=np.int64)
     need = int(sum(round_up(int(t), P) - (int(lf) // P) * P for t, lf in zip(seq, live_from)))
-    n_swa = max(round_up(int(math.floor(ratio * n_full)), P), round_up(need + slack_pages * P, P))
+    n_swa = max(round_up(int(math.floor(ratio * n_full)), P), round_up(need + slack_pages * P, P)) if two_pools else 0
     r2t, mapping, slot_lists = _layout(seq, P, n_full, n_swa, live_from, r_full, r_swa)
-    rows = n_swa + P
+    rows = (n_swa if two_pools else n_full) + P
     # pool holds the live prefix window only; chunk rows start as NaN and are stored
     prefix_slots = [s[:int(p)] for s, p in zip(slot_lists, prefix)]
     pk, pv = _fill_pool(rows, kv_heads, head_dim, "bf16", prefix_slots, r_k, r_v)
@@ -251,7 +257,7 @@ def extend_workload(name, seed, prefix_lens, chunk_lens, q_heads, kv_heads, wind
     qo[1:] = np.cumsum(chunk)
     new_loc = np.concatenate([r2t[b + 1, int(prefix[b]):int(seq[b])] for b in range(B)]).astype(np.int64)
     wl = Workload(name, B, q_heads, kv_heads, head_dim, window, P, "bf16", "bf16", seq.astype(np.int32), r2t,
-                  np.arange(1, B + 1, dtype=np.int32), mapping, n_full, n_swa, pk, pv, q, s,
+                  np.arange(1, B + 1, dtype=np.int32), mapping if two_pools else None, n_full, n_swa, pk, pv, q, s,
                   prefix_lens=prefix.astype(np.int32), qo_indptr=qo, ratio=ratio)
     wl.new_full_loc = new_loc
     wl.new_k = to_store(r_new.standard_normal((total, kv_heads, head_dim), dtype=np.float32), "bf16")
@@ -563,3 +569,55 @@ def unified_c2_decode(seed=SEED_BASE + 2, layers=32) -> UnifiedBatch:
     return unified_batch("unified_c2_B64_L%d" % layers, seed, lens, layers, 64, 8, 128, 16, live_margin=0,
                          with_rows=False)
 
+
+
+# ---------------------------------------------------------------------------
+# Per-request SWA ring: logical K/V of each request's live positions (which
+# ring row holds a position is the layout under test, so it is not decided
+# here)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class RingBatch:
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    window: int
+    request_slots: int            # request slots of the ring pool (slot 0 padding)
+    seq_lens: np.ndarray          # int32 (B,)
+    prefix_lens: np.ndarray       # int32 (B,): decode = seq - 1
+    req_pool_idx: np.ndarray      # int32 (B,): distinct slots in 1 .. request_slots - 1
+    live_lo: np.ndarray           # int64 (B,): first live position (the first query's first key)
+    k_rows: List[np.ndarray]      # per request (prefix - live_lo, Hkv, D) bf16 bits: positions live_lo .. prefix-1
+    v_rows: List[np.ndarray]
+    q: np.ndarray                 # (sum of new positions, Hq, D) bf16 bits
+    sinks: Optional[np.ndarray]
+    new_k: np.ndarray             # (sum of new positions, Hkv, D) bf16 bits
+    new_v: np.ndarray
+
+
+def ring_batch(name, seed, prefix_lens, new_lens, q_heads, kv_heads, window, request_slots=None, sinks=True,
+               head_dim=128) -> RingBatch:
+    """Requests on seeded distinct request slots; each holds the K/V of the
+    positions its next step reads from before its prefix (from the first new
+    query's first key on) and brings new_lens new positions."""
+    r_len, r_slot, _, r_q, r_k, r_v, r_s, r_new = _streams(seed)
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    new = np.asarray(new_lens, dtype=np.int64)
+    B = len(pre)
+    slots = request_slots or 2 * B + 2
+    rows = (1 + r_slot.permutation(slots - 1)[:B]).astype(np.int32)
+    lo = np.maximum(pre - window, 0) if window >= 0 else np.zeros(B, np.int64)
+    k_rows = [to_store(r_k.standard_normal((int(p - l), kv_heads, head_dim), dtype=np.float32), "bf16")
+              for p, l in zip(pre, lo)]
+    v_rows = [to_store(r_v.standard_normal((int(p - l), kv_heads, head_dim), dtype=np.float32), "bf16")
+              for p, l in zip(pre, lo)]
+    total = int(new.sum())
+    q = to_store(r_q.standard_normal((total, q_heads, head_dim), dtype=np.float32), "bf16")
+    s = r_s.standard_normal(q_heads).astype(np.float32) if sinks else None
+    new_k = to_store(r_new.standard_normal((total, kv_heads, head_dim), dtype=np.float32), "bf16")
+    new_v = to_store(r_new.standard_normal((total, kv_heads, head_dim), dtype=np.float32), "bf16")
+    return RingBatch(name, B, q_heads, kv_heads, head_dim, window, slots, (pre + new).astype(np.int32),
+                     pre.astype(np.int32), rows, lo, k_rows, v_rows, q, s, new_k, new_v)

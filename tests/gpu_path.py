@@ -138,21 +138,29 @@ def run_decode(dw: DeviceWorkload, out_dtype="f32", num_splits=None, use_table=T
     return out
 
 
-def run_extend(dw: DeviceWorkload, out_dtype="f32", use_table=True):
+def run_extend(dw: DeviceWorkload, out_dtype="f32", use_table=True, chunk=0):
+    """swa_extend (chunk > 0: swa_extend_chunked over a chunked table)."""
     from sliding_window_attention_swa_amd import swa
     wl = dw.wl
     B = wl.batch
     table = indptr = None
+    use_map = dw.map is not None
     if use_table:
-        lo = np.maximum(wl.prefix_lens.astype(np.int64) - wl.window, 0) if wl.window >= 0 else np.zeros(B, np.int64)
-        cap = int((wl.seq_lens.astype(np.int64) - lo).sum())
+        cap = int(wl.seq_lens.astype(np.int64).sum())   # at least every window
         table = torch.empty(max(cap, 1), dtype=torch.int32, device="cuda")
         indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
-        swa.swa_translate_window(dw.index, wl.window, table, indptr, prefix_lens=dw.prefix,
-                                 use_map=dw.map is not None)
+        if chunk:
+            swa.swa_translate_window_chunked(dw.index, wl.window, chunk, table, indptr, prefix_lens=dw.prefix,
+                                             use_map=use_map)
+        else:
+            swa.swa_translate_window(dw.index, wl.window, table, indptr, prefix_lens=dw.prefix, use_map=use_map)
     out = torch.empty((wl.q.shape[0], wl.q_heads, wl.head_dim), dtype=TORCH_STORE[out_dtype], device="cuda")
-    swa.swa_extend(dw.q, dw.qo, dw.prefix, dw.layer, dw.index, wl.window, out, sinks=dw.sinks, slot_table=table,
-                   table_indptr=indptr, use_map=dw.map is not None)
+    if chunk:
+        swa.swa_extend_chunked(dw.q, dw.qo, dw.prefix, dw.layer, dw.index, wl.window, chunk, out, sinks=dw.sinks,
+                               slot_table=table, table_indptr=indptr, use_map=use_map)
+    else:
+        swa.swa_extend(dw.q, dw.qo, dw.prefix, dw.layer, dw.index, wl.window, out, sinks=dw.sinks,
+                       slot_table=table, table_indptr=indptr, use_map=use_map)
     torch.cuda.synchronize()
     return out
 
@@ -165,16 +173,16 @@ def oracle_pools_after_store(wl: WL.Workload):
     return O.kv_store(wl.pool_k, wl.pool_v, loc, wl.new_k, wl.new_v, wl.new_dtype, wl.kv_dtype)
 
 
-def oracle_decode(wl: WL.Workload, only=None):
+def oracle_decode(wl: WL.Workload, only=None, chunk=0):
     pk, pv = oracle_pools_after_store(wl)
     return O.decode(wl.q, wl.q_dtype, pk, pv, wl.kv_dtype, wl.req_to_token, wl.req_pool_idx, wl.seq_lens,
-                    wl.full_to_swa, wl.window, wl.sinks, only=only)
+                    wl.full_to_swa, wl.window, wl.sinks, only=only, chunk=chunk)
 
 
-def oracle_extend(wl: WL.Workload, only=None):
+def oracle_extend(wl: WL.Workload, only=None, chunk=0):
     pk, pv = oracle_pools_after_store(wl)
     return O.extend(wl.q, wl.q_dtype, wl.qo_indptr, wl.prefix_lens, pk, pv, wl.kv_dtype, wl.req_to_token,
-                    wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window, wl.sinks, only=only)
+                    wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window, wl.sinks, only=only, chunk=chunk)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

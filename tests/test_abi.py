@@ -338,3 +338,25 @@ def test_unified_translate_argument_errors(swa):
     assert win(window=-2) == E.SWA_E_ARG
     assert win(table=None) == E.SWA_E_ARG
     assert win(n_pages=(1 << 31) // (16 * 64) + 1) == E.SWA_E_SHAPE     # ids would pass 2^31
+
+
+def test_variant_argument_errors(swa):
+    lib, E = swa.lib, swa
+    ix = index(swa)
+    assert lib.swa_translate_window_chunked(ctypes.byref(ix), 128, -1, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window_chunked(ctypes.byref(ix), -2, 64, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window_chunked(ctypes.byref(ix), -1, 64, None, FAKE, None, 10, None) == E.SWA_E_ARG
+    ring_ix = swa.IndexStruct(None, 8, 100, FAKE, FAKE, None, 0, 2, 16)
+    assert lib.swa_translate_window_ring(ctypes.byref(ring_ix), 0, 128, 0, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window_ring(ctypes.byref(ring_ix), 144, -2, 0, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_translate_window_ring(ctypes.byref(ring_ix), (1 << 31) // 8 + 1, 128, 0, None, FAKE, FAKE, 10,
+                                         None) == E.SWA_E_SHAPE
+    no_rows = swa.IndexStruct(None, 8, 100, None, FAKE, None, 0, 2, 16)
+    assert lib.swa_translate_window_ring(ctypes.byref(no_rows), 144, 128, 0, None, FAKE, FAKE, 10, None) == E.SWA_E_ARG
+    assert lib.swa_ring_locs(ctypes.byref(ring_ix), 0, None, FAKE, 2, None) == E.SWA_E_ARG
+    assert lib.swa_ring_locs(ctypes.byref(ring_ix), 144, None, None, 2, None) == E.SWA_E_ARG
+    ly = layer(swa)
+    assert lib.swa_extend_chunked(FAKE, 1, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, 128,
+                                  -1, None, 0.088, FAKE, 0, None) == E.SWA_E_ARG
+    assert lib.swa_extend_chunked(FAKE, 0, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, 128,
+                                  64, None, 0.088, FAKE, 0, None) == E.SWA_E_DTYPE

@@ -883,3 +883,158 @@ def test_unified_decode_matches_oracle_and_two_pool(P):
                         m_unified, 128, ub.sinks)
         check(out, want, TOL["bf16"], f"unified decode layer {layer}")
         assert torch.equal(out, out2)
+
+
+# ---------------------------------------------------------------------------
+# attention variants: single-pool windowed mode, chunked local attention,
+# per-request SWA ring
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,W,P", [(8, 128, 16), (1, 20, 1), (16, 300, 64)])
+def test_single_pool_windowed_decode(G, W, P):
+    say(f"single-pool decode G={G} W={W} P={P}")
+    wl = WL.decode_workload(f"sp{G}_{W}", 81, [1, 40, 300, 1000, 129, 2000], 2 * G, 2, W, P, "bf16", "bf16",
+                            with_store=True, two_pools=False)
+    assert wl.full_to_swa is None
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    splits = None if W <= 255 else 3
+    check(run_decode(dw, "f32", num_splits=splits), oracle_decode(wl), TOL["bf16"], "single-pool decode")
+
+
+def test_single_pool_windowed_extend():
+    say("single-pool extend")
+    wl = WL.extend_workload("spx", 82, [0, 100, 700], [300, 33, 129], 16, 2, 128, 16, two_pools=False)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    check(run_extend(dw, "f32"), oracle_extend(wl), TOL["bf16"], "single-pool extend")
+
+
+@pytest.mark.parametrize("C,W", [(64, -1), (256, -1), (1000, -1), (100, 128), (1, -1)])
+def test_chunked_local_decode(C, W):
+    """Chunked local decode is swa_decode over the chunked window table."""
+    from sliding_window_attention_swa_amd import swa
+    say(f"chunked decode C={C} W={W}")
+    lens = [1, 40, 256, 257, 1000, 1001, 2048, 2100]
+    wl = WL.decode_workload(f"ch{C}_{W}", 83, lens, 16, 2, W, 16, "bf16", "bf16", two_pools=False)
+    dw = DeviceWorkload(wl)
+    B = wl.batch
+    table = torch.empty(B * min(C, 2100), dtype=torch.int32, device="cuda")
+    indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window_chunked(dw.index, W, C, table, indptr, use_map=False)
+    want_t = O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, None, W, chunk=C)
+    torch.cuda.synchronize()
+    assert np.array_equal(indptr.cpu().numpy(), want_t[1])
+    assert np.array_equal(table.cpu().numpy()[:want_t[1][-1]], want_t[0])
+    keys = min(C, W + 1) if W >= 0 else C
+    if keys <= 256:
+        win, splits, ws = keys - 1, 1, None
+    else:
+        win = -1
+        splits, ws_bytes = swa.swa_decode_plan(B, wl.q_heads, wl.kv_heads, wl.head_dim, -1, keys)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, wl.q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    swa.swa_decode(dw.q, dw.layer, dw.index, win, out, sinks=dw.sinks, slot_table=table, table_indptr=indptr,
+                   num_splits=splits, workspace=ws, use_map=False)
+    torch.cuda.synchronize()
+    check(out, oracle_decode(wl, chunk=C), TOL["bf16"], f"chunked decode C={C}")
+
+
+CHUNKED_EXTEND = [
+    # (G, W, C, prefix_lens, chunk_lens)
+    (8, -1, 16, [0, 100, 37], [300, 33, 129]),
+    (8, -1, 100, [0, 250, 1000], [700, 129, 64]),
+    (8, 128, 48, [0, 300], [400, 77]),
+    (1, -1, 64, [10, 0], [200, 150]),
+    (16, -1, 80, [0, 90], [260, 70]),
+    (8, -1, 4096, [0, 4000], [1100, 300]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CHUNKED_EXTEND)))
+def test_chunked_local_extend(case):
+    G, W, C, pre, new = CHUNKED_EXTEND[case]
+    say(f"chunked extend G={G} W={W} C={C}")
+    wl = WL.extend_workload(f"chx{case}", 84 + case, pre, new, 2 * G, 2, W, 16, two_pools=False)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_extend(dw, "f32", chunk=C)
+    check(out, oracle_extend(wl, chunk=C), TOL["bf16"], f"chunked extend C={C}")
+    bf = run_extend(dw, "bf16", chunk=C)
+    assert np.array_equal(bf16_of(out), device_to_bits(bf))
+
+
+def _ring_pool(rb, R):
+    """The ring pool of a ring batch: every live position's rows at its ring row
+    (placed with the oracle's ring_slot), NaN elsewhere."""
+    rows = rb.request_slots * R
+    pk = np.full((rows, rb.kv_heads, rb.head_dim), NAN_BF16, dtype=np.uint16)
+    pv = pk.copy()
+    for b in range(rb.batch):
+        for n, j in enumerate(range(int(rb.live_lo[b]), int(rb.prefix_lens[b]))):
+            s = O.ring_slot(int(rb.req_pool_idx[b]), j, R)
+            pk[s] = rb.k_rows[b][n]
+            pv[s] = rb.v_rows[b][n]
+    return pk, pv
+
+
+@pytest.mark.parametrize("decode,W,ring,P", [(True, 128, 129, 16), (True, 20, 21, 1), (False, 128, 128 + 300, 64),
+                                             (False, 32, 40, 16)])
+def test_ring_attention(decode, W, ring, P):
+    """Per-request SWA ring: ring locations and the window table are bit-exact,
+    the new rows land in the ring, and attention matches the oracle over the
+    same ring layout."""
+    from sliding_window_attention_swa_amd import swa
+    say(f"ring decode={decode} W={W} ring={ring} P={P}")
+    if decode:
+        rb = WL.ring_batch(f"rd{W}", 91, [0, 5, 300, 1000, 128, 129], [1] * 6, 16, 2, W)
+    else:
+        # each request's step spans min(prefix, W) + (ring - W) <= ring positions: no wrap
+        rb = WL.ring_batch(f"rx{W}", 92, [0, 40, 700], [ring - W] * 3, 16, 2, W)
+    R = O.ring_rows(ring, P)
+    B, total = rb.batch, int((rb.seq_lens - rb.prefix_lens).sum())
+    pk, pv = _ring_pool(rb, R)
+    d_rows = torch.from_numpy(rb.req_pool_idx).cuda()
+    d_lens = torch.from_numpy(rb.seq_lens).cuda()
+    d_pre = torch.from_numpy(rb.prefix_lens).cuda()
+    stride = int(rb.seq_lens.max())
+    # where the new positions go
+    locs = torch.empty(total, dtype=torch.int64, device="cuda")
+    swa.swa_ring_locs(d_rows, d_lens, rb.request_slots, R, locs, prefix_lens=None if decode else d_pre)
+    want_locs = np.concatenate([[O.ring_slot(int(rb.req_pool_idx[b]), j, R)
+                                 for j in range(int(rb.prefix_lens[b]), int(rb.seq_lens[b]))] for b in range(B)])
+    # the window table
+    ring_r2t = O.ring_req_to_token(rb.request_slots, stride, R)
+    want_t = O.window_table(ring_r2t, rb.req_pool_idx, rb.seq_lens, None, W,
+                            prefix_lens=None if decode else rb.prefix_lens)
+    table = torch.empty(int(want_t[1][-1]) + 5, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window_ring(d_rows, d_lens, rb.request_slots, stride, R, W, table, indptr,
+                                  prefix_lens=None if decode else d_pre)
+    torch.cuda.synchronize()
+    assert np.array_equal(locs.cpu().numpy(), want_locs)
+    assert np.array_equal(indptr.cpu().numpy(), want_t[1])
+    assert np.array_equal(table.cpu().numpy()[:want_t[1][-1]], want_t[0])
+    # store the new rows through the ring, then attend
+    k = bits_to_device(pk, "bf16")
+    v = bits_to_device(pv, "bf16")
+    layer = swa.KvLayer(k, v)
+    swa.swa_kv_store(layer, locs, bits_to_device(rb.new_k, "bf16"), bits_to_device(rb.new_v, "bf16"))
+    pk2, pv2 = O.kv_store(pk, pv, want_locs, rb.new_k, rb.new_v, "bf16", "bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(device_to_bits(k), pk2) and np.array_equal(device_to_bits(v), pv2)
+    ix = swa.IndexTables(torch.from_numpy(ring_r2t.astype(np.int32)).cuda(), d_rows, d_lens, None, P)
+    q = bits_to_device(rb.q, "bf16")
+    sinks = torch.from_numpy(rb.sinks).cuda()
+    out = torch.empty((total, rb.q_heads, rb.head_dim), dtype=torch.float32, device="cuda")
+    if decode:
+        swa.swa_decode(q, layer, ix, W, out, sinks=sinks, slot_table=table, table_indptr=indptr, use_map=False)
+        want = O.decode(rb.q, "bf16", pk2, pv2, "bf16", ring_r2t, rb.req_pool_idx, rb.seq_lens, None, W, rb.sinks)
+    else:
+        qo = np.concatenate([[0], np.cumsum(rb.seq_lens - rb.prefix_lens)]).astype(np.int32)
+        swa.swa_extend(q, torch.from_numpy(qo).cuda(), d_pre, layer, ix, W, out, sinks=sinks, slot_table=table,
+                       table_indptr=indptr, use_map=False)
+        want = O.extend(rb.q, "bf16", qo, rb.prefix_lens, pk2, pv2, "bf16", ring_r2t, rb.req_pool_idx, rb.seq_lens,
+                        None, W, rb.sinks)
+    torch.cuda.synchronize()
+    check(out, want, TOL["bf16"], "ring attention")
