@@ -46,14 +46,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return u;
 }
 
-// Sum of the two bf16 values of a packed pair, in f32.  The softmax weights
-// that enter P.V are rounded to bf16; summing the same rounded weights for the
+// acc + both bf16 values of a packed pair, in f32.  The softmax weights that
+// enter P.V are rounded to bf16; summing the same rounded weights for the
 // normaliser makes the output an exact convex combination of V rows (plus the
 // sink), so the rounding only perturbs relative weights: a query with few keys,
 // whose output is as large as a V row, then carries no more error than one
-// with many.
-__device__ __forceinline__ float bf16x2_sum(uint32_t u) {
-  return __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+// with many.  One dot product against (1, 1) (v_dot2c_f32_bf16; the products
+// are exact).
+__device__ __forceinline__ float bf16x2_acc(uint32_t u, float acc) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  bf16x2_v a, ones;
+  const uint32_t one2 = 0x3F803F80u;
+  __builtin_memcpy(&a, &u, 4);
+  __builtin_memcpy(&ones, &one2, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(a, ones, acc, false);
+}
+
+// Reductions over the four 16-lane rows of a wavefront (lanes l, l^16, l^32,
+// l^48).  gfx950's row swaps do it in the VALU: v_permlane16_swap pairs rows
+// (0, 1) and (2, 3), v_permlane32_swap the two halves, so no LDS round trip
+// (and no wait on LDS loads issued before it) sits in the softmax.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane r supplies the LDS

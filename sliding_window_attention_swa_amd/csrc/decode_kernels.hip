@@ -115,16 +115,8 @@ __device__ __forceinline__ int64_t safe_slot(int32_t s, int64_t rows) {
   return (s < 0 || s >= rows) ? 0 : static_cast<int64_t>(s);
 }
 
-__device__ __forceinline__ float wave_max_q(float x) {  // over the 4 lane groups (lanes l, l^16, l^32, l^48)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float wave_sum_q(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
+__device__ __forceinline__ float wave_max_q(float x) { return rows_max(x); }  // lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float wave_sum_q(float x) { return rows_sum(x); }
 __device__ __forceinline__ float wave_sum_all(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -452,7 +444,7 @@ __device__ __forceinline__ void stream_compute(const DecodeParams &p, const Stre
     uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
                       pack_bf16x2_hw(pv[6], pv[7])};
     // the normaliser sums the rounded weights that enter P.V
-    l_run = l_run * alpha + ((bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3])));
+    l_run = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run * alpha))));
     __builtin_memcpy(&pop, u4, 16);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
@@ -729,7 +721,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
       uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
                         pack_bf16x2_hw(pv[6], pv[7])};
       // the normaliser sums the rounded weights that enter P.V
-      l_run += (bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3]));
+      l_run = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run))));
       __builtin_memcpy(&pop[u2], u4, 16);
     }
     // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1), each pair's V rows

@@ -80,16 +80,8 @@ __device__ __forceinline__ int32_t first_key(int32_t i, int32_t window, int32_t 
   return lo;
 }
 
-__device__ __forceinline__ float wave_max_q(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float wave_sum_q(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
+__device__ __forceinline__ float wave_max_q(float x) { return rows_max(x); }  // lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float wave_sum_q(float x) { return rows_sum(x); }
 
 // Workgroup barrier for LDS data only.  __syncthreads() also fences global
 // memory, i.e. waits for every outstanding global load and store of the wave;
@@ -299,8 +291,7 @@ __device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const
       uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][ja][0], sacc[m][ja][1]), pack_bf16x2_hw(sacc[m][ja][2], sacc[m][ja][3]),
                         second ? pack_bf16x2_hw(sacc[m][jb][0], sacc[m][jb][1]) : 0u,
                         second ? pack_bf16x2_hw(sacc[m][jb][2], sacc[m][jb][3]) : 0u};
-      const float ps = (bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3]));
-      l_run[m] = u == 0 ? ps : l_run[m] + ps;
+      l_run[m] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], u == 0 ? 0.f : l_run[m]))));
       __builtin_memcpy(&pop[m], u4, 16);
     }
     const uint16_t *va = vtile + slot[ja] * 16 * kVRow + voff;
@@ -440,7 +431,7 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
                             pack_bf16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
                             second ? pack_bf16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
                             second ? pack_bf16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
-          l_run[m] += (bf16x2_sum(u4[0]) + bf16x2_sum(u4[1])) + (bf16x2_sum(u4[2]) + bf16x2_sum(u4[3]));
+          l_run[m] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[m]))));
           __builtin_memcpy(&pop[m], u4, 16);
         }
 #pragma unroll
