@@ -165,6 +165,13 @@ swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, i
                              int32_t window, int64_t max_seq_len, int32_t *num_splits,
                              size_t *workspace_bytes);
 
+/* [host] Workspace bytes that suffice for every split count swa_decode_plan
+ * can return for this batch, q_heads and head_dim when no request has more than
+ * max_keys keys (its split count is capped at ceil(max_keys / 512)): an upper
+ * bound for callers that size the workspace once.  0 when no split is needed
+ * or the arguments are out of range. */
+size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim, int32_t max_keys);
+
 /* ---------------------------------------------------------------------------
  * decode — one query per request at position i = seq_lens[b] - 1 ([SWA]
  * opening paragraph: each query sees the most recent window; 实现: W excludes

@@ -169,6 +169,14 @@ swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, i
   return SWA_OK;
 }
 
+size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim, int32_t max_keys) {
+  if (batch <= 0 || q_heads <= 0 || head_dim != kHeadDim || max_keys <= 0) return 0;
+  int64_t splits = (static_cast<int64_t>(max_keys) + kMinKeysPerSplit - 1) / kMinKeysPerSplit;  // the planner's cap
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(batch) * q_heads * splits * (2 + kHeadDim) * sizeof(float);
+}
+
 }  // extern "C"
 
 namespace {

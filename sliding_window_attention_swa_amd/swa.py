@@ -30,7 +30,7 @@ EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_
            "swa_evict_workspace_bytes", "swa_evict", "swa_alloc_pages_needed", "swa_alloc_extend",
            "swa_alloc_decode", "swa_unified_pool_bytes", "swa_unified_layer_views", "swa_translate_kernel_ids",
            "swa_translate_window_unified", "swa_translate_window_chunked", "swa_extend_chunked",
-           "swa_translate_window_ring", "swa_ring_locs", "swa_status_string")
+           "swa_translate_window_ring", "swa_ring_locs", "swa_decode_workspace_bytes", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -108,6 +108,7 @@ _sig = {
                                   ctypes.POINTER(IndexStruct), _p, _p, _i64, _i32, _i32, _p, _f32, _p, _i32, _p]),
     "swa_translate_window_ring": (_i32, [ctypes.POINTER(IndexStruct), _i64, _i32, _i32, _p, _p, _p, _i64, _p]),
     "swa_ring_locs": (_i32, [ctypes.POINTER(IndexStruct), _i64, _p, _p, _i64, _p]),
+    "swa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():

@@ -360,3 +360,15 @@ def test_variant_argument_errors(swa):
                                   -1, None, 0.088, FAKE, 0, None) == E.SWA_E_ARG
     assert lib.swa_extend_chunked(FAKE, 0, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, 128,
                                   64, None, 0.088, FAKE, 0, None) == E.SWA_E_DTYPE
+
+
+def test_decode_workspace_bytes_bounds_every_plan(swa):
+    lib = swa.lib
+    for B, Hq, Hkv, keys in ((32, 64, 4, 32768), (1, 8, 8, 512), (3, 16, 2, 5000), (256, 64, 8, 65536)):
+        bound = lib.swa_decode_workspace_bytes(B, Hq, 128, keys)
+        for T in (t for t in (1, 100, 511, 512, 513, keys // 2, keys) if t <= keys):
+            ns, ws = ctypes.c_int32(), ctypes.c_size_t()
+            assert lib.swa_decode_plan(B, Hq, Hkv, 128, -1, T, ctypes.byref(ns), ctypes.byref(ws)) == swa.SWA_OK
+            assert ws.value <= bound
+    assert lib.swa_decode_workspace_bytes(4, 8, 128, 512) == 0          # one split: no workspace
+    assert lib.swa_decode_workspace_bytes(4, 8, 64, 5000) == 0          # head_dim other than 128
