@@ -801,9 +801,10 @@ __device__ __forceinline__ void f32_issue(const DecodeParams &p, int32_t slot, i
   for (int i = 0; i < 8; ++i) r.v[i] = vp[i];
 }
 
-template <int G, bool OUT_BF16>
-__global__ void __launch_bounds__(kF32Waves * 64) decode_f32_kernel(DecodeParams p) {
-  constexpr int NW = kF32Waves;
+// NW wavefronts per workgroup: 4, or 8 when the grid is too small to fill the
+// chip (each wavefront then walks half as many chunks of the window).
+template <int G, bool OUT_BF16, int NW>
+__global__ void __launch_bounds__(NW * 64) decode_f32_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float q_lds[kMaxG * kD];
   // per-wavefront V chunk during the loop; the cross-wavefront partials after it
   __shared__ __attribute__((aligned(16))) float big[NW * kMaxG * kD];
@@ -897,14 +898,14 @@ __global__ void __launch_bounds__(kF32Waves * 64) decode_f32_kernel(DecodeParams
         dot += __shfl_xor(dot, 2);
         const float sc = valid ? dot * p.scale2 : -INFINITY;
         float cm = sc;
-#pragma unroll
-        for (int o = 4; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+        cm = fmaxf(cm, __shfl_xor(cm, 4));
+        cm = rows_max(fmaxf(cm, __shfl_xor(cm, 8)));
         const float m_new = fmaxf(m_run[hh], cm);
         const float alpha = exp2f(m_run[hh] - m_new);
         const float pj = exp2f(sc - m_new);
         float ps = pj;
-#pragma unroll
-        for (int o = 4; o < 64; o <<= 1) ps += __shfl_xor(ps, o);
+        ps += __shfl_xor(ps, 4);
+        ps = rows_sum(ps + __shfl_xor(ps, 8));
         m_run[hh] = m_new;
         l_run[hh] = l_run[hh] * alpha + ps;
         acc[hh].x *= alpha;
@@ -977,15 +978,23 @@ __global__ void __launch_bounds__(kD) decode_merge_kernel(DecodeParams p) {
 
 template <bool OUT_BF16>
 hipError_t launch_f32(const DecodeParams &p, dim3 grid, hipStream_t stream) {
-  const dim3 block(kF32Waves * 64);
+  // fewer workgroups than half the CUs: twice the wavefronts per workgroup
+  const bool wide = static_cast<int64_t>(grid.x) * grid.y * grid.z < 128;
+  const dim3 block((wide ? 8 : kF32Waves) * 64);
+#define SWA_F32_LAUNCH(GG)                                                                                  \
+  if (wide)                                                                                                 \
+    hipLaunchKernelGGL((decode_f32_kernel<GG, OUT_BF16, 8>), grid, block, 0, stream, p);                    \
+  else                                                                                                      \
+    hipLaunchKernelGGL((decode_f32_kernel<GG, OUT_BF16, kF32Waves>), grid, block, 0, stream, p);
   switch (p.group) {  // validated on the host: 1, 2, 4, 8 or 16
-    case 1: hipLaunchKernelGGL((decode_f32_kernel<1, OUT_BF16>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_f32_kernel<2, OUT_BF16>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_f32_kernel<4, OUT_BF16>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_f32_kernel<8, OUT_BF16>), grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((decode_f32_kernel<16, OUT_BF16>), grid, block, 0, stream, p); break;
+    case 1: SWA_F32_LAUNCH(1) break;
+    case 2: SWA_F32_LAUNCH(2) break;
+    case 4: SWA_F32_LAUNCH(4) break;
+    case 8: SWA_F32_LAUNCH(8) break;
+    case 16: SWA_F32_LAUNCH(16) break;
     default: return hipErrorInvalidValue;
   }
+#undef SWA_F32_LAUNCH
   return hipGetLastError();
 }
 
