@@ -188,7 +188,9 @@ size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_d
  * (SWA_F32, or SWA_BF16 = the f32 result rounded to nearest even).
  * Supported: head_dim 128; q_dtype f32 with f32 K/V; q_dtype bf16 with bf16 or
  * e4m3 K/V; q_heads / kv_heads in {1, 2, 4, 8, 16}.
- * num_splits and workspace come from swa_decode_plan for the same shape. */
+ * num_splits and workspace come from swa_decode_plan for the same shape.
+ * An empty batch (idx->batch == 0) launches nothing and returns SWA_OK after
+ * the same argument checks; q, out and the workspace may then be NULL. */
 swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
                         const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
                         int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
@@ -208,7 +210,8 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
  * current token is attended from these rows converted to the pool format
  * exactly as stored.  Supported: windowed layers with 0 <= window <= 255,
  * bf16 q, bf16 or e4m3 pools, new_dtype SWA_BF16; other cases return
- * SWA_E_DTYPE / SWA_E_SHAPE (use the two calls). */
+ * SWA_E_DTYPE / SWA_E_SHAPE (use the two calls).  An empty batch launches
+ * nothing; q, out, loc, k_new and v_new may then be NULL. */
 swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
                               const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
                               int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
@@ -225,7 +228,9 @@ swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, c
  * and out, i.e. qo_indptr[batch].  Keys come from the window table built by
  * swa_translate_window(prefix_lens) when table_indptr is given, else from
  * req_to_token directly.  Supported: head_dim 128, bf16 q with bf16 K/V,
- * q_heads / kv_heads in {1, 2, 4, 8, 16}. */
+ * q_heads / kv_heads in {1, 2, 4, 8, 16}.  Requests with no new tokens
+ * (qo_indptr[b] == qo_indptr[b+1]) contribute nothing; an empty batch or
+ * total_q == 0 launches nothing, and q and out may then be NULL. */
 swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
                         const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
                         const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,

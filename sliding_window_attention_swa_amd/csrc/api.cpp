@@ -181,17 +181,20 @@ size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_d
 
 namespace {
 
-// Checks and launch shared by swa_decode and swa_decode_store (loc == null: no store).
+// Checks and launch shared by swa_decode and swa_decode_store (fused: with the
+// store).  An empty batch passes the same checks, may leave q, out, loc and the
+// new rows NULL, and launches nothing.
 swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
                          const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
                          int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
-                         int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                         int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes, bool fused,
                          const int64_t *loc, const void *k_new, const void *v_new, hipStream_t stream) {
   swa_status_t st = check_layer(layer);
   if (st != SWA_OK) return st;
   st = check_index(idx, table_indptr == nullptr);
   if (st != SWA_OK) return st;
-  if (!q || !out || window < -1 || num_splits < 1 || num_splits > kMaxSplits) return SWA_E_ARG;
+  const bool empty = idx->batch == 0;
+  if ((!empty && (!q || !out)) || window < -1 || num_splits < 1 || num_splits > kMaxSplits) return SWA_E_ARG;
   if (!std::isfinite(sm_scale)) return SWA_E_ARG;
   if (table_indptr && (!slot_table || table_capacity < 0)) return SWA_E_ARG;
   if (layer->head_dim != kHeadDim) return SWA_E_SHAPE;
@@ -202,12 +205,13 @@ swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const 
   if (!f32_path && !mfma_path) return SWA_E_DTYPE;
   if (out_dtype != SWA_F32 && out_dtype != SWA_BF16) return SWA_E_DTYPE;
   if (!aligned16(q) || !aligned16(out)) return SWA_E_ARG;
-  if (num_splits > 1) {
+  if (num_splits > 1 && !empty) {
     const size_t need = static_cast<size_t>(idx->batch) * q_heads * num_splits * (2 + kHeadDim) * sizeof(float);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SWA_E_WORKSPACE;
   }
-  if (loc) {
-    if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return SWA_E_ARG;
+  if (fused) {
+    if (!empty && (!loc || !k_new || !v_new)) return SWA_E_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return SWA_E_ARG;
     if (!mfma_path) return SWA_E_DTYPE;
     if (window < 0 || window > swa::kMaxFusedWindow || num_splits != 1) return SWA_E_SHAPE;
   }
@@ -243,8 +247,8 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
                         int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   return decode_impl(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity, window, sinks,
-                     sm_scale, out, out_dtype, num_splits, workspace, workspace_bytes, nullptr, nullptr, nullptr,
-                     stream);
+                     sm_scale, out, out_dtype, num_splits, workspace, workspace_bytes, false, nullptr, nullptr,
+                     nullptr, stream);
 }
 
 swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
@@ -252,10 +256,9 @@ swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, c
                               int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
                               const int64_t *loc, const void *k_new, const void *v_new, int32_t new_dtype,
                               void *out, int32_t out_dtype, hipStream_t stream) {
-  if (!loc) return SWA_E_ARG;
   if (new_dtype != SWA_BF16) return SWA_E_DTYPE;
   return decode_impl(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity, window, sinks,
-                     sm_scale, out, out_dtype, 1, nullptr, 0, loc, k_new, v_new, stream);
+                     sm_scale, out, out_dtype, 1, nullptr, 0, true, loc, k_new, v_new, stream);
 }
 
 namespace {

@@ -114,6 +114,27 @@ def test_decode_argument_errors(swa):
     assert decode(swa, ly, bad_ix, table=None, indptr=None, window=-1) == E.SWA_E_ARG
 
 
+def test_empty_batch_launches_nothing(swa):
+    """Batch 0 (and an extend with no new tokens) passes the argument checks with
+    NULL buffers and returns before any device call, so it runs without a GPU."""
+    E, lib = swa, swa.lib
+    ly = layer(swa)
+    empty = index(swa, batch=0)
+    assert decode(swa, ly, empty, q=None, out=None) == E.SWA_OK
+    assert decode(swa, ly, empty, q=None, out=None, splits=4) == E.SWA_OK   # no workspace for no requests
+    assert decode(swa, ly, empty, window=-2) == E.SWA_E_ARG                  # the checks still apply
+    assert decode(swa, layer(swa, head_dim=64), empty) == E.SWA_E_SHAPE
+    assert lib.swa_decode_store(None, 1, 64, ctypes.byref(ly), ctypes.byref(empty), FAKE, FAKE, 0, 128, None, 0.088,
+                                None, None, None, 1, None, 0, None) == E.SWA_OK
+    assert lib.swa_decode_store(None, 1, 64, ctypes.byref(ly), ctypes.byref(empty), FAKE, FAKE, 0, 300, None, 0.088,
+                                None, None, None, 1, None, 0, None) == E.SWA_E_SHAPE
+    for ix, qo, pre in ((empty, None, None), (index(swa), FAKE, FAKE)):
+        assert lib.swa_extend(None, 1, 64, qo, pre, 0, ctypes.byref(ly), ctypes.byref(ix), FAKE, FAKE, 1000, 128,
+                              None, 0.088, None, 0, None) == E.SWA_OK
+        assert lib.swa_extend_chunked(None, 1, 64, qo, pre, 0, ctypes.byref(ly), ctypes.byref(ix), FAKE, FAKE, 1000,
+                                      128, 64, None, 0.088, None, 0, None) == E.SWA_OK
+
+
 def test_extend_argument_errors(swa):
     E = swa
     ly, ix = layer(swa), index(swa)

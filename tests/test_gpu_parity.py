@@ -184,6 +184,11 @@ DECODE_CASES = {
     "bf16_w0": ([1, 9, 500], 16, 2, 0, 16, "bf16", "bf16", True),
     "bf16_w1": ([1, 9, 500], 16, 2, 1, 16, "bf16", "bf16", True),
     "bf16_w300_p64": ([1, 299, 300, 301, 302, 1500], 16, 2, 300, 64, "bf16", "bf16", True),
+    # the largest window the one-split window kernel holds (256 keys), and the first past it
+    "bf16_w255": ([1, 200, 255, 256, 257, 1200], 16, 2, 255, 16, "bf16", "bf16", True),
+    "bf16_w256": ([1, 256, 257, 258, 1200], 16, 2, 256, 16, "bf16", "bf16", True),
+    "e4m3_w255_g16": ([256, 2000], 32, 2, 255, 64, "bf16", "e4m3", True),
+    "f32_g8_w255": ([1, 256, 300], 16, 2, 255, 16, "f32", "f32", True),
     "e4m3_g8": ([1, 2, 129, 130, 1000], 16, 2, 128, 16, "bf16", "e4m3", True),
     "e4m3_g16_nosink": ([5, 600], 32, 2, 128, 64, "bf16", "e4m3", False),
 }
@@ -209,7 +214,7 @@ def test_decode_small(name):
 
 
 FUSED_CASES = ["bf16_g8", "bf16_g8_nosink", "bf16_g1", "bf16_g2", "bf16_g4", "bf16_g16", "bf16_w0", "bf16_w1",
-               "e4m3_g8", "e4m3_g16_nosink"]
+               "e4m3_g8", "e4m3_g16_nosink", "bf16_w255", "e4m3_w255_g16"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
@@ -452,7 +457,35 @@ EXTEND_CASES = {
     "g2": ([20, 300], [40, 90], 4, 2, 128, 16, True),
     "g4": ([20, 300], [40, 90], 8, 2, 128, 16, True),
     "g16": ([20, 300], [40, 90], 32, 2, 128, 16, True),
+    # ragged batches with requests that add no tokens (one of them with no prefix either)
+    "g8_ragged_empty": ([300, 50, 0, 7, 129], [40, 0, 1, 0, 64], 16, 2, 128, 16, True),
+    "g4_empty_first": ([64, 0, 500], [0, 0, 200], 8, 2, 128, 16, False),
+    "g8_one_token": ([0], [1], 16, 2, 128, 16, True),
+    "g8_w255": ([100, 400], [300, 70], 16, 2, 255, 16, True),
 }
+
+
+def test_empty_launches_write_nothing():
+    """An extend whose requests add no tokens, and decodes of an empty batch
+    (plain and with the fused store): status OK, pools untouched."""
+    from sliding_window_attention_swa_amd import swa
+    say("empty launches")
+    wl = WL.extend_workload("noq", 47, [30, 200], [0, 0], 16, 2, 128, 16)
+    dw = DeviceWorkload(wl)
+    k0, v0 = dw.k.clone(), dw.v.clone()
+    run_store(dw)
+    assert run_extend(dw, "f32").shape[0] == 0
+    assert run_extend(dw, "bf16", chunk=64).shape[0] == 0
+    empty = swa.IndexTables(dw.r2t, dw.rows[:0], dw.lens[:0], dw.map, 16)
+    out = torch.empty((0, 16, 128), dtype=torch.float32, device="cuda")
+    swa.swa_decode(dw.q, dw.layer, empty, 128, out, sinks=dw.sinks)
+    swa.swa_decode(dw.q, dw.layer, empty, -1, out, num_splits=4)
+    rows = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    swa.swa_decode_store(dw.q, dw.layer, empty, 128, out, torch.zeros(0, dtype=torch.int64, device="cuda"), rows,
+                         rows, sinks=dw.sinks)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.k.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(dw.v.view(torch.int16), v0.view(torch.int16))
 
 
 @pytest.mark.parametrize("name", list(EXTEND_CASES))
