@@ -306,6 +306,30 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 &x, uint4 (&out)[2]) 
   out[1] = make_uint4(u[4], u[5], u[6], u[7]);
 }
 
+// This lane's raw bf16 pieces of request b's new K and V rows (kv head g), in
+// the lane layout of Layout<KV> (bf16 pieces as they are; each e4m3 piece from
+// two bf16 pieces).
+template <typename KV>
+__device__ __forceinline__ void load_new_rows(const DecodeParams &p, int32_t b, int32_t g, int32_t lane,
+                                              uint4 (&kn_raw)[4], uint4 (&vn_raw)[2]) {
+  const int32_t lq = lane >> 4;
+  const uint16_t *krow = p.k_new + (static_cast<int64_t>(b) * p.kv_heads + g) * kD;
+  const uint16_t *vrow = p.v_new + (static_cast<int64_t>(b) * p.kv_heads + g) * kD;
+  if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kn_raw[c] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq));
+    vn_raw[0] = *reinterpret_cast<const uint4 *>(vrow + Layout<KV>::v_off(lane));
+  } else {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      kn_raw[2 * c] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq));
+      kn_raw[2 * c + 1] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq) + 8);
+    }
+    vn_raw[0] = *reinterpret_cast<const uint4 *>(vrow + Layout<KV>::v_off(lane));
+    vn_raw[1] = *reinterpret_cast<const uint4 *>(vrow + Layout<KV>::v_off(lane) + 8);
+  }
+}
+
 // Component-wise select (a ternary on the vector struct goes through memory).
 __device__ __forceinline__ uint4 sel4(bool c, const uint4 &a, const uint4 &b) {
   return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
@@ -628,27 +652,18 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   uint4 qraw[4];
   load_q<KV>(p, b, g * G + (kr < G ? kr : 0), lq, qraw);
   // Fused store: the current token (window key n - 1) is attended from the new
-  // rows, converted to the pool format exactly as they are stored at the end.
-  // A lane's piece depends only on its lane position (lanes of a group read the
-  // same addresses); the raw bf16 pieces are loaded by every lane, without a
-  // branch, and converted only by the wavefront that owns key n - 1.
+  // rows, converted to the pool format exactly as they are stored.  Only the
+  // wavefront that holds key n - 1 needs them.  It is known once the window
+  // length is; the wavefront that holds it in a full window (n = W + 1, every
+  // request at least W + 1 long) loads them now, with the other first-hop
+  // loads, and another owner loads them after the window length arrives.
+  const int32_t wu = __builtin_amdgcn_readfirstlane(w);  // w, known to the compiler as wave-uniform
+  const int32_t full_owner = (p.window >> 4) % kWinWaves;
   uint4 kn_raw[4], vn_raw[2];
+  int64_t new_loc = -1;
   if constexpr (FUSED) {
-    const uint16_t *krow = p.k_new + (static_cast<int64_t>(b) * p.kv_heads + g) * kD;
-    const uint16_t *vrow_new = p.v_new + (static_cast<int64_t>(b) * p.kv_heads + g) * kD;
-    if constexpr (sizeof(KV) == 2) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kn_raw[c] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq));
-      vn_raw[0] = *reinterpret_cast<const uint4 *>(vrow_new + Layout<KV>::v_off(lane));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        kn_raw[2 * c] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq));
-        kn_raw[2 * c + 1] = *reinterpret_cast<const uint4 *>(krow + Layout<KV>::k_off(c, lq) + 8);
-      }
-      vn_raw[0] = *reinterpret_cast<const uint4 *>(vrow_new + Layout<KV>::v_off(lane));
-      vn_raw[1] = *reinterpret_cast<const uint4 *>(vrow_new + Layout<KV>::v_off(lane) + 8);
-    }
+    new_loc = p.new_loc[b];
+    if (wu == full_owner) load_new_rows<KV>(p, b, g, lane, kn_raw, vn_raw);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -658,6 +673,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   const int32_t nblk = (n + 15) >> 4;  // <= kWinWaves * MAXB for this instantiation
   const bool spec_ok = p.indptr && p.capacity > 0 && src == p.table + spec_base;
   const int32_t owner = ((n > 0 ? n - 1 : 0) >> 4) % kWinWaves;  // wavefront holding key n - 1
+  const int32_t last = n - 1;
   uint4 knew[kKL], vnew;  // (fused store) the new rows in the pool format, owner wave only
 
   f32x4_t acc[8];
@@ -667,7 +683,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   float l_run = 0.f;
   uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * 32 * kSVRow;
 
-  if (w < nblk) {  // wave-uniform: this wavefront owns at least one block
+  if (wu < nblk) {  // this wavefront owns at least one block
     // All row loads are unconditional (no control flow between them, so none
     // of them waits for another); rows of keys past the end are masked out
     // below.  The phases are fenced with scheduling barriers so that the
@@ -680,6 +696,10 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
         sl[u] = src[key < n ? key : 16 * w];
       }
     }
+    if constexpr (FUSED) {
+      // a short window's owner: the new rows go out ahead of its K/V rows
+      if (wu == owner && owner != full_owner) load_new_rows<KV>(p, b, g, lane, kn_raw, vn_raw);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // every K row first, then every V row: the scores only wait for K
     uint4 kraw[MAXB][kKL], vraw[MAXB][kVL];
@@ -689,17 +709,23 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     for (int u = 0; u < MAXB; ++u) load_v<KV>(p, sl[u], g, lane, vraw[u]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FUSED) {
-      if (w == owner) {  // wave-uniform
+      // The owner converts the new rows (they were issued before its K/V rows,
+      // so this waits for them only) and stores its kv head's slice of them at
+      // once: no load of this wavefront follows, so no later wait includes the
+      // stores.  No other workgroup reads this slice, and the rows this
+      // workgroup reads there belong to masked keys.  The new rows replace
+      // key n - 1's K just before its block's scores and its V just before the
+      // block is staged, so nothing here waits for the pool rows.
+      if (wu == owner) {
         new_pieces<KV>(kn_raw, vn_raw, knew, vnew);
-        const int32_t last = n - 1;
+        if (new_loc >= 0 && new_loc < p.rows) {
+          KV *kdst = static_cast<KV *>(const_cast<void *>(p.k)) + row_elem(new_loc, p.kv_heads, g, kD);
+          KV *vdst = static_cast<KV *>(const_cast<void *>(p.v)) + row_elem(new_loc, p.kv_heads, g, kD);
+          if (kr == 0) {
 #pragma unroll
-        for (int u = 0; u < MAXB; ++u) {
-          const int32_t kb = 16 * (w + kWinWaves * u);
-#pragma unroll
-          for (int c = 0; c < kKL; ++c) kraw[u][c] = sel4(kb + kr == last, knew[c], kraw[u][c]);
-#pragma unroll
-          for (int j = 0; j < kVL; ++j)
-            vraw[u][j] = sel4(kb + Layout<KV>::v_key(j, lane) == last, vnew, vraw[u][j]);
+            for (int c = 0; c < kKL; ++c) *reinterpret_cast<uint4 *>(kdst + Layout<KV>::k_off(c, lq)) = knew[c];
+          }
+          if (Layout<KV>::v_key(0, lane) == 0) *reinterpret_cast<uint4 *>(vdst + Layout<KV>::v_off(lane)) = vnew;
         }
       }
     }
@@ -713,6 +739,12 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     for (int u = 0; u < MAXB; ++u) {
       const int32_t t = w + kWinWaves * u;
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FUSED) {
+        if (wu == owner) {
+#pragma unroll
+          for (int c = 0; c < kKL; ++c) kraw[u][c] = sel4(16 * t + kr == last, knew[c], kraw[u][c]);
+        }
+      }
       bf16x8_t kk[4];
       KvLoad<KV>::to_bf16(kraw[u], kk);
 #pragma unroll
@@ -747,6 +779,17 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
 #pragma unroll
     for (int u2 = 0; u2 < kPairs; ++u2) {
       const int32_t u0 = 2 * u2;
+      if constexpr (FUSED) {
+        if (wu == owner) {
+#pragma unroll
+          for (int u = u0; u < u0 + 2 && u < MAXB; ++u) {
+            const int32_t kb = 16 * (w + kWinWaves * u);
+#pragma unroll
+            for (int j = 0; j < kVL; ++j)
+              vraw[u][j] = sel4(kb + Layout<KV>::v_key(j, lane) == last, vnew, vraw[u][j]);
+          }
+        }
+      }
       v_to_lds<KV>(vraw[u0], vt, lane, 16 * (w + kWinWaves * u0), n);
       if (u0 + 1 < MAXB)
         v_to_lds<KV>(vraw[u0 + 1 < MAXB ? u0 + 1 : u0], vt + 16 * kSVRow, lane, 16 * (w + kWinWaves * (u0 + 1)), n);
@@ -776,20 +819,6 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     }
   }
   __syncthreads();
-  if constexpr (FUSED) {
-    // the owner wavefront stores this kv head's slice of the new row; after every load
-    // (a wait for a load issued after a store would also wait for the store)
-    const int64_t loc = p.new_loc[b];
-    if (w == owner && n > 0 && loc >= 0 && loc < p.rows) {
-      KV *kdst = static_cast<KV *>(const_cast<void *>(p.k)) + row_elem(loc, p.kv_heads, g, kD);
-      KV *vdst = static_cast<KV *>(const_cast<void *>(p.v)) + row_elem(loc, p.kv_heads, g, kD);
-      if (kr == 0) {
-#pragma unroll
-        for (int c = 0; c < kKL; ++c) *reinterpret_cast<uint4 *>(kdst + Layout<KV>::k_off(c, lq)) = knew[c];
-      }
-      if (Layout<KV>::v_key(0, lane) == 0) *reinterpret_cast<uint4 *>(vdst + Layout<KV>::v_off(lane)) = vnew;
-    }
-  }
   merge_waves_and_store<OUT_BF16>(p, kWinWaves, red_m, red_l, red_acc, b, g, 0);
 }
 
