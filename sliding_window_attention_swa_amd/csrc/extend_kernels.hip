@@ -449,53 +449,12 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
   }
 }
 
-// Sink once, normalise, store this lane's query row of every head of the wave.
-template <int MB, bool OUT_BF16>
-__device__ __forceinline__ void store_tile(const ExtendParams &p, f32x4_t (&acc)[MB][8], const float (&m_run)[MB],
-                                           const float (&l_run)[MB], const float (&sink2)[MB], int32_t g,
-                                           int32_t row0, bool qvalid) {
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t w = threadIdx.x >> 6;
-  const int32_t kr = lane & 15;
-  const int32_t lq = lane >> 4;
-  const int32_t G = p.group;
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int32_t hh = w * MB + m;
-    const float l = wave_sum_q(l_run[m]);
-    if (hh >= G || !qvalid) continue;
-    const int32_t h = g * G + hh;
-    float M = m_run[m];
-    float L = l;
-    float a = 1.f;
-    if (p.sinks) {
-      const float sig2 = sink2[m];
-      const float Mn = fmaxf(M, sig2);
-      a = __builtin_amdgcn_exp2f(M - Mn);
-      L = L * a + __builtin_amdgcn_exp2f(sig2 - Mn);
-    }
-    const float inv = L > 0.f ? a / L : 0.f;
-    const int64_t obase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + h) * kD + 4 * lq;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const float o0 = acc[m][n][0] * inv, o1 = acc[m][n][1] * inv, o2 = acc[m][n][2] * inv,
-                  o3 = acc[m][n][3] * inv;
-      if (OUT_BF16) {
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + obase + 16 * n) =
-            make_uint2(pack_bf16x2_hw(o0, o1), pack_bf16x2_hw(o2, o3));
-      } else {
-        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + obase + 16 * n) = make_float4(o0, o1, o2, o3);
-      }
-    }
-  }
-}
-
 // A finished tile's normalised output for this lane, packed for its stores.
 template <int MB, bool OUT_BF16>
 struct TileOut;
 template <int MB>
-struct TileOut<MB, true> {
-  uint2 v[MB][8];
+struct TileOut<MB, true> {  // bf16: 8 consecutive dims per lane and block pair (see finish_tile)
+  uint4 v[MB][4];
 };
 template <int MB>
 struct TileOut<MB, false> {
@@ -517,21 +476,36 @@ __device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t
       L = L * a + __builtin_amdgcn_exp2f(sink2[m] - Mn);
     }
     const float inv = L > 0.f ? a / L : 0.f;
+    if constexpr (OUT_BF16) {
+      // Lane (query kr, group lq) holds dims 16n + 4lq + 0..3 of block n.  For
+      // each block pair (2t, 2t+1), rows lq and lq ^ 1 swap halves (gfx950's
+      // row swap), so that the even row gets dims 32t + 8(lq/2) + 0..7 and the
+      // odd row dims 32t + 16 + 8(lq/2) + 0..7: 16-byte stores that cover 64
+      // contiguous bytes of a query row per instruction.
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const float o0 = acc[m][n][0] * inv, o1 = acc[m][n][1] * inv, o2 = acc[m][n][2] * inv,
-                  o3 = acc[m][n][3] * inv;
-      if constexpr (OUT_BF16)
-        o.v[m][n] = make_uint2(pack_bf16x2_hw(o0, o1), pack_bf16x2_hw(o2, o3));
-      else
+      for (int t = 0; t < 4; ++t) {
+        const f32x4_t &x0 = acc[m][2 * t], &x1 = acc[m][2 * t + 1];
+        const uint32_t a0 = pack_bf16x2_hw(x0[0] * inv, x0[1] * inv), a1 = pack_bf16x2_hw(x0[2] * inv, x0[3] * inv);
+        const uint32_t b0 = pack_bf16x2_hw(x1[0] * inv, x1[1] * inv), b1 = pack_bf16x2_hw(x1[2] * inv, x1[3] * inv);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+        o.v[m][t] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const float o0 = acc[m][n][0] * inv, o1 = acc[m][n][1] * inv, o2 = acc[m][n][2] * inv,
+                    o3 = acc[m][n][3] * inv;
         o.v[m][n] = make_float4(o0, o1, o2, o3);
+      }
     }
   }
 }
 
+// Stores this lane's query row (when qvalid) of every head of the wave.
 template <int MB, bool OUT_BF16>
 __device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<MB, OUT_BF16> &o, int32_t g,
-                                           int32_t row0) {
+                                           int32_t row0, bool qvalid = true) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
   const int32_t kr = lane & 15;
@@ -539,14 +513,17 @@ __device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    if (hh >= p.group) continue;
-    const int64_t obase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + g * p.group + hh) * kD + 4 * lq;
+    if (hh >= p.group || !qvalid) continue;
+    const int64_t hbase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + g * p.group + hh) * kD;
+    if constexpr (OUT_BF16) {
+      const int32_t d0 = 16 * (lq & 1) + 8 * (lq >> 1);  // see finish_tile
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      if constexpr (OUT_BF16)
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + obase + 16 * n) = o.v[m][n];
-      else
-        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + obase + 16 * n) = o.v[m][n];
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + hbase + 32 * t + d0) = o.v[m][t];
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + hbase + 4 * lq + 16 * n) = o.v[m][n];
     }
   }
 }
@@ -739,7 +716,10 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
     bf16x8_t qop[MB][4];
     q_operands<MB>(qr, qop);
     tile_general<MB, CHUNKED>(p, ks, tl, qop, g, ktile, vtile, acc, m_run, l_run);
-    store_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, g, tl.row0, qvalid);
+    // sink once, normalise (every lane: the bf16 packing swaps rows), store
+    TileOut<MB, OUT_BF16> o;
+    finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
+    write_tile<MB, OUT_BF16>(p, o, g, tl.row0, qvalid);
   }
 }
 
