@@ -263,6 +263,21 @@ def test_decode_full_layer_splits(name, splits):
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
+@pytest.mark.parametrize("kvd", ["bf16", "e4m3", "f32"])
+def test_decode_full_layer_max_splits(kvd):
+    """The largest split count the library accepts (1024): most splits hold no
+    key and the merge must ignore them; the workspace is sized by the planner's
+    upper bound for this many keys."""
+    from sliding_window_attention_swa_amd import swa
+    lens = [1, 700, 3000]
+    qd = "f32" if kvd == "f32" else "bf16"
+    say(f"decode full max splits {kvd}")
+    wl = WL.decode_workload("maxsplit", 77, lens, 16, 2, -1, 16, qd, kvd, sinks=True)
+    assert swa.lib.swa_decode_workspace_bytes(len(lens), 16, 128, 1 << 20) >= len(lens) * 16 * 1024 * 130 * 4
+    out = run_decode(DeviceWorkload(wl), "f32", num_splits=1024)
+    check(out, oracle_decode(wl), TOL[kvd], f"max splits {kvd}")
+
+
 def relabel_swa_pages(wl: WL.Workload, seed: int) -> WL.Workload:
     """Same logical K/V under another SWA page permutation."""
     import copy
