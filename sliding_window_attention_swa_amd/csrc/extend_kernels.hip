@@ -568,16 +568,18 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
     sink2[m] = (p.sinks && hh < p.group) ? p.sinks[g * p.group + hh] * kLog2e : 0.f;
   }
 
-  // gfx950 counts global loads and stores on one counter, so a wait for a
-  // load can also wait for stores issued before it (the compiler cannot count
-  // stores that sit in a branch, such as the deferred output below, and then
-  // waits for them too).  A steady tile therefore waits for memory at its top,
-  // where everything it needs arrives together (issued one tile earlier); the
-  // previous tile's output is stored right after that wait (bf16 output), so
-  // its stores have a whole tile to drain before the next.  (Measured on
-  // MI355X, C3 shape: storing each tile's output at its end, outside any
-  // branch, was 5% slower; issuing the prefetch before the deferred stores,
-  // 9% slower.)
+  // gfx950 counts global loads and stores on one counter that retires in
+  // issue order, so a wait for a load also waits for every store issued before
+  // it, and the compiler cannot count stores that sit in a branch (it then
+  // waits for them as well).  A steady tile waits for memory at its top, where
+  // the band block, slots and queries issued one tile earlier arrive together,
+  // and stores its output at its end, outside any branch: the waits of the
+  // next tile are for loads issued before these stores, so the stores stay in
+  // flight.  With one wavefront per SIMD (MB >= 2) a stall is not hidden by
+  // another wavefront, so this matters: storing each tile's output at the top
+  // of the next one instead (inside a branch) was 6% slower.  (With two
+  // workgroups per CU it was the other way round, and two workgroups were no
+  // faster than one.)
   int32_t qt = qt_begin;
   while (qt < qt_end) {
     Tile tl = tile_at<false>(p, ks, qo0, qt, prefix, n_new, seq);
@@ -613,9 +615,6 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
     // issued one tile earlier arrive together.
     int32_t q0 = 0;  // ring slot of band block 0
     bool first = true;
-    bool have_o = false;
-    int32_t pend_row0 = 0;
-    TileOut<MB, OUT_BF16> pend;
     uint4 nk = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
     for (;;) {
       if (!first) {
@@ -624,10 +623,6 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
         lds_barrier();
       }
       first = false;
-      if (have_o) {  // the previous tile's output (bf16): its stores drain during this tile
-        write_tile<MB, OUT_BF16>(p, pend, g, pend_row0);
-        have_o = false;
-      }
       // ---- in flight during this tile: the next tile's band block 8, the
       // slots of the one after, and the next tile's queries
       uint4 qn[MB][4];
@@ -647,11 +642,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
         ring_scores<MB>(p, ktile, q0, qop, sacc, m_run);
       }
       ring_pv<MB>(vtile, q0, sacc, acc, l_run);
-      if constexpr (OUT_BF16) {
-        finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, pend);
-        pend_row0 = tl.row0;
-        have_o = true;
-      } else {
+      {
         TileOut<MB, OUT_BF16> o;
         finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
         write_tile<MB, OUT_BF16>(p, o, g, tl.row0);
@@ -666,7 +657,6 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
 #pragma unroll
         for (int c = 0; c < 4; ++c) qraw[m][c] = qn[m][c];
     }
-    if (have_o) write_tile<MB, OUT_BF16>(p, pend, g, pend_row0);
   }
 }
 
@@ -753,7 +743,7 @@ __device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t 
 // CHUNKED: chunked local attention (p.chunk > 0), a separate instantiation so
 // the window-only code carries none of it.
 template <int MB, bool OUT_BF16, bool CHUNKED>
-__global__ void __launch_bounds__(kNW * 64, MB >= 4 ? 1 : 2) extend_kernel(ExtendParams p) {
+__global__ void __launch_bounds__(kNW * 64, MB >= 2 ? 1 : 2) extend_kernel(ExtendParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
   const int32_t T = p.run_tiles;
@@ -793,8 +783,10 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
   return hipGetLastError();
 }
 
-// Workgroups of the persistent grid: two per CU of the 256 on MI355X (the LDS
-// ring allows two).
+// Workgroups of the persistent grid: two per CU of the 256 on MI355X for one
+// head per wavefront (the LDS ring allows two); one per CU for MB >= 2, whose
+// wavefronts then have the whole register file (measured as fast as two per
+// CU, and faster once the output stores leave their branch).
 constexpr int64_t kResidentGroups = 512;
 
 }  // namespace
@@ -831,7 +823,7 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   // so fewer, longer runs are cheaper; more runs than workgroups would leave
   // some workgroups a second run while others idle).
   const int32_t mb = p.group >= 16 ? 4 : (p.group >= 8 ? 2 : 1);
-  const int64_t resident = mb == 4 ? kResidentGroups / 2 : kResidentGroups;  // G = 16: one per CU
+  const int64_t resident = mb >= 2 ? kResidentGroups / 2 : kResidentGroups;  // G >= 8: one per CU
   const int64_t tiles = ((a.total_q + kTQ - 1) / kTQ + a.idx.batch) * a.layer.kv_heads;
   int64_t T = tiles / resident;
   if (T < 1) T = 1;
