@@ -553,12 +553,20 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
           l_run[m] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[m]))));
           __builtin_memcpy(&pop[m], u4, 16);
         }
+        // (MB <= 2) the pair's transposed reads go out before its MFMAs, so
+        // their LDS latency overlaps; at MB = 4 the registers are short
+        constexpr int kAhead = MB <= 2 ? 8 : 1;
+        i16x4_t lo[8], hi[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          i16x4_t lo = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * n);
-          i16x4_t hi = {0, 0, 0, 0};
-          if (second) hi = lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * n);
-          bf16x8_t vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          if (n % kAhead == 0) {
+#pragma unroll
+            for (int k = n; k < n + kAhead; ++k) {
+              lo[k] = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * k);
+              hi[k] = second ? lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * k) : i16x4_t{0, 0, 0, 0};
+            }
+          }
+          bf16x8_t vop = {lo[n][0], lo[n][1], lo[n][2], lo[n][3], hi[n][0], hi[n][1], hi[n][2], hi[n][3]};
 #pragma unroll
           for (int m = 0; m < MB; ++m)
             acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], acc[m][n], 0, 0, 0);
