@@ -9,7 +9,9 @@
 // MI355X design (not the pages' kernels):
 //   * a tile = 16 consecutive queries x the G query heads of one kv head (GQA
 //     packed into the M side), so each K/V row staged in LDS serves G heads;
-//     the key range of a tile is only its band [i0 - W, i0 + 15];
+//     G = 16 is split into two groups of 8 (eight heads fill the four
+//     wavefronts at two heads each; four each would spill registers); the key
+//     range of a tile is only its band [i0 - W, i0 + 15];
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32
 //     accumulation; P is rounded to bf16 for the second product and never leaves
 //     registers (the first product's accumulator layout is the second's B
@@ -24,7 +26,7 @@
 //     not a memory round trip.  Other tiles (other windows, band clipped at
 //     position 0, partial tiles) take a general path that stages the band in
 //     chunks of 9 blocks;
-//   * runs are numbered (request, kv head, run) and dealt to the 8 XCDs in
+//   * runs are numbered (request, kv head, run, q-head group) and dealt to the 8 XCDs in
 //     contiguous ranges, so neighbouring runs, which share band blocks, hit the
 //     same L2.
 #include "common.hpp"
@@ -66,6 +68,8 @@ struct ExtendParams {
   void *out;
   int32_t run_tiles;  // tiles per workgroup run
   int32_t chunk;      // chunked local attention: chunk size, 0 = none
+  int32_t halves;     // q-head groups per kv head (G = 16: two groups of 8)
+  int32_t ghead;      // q heads per group, G / halves
 };
 
 // First key position query i sees: i - W (W >= 0), the start of i's chunk of C
@@ -178,13 +182,12 @@ __device__ __forceinline__ int32_t slot_in(const KeySrc &ks, int32_t pos) { retu
 // bytes of every query row.  Padding heads read a real head; their columns
 // are never stored.
 template <int MB>
-__device__ __forceinline__ void load_q(const ExtendParams &p, int64_t qrow, int32_t g, int32_t w, int32_t lq,
+__device__ __forceinline__ void load_q(const ExtendParams &p, int64_t qrow, int32_t hq0, int32_t w, int32_t lq,
                                        uint4 (&raw)[MB][4]) {
-  const int32_t G = p.group;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    const uint16_t *qp = p.q + (qrow * p.q_heads + g * G + (hh < G ? hh : 0)) * kD + 8 * lq;
+    const uint16_t *qp = p.q + (qrow * p.q_heads + hq0 + (hh < p.ghead ? hh : 0)) * kD + 8 * lq;
 #pragma unroll
     for (int c = 0; c < 4; ++c) raw[m][c] = *reinterpret_cast<const uint4 *>(qp + 32 * c);
   }
@@ -328,106 +331,6 @@ __device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const
   }
 }
 
-// Four heads per wavefront (MB = 4, whose registers are already short): the
-// numerators stay in f32 (sacc ends up holding 2^(s - m) per key; m_run the
-// tile's max) and are rounded and packed pair by pair in ring_pv_f32, which
-// also takes the sum of the rounded weights.  Measured faster at MB = 4 than
-// packing at once.
-template <int MB>
-__device__ __forceinline__ void ring_scores_f32(const ExtendParams &p, const uint16_t *ktile, int32_t q0,
-                                            const bf16x8_t (&qop)[MB][4], f32x4_t (&sacc)[MB][kKB],
-                                            float (&m_run)[MB]) {
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t kr = lane & 15;
-  const int32_t lq = lane >> 4;
-  int32_t slot[kKB];
-#pragma unroll
-  for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
-  // ---- S^T = K Q^T
-#pragma unroll
-  for (int j = 0; j < kKB; ++j) {
-    bf16x8_t kop[4];
-    const uint16_t *kp = ktile + (slot[j] * 16 + kr) * kKRow + 8 * lq;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[c], kp + 32 * c, 16);
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      sacc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        sacc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c], qop[m][c], sacc[m][j], 0, 0, 0);
-    }
-  }
-  // ---- band edges
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int32_t k = 4 * lq + r;
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      sacc[m][0][r] = (k >= kr) ? sacc[m][0][r] : -INFINITY;
-      sacc[m][kKB - 1][r] = (k <= kr) ? sacc[m][kKB - 1][r] : -INFINITY;
-    }
-  }
-  // ---- softmax (the whole band at once: no rescaling)
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kKB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][j][r]);
-    const float m_new = wave_max_q(mx) * p.scale2;  // finite: every query sees its own key
-    m_run[m] = m_new;
-#pragma unroll
-    for (int j = 0; j < kKB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[m][j][r] = __builtin_amdgcn_exp2f(fmaf(sacc[m][j][r], p.scale2, -m_new));
-  }
-}
-
-// O^T = V^T P^T of a steady tile over block pairs (2u, 2u+1) of its band.
-// acc is written, not accumulated into: the first pair starts from zero, so
-// acc holds no registers while the scores are computed.
-// l_run receives the sum of the bf16-rounded weights that enter the product.
-template <int MB>
-__device__ __forceinline__ void ring_pv_f32(const uint16_t *vtile, int32_t q0, const f32x4_t (&sacc)[MB][kKB],
-                                        f32x4_t (&acc)[MB][8], float (&l_run)[MB]) {
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t kr = lane & 15;
-  const int32_t lq = lane >> 4;
-  int32_t slot[kKB];
-#pragma unroll
-  for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
-  const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
-#pragma unroll
-  for (int u = 0; u < (kKB + 1) / 2; ++u) {
-    const bool second = 2 * u + 1 < kKB;  // compile-time after unrolling
-    const int ja = 2 * u;
-    const int jb = second ? 2 * u + 1 : 2 * u;
-    bf16x8_t pop[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][ja][0], sacc[m][ja][1]), pack_bf16x2_hw(sacc[m][ja][2], sacc[m][ja][3]),
-                        second ? pack_bf16x2_hw(sacc[m][jb][0], sacc[m][jb][1]) : 0u,
-                        second ? pack_bf16x2_hw(sacc[m][jb][2], sacc[m][jb][3]) : 0u};
-      l_run[m] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], u == 0 ? 0.f : l_run[m]))));
-      __builtin_memcpy(&pop[m], u4, 16);
-    }
-    const uint16_t *va = vtile + slot[ja] * 16 * kVRow + voff;
-    const uint16_t *vb = vtile + slot[jb] * 16 * kVRow + voff;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const i16x4_t lo = lds_read_tr16(va + 16 * n);
-      const i16x4_t hi = second ? lds_read_tr16(vb + 16 * n) : i16x4_t{0, 0, 0, 0};
-      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], u == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[m][n],
-                                                            0, 0, 0);
-    }
-  }
-}
-
 // General tile: the band staged in chunks of up to 9 blocks, online softmax
 // across chunks, per-key masks on blocks that touch the band's edges.
 template <int MB, bool CHUNKED>
@@ -553,19 +456,16 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
           l_run[m] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[m]))));
           __builtin_memcpy(&pop[m], u4, 16);
         }
-        // (MB <= 2) the pair's transposed reads go out before its MFMAs, so
-        // their LDS latency overlaps; at MB = 4 the registers are short
-        constexpr int kAhead = MB <= 2 ? 8 : 1;
+        // the pair's transposed reads go out before its MFMAs, so their LDS
+        // latency overlaps
         i16x4_t lo[8], hi[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          if (n % kAhead == 0) {
+          lo[n] = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * n);
+          hi[n] = second ? lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * n) : i16x4_t{0, 0, 0, 0};
+        }
 #pragma unroll
-            for (int k = n; k < n + kAhead; ++k) {
-              lo[k] = lds_read_tr16(vrow + (32 * u) * kVRow + 16 * k);
-              hi[k] = second ? lds_read_tr16(vrow + (32 * u + 16) * kVRow + 16 * k) : i16x4_t{0, 0, 0, 0};
-            }
-          }
+        for (int n = 0; n < 8; ++n) {
           bf16x8_t vop = {lo[n][0], lo[n][1], lo[n][2], lo[n][3], hi[n][0], hi[n][1], hi[n][2], hi[n][3]};
 #pragma unroll
           for (int m = 0; m < MB; ++m)
@@ -631,7 +531,7 @@ __device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t
 
 // Stores this lane's query row (when qvalid) of every head of the wave.
 template <int MB, bool OUT_BF16>
-__device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<MB, OUT_BF16> &o, int32_t g,
+__device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<MB, OUT_BF16> &o, int32_t hq0,
                                            int32_t row0, bool qvalid = true) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
@@ -640,8 +540,8 @@ __device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    if (hh >= p.group || !qvalid) continue;
-    const int64_t hbase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + g * p.group + hh) * kD;
+    if (hh >= p.ghead || !qvalid) continue;
+    const int64_t hbase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + hq0 + hh) * kD;
     if constexpr (OUT_BF16) {
       const int32_t d0 = 16 * (lq & 1) + 8 * (lq >> 1);  // see finish_tile
 #pragma unroll
@@ -671,7 +571,7 @@ __device__ __forceinline__ void q_operands(const uint4 (&raw)[MB][4], bf16x8_t (
 // paths' registers apart.
 template <int MB, bool OUT_BF16>
 __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
-                                          int32_t g, int32_t qt_begin, int32_t qt_end) {
+                                          int32_t g, int32_t hq0, int32_t qt_begin, int32_t qt_end) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
   const int32_t kr = lane & 15;
@@ -692,7 +592,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    sink2[m] = (p.sinks && hh < p.group) ? p.sinks[g * p.group + hh] * kLog2e : 0.f;
+    sink2[m] = (p.sinks && hh < p.ghead) ? p.sinks[hq0 + hh] * kLog2e : 0.f;
   }
 
   // gfx950 counts global loads and stores on one counter that retires in
@@ -718,7 +618,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
     // of its first tile (slots 0..8), all 18 loads in flight before the first
     // LDS write waits for one.
     uint4 qraw[MB][4];
-    load_q<MB>(p, static_cast<int64_t>(tl.row0) + kr, g, w, lq, qraw);
+    load_q<MB>(p, static_cast<int64_t>(tl.row0) + kr, hq0, w, lq, qraw);
     bool next_steady = qt + 1 < qt_end && tile_at<false>(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
     int32_t nslot;  // slot of this thread's row of the next tile's band block 8
     {
@@ -757,12 +657,12 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
         fetch_piece(p, nslot, g, nk, nv);
         const bool next2 = qt + 2 < qt_end && tile_at<false>(p, ks, qo0, qt + 2, prefix, n_new, seq).steady;
         nslot = slot_in(ks, next2 ? tl.kj0 + 16 + kBand + row : tl.kj0 + row);
-        load_q<MB>(p, static_cast<int64_t>(tl.row0) + kTQ + kr, g, w, lq, qn);
+        load_q<MB>(p, static_cast<int64_t>(tl.row0) + kTQ + kr, hq0, w, lq, qn);
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x4_t acc[MB][8];  // written by ring_pv
       float m_run[MB], l_run[MB];
-      if constexpr (MB <= 2) {
+      {
         uint32_t pw[MB][kKB][2];
         {
           bf16x8_t qop[MB][4];
@@ -770,19 +670,11 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
           ring_scores<MB>(p, ktile, q0, qop, pw, m_run, l_run);
         }
         ring_pv<MB>(vtile, q0, pw, acc);
-      } else {
-        f32x4_t sacc[MB][kKB];
-        {
-          bf16x8_t qop[MB][4];
-          q_operands<MB>(qraw, qop);
-          ring_scores_f32<MB>(p, ktile, q0, qop, sacc, m_run);
-        }
-        ring_pv_f32<MB>(vtile, q0, sacc, acc, l_run);
       }
       {
         TileOut<MB, OUT_BF16> o;
         finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
-        write_tile<MB, OUT_BF16>(p, o, g, tl.row0);
+        write_tile<MB, OUT_BF16>(p, o, hq0, tl.row0);
       }
       ++qt;
       if (!next_steady) break;
@@ -799,7 +691,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
 
 template <int MB, bool OUT_BF16, bool CHUNKED>
 __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
-                                           int32_t g, int32_t qt_begin, int32_t qt_end) {
+                                           int32_t g, int32_t hq0, int32_t qt_begin, int32_t qt_end) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
   const int32_t kr = lane & 15;
@@ -819,7 +711,7 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    sink2[m] = (p.sinks && hh < p.group) ? p.sinks[g * p.group + hh] * kLog2e : 0.f;
+    sink2[m] = (p.sinks && hh < p.ghead) ? p.sinks[hq0 + hh] * kLog2e : 0.f;
   }
 
   for (int32_t qt = qt_begin; qt < qt_end; ++qt) {
@@ -839,20 +731,23 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
     }
     // rows past the request (last partial tile) read a real row; never stored
     uint4 qr[MB][4];
-    load_q<MB>(p, qvalid ? static_cast<int64_t>(tl.row0) + kr : static_cast<int64_t>(tl.row0), g, w, lq, qr);
+    load_q<MB>(p, qvalid ? static_cast<int64_t>(tl.row0) + kr : static_cast<int64_t>(tl.row0), hq0, w, lq, qr);
     bf16x8_t qop[MB][4];
     q_operands<MB>(qr, qop);
     tile_general<MB, CHUNKED>(p, ks, tl, qop, g, ktile, vtile, acc, m_run, l_run);
     // sink once, normalise (every lane: the bf16 packing swaps rows), store
     TileOut<MB, OUT_BF16> o;
     finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
-    write_tile<MB, OUT_BF16>(p, o, g, tl.row0, qvalid);
+    write_tile<MB, OUT_BF16>(p, o, hq0, tl.row0, qvalid);
   }
 }
 
-// Run r of the numbering (request, kv head, run of T tiles); b = -1 past the end.
+// Run r of the numbering (request, kv head, run of T tiles, q-head group);
+// b = -1 past the end.  The groups of one kv head's run are neighbours, so
+// they read the same K/V blocks at about the same time.  hq0: the group's
+// first q head.
 struct Run {
-  int32_t b, g, qt_begin, qt_end;
+  int32_t b, g, hq0, qt_begin, qt_end;
 };
 
 __device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t r) {
@@ -860,32 +755,37 @@ __device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t 
   for (; b < p.batch; ++b) {
     ntile = (new_count(p, b) + kTQ - 1) / kTQ;
     nrun = (ntile + T - 1) / T;
-    const int32_t tb = nrun * p.kv_heads;
+    const int32_t tb = nrun * p.kv_heads * p.halves;
     if (t < tb) break;
     t -= tb;
   }
-  Run run{-1, 0, 0, 0};
+  Run run{-1, 0, 0, 0, 0};
   if (b >= p.batch) return run;
+  const int32_t half = t % p.halves;
+  t /= p.halves;
   run.b = b;
   run.g = t / nrun;
+  run.hq0 = run.g * p.group + half * p.ghead;
   run.qt_begin = (t % nrun) * T;
   run.qt_end = run.qt_begin + T < ntile ? run.qt_begin + T : ntile;
   return run;
 }
 
-// Persistent grid (about two workgroups per CU): the runs, numbered
-// (request, kv head, run), are split into 8 contiguous ranges, one per XCD
+// Persistent grid (one or two workgroups per CU): the runs, numbered
+// (request, kv head, run, q-head group), are split into 8 contiguous ranges, one per XCD
 // (workgroup i runs on XCD i % 8), so neighbouring runs, which share band
 // blocks, meet in one L2; the workgroups of an XCD stride through its range.
 // CHUNKED: chunked local attention (p.chunk > 0), a separate instantiation so
 // the window-only code carries none of it.
 template <int MB, bool OUT_BF16, bool CHUNKED>
 __global__ void __launch_bounds__(kNW * 64, MB >= 2 ? 1 : 2) extend_kernel(ExtendParams p) {
+  static_assert(MB == 1 || MB == 2, "one or two q heads per wavefront");
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
   const int32_t T = p.run_tiles;
   int32_t total = 0;
-  for (int32_t b = 0; b < p.batch; ++b) total += (new_count(p, b) + kTQ * T - 1) / (kTQ * T) * p.kv_heads;
+  for (int32_t b = 0; b < p.batch; ++b)
+    total += (new_count(p, b) + kTQ * T - 1) / (kTQ * T) * p.kv_heads * p.halves;
   const int32_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
   const int32_t x = blockIdx.x % 8;
   const int32_t r_lo = static_cast<int32_t>(static_cast<int64_t>(total) * x / 8);
@@ -895,13 +795,13 @@ __global__ void __launch_bounds__(kNW * 64, MB >= 2 ? 1 : 2) extend_kernel(Exten
     for (int32_t r = r0; r < r_hi; r += per_xcd) {
       const Run run = run_of(p, T, r);
       if (run.b < 0) break;
-      run_steady<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+      run_steady<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.hq0, run.qt_begin, run.qt_end);
     }
   }
   for (int32_t r = r0; r < r_hi; r += per_xcd) {
     const Run run = run_of(p, T, r);
     if (run.b < 0) break;
-    run_general<MB, OUT_BF16, CHUNKED>(p, ktile, vtile, run.b, run.g, run.qt_begin, run.qt_end);
+    run_general<MB, OUT_BF16, CHUNKED>(p, ktile, vtile, run.b, run.g, run.hq0, run.qt_begin, run.qt_end);
   }
 }
 
@@ -959,19 +859,23 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   // one run per workgroup of the persistent grid (each run fills its ring once,
   // so fewer, longer runs are cheaper; more runs than workgroups would leave
   // some workgroups a second run while others idle).
-  const int32_t mb = p.group >= 16 ? 4 : (p.group >= 8 ? 2 : 1);
+  // G = 16 runs as two groups of 8 q heads per kv head on the two-heads-per-
+  // wavefront kernel: K/V is read twice (mostly from L2, the two groups being
+  // neighbours), but four heads per wavefront spill registers.
+  p.halves = p.group >= 16 ? 2 : 1;
+  p.ghead = p.group / p.halves;
+  const int32_t mb = p.ghead >= 8 ? 2 : 1;
   const int64_t resident = mb >= 2 ? kResidentGroups / 2 : kResidentGroups;  // G >= 8: one per CU
-  const int64_t tiles = ((a.total_q + kTQ - 1) / kTQ + a.idx.batch) * a.layer.kv_heads;
+  const int64_t tiles = ((a.total_q + kTQ - 1) / kTQ + a.idx.batch) * a.layer.kv_heads * p.halves;
   int64_t T = tiles / resident;
   if (T < 1) T = 1;
   if (T > 64) T = 64;
   p.run_tiles = static_cast<int32_t>(T);
-  int64_t grid = (tiles + T - 1) / T + static_cast<int64_t>(a.idx.batch) * a.layer.kv_heads;
+  int64_t grid = (tiles + T - 1) / T + static_cast<int64_t>(a.idx.batch) * a.layer.kv_heads * p.halves;
   if (grid > resident) grid = resident;
   grid = (grid + 7) / 8 * 8;
   const uint32_t runs = static_cast<uint32_t>(grid);
   const bool out_bf16 = a.out_dtype == SWA_BF16;
-  if (mb == 4) return launch_mb<4>(p, static_cast<uint32_t>(runs), out_bf16, stream);
   if (mb == 2) return launch_mb<2>(p, static_cast<uint32_t>(runs), out_bf16, stream);
   return launch_mb<1>(p, static_cast<uint32_t>(runs), out_bf16, stream);
 }

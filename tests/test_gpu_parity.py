@@ -472,6 +472,8 @@ EXTEND_CASES = {
     "g2": ([20, 300], [40, 90], 4, 2, 128, 16, True),
     "g4": ([20, 300], [40, 90], 8, 2, 128, 16, True),
     "g16": ([20, 300], [40, 90], 32, 2, 128, 16, True),
+    "g16_full_one_kv": ([0, 40], [50, 17], 16, 1, -1, 8, True),
+    "g16_w300_ragged": ([50, 700, 9], [400, 31, 0], 32, 2, 300, 64, False),
     # ragged batches with requests that add no tokens (one of them with no prefix either)
     "g8_ragged_empty": ([300, 50, 0, 7, 129], [40, 0, 1, 0, 64], 16, 2, 128, 16, True),
     "g4_empty_first": ([64, 0, 500], [0, 0, 200], 8, 2, 128, 16, False),
