@@ -530,7 +530,13 @@ __device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t
 }
 
 // Stores this lane's query row (when qvalid) of every head of the wave.
-template <int MB, bool OUT_BF16>
+// ALLH: the group has exactly kNW * MB heads (8 at two heads per wavefront, 4
+// at one), so every head of every wavefront is valid and the steady tiles'
+// stores are branch-free: the wait for the next tile's queries (loaded before
+// these stores, and counted with them in issue order) then leaves the stores
+// in flight.  A store under a branch makes that wait drain every store of the
+// tile (C3: 84 -> 81 us without the branch).
+template <int MB, bool OUT_BF16, bool ALLH>
 __device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<MB, OUT_BF16> &o, int32_t hq0,
                                            int32_t row0, bool qvalid = true) {
   const int32_t lane = threadIdx.x & 63;
@@ -540,7 +546,7 @@ __device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
-    if (hh >= p.ghead || !qvalid) continue;
+    if ((!ALLH && hh >= p.ghead) || !qvalid) continue;
     const int64_t hbase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + hq0 + hh) * kD;
     if constexpr (OUT_BF16) {
       const int32_t d0 = 16 * (lq & 1) + 8 * (lq >> 1);  // see finish_tile
@@ -569,7 +575,7 @@ __device__ __forceinline__ void q_operands(const uint4 (&raw)[MB][4], bf16x8_t (
 // general path (run_general).  Tiles are independent; the kernel runs all
 // first passes of its runs, then all second passes, which keeps the two
 // paths' registers apart.
-template <int MB, bool OUT_BF16>
+template <int MB, bool OUT_BF16, bool ALLH>
 __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
                                           int32_t g, int32_t hq0, int32_t qt_begin, int32_t qt_end) {
   const int32_t lane = threadIdx.x & 63;
@@ -600,9 +606,9 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
   // it, and the compiler cannot count stores that sit in a branch (it then
   // waits for them as well).  A steady tile waits for memory at its top, where
   // the band block, slots and queries issued one tile earlier arrive together,
-  // and stores its output at its end, outside any branch: the waits of the
-  // next tile are for loads issued before these stores, so the stores stay in
-  // flight.  With one wavefront per SIMD (MB >= 2) a stall is not hidden by
+  // and stores its output at its end, outside any branch when every head of
+  // the wavefronts is valid (ALLH): the waits of the next tile are for loads
+  // issued before these stores, so the stores stay in flight.  With one wavefront per SIMD (MB >= 2) a stall is not hidden by
   // another wavefront, so this matters: storing each tile's output at the top
   // of the next one instead (inside a branch) was 6% slower.  (With two
   // workgroups per CU it was the other way round, and two workgroups were no
@@ -616,7 +622,9 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
     }
     // ---- a stretch of steady tiles starts: fill the ring with the whole band
     // of its first tile (slots 0..8), all 18 loads in flight before the first
-    // LDS write waits for one.
+    // LDS write waits for one (at two heads per wavefront; at one, two
+    // wavefronts per SIMD leave too few registers, and the compiler pairs each
+    // load with its write).
     uint4 qraw[MB][4];
     load_q<MB>(p, static_cast<int64_t>(tl.row0) + kr, hq0, w, lq, qraw);
     bool next_steady = qt + 1 < qt_end && tile_at<false>(p, ks, qo0, qt + 1, prefix, n_new, seq).steady;
@@ -674,7 +682,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
       {
         TileOut<MB, OUT_BF16> o;
         finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
-        write_tile<MB, OUT_BF16>(p, o, hq0, tl.row0);
+        write_tile<MB, OUT_BF16, ALLH>(p, o, hq0, tl.row0);
       }
       ++qt;
       if (!next_steady) break;
@@ -689,7 +697,7 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
   }
 }
 
-template <int MB, bool OUT_BF16, bool CHUNKED>
+template <int MB, bool OUT_BF16, bool CHUNKED, bool ALLH>
 __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *ktile, uint16_t *vtile, int32_t b,
                                            int32_t g, int32_t hq0, int32_t qt_begin, int32_t qt_end) {
   const int32_t lane = threadIdx.x & 63;
@@ -738,7 +746,7 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
     // sink once, normalise (every lane: the bf16 packing swaps rows), store
     TileOut<MB, OUT_BF16> o;
     finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
-    write_tile<MB, OUT_BF16>(p, o, hq0, tl.row0, qvalid);
+    write_tile<MB, OUT_BF16, ALLH>(p, o, hq0, tl.row0, qvalid);
   }
 }
 
@@ -777,7 +785,7 @@ __device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t 
 // blocks, meet in one L2; the workgroups of an XCD stride through its range.
 // CHUNKED: chunked local attention (p.chunk > 0), a separate instantiation so
 // the window-only code carries none of it.
-template <int MB, bool OUT_BF16, bool CHUNKED>
+template <int MB, bool OUT_BF16, bool CHUNKED, bool ALLH>
 __global__ void __launch_bounds__(kNW * 64, MB >= 2 ? 1 : 2) extend_kernel(ExtendParams p) {
   static_assert(MB == 1 || MB == 2, "one or two q heads per wavefront");
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
@@ -795,27 +803,27 @@ __global__ void __launch_bounds__(kNW * 64, MB >= 2 ? 1 : 2) extend_kernel(Exten
     for (int32_t r = r0; r < r_hi; r += per_xcd) {
       const Run run = run_of(p, T, r);
       if (run.b < 0) break;
-      run_steady<MB, OUT_BF16>(p, ktile, vtile, run.b, run.g, run.hq0, run.qt_begin, run.qt_end);
+      run_steady<MB, OUT_BF16, ALLH>(p, ktile, vtile, run.b, run.g, run.hq0, run.qt_begin, run.qt_end);
     }
   }
   for (int32_t r = r0; r < r_hi; r += per_xcd) {
     const Run run = run_of(p, T, r);
     if (run.b < 0) break;
-    run_general<MB, OUT_BF16, CHUNKED>(p, ktile, vtile, run.b, run.g, run.hq0, run.qt_begin, run.qt_end);
+    run_general<MB, OUT_BF16, CHUNKED, ALLH>(p, ktile, vtile, run.b, run.g, run.hq0, run.qt_begin, run.qt_end);
   }
 }
 
-template <int MB>
+template <int MB, bool ALLH>
 hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStream_t stream) {
   if (p.chunk > 0) {
     if (out_bf16)
-      hipLaunchKernelGGL((extend_kernel<MB, true, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+      hipLaunchKernelGGL((extend_kernel<MB, true, true, ALLH>), dim3(grid), dim3(kNW * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((extend_kernel<MB, false, true>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+      hipLaunchKernelGGL((extend_kernel<MB, false, true, ALLH>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   } else if (out_bf16) {
-    hipLaunchKernelGGL((extend_kernel<MB, true, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+    hipLaunchKernelGGL((extend_kernel<MB, true, false, ALLH>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((extend_kernel<MB, false, false>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+    hipLaunchKernelGGL((extend_kernel<MB, false, false, ALLH>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -864,7 +872,7 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   // neighbours), but four heads per wavefront spill registers.
   p.halves = p.group >= 16 ? 2 : 1;
   p.ghead = p.group / p.halves;
-  const int32_t mb = p.ghead >= 8 ? 2 : 1;
+  const int32_t mb = p.ghead >= 8 ? 2 : 1;  // ghead is 1, 2, 4 or 8
   const int64_t resident = mb >= 2 ? kResidentGroups / 2 : kResidentGroups;  // G >= 8: one per CU
   const int64_t tiles = ((a.total_q + kTQ - 1) / kTQ + a.idx.batch) * a.layer.kv_heads * p.halves;
   int64_t T = tiles / resident;
@@ -876,8 +884,12 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   grid = (grid + 7) / 8 * 8;
   const uint32_t runs = static_cast<uint32_t>(grid);
   const bool out_bf16 = a.out_dtype == SWA_BF16;
-  if (mb == 2) return launch_mb<2>(p, static_cast<uint32_t>(runs), out_bf16, stream);
-  return launch_mb<1>(p, static_cast<uint32_t>(runs), out_bf16, stream);
+  if (mb == 2) {
+    if (p.ghead != kNW * 2) return hipErrorInvalidValue;
+    return launch_mb<2, true>(p, runs, out_bf16, stream);
+  }
+  if (p.ghead == kNW) return launch_mb<1, true>(p, runs, out_bf16, stream);
+  return launch_mb<1, false>(p, runs, out_bf16, stream);
 }
 
 }  // namespace swa
