@@ -214,23 +214,20 @@ __device__ __forceinline__ void put_piece(uint16_t *ktile, uint16_t *vtile, int3
 // every query.
 __device__ __forceinline__ int32_t ring_slot(int32_t q0, int j) { return q0 + j < kKB ? q0 + j : q0 + j - kKB; }
 
-// Scores and softmax numerators of a steady tile: pw ends up holding the
-// weights 2^(s - m), rounded to bf16 and packed in pairs (keys 4lq + {0,1} and
-// 4lq + {2,3} of each block), m_run the tile's max and l_run the sum of the
-// rounded weights (the weights that enter P.V), taken block by block.  Packing
-// here halves the registers the weights hold while P.V runs.
-template <int MB>
-__device__ __forceinline__ void ring_scores(const ExtendParams &p, const uint16_t *ktile, int32_t q0,
-                                            const bf16x8_t (&qop)[MB][4], uint32_t (&pw)[MB][kKB][2],
-                                            float (&m_run)[MB], float (&l_run)[MB]) {
-  f32x4_t sacc[MB][kKB];
+// A steady tile, one head at a time.  With two heads per wavefront the two
+// heads' phases are staggered (head 1's QK^T next to head 0's softmax, head 0's
+// P.V next to head 1's softmax, head 1's P.V next to head 0's normalisation),
+// so the MFMAs of one head run while the other head's VALU work issues (C3:
+// 81 -> 78 us); K and V are then read from LDS once per head instead of once
+// per pair of heads (LDS was 14% busy).
+
+// One head's S^T = K Q^T over the band (block j + 1's K rows read while block
+// j's MFMAs run), band edges masked.
+__device__ __forceinline__ void head_scores(const uint16_t *ktile, const int32_t (&slot)[kKB],
+                                            const bf16x8_t (&qop)[4], f32x4_t (&s)[kKB]) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
-  int32_t slot[kKB];
-#pragma unroll
-  for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
-  // ---- S^T = K Q^T; block j + 1's K rows are read while block j's MFMAs run
   bf16x8_t kop[2][4];
   {
     const uint16_t *kp = ktile + (slot[0] * 16 + kr) * kKRow + 8 * lq;
@@ -244,76 +241,68 @@ __device__ __forceinline__ void ring_scores(const ExtendParams &p, const uint16_
 #pragma unroll
       for (int c = 0; c < 4; ++c) __builtin_memcpy(&kop[(j + 1) & 1][c], kp + 32 * c, 16);
     }
+    s[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      sacc[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        sacc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j & 1][c], qop[m][c], sacc[m][j], 0, 0, 0);
-    }
+    for (int c = 0; c < 4; ++c) s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j & 1][c], qop[c], s[j], 0, 0, 0);
   }
-  // ---- band edges
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int32_t k = 4 * lq + r;
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      sacc[m][0][r] = (k >= kr) ? sacc[m][0][r] : -INFINITY;
-      sacc[m][kKB - 1][r] = (k <= kr) ? sacc[m][kKB - 1][r] : -INFINITY;
-    }
-  }
-  // ---- softmax (the whole band at once: no rescaling)
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kKB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[m][j][r]);
-    const float m_new = wave_max_q(mx) * p.scale2;  // finite: every query sees its own key
-    m_run[m] = m_new;
-    float l = 0.f;
-#pragma unroll
-    for (int j = 0; j < kKB; ++j) {
-      float e[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sacc[m][j][r], p.scale2, -m_new));
-      pw[m][j][0] = pack_bf16x2_hw(e[0], e[1]);
-      pw[m][j][1] = pack_bf16x2_hw(e[2], e[3]);
-      l = bf16x2_acc(pw[m][j][1], bf16x2_acc(pw[m][j][0], l));
-    }
-    l_run[m] = l;
+    s[0][r] = (k >= kr) ? s[0][r] : -INFINITY;
+    s[kKB - 1][r] = (k <= kr) ? s[kKB - 1][r] : -INFINITY;
   }
 }
 
-// O^T = V^T P^T of a steady tile over block pairs (2u, 2u+1) of its band.
-// acc is written, not accumulated into: the first pair starts from zero, so
-// acc holds no registers while the scores are computed.
-template <int MB>
-__device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const uint32_t (&pw)[MB][kKB][2],
-                                        f32x4_t (&acc)[MB][8]) {
+// One head's softmax numerators: pw holds the weights 2^(s - m), rounded to
+// bf16 and packed in pairs (keys 4lq + {0,1} and 4lq + {2,3} of each block), m
+// the band's max and l the sum of the rounded weights (the weights that enter
+// P.V), taken block by block.  The whole band at once: no rescaling.  Packing
+// here halves the registers the weights hold while P.V runs.
+__device__ __forceinline__ void head_weights(float scale2, const f32x4_t (&s)[kKB], uint32_t (&pw)[kKB][2],
+                                             float &m_run, float &l_run) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kKB; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][r]);
+  const float m_new = wave_max_q(mx) * scale2;  // finite: every query sees its own key
+  m_run = m_new;
+  float l = 0.f;
+#pragma unroll
+  for (int j = 0; j < kKB; ++j) {
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[j][r], scale2, -m_new));
+    pw[j][0] = pack_bf16x2_hw(e[0], e[1]);
+    pw[j][1] = pack_bf16x2_hw(e[2], e[3]);
+    l = bf16x2_acc(pw[j][1], bf16x2_acc(pw[j][0], l));
+  }
+  l_run = l;
+}
+
+// One head's O^T = V^T P^T over block pairs (2u, 2u+1) of its band.  acc is
+// written, not accumulated into: the first pair starts from zero, so acc holds
+// no registers while the scores are computed.  Each pair's 16 transposed reads
+// go out before its MFMAs, so their LDS latency overlaps instead of stalling
+// every step (C3: 90.5 -> 84.6 us).
+__device__ __forceinline__ void head_pv(const uint16_t *vtile, const int32_t (&slot)[kKB], const uint32_t (&pw)[kKB][2],
+                                        f32x4_t (&acc)[8]) {
   const int32_t lane = threadIdx.x & 63;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
-  int32_t slot[kKB];
-#pragma unroll
-  for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
   const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
 #pragma unroll
   for (int u = 0; u < (kKB + 1) / 2; ++u) {
-    const bool second = 2 * u + 1 < kKB;  // compile-time after unrolling
+    const bool second = 2 * u + 1 < kKB;
     const int ja = 2 * u;
     const int jb = second ? 2 * u + 1 : 2 * u;
-    bf16x8_t pop[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      uint32_t u4[4] = {pw[m][ja][0], pw[m][ja][1], second ? pw[m][jb][0] : 0u, second ? pw[m][jb][1] : 0u};
-      __builtin_memcpy(&pop[m], u4, 16);
+    bf16x8_t pop;
+    {
+      uint32_t u4[4] = {pw[ja][0], pw[ja][1], second ? pw[jb][0] : 0u, second ? pw[jb][1] : 0u};
+      __builtin_memcpy(&pop, u4, 16);
     }
     const uint16_t *va = vtile + slot[ja] * 16 * kVRow + voff;
     const uint16_t *vb = vtile + slot[jb] * 16 * kVRow + voff;
-    // The pair's 16 transposed reads go out before its MFMAs, so their LDS
-    // latency overlaps instead of stalling every step (C3: 90.5 -> 84.6 us).
     i16x4_t lo[8], hi[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
@@ -323,10 +312,7 @@ __device__ __forceinline__ void ring_pv(const uint16_t *vtile, int32_t q0, const
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const bf16x8_t vop = __builtin_shufflevector(lo[n], hi[n], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], u == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[m][n],
-                                                            0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, u == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[n], 0, 0, 0);
     }
   }
 }
@@ -477,30 +463,30 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
 }
 
 // A finished tile's normalised output for this lane, packed for its stores.
-template <int MB, bool OUT_BF16>
-struct TileOut;
-template <int MB>
-struct TileOut<MB, true> {  // bf16: 8 consecutive dims per lane and block pair (see finish_tile)
-  uint4 v[MB][4];
+template <bool OUT_BF16>
+struct HeadOut {  // bf16: 8 consecutive dims per lane and block pair (see finish_head)
+  using type = uint4[4];
 };
-template <int MB>
-struct TileOut<MB, false> {
-  float4 v[MB][8];
+template <>
+struct HeadOut<false> {
+  using type = float4[8];
+};
+template <int MB, bool OUT_BF16>
+struct TileOut {
+  typename HeadOut<OUT_BF16>::type v[MB];
 };
 
-template <int MB, bool OUT_BF16>
-__device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t (&acc)[MB][8],
-                                            const float (&m_run)[MB], const float (&l_run)[MB],
-                                            const float (&sink2)[MB], TileOut<MB, OUT_BF16> &o) {
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const float M = m_run[m];
-    float L = wave_sum_q(l_run[m]);
+// One head: the sink once, normalise, and (bf16) pack for the stores.
+template <bool OUT_BF16>
+__device__ __forceinline__ void finish_head(const ExtendParams &p, const f32x4_t (&acc)[8], float M, float l_run,
+                                            float sink2, typename HeadOut<OUT_BF16>::type &ov) {
+  {
+    float L = wave_sum_q(l_run);
     float a = 1.f;
     if (p.sinks) {
-      const float Mn = fmaxf(M, sink2[m]);
+      const float Mn = fmaxf(M, sink2);
       a = __builtin_amdgcn_exp2f(M - Mn);
-      L = L * a + __builtin_amdgcn_exp2f(sink2[m] - Mn);
+      L = L * a + __builtin_amdgcn_exp2f(sink2 - Mn);
     }
     const float inv = L > 0.f ? a / L : 0.f;
     if constexpr (OUT_BF16) {
@@ -511,21 +497,45 @@ __device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t
       // contiguous bytes of a query row per instruction.
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f32x4_t &x0 = acc[m][2 * t], &x1 = acc[m][2 * t + 1];
+        const f32x4_t &x0 = acc[2 * t], &x1 = acc[2 * t + 1];
         const uint32_t a0 = pack_bf16x2_hw(x0[0] * inv, x0[1] * inv), a1 = pack_bf16x2_hw(x0[2] * inv, x0[3] * inv);
         const uint32_t b0 = pack_bf16x2_hw(x1[0] * inv, x1[1] * inv), b1 = pack_bf16x2_hw(x1[2] * inv, x1[3] * inv);
         const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
         const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
-        o.v[m][t] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        ov[t] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
       }
     } else {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const float o0 = acc[m][n][0] * inv, o1 = acc[m][n][1] * inv, o2 = acc[m][n][2] * inv,
-                    o3 = acc[m][n][3] * inv;
-        o.v[m][n] = make_float4(o0, o1, o2, o3);
+        const float o0 = acc[n][0] * inv, o1 = acc[n][1] * inv, o2 = acc[n][2] * inv, o3 = acc[n][3] * inv;
+        ov[n] = make_float4(o0, o1, o2, o3);
       }
     }
+  }
+}
+
+template <int MB, bool OUT_BF16>
+__device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t (&acc)[MB][8],
+                                            const float (&m_run)[MB], const float (&l_run)[MB],
+                                            const float (&sink2)[MB], TileOut<MB, OUT_BF16> &o) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m) finish_head<OUT_BF16>(p, acc[m], m_run[m], l_run[m], sink2[m], o.v[m]);
+}
+
+// Stores this lane's query row `qrow` of q head `hq`.
+template <bool OUT_BF16>
+__device__ __forceinline__ void write_head(const ExtendParams &p, const typename HeadOut<OUT_BF16>::type &ov,
+                                           int32_t hq, int32_t qrow) {
+  const int32_t lq = (threadIdx.x & 63) >> 4;
+  const int64_t hbase = (static_cast<int64_t>(qrow) * p.q_heads + hq) * kD;
+  if constexpr (OUT_BF16) {
+    const int32_t d0 = 16 * (lq & 1) + 8 * (lq >> 1);  // see finish_head
+#pragma unroll
+    for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + hbase + 32 * t + d0) = ov[t];
+  } else {
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + hbase + 4 * lq + 16 * n) = ov[n];
   }
 }
 
@@ -539,25 +549,13 @@ __device__ __forceinline__ void finish_tile(const ExtendParams &p, const f32x4_t
 template <int MB, bool OUT_BF16, bool ALLH>
 __device__ __forceinline__ void write_tile(const ExtendParams &p, const TileOut<MB, OUT_BF16> &o, int32_t hq0,
                                            int32_t row0, bool qvalid = true) {
-  const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
-  const int32_t kr = lane & 15;
-  const int32_t lq = lane >> 4;
+  const int32_t kr = threadIdx.x & 15;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int32_t hh = w * MB + m;
     if ((!ALLH && hh >= p.ghead) || !qvalid) continue;
-    const int64_t hbase = ((static_cast<int64_t>(row0) + kr) * p.q_heads + hq0 + hh) * kD;
-    if constexpr (OUT_BF16) {
-      const int32_t d0 = 16 * (lq & 1) + 8 * (lq >> 1);  // see finish_tile
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + hbase + 32 * t + d0) = o.v[m][t];
-    } else {
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + hbase + 4 * lq + 16 * n) = o.v[m][n];
-    }
+    write_head<OUT_BF16>(p, o.v[m], hq0 + hh, row0 + kr);
   }
 }
 
@@ -668,21 +666,40 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
         load_q<MB>(p, static_cast<int64_t>(tl.row0) + kTQ + kr, hq0, w, lq, qn);
       }
       __builtin_amdgcn_sched_barrier(0);
-      f32x4_t acc[MB][8];  // written by ring_pv
-      float m_run[MB], l_run[MB];
       {
-        uint32_t pw[MB][kKB][2];
-        {
-          bf16x8_t qop[MB][4];
-          q_operands<MB>(qraw, qop);
-          ring_scores<MB>(p, ktile, q0, qop, pw, m_run, l_run);
+        int32_t slot[kKB];
+#pragma unroll
+        for (int j = 0; j < kKB; ++j) slot[j] = ring_slot(q0, j);
+        bf16x8_t qop[MB][4];
+        q_operands<MB>(qraw, qop);
+        f32x4_t s0[kKB];
+        uint32_t pw0[kKB][2];
+        float m0, l0;
+        f32x4_t acc0[8];
+        typename HeadOut<OUT_BF16>::type o0;
+        if constexpr (MB == 2) {
+          f32x4_t s1[kKB];
+          uint32_t pw1[kKB][2];
+          float m1, l1;
+          f32x4_t acc1[8];
+          typename HeadOut<OUT_BF16>::type o1;
+          head_scores(ktile, slot, qop[0], s0);
+          head_scores(ktile, slot, qop[1], s1);
+          head_weights(p.scale2, s0, pw0, m0, l0);
+          head_pv(vtile, slot, pw0, acc0);
+          head_weights(p.scale2, s1, pw1, m1, l1);
+          head_pv(vtile, slot, pw1, acc1);
+          finish_head<OUT_BF16>(p, acc0, m0, l0, sink2[0], o0);
+          write_head<OUT_BF16>(p, o0, hq0 + 2 * w, tl.row0 + kr);
+          finish_head<OUT_BF16>(p, acc1, m1, l1, sink2[1], o1);
+          write_head<OUT_BF16>(p, o1, hq0 + 2 * w + 1, tl.row0 + kr);
+        } else {
+          head_scores(ktile, slot, qop[0], s0);
+          head_weights(p.scale2, s0, pw0, m0, l0);
+          head_pv(vtile, slot, pw0, acc0);
+          finish_head<OUT_BF16>(p, acc0, m0, l0, sink2[0], o0);
+          if (ALLH || w < p.ghead) write_head<OUT_BF16>(p, o0, hq0 + w, tl.row0 + kr);
         }
-        ring_pv<MB>(vtile, q0, pw, acc);
-      }
-      {
-        TileOut<MB, OUT_BF16> o;
-        finish_tile<MB, OUT_BF16>(p, acc, m_run, l_run, sink2, o);
-        write_tile<MB, OUT_BF16, ALLH>(p, o, hq0, tl.row0);
       }
       ++qt;
       if (!next_steady) break;
@@ -788,6 +805,7 @@ __device__ __forceinline__ Run run_of(const ExtendParams &p, int32_t T, int32_t 
 template <int MB, bool OUT_BF16, bool CHUNKED, bool ALLH>
 __global__ void __launch_bounds__(kNW * 64, MB >= 2 ? 1 : 2) extend_kernel(ExtendParams p) {
   static_assert(MB == 1 || MB == 2, "one or two q heads per wavefront");
+  static_assert(MB == 1 || ALLH, "two heads per wavefront only for groups of 8");
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kKB * 16 * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vtile[kKB * 16 * kVRow];
   const int32_t T = p.run_tiles;
