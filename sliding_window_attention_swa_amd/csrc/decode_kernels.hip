@@ -526,21 +526,31 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 1) decode_stream_kernel(Dec
     };
     bf16x8_t qop[4];
     KvLoad<uint16_t>::to_bf16(qraw, qop);
+    // Loads retire in issue order, so a wait for a round's slots also waits
+    // for everything issued before them.  Each step therefore loads the slots
+    // of the round after next before it issues the next round's K/V rows: the
+    // wait for those slots, one step later, leaves that round's rows in flight
+    // (two rounds of rows in flight per wavefront).  Both are issued
+    // unconditionally (past the split's end, slots_of gives every lane the
+    // split's first key, so such a round re-reads one cached row): under a
+    // branch, each round's waits would also wait for the loads issued after.
     int32_t slA[2], slB[2];
     StreamRound<KV> A, B;
     slots_of(0, slA);
-    if (nround > 1) slots_of(1, slB);
+    slots_of(1, slB);
     __builtin_amdgcn_sched_barrier(0);
     stream_issue<KV>(p, slA, g, lane, A);
     __builtin_amdgcn_sched_barrier(0);
     for (int32_t r = 0; r < nround; r += 2) {
-      if (r + 1 < nround) stream_issue<KV>(p, slB, g, lane, B);
-      if (r + 2 < nround) slots_of(r + 2, slA);
+      slots_of(r + 2, slA);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_issue<KV>(p, slB, g, lane, B);
       __builtin_amdgcn_sched_barrier(0);
       stream_compute<KV>(p, A, key_of(2 * r), key_of(2 * r + 1), k1, qop, vt, lane, acc, m_run, l_run);
       if (r + 1 >= nround) break;
-      if (r + 2 < nround) stream_issue<KV>(p, slA, g, lane, A);
-      if (r + 3 < nround) slots_of(r + 3, slB);
+      slots_of(r + 3, slB);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_issue<KV>(p, slA, g, lane, A);
       __builtin_amdgcn_sched_barrier(0);
       stream_compute<KV>(p, B, key_of(2 * r + 2), key_of(2 * r + 3), k1, qop, vt, lane, acc, m_run, l_run);
     }
