@@ -160,7 +160,11 @@ swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64
  * Decode planning [host]: number of key splits per (request, kv head) and the
  * workspace swa_decode needs.  max_seq_len is a host-side upper bound of
  * seq_lens (a performance hint: any split count gives correct results).
- * SWA layers (window >= 0) use one split and no workspace. */
+ * Windows of up to 256 keys (0 <= window <= 255) use one split and no
+ * workspace.  Full layers (window = -1) and longer windows (a per-layer
+ * sliding_window_size, [SWA] 实现) are split by their key count,
+ * min(max_seq_len, window + 1) for a window, into pieces of at least 512 keys,
+ * up to about four (request, kv head, split) streams per compute unit. */
 swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                              int32_t window, int64_t max_seq_len, int32_t *num_splits,
                              size_t *workspace_bytes);
@@ -217,6 +221,81 @@ swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, c
                               int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,
                               const int64_t *loc, const void *k_new, const void *v_new, int32_t new_dtype,
                               void *out, int32_t out_dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * One decode step of a hybrid model ([SWA] 双池与映射表: SWAKVPool holds a
+ * full pool and an SWA pool, and layers_mapping sends each global layer id to
+ * (its layer number inside its pool, whether it is an SWA layer); 设计:
+ * MiMo-V2-Flash mixes 39 SWA layers with 9 full-attention layers; Attention
+ * backend: the window's translated indices are built once per batch and
+ * shared by every SWA layer; 实现: -1 is full attention).
+ *
+ * The step enqueues, in this order:
+ *   1. swa_translate_window(idx, window) once, when any layer is an SWA layer;
+ *   2. with a store and a mapping: swa_translate_loc(full_loc -> swa_loc) once;
+ *   3. for each global layer l in order, through layers_mapping[l]:
+ *      SWA layer  (swa_layers[pool_layer], window W):  the current token's
+ *                 K/V stored at swa_loc (fused into the decode launch for bf16
+ *                 pools, a separate swa_kv_store otherwise), then swa_decode
+ *                 over the shared window table;
+ *      full layer (full_layers[pool_layer], W = -1): the current token's K/V
+ *                 stored at full_loc, then swa_decode over req_to_token with
+ *                 the split count swa_decode_plan gives for max_seq_len and the
+ *                 widest full layer's kv heads; the split partials use the
+ *                 workspace, one layer at a time.
+ * Every argument of every layer is checked before anything is enqueued; an
+ * error launches nothing.  Without a mapping (idx->full_to_swa NULL, the
+ * single-pool windowed mode) the SWA layers' window table and store use full
+ * slots directly.
+ *   layers_mapping, full_layers, swa_layers, q, out, sinks, k_new, v_new:
+ *                [host] arrays (q, out, sinks, k_new, v_new: n_layers device
+ *                pointers each, indexed by the global layer id; sinks may be
+ *                NULL, or hold NULL entries for layers without sinks).
+ *   q, out       (batch, q_heads, 128) of q_dtype / out_dtype, as swa_decode.
+ *   full_loc     device int64 (batch): full slot of each request's current
+ *                token (position seq_lens[b] - 1); NULL together with k_new and
+ *                v_new: no store.
+ *   swa_loc      device int64 (batch), written by the step (the translated
+ *                full_loc); needed with a store, SWA layers and a mapping.
+ *   k_new, v_new bf16 (batch, the layer's kv_heads, 128) per layer.
+ *   slot_table, table_indptr, table_capacity: the window table
+ *                (capacity >= batch * (window + 1)).
+ *   workspace    swa_decode_step_workspace_bytes(step, idx, max_seq_len) bytes.
+ * Errors: those of the calls above, plus SWA_E_ARG for a mapping entry outside
+ * its pool's layer list, window < 0, or a store with a missing buffer. */
+typedef struct swa_layer_map {
+  int32_t pool_layer; /* index into full_layers or swa_layers */
+  int32_t is_swa;     /* 1: SWA layer, 0: full-attention layer */
+} swa_layer_map_t;
+
+typedef struct swa_decode_step {
+  int32_t n_layers;
+  const swa_layer_map_t *layers_mapping;
+  const swa_kv_layer_t *full_layers;
+  int32_t n_full_layers;
+  const swa_kv_layer_t *swa_layers;
+  int32_t n_swa_layers;
+  int32_t window;     /* the SWA layers' window, >= 0 */
+  int32_t q_heads;
+  int32_t q_dtype;
+  int32_t out_dtype;
+  const void *const *q;
+  void *const *out;
+  const float *const *sinks;
+  float sm_scale;
+  const int64_t *full_loc;
+  int64_t *swa_loc;
+  const void *const *k_new;
+  const void *const *v_new;
+} swa_decode_step_t;
+
+/* [host] Workspace bytes swa_decode_step needs (0 without full layers or on
+ * bad arguments). */
+size_t swa_decode_step_workspace_bytes(const swa_decode_step_t *step, const swa_index_t *idx, int64_t max_seq_len);
+
+swa_status_t swa_decode_step(const swa_decode_step_t *step, const swa_index_t *idx, int64_t max_seq_len,
+                             int32_t *slot_table, int32_t *table_indptr, int64_t table_capacity, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * extend — windowed-causal prefill of a chunk over a cached prefix ([SWA]
@@ -452,6 +531,11 @@ swa_status_t swa_alloc_decode(int32_t batch, int32_t page_size, const int32_t *s
  *   slot_out_of_range  any other slot outside [0, pool_rows)
  * Store part (n_store locs, may be 0 / NULL): locs outside [0, pool_rows), and
  * repeats of a loc outside page 0 (each occurrence after the first counts).
+ * Extend part (qo_indptr may be NULL): qo_bad counts requests b whose query
+ * rows qo_indptr[b] .. qo_indptr[b+1]-1 are not in order inside [0, total_q],
+ * or (for a request that is not bad, with prefix_lens) are not exactly its
+ * seq_lens[b] - prefix_lens[b] new positions.  swa_extend clamps such rows
+ * into [0, total_q] and never reads or writes outside q and out.
  * pool_rows: rows of the pool the window and the locs address (the SWA pool
  * with a map, the full pool without).
  * workspace: device, at least swa_validate_workspace_bytes(pool_rows) bytes,
@@ -467,13 +551,15 @@ typedef struct swa_validate_report {
   int64_t store_locs;
   int64_t store_out_of_range;
   int64_t store_duplicates;
+  int64_t qo_bad;
 } swa_validate_report_t;
 
 size_t swa_validate_workspace_bytes(int64_t pool_rows);
 
-swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
-                          const int64_t *store_loc, int64_t n_store, void *workspace, size_t workspace_bytes,
-                          swa_validate_report_t *report, hipStream_t stream);
+swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens,
+                          const int32_t *qo_indptr, int64_t total_q, int64_t pool_rows, const int64_t *store_loc,
+                          int64_t n_store, void *workspace, size_t workspace_bytes, swa_validate_report_t *report,
+                          hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *swa_status_string(swa_status_t status);

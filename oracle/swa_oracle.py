@@ -579,11 +579,11 @@ def unified_views(raw, anchor, layer_num, kv_heads, head_dim, store_dtype, page_
 # ---------------------------------------------------------------------------
 
 VALIDATE_FIELDS = ("bad_requests", "positions", "full_out_of_range", "tombstones", "sentinels",
-                   "slot_out_of_range", "store_locs", "store_out_of_range", "store_duplicates")
+                   "slot_out_of_range", "store_locs", "store_out_of_range", "store_duplicates", "qo_bad")
 
 
 def validate(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, pool_rows, page_size,
-             prefix_lens=None, store_loc=None):
+             prefix_lens=None, store_loc=None, qo_indptr=None, total_q=0):
     """Counts of violations in a batch's index data.
 
     A request is bad when its req_to_token row, its length or its prefix lies
@@ -591,14 +591,22 @@ def validate(req_to_token, req_pool_idx, seq_lens, full_to_swa, window, pool_row
     positions window_range gives) is classified once: a full slot outside the
     mapping (with a mapping), a tombstone (slot 0), the sentinel (slot -1) or
     another slot outside [0, pool_rows).  Store locations: outside
-    [0, pool_rows), or a repeat of a location outside page 0."""
+    [0, pool_rows), or a repeat of a location outside page 0.  Query rows of
+    an extend (qo_indptr given): a request whose rows qo_indptr[b] ..
+    qo_indptr[b+1]-1 are not in order inside [0, total_q], or, when it is not
+    bad and prefix_lens is given, are not its seq - prefix new positions."""
     r2t = np.asarray(req_to_token)
     n_rows, stride = r2t.shape
     c = dict.fromkeys(VALIDATE_FIELDS, 0)
     for b in range(len(seq_lens)):
         row, n = int(req_pool_idx[b]), int(seq_lens[b])
         pre = n - 1 if prefix_lens is None else int(prefix_lens[b])
-        if not (0 <= row < n_rows) or not (0 <= n <= stride) or (prefix_lens is not None and not 0 <= pre <= n):
+        bad = not (0 <= row < n_rows) or not (0 <= n <= stride) or (prefix_lens is not None and not 0 <= pre <= n)
+        if qo_indptr is not None:
+            q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+            if not 0 <= q0 <= q1 <= total_q or (not bad and prefix_lens is not None and q1 - q0 != n - pre):
+                c["qo_bad"] += 1
+        if bad:
             c["bad_requests"] += 1
             continue
         if n == 0:

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "common.hpp"
 
@@ -134,8 +135,13 @@ swa_status_t swa_ring_locs(const swa_index_t *idx, int64_t ring_rows, const int3
   return from_hip(swa::launch_ring_locs(*idx, ring_rows, prefix_lens, out, n_out, stream));
 }
 
-swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64_t n, const void *k_new,
-                          const void *v_new, int32_t in_dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks of swa_kv_store (every check runs before a launch).
+swa_status_t store_check(const swa_kv_layer_t *layer, const int64_t *loc, int64_t n, const void *k_new,
+                         const void *v_new, int32_t in_dtype) {
   swa_status_t st = check_layer(layer);
   if (st != SWA_OK) return st;
   if (n < 0) return SWA_E_ARG;
@@ -146,6 +152,17 @@ swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64
   if ((static_cast<int64_t>(layer->kv_heads) * layer->head_dim) % 8) return SWA_E_SHAPE;
   if (n == 0) return SWA_OK;
   if (!loc || !k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return SWA_E_ARG;
+  return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+swa_status_t swa_kv_store(const swa_kv_layer_t *layer, const int64_t *loc, int64_t n, const void *k_new,
+                          const void *v_new, int32_t in_dtype, hipStream_t stream) {
+  const swa_status_t st = store_check(layer, loc, n, k_new, v_new, in_dtype);
+  if (st != SWA_OK || n == 0) return st;
   return from_hip(swa::launch_kv_store(*layer, loc, n, k_new, v_new, in_dtype, stream));
 }
 
@@ -156,10 +173,15 @@ swa_status_t swa_decode_plan(int32_t batch, int32_t q_heads, int32_t kv_heads, i
   if (head_dim != kHeadDim) return SWA_E_SHAPE;
   if (!valid_group(q_heads, kv_heads)) return SWA_E_SHAPE;
   int64_t splits = 1;
-  if (window < 0 && batch > 0) {
+  // Full layers, and windows past the one-split window kernel (W + 1 > 256
+  // keys), stream their keys and are split by length: a request holds at most
+  // W + 1 keys of a window.
+  const bool streamed = window < 0 || window > swa::kMaxFusedWindow;
+  if (streamed && batch > 0) {
+    const int64_t keys = (window >= 0 && window + 1 < max_seq_len) ? window + 1 : max_seq_len;
     const int64_t by_fill = (kTargetStreams + static_cast<int64_t>(batch) * kv_heads - 1) /
                             (static_cast<int64_t>(batch) * kv_heads);
-    const int64_t by_len = (max_seq_len + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
+    const int64_t by_len = (keys + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
     splits = by_fill < by_len ? by_fill : by_len;
     if (splits < 1) splits = 1;
     if (splits > kMaxSplits) splits = kMaxSplits;
@@ -181,22 +203,26 @@ size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_d
 
 namespace {
 
-// Checks and launch shared by swa_decode and swa_decode_store (fused: with the
-// store).  An empty batch passes the same checks, may leave q, out, loc and the
-// new rows NULL, and launches nothing.
-swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
-                         const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
-                         int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
-                         int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes, bool fused,
-                         const int64_t *loc, const void *k_new, const void *v_new, hipStream_t stream) {
+// Checks shared by swa_decode and swa_decode_store (fused: with the store);
+// on SWA_OK `a` holds the launch.  An empty batch passes the same checks, may
+// leave q, out, loc and the new rows NULL, and launches nothing.
+swa_status_t decode_prepare(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                            const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                            int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                            int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                            bool fused, const int64_t *loc, const void *k_new, const void *v_new,
+                            swa::DecodeArgs &a) {
   swa_status_t st = check_layer(layer);
   if (st != SWA_OK) return st;
   st = check_index(idx, table_indptr == nullptr);
   if (st != SWA_OK) return st;
   const bool empty = idx->batch == 0;
   if ((!empty && (!q || !out)) || window < -1 || num_splits < 1 || num_splits > kMaxSplits) return SWA_E_ARG;
-  if (!std::isfinite(sm_scale)) return SWA_E_ARG;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return SWA_E_ARG;
   if (table_indptr && (!slot_table || table_capacity < 0)) return SWA_E_ARG;
+  // the kernels translate through the window table only: a mapping without
+  // one would read full-pool slots from this pool
+  if (idx->full_to_swa && !table_indptr) return SWA_E_ARG;
   if (layer->head_dim != kHeadDim) return SWA_E_SHAPE;
   if (!valid_group(q_heads, layer->kv_heads)) return SWA_E_SHAPE;
   if (layer->rows > kMaxRows) return SWA_E_SHAPE;
@@ -215,7 +241,7 @@ swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const 
     if (!mfma_path) return SWA_E_DTYPE;
     if (window < 0 || window > swa::kMaxFusedWindow || num_splits != 1) return SWA_E_SHAPE;
   }
-  swa::DecodeArgs a{};
+  a = swa::DecodeArgs{};
   a.q = q;
   a.q_dtype = q_dtype;
   a.q_heads = q_heads;
@@ -234,6 +260,19 @@ swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const 
   a.new_loc = loc;
   a.k_new = k_new;
   a.v_new = v_new;
+  return SWA_OK;
+}
+
+swa_status_t decode_impl(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                         const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                         int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                         int32_t out_dtype, int32_t num_splits, void *workspace, size_t workspace_bytes, bool fused,
+                         const int64_t *loc, const void *k_new, const void *v_new, hipStream_t stream) {
+  swa::DecodeArgs a;
+  const swa_status_t st = decode_prepare(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity,
+                                         window, sinks, sm_scale, out, out_dtype, num_splits, workspace,
+                                         workspace_bytes, fused, loc, k_new, v_new, a);
+  if (st != SWA_OK) return st;
   return from_hip(swa::launch_decode(a, stream));
 }
 
@@ -263,6 +302,142 @@ swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, c
 
 namespace {
 
+// One layer's work in a decode step, checked before anything is launched.
+struct StepLaunch {
+  bool store;                 // swa_kv_store first
+  swa_kv_layer_t store_layer;
+  const int64_t *store_loc;
+  const void *k_new, *v_new;
+  swa::DecodeArgs decode;
+};
+
+swa_status_t step_plan(const swa_decode_step_t *st, const swa_index_t *idx, int64_t max_seq_len,
+                       int32_t *full_splits, size_t *workspace_bytes) {
+  *full_splits = 1;
+  *workspace_bytes = 0;
+  if (!st || !idx || idx->batch < 0 || max_seq_len < 0 || st->n_layers < 0) return SWA_E_ARG;
+  if (st->n_layers > 0 && !st->layers_mapping) return SWA_E_ARG;
+  if (st->n_full_layers < 0 || st->n_swa_layers < 0) return SWA_E_ARG;
+  if ((st->n_full_layers > 0 && !st->full_layers) || (st->n_swa_layers > 0 && !st->swa_layers)) return SWA_E_ARG;
+  int32_t full_kv = 0;
+  for (int32_t l = 0; l < st->n_layers; ++l) {
+    const swa_layer_map_t &m = st->layers_mapping[l];
+    const int32_t n = m.is_swa ? st->n_swa_layers : st->n_full_layers;
+    if ((m.is_swa != 0 && m.is_swa != 1) || m.pool_layer < 0 || m.pool_layer >= n) return SWA_E_ARG;
+    if (!m.is_swa) {
+      const int32_t kv = st->full_layers[m.pool_layer].kv_heads;
+      full_kv = kv > full_kv ? kv : full_kv;
+    }
+  }
+  if (full_kv == 0) return SWA_OK;
+  // the split count of the widest full layer's plan serves every full layer
+  // (the workspace holds batch * q_heads * splits partials whatever kv_heads is)
+  size_t ws = 0;
+  const swa_status_t s = swa_decode_plan(idx->batch, st->q_heads, full_kv, kHeadDim, -1, max_seq_len, full_splits, &ws);
+  if (s != SWA_OK) return s;
+  *workspace_bytes = ws;
+  return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t swa_decode_step_workspace_bytes(const swa_decode_step_t *step, const swa_index_t *idx, int64_t max_seq_len) {
+  int32_t splits;
+  size_t ws;
+  return step_plan(step, idx, max_seq_len, &splits, &ws) == SWA_OK ? ws : 0;
+}
+
+swa_status_t swa_decode_step(const swa_decode_step_t *st, const swa_index_t *idx, int64_t max_seq_len,
+                             int32_t *slot_table, int32_t *table_indptr, int64_t table_capacity, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  int32_t full_splits;
+  size_t ws_need;
+  swa_status_t status = step_plan(st, idx, max_seq_len, &full_splits, &ws_need);
+  if (status != SWA_OK) return status;
+  if (!st->q || !st->out) return SWA_E_ARG;
+  if (st->window < 0) return SWA_E_ARG;
+  const bool store = st->k_new || st->v_new || st->full_loc;
+  if (store && (!st->k_new || !st->v_new || !st->full_loc)) return SWA_E_ARG;
+  const int32_t B = idx->batch;
+  bool any_swa = false;
+  for (int32_t l = 0; l < st->n_layers; ++l) any_swa = any_swa || st->layers_mapping[l].is_swa;
+  const bool translate = store && any_swa && idx->full_to_swa;  // the store's SWA slots: full_loc translated
+  if (translate && !st->swa_loc) return SWA_E_ARG;
+  const int64_t *swa_loc = idx->full_to_swa ? st->swa_loc : st->full_loc;
+  if (any_swa) {
+    status = check_index(idx, true);
+    if (status != SWA_OK) return status;
+    if (!table_indptr || table_capacity < 0 || (table_capacity > 0 && !slot_table)) return SWA_E_ARG;
+  }
+  if (translate && B > 0 && idx->map_len < 2) return SWA_E_ARG;
+  // full layers read req_to_token directly: the same batch without the mapping
+  swa_index_t full_idx = *idx;
+  full_idx.full_to_swa = nullptr;
+  full_idx.map_len = 0;
+
+  std::vector<StepLaunch> plan(static_cast<size_t>(st->n_layers));
+  for (int32_t l = 0; l < st->n_layers; ++l) {
+    const swa_layer_map_t &m = st->layers_mapping[l];
+    const swa_kv_layer_t *layer = m.is_swa ? &st->swa_layers[m.pool_layer] : &st->full_layers[m.pool_layer];
+    const float *sinks = st->sinks ? st->sinks[l] : nullptr;
+    StepLaunch &x = plan[static_cast<size_t>(l)];
+    x.store = false;
+    const void *kn = store ? st->k_new[l] : nullptr;
+    const void *vn = store ? st->v_new[l] : nullptr;
+    // the new token is fused into the window kernel for bf16 pools; e4m3 pools
+    // store with their own launch (the fused e4m3 kernel holds more registers,
+    // which costs a workgroup per CU)
+    const bool fuse = store && m.is_swa && layer->dtype == SWA_BF16 && st->window <= swa::kMaxFusedWindow &&
+                      st->q_dtype == SWA_BF16;
+    if (store && !fuse) {
+      x.store = true;
+      x.store_layer = *layer;
+      x.store_loc = m.is_swa ? swa_loc : st->full_loc;
+      x.k_new = kn;
+      x.v_new = vn;
+      status = store_check(layer, x.store_loc, B, kn, vn, SWA_BF16);
+      if (status != SWA_OK) return status;
+    }
+    if (m.is_swa) {
+      status = decode_prepare(st->q[l], st->q_dtype, st->q_heads, layer, idx, slot_table, table_indptr,
+                              table_capacity, st->window, sinks, st->sm_scale, st->out[l], st->out_dtype, 1, nullptr, 0,
+                              fuse, fuse ? swa_loc : nullptr, fuse ? kn : nullptr, fuse ? vn : nullptr, x.decode);
+    } else {
+      status = decode_prepare(st->q[l], st->q_dtype, st->q_heads, layer, &full_idx, nullptr, nullptr, 0, -1, sinks,
+                              st->sm_scale, st->out[l], st->out_dtype, full_splits, workspace, workspace_bytes, false,
+                              nullptr, nullptr, nullptr, x.decode);
+    }
+    if (status != SWA_OK) return status;
+  }
+  if (B == 0) return SWA_OK;
+
+  // a3 once for every SWA layer, a2 once for the store, then the layers in order
+  if (any_swa) {
+    status = from_hip(swa::launch_translate_window(*idx, st->window, 0, nullptr, slot_table, table_indptr,
+                                                   table_capacity, stream));
+    if (status != SWA_OK) return status;
+  }
+  if (translate) {
+    status = from_hip(swa::launch_translate_loc(st->full_loc, B, idx->full_to_swa, idx->map_len, st->swa_loc, stream));
+    if (status != SWA_OK) return status;
+  }
+  for (const StepLaunch &x : plan) {
+    if (x.store) {
+      status = from_hip(swa::launch_kv_store(x.store_layer, x.store_loc, B, x.k_new, x.v_new, SWA_BF16, stream));
+      if (status != SWA_OK) return status;
+    }
+    status = from_hip(swa::launch_decode(x.decode, stream));
+    if (status != SWA_OK) return status;
+  }
+  return SWA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
 swa_status_t extend_impl(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,
                          const int32_t *prefix_lens, int64_t total_q, const swa_kv_layer_t *layer,
                          const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
@@ -272,10 +447,11 @@ swa_status_t extend_impl(const void *q, int32_t q_dtype, int32_t q_heads, const 
   if (st != SWA_OK) return st;
   st = check_index(idx, true);
   if (st != SWA_OK) return st;
-  if (total_q < 0 || window < -1 || chunk < 0 || !std::isfinite(sm_scale)) return SWA_E_ARG;
+  if (total_q < 0 || window < -1 || chunk < 0 || !(sm_scale > 0.f) || !std::isfinite(sm_scale)) return SWA_E_ARG;
   if (idx->batch > 0 && (!qo_indptr || !prefix_lens)) return SWA_E_ARG;
   if (total_q > 0 && (!q || !out)) return SWA_E_ARG;
   if (table_indptr && (!slot_table || table_capacity < 0)) return SWA_E_ARG;
+  if (idx->full_to_swa && !table_indptr) return SWA_E_ARG;  // as in decode: no translation without the table
   if (layer->head_dim != kHeadDim) return SWA_E_SHAPE;
   if (!valid_group(q_heads, layer->kv_heads)) return SWA_E_SHAPE;
   if (layer->rows > kMaxRows || total_q > INT32_MAX) return SWA_E_SHAPE;
@@ -523,10 +699,12 @@ size_t swa_validate_workspace_bytes(int64_t pool_rows) {
   return static_cast<size_t>(kValidateCounterBytes + (pool_rows + 31) / 32 * 4);
 }
 
-swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
-                          const int64_t *store_loc, int64_t n_store, void *workspace, size_t workspace_bytes,
-                          swa_validate_report_t *report, hipStream_t stream) {
-  if (!report || !idx || idx->batch < 0 || window < -1 || pool_rows < 0 || n_store < 0) return SWA_E_ARG;
+swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t *prefix_lens,
+                          const int32_t *qo_indptr, int64_t total_q, int64_t pool_rows, const int64_t *store_loc,
+                          int64_t n_store, void *workspace, size_t workspace_bytes, swa_validate_report_t *report,
+                          hipStream_t stream) {
+  if (!report || !idx || idx->batch < 0 || window < -1 || pool_rows < 0 || n_store < 0 || total_q < 0)
+    return SWA_E_ARG;
   if (idx->page_size < 1) return SWA_E_ARG;
   swa_status_t st = check_index(idx, true);
   if (st != SWA_OK) return st;
@@ -534,8 +712,8 @@ swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t 
   if (!workspace || !aligned16(workspace)) return SWA_E_WORKSPACE;
   const size_t need = n_store > 0 ? swa_validate_workspace_bytes(pool_rows) : kValidateCounterBytes;
   if (workspace_bytes < need) return SWA_E_WORKSPACE;
-  hipError_t e = swa::launch_validate(*idx, window, prefix_lens, pool_rows, store_loc, n_store, workspace,
-                                      kValidateCounterBytes, stream);
+  hipError_t e = swa::launch_validate(*idx, window, prefix_lens, qo_indptr, total_q, pool_rows, store_loc, n_store,
+                                      workspace, kValidateCounterBytes, stream);
   if (e != hipSuccess) return SWA_E_HIP;
   int64_t c[16];
   e = hipMemcpyAsync(c, workspace, sizeof(c), hipMemcpyDeviceToHost, stream);
@@ -550,6 +728,7 @@ swa_status_t swa_validate(const swa_index_t *idx, int32_t window, const int32_t 
   report->store_locs = c[6];
   report->store_out_of_range = c[7];
   report->store_duplicates = c[8];
+  report->qo_bad = c[9];
   return SWA_OK;
 }
 

@@ -155,9 +155,9 @@ struct DecodeArgs {
 constexpr int32_t kMaxFusedWindow = 255;
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
-hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
-                           const int64_t *store_loc, int64_t n_store, void *workspace, int64_t counters_bytes,
-                           hipStream_t stream);
+hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
+                           const int32_t *qo_indptr, int64_t total_q, int64_t pool_rows, const int64_t *store_loc,
+                           int64_t n_store, void *workspace, int64_t counters_bytes, hipStream_t stream);
 
 // Eviction works on chunks of positions that start at page boundaries: the
 // smallest multiple of the page size that is at least one apply pass (256

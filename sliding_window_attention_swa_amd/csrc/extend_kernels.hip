@@ -97,11 +97,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Queries of request b.
-__device__ __forceinline__ int32_t new_count(const ExtendParams &p, int32_t b) {
-  int32_t n = p.qo_indptr[b + 1] - p.qo_indptr[b];
-  return n > 0 ? n : 0;
+// Query rows of request b: [qo0, qo0 + n).  The entries are clamped into
+// [0, total_q], so a bad qo_indptr never reads or writes outside q and out (a
+// decreasing pair is an empty request).
+struct QoRows {
+  int32_t qo0;
+  int32_t n;
+};
+
+__device__ __forceinline__ QoRows qo_rows(const ExtendParams &p, int32_t b) {
+  int64_t lo = p.qo_indptr[b], hi = p.qo_indptr[b + 1];
+  if (lo < 0) lo = 0;
+  if (lo > p.total_q) lo = p.total_q;
+  if (hi > p.total_q) hi = p.total_q;
+  return QoRows{static_cast<int32_t>(lo), hi > lo ? static_cast<int32_t>(hi - lo) : 0};
 }
+
+__device__ __forceinline__ int32_t new_count(const ExtendParams &p, int32_t b) { return qo_rows(p, b).n; }
 
 // Key position -> pool slot for one request: src[pos - pos_base], 0 <= . < hi.
 struct KeySrc {
@@ -586,8 +598,9 @@ __device__ __forceinline__ void run_steady(const ExtendParams &p, uint16_t *ktil
   // sinks of this wave's heads) is read once here: a load inside the loop
   // would make the wave wait for all of its older memory operations, i.e. the
   // previous tile's output stores and the prefetches.
-  const int32_t n_new = new_count(p, b);
-  const int32_t qo0 = p.qo_indptr[b];
+  const QoRows qrows = qo_rows(p, b);
+  const int32_t n_new = qrows.n;
+  const int32_t qo0 = qrows.qo0;
   int32_t seq = p.seq_lens[b];
   if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
   const int32_t prefix = p.prefix_lens[b];
@@ -726,8 +739,9 @@ __device__ __forceinline__ void run_general(const ExtendParams &p, uint16_t *kti
   // sinks of this wave's heads) is read once here: a load inside the loop
   // would make the wave wait for all of its older memory operations, i.e. the
   // previous tile's output stores and the prefetches.
-  const int32_t n_new = new_count(p, b);
-  const int32_t qo0 = p.qo_indptr[b];
+  const QoRows qrows = qo_rows(p, b);
+  const int32_t n_new = qrows.n;
+  const int32_t qo0 = qrows.qo0;
   int32_t seq = p.seq_lens[b];
   if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
   const int32_t prefix = p.prefix_lens[b];

@@ -9,7 +9,9 @@
 //     eviction only releases positions that left the window;
 //   * req_to_token rows, full slots and SWA slots index inside their tables;
 //   * a store location is used once per batch, except in page 0, the padding
-//     sink that padded (dummy) writes share.
+//     sink that padded (dummy) writes share;
+//   * (extend) request b's query rows qo_indptr[b] .. qo_indptr[b+1]-1 lie in
+//     order inside the query array and are its new positions, seq - prefix.
 //
 // Workspace layout (device, caller-owned): 16 int64 counters, then a bitmap of
 // ceil(pool_rows / 32) 32-bit words used to find repeated store locations.
@@ -28,6 +30,7 @@ enum Counter {
   kStoreLocs,
   kStoreOutOfRange,
   kStoreDuplicates,
+  kQoBad,
   kNumCounters
 };
 
@@ -54,7 +57,8 @@ __device__ void block_add(unsigned long long *counters, int c, int64_t v, int64_
 
 // One workgroup per request: walk its window and classify every position.
 __global__ void __launch_bounds__(256) validate_window_kernel(swa_index_t idx, int32_t window,
-                                                              const int32_t *prefix_lens, int64_t pool_rows,
+                                                              const int32_t *prefix_lens, const int32_t *qo_indptr,
+                                                              int64_t total_q, int64_t pool_rows,
                                                               unsigned long long *counters) {
   __shared__ int64_t red[4];
   const int32_t b = blockIdx.x;
@@ -91,6 +95,14 @@ __global__ void __launch_bounds__(256) validate_window_kernel(swa_index_t idx, i
       }
     }
   }
+  // query rows of an extend: inside [0, total_q], in order, and (for a request
+  // whose row and lengths are valid) as many as its new positions
+  bool qo_bad = false;
+  if (qo_indptr && threadIdx.x == 0) {
+    const int64_t q0 = qo_indptr[b], q1 = qo_indptr[b + 1];
+    qo_bad = q0 < 0 || q1 < q0 || q1 > total_q || (!bad && prefix_lens && q1 - q0 != len - pre);
+  }
+  block_add(counters, kQoBad, qo_bad ? 1 : 0, red);
   block_add(counters, kBadRequests, (bad && threadIdx.x == 0) ? 1 : 0, red);
   block_add(counters, kPositions, n_pos, red);
   block_add(counters, kFullOutOfRange, n_full, red);
@@ -125,9 +137,9 @@ __global__ void __launch_bounds__(256) validate_store_kernel(const int64_t *loc,
 
 }  // namespace
 
-hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens, int64_t pool_rows,
-                           const int64_t *store_loc, int64_t n_store, void *workspace, int64_t counters_bytes,
-                           hipStream_t stream) {
+hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
+                           const int32_t *qo_indptr, int64_t total_q, int64_t pool_rows, const int64_t *store_loc,
+                           int64_t n_store, void *workspace, int64_t counters_bytes, hipStream_t stream) {
   unsigned long long *counters = static_cast<unsigned long long *>(workspace);
   uint32_t *bitmap = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + counters_bytes);
   const int64_t words = counters_bytes / 4 + (store_loc && n_store > 0 ? (pool_rows + 31) / 32 : 0);
@@ -139,7 +151,7 @@ hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t
   if (e != hipSuccess) return e;
   if (idx.batch > 0) {
     hipLaunchKernelGGL(validate_window_kernel, dim3(static_cast<uint32_t>(idx.batch)), dim3(256), 0, stream, idx,
-                       window, prefix_lens, pool_rows, counters);
+                       window, prefix_lens, qo_indptr, total_q, pool_rows, counters);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -30,7 +30,8 @@ EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_
            "swa_evict_workspace_bytes", "swa_evict", "swa_alloc_pages_needed", "swa_alloc_extend",
            "swa_alloc_decode", "swa_unified_pool_bytes", "swa_unified_layer_views", "swa_translate_kernel_ids",
            "swa_translate_window_unified", "swa_translate_window_chunked", "swa_extend_chunked",
-           "swa_translate_window_ring", "swa_ring_locs", "swa_decode_workspace_bytes", "swa_status_string")
+           "swa_translate_window_ring", "swa_ring_locs", "swa_decode_workspace_bytes", "swa_decode_step",
+           "swa_decode_step_workspace_bytes", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -60,12 +61,27 @@ class IndexStruct(ctypes.Structure):
                 ("map_len", ctypes.c_int64), ("batch", ctypes.c_int32), ("page_size", ctypes.c_int32)]
 
 
+class LayerMapStruct(ctypes.Structure):
+    _fields_ = [("pool_layer", ctypes.c_int32), ("is_swa", ctypes.c_int32)]
+
+
+class DecodeStepStruct(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("layers_mapping", ctypes.POINTER(LayerMapStruct)),
+                ("full_layers", ctypes.POINTER(KvLayerStruct)), ("n_full_layers", ctypes.c_int32),
+                ("swa_layers", ctypes.POINTER(KvLayerStruct)), ("n_swa_layers", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("q", ctypes.POINTER(ctypes.c_void_p)),
+                ("out", ctypes.POINTER(ctypes.c_void_p)), ("sinks", ctypes.POINTER(ctypes.c_void_p)),
+                ("sm_scale", ctypes.c_float), ("full_loc", ctypes.c_void_p), ("swa_loc", ctypes.c_void_p),
+                ("k_new", ctypes.POINTER(ctypes.c_void_p)), ("v_new", ctypes.POINTER(ctypes.c_void_p))]
+
+
 class FreeListStruct(ctypes.Structure):
     _fields_ = [("pages", ctypes.c_void_p), ("count", ctypes.c_int64)]
 
 
 VALIDATE_FIELDS = ("bad_requests", "positions", "full_out_of_range", "tombstones", "sentinels", "slot_out_of_range",
-                   "store_locs", "store_out_of_range", "store_duplicates")
+                   "store_locs", "store_out_of_range", "store_duplicates", "qo_bad")
 
 
 class ValidateReportStruct(ctypes.Structure):
@@ -88,7 +104,7 @@ _sig = {
     "swa_extend": (_i32, [_p, _i32, _i32, _p, _p, _i64, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct),
                           _p, _p, _i64, _i32, _p, _f32, _p, _i32, _p]),
     "swa_validate_workspace_bytes": (_sz, [_i64]),
-    "swa_validate": (_i32, [ctypes.POINTER(IndexStruct), _i32, _p, _i64, _p, _i64, _p, _sz,
+    "swa_validate": (_i32, [ctypes.POINTER(IndexStruct), _i32, _p, _p, _i64, _i64, _p, _i64, _p, _sz,
                             ctypes.POINTER(ValidateReportStruct), _p]),
     "swa_evict_workspace_bytes": (_sz, [_i32, _i64, _i32]),
     "swa_evict": (_i32, [ctypes.POINTER(IndexStruct), _p, _p, _p, _p, _i32, _i32, _i32, _p, _i64, _p, _p, _sz, _p]),
@@ -109,6 +125,9 @@ _sig = {
     "swa_translate_window_ring": (_i32, [ctypes.POINTER(IndexStruct), _i64, _i32, _i32, _p, _p, _p, _i64, _p]),
     "swa_ring_locs": (_i32, [ctypes.POINTER(IndexStruct), _i64, _p, _p, _i64, _p]),
     "swa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "swa_decode_step_workspace_bytes": (_sz, [ctypes.POINTER(DecodeStepStruct), ctypes.POINTER(IndexStruct), _i64]),
+    "swa_decode_step": (_i32, [ctypes.POINTER(DecodeStepStruct), ctypes.POINTER(IndexStruct), _i64, _p, _p, _i64, _p,
+                               _sz, _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -282,6 +301,56 @@ def swa_decode_store(q: torch.Tensor, layer: KvLayer, index: IndexTables, window
                                 _ptr(out, name="out"), dtype_code(out), _stream(stream)), "swa_decode_store")
 
 
+class DecodeStep:
+    """The arguments of swa_decode_step, marshalled once (the host arrays are
+    kept alive here).  layers_mapping: one (pool_layer, is_swa) pair per global
+    layer; q, out (and sinks, k_new, v_new when given): one tensor (or None for
+    sinks) per global layer."""
+
+    def __init__(self, layers_mapping, full_layers, swa_layers, window: int, q, out, sinks=None,
+                 sm_scale: Optional[float] = None, full_loc: Optional[torch.Tensor] = None,
+                 swa_loc: Optional[torch.Tensor] = None, k_new=None, v_new=None):
+        n = len(layers_mapping)
+        if len(q) != n or len(out) != n or (sinks is not None and len(sinks) != n):
+            raise ValueError("q, out and sinks need one entry per layer")
+        if (k_new is None) != (v_new is None) or (k_new is not None and (len(k_new) != n or len(v_new) != n)):
+            raise ValueError("k_new and v_new need one entry per layer, or neither is given")
+        self._map = (LayerMapStruct * max(n, 1))(*[LayerMapStruct(int(p), int(bool(w))) for p, w in layers_mapping])
+        self._full = (KvLayerStruct * max(len(full_layers), 1))(*[ly.struct() for ly in full_layers])
+        self._swa = (KvLayerStruct * max(len(swa_layers), 1))(*[ly.struct() for ly in swa_layers])
+        ptrs = lambda ts, name: (ctypes.c_void_p * max(n, 1))(*[_ptr(t, name=name) for t in ts])  # noqa: E731
+        self._q, self._out = ptrs(q, "q"), ptrs(out, "out")
+        self._sinks = None if sinks is None else (ctypes.c_void_p * max(n, 1))(
+            *[_ptr(t, torch.float32, "sinks") for t in sinks])
+        self._k = None if k_new is None else ptrs(k_new, "k_new")
+        self._v = None if v_new is None else ptrs(v_new, "v_new")
+        self.tensors = (q, out, sinks, k_new, v_new, full_loc, swa_loc, full_layers, swa_layers)
+        scale = sm_scale if sm_scale is not None else q[0].shape[2] ** -0.5
+        cast = lambda a, t: None if a is None else ctypes.cast(a, ctypes.POINTER(t))  # noqa: E731
+        self.struct = DecodeStepStruct(
+            n, cast(self._map, LayerMapStruct), cast(self._full, KvLayerStruct), len(full_layers),
+            cast(self._swa, KvLayerStruct), len(swa_layers), window, q[0].shape[1], dtype_code(q[0]),
+            dtype_code(out[0]), cast(self._q, ctypes.c_void_p), cast(self._out, ctypes.c_void_p),
+            cast(self._sinks, ctypes.c_void_p), scale, _ptr(full_loc, torch.int64, "full_loc"),
+            _ptr(swa_loc, torch.int64, "swa_loc"), cast(self._k, ctypes.c_void_p), cast(self._v, ctypes.c_void_p))
+
+    def workspace_bytes(self, index: IndexTables, max_seq_len: int) -> int:
+        ix = index.struct()
+        return lib.swa_decode_step_workspace_bytes(ctypes.byref(self.struct), ctypes.byref(ix), max_seq_len)
+
+
+def swa_decode_step(step: DecodeStep, index: IndexTables, max_seq_len: int, slot_table: torch.Tensor,
+                    table_indptr: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None):
+    """One decode step over every layer of a hybrid model (see swa.h)."""
+    ix = index.struct()
+    _check(lib.swa_decode_step(ctypes.byref(step.struct), ctypes.byref(ix), max_seq_len,
+                               _ptr(slot_table, torch.int32, "slot_table"),
+                               _ptr(table_indptr, torch.int32, "table_indptr"), slot_table.numel(),
+                               _ptr(workspace, name="workspace"),
+                               0 if workspace is None else workspace.numel() * workspace.element_size(),
+                               _stream(stream)), "swa_decode_step")
+
+
 def swa_extend(q: torch.Tensor, qo_indptr: torch.Tensor, prefix_lens: torch.Tensor, layer: KvLayer,
                index: IndexTables, window: int, out: torch.Tensor, sinks: Optional[torch.Tensor] = None,
                sm_scale: Optional[float] = None, slot_table: Optional[torch.Tensor] = None,
@@ -301,7 +370,8 @@ def swa_extend(q: torch.Tensor, qo_indptr: torch.Tensor, prefix_lens: torch.Tens
 
 def swa_validate(index: IndexTables, window: int, pool_rows: int, prefix_lens: Optional[torch.Tensor] = None,
                  store_loc: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                 use_map: bool = True, stream=None) -> dict:
+                 use_map: bool = True, qo_indptr: Optional[torch.Tensor] = None, total_q: int = 0,
+                 stream=None) -> dict:
     """Counts of contract violations in the batch's index data (synchronous).
     The workspace is allocated here when not given."""
     if workspace is None:
@@ -309,7 +379,8 @@ def swa_validate(index: IndexTables, window: int, pool_rows: int, prefix_lens: O
         workspace = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.int32, device=index.seq_lens.device)
     rep = ValidateReportStruct()
     ix = index.struct(with_map=use_map)
-    _check(lib.swa_validate(ctypes.byref(ix), window, _ptr(prefix_lens, torch.int32, "prefix_lens"), pool_rows,
+    _check(lib.swa_validate(ctypes.byref(ix), window, _ptr(prefix_lens, torch.int32, "prefix_lens"),
+                            _ptr(qo_indptr, torch.int32, "qo_indptr"), total_q, pool_rows,
                             _ptr(store_loc, torch.int64, "store_loc"), 0 if store_loc is None else store_loc.numel(),
                             _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
                             ctypes.byref(rep), _stream(stream)), "swa_validate")

@@ -82,9 +82,9 @@ def index(swa, batch=2, map_ptr=FAKE):
 
 
 def decode(swa, ly, ix, q_dtype=1, q_heads=64, out_dtype=0, splits=1, ws=None, ws_bytes=0, window=128,
-           table=FAKE, indptr=FAKE, q=FAKE, out=FAKE):
+           table=FAKE, indptr=FAKE, q=FAKE, out=FAKE, scale=0.088):
     return swa.lib.swa_decode(q, q_dtype, q_heads, ctypes.byref(ly), ctypes.byref(ix), table, indptr, 1000, window,
-                              None, 0.088, out, out_dtype, splits, ws, ws_bytes, None)
+                              None, scale, out, out_dtype, splits, ws, ws_bytes, None)
 
 
 def test_decode_argument_errors(swa):
@@ -112,6 +112,20 @@ def test_decode_argument_errors(swa):
     assert decode(swa, ly, bad_ix) == E.SWA_E_ARG
     bad_ix = swa.IndexStruct(None, 3, 100, FAKE, FAKE, None, 0, 2, 16)      # full layer, no req_to_token
     assert decode(swa, ly, bad_ix, table=None, indptr=None, window=-1) == E.SWA_E_ARG
+    # a mapping without the window table: the kernels would read full-pool
+    # slots from this pool, so the call is refused
+    assert decode(swa, ly, ix, table=None, indptr=None) == E.SWA_E_ARG
+    assert decode(swa, ly, ix, table=None, indptr=None, window=-1) == E.SWA_E_ARG
+    # the softmax scale must be a positive finite number
+    for bad in (0.0, -0.088, float("nan"), float("inf")):
+        assert decode(swa, ly, ix, scale=bad) == E.SWA_E_ARG
+    assert lib_fused_scale(swa, ly, ix, 0.0) == E.SWA_E_ARG
+    assert lib_fused_scale(swa, ly, ix, -1.0) == E.SWA_E_ARG
+
+
+def lib_fused_scale(swa, ly, ix, scale):
+    return swa.lib.swa_decode_store(FAKE, 1, 64, ctypes.byref(ly), ctypes.byref(ix), FAKE, FAKE, 1000, 128, None,
+                                    scale, FAKE, FAKE, FAKE, 1, FAKE, 0, None)
 
 
 def test_empty_batch_launches_nothing(swa):
@@ -139,9 +153,10 @@ def test_extend_argument_errors(swa):
     E = swa
     ly, ix = layer(swa), index(swa)
 
-    def ext(ly=ly, ix=ix, q_dtype=1, out_dtype=0, total=100, qo=FAKE, pre=FAKE, window=128):
-        return swa.lib.swa_extend(FAKE, q_dtype, 64, qo, pre, total, ctypes.byref(ly), ctypes.byref(ix), FAKE, FAKE,
-                                  1000, window, None, 0.088, FAKE, out_dtype, None)
+    def ext(ly=ly, ix=ix, q_dtype=1, out_dtype=0, total=100, qo=FAKE, pre=FAKE, window=128, table=FAKE, indptr=FAKE,
+            scale=0.088):
+        return swa.lib.swa_extend(FAKE, q_dtype, 64, qo, pre, total, ctypes.byref(ly), ctypes.byref(ix), table, indptr,
+                                  1000, window, None, scale, FAKE, out_dtype, None)
 
     assert ext(ly=layer(swa, dtype=2)) == E.SWA_E_DTYPE   # extend takes bf16 K/V
     assert ext(q_dtype=0) == E.SWA_E_DTYPE
@@ -151,6 +166,9 @@ def test_extend_argument_errors(swa):
     assert ext(total=-1) == E.SWA_E_ARG
     assert ext(total=1 << 31) == E.SWA_E_SHAPE
     assert ext(window=-3) == E.SWA_E_ARG
+    assert ext(table=None, indptr=None) == E.SWA_E_ARG        # a mapping needs the window table
+    for bad in (0.0, -1.0, float("nan")):
+        assert ext(scale=bad) == E.SWA_E_ARG
 
 
 def test_store_and_translate_argument_errors(swa):
@@ -194,8 +212,9 @@ def test_validate_argument_errors(swa):
     assert need == 128 + (1000 + 31) // 32 * 4
     assert lib.swa_validate_workspace_bytes(-1) == 0
 
-    def val(ix=ix, window=128, pre=None, rows=1000, loc=FAKE, n=8, ws=FAKE, ws_bytes=need, report=rep):
-        return lib.swa_validate(ctypes.byref(ix), window, pre, rows, loc, n, ws, ws_bytes,
+    def val(ix=ix, window=128, pre=None, rows=1000, loc=FAKE, n=8, ws=FAKE, ws_bytes=need, report=rep, qo=None,
+            total_q=0):
+        return lib.swa_validate(ctypes.byref(ix), window, pre, qo, total_q, rows, loc, n, ws, ws_bytes,
                                 None if report is None else ctypes.byref(report), None)
 
     assert val(report=None) == E.SWA_E_ARG
@@ -206,6 +225,7 @@ def test_validate_argument_errors(swa):
     assert val(ws=None) == E.SWA_E_WORKSPACE
     assert val(ws=FAKE + 8) == E.SWA_E_WORKSPACE              # misaligned
     assert val(ws_bytes=need - 4) == E.SWA_E_WORKSPACE
+    assert val(qo=FAKE, total_q=-1) == E.SWA_E_ARG
     no_page = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, FAKE, 50, 2, 0)
     assert val(ix=no_page) == E.SWA_E_ARG
 
@@ -379,8 +399,11 @@ def test_variant_argument_errors(swa):
     ly = layer(swa)
     assert lib.swa_extend_chunked(FAKE, 1, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, 128,
                                   -1, None, 0.088, FAKE, 0, None) == E.SWA_E_ARG
-    assert lib.swa_extend_chunked(FAKE, 0, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, 128,
-                                  64, None, 0.088, FAKE, 0, None) == E.SWA_E_DTYPE
+    one_pool = index(swa, map_ptr=None)
+    assert lib.swa_extend_chunked(FAKE, 0, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(one_pool), None, None, 0,
+                                  128, 64, None, 0.088, FAKE, 0, None) == E.SWA_E_DTYPE
+    assert lib.swa_extend_chunked(FAKE, 1, 64, FAKE, FAKE, 16, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, 128,
+                                  64, None, 0.088, FAKE, 0, None) == E.SWA_E_ARG   # a mapping needs the table
 
 
 def test_decode_workspace_bytes_bounds_every_plan(swa):
@@ -393,3 +416,57 @@ def test_decode_workspace_bytes_bounds_every_plan(swa):
             assert ws.value <= bound
     assert lib.swa_decode_workspace_bytes(4, 8, 128, 512) == 0          # one split: no workspace
     assert lib.swa_decode_workspace_bytes(4, 8, 64, 5000) == 0          # head_dim other than 128
+
+
+def step_struct(swa, n_swa=3, n_full=2, mapping=None, window=128, q=True, store=False, swa_loc=True,
+                full_kv=4):
+    """A decode-step descriptor over fake device pointers (never dereferenced:
+    every case below fails its checks, or has an empty batch, before a launch)."""
+    mapping = [(0, 0), (0, 1), (1, 1), (1, 0), (2, 1)] if mapping is None else mapping
+    n = len(mapping)
+    keep = []
+
+    def arr(t, vals):
+        a = (t * max(len(vals), 1))(*vals)
+        keep.append(a)
+        return ctypes.cast(a, ctypes.POINTER(t))
+
+    m = arr(swa.LayerMapStruct, [swa.LayerMapStruct(p, s) for p, s in mapping])
+    full = arr(swa.KvLayerStruct, [layer(swa, kv_heads=full_kv) for _ in range(n_full)])
+    swal = arr(swa.KvLayerStruct, [layer(swa) for _ in range(n_swa)])
+    ptrs = arr(ctypes.c_void_p, [FAKE] * n)
+    st = swa.DecodeStepStruct(n, m, full, n_full, swal, n_swa, window, 64, 1, 0, ptrs if q else None, ptrs, None,
+                              0.088, FAKE if store else None, FAKE if (store and swa_loc) else None,
+                              ptrs if store else None, ptrs if store else None)
+    st._keep = keep
+    return st
+
+
+def test_decode_step_argument_errors(swa):
+    lib, E = swa.lib, swa
+    ix = index(swa)
+
+    def step(st, ws=None, ws_bytes=0, table=FAKE, indptr=FAKE, ix=ix, max_seq=32768):
+        return lib.swa_decode_step(ctypes.byref(st), ctypes.byref(ix), max_seq, table, indptr, 1000, ws, ws_bytes,
+                                   None)
+
+    need = lib.swa_decode_step_workspace_bytes(ctypes.byref(step_struct(swa)), ctypes.byref(ix), 32768)
+    ns, ws = ctypes.c_int32(), ctypes.c_size_t()
+    assert lib.swa_decode_plan(2, 64, 4, 128, -1, 32768, ctypes.byref(ns), ctypes.byref(ws)) == E.SWA_OK
+    assert need == ws.value > 0                                     # the full layers' split-K plan
+    assert lib.swa_decode_step_workspace_bytes(ctypes.byref(step_struct(swa, mapping=[(0, 1)])), ctypes.byref(ix),
+                                               32768) == 0           # SWA layers only: no workspace
+    assert step(step_struct(swa, mapping=[(3, 1)])) == E.SWA_E_ARG   # SWA pool has 3 layers
+    assert step(step_struct(swa, mapping=[(2, 0)])) == E.SWA_E_ARG   # full pool has 2 layers
+    assert step(step_struct(swa, mapping=[(0, 2)])) == E.SWA_E_ARG   # is_swa is 0 or 1
+    assert step(step_struct(swa, mapping=[(-1, 1)])) == E.SWA_E_ARG
+    assert step(step_struct(swa, window=-1)) == E.SWA_E_ARG
+    assert step(step_struct(swa, q=False)) == E.SWA_E_ARG
+    assert step(step_struct(swa, store=True, swa_loc=False), ws=FAKE, ws_bytes=need) == E.SWA_E_ARG
+    assert step(step_struct(swa)) == E.SWA_E_WORKSPACE               # full layers need the split workspace
+    assert step(step_struct(swa), ws=FAKE, ws_bytes=need - 16) == E.SWA_E_WORKSPACE
+    assert step(step_struct(swa), ws=FAKE, ws_bytes=need, table=None) == E.SWA_E_ARG
+    assert step(step_struct(swa, full_kv=3), ws=FAKE, ws_bytes=need) == E.SWA_E_SHAPE   # 64 q over 3 kv heads
+    # an empty batch passes the checks and launches nothing
+    assert step(step_struct(swa), ix=index(swa, batch=0), ws=None) == E.SWA_OK
+    assert step(step_struct(swa, mapping=[])) == E.SWA_OK

@@ -13,7 +13,7 @@ from oracle import swa_oracle as O
 from sliding_window_attention_swa_amd import workloads as WL
 
 from gpu_path import (TOL, DeviceWorkload, bits_to_device, check, device_to_bits, oracle_decode, oracle_extend,
-                      run_decode, run_decode_store, run_extend, run_store, say)
+                      oracle_pools_after_store, run_decode, run_decode_store, run_extend, run_store, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,6 +191,10 @@ DECODE_CASES = {
     "f32_g8_w255": ([1, 256, 300], 16, 2, 255, 16, "f32", "f32", True),
     "e4m3_g8": ([1, 2, 129, 130, 1000], 16, 2, 128, 16, "bf16", "e4m3", True),
     "e4m3_g16_nosink": ([5, 600], 32, 2, 128, 64, "bf16", "e4m3", False),
+    # batches that are a multiple of 8: the window kernel relabels its workgroups across the XCDs
+    "bf16_g8_b8": ([1, 130, 2, 129, 900, 17, 128, 3000], 16, 2, 128, 16, "bf16", "bf16", True),
+    "e4m3_g8_b16": ([1, 130, 2, 129, 900, 17, 128, 3000, 5, 77, 256, 1000, 129, 130, 131, 64], 16, 2, 128, 64,
+                    "bf16", "e4m3", True),
 }
 
 
@@ -214,7 +218,7 @@ def test_decode_small(name):
 
 
 FUSED_CASES = ["bf16_g8", "bf16_g8_nosink", "bf16_g1", "bf16_g2", "bf16_g4", "bf16_g16", "bf16_w0", "bf16_w1",
-               "e4m3_g8", "e4m3_g16_nosink", "bf16_w255", "e4m3_w255_g16"]
+               "e4m3_g8", "e4m3_g16_nosink", "bf16_w255", "e4m3_w255_g16", "bf16_g8_b8", "e4m3_g8_b16"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
@@ -332,6 +336,61 @@ def test_decode_c5_full_size():
     loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
     want = codecs.f64_to_e4m3(codecs.bf16_bits_to_f64(wl.new_k))
     assert np.array_equal(dw.k[torch.from_numpy(loc).cuda()].cpu().numpy(), want)
+
+
+def _pool_rows_equal_oracle_store(wl, dev_pool, oracle_pool):
+    """The pool after the store holds the oracle's bytes on every row the
+    workload wrote or the store targets, and the NaN fill everywhere else."""
+    loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+    rows = np.union1d(oracle_pool.written_rows(), loc[(loc >= 0) & (loc < wl.pool_rows)])
+    rows = rows[rows >= wl.page_size]            # page 0 may absorb padded writes
+    got = device_to_bits(dev_pool[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(got.view(np.uint8), oracle_pool[rows].view(np.uint8))
+    nan = WL.NAN_BITS[wl.kv_dtype]
+    flat = dev_pool.view(torch.int16) if wl.kv_dtype == "bf16" else dev_pool
+    fill = int(np.int16(nan.view(np.int16))) if wl.kv_dtype == "bf16" else int(nan)
+    touched = (flat[wl.page_size:] != fill).flatten(1).any(dim=1).sum().item()
+    assert touched == rows.size, f"{touched} rows differ from the fill, {rows.size} expected"
+
+
+def test_decode_store_fused_c2_full_size():
+    """The launch the benchmark times, at its timed shape: swa_decode_store on
+    C2 (B = 64, a multiple of 8, so the workgroups are relabelled across the
+    XCDs and the window table is read speculatively at b * (W + 1)).  f32
+    output against the oracle; bf16 output = RNE(f32 output); the pool bytes
+    equal the oracle's store."""
+    wl = WL.c2_decode_bf16()
+    say("decode+store fused c2 (64 requests, bf16)")
+    dw = DeviceWorkload(wl)
+    out = run_decode_store(dw, "f32")
+    check(out, oracle_decode(wl), TOL["bf16"], "c2 fused")
+    pk, pv = oracle_pools_after_store(wl)
+    _pool_rows_equal_oracle_store(wl, dw.k, pk)
+    _pool_rows_equal_oracle_store(wl, dw.v, pv)
+    out_bf = run_decode_store(DeviceWorkload(wl), "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
+def test_decode_store_fused_c5_full_size():
+    """The fused store with e4m3 pools at C5's shape (B = 256): the same output
+    bits and pool bytes as swa_kv_store + swa_decode, within tolerance of the
+    oracle on sampled requests (every q head), and pool bytes equal to the
+    oracle's encoding."""
+    wl = WL.c5_decode_fp8()
+    say("decode+store fused c5 (256 requests, e4m3 K/V)")
+    two = DeviceWorkload(wl)
+    run_store(two)
+    want = run_decode(two, "f32")
+    one = DeviceWorkload(wl)
+    got = run_decode_store(one, "f32")
+    assert torch.equal(got, want)
+    assert torch.equal(one.k, two.k) and torch.equal(one.v, two.v)
+    reqs = [0, 7, 8, 100, 201, 255]
+    ref = oracle_decode(wl, only=[(b, h) for b in reqs for h in range(wl.q_heads)])
+    check(got, ref, TOL["e4m3"], "c5 fused sampled")
+    pk, pv = oracle_pools_after_store(wl)
+    _pool_rows_equal_oracle_store(wl, one.k, pk)
+    _pool_rows_equal_oracle_store(wl, one.v, pv)
 
 
 def _c4_oracle_layer(st, ly, q, k, v, reqs):
@@ -518,6 +577,38 @@ def test_extend_small(name):
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
+def test_extend_bad_qo_indptr_stays_in_bounds():
+    """qo_indptr entries outside [0, total_q] or out of order: every request's
+    rows are clamped into [0, total_q], so nothing outside `out` is written,
+    and swa_validate counts the bad requests exactly as the oracle does."""
+    from sliding_window_attention_swa_amd import swa
+    wl = WL.extend_workload("badqo", 41, [100, 300, 0], [40, 70, 33], 16, 2, 128, 16)
+    say("extend with bad qo_indptr: guard rows around out")
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    total, B = wl.q.shape[0], wl.batch
+    cap = int(wl.seq_lens.astype(np.int64).sum())
+    table = torch.empty(cap, dtype=torch.int32, device="cuda")
+    indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    swa.swa_translate_window(dw.index, wl.window, table, indptr, prefix_lens=dw.prefix)
+    guard = 64
+    want = O.validate(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window, wl.pool_rows,
+                      wl.page_size, prefix_lens=wl.prefix_lens, qo_indptr=wl.qo_indptr, total_q=total)
+    assert want["qo_bad"] == 0
+    for qo in ([-32, 20, 5, total + 50], [total + 5, total + 9, -3, 2], [0, 40, 30, total], [1 << 30, -(1 << 30), 0, 7]):
+        big = torch.full((total + 2 * guard, wl.q_heads, wl.head_dim), 7.0, dtype=torch.float32, device="cuda")
+        out = big[guard:guard + total]
+        qo_t = torch.tensor(qo, dtype=torch.int32, device="cuda")
+        swa.swa_extend(dw.q, qo_t, dw.prefix, dw.layer, dw.index, wl.window, out, sinks=dw.sinks, slot_table=table,
+                       table_indptr=indptr)
+        torch.cuda.synchronize()
+        assert bool((big[:guard] == 7.0).all()) and bool((big[guard + total:] == 7.0).all()), qo
+        got = swa.swa_validate(dw.index, wl.window, wl.pool_rows, prefix_lens=dw.prefix, qo_indptr=qo_t, total_q=total)
+        want = O.validate(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window, wl.pool_rows,
+                          wl.page_size, prefix_lens=wl.prefix_lens, qo_indptr=qo, total_q=total)
+        assert got == want and got["qo_bad"] > 0, (qo, got, want)
+
+
 def test_extend_tile_runs_sampled():
     """Enough tiles that every workgroup walks a run of several tiles (band
     blocks rotating through the LDS ring), mixed with band-clipped and
@@ -545,9 +636,11 @@ def test_extend_c3_full_size_sampled():
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(wl.q.shape[0] - 40, wl.q.shape[0]),
                                      rng.choice(wl.q.shape[0], 300, replace=False)]))
-    only = [(int(r), h) for r in rows for h in range(wl.q_heads)]
-    ref = oracle_extend(wl, only=only)
-    check(out, ref, TOL["bf16"], "c3 sampled")
+    heads4 = (0, 21, 42, 63)   # one q head of four different kv heads, the first and the last included
+    only = {(int(r), h) for r in rows for h in range(wl.q_heads)}
+    only |= {(r, h) for r in range(wl.q.shape[0]) for h in heads4}
+    ref = oracle_extend(wl, only=sorted(only))
+    check(out, ref, TOL["bf16"], "c3: every row x 4 heads, 380 rows x every head")
 
 
 # ---------------------------------------------------------------------------

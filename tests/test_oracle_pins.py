@@ -543,15 +543,22 @@ def hand_built_batch():
 HAND_COUNTS = {
     # decode, W = 2, with the mapping (SWA pool of 6 rows)
     "decode": dict(bad_requests=2, positions=11, full_out_of_range=1, tombstones=4, sentinels=2,
-                   slot_out_of_range=1, store_locs=11, store_out_of_range=2, store_duplicates=3),
+                   slot_out_of_range=1, store_locs=11, store_out_of_range=2, store_duplicates=3, qo_bad=0),
     # extend, W = 2, prefixes [4, 5, 0, 0, 1, 3] (the last one exceeds its length)
     "extend": dict(bad_requests=3, positions=9, full_out_of_range=0, tombstones=4, sentinels=2,
-                   slot_out_of_range=1, store_locs=0, store_out_of_range=0, store_duplicates=0),
+                   slot_out_of_range=1, store_locs=0, store_out_of_range=0, store_duplicates=0, qo_bad=0),
     # full layer (no mapping), W = -1, full pool of 10 rows
     "full": dict(bad_requests=2, positions=16, full_out_of_range=0, tombstones=3, sentinels=0,
-                 slot_out_of_range=2, store_locs=0, store_out_of_range=0, store_duplicates=0),
+                 slot_out_of_range=2, store_locs=0, store_out_of_range=0, store_duplicates=0, qo_bad=0),
 }
 EXTEND_PREFIX = np.array([4, 5, 0, 0, 1, 3], dtype=np.int32)
+# Query rows of the extend batch above, 9 rows in all.  New positions per request
+# (seq - prefix): 2, 0, bad, 7 (bad), 2, bad.  Rows given: [0, 2) right; [2, 1)
+# decreasing (1); [1, 4) a bad request, its count not checked, rows in order;
+# [4, 4) for a bad request; [4, 5) one row for two positions (2); [5, 10) past
+# total_q = 9 (3).
+EXTEND_QO = np.array([0, 2, 1, 4, 4, 5, 10], dtype=np.int32)
+EXTEND_QO_BAD = 3
 
 
 def test_validate_hand_counted():
@@ -559,6 +566,8 @@ def test_validate_hand_counted():
     assert O.validate(r2t, rows, lens, mapping, 2, 6, 2, store_loc=store) == HAND_COUNTS["decode"]
     assert O.validate(r2t, rows, lens, mapping, 2, 6, 2, prefix_lens=EXTEND_PREFIX) == HAND_COUNTS["extend"]
     assert O.validate(r2t, rows, lens, None, -1, 10, 2) == HAND_COUNTS["full"]
+    got = O.validate(r2t, rows, lens, mapping, 2, 6, 2, prefix_lens=EXTEND_PREFIX, qo_indptr=EXTEND_QO, total_q=9)
+    assert got == dict(HAND_COUNTS["extend"], qo_bad=EXTEND_QO_BAD)
 
 
 def test_validate_clean_workload_counts_nothing():
