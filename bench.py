@@ -1,36 +1,47 @@
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|evict|alloc|unified]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|c1|c2|c3|c3w|c4|c5|evict|alloc|unified]
 
-Other workloads (one JSON line each, same fields): c1 single f32 decode; c3
-chunked-prefill extend (store + extend over 4 layers); c4 the 48-layer mixed
-decode step (39 SWA + 9 full layers); c5 fp8-KV decode with store; evict the
-SWA eviction of the c5 batch right after its prefill; alloc the paired
-allocation of a prefill chunk (and of a decode step) for the c5 batch;
-unified the c2 decode step over one unified sub-pool of 32 layers.
+Default (all): one JSON line whose headline is the largest single-GPU
+configuration, the long-context mixed-layer decode step (B = 32, T = 32K, 48
+layers: 39 SWA layers with W = 128 and 8 kv heads, 9 full-attention layers with
+4 kv heads, 64 q heads, head_dim 128, bf16, page 64, SWA pool at ratio 0.1):
+    swa_decode_step: the window table once (req_to_token -> full -> SWA
+    slots), then the 48 layers in order through the layers mapping (SWA
+    layers: windowed decode over the shared table; full layers: split-K decode
+    over req_to_token + merge).
+The same line carries the other configurations as sub-results, each with its
+own roofline and CPU baseline:
+    c2   batched SWA decode, B = 64, T ~ U[1K, 8K], W = 128, 64 q / 8 kv, bf16,
+         page 16, with the new token's store fused (32 layers per step)
+    c5   fp8-KV SWA decode, B = 256, lognormal T (median 16K), e4m3 K/V, page 64,
+         translate + store + decode (16 layers per step)
+    c3   chunked-prefill extend, B = 4, prefix 8K + chunk 2K, W = 128, page 64,
+         store + extend (4 layers per step): TFLOP/s, fraction of MFMA peak and of
+         the attainable roofline
+    c3w  the c3 shape with W = 512, 1024, 4096 (compute-bound windows)
+    c1   one f32 request, T = 512, W = 128 (latency)
+Every step is captured once as a HIP graph and replayed; inputs are resident in
+HBM before the timed region.  `value` is algorithmic HBM bytes of the whole step
+per second.  Each `roofline` is its dominant kernel, timed live with HIP events
+around back-to-back graph replays on the replay stream.  Each `cpu_baseline` is
+the CPU oracle as it stands, run on a process pool of one worker per host core
+(at most 16, BLAS at one thread each) over a bounded sample of the same work,
+before the GPU is first touched.
 
-Default workload (c2): batched SWA decode, B = 64 requests with context lengths
-uniform in [1K, 8K], W = 128, 64 q / 8 kv heads, head_dim 128, bf16, page 16,
-two-pool cache with out-of-window pages tombstoned.  One step is one decode
-step of that batch through a stack of 32 SWA layers, each with its own K/V
-pool (so the 256 MB Infinity Cache cannot serve repeats):
-    translate_loc (new tokens' full locs -> SWA slots)    once per step
-    translate_window (req_to_token -> full -> SWA slots)  once per step
-    per layer: swa_decode_store (the new token's K/V store fused into the
-               windowed decode; equal to kv_store followed by swa_decode)
-The step is captured once as a HIP graph and replayed; inputs are resident in
-HBM before timing starts.  The JSON line reports algorithmic HBM bytes per
-second of the whole step, the dominant kernel's roofline (swa_decode, timed
-live with HIP events over back-to-back launches), and the CPU oracle timed on
-the host for a bounded sample of the same work.
+Single workloads (--workload NAME) print their own line in the same format;
+evict, alloc and unified are the next-row kernels (eviction, paired allocation,
+unified pool layout).
 """
 
 from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import math
+import multiprocessing
 import os
 import sys
 import time
@@ -42,7 +53,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+SIMDS = 1024                 # 256 CUs x 4 SIMDs
 METRIC = "SWA decode HBM GB/s & tokens/s; windowed prefill TFLOP/s (% of MI355X peak)"
+SWEEP_WINDOWS = (512, 1024, 4096)
 
 
 def log(msg):
@@ -57,8 +70,12 @@ def source_sha(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(name: str, kernel_files, per_launch_units: float):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+DECODE_SRC = ["decode_kernels.hip", "common.hpp", "api.cpp"]
+EXTEND_SRC = ["extend_kernels.hip", "common.hpp", "api.cpp"]
+
+
+def profile_record(name: str, kernel_files):
+    """A committed rocprofv3 counter summary (profiles/<name>_pmc.json), or None
     when absent or taken on another version of the kernel source."""
     path = os.path.join(ROOT, "profiles", f"{name}_pmc.json")
     if not os.path.exists(path):
@@ -67,20 +84,185 @@ def traffic_from_profile(name: str, kernel_files, per_launch_units: float):
         d = json.load(f)
     if d.get("kernel_source_sha") != source_sha(*kernel_files):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
+
+
+def traffic_from_profile(name: str, kernel_files):
+    d = profile_record(name, kernel_files)
+    return None if d is None else d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a fork pool of one process per host
+# core (at most 16: the host share of one GPU), BLAS limited to one thread per
+# process, over a bounded sample of the benchmarked work.  It runs before the GPU
+# is first used; the workers inherit the host inputs in _HOST.
+# ---------------------------------------------------------------------------
+
+_HOST = {}
+CPU_BUDGET_S = 20.0   # CPU seconds of oracle work per measured item (wall = budget / workers)
+
+
+def cpu_workers() -> int:
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def _cpu_task(task):
+    """One task of oracle work on the host inputs in _HOST."""
+    from oracle import swa_oracle as O
+    kind, name = task[0], task[1]
+    d = _HOST[name]
+    if kind == "decode":          # one request of one layer, every q head
+        wl, b = d, task[2]
+        O.decode(wl.q, wl.q_dtype, wl.pool_k, wl.pool_v, wl.kv_dtype, wl.req_to_token, wl.req_pool_idx,
+                 wl.seq_lens, wl.full_to_swa, wl.window, wl.sinks, only=[(b, h) for h in range(wl.q_heads)])
+    elif kind == "store":         # translate + store of the new rows + window table, whole batch, one layer
+        wl = d
+        loc = wl.new_full_loc if wl.full_to_swa is None else O.translate_loc(wl.new_full_loc, wl.full_to_swa)
+        O.kv_store(wl.pool_k, wl.pool_v, loc, wl.new_k, wl.new_v, wl.new_dtype, wl.kv_dtype)
+        O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window,
+                       prefix_lens=wl.prefix_lens)
+    elif kind == "extend":        # query rows r0 .. r1-1 of one layer, every q head
+        wl, r0, r1 = d, task[2], task[3]
+        O.extend(wl.q, "bf16", wl.qo_indptr, wl.prefix_lens, wl.pool_k, wl.pool_v, "bf16", wl.req_to_token,
+                 wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window, wl.sinks,
+                 only=[(r, h) for r in range(r0, r1) for h in range(wl.q_heads)])
+    elif kind == "mixed":         # one request of one full or SWA layer of the mixed step, every q head
+        part, b = task[2], task[3]
+        x = d[part]
+        O.decode(x["q"], "bf16", x["k"], x["v"], "bf16", d["r2t"], d["rows"], d["lens"], x["map"], x["window"],
+                 None, only=[(b, h) for h in range(d["q_heads"])])
+    else:
+        raise ValueError(kind)
+    return 1
+
+
+def pool_time(pool, nw, tasks, unit_tasks):
+    """Wall time of whole units of `tasks` (each unit is `unit_tasks` tasks, in
+    order) on the pool, sized to about CPU_BUDGET_S of oracle work: the number
+    of units grows from one (after one untimed unit) until a run lasts about
+    CPU_BUDGET_S / workers seconds; the last run is the measurement.  Returns
+    (units, seconds)."""
+    target = CPU_BUDGET_S / nw
+    pool.map(_cpu_task, tasks[:unit_tasks], chunksize=1)   # warm-up: first touch of the inputs in every worker
+    units = 1
+    while True:
+        work = list(itertools.islice(itertools.cycle(tasks[:unit_tasks]), units * unit_tasks))
+        chunk = max(1, min(8, len(work) // (4 * nw)))
+        t0 = time.perf_counter()
+        pool.map(_cpu_task, work, chunksize=chunk)
+        secs = time.perf_counter() - t0
+        if secs >= 0.5 * target or units >= 1 << 20:
+            return units, secs
+        units = max(2 * units, int(units * target / max(secs, 1e-3)))
+
+
+def cpu_decode_layer(pool, nw, name, wl):
+    """Layers of decode work per second: the batch's store and window table,
+    then every request's decode."""
+    tasks = ([("store", name)] if wl.new_full_loc is not None else []) + [("decode", name, b)
+                                                                           for b in range(wl.batch)]
+    return pool_time(pool, nw, tasks, len(tasks))
+
+
+def cpu_extend_layer(pool, nw, name, wl, rows_per_task):
+    """Extend query rows per second (every q head): a unit is one task of
+    `rows_per_task` consecutive rows per worker, the tasks spread over the
+    chunk."""
+    total = wl.q.shape[0]
+    starts = np.linspace(0, total - rows_per_task, nw).astype(int)
+    tasks = [("extend", name, int(r), int(r) + rows_per_task) for r in starts]
+    units, secs = pool_time(pool, nw, tasks, len(tasks))
+    return units * len(tasks) * rows_per_task, secs
+
+
+def mixed_host_data(st, full_sample=4, seed=97):
+    """Host inputs of the mixed step's oracle sample: one full layer holding the
+    K/V rows of `full_sample` requests, one SWA layer holding every request's
+    window (values drawn here; the oracle reads them as it reads any pool)."""
+    from sliding_window_attention_swa_amd import workloads as W
+    from oracle import swa_oracle as O
+    rng = np.random.default_rng(seed)
+    B, Hq, D, T = st.batch, st.q_heads, st.head_dim, int(st.seq_lens[0])
+    r2t, rows = st.req_to_token, st.req_pool_idx
+    sample = list(range(0, B, B // full_sample))[:full_sample]
+    used_f = np.unique(np.concatenate([r2t[rows[b], :T] for b in sample]).astype(np.int64))
+    used_s = np.unique(np.concatenate([O.translate_loc(r2t[rows[b], T - 129:T], st.full_to_swa) for b in range(B)]))
+    draw = lambda n, h: W.to_store(rng.standard_normal((n, h, D), dtype=np.float32), "bf16")  # noqa: E731
+    full = dict(q=draw(B, Hq), map=None, window=-1,
+                k=W.SparsePool(st.n_full + st.page_size, 4, D, "bf16", used_f, draw(used_f.size, 4)),
+                v=W.SparsePool(st.n_full + st.page_size, 4, D, "bf16", used_f, draw(used_f.size, 4)))
+    swl = dict(q=draw(B, Hq), map=st.full_to_swa, window=128,
+               k=W.SparsePool(st.n_swa + st.page_size, 8, D, "bf16", used_s, draw(used_s.size, 8)),
+               v=W.SparsePool(st.n_swa + st.page_size, 8, D, "bf16", used_s, draw(used_s.size, 8)))
+    return dict(full=full, swa=swl, r2t=r2t, rows=rows, lens=st.seq_lens, q_heads=Hq, sample=sample, batch=B)
+
+
+def cpu_mixed_step(pool, nw, d):
+    """The 48-layer step's oracle time: a full layer over the sampled requests
+    and an SWA layer over every request, timed on the pool; the step is 9 full
+    plus 39 SWA layers over all 32 requests."""
+    B, sample, full_sample = d["batch"], d["sample"], len(d["sample"])
+    n_full, t_full = pool_time(pool, nw, [("mixed", "c4", "full", b) for b in sample], len(sample))
+    n_swa, t_swa = pool_time(pool, nw, [("mixed", "c4", "swa", b) for b in range(B)], B)
+    per_full = t_full / (n_full * len(sample))        # seconds per (request, full layer) on the pool
+    per_swa = t_swa / (n_swa * B)
+    step_s = B * (9 * per_full + 39 * per_swa)
+    return step_s, (f"one full layer (32K keys, 4 kv heads) on {full_sample} of {B} requests, {n_full} times, "
+                    f"and one SWA layer on all {B} requests, {n_swa} times, every q head; step time = "
+                    f"{B} requests x (9 x {per_full * 1e3:.2f} ms + 39 x {per_swa * 1e3:.3f} ms per request and layer)")
+
+
+def cpu_baseline_entry(value, unit, nw, sample):
+    return dict(value=value, unit=unit, cores=nw, kind="oracle", sample=sample)
+
+
+def run_cpu_baselines(names, hosts):
+    """The oracle timed for each named workload (host inputs in `hosts`), before
+    any GPU use.  Returns {name: cpu_baseline dict}."""
+    nw = cpu_workers()
+    # the workers see what _HOST holds when the pool forks
+    for name in names:
+        _HOST[name] = mixed_host_data(hosts[name]["st"]) if name == "c4" else hosts[name]["wl"]
+    ctx = multiprocessing.get_context("fork")
+    out = {}
+    with ctx.Pool(nw, initializer=_worker_init) as pool:
+        pool.map(abs, range(nw), chunksize=1)  # every worker started before the timing
+        for name in names:
+            t0 = time.perf_counter()
+            h = hosts[name]
+            if name == "c4":
+                step_s, sample = cpu_mixed_step(pool, nw, _HOST["c4"])
+                out[name] = cpu_baseline_entry(round(h["step_bytes"] / step_s / 1e9, 6), "GB/s", nw, sample)
+                out[name]["tokens_per_s"] = round(h["st"].batch / step_s, 4)
+            elif name in ("c1", "c2", "c5"):
+                wl = h["wl"]
+                units, secs = cpu_decode_layer(pool, nw, name, wl)
+                out[name] = cpu_baseline_entry(round(units * h["layer_bytes"] / secs / 1e9, 6), "GB/s", nw,
+                                               f"{units} layers of {wl.batch} requests (translate + store + window "
+                                               f"table, then every request's decode, every q head) in {secs:.2f} s")
+                out[name]["tokens_per_s"] = round(units * wl.batch / h["layers"] / secs, 4)
+            else:  # c3, c3w_<W>
+                wl = h["wl"]
+                rows, secs = cpu_extend_layer(pool, nw, name, wl, h["rows_per_task"])
+                flops = rows * h["flops_per_row"]
+                out[name] = cpu_baseline_entry(round(flops / secs / 1e12, 9), "TFLOP/s", nw,
+                                               f"{rows} query rows x {wl.q_heads} q heads of the extend "
+                                               f"(W = {wl.window}) in {secs:.2f} s")
+            log(f"[cpu] {name}: {out[name]['value']} {out[name]['unit']} on {nw} processes "
+                f"({time.perf_counter() - t0:.1f} s)")
+    _HOST.clear()
+    return out
 
 
 # ---------------------------------------------------------------------------
 # device setup helpers (torch for memory only)
 # ---------------------------------------------------------------------------
-
-
-def dev_from_bits(torch, bits, dtype):
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
-    if dtype == "e4m3":
-        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).cuda()
-    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).cuda()
 
 
 def randn_store(torch, shape, gen, dtype):
@@ -101,97 +283,6 @@ def nan_pool(torch, rows, H, D, dtype):
     else:
         t = torch.full((rows, H, D), float("nan"), dtype=torch.float32, device="cuda")
     return t
-
-
-class DecodeBench:
-    """A decode batch of one workload replicated over `layers` SWA layers."""
-
-    def __init__(self, torch, swa, wl, layers, out_dtype="bf16", seed=7):
-        self.torch, self.swa, self.wl, self.L = torch, swa, wl, layers
-        B, Hq, Hkv, D = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
-        self.r2t = torch.from_numpy(wl.req_to_token).cuda()
-        self.rows = torch.from_numpy(wl.req_pool_idx).cuda()
-        self.lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).cuda()
-        self.map = torch.from_numpy(wl.full_to_swa).cuda()
-        self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, wl.page_size)
-        self.has_store = wl.new_full_loc is not None
-        if self.has_store:
-            self.full_loc = torch.from_numpy(wl.new_full_loc).cuda()
-            self.swa_loc = torch.empty_like(self.full_loc)
-        self.cap = B * (wl.window + 1)
-        self.table = torch.empty(self.cap, dtype=torch.int32, device="cuda")
-        self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
-        used = torch.from_numpy(wl.pool_k.used_rows).cuda()
-        g = torch.Generator(device="cuda")
-        g.manual_seed(seed)
-        self.layers = []
-        for _ in range(layers):
-            k = nan_pool(torch, wl.pool_rows, Hkv, D, wl.kv_dtype)
-            v = nan_pool(torch, wl.pool_rows, Hkv, D, wl.kv_dtype)
-            k[used] = randn_store(torch, (used.numel(), Hkv, D), g, wl.kv_dtype)
-            v[used] = randn_store(torch, (used.numel(), Hkv, D), g, wl.kv_dtype)
-            self.layers.append(dict(
-                kv=swa.KvLayer(k, v),
-                q=randn_store(torch, (B, Hq, D), g, wl.q_dtype),
-                new_k=randn_store(torch, (B, Hkv, D), g, "bf16" if wl.kv_dtype != "f32" else "f32"),
-                new_v=randn_store(torch, (B, Hkv, D), g, "bf16" if wl.kv_dtype != "f32" else "f32"),
-                out=torch.empty((B, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
-                                device="cuda"),
-            ))
-        self.sinks = torch.from_numpy(wl.sinks).cuda() if wl.sinks is not None else None
-        # algorithmic bytes (window only): K/V rows, Q, O, window table
-        n_keys = np.minimum(wl.seq_lens.astype(np.int64), wl.window + 1)
-        kv_b = {"bf16": 2, "e4m3": 1, "f32": 4}[wl.kv_dtype]
-        q_b = {"bf16": 2, "f32": 4}[wl.q_dtype]
-        o_b = 2 if out_dtype == "bf16" else 4
-        self.decode_bytes = int(n_keys.sum() * Hkv * D * kv_b * 2 + B * Hq * D * (q_b + o_b) + n_keys.sum() * 4
-                                + (B + 1) * 4)
-        new_b = 2 if wl.kv_dtype != "f32" else 4
-        # The new token's store is fused into the decode launch (swa_decode_store):
-        # its K/V are read once, as the window's last row (counted in
-        # decode_bytes), and written once to the pool (counted here).
-        # (bf16 pools only: the e4m3 variant needs more registers, which costs
-        # a workgroup per CU, more than the separate store launch costs)
-        self.fused = self.has_store and wl.kv_dtype == "bf16" and 0 <= wl.window <= 255
-        if self.fused:
-            self.store_bytes = B * Hkv * D * kv_b * 2 + B * 8
-        else:
-            self.store_bytes = B * Hkv * D * 2 * (new_b + kv_b) + B * 8 if self.has_store else 0
-        self.translate_bytes = (B * 8 * 3 if self.has_store else 0) + int(n_keys.sum()) * (4 + 8 + 4) + B * 12
-        self.step_bytes = self.translate_bytes + layers * (self.store_bytes + self.decode_bytes)
-        self.flops_decode = int(n_keys.sum()) * Hq * D * 4
-
-    def step(self):
-        swa, wl = self.swa, self.wl
-        if self.has_store:
-            swa.swa_translate_loc(self.full_loc, self.map, self.swa_loc)
-        swa.swa_translate_window(self.index, wl.window, self.table, self.indptr)
-        for ly in self.layers:
-            self.layer_call(ly)
-
-    def layer_call(self, ly):
-        swa, wl = self.swa, self.wl
-        if self.fused:
-            swa.swa_decode_store(ly["q"], ly["kv"], self.index, wl.window, ly["out"], self.swa_loc, ly["new_k"],
-                                 ly["new_v"], sinks=self.sinks, slot_table=self.table, table_indptr=self.indptr)
-            return
-        if self.has_store:
-            swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
-        swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                       slot_table=self.table, table_indptr=self.indptr)
-
-    def dominant(self):
-        """Back-to-back decode launches only (one per layer; with the store fused
-        in when the step fuses it)."""
-        swa, wl = self.swa, self.wl
-        for ly in self.layers:
-            if self.fused:
-                swa.swa_decode_store(ly["q"], ly["kv"], self.index, wl.window, ly["out"], self.swa_loc,
-                                     ly["new_k"], ly["new_v"], sinks=self.sinks, slot_table=self.table,
-                                     table_indptr=self.indptr)
-            else:
-                swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                               slot_table=self.table, table_indptr=self.indptr)
 
 
 def graph_of(torch, fn):
@@ -234,96 +325,179 @@ def replay_percentiles(torch, g, n, per_replay):
     return {k: round(float(np.percentile(d, q)) * 1e3, 3) for k, q in (("p10_us", 10), ("p50_us", 50), ("p90_us", 90))}
 
 
-# ---------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, single-threaded, on a bounded sample
-# ---------------------------------------------------------------------------
+def timed_step(torch, fn, steps, warmup):
+    g = graph_of(torch, fn)
+    for _ in range(warmup):
+        g.replay()
+    return time_replays(torch, g, steps)
 
 
-def cpu_baseline_decode(wl, budget_s=12.0):
-    from threadpoolctl import threadpool_limits
-    from oracle import swa_oracle as O
-    B = wl.batch
-    done_req = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        pk, pv = wl.pool_k, wl.pool_v
-        if wl.new_full_loc is not None:
-            swa_loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
-            pk, pv = O.kv_store(pk, pv, swa_loc, wl.new_k, wl.new_v, wl.new_dtype, wl.kv_dtype)
-        O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window)
-        b = 0
-        while time.perf_counter() - t0 < budget_s:
-            only = [(b, h) for h in range(wl.q_heads)]
-            O.decode(wl.q, wl.q_dtype, pk, pv, wl.kv_dtype, wl.req_to_token, wl.req_pool_idx, wl.seq_lens,
-                     wl.full_to_swa, wl.window, wl.sinks, only=only)
-            b = (b + 1) % B
-            done_req += 1
-    return time.perf_counter() - t0, done_req
+def timed_dominant(torch, fn, reps, per_replay):
+    g = graph_of(torch, fn)
+    g.replay()
+    ms = time_replays(torch, g, reps) / per_replay
+    return ms, replay_percentiles(torch, g, reps, per_replay)
 
 
 # ---------------------------------------------------------------------------
+# decode workloads (c1, c2, c5): one batch replicated over `layers` SWA layers
+# ---------------------------------------------------------------------------
 
 
-def run_decode_workload(args, torch, swa, W):
-    name = args.workload
+def decode_host(name):
+    from sliding_window_attention_swa_amd import workloads as W
     if name == "c2":
-        wl, layers = W.c2_decode_bf16(), 32
-        desc = "batched SWA decode B=64, T~U[1K,8K], W=128, 64q/8kv, D=128, bf16, page 16"
-    elif name == "c5":
-        wl, layers = W.c5_decode_fp8(), 16
-        desc = "fp8 KV decode B=256, T~lognormal(16K), W=128, 64q/8kv, D=128, e4m3 K/V, bf16 q, page 64"
+        return W.c2_decode_bf16(), 32, "batched SWA decode B=64, T~U[1K,8K], W=128, 64q/8kv, D=128, bf16, page 16"
+    if name == "c5":
+        return (W.c5_decode_fp8(), 16,
+                "fp8 KV decode B=256, T~lognormal(16K), W=128, 64q/8kv, D=128, e4m3 K/V, bf16 q, page 64")
+    return W.c1_decode_f32(), 8, "single SWA decode T=512, W=128, 8q/8kv, D=128, f32, page 1"
+
+
+def decode_bytes(wl, out_dtype):
+    """Algorithmic bytes of one layer's decode (window only: K/V rows, Q, O,
+    window table) and of its store (the new rows written; read as the window's
+    last row when fused)."""
+    B, Hq, Hkv, D = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
+    n_keys = np.minimum(wl.seq_lens.astype(np.int64), wl.window + 1)
+    kv_b = {"bf16": 2, "e4m3": 1, "f32": 4}[wl.kv_dtype]
+    q_b = {"bf16": 2, "f32": 4}[wl.q_dtype]
+    o_b = 2 if out_dtype == "bf16" else 4
+    dec = int(n_keys.sum() * Hkv * D * kv_b * 2 + B * Hq * D * (q_b + o_b) + n_keys.sum() * 4 + (B + 1) * 4)
+    new_b = 2 if wl.kv_dtype != "f32" else 4
+    fused = wl.new_full_loc is not None and wl.kv_dtype == "bf16" and 0 <= wl.window <= 255
+    if wl.new_full_loc is None:
+        store = 0
+    elif fused:
+        store = B * Hkv * D * kv_b * 2 + B * 8
     else:
-        wl, layers = W.c1_decode_f32(), 8
-        desc = "single SWA decode T=512, W=128, 8q/8kv, D=128, f32, page 1"
+        store = B * Hkv * D * 2 * (new_b + kv_b) + B * 8
+    translate = (B * 8 * 3 if wl.new_full_loc is not None else 0) + int(n_keys.sum()) * (4 + 8 + 4) + B * 12
+    return dec, store, translate, fused, int(n_keys.sum()) * Hq * D * 4
+
+
+class DecodeBench:
+    """A decode batch of one workload replicated over `layers` SWA layers, each
+    with its own pools (so the 256 MB Infinity Cache cannot serve repeats)."""
+
+    def __init__(self, torch, swa, wl, layers, out_dtype="bf16", seed=7):
+        self.torch, self.swa, self.wl, self.L = torch, swa, wl, layers
+        B, Hq, Hkv, D = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
+        self.r2t = torch.from_numpy(wl.req_to_token).cuda()
+        self.rows = torch.from_numpy(wl.req_pool_idx).cuda()
+        self.lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).cuda()
+        self.map = torch.from_numpy(wl.full_to_swa).cuda()
+        self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, wl.page_size)
+        self.has_store = wl.new_full_loc is not None
+        if self.has_store:
+            self.full_loc = torch.from_numpy(wl.new_full_loc).cuda()
+            self.swa_loc = torch.empty_like(self.full_loc)
+        self.cap = B * (wl.window + 1)
+        self.table = torch.empty(self.cap, dtype=torch.int32, device="cuda")
+        self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+        used = torch.from_numpy(wl.pool_k.used_rows).cuda()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.layers = []
+        for _ in range(layers):
+            k = nan_pool(torch, wl.pool_rows, Hkv, D, wl.kv_dtype)
+            v = nan_pool(torch, wl.pool_rows, Hkv, D, wl.kv_dtype)
+            k[used] = randn_store(torch, (used.numel(), Hkv, D), g, wl.kv_dtype)
+            v[used] = randn_store(torch, (used.numel(), Hkv, D), g, wl.kv_dtype)
+            new_dt = "bf16" if wl.kv_dtype != "f32" else "f32"
+            self.layers.append(dict(
+                kv=swa.KvLayer(k, v), q=randn_store(torch, (B, Hq, D), g, wl.q_dtype),
+                new_k=randn_store(torch, (B, Hkv, D), g, new_dt), new_v=randn_store(torch, (B, Hkv, D), g, new_dt),
+                out=torch.empty((B, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
+                                device="cuda")))
+        self.sinks = torch.from_numpy(wl.sinks).cuda() if wl.sinks is not None else None
+        self.decode_bytes, self.store_bytes, self.translate_bytes, self.fused, self.flops = decode_bytes(wl, out_dtype)
+        self.step_bytes = self.translate_bytes + layers * (self.store_bytes + self.decode_bytes)
+
+    def step(self):
+        swa, wl = self.swa, self.wl
+        if self.has_store:
+            swa.swa_translate_loc(self.full_loc, self.map, self.swa_loc)
+        swa.swa_translate_window(self.index, wl.window, self.table, self.indptr)
+        for ly in self.layers:
+            if self.has_store and not self.fused:
+                swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
+            self.decode_call(ly)
+
+    def decode_call(self, ly):
+        swa, wl = self.swa, self.wl
+        if self.fused:
+            swa.swa_decode_store(ly["q"], ly["kv"], self.index, wl.window, ly["out"], self.swa_loc, ly["new_k"],
+                                 ly["new_v"], sinks=self.sinks, slot_table=self.table, table_indptr=self.indptr)
+        else:
+            swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
+                           slot_table=self.table, table_indptr=self.indptr)
+
+    def dominant(self):
+        """Back-to-back decode launches only (one per layer; with the store fused
+        in when the step fuses it)."""
+        for ly in self.layers:
+            self.decode_call(ly)
+
+
+def run_decode_gpu(args, torch, swa, name, wl, layers, desc, cpu):
     out_dtype = "f32" if wl.q_dtype == "f32" else "bf16"
     log(f"[bench] {name}: building {layers} layers")
     bench = DecodeBench(torch, swa, wl, layers, out_dtype)
-    g_step = graph_of(torch, bench.step)
-    for _ in range(args.warmup):
-        g_step.replay()
-    ms = time_replays(torch, g_step, args.steps)
-    log(f"[bench] step {ms:.4f} ms")
-    g_dec = graph_of(torch, bench.dominant)
-    dec_reps = max(10, args.steps // 2)
-    ms_dec = time_replays(torch, g_dec, dec_reps) / layers
-    pct = replay_percentiles(torch, g_dec, dec_reps, layers)
-    log(f"[bench] swa_decode {ms_dec * 1e3:.2f} us per launch")
+    ms = timed_step(torch, bench.step, args.steps, args.warmup)
+    reps = max(10, args.steps // 2)
+    ms_dec, pct = timed_dominant(torch, bench.dominant, reps, layers)
+    log(f"[bench] {name}: step {ms:.4f} ms, decode {ms_dec * 1e3:.2f} us per launch")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     dom_bytes = bench.decode_bytes + (bench.store_bytes if bench.fused else 0)
     achieved = dom_bytes / (ms_dec * 1e-3) / 1e9
-    traffic = traffic_from_profile(f"swa_decode_{name}", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1)
     res = dict(
-        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
-        dtype={"c5": "bf16 q / e4m3 kv", "c1": "f32"}.get(name, "bf16"), data="synthetic",
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5), dtype={"c5": "bf16 q / e4m3 kv",
+                                                                            "c1": "f32"}.get(name, "bf16"),
         config={"workload": desc, "global_batch": int(wl.batch), "layers_per_step": layers, "window": wl.window,
-                "max_seq_len": int(wl.seq_lens.max()), "parallelism": "none (1 GPU)"},
+                "max_seq_len": int(wl.seq_lens.max())},
         tokens_per_s=round(wl.batch / (ms * 1e-3), 1),
         layer_tokens_per_s=round(wl.batch * layers / (ms * 1e-3), 1),
-        frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
         roofline=dict(kernel="swa_decode_store (store fused)" if bench.fused else "swa_decode", bound="hbm",
-                      achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                      unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                      achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=traffic_from_profile(f"swa_decode_{name}", DECODE_SRC),
                       bytes_per_launch=dom_bytes, us_per_launch=round(ms_dec * 1e3, 3), **pct),
     )
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        secs, nreq = cpu_baseline_decode(wl)
-        per_req_bytes = bench.decode_bytes / wl.batch
-        res["cpu_baseline"] = dict(value=round(nreq * per_req_bytes / secs / 1e9, 6), unit="GB/s", cores=1,
-                                   kind="oracle",
-                                   sample=f"one layer: translate + store + window table for all {wl.batch} requests, "
-                                          f"then decode of {nreq} requests x {wl.q_heads} heads ({secs:.1f} s)")
+    if name == "c1":
+        res["roofline"]["note"] = "latency configuration: 1 MB per launch, far below what fills the chip"
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    del bench
+    torch.cuda.empty_cache()
     return res
 
 
 # ---------------------------------------------------------------------------
-# c3: chunked-prefill extend
+# extend workloads (c3 and the window sweep)
 # ---------------------------------------------------------------------------
 
 
+def extend_counts(wl):
+    """Band-only FLOPs and algorithmic bytes of one extend launch, and of the
+    store of the chunk."""
+    B, Hq, Hkv, D = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
+    total_q = wl.q.shape[0]
+    lo = np.maximum(wl.prefix_lens.astype(np.int64) - wl.window, 0)
+    n_keys = wl.seq_lens.astype(np.int64) - lo
+    pairs = 0
+    for b in range(B):
+        i = np.arange(int(wl.prefix_lens[b]), int(wl.seq_lens[b]))
+        pairs += int(np.sum(i - np.maximum(i - wl.window, 0) + 1))
+    flops = pairs * Hq * D * 4
+    ext_bytes = int(total_q * Hq * D * 2 * 2 + n_keys.sum() * Hkv * D * 2 * 2 + n_keys.sum() * 4
+                    + (B + 1) * 4 * 2 + B * 4 * 2)
+    store_bytes = total_q * Hkv * D * 2 * 2 * 2 + total_q * 8
+    return flops, ext_bytes, store_bytes, int(n_keys.sum())
+
+
 class ExtendBench:
-    """The c3 extend batch replicated over `layers` SWA layers."""
+    """An extend batch replicated over `layers` SWA layers."""
 
     def __init__(self, torch, swa, wl, layers, seed=11):
         self.torch, self.swa, self.wl = torch, swa, wl
@@ -337,9 +511,7 @@ class ExtendBench:
         self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, wl.page_size)
         self.full_loc = torch.from_numpy(wl.new_full_loc).cuda()
         self.swa_loc = torch.empty_like(self.full_loc)
-        lo = np.maximum(wl.prefix_lens.astype(np.int64) - wl.window, 0)
-        self.n_keys = (wl.seq_lens.astype(np.int64) - lo)
-        self.cap = int(self.n_keys.sum())
+        self.extend_flops, self.extend_bytes, self.store_bytes, self.cap = extend_counts(wl)
         self.table = torch.empty(self.cap, dtype=torch.int32, device="cuda")
         self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
         used = torch.from_numpy(wl.pool_k.used_rows).cuda()
@@ -357,15 +529,6 @@ class ExtendBench:
                                     new_v=randn_store(torch, (total_q, Hkv, D), g, "bf16"),
                                     out=torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device="cuda")))
         self.sinks = torch.from_numpy(wl.sinks).cuda()
-        # algorithmic bytes and band-only FLOPs of one extend launch
-        self.extend_bytes = int(total_q * Hq * D * 2 * 2 + self.n_keys.sum() * Hkv * D * 2 * 2 + self.cap * 4
-                                + (B + 1) * 4 * 2 + B * 4 * 2)
-        pairs = 0
-        for b in range(B):
-            i = np.arange(int(wl.prefix_lens[b]), int(wl.seq_lens[b]))
-            pairs += int(np.sum(i - np.maximum(i - wl.window, 0) + 1))
-        self.extend_flops = pairs * Hq * D * 4
-        self.store_bytes = total_q * Hkv * D * 2 * 2 * 2 + total_q * 8
         self.step_bytes = total_q * 8 * 3 + self.cap * 16 + layers * (self.store_bytes + self.extend_bytes)
         self.step_flops = layers * self.extend_flops
 
@@ -375,155 +538,139 @@ class ExtendBench:
         swa.swa_translate_window(self.index, wl.window, self.table, self.indptr, prefix_lens=self.prefix)
         for ly in self.layers:
             swa.swa_kv_store(ly["kv"], self.swa_loc, ly["new_k"], ly["new_v"])
-            swa.swa_extend(ly["q"], self.qo, self.prefix, ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                           slot_table=self.table, table_indptr=self.indptr)
+            self.extend_call(ly)
+
+    def extend_call(self, ly):
+        self.swa.swa_extend(ly["q"], self.qo, self.prefix, ly["kv"], self.index, self.wl.window, ly["out"],
+                            sinks=self.sinks, slot_table=self.table, table_indptr=self.indptr)
 
     def dominant(self):
-        swa, wl = self.swa, self.wl
         for ly in self.layers:
-            swa.swa_extend(ly["q"], self.qo, self.prefix, ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                           slot_table=self.table, table_indptr=self.indptr)
+            self.extend_call(ly)
 
 
-def cpu_baseline_extend(wl, budget_s=12.0):
-    from threadpoolctl import threadpool_limits
-    from oracle import swa_oracle as O
-    rows_done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        swa_loc = O.translate_loc(wl.new_full_loc, wl.full_to_swa)
-        pk, pv = O.kv_store(wl.pool_k, wl.pool_v, swa_loc, wl.new_k, wl.new_v, "bf16", "bf16")
-        O.window_table(wl.req_to_token, wl.req_pool_idx, wl.seq_lens, wl.full_to_swa, wl.window,
-                       prefix_lens=wl.prefix_lens)
-        r = 0
-        while time.perf_counter() - t0 < budget_s:
-            only = [(r, h) for h in range(wl.q_heads)]
-            O.extend(wl.q, "bf16", wl.qo_indptr, wl.prefix_lens, pk, pv, "bf16", wl.req_to_token, wl.req_pool_idx,
-                     wl.seq_lens, wl.full_to_swa, wl.window, wl.sinks, only=only)
-            r = (r + 997) % wl.q.shape[0]
-            rows_done += 1
-    return time.perf_counter() - t0, rows_done
+def extend_host(window=128):
+    from sliding_window_attention_swa_amd import workloads as W
+    return W.c3_extend_bf16(window=window)
 
 
-def run_extend_workload(args, torch, swa, W):
-    wl, layers = W.c3_extend_bf16(), 4
-    log(f"[bench] c3: building {layers} layers")
+def run_extend_gpu(args, torch, swa, name, wl, cpu, layers=4):
+    log(f"[bench] {name}: building {layers} layers (W = {wl.window})")
     bench = ExtendBench(torch, swa, wl, layers)
-    g_step = graph_of(torch, bench.step)
-    for _ in range(args.warmup):
-        g_step.replay()
-    ms = time_replays(torch, g_step, args.steps)
-    g_dom = graph_of(torch, bench.dominant)
-    ms_ext = time_replays(torch, g_dom, max(5, args.steps)) / layers
-    pct = replay_percentiles(torch, g_dom, max(5, args.steps), layers)
-    log(f"[bench] step {ms:.4f} ms, extend {ms_ext * 1e3:.2f} us")
+    ms = timed_step(torch, bench.step, args.steps, args.warmup)
+    reps = max(5, args.steps)
+    ms_ext, pct = timed_dominant(torch, bench.dominant, reps, layers)
+    log(f"[bench] {name}: step {ms:.4f} ms, extend {ms_ext * 1e3:.2f} us")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
-    achieved = bench.extend_bytes / (ms_ext * 1e-3) / 1e9
+    achieved_gbs = bench.extend_bytes / (ms_ext * 1e-3) / 1e9
     tflops = bench.extend_flops / (ms_ext * 1e-3) / 1e12
+    intensity = bench.extend_flops / bench.extend_bytes
+    attainable = min(BF16_PEAK_TFLOPS, intensity * HBM_PEAK_GBS / 1e3)
+    bound = "hbm" if intensity * HBM_PEAK_GBS / 1e3 < BF16_PEAK_TFLOPS else "mfma"
+    prof = profile_record(f"swa_extend_{name}", EXTEND_SRC)
+    roof = dict(kernel="swa_extend", bound=bound, flops_per_launch=bench.extend_flops,
+                bytes_per_launch=bench.extend_bytes, us_per_launch=round(ms_ext * 1e3, 3), **pct,
+                tflops=round(tflops, 2), frac_of_mfma_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
+                attainable_tflops=round(attainable, 1), frac_of_attainable=round(tflops / attainable, 4),
+                achieved_gbs=round(achieved_gbs, 1), frac_of_hbm_peak=round(achieved_gbs / HBM_PEAK_GBS, 4),
+                traffic=None if prof is None else prof.get("hbm_bytes_per_launch"),
+                mfma_busy_counter=None if prof is None else prof.get("mfma_busy_frac"))
+    if bound == "hbm":
+        roof.update(achieved=round(achieved_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved_gbs / HBM_PEAK_GBS, 4))
+    else:
+        roof.update(achieved=round(tflops, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tflops / BF16_PEAK_TFLOPS, 4))
     res = dict(
-        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
-        data="synthetic",
-        config={"workload": "chunked-prefill extend B=4, prefix 8K + chunk 2K, W=128, 64q/8kv, D=128, bf16, page 64",
-                "global_batch": int(wl.batch), "new_tokens": int(wl.q.shape[0]), "layers_per_step": layers,
-                "window": wl.window, "parallelism": "none (1 GPU)"},
-        tokens_per_s=round(wl.q.shape[0] / (ms * 1e-3) * layers / layers, 1),
-        extend_tflops=round(tflops, 2), extend_frac_of_mfma_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
-        extend_attainable_tflops=round(min(BF16_PEAK_TFLOPS, bench.extend_flops / bench.extend_bytes * HBM_PEAK_GBS
-                                           / 1e3), 1),
-        roofline=dict(kernel="swa_extend", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4),
-                      traffic=traffic_from_profile("swa_extend_c3", ["extend_kernels.hip", "common.hpp", "api.cpp"], 1),
-                      bytes_per_launch=bench.extend_bytes, flops_per_launch=bench.extend_flops,
-                      us_per_launch=round(ms_ext * 1e3, 3), **pct),
+        value=round(bench.step_flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", step_gbs=round(value, 1),
+        ms_per_step=round(ms, 5), dtype="bf16",
+        config={"workload": f"chunked-prefill extend B={wl.batch}, prefix 8K + chunk 2K, W={wl.window}, 64q/8kv, "
+                            f"D=128, bf16, page 64 (store + extend per layer)", "global_batch": int(wl.batch),
+                "new_tokens": int(wl.q.shape[0]), "layers_per_step": layers, "window": wl.window},
+        tokens_per_s=round(wl.q.shape[0] * layers / (ms * 1e-3), 1),
+        roofline=roof,
     )
-    if not args.no_cpu_baseline:
-        secs, rows = cpu_baseline_extend(wl)
-        per_row_flops = bench.extend_flops / wl.q.shape[0]
-        res["cpu_baseline"] = dict(value=round(rows * per_row_flops / secs / 1e12, 9), unit="TFLOP/s", cores=1,
-                                   kind="oracle", sample=f"translate + store + window table, then {rows} query rows x "
-                                                         f"{wl.q_heads} heads ({secs:.1f} s)")
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    del bench
+    torch.cuda.empty_cache()
     return res
 
 
 # ---------------------------------------------------------------------------
-# c4: 48-layer mixed decode step (39 SWA + 9 full layers)
+# c4: 48-layer mixed decode step (39 SWA + 9 full layers) through swa_decode_step
 # ---------------------------------------------------------------------------
 
 
+def mixed_bytes(st):
+    B, Hq, D, T, W1 = st.batch, st.q_heads, st.head_dim, int(st.seq_len), 129
+    full = B * T * 4 * D * 2 * 2 + B * Hq * D * 4 + B * T * 4
+    swl = B * W1 * 8 * D * 2 * 2 + B * Hq * D * 4 + B * W1 * 4
+    return full, swl, 9 * full + 39 * swl + B * W1 * 16
+
+
 class MixedBench:
-    def __init__(self, torch, swa, W):
-        self.torch, self.swa = torch, swa
-        st = self.st = W.c4_mixed_step()
+    def __init__(self, torch, swa, st):
+        from sliding_window_attention_swa_amd import workloads as W
+        self.torch, self.swa, self.st = torch, swa, st
         B, Hq, D = st.batch, st.q_heads, st.head_dim
-        self.r2t = torch.from_numpy(st.req_to_token).cuda()
-        self.rows = torch.from_numpy(st.req_pool_idx).cuda()
-        self.lens = torch.from_numpy(st.seq_lens).cuda()
-        self.map = torch.from_numpy(st.full_to_swa).cuda()
-        self.index = swa.IndexTables(self.r2t, self.rows, self.lens, self.map, st.page_size)
+        self.index = swa.IndexTables(torch.from_numpy(st.req_to_token).cuda(),
+                                     torch.from_numpy(st.req_pool_idx).cuda(), torch.from_numpy(st.seq_lens).cuda(),
+                                     torch.from_numpy(st.full_to_swa).cuda(), st.page_size)
         self.table = torch.empty(B * 129, dtype=torch.int32, device="cuda")
         self.indptr = torch.empty(B + 1, dtype=torch.int32, device="cuda")
-        self.layers = []
-        self.splits, ws_bytes = swa.swa_decode_plan(B, Hq, 4, D, -1, st.seq_len)
-        self.ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
-        for ly in st.layers:
-            q, k, v = W.c4_layer_tensors(st, ly)
-            self.layers.append(dict(meta=ly, q=q, kv=swa.KvLayer(k, v),
-                                    out=torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")))
-        T, W1 = st.seq_len, 129
-        self.full_bytes = B * T * 4 * D * 2 * 2 + B * Hq * D * 4 + B * T * 4
-        self.swa_bytes = B * W1 * 8 * D * 2 * 2 + B * Hq * D * 4 + B * W1 * 4
-        self.step_bytes = 9 * self.full_bytes + 39 * self.swa_bytes + B * W1 * 16
-        self.full_flops = B * T * Hq * D * 4
-
-    def layer_call(self, ly):
-        swa, m = self.swa, ly["meta"]
-        if m["kind"] == "full":
-            swa.swa_decode(ly["q"], ly["kv"], self.index, -1, ly["out"], num_splits=self.splits, workspace=self.ws,
-                           use_map=False)
-        else:
-            swa.swa_decode(ly["q"], ly["kv"], self.index, 128, ly["out"], slot_table=self.table,
-                           table_indptr=self.indptr)
+        full_ids = [ly["id"] for ly in st.layers if ly["kind"] == "full"]
+        swa_ids = [ly["id"] for ly in st.layers if ly["kind"] == "swa"]
+        self.mapping = [(full_ids.index(ly["id"]), 0) if ly["kind"] == "full" else (swa_ids.index(ly["id"]), 1)
+                        for ly in st.layers]
+        tensors = [W.c4_layer_tensors(st, ly) for ly in st.layers]
+        self.full_layers = [swa.KvLayer(tensors[i][1], tensors[i][2]) for i in full_ids]
+        self.swa_layers = [swa.KvLayer(tensors[i][1], tensors[i][2]) for i in swa_ids]
+        self.q = [t[0] for t in tensors]
+        self.out = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in st.layers]
+        self.dstep = swa.DecodeStep(self.mapping, self.full_layers, self.swa_layers, 128, self.q, self.out)
+        self.ws = torch.empty(max(self.dstep.workspace_bytes(self.index, st.seq_len) // 4, 1), dtype=torch.float32,
+                              device="cuda")
+        self.splits, _ = swa.swa_decode_plan(B, Hq, 4, D, -1, st.seq_len)
+        self.full_ids = full_ids
+        self.full_bytes, self.swa_bytes, self.step_bytes = mixed_bytes(st)
 
     def step(self):
-        self.swa.swa_translate_window(self.index, 128, self.table, self.indptr)
-        for ly in self.layers:
-            self.layer_call(ly)
+        self.swa.swa_decode_step(self.dstep, self.index, self.st.seq_len, self.table, self.indptr, self.ws)
 
     def dominant(self):
-        for ly in self.layers:
-            if ly["meta"]["kind"] == "full":
-                self.layer_call(ly)
+        """The full layers' decodes only (split-K + merge), as the step issues them."""
+        for i, lid in enumerate(self.full_ids):
+            self.swa.swa_decode(self.q[lid], self.full_layers[i], self.index, -1, self.out[lid],
+                                num_splits=self.splits, workspace=self.ws, use_map=False)
 
 
-def run_mixed_workload(args, torch, swa, W):
+def run_mixed_gpu(args, torch, swa, st, cpu):
     log("[bench] c4: building 48 layers")
-    bench = MixedBench(torch, swa, W)
-    g_step = graph_of(torch, bench.step)
-    for _ in range(args.warmup):
-        g_step.replay()
-    ms = time_replays(torch, g_step, args.steps)
-    g_dom = graph_of(torch, bench.dominant)
-    ms_full = time_replays(torch, g_dom, max(3, args.steps // 2)) / 9
-    pct = replay_percentiles(torch, g_dom, max(3, args.steps // 2), 9)
-    log(f"[bench] step {ms:.3f} ms, full-layer decode {ms_full * 1e3:.1f} us")
+    bench = MixedBench(torch, swa, st)
+    ms = timed_step(torch, bench.step, args.steps, args.warmup)
+    reps = max(3, args.steps // 2)
+    ms_full, pct = timed_dominant(torch, bench.dominant, reps, 9)
+    log(f"[bench] c4: step {ms:.3f} ms, full-layer decode {ms_full * 1e3:.1f} us")
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     achieved = bench.full_bytes / (ms_full * 1e-3) / 1e9
-    st = bench.st
     res = dict(
-        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
-        data="synthetic",
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 4), dtype="bf16",
         config={"workload": "mixed 48-layer decode step B=32, T=32K, 39 SWA (W=128, 8kv) + 9 full (4kv) layers, "
-                            "64q, D=128, bf16, page 64, SWA ratio 0.1", "global_batch": st.batch,
-                "seq_len": st.seq_len, "layers": 48, "parallelism": "none (1 GPU)"},
+                            "64q, D=128, bf16, page 64, SWA ratio 0.1, one swa_decode_step call",
+                "global_batch": st.batch, "seq_len": st.seq_len, "layers": 48},
         tokens_per_s=round(st.batch / (ms * 1e-3), 1),
+        frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
         roofline=dict(kernel="swa_decode full layer (split-K + merge)", bound="hbm", achieved=round(achieved, 1),
                       peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                      traffic=traffic_from_profile("swa_decode_full_c4", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1),
+                      traffic=traffic_from_profile("swa_decode_full_c4", DECODE_SRC),
                       bytes_per_launch=bench.full_bytes, us_per_launch=round(ms_full * 1e3, 2),
                       splits=bench.splits, **pct),
     )
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+    del bench
+    torch.cuda.empty_cache()
     return res
 
 
@@ -585,65 +732,28 @@ class UnifiedBench:
                                  use_map=False)
 
 
-def cpu_baseline_unified(bench, budget_s=12.0):
-    """The oracle over the first layer's view (read back to the host once), on
-    as many requests as fit the budget."""
-    from threadpoolctl import threadpool_limits
-    from oracle import swa_oracle as O
-    ub = bench.ub
-    raw = bench.raw.cpu().numpy()
-    ks, vs = O.unified_views(raw, 0, ub.layers, ub.kv_heads, ub.head_dim, np.uint16, ub.page_size, ub.n_phys)
-    m = O.unified_mapping(ub.v2p, ub.page_size, bench.mult)
-    q = bench.layers[0]["q"].view(bench.torch.int16).cpu().numpy().view(np.uint16)
-    done, b = 0, 0
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        while time.perf_counter() - t0 < budget_s:
-            O.decode(q, "bf16", ks[0], vs[0], "bf16", ub.req_to_token, ub.req_pool_idx, ub.seq_lens, m, ub.window,
-                     ub.sinks, only=[(b, h) for h in range(ub.q_heads)])
-            b = (b + 1) % ub.batch
-            done += 1
-    return time.perf_counter() - t0, done
-
-
 def run_unified_workload(args, torch, swa, W):
     ub = W.unified_c2_decode()
     log(f"[bench] unified: building one sub-pool of {ub.layers} layers")
     bench = UnifiedBench(torch, swa, ub)
-    g_step = graph_of(torch, bench.step)
-    for _ in range(args.warmup):
-        g_step.replay()
-    ms = time_replays(torch, g_step, args.steps)
-    g_dec = graph_of(torch, bench.dominant)
-    dec_reps = max(10, args.steps // 2)
-    ms_dec = time_replays(torch, g_dec, dec_reps) / ub.layers
-    pct = replay_percentiles(torch, g_dec, dec_reps, ub.layers)
+    ms = timed_step(torch, bench.step, args.steps, args.warmup)
+    ms_dec, pct = timed_dominant(torch, bench.dominant, max(10, args.steps // 2), ub.layers)
     value = bench.step_bytes / (ms * 1e-3) / 1e9
     dom_bytes = bench.decode_bytes + bench.store_bytes
     achieved = dom_bytes / (ms_dec * 1e-3) / 1e9
     log(f"[bench] unified step {ms:.4f} ms; swa_decode_store {ms_dec * 1e3:.2f} us per layer")
-    traffic = traffic_from_profile("swa_decode_unified_c2", ["decode_kernels.hip", "common.hpp", "api.cpp"], 1)
-    res = dict(
-        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
-        data="synthetic",
+    return dict(
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5), dtype="bf16",
         config={"workload": "batched SWA decode B=64, T~U[1K,8K], W=128, 64q/8kv, D=128, bf16, page 16, over one "
                             "unified sub-pool of 32 layers (page-major envelopes, dense per-layer views)",
                 "global_batch": int(ub.batch), "layers_per_step": ub.layers, "window": ub.window,
-                "pool_bytes": int(bench.raw_bytes), "parallelism": "none (1 GPU)"},
+                "pool_bytes": int(bench.raw_bytes)},
         tokens_per_s=round(ub.batch / (ms * 1e-3), 1),
         roofline=dict(kernel="swa_decode_store (store fused) over unified views", bound="hbm",
                       achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                      traffic=traffic, bytes_per_launch=dom_bytes, us_per_launch=round(ms_dec * 1e3, 3), **pct),
+                      traffic=traffic_from_profile("swa_decode_unified_c2", DECODE_SRC), bytes_per_launch=dom_bytes,
+                      us_per_launch=round(ms_dec * 1e3, 3), **pct),
     )
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        secs, nreq = cpu_baseline_unified(bench)
-        res["cpu_baseline"] = dict(value=round(nreq * bench.decode_bytes / ub.batch / secs / 1e9, 6), unit="GB/s",
-                                   cores=1, kind="oracle",
-                                   sample=f"one layer's decode of {nreq} requests x {ub.q_heads} heads over the "
-                                          f"unified view ({secs:.1f} s)")
-    return res
 
 
 # ---------------------------------------------------------------------------
@@ -694,17 +804,6 @@ class EvictBench:
                                self.count[i], interval=128, workspace=self.ws)
 
 
-def cpu_baseline_evict(eb, budget_s=12.0):
-    from oracle import swa_oracle as O
-    reps = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        O.evict(eb.req_to_token, eb.req_pool_idx, eb.full_to_swa, eb.pre_lens, eb.evicted_lens, eb.window,
-                eb.page_size, interval=128)
-        reps += 1
-    return time.perf_counter() - t0, reps
-
-
 def run_evict_workload(args, torch, swa, W):
     eb = W.evict_after_prefill()
     log("[bench] evict: building 16 copies of the index tables")
@@ -727,8 +826,7 @@ def run_evict_workload(args, torch, swa, W):
     ms = float(per_call.mean())
     positions, pages = bench.released()
     # a further replay finds every request's interval gate shut: the per-step cost
-    # of calling the eviction when nothing is due (skipped in profiling runs, whose
-    # per-kernel averages should cover the releasing calls only)
+    # of calling the eviction when nothing is due (skipped in profiling runs)
     noop = None if args.skip_noop else time_replays(torch, g, 20) / bench.copies
     # algorithmic bytes of one call: per released position its req_to_token
     # entry (4 B) and its mapping entry read and cleared (8 + 8 B); per released
@@ -738,33 +836,25 @@ def run_evict_workload(args, torch, swa, W):
     value = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] evict {ms * 1e3:.2f} us per call, {positions} positions, {pages} pages; "
         f"no-op call {'-' if noop is None else f'{noop * 1e3:.2f}'} us")
-    traffic = traffic_from_profile("swa_evict_after_prefill", ["evict_kernels.hip", "common.hpp", "api.cpp"], 1)
-    res = dict(
-        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=n_rep * bench.copies,
-        warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
-        dtype="int64", data="synthetic",
+    return dict(
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5), dtype="int64", steps=n_rep * bench.copies,
         config={"workload": "SWA eviction right after prefill: B=256, lognormal lengths (median 16K, clipped to "
                             "[512, 64K]), W=128, page 64, decode interval 128, every position mapped",
                 "global_batch": int(eb.batch), "window": eb.window, "page_size": eb.page_size,
-                "released_positions": int(positions), "released_pages": pages,
-                "parallelism": "none (1 GPU)"},
+                "released_positions": int(positions), "released_pages": pages},
         timed="back-to-back calls on 16 distinct copies of the index tables, replayed as one graph; the "
               "mappings are restored between replays, outside the timed events",
         positions_per_s=round(positions / (ms * 1e-3), 1),
         noop_call_us=None if noop is None else round(noop * 1e3, 3),
         roofline=dict(kernel="swa_evict (scan + apply)", bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS,
-                      unit="GB/s", frac=round(value / HBM_PEAK_GBS, 4), traffic=traffic, bytes_per_launch=nbytes,
-                      us_per_launch=round(ms * 1e3, 3),
+                      unit="GB/s", frac=round(value / HBM_PEAK_GBS, 4),
+                      traffic=traffic_from_profile("swa_evict_after_prefill", ["evict_kernels.hip", "common.hpp",
+                                                                               "api.cpp"]),
+                      bytes_per_launch=nbytes, us_per_launch=round(ms * 1e3, 3),
                       p10_us=round(float(np.percentile(per_call, 10)) * 1e3, 3),
                       p50_us=round(float(np.percentile(per_call, 50)) * 1e3, 3),
                       p90_us=round(float(np.percentile(per_call, 90)) * 1e3, 3)),
     )
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        secs, reps = cpu_baseline_evict(eb)
-        res["cpu_baseline"] = dict(value=round(reps * nbytes / secs / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
-                                   sample=f"the whole batch, {reps} times ({secs:.1f} s)")
-    return res
 
 
 # ---------------------------------------------------------------------------
@@ -779,7 +869,7 @@ class AllocBench:
 
     def __init__(self, torch, swa, ab, decode):
         self.torch, self.swa, self.ab, self.decode = torch, swa, ab, decode
-        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
         self.pre, self.seq, self.last = dev(ab.pre_lens), dev(ab.seq_lens), dev(ab.last_loc)
         self.map = dev(ab.full_to_swa)
         self.free_full, self.free_swa = dev(ab.free_full), dev(ab.free_swa)
@@ -807,17 +897,6 @@ class AllocBench:
             raise RuntimeError("allocation refused: free lists too short")
 
 
-def cpu_baseline_alloc(ab, decode, budget_s=12.0):
-    from oracle import swa_oracle as O
-    reps = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        O.alloc_paired(ab.pre_lens, ab.seq_lens, ab.last_loc, ab.free_full, ab.free_swa, ab.full_to_swa,
-                       ab.page_size, decode=decode)
-        reps += 1
-    return time.perf_counter() - t0, reps
-
-
 def run_alloc_workload(args, torch, swa, W):
     log("[bench] alloc: building the prefill-chunk and decode-step states")
     ext = AllocBench(torch, swa, W.alloc_prefill_chunk(), decode=False)
@@ -835,28 +914,21 @@ def run_alloc_workload(args, torch, swa, W):
     value = ext.bytes / (ms * 1e-3) / 1e9
     log(f"[bench] alloc_extend {ms * 1e3:.2f} us ({ext.n} positions, {ext.pages} pages per pool); "
         f"alloc_decode {ms_dec * 1e3:.2f} us ({dec.n} requests, {dec.pages} pages)")
-    traffic = traffic_from_profile("swa_alloc_prefill_chunk", ["alloc_kernels.hip", "common.hpp", "api.cpp"], 1)
-    res = dict(
-        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=n_rep * reps, warmup=args.warmup,
-        ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="int64",
-        data="synthetic",
+    return dict(
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5), dtype="int64", steps=n_rep * reps,
         config={"workload": "paired allocation (full and SWA pool, mapping written) of one 2048-position prefill "
                             "chunk for each of 256 requests with lognormal lengths (median 16K), page 64",
                 "global_batch": int(ext.ab.batch), "page_size": ext.ab.page_size, "new_positions": ext.n,
-                "new_pages_per_pool": int(ext.pages), "parallelism": "none (1 GPU)"},
+                "new_pages_per_pool": int(ext.pages)},
         positions_per_s=round(ext.n / (ms * 1e-3), 1),
         decode_step_us=round(ms_dec * 1e3, 3),
         decode_step="alloc_decode of one position for each of the same 256 requests",
         roofline=dict(kernel="alloc_extend", bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(value / HBM_PEAK_GBS, 4), traffic=traffic, bytes_per_launch=ext.bytes,
-                      us_per_launch=round(ms * 1e3, 3), **pct),
+                      frac=round(value / HBM_PEAK_GBS, 4),
+                      traffic=traffic_from_profile("swa_alloc_prefill_chunk", ["alloc_kernels.hip", "common.hpp",
+                                                                               "api.cpp"]),
+                      bytes_per_launch=ext.bytes, us_per_launch=round(ms * 1e3, 3), **pct),
     )
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        secs, n = cpu_baseline_alloc(ext.ab, False)
-        res["cpu_baseline"] = dict(value=round(n * ext.bytes / secs / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
-                                   sample=f"the whole prefill-chunk allocation, {n} times ({secs:.1f} s)")
-    return res
 
 
 def copy_probe(torch, reps=5):
@@ -873,22 +945,79 @@ def copy_probe(torch, reps=5):
             "launches": reps}
 
 
+# ---------------------------------------------------------------------------
+
+
+def host_inputs(names):
+    """Host-side workloads (numpy; no GPU) and the per-unit counts the CPU
+    baselines need."""
+    from sliding_window_attention_swa_amd import workloads as W
+    hosts = {}
+    for n in names:
+        if n == "c4":
+            st = W.c4_mixed_step()
+            hosts[n] = dict(st=st, step_bytes=mixed_bytes(st)[2])
+        elif n in ("c1", "c2", "c5"):
+            wl, layers, desc = decode_host(n)
+            out_dtype = "f32" if wl.q_dtype == "f32" else "bf16"
+            dec, store, translate, fused, _ = decode_bytes(wl, out_dtype)
+            hosts[n] = dict(wl=wl, layers=layers, desc=desc, layer_bytes=dec + store + translate)
+        else:
+            window = 128 if n == "c3" else int(n.split("_")[1])
+            wl = extend_host(window)
+            flops = extend_counts(wl)[0]
+            # a call of the oracle decodes the whole chunk's queries first (~0.4 s) and a row
+            # costs about W + 1 keys: tasks of ~1 s of rows keep that fixed part small
+            hosts[n] = dict(wl=wl, flops_per_row=flops / wl.q.shape[0],
+                            rows_per_task=max(16, 512 * 128 // window))
+    return hosts
+
+
+def contract_line(args, res, name):
+    """The one JSON line of the benchmark contract around a workload result."""
+    line = dict(metric=METRIC, value=res["value"], unit=res["unit"], n_gpus=1, steps=res.get("steps", args.steps),
+                warmup=args.warmup, ms_per_step=res["ms_per_step"], higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype=res.get("dtype", "bf16"), data="synthetic",
+                config=dict(res["config"], parallelism="none (1 GPU)"))
+    for k, v in res.items():
+        if k not in line and k not in ("steps",):
+            line[k] = v
+    line["config"]["workload_name"] = name
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "evict", "alloc", "unified"])
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "c1", "c2", "c3", "c3w", "c4", "c5", "evict", "alloc", "unified"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-noop", action="store_true",
                     help="evict: skip timing the calls that release nothing (for profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a copy kernel of known size (counter calibration)")
+    ap.add_argument("--window", type=int, default=None, help="c3w: one window of the sweep only")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
+
+    if args.copy_probe:
+        names = []
+    elif args.workload == "all":
+        names = ["c4", "c2", "c5", "c3"] + [f"c3w_{w}" for w in SWEEP_WINDOWS] + ["c1"]
+    elif args.workload == "c3w":
+        names = [f"c3w_{w}" for w in ((args.window,) if args.window else SWEEP_WINDOWS)]
+    elif args.workload in ("c1", "c2", "c3", "c4", "c5"):
+        names = [args.workload]
+    else:
+        names = []
+    hosts = host_inputs(names)
+    cpu = {} if args.no_cpu_baseline or not names else run_cpu_baselines(names, hosts)
+
     import torch
     from sliding_window_attention_swa_amd import swa
     from sliding_window_attention_swa_amd import workloads as W
@@ -899,19 +1028,25 @@ def main():
     if args.copy_probe:
         print(json.dumps(copy_probe(torch)), flush=True)
         return
-    if args.workload == "c3":
-        res = run_extend_workload(args, torch, swa, W)
-    elif args.workload == "c4":
-        res = run_mixed_workload(args, torch, swa, W)
-    elif args.workload == "evict":
-        res = run_evict_workload(args, torch, swa, W)
-    elif args.workload == "alloc":
-        res = run_alloc_workload(args, torch, swa, W)
-    elif args.workload == "unified":
-        res = run_unified_workload(args, torch, swa, W)
-    else:
-        res = run_decode_workload(args, torch, swa, W)
-    print(json.dumps(res), flush=True)
+    if args.workload in ("evict", "alloc", "unified"):
+        fn = {"evict": run_evict_workload, "alloc": run_alloc_workload, "unified": run_unified_workload}
+        print(json.dumps(contract_line(args, fn[args.workload](args, torch, swa, W), args.workload)), flush=True)
+        return
+
+    results = {}
+    for n in names:
+        h = hosts[n]
+        if n == "c4":
+            results[n] = run_mixed_gpu(args, torch, swa, h["st"], cpu.get(n))
+        elif n in ("c1", "c2", "c5"):
+            results[n] = run_decode_gpu(args, torch, swa, n, h["wl"], h["layers"], h["desc"], cpu.get(n))
+        else:
+            results[n] = run_extend_gpu(args, torch, swa, n, h["wl"], cpu.get(n))
+    head = names[0]
+    line = contract_line(args, results[head], head)
+    if len(names) > 1:
+        line["sub_results"] = {n: results[n] for n in names[1:]}
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -289,10 +289,12 @@ def c2_decode_bf16(seed=SEED_BASE + 2, batch=64, q_heads=64, kv_heads=8) -> Work
                            with_store=True)
 
 
-def c3_extend_bf16(seed=SEED_BASE + 3, batch=4, prefix=8192, chunk=2048) -> Workload:
+def c3_extend_bf16(seed=SEED_BASE + 3, batch=4, prefix=8192, chunk=2048, window=128) -> Workload:
     """Chunked-prefill extend: B = 4, prefix 8K + chunk 2K, W = 128, 64 q / 8 kv
-    heads, D = 128, bf16, P = 64; the chunk's K/V are stored first."""
-    return extend_workload("c3_extend_bf16_B4_8K+2K", seed, [prefix] * batch, [chunk] * batch, 64, 8, 128, 64)
+    heads, D = 128, bf16, P = 64; the chunk's K/V are stored first.  Other
+    windows give the same shape with a longer band (the prefill window sweep)."""
+    name = "c3_extend_bf16_B4_8K+2K" + ("" if window == 128 else f"_W{window}")
+    return extend_workload(name, seed, [prefix] * batch, [chunk] * batch, 64, 8, window, 64)
 
 
 def c5_lengths(seed, batch):

@@ -191,6 +191,11 @@ DECODE_CASES = {
     "f32_g8_w255": ([1, 256, 300], 16, 2, 255, 16, "f32", "f32", True),
     "e4m3_g8": ([1, 2, 129, 130, 1000], 16, 2, 128, 16, "bf16", "e4m3", True),
     "e4m3_g16_nosink": ([5, 600], 32, 2, 128, 64, "bf16", "e4m3", False),
+    # long windows (a per-layer sliding_window_size): split by length as planned by swa_decode_plan
+    "bf16_w1023": ([1, 1000, 1023, 1024, 1025, 3000, 5000], 16, 2, 1023, 16, "bf16", "bf16", True),
+    "bf16_w4095": ([1, 4000, 4096, 4097, 9000], 16, 2, 4095, 64, "bf16", "bf16", True),
+    "e4m3_w4095_g16": ([5, 4097, 7000], 32, 2, 4095, 64, "bf16", "e4m3", True),
+    "f32_w1023": ([1, 1024, 2500], 16, 2, 1023, 16, "f32", "f32", True),
     # batches that are a multiple of 8: the window kernel relabels its workgroups across the XCDs
     "bf16_g8_b8": ([1, 130, 2, 129, 900, 17, 128, 3000], 16, 2, 128, 16, "bf16", "bf16", True),
     "e4m3_g8_b16": ([1, 130, 2, 129, 900, 17, 128, 3000, 5, 77, 256, 1000, 129, 130, 131, 64], 16, 2, 128, 64,
@@ -307,6 +312,27 @@ def test_decode_layout_invariance(kvd):
     a = run_decode(DeviceWorkload(wl), "f32")
     b = run_decode(DeviceWorkload(relabel_swa_pages(wl, 5)), "f32")
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("window", [1023, 4095])
+def test_decode_long_window_planned_splits(window):
+    """C2's batch (B = 64, T ~ U[1K, 8K]) with a long window: swa_decode_plan
+    splits the window by its length (no hand-passed split count), the split
+    partials merge with the sink added once."""
+    from sliding_window_attention_swa_amd import swa
+    lens = WL.c2_decode_bf16().seq_lens
+    wl = WL.decode_workload(f"c2_w{window}", 700 + window, lens, 64, 8, window, 16, "bf16", "bf16", with_store=True)
+    splits, ws = swa.swa_decode_plan(wl.batch, 64, 8, 128, window, int(lens.max()))
+    say(f"decode c2 lengths, W={window}: {splits} planned splits")
+    assert splits > 1 and ws > 0
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_decode(dw, "f32")
+    reqs = [0, 1, 17, 40, 63]
+    check(out, oracle_decode(wl, only=[(b, h) for b in reqs for h in range(wl.q_heads)]), TOL["bf16"],
+          f"W={window} sampled requests")
+    out_bf = run_decode(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
 def test_decode_c1_full_size():
