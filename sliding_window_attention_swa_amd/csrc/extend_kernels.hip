@@ -31,6 +31,11 @@
 //     same L2.
 #include "common.hpp"
 
+// Row blocks per wavefront of the long-band kernel (16 / RB wavefronts per workgroup).
+#ifndef SWA_BAND_RB
+#define SWA_BAND_RB 2
+#endif
+
 namespace swa {
 namespace {
 
@@ -860,6 +865,314 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Long-band kernel: windows of 256 keys or more, and full attention (W = -1).
+// There a query sees hundreds to thousands of keys, the work per query is
+// O(W) MFMA and the kernel is bound by the matrix cores, not by HBM.
+//   * a tile is 256 q rows: the group's q heads x (256 / heads) consecutive
+//     queries of one request, in 16 row blocks of 16 queries x one head; each
+//     wavefront owns RB row blocks, so each K / V fragment it reads from LDS
+//     feeds RB MFMAs (LDS bandwidth per flop falls as 1 / RB);
+//   * the band [first key of the first query, last query] is walked in blocks
+//     of 64 keys, double-buffered in LDS: while block j is computed the rows
+//     of block j + 1 are in flight in registers and the slots of block j + 2
+//     are read; one workgroup barrier per block;
+//   * online softmax in base 2 that rescales lazily: the running max of a row
+//     moves only when a block's max exceeds it by more than 8, so a row's
+//     weights stay below 2^8 (exact in bf16 up to its relative precision) and,
+//     past the first blocks, the accumulators are almost never rescaled;
+//   * tiles are numbered (request, kv head, tile, q-head group) and dealt to
+//     the XCDs in contiguous ranges: neighbouring tiles share most of their
+//     band, so they meet in one L2.
+// ---------------------------------------------------------------------------
+constexpr int kBK = 64;                                  // keys per band block
+constexpr int kBandRowBlocks = 16;                       // 16-row MFMA blocks per tile (256 q rows)
+constexpr int kBandStage = kBK * (kKRow + kVRow);        // elements of one LDS stage (K rows, then V rows)
+constexpr int32_t kBandMinWindow = 256;                  // windows at least this long use the band kernel
+constexpr float kRescaleSlack = 8.f;                     // log2 of the largest weight before a rescale
+constexpr int32_t kPreciseBelow = 128;                   // tiles with queries before this position: two-term weights
+
+struct BandTile {
+  int32_t b, g, hq0, tile;  // request, kv head, first q head of the group, tile of the request
+};
+
+// Tile t of the numbering (request, kv head, tile, q-head group); b = -1 past the end.
+__device__ __forceinline__ BandTile band_tile(const ExtendParams &p, int32_t TQ, int32_t t) {
+  BandTile bt{-1, 0, 0, 0};
+  int32_t b = 0, ntile = 0;
+  for (; b < p.batch; ++b) {
+    ntile = (new_count(p, b) + TQ - 1) / TQ;
+    const int32_t n = ntile * p.kv_heads * p.halves;
+    if (t < n) break;
+    t -= n;
+  }
+  if (b >= p.batch) return bt;
+  const int32_t half = t % p.halves;
+  t /= p.halves;
+  bt.b = b;
+  bt.g = t / ntile;
+  bt.tile = t % ntile;
+  bt.hq0 = bt.g * p.group + half * p.ghead;
+  return bt;
+}
+
+template <int RB, int NW>
+struct BandStage {
+  static constexpr int kRowsPerPass = NW * 64 / 16;   // 16 threads per 256-byte row
+  static constexpr int kPasses = kBK / kRowsPerPass;  // K and V pieces per thread per block
+};
+
+template <int RB, int NW, bool OUT_BF16>
+__global__ void __launch_bounds__(NW * 64, 1) band_kernel(ExtendParams p) {
+  static_assert(RB * NW == kBandRowBlocks, "a tile is 16 row blocks");
+  constexpr int kPasses = BandStage<RB, NW>::kPasses;
+  constexpr int kRowsPerPass = BandStage<RB, NW>::kRowsPerPass;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBandStage];
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  const int32_t srow = threadIdx.x >> 4;   // K / V row this thread stages (plus kRowsPerPass * pass)
+  const int32_t spiece = threadIdx.x & 15;
+  const int32_t TQ = kBandRowBlocks * 16 / p.ghead;  // queries per tile
+  const int32_t nsub = TQ / 16;                      // 16-query sub-blocks per head
+  const int32_t W = p.window;
+
+  int32_t total = 0;
+  for (int32_t b = 0; b < p.batch; ++b) total += (new_count(p, b) + TQ - 1) / TQ * p.kv_heads * p.halves;
+  const int32_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
+  const int32_t x = blockIdx.x % 8;
+  const int32_t t_lo = static_cast<int32_t>(static_cast<int64_t>(total) * x / 8);
+  const int32_t t_hi = static_cast<int32_t>(static_cast<int64_t>(total) * (x + 1) / 8);
+
+  for (int32_t t = t_lo + static_cast<int32_t>(blockIdx.x / 8); t < t_hi; t += per_xcd) {
+    const BandTile bt = band_tile(p, TQ, t);
+    if (bt.b < 0) break;
+    const QoRows qrows = qo_rows(p, bt.b);
+    int32_t seq = p.seq_lens[bt.b];
+    if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
+    const int32_t prefix = p.prefix_lens[bt.b];
+    const KeySrc ks = key_src<false>(p, bt.b, prefix);
+    const int32_t i0 = prefix + bt.tile * TQ;
+    int32_t i_last = i0 + TQ - 1;
+    if (i_last > prefix + qrows.n - 1) i_last = prefix + qrows.n - 1;
+    if (i_last > seq - 1) i_last = seq - 1;
+    int32_t kj0 = W < 0 ? 0 : i0 - W;
+    if (kj0 < 0) kj0 = 0;
+    const int32_t nkeys = i_last >= kj0 ? i_last - kj0 + 1 : 0;
+    const int32_t nblk = (nkeys + kBK - 1) / kBK;
+    // queries at positions below kPreciseBelow see fewer keys than that (W >= 256)
+    const bool precise = i0 < kPreciseBelow;
+
+    // this wave's row blocks: head hh, 16-query sub-block qs
+    int32_t hh[RB], qs[RB];
+    float sink2[RB];
+    uint4 qraw[RB][4];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int32_t r = RB * w + i;
+      hh[i] = r / nsub;
+      qs[i] = r % nsub;
+      const int32_t qi = bt.tile * TQ + 16 * qs[i] + kr;  // query index within the request
+      const int64_t qrow = qrows.qo0 + (qi < qrows.n ? qi : 0);
+      const uint16_t *qp = p.q + (qrow * p.q_heads + bt.hq0 + hh[i]) * kD + 8 * lq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qraw[i][c] = *reinterpret_cast<const uint4 *>(qp + 32 * c);
+      sink2[i] = p.sinks ? p.sinks[bt.hq0 + hh[i]] * kLog2e : 0.f;
+    }
+
+    // slots of block j for this thread's rows (rows past the band read slot 0 and are zeroed)
+    auto block_slots = [&](int32_t j, int32_t (&sl)[kPasses]) {
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const int32_t k = kBK * j + srow + kRowsPerPass * ps;
+        sl[ps] = (j < nblk && k < nkeys) ? slot_at(ks, static_cast<int64_t>(kj0) + k) : 0;
+      }
+    };
+    auto block_fetch = [&](const int32_t (&sl)[kPasses], uint4 (&kv)[kPasses], uint4 (&vv)[kPasses]) {
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const int64_t s = (sl[ps] < 0 || sl[ps] >= p.rows) ? 0 : static_cast<int64_t>(sl[ps]);
+        const int64_t off = row_elem(s, p.kv_heads, bt.g, kD) + 8 * spiece;
+        kv[ps] = *reinterpret_cast<const uint4 *>(p.k + off);
+        vv[ps] = *reinterpret_cast<const uint4 *>(p.v + off);
+      }
+    };
+    auto block_put = [&](int32_t j, uint16_t *stage, const uint4 (&kv)[kPasses], const uint4 (&vv)[kPasses]) {
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const int32_t row = srow + kRowsPerPass * ps;
+        const bool ok = kBK * j + row < nkeys;
+        *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = ok ? kv[ps] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) =
+            ok ? vv[ps] : make_uint4(0, 0, 0, 0);
+      }
+    };
+
+    f32x4_t acc[RB][8];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[RB], l_run[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      m_run[i] = kNegBig;
+      l_run[i] = 0.f;
+    }
+    bf16x8_t qop[RB][4];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) __builtin_memcpy(&qop[i][c], &qraw[i][c], 16);
+
+    if (nblk > 0) {
+      int32_t sl[kPasses];
+      uint4 kv[kPasses], vv[kPasses];
+      block_slots(0, sl);
+      block_fetch(sl, kv, vv);
+      block_slots(1, sl);
+      lds_barrier();  // the previous tile's last block is consumed
+      block_put(0, lds, kv, vv);
+      lds_barrier();
+      for (int32_t j = 0; j < nblk; ++j) {
+        const bool more = j + 1 < nblk;  // workgroup-uniform
+        if (more) {
+          block_fetch(sl, kv, vv);  // block j + 1 in flight during block j
+          block_slots(j + 2, sl);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const uint16_t *kt_base = lds + (j & 1) * kBandStage;
+        const uint16_t *vt_base = kt_base + kBK * kKRow;
+        const int32_t kb = kj0 + kBK * j;  // position of the block's first key
+        // ---- S^T = K Q^T: key tile kt (16 keys), lane holds keys 4lq..4lq+3 of query kr
+        f32x4_t s[RB][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+          for (int i = 0; i < RB; ++i) s[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bf16x8_t kop;
+            __builtin_memcpy(&kop, kt_base + (16 * kt + kr) * kKRow + 32 * c + 8 * lq, 16);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) s[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[i][c], s[i][kt], 0, 0, 0);
+          }
+        }
+        // ---- masks on blocks that touch the band's edges or its end (workgroup-uniform test)
+        const bool interior = kb + kBK - 1 <= i0 && (W < 0 || kb >= i_last - W) && kBK * (j + 1) <= nkeys;
+        if (!interior) {
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const int32_t q = i0 + 16 * qs[i] + kr;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int32_t key = kb + 16 * kt + 4 * lq + r;
+                const bool ok = key <= q && (W < 0 || key >= q - W) && key - kj0 < nkeys;
+                s[i][kt][r] = ok ? s[i][kt][r] : -INFINITY;
+              }
+          }
+        }
+        // ---- softmax: block max per row, lazy rescale, weights packed to bf16
+        float mx[RB];
+        bool grow = false;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, s[i][kt][r]);
+          mx[i] = wave_max_q(m) * p.scale2;
+          grow = grow || mx[i] > m_run[i] + kRescaleSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const float m_new = fmaxf(m_run[i], mx[i]);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
+            m_run[i] = m_new;
+            l_run[i] *= alpha;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc[i][n] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[i][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[i][kt][r], p.scale2, -m_run[i]));
+        // ---- O^T += V^T P^T over the key-tile pairs (0, 1) and (2, 3).  The
+        // weights enter as bf16 and the normaliser sums the same rounded
+        // weights.  In a tile with queries of fewer than kPreciseBelow keys a
+        // weight also enters its rounding remainder (a second bf16 term), so
+        // that the few weights of such a query carry 16 significant bits.
+        const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t pop[RB], plo[RB];
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const f32x4_t &e0 = s[i][2 * u], &e1 = s[i][2 * u + 1];
+            const uint32_t u4[4] = {pack_bf16x2_hw(e0[0], e0[1]), pack_bf16x2_hw(e0[2], e0[3]),
+                                    pack_bf16x2_hw(e1[0], e1[1]), pack_bf16x2_hw(e1[2], e1[3])};
+            l_run[i] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[i]))));
+            __builtin_memcpy(&pop[i], u4, 16);
+            if (precise) {
+              const float ev[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+              uint32_t r4[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float h0 = __uint_as_float(u4[k] << 16), h1 = __uint_as_float(u4[k] & 0xFFFF0000u);
+                r4[k] = pack_bf16x2_hw(ev[2 * k] - h0, ev[2 * k + 1] - h1);
+              }
+              l_run[i] = bf16x2_acc(r4[3], bf16x2_acc(r4[2], bf16x2_acc(r4[1], bf16x2_acc(r4[0], l_run[i]))));
+              __builtin_memcpy(&plo[i], r4, 16);
+            }
+          }
+          const uint16_t *va = vt_base + (32 * u) * kVRow + voff;
+          const uint16_t *vb = va + 16 * kVRow;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            const i16x4_t lo = lds_read_tr16(va + 16 * n);
+            const i16x4_t hi = lds_read_tr16(vb + 16 * n);
+            const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i], acc[i][n], 0, 0, 0);
+            if (precise) {
+#pragma unroll
+              for (int i = 0; i < RB; ++i)
+                acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[i], acc[i][n], 0, 0, 0);
+            }
+          }
+        }
+        if (more) block_put(j + 1, lds + ((j + 1) & 1) * kBandStage, kv, vv);
+        lds_barrier();
+      }
+    }
+    // ---- sink once, normalise, store the valid query rows
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      typename HeadOut<OUT_BF16>::type o;
+      finish_head<OUT_BF16>(p, acc[i], m_run[i], l_run[i], sink2[i], o);
+      const int32_t qi = bt.tile * TQ + 16 * qs[i] + kr;
+      if (qi < qrows.n) write_head<OUT_BF16>(p, o, bt.hq0 + hh[i], qrows.qo0 + qi);
+    }
+  }
+}
+
+template <int RB, int NW>
+hipError_t launch_band(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStream_t stream) {
+  if (out_bf16)
+    hipLaunchKernelGGL((band_kernel<RB, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((band_kernel<RB, NW, false>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 // Workgroups of the persistent grid: two per CU of the 256 on MI355X for one
 // head per wavefront (the LDS ring allows two); one per CU for MB >= 2, whose
 // wavefronts then have the whole register file (measured as fast as two per
@@ -916,6 +1229,14 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   grid = (grid + 7) / 8 * 8;
   const uint32_t runs = static_cast<uint32_t>(grid);
   const bool out_bf16 = a.out_dtype == SWA_BF16;
+  if (a.chunk == 0 && (a.window < 0 || a.window >= kBandMinWindow)) {
+    // long bands: 256-row tiles, one workgroup per CU
+    const int64_t tq = kBandRowBlocks * 16 / p.ghead;
+    const int64_t band_tiles = ((a.total_q + tq - 1) / tq + a.idx.batch) * a.layer.kv_heads * p.halves;
+    int64_t bgrid = band_tiles < kResidentGroups / 2 ? band_tiles : kResidentGroups / 2;
+    bgrid = (bgrid + 7) / 8 * 8;
+    return launch_band<SWA_BAND_RB, kBandRowBlocks / SWA_BAND_RB>(p, static_cast<uint32_t>(bgrid), out_bf16, stream);
+  }
   if (mb == 2) {
     if (p.ghead != kNW * 2) return hipErrorInvalidValue;
     return launch_mb<2, true>(p, runs, out_bf16, stream);

@@ -564,6 +564,15 @@ EXTEND_CASES = {
     "g4_empty_first": ([64, 0, 500], [0, 0, 200], 8, 2, 128, 16, False),
     "g8_one_token": ([0], [1], 16, 2, 128, 16, True),
     "g8_w255": ([100, 400], [300, 70], 16, 2, 255, 16, True),
+    # long bands (W >= 256 and W = -1): the 256-row tiles of the band kernel
+    "g8_w256": ([0, 300, 1000], [500, 40, 129], 16, 2, 256, 16, True),
+    "g8_w512": ([0, 600, 1500], [700, 300, 64], 16, 2, 512, 16, True),
+    "g8_w4095_ragged": ([4100, 10, 0, 5000], [300, 17, 0, 1], 16, 2, 4095, 64, True),
+    "g8_full_long": ([3000, 0], [200, 77], 16, 2, -1, 64, False),
+    "g1_w1000": ([200, 1500], [300, 40], 2, 2, 1000, 16, True),
+    "g2_w600": ([700, 0], [260, 300], 4, 2, 600, 16, True),
+    "g4_w2000": ([2500, 100], [150, 400], 8, 2, 2000, 64, False),
+    "g16_w1024": ([1200, 33], [100, 260], 32, 2, 1024, 16, True),
 }
 
 
@@ -667,6 +676,26 @@ def test_extend_c3_full_size_sampled():
     only |= {(r, h) for r in range(wl.q.shape[0]) for h in heads4}
     ref = oracle_extend(wl, only=sorted(only))
     check(out, ref, TOL["bf16"], "c3: every row x 4 heads, 380 rows x every head")
+
+
+@pytest.mark.parametrize("window", [512, 4096])
+def test_extend_c3_shape_long_window_sampled(window):
+    """The C3 shape (4 x (8K prefix + 2K chunk), 64 q / 8 kv heads) with a long
+    window, on the band kernel: sampled rows (the first and last of each
+    request's chunk and a seeded spread), every q head."""
+    wl = WL.c3_extend_bf16(window=window)
+    say(f"extend c3 shape, W={window} — sampled rows")
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_extend(dw, "f32")
+    rng = np.random.default_rng(window)
+    edges = np.concatenate([np.arange(q0, q0 + 3) for q0 in wl.qo_indptr[:-1]] +
+                           [np.arange(q1 - 3, q1) for q1 in wl.qo_indptr[1:]])
+    rows = np.unique(np.concatenate([edges, rng.choice(wl.q.shape[0], 60, replace=False)]))
+    only = [(int(r), h) for r in rows for h in range(wl.q_heads)]
+    check(out, oracle_extend(wl, only=only), TOL["bf16"], f"c3 shape W={window} sampled")
+    out_bf = run_extend(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
 # ---------------------------------------------------------------------------
