@@ -31,10 +31,18 @@
 //     same L2.
 #include "common.hpp"
 
-// Row blocks per wavefront of the long-band kernel (16 / RB wavefronts per workgroup).
+// Long-band kernel shape: row blocks per wavefront, wavefronts per workgroup,
+// workgroups per CU.
 #ifndef SWA_BAND_RB
 #define SWA_BAND_RB 2
 #endif
+#ifndef SWA_BAND_NW
+#define SWA_BAND_NW 8
+#endif
+#ifndef SWA_BAND_WGS
+#define SWA_BAND_WGS 1
+#endif
+
 
 namespace swa {
 namespace {
@@ -886,7 +894,6 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
 //     band, so they meet in one L2.
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;                                  // keys per band block
-constexpr int kBandRowBlocks = 16;                       // 16-row MFMA blocks per tile (256 q rows)
 constexpr int kBandStage = kBK * (kKRow + kVRow);        // elements of one LDS stage (K rows, then V rows)
 constexpr int32_t kBandMinWindow = 256;                  // windows at least this long use the band kernel
 constexpr float kRescaleSlack = 8.f;                     // log2 of the largest weight before a rescale
@@ -916,26 +923,223 @@ __device__ __forceinline__ BandTile band_tile(const ExtendParams &p, int32_t TQ,
   return bt;
 }
 
-template <int RB, int NW>
+// Everything a tile's block loop needs, fixed per tile.
+struct BandCtx {
+  KeySrc ks;
+  int32_t g;       // kv head
+  int32_t i0;      // position of the tile's first query
+  int32_t i_last;  // position of its last valid query
+  int32_t kj0;     // first key of the band
+  int32_t nkeys;   // keys in the band
+  int32_t nblk;    // 64-key blocks
+};
+
+template <int NW>
 struct BandStage {
   static constexpr int kRowsPerPass = NW * 64 / 16;   // 16 threads per 256-byte row
   static constexpr int kPasses = kBK / kRowsPerPass;  // K and V pieces per thread per block
 };
 
-template <int RB, int NW, bool OUT_BF16>
-__global__ void __launch_bounds__(NW * 64, 1) band_kernel(ExtendParams p) {
-  static_assert(RB * NW == kBandRowBlocks, "a tile is 16 row blocks");
-  constexpr int kPasses = BandStage<RB, NW>::kPasses;
-  constexpr int kRowsPerPass = BandStage<RB, NW>::kRowsPerPass;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBandStage];
+// The band's blocks for this wave's RB row blocks (query positions q_of[i] +
+// kr): S^T = K Q^T, masks on edge blocks, softmax with lazy rescaling, O^T +=
+// V^T P^T.  PRECISE: each weight also enters its bf16 rounding remainder.
+//
+// Two wavefronts share each SIMD.  The odd wavefronts run one block behind in
+// their P.V: in the iteration of block j they first do P.V of block j - 1, then
+// QK^T and the softmax of block j, so the two wavefronts of a SIMD more often
+// sit in different phases (one issuing MFMAs while the other issues the
+// softmax's VALU work).  Measured at the C3 shape with W = 4096: 1128 us against
+// 1139 us with no wavefront behind, and 1208 us with the upper four behind
+// (waves 2k and 2k + 1 appear to share a SIMD).  That P.V reads the V rows of
+// block j - 1 while block j + 1 is written, hence three LDS stages.
+template <int RB, int NW, bool PRECISE>
+__device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx &c, uint16_t *lds,
+                                            const bf16x8_t (&qop)[RB][4], const int32_t (&q_of)[RB],
+                                            f32x4_t (&acc)[RB][8], float (&m_run)[RB], float (&l_run)[RB]) {
+  constexpr int kPasses = BandStage<NW>::kPasses;
+  constexpr int kRowsPerPass = BandStage<NW>::kRowsPerPass;
   const int32_t lane = threadIdx.x & 63;
-  const int32_t w = threadIdx.x >> 6;
   const int32_t kr = lane & 15;
   const int32_t lq = lane >> 4;
   const int32_t srow = threadIdx.x >> 4;   // K / V row this thread stages (plus kRowsPerPass * pass)
   const int32_t spiece = threadIdx.x & 15;
-  const int32_t TQ = kBandRowBlocks * 16 / p.ghead;  // queries per tile
-  const int32_t nsub = TQ / 16;                      // 16-query sub-blocks per head
+  const int32_t W = p.window;
+  const bool lag = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) != 0;  // wave-uniform
+
+  // slots of block j for this thread's rows (rows past the band read slot 0 and are zeroed)
+  auto block_slots = [&](int32_t j, int32_t (&sl)[kPasses]) {
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int32_t k = kBK * j + srow + kRowsPerPass * ps;
+      sl[ps] = (j < c.nblk && k < c.nkeys) ? slot_at(c.ks, static_cast<int64_t>(c.kj0) + k) : 0;
+    }
+  };
+  auto block_fetch = [&](const int32_t (&sl)[kPasses], uint4 (&kv)[kPasses], uint4 (&vv)[kPasses]) {
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int64_t s = (sl[ps] < 0 || sl[ps] >= p.rows) ? 0 : static_cast<int64_t>(sl[ps]);
+      const int64_t off = row_elem(s, p.kv_heads, c.g, kD) + 8 * spiece;
+      kv[ps] = *reinterpret_cast<const uint4 *>(p.k + off);
+      vv[ps] = *reinterpret_cast<const uint4 *>(p.v + off);
+    }
+  };
+  auto block_put = [&](int32_t j, uint16_t *stage, const uint4 (&kv)[kPasses], const uint4 (&vv)[kPasses]) {
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int32_t row = srow + kRowsPerPass * ps;
+      const bool ok = kBK * j + row < c.nkeys;
+      *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = ok ? kv[ps] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) =
+          ok ? vv[ps] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
+  // O^T += V^T P^T over the key-tile pairs (0, 1) and (2, 3) of the block whose V rows are at vt
+  auto pv = [&](const uint16_t *vt, const bf16x8_t (&pop)[RB][2], const bf16x8_t (&plo)[RB][2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t *va = vt + (32 * u) * kVRow + voff;
+      const uint16_t *vb = va + 16 * kVRow;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const i16x4_t lo = lds_read_tr16(va + 16 * n);
+        const i16x4_t hi = lds_read_tr16(vb + 16 * n);
+        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i][u], acc[i][n], 0, 0, 0);
+          if constexpr (PRECISE) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[i][u], acc[i][n], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  int32_t sl[kPasses];
+  uint4 kv[kPasses], vv[kPasses];
+  bf16x8_t pop[RB][2], plo[RB][2];  // the weights of the last softmax (the lagging half's next P.V)
+  block_slots(0, sl);
+  block_fetch(sl, kv, vv);
+  block_slots(1, sl);
+  lds_barrier();  // the previous tile's last blocks are consumed
+  block_put(0, lds, kv, vv);
+  lds_barrier();
+  uint16_t *cur = lds, *prev = lds + 2 * kBandStage, *next = lds + kBandStage;  // stages of blocks j, j - 1, j + 1
+  for (int32_t j = 0; j < c.nblk; ++j) {
+    const bool more = j + 1 < c.nblk;  // workgroup-uniform
+    if (more) {
+      block_fetch(sl, kv, vv);  // block j + 1 in flight during block j
+      block_slots(j + 2, sl);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (lag && j > 0) pv(prev + kBK * kKRow, pop, plo);  // the lagging half: P.V of block j - 1
+    const uint16_t *vt_base = cur + kBK * kKRow;
+    const int32_t kb = c.kj0 + kBK * j;  // position of the block's first key
+    // ---- S^T = K Q^T: key tile kt (16 keys), lane holds keys 4lq..4lq+3 of query kr
+    f32x4_t s[RB][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8_t kop[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) __builtin_memcpy(&kop[cc], cur + (16 * kt + kr) * kKRow + 32 * cc + 8 * lq, 16);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        s[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) s[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[cc], qop[i][cc], s[i][kt], 0, 0, 0);
+      }
+    }
+    // ---- masks on blocks that touch the band's edges or its end (workgroup-uniform test)
+    const bool interior = kb + kBK - 1 <= c.i0 && (W < 0 || kb >= c.i_last - W) && kBK * (j + 1) <= c.nkeys;
+    if (!interior) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int32_t q = q_of[i] + kr;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int32_t key = kb + 16 * kt + 4 * lq + r;
+            const bool ok = key <= q && (W < 0 || key >= q - W) && key - c.kj0 < c.nkeys;
+            s[i][kt][r] = ok ? s[i][kt][r] : -INFINITY;
+          }
+      }
+    }
+    // ---- softmax: block max per row, lazy rescale, weights packed to bf16 (the
+    // normaliser sums the same rounded weights; PRECISE adds each weight's
+    // rounding remainder as a second bf16 term, so a query's few weights carry
+    // 16 significant bits)
+    float mx[RB];
+    bool grow = false;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, s[i][kt][r]);
+      mx[i] = wave_max_q(m) * p.scale2;
+      grow = grow || mx[i] > m_run[i] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const float m_new = fmaxf(m_run[i], mx[i]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
+        m_run[i] = m_new;
+        l_run[i] *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[i][n] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[i][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[i][kt][r], p.scale2, -m_run[i]));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4_t &e0 = s[i][2 * u], &e1 = s[i][2 * u + 1];
+        const uint32_t u4[4] = {pack_bf16x2_hw(e0[0], e0[1]), pack_bf16x2_hw(e0[2], e0[3]),
+                                pack_bf16x2_hw(e1[0], e1[1]), pack_bf16x2_hw(e1[2], e1[3])};
+        l_run[i] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[i]))));
+        __builtin_memcpy(&pop[i][u], u4, 16);
+        if constexpr (PRECISE) {
+          const float ev[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+          uint32_t r4[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float h0 = __uint_as_float(u4[k] << 16), h1 = __uint_as_float(u4[k] & 0xFFFF0000u);
+            r4[k] = pack_bf16x2_hw(ev[2 * k] - h0, ev[2 * k + 1] - h1);
+          }
+          l_run[i] = bf16x2_acc(r4[3], bf16x2_acc(r4[2], bf16x2_acc(r4[1], bf16x2_acc(r4[0], l_run[i]))));
+          __builtin_memcpy(&plo[i][u], r4, 16);
+        }
+      }
+    }
+    if (!lag) pv(vt_base, pop, plo);  // the leading half: P.V of block j now
+    if (more) block_put(j + 1, next, kv, vv);
+    lds_barrier();
+    uint16_t *t = prev;
+    prev = cur;
+    cur = next;
+    next = t;
+  }
+  if (lag) pv(prev + kBK * kKRow, pop, plo);  // the last block's P.V (its stage is not rewritten before a barrier)
+}
+
+// A tile is RB * NW row blocks of 16 q rows (heads x queries); WGS
+// workgroups share a CU.
+template <int RB, int NW, int WGS, bool OUT_BF16>
+__global__ void __launch_bounds__(NW * 64, WGS) band_kernel(ExtendParams p) {
+  constexpr int kRowBlocks = RB * NW;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * kBandStage];
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  const int32_t TQ = kRowBlocks * 16 / p.ghead;  // queries per tile
+  const int32_t nsub = TQ / 16;                  // 16-query sub-blocks per head
   const int32_t W = p.window;
 
   int32_t total = 0;
@@ -952,62 +1156,38 @@ __global__ void __launch_bounds__(NW * 64, 1) band_kernel(ExtendParams p) {
     int32_t seq = p.seq_lens[bt.b];
     if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
     const int32_t prefix = p.prefix_lens[bt.b];
-    const KeySrc ks = key_src<false>(p, bt.b, prefix);
-    const int32_t i0 = prefix + bt.tile * TQ;
-    int32_t i_last = i0 + TQ - 1;
-    if (i_last > prefix + qrows.n - 1) i_last = prefix + qrows.n - 1;
-    if (i_last > seq - 1) i_last = seq - 1;
-    int32_t kj0 = W < 0 ? 0 : i0 - W;
-    if (kj0 < 0) kj0 = 0;
-    const int32_t nkeys = i_last >= kj0 ? i_last - kj0 + 1 : 0;
-    const int32_t nblk = (nkeys + kBK - 1) / kBK;
-    // queries at positions below kPreciseBelow see fewer keys than that (W >= 256)
-    const bool precise = i0 < kPreciseBelow;
+    BandCtx c;
+    c.ks = key_src<false>(p, bt.b, prefix);
+    c.g = bt.g;
+    c.i0 = prefix + bt.tile * TQ;
+    c.i_last = c.i0 + TQ - 1;
+    if (c.i_last > prefix + qrows.n - 1) c.i_last = prefix + qrows.n - 1;
+    if (c.i_last > seq - 1) c.i_last = seq - 1;
+    c.kj0 = W < 0 ? 0 : c.i0 - W;
+    if (c.kj0 < 0) c.kj0 = 0;
+    c.nkeys = c.i_last >= c.kj0 ? c.i_last - c.kj0 + 1 : 0;
+    c.nblk = (c.nkeys + kBK - 1) / kBK;
 
     // this wave's row blocks: head hh, 16-query sub-block qs
-    int32_t hh[RB], qs[RB];
+    int32_t hh[RB], qi0[RB], q_of[RB];
     float sink2[RB];
-    uint4 qraw[RB][4];
+    bf16x8_t qop[RB][4];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int32_t r = RB * w + i;
       hh[i] = r / nsub;
-      qs[i] = r % nsub;
-      const int32_t qi = bt.tile * TQ + 16 * qs[i] + kr;  // query index within the request
+      qi0[i] = bt.tile * TQ + 16 * (r % nsub);  // first query index (within the request) of the block
+      q_of[i] = prefix + qi0[i];
+      const int32_t qi = qi0[i] + kr;
       const int64_t qrow = qrows.qo0 + (qi < qrows.n ? qi : 0);
       const uint16_t *qp = p.q + (qrow * p.q_heads + bt.hq0 + hh[i]) * kD + 8 * lq;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qraw[i][c] = *reinterpret_cast<const uint4 *>(qp + 32 * c);
+      for (int cc = 0; cc < 4; ++cc) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 32 * cc);
+        __builtin_memcpy(&qop[i][cc], &raw, 16);
+      }
       sink2[i] = p.sinks ? p.sinks[bt.hq0 + hh[i]] * kLog2e : 0.f;
     }
-
-    // slots of block j for this thread's rows (rows past the band read slot 0 and are zeroed)
-    auto block_slots = [&](int32_t j, int32_t (&sl)[kPasses]) {
-#pragma unroll
-      for (int ps = 0; ps < kPasses; ++ps) {
-        const int32_t k = kBK * j + srow + kRowsPerPass * ps;
-        sl[ps] = (j < nblk && k < nkeys) ? slot_at(ks, static_cast<int64_t>(kj0) + k) : 0;
-      }
-    };
-    auto block_fetch = [&](const int32_t (&sl)[kPasses], uint4 (&kv)[kPasses], uint4 (&vv)[kPasses]) {
-#pragma unroll
-      for (int ps = 0; ps < kPasses; ++ps) {
-        const int64_t s = (sl[ps] < 0 || sl[ps] >= p.rows) ? 0 : static_cast<int64_t>(sl[ps]);
-        const int64_t off = row_elem(s, p.kv_heads, bt.g, kD) + 8 * spiece;
-        kv[ps] = *reinterpret_cast<const uint4 *>(p.k + off);
-        vv[ps] = *reinterpret_cast<const uint4 *>(p.v + off);
-      }
-    };
-    auto block_put = [&](int32_t j, uint16_t *stage, const uint4 (&kv)[kPasses], const uint4 (&vv)[kPasses]) {
-#pragma unroll
-      for (int ps = 0; ps < kPasses; ++ps) {
-        const int32_t row = srow + kRowsPerPass * ps;
-        const bool ok = kBK * j + row < nkeys;
-        *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = ok ? kv[ps] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) =
-            ok ? vv[ps] : make_uint4(0, 0, 0, 0);
-      }
-    };
 
     f32x4_t acc[RB][8];
 #pragma unroll
@@ -1020,156 +1200,34 @@ __global__ void __launch_bounds__(NW * 64, 1) band_kernel(ExtendParams p) {
       m_run[i] = kNegBig;
       l_run[i] = 0.f;
     }
-    bf16x8_t qop[RB][4];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) __builtin_memcpy(&qop[i][c], &qraw[i][c], 16);
-
-    if (nblk > 0) {
-      int32_t sl[kPasses];
-      uint4 kv[kPasses], vv[kPasses];
-      block_slots(0, sl);
-      block_fetch(sl, kv, vv);
-      block_slots(1, sl);
-      lds_barrier();  // the previous tile's last block is consumed
-      block_put(0, lds, kv, vv);
-      lds_barrier();
-      for (int32_t j = 0; j < nblk; ++j) {
-        const bool more = j + 1 < nblk;  // workgroup-uniform
-        if (more) {
-          block_fetch(sl, kv, vv);  // block j + 1 in flight during block j
-          block_slots(j + 2, sl);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const uint16_t *kt_base = lds + (j & 1) * kBandStage;
-        const uint16_t *vt_base = kt_base + kBK * kKRow;
-        const int32_t kb = kj0 + kBK * j;  // position of the block's first key
-        // ---- S^T = K Q^T: key tile kt (16 keys), lane holds keys 4lq..4lq+3 of query kr
-        f32x4_t s[RB][4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-          for (int i = 0; i < RB; ++i) s[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            bf16x8_t kop;
-            __builtin_memcpy(&kop, kt_base + (16 * kt + kr) * kKRow + 32 * c + 8 * lq, 16);
-#pragma unroll
-            for (int i = 0; i < RB; ++i) s[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[i][c], s[i][kt], 0, 0, 0);
-          }
-        }
-        // ---- masks on blocks that touch the band's edges or its end (workgroup-uniform test)
-        const bool interior = kb + kBK - 1 <= i0 && (W < 0 || kb >= i_last - W) && kBK * (j + 1) <= nkeys;
-        if (!interior) {
-#pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            const int32_t q = i0 + 16 * qs[i] + kr;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int32_t key = kb + 16 * kt + 4 * lq + r;
-                const bool ok = key <= q && (W < 0 || key >= q - W) && key - kj0 < nkeys;
-                s[i][kt][r] = ok ? s[i][kt][r] : -INFINITY;
-              }
-          }
-        }
-        // ---- softmax: block max per row, lazy rescale, weights packed to bf16
-        float mx[RB];
-        bool grow = false;
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          float m = -INFINITY;
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) m = fmaxf(m, s[i][kt][r]);
-          mx[i] = wave_max_q(m) * p.scale2;
-          grow = grow || mx[i] > m_run[i] + kRescaleSlack;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
-#pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            const float m_new = fmaxf(m_run[i], mx[i]);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
-            m_run[i] = m_new;
-            l_run[i] *= alpha;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) acc[i][n] *= alpha;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[i][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[i][kt][r], p.scale2, -m_run[i]));
-        // ---- O^T += V^T P^T over the key-tile pairs (0, 1) and (2, 3).  The
-        // weights enter as bf16 and the normaliser sums the same rounded
-        // weights.  In a tile with queries of fewer than kPreciseBelow keys a
-        // weight also enters its rounding remainder (a second bf16 term), so
-        // that the few weights of such a query carry 16 significant bits.
-        const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pop[RB], plo[RB];
-#pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            const f32x4_t &e0 = s[i][2 * u], &e1 = s[i][2 * u + 1];
-            const uint32_t u4[4] = {pack_bf16x2_hw(e0[0], e0[1]), pack_bf16x2_hw(e0[2], e0[3]),
-                                    pack_bf16x2_hw(e1[0], e1[1]), pack_bf16x2_hw(e1[2], e1[3])};
-            l_run[i] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[i]))));
-            __builtin_memcpy(&pop[i], u4, 16);
-            if (precise) {
-              const float ev[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
-              uint32_t r4[4];
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const float h0 = __uint_as_float(u4[k] << 16), h1 = __uint_as_float(u4[k] & 0xFFFF0000u);
-                r4[k] = pack_bf16x2_hw(ev[2 * k] - h0, ev[2 * k + 1] - h1);
-              }
-              l_run[i] = bf16x2_acc(r4[3], bf16x2_acc(r4[2], bf16x2_acc(r4[1], bf16x2_acc(r4[0], l_run[i]))));
-              __builtin_memcpy(&plo[i], r4, 16);
-            }
-          }
-          const uint16_t *va = vt_base + (32 * u) * kVRow + voff;
-          const uint16_t *vb = va + 16 * kVRow;
-#pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            const i16x4_t lo = lds_read_tr16(va + 16 * n);
-            const i16x4_t hi = lds_read_tr16(vb + 16 * n);
-            const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int i = 0; i < RB; ++i) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i], acc[i][n], 0, 0, 0);
-            if (precise) {
-#pragma unroll
-              for (int i = 0; i < RB; ++i)
-                acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[i], acc[i][n], 0, 0, 0);
-            }
-          }
-        }
-        if (more) block_put(j + 1, lds + ((j + 1) & 1) * kBandStage, kv, vv);
-        lds_barrier();
-      }
+    if (c.nblk > 0) {
+      // queries at positions below kPreciseBelow see fewer keys than that (W >= 256)
+      if (c.i0 < kPreciseBelow)
+        band_blocks<RB, NW, true>(p, c, lds, qop, q_of, acc, m_run, l_run);
+      else
+        band_blocks<RB, NW, false>(p, c, lds, qop, q_of, acc, m_run, l_run);
     }
     // ---- sink once, normalise, store the valid query rows
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       typename HeadOut<OUT_BF16>::type o;
       finish_head<OUT_BF16>(p, acc[i], m_run[i], l_run[i], sink2[i], o);
-      const int32_t qi = bt.tile * TQ + 16 * qs[i] + kr;
+      const int32_t qi = qi0[i] + kr;
       if (qi < qrows.n) write_head<OUT_BF16>(p, o, bt.hq0 + hh[i], qrows.qo0 + qi);
     }
   }
 }
 
-template <int RB, int NW>
-hipError_t launch_band(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStream_t stream) {
+template <int RB, int NW, int WGS>
+hipError_t launch_band(const ExtendParams &p, int64_t total_q, int32_t batch, bool out_bf16, hipStream_t stream) {
+  const int64_t tq = RB * NW * 16 / p.ghead;
+  const int64_t tiles = ((total_q + tq - 1) / tq + batch) * p.kv_heads * p.halves;
+  int64_t grid = tiles < 256 * WGS ? tiles : 256 * WGS;  // at most WGS per CU
+  grid = (grid + 7) / 8 * 8;
   if (out_bf16)
-    hipLaunchKernelGGL((band_kernel<RB, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((band_kernel<RB, NW, WGS, true>), dim3(static_cast<uint32_t>(grid)), dim3(NW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((band_kernel<RB, NW, false>), dim3(grid), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((band_kernel<RB, NW, WGS, false>), dim3(static_cast<uint32_t>(grid)), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1229,14 +1287,8 @@ hipError_t launch_extend(const ExtendArgs &a, hipStream_t stream) {
   grid = (grid + 7) / 8 * 8;
   const uint32_t runs = static_cast<uint32_t>(grid);
   const bool out_bf16 = a.out_dtype == SWA_BF16;
-  if (a.chunk == 0 && (a.window < 0 || a.window >= kBandMinWindow)) {
-    // long bands: 256-row tiles, one workgroup per CU
-    const int64_t tq = kBandRowBlocks * 16 / p.ghead;
-    const int64_t band_tiles = ((a.total_q + tq - 1) / tq + a.idx.batch) * a.layer.kv_heads * p.halves;
-    int64_t bgrid = band_tiles < kResidentGroups / 2 ? band_tiles : kResidentGroups / 2;
-    bgrid = (bgrid + 7) / 8 * 8;
-    return launch_band<SWA_BAND_RB, kBandRowBlocks / SWA_BAND_RB>(p, static_cast<uint32_t>(bgrid), out_bf16, stream);
-  }
+  if (a.chunk == 0 && (a.window < 0 || a.window >= kBandMinWindow))
+    return launch_band<SWA_BAND_RB, SWA_BAND_NW, SWA_BAND_WGS>(p, a.total_q, a.idx.batch, out_bf16, stream);
   if (mb == 2) {
     if (p.ghead != kNW * 2) return hipErrorInvalidValue;
     return launch_mb<2, true>(p, runs, out_bf16, stream);

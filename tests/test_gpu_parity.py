@@ -100,7 +100,7 @@ def test_translate_window_capacity_and_empty_batch():
     assert np.array_equal(table.cpu().numpy(), ref[:60])
     assert np.all(guard.cpu().numpy() == -5)
     # empty batch: indptr = [0]
-    empty = swa.IndexTables(dw.r2t, dw.rows[:0], dw.lens[:0], dw.map, 16)
+    empty = swa.IndexTables(dw.r2t, dw.rows[:0], dw.lens[:0], None, 16)  # no window table: no mapping either
     ip = torch.full((1,), 9, dtype=torch.int32, device="cuda")
     swa.swa_translate_window(empty, 128, table, ip)
     torch.cuda.synchronize()
@@ -587,7 +587,7 @@ def test_empty_launches_write_nothing():
     run_store(dw)
     assert run_extend(dw, "f32").shape[0] == 0
     assert run_extend(dw, "bf16", chunk=64).shape[0] == 0
-    empty = swa.IndexTables(dw.r2t, dw.rows[:0], dw.lens[:0], dw.map, 16)
+    empty = swa.IndexTables(dw.r2t, dw.rows[:0], dw.lens[:0], None, 16)  # no window table: no mapping either
     out = torch.empty((0, 16, 128), dtype=torch.float32, device="cuda")
     swa.swa_decode(dw.q, dw.layer, empty, 128, out, sinks=dw.sinks)
     swa.swa_decode(dw.q, dw.layer, empty, -1, out, num_splits=4)
