@@ -202,6 +202,24 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * decode that allocates nothing — for callers that cannot allocate device
+ * memory or hand over a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  swa_decode with the same
+ * arguments minus the workspace: the split-K partials of a plan with
+ * num_splits > 1 go to a static device array of 32 MiB that the library holds
+ * on every GPU it runs on until the process ends; its address is looked up once
+ * per device.  No hipMalloc / hipFree.  A plan whose partials
+ * (batch * q_heads * num_splits * 520 bytes) exceed 32 MiB returns
+ * SWA_E_WORKSPACE before any device call.  Every call on one GPU shares that
+ * array: calls that overlap on one GPU (other streams, concurrent threads)
+ * race.  Each call writes every partial it reads, so nothing carries over from
+ * an earlier call. */
+swa_status_t swa_decode_noalloc(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                                const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                                int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                                int32_t out_dtype, int32_t num_splits, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * decode with the current token's store fused in — the same result as
  *   swa_kv_store(layer, loc, batch, k_new, v_new, new_dtype);
  *   swa_decode(..., num_splits = 1, ...);

@@ -290,6 +290,29 @@ swa_status_t swa_decode(const void *q, int32_t q_dtype, int32_t q_heads, const s
                      nullptr, stream);
 }
 
+swa_status_t swa_decode_noalloc(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
+                                const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
+                                int64_t table_capacity, int32_t window, const float *sinks, float sm_scale, void *out,
+                                int32_t out_dtype, int32_t num_splits, hipStream_t stream) {
+  // every argument check first, with no workspace: SWA_E_WORKSPACE then means
+  // that the plan has split partials, which go to the static scratch if they fit
+  swa::DecodeArgs a;
+  swa_status_t st = decode_prepare(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity, window,
+                                   sinks, sm_scale, out, out_dtype, num_splits, nullptr, 0, false, nullptr, nullptr,
+                                   nullptr, a);
+  if (st == SWA_E_WORKSPACE) {
+    const size_t need = static_cast<size_t>(idx->batch) * q_heads * num_splits * (2 + kHeadDim) * sizeof(float);
+    if (need > swa::kStaticScratchBytes) return SWA_E_WORKSPACE;
+    void *ws = nullptr;
+    if (swa::static_scratch(&ws) != hipSuccess) return SWA_E_HIP;
+    st = decode_prepare(q, q_dtype, q_heads, layer, idx, slot_table, table_indptr, table_capacity, window, sinks,
+                        sm_scale, out, out_dtype, num_splits, ws, swa::kStaticScratchBytes, false, nullptr, nullptr,
+                        nullptr, a);
+  }
+  if (st != SWA_OK) return st;
+  return from_hip(swa::launch_decode(a, stream));
+}
+
 swa_status_t swa_decode_store(const void *q, int32_t q_dtype, int32_t q_heads, const swa_kv_layer_t *layer,
                               const swa_index_t *idx, const int32_t *slot_table, const int32_t *table_indptr,
                               int64_t table_capacity, int32_t window, const float *sinks, float sm_scale,

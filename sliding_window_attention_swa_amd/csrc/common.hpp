@@ -154,6 +154,10 @@ struct DecodeArgs {
 // Largest window the one-split window kernel (and so the fused store) handles.
 constexpr int32_t kMaxFusedWindow = 255;
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Static scratch of the no-allocation decode (split-K partials): its size, and
+// its device address on the current device.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void **ptr);
 
 hipError_t launch_validate(const swa_index_t &idx, int32_t window, const int32_t *prefix_lens,
                            const int32_t *qo_indptr, int64_t total_q, int64_t pool_rows, const int64_t *store_loc,

@@ -36,10 +36,18 @@
 // into the logit scale and the output.
 //
 // f32 path: plain VALU; 16 keys per wavefront step, 4 lanes per key row.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace swa {
 namespace {
+
+// Split-K partials of swa_decode_noalloc: a static device array of
+// kStaticScratchBytes on every GPU the library runs on, held until the process
+// ends.  Host code never uses its name as an address: it reads the array's
+// device address with hipGetSymbolAddress (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 constexpr int kD = 128;           // head_dim handled by these kernels
 constexpr int kMaxG = 16;         // q heads per kv head (MFMA N = 16)
@@ -1095,6 +1103,23 @@ hipError_t launch_stream(const DecodeParams &p, dim3 grid0, bool out_bf16, hipSt
 }
 
 }  // namespace
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t static_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void *addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] { err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)); });
+  if (err[dev] != hipSuccess) return err[dev];
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.idx.batch == 0) return hipSuccess;

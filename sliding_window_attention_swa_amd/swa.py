@@ -31,7 +31,7 @@ EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_
            "swa_alloc_decode", "swa_unified_pool_bytes", "swa_unified_layer_views", "swa_translate_kernel_ids",
            "swa_translate_window_unified", "swa_translate_window_chunked", "swa_extend_chunked",
            "swa_translate_window_ring", "swa_ring_locs", "swa_decode_workspace_bytes", "swa_decode_step",
-           "swa_decode_step_workspace_bytes", "swa_status_string")
+           "swa_decode_step_workspace_bytes", "swa_decode_noalloc", "swa_status_string")
 
 
 class SwaError(RuntimeError):
@@ -99,6 +99,8 @@ _sig = {
     "swa_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_sz)]),
     "swa_decode": (_i32, [_p, _i32, _i32, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct), _p, _p, _i64,
                           _i32, _p, _f32, _p, _i32, _i32, _p, _sz, _p]),
+    "swa_decode_noalloc": (_i32, [_p, _i32, _i32, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct), _p,
+                                  _p, _i64, _i32, _p, _f32, _p, _i32, _i32, _p]),
     "swa_decode_store": (_i32, [_p, _i32, _i32, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct), _p, _p,
                                 _i64, _i32, _p, _f32, _p, _p, _p, _i32, _p, _i32, _p]),
     "swa_extend": (_i32, [_p, _i32, _i32, _p, _p, _i64, ctypes.POINTER(KvLayerStruct), ctypes.POINTER(IndexStruct),
@@ -276,6 +278,23 @@ def swa_decode(q: torch.Tensor, layer: KvLayer, index: IndexTables, window: int,
                           num_splits, _ptr(workspace, name="workspace"),
                           0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)),
            "swa_decode")
+
+
+def swa_decode_noalloc(q: torch.Tensor, layer: KvLayer, index: IndexTables, window: int, out: torch.Tensor,
+                       sinks: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                       slot_table: Optional[torch.Tensor] = None, table_indptr: Optional[torch.Tensor] = None,
+                       num_splits: int = 1, use_map: bool = True, stream=None):
+    """swa_decode with the split partials in the library's static scratch (no workspace)."""
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be (batch, q_heads, head_dim)")
+    scale = sm_scale if sm_scale is not None else q.shape[2] ** -0.5
+    ls, ix = layer.struct(), index.struct(with_map=use_map)
+    _check(lib.swa_decode_noalloc(_ptr(q, name="q"), dtype_code(q), q.shape[1], ctypes.byref(ls), ctypes.byref(ix),
+                                  _ptr(slot_table, torch.int32, "slot_table"),
+                                  _ptr(table_indptr, torch.int32, "table_indptr"),
+                                  0 if slot_table is None else slot_table.numel(), window,
+                                  _ptr(sinks, torch.float32, "sinks"), scale, _ptr(out, name="out"), dtype_code(out),
+                                  num_splits, _stream(stream)), "swa_decode_noalloc")
 
 
 def swa_decode_store(q: torch.Tensor, layer: KvLayer, index: IndexTables, window: int, out: torch.Tensor,

@@ -470,3 +470,26 @@ def test_decode_step_argument_errors(swa):
     # an empty batch passes the checks and launches nothing
     assert step(step_struct(swa), ix=index(swa, batch=0), ws=None) == E.SWA_OK
     assert step(step_struct(swa, mapping=[])) == E.SWA_OK
+
+
+def test_decode_noalloc_host_checks(swa):
+    """The no-allocation decode checks its arguments like swa_decode, and a plan
+    whose split partials exceed the static scratch is refused before any
+    device call (so these run without a GPU)."""
+    lib, E = swa.lib, swa
+    ly = layer(swa, kv_heads=4)
+    full = index(swa, map_ptr=None)
+
+    def nd(ix=full, splits=8, q=FAKE, window=-1, scale=0.088, q_heads=64):
+        return lib.swa_decode_noalloc(q, 1, q_heads, ctypes.byref(ly), ctypes.byref(ix), None, None, 0, window, None,
+                                      scale, FAKE, 0, splits, None)
+
+    assert nd(q=None) == E.SWA_E_ARG
+    assert nd(window=-2) == E.SWA_E_ARG
+    assert nd(scale=0.0) == E.SWA_E_ARG
+    assert nd(q_heads=24) == E.SWA_E_SHAPE
+    assert nd(splits=0) == E.SWA_E_ARG
+    # 32 MiB holds batch * q_heads * splits <= 64527 partials of 520 bytes
+    big = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, None, 0, 1024, 16)
+    assert nd(ix=big, splits=8) == E.SWA_E_WORKSPACE       # 1024 x 64 x 8 partials
+    assert nd(ix=index(swa, batch=0, map_ptr=None)) == E.SWA_OK   # empty batch: nothing launched
