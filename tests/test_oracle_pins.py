@@ -132,9 +132,15 @@ def test_pool_config_page_rounding_and_nospace():
 
 
 def test_page_math_examples():
+    """The page maths the Pools article prints (slot = page x size + offset,
+    page = slot // size), through the oracle's allocator: a request that starts
+    a fresh page gets, at in-page offset k, the slot page x size + k of the page
+    its free list hands out."""
     for ex in golden()["page_math"]["examples"]:
-        assert ex["page"] * ex["page_size"] + ex["offset"] == ex["slot"]
-        assert ex["slot"] // ex["page_size"] == ex["page"]
+        P, page, off = ex["page_size"], ex["page"], ex["offset"]
+        out, taken = O.alloc_extend(np.array([0]), np.array([off + 1]), np.array([-1]), np.array([page]), P)
+        assert taken == 1 and int(out[off]) == ex["slot"]
+        assert int(out[off]) // P == page
 
 
 def make_two_pool(rng, seq_lens, P, window, margin, n_full_pages=None, n_swa_pages=None):
@@ -710,6 +716,17 @@ def test_alloc_extend_equals_token_by_token(P):
         pos = np.concatenate([np.arange(p, s) for p, s in zip(pre, seq)])
         assert np.array_equal(out % P, pos % P)                                         # in-page offsets
         assert O.pages_bound(int((seq - pre).sum()), len(pre), P) >= n
+
+
+def test_pages_bound_hand_worked():
+    """The optimistic page bound printed in the Pools article (扩容与不足):
+    extend_num_tokens // page_size + batch + 1, worked by hand.  A dropped "+ 1"
+    or a ceiling in place of the floor changes every value below."""
+    assert O.pages_bound(230, 3, 16) == 18        # 230 // 16 = 14; 14 + 3 + 1
+    assert O.pages_bound(2048, 1, 64) == 34       # 32 + 1 + 1
+    assert O.pages_bound(524288, 256, 64) == 8449  # 8192 + 256 + 1 (one 2048-token chunk each)
+    assert O.pages_bound(15, 1, 16) == 2          # 0 + 1 + 1: the floor, not the ceiling
+    assert O.pages_bound(0, 0, 16) == 1
 
 
 def test_alloc_page_size_one_slices_the_free_list():
