@@ -408,6 +408,16 @@ __device__ __forceinline__ void pv_pair(const uint16_t *pair, int32_t kr, int32_
   }
 }
 
+// O^T += V^T P^T for one 16-key block whose rows start at `blk` in the LDS
+// tile (16x16x16 MFMA); pop holds P^T of the block (keys 4lq..4lq+3, head kr).
+__device__ __forceinline__ void pv_single(const uint16_t *blk, int32_t kr, int32_t lq, const i16x4_t &pop,
+                                          f32x4_t (&acc)[8]) {
+  const uint16_t *vrow = blk + (4 * lq + (kr >> 2)) * kSVRow + 4 * (kr & 3);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(vrow + 16 * c), pop, acc[c], 0, 0, 0);
+}
+
 // Streaming kernel (long key ranges: full layers, split-K).  Each wavefront
 // walks the blocks w, w+4, w+8, ... of its workgroup's key range (the four
 // wavefronts read neighbouring blocks at the same time), two blocks per round,
@@ -631,11 +641,13 @@ __device__ __forceinline__ void window_item(int32_t &g, int32_t &b) {
 template <typename KV, int MAXB, bool OUT_BF16, bool FUSED>
 __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodeParams p) {
   // each wavefront stages one pair of blocks (32 V rows) at a time
-  constexpr int kTileBytes = kWinWaves * 32 * kSVRow * 2;
-  constexpr int kRedBytes = kWinWaves * kMaxG * kD * 4;
+  constexpr int NW = kWinWaves;
+  constexpr int kStageRows = 32;
+  constexpr int kTileBytes = NW * kStageRows * kSVRow * 2;
+  constexpr int kRedBytes = NW * kMaxG * kD * 4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
-  __shared__ float red_m[kWinWaves * kMaxG];
-  __shared__ float red_l[kWinWaves * kMaxG];
+  __shared__ float red_m[NW * kMaxG];
+  __shared__ float red_l[NW * kMaxG];
   int32_t g, b;
   window_item(g, b);
   const int32_t lane = threadIdx.x & 63;
@@ -659,7 +671,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
 #pragma unroll
     for (int u = 0; u < MAXB; ++u) {
       // keys past the window re-read its last entry (one row, cached)
-      const int32_t key = 16 * (w + kWinWaves * u) + kr;
+      const int32_t key = 16 * (w + NW * u) + kr;
       int64_t idx = spec_base + (key < p.window ? key : p.window);
       idx = idx < p.capacity ? idx : p.capacity - 1;
       sl[u] = p.table[idx < 0 ? 0 : idx];
@@ -676,7 +688,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   // request at least W + 1 long) loads them now, with the other first-hop
   // loads, and another owner loads them after the window length arrives.
   const int32_t wu = __builtin_amdgcn_readfirstlane(w);  // w, known to the compiler as wave-uniform
-  const int32_t full_owner = (p.window >> 4) % kWinWaves;
+  const int32_t full_owner = (p.window >> 4) % NW;
   uint4 kn_raw[4], vn_raw[2];
   int64_t new_loc = -1;
   if constexpr (FUSED) {
@@ -688,9 +700,9 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   const KeySource ks = key_source(p, b);
   const int32_t n = ks.n < p.window + 1 ? ks.n : p.window + 1;
   const int32_t *src = ks.src + (ks.n - n);
-  const int32_t nblk = (n + 15) >> 4;  // <= kWinWaves * MAXB for this instantiation
+  const int32_t nblk = (n + 15) >> 4;  // <= NW * MAXB for this instantiation
   const bool spec_ok = p.indptr && p.capacity > 0 && src == p.table + spec_base;
-  const int32_t owner = ((n > 0 ? n - 1 : 0) >> 4) % kWinWaves;  // wavefront holding key n - 1
+  const int32_t owner = ((n > 0 ? n - 1 : 0) >> 4) % NW;  // wavefront holding key n - 1
   const int32_t last = n - 1;
   uint4 knew[kKL], vnew;  // (fused store) the new rows in the pool format, owner wave only
 
@@ -699,7 +711,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
   for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig;
   float l_run = 0.f;
-  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * 32 * kSVRow;
+  uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + w * kStageRows * kSVRow;
 
   if (wu < nblk) {  // this wavefront owns at least one block
     // All row loads are unconditional (no control flow between them, so none
@@ -710,7 +722,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     if (!spec_ok) {
 #pragma unroll
       for (int u = 0; u < MAXB; ++u) {
-        const int32_t key = 16 * (w + kWinWaves * u) + kr;
+        const int32_t key = 16 * (w + NW * u) + kr;
         sl[u] = src[key < n ? key : 16 * w];
       }
     }
@@ -755,7 +767,7 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     float mb = -INFINITY;
 #pragma unroll
     for (int u = 0; u < MAXB; ++u) {
-      const int32_t t = w + kWinWaves * u;
+      const int32_t t = w + NW * u;
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FUSED) {
         if (wu == owner) {
@@ -775,10 +787,10 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     }
     // ---- one softmax over the wavefront's keys (no rescaling needed)
     m_run = fmaxf(kNegBig, wave_max_q(mb));
-    constexpr int kPairs = (MAXB + 1) / 2;
-    bf16x8_t pop[kPairs];
+    constexpr int kPairsN = (MAXB + 1) / 2;
+    bf16x8_t pop[kPairsN];
 #pragma unroll
-    for (int u2 = 0; u2 < kPairs; ++u2) {
+    for (int u2 = 0; u2 < kPairsN; ++u2) {
       float pv[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -795,22 +807,22 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1), each pair's V rows
     // staged in this wave's 32-row LDS tile
 #pragma unroll
-    for (int u2 = 0; u2 < kPairs; ++u2) {
+    for (int u2 = 0; u2 < kPairsN; ++u2) {
       const int32_t u0 = 2 * u2;
       if constexpr (FUSED) {
         if (wu == owner) {
 #pragma unroll
           for (int u = u0; u < u0 + 2 && u < MAXB; ++u) {
-            const int32_t kb = 16 * (w + kWinWaves * u);
+            const int32_t kb = 16 * (w + NW * u);
 #pragma unroll
             for (int j = 0; j < kVL; ++j)
               vraw[u][j] = sel4(kb + Layout<KV>::v_key(j, lane) == last, vnew, vraw[u][j]);
           }
         }
       }
-      v_to_lds<KV>(vraw[u0], vt, lane, 16 * (w + kWinWaves * u0), n);
+      v_to_lds<KV>(vraw[u0], vt, lane, 16 * (w + NW * u0), n);
       if (u0 + 1 < MAXB)
-        v_to_lds<KV>(vraw[u0 + 1 < MAXB ? u0 + 1 : u0], vt + 16 * kSVRow, lane, 16 * (w + kWinWaves * (u0 + 1)), n);
+        v_to_lds<KV>(vraw[u0 + 1 < MAXB ? u0 + 1 : u0], vt + 16 * kSVRow, lane, 16 * (w + NW * (u0 + 1)), n);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
       __builtin_amdgcn_wave_barrier();
       if (u0 + 1 < MAXB)
@@ -837,7 +849,150 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
     }
   }
   __syncthreads();
-  merge_waves_and_store<OUT_BF16>(p, kWinWaves, red_m, red_l, red_acc, b, g, 0);
+  merge_waves_and_store<OUT_BF16>(p, NW, red_m, red_l, red_acc, b, g, 0);
+}
+
+// --------------------------------------------------------------------------
+// One-wavefront window kernel (e4m3 pools, windows of at most 9 blocks, big
+// batches).  Each wavefront owns one (kv head, request) and holds its whole
+// window in flight in registers: the e4m3 rows are small enough (9 blocks x 4
+// loads) that no split over wavefronts, and so no cross-wavefront merge and no
+// duplicated accumulator, is needed.  178 registers give two wavefronts
+// per SIMD: 2048 items are resident at once, where the four-wavefront kernel
+// (whose accumulators sit in every wavefront) runs such a batch in two rounds.
+// At 256 requests x 8 kv heads (W = 128, e4m3): 22.1 -> 20.7 us per launch.  A
+// loads-only probe of the same rows takes 13.4 us (head slices) and 12.7 us
+// (whole rows), and delaying the loads of half the workgroups made the launch
+// slower, not faster: what remains is the time for the rows to arrive.
+// A workgroup holds four wavefronts, four kv heads of one request (half of an
+// e4m3 token row at 8 kv heads); with a batch of a multiple of 8 the two
+// workgroups of a request are placed on one XCD.
+// --------------------------------------------------------------------------
+constexpr int kOneWaveBlocks = 9;
+
+__device__ __forceinline__ void wave_item(int32_t kv_heads, int32_t batch, int32_t w, int32_t &g, int32_t &b) {
+  const int32_t per_req = kv_heads / 4;                        // workgroups per request (kv_heads % 4 == 0)
+  int32_t i = static_cast<int32_t>(blockIdx.x);
+  if ((batch & 7) == 0) {                                       // XCD i % 8 serves requests x, x + 8, ...
+    const int32_t x = i & 7, j = i >> 3;
+    i = (x + 8 * (j / per_req)) * per_req + j % per_req;
+  }
+  b = i / per_req;
+  g = 4 * (i % per_req) + w;
+}
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256, 2) decode_wave_kernel(DecodeParams p) {
+  using KV = uint8_t;
+  constexpr int NB = kOneWaveBlocks;
+  constexpr int kKL = Layout<KV>::kKLoads;
+  constexpr int kVL = Layout<KV>::kVLoads;
+  __shared__ __attribute__((aligned(16))) uint16_t vtiles[4 * 16 * kSVRow];
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t w = threadIdx.x >> 6;
+  const int32_t kr = lane & 15;
+  const int32_t lq = lane >> 4;
+  const int32_t G = p.group;
+  int32_t g, b;
+  wave_item(p.kv_heads, static_cast<int32_t>(gridDim.x) * 4 / p.kv_heads, w, g, b);
+
+  // slots (read speculatively at b * (W + 1), as in the window kernel) and Q
+  int32_t sl[NB];
+  int64_t spec_base = 0;
+  if (p.indptr && p.capacity > 0) {
+    spec_base = static_cast<int64_t>(b) * (p.window + 1);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int32_t key = 16 * u + kr;
+      int64_t idx = spec_base + (key < p.window ? key : p.window);
+      idx = idx < p.capacity ? idx : p.capacity - 1;
+      sl[u] = p.table[idx < 0 ? 0 : idx];
+    }
+  }
+  uint4 qraw[4];
+  load_q<KV>(p, b, g * G + (kr < G ? kr : 0), lq, qraw);
+  __builtin_amdgcn_sched_barrier(0);
+  const KeySource ks = key_source(p, b);
+  const int32_t n = ks.n < p.window + 1 ? ks.n : p.window + 1;
+  const int32_t *src = ks.src + (ks.n - n);
+  const bool spec_ok = p.indptr && p.capacity > 0 && src == p.table + spec_base;
+  if (!spec_ok) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int32_t key = 16 * u + kr;
+      sl[u] = n > 0 ? src[key < n ? key : 0] : 0;  // an empty window reads nothing from the table
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // every K row, then every V row, unconditionally (keys past n are masked)
+  uint4 kraw[NB][kKL], vraw[NB][kVL];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) load_k<KV>(p, sl[u], g, lq, kraw[u]);
+#pragma unroll
+  for (int u = 0; u < NB; ++u) load_v<KV>(p, sl[u], g, lane, vraw[u]);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8_t qop[4];
+  KvLoad<uint16_t>::to_bf16(qraw, qop);
+  // ---- S^T = K Q^T for every block, one softmax over the window
+  float sc[NB][4];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8_t kk[4];
+    KvLoad<KV>::to_bf16(kraw[u], kk);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c], qop[c], sacc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[u][r] = (16 * u + 4 * lq + r < n) ? sacc[r] * p.scale2 : -INFINITY;
+      mb = fmaxf(mb, sc[u][r]);
+    }
+  }
+  const float m_run = fmaxf(kNegBig, wave_max_q(mb));
+  float l_run = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // ---- O^T += V^T P^T block by block (16x16x16 MFMA), V through this wave's LDS tile
+  uint16_t *vt = vtiles + w * 16 * kSVRow;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    uint32_t u2[2] = {pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[u][0] - m_run), __builtin_amdgcn_exp2f(sc[u][1] - m_run)),
+                      pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[u][2] - m_run), __builtin_amdgcn_exp2f(sc[u][3] - m_run))};
+    l_run = bf16x2_acc(u2[1], bf16x2_acc(u2[0], l_run));  // the normaliser sums the rounded weights
+    i16x4_t pop;
+    __builtin_memcpy(&pop, u2, 8);
+    v_to_lds<KV>(vraw[u], vt, lane, 16 * u, n);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+    pv_single(vt, kr, lq, pop, acc);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the tile is rewritten
+  }
+  l_run = wave_sum_q(l_run);
+  // ---- sink once, normalise, store head g * G + kr
+  if (kr >= G) return;
+  const int32_t h = g * G + kr;
+  float M = m_run, L = l_run, a = 1.f;
+  if (p.sinks) {
+    const float sig2 = p.sinks[h] * kLog2e;
+    const float Mn = fmaxf(M, sig2);
+    a = __builtin_amdgcn_exp2f(M - Mn);
+    L = L * a + __builtin_amdgcn_exp2f(sig2 - Mn);
+  }
+  const float inv = L > 0.f ? a * p.v_scale / L : 0.f;
+  const int64_t off = (static_cast<int64_t>(b) * p.q_heads + h) * kD + 4 * lq;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float o0 = acc[c][0] * inv, o1 = acc[c][1] * inv, o2 = acc[c][2] * inv, o3 = acc[c][3] * inv;
+    if (OUT_BF16)
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + off + 16 * c) =
+          make_uint2(pack_bf16x2_hw(o0, o1), pack_bf16x2_hw(o2, o3));
+    else
+      *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + off + 16 * c) = make_float4(o0, o1, o2, o3);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -1080,10 +1235,23 @@ hipError_t launch_window_b(const DecodeParams &p, dim3 grid, bool out_bf16, hipS
   return hipGetLastError();
 }
 
+// Workgroups of four wavefronts that are resident at once (four per CU of the
+// 256, by their LDS); a bigger grid runs in rounds.
+constexpr int64_t kWindowResident = 1024;
+
 // Blocks per wavefront for a window of W + 1 keys over kWinWaves wavefronts.
 template <typename KV>
 hipError_t launch_window(const DecodeParams &p, dim3 grid, int window, bool out_bf16, hipStream_t stream) {
   const int blocks = (window + 1 + 15) / 16;
+  const int64_t items = static_cast<int64_t>(grid.y) * grid.z;
+  if (sizeof(KV) == 1 && !p.new_loc && items > kWindowResident && blocks <= kOneWaveBlocks && p.kv_heads % 4 == 0) {
+    const dim3 wgrid(static_cast<uint32_t>(items / 4));
+    if (out_bf16)
+      hipLaunchKernelGGL((decode_wave_kernel<true>), wgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_wave_kernel<false>), wgrid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   const int maxb = (blocks + kWinWaves - 1) / kWinWaves;
   if (maxb <= 1) return launch_window_b<KV, 1>(p, grid, out_bf16, stream);
   if (maxb == 2) return launch_window_b<KV, 2>(p, grid, out_bf16, stream);

@@ -335,6 +335,27 @@ def test_decode_long_window_planned_splits(window):
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
+@pytest.mark.parametrize("batch,sinks", [(136, True), (160, False)])
+def test_decode_e4m3_big_batch_one_wave_per_item(batch, sinks):
+    """Batches with more (request, kv head) items than the four-wavefront
+    window kernel keeps resident (1024) run e4m3 windows on one wavefront per
+    item: ragged lengths (some shorter than the window, one empty), a batch that
+    is not a multiple of 8 (plain workgroup order) and one that is (requests
+    paired on an XCD), every request against the oracle."""
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, 3000, size=batch)
+    lens[:6] = [1, 2, 16, 128, 129, 130]
+    wl = WL.decode_workload(f"e4m3_b{batch}", 800 + batch, lens, 64, 8, 128, 64, "bf16", "e4m3", sinks=sinks,
+                            with_store=True, live_margin=3)
+    say(f"decode e4m3 one wave per item: B={batch}")
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_decode(dw, "f32")
+    check(out, oracle_decode(wl), TOL["e4m3"], f"e4m3 B={batch}")
+    out_bf = run_decode(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
 def test_decode_c1_full_size():
     wl = WL.c1_decode_f32()
     say("decode c1 (1 x 512, f32)")
@@ -398,10 +419,11 @@ def test_decode_store_fused_c2_full_size():
 
 
 def test_decode_store_fused_c5_full_size():
-    """The fused store with e4m3 pools at C5's shape (B = 256): the same output
-    bits and pool bytes as swa_kv_store + swa_decode, within tolerance of the
-    oracle on sampled requests (every q head), and pool bytes equal to the
-    oracle's encoding."""
+    """The fused store with e4m3 pools at C5's shape (B = 256): the same pool
+    bytes as swa_kv_store + swa_decode and equal to the oracle's encoding; both
+    outputs within tolerance of the oracle on sampled requests (every q head).
+    (The two calls run this batch on the one-wavefront kernel, whose sums run
+    in another order than the fused kernel's, so the bits may differ.)"""
     wl = WL.c5_decode_fp8()
     say("decode+store fused c5 (256 requests, e4m3 K/V)")
     two = DeviceWorkload(wl)
@@ -409,11 +431,11 @@ def test_decode_store_fused_c5_full_size():
     want = run_decode(two, "f32")
     one = DeviceWorkload(wl)
     got = run_decode_store(one, "f32")
-    assert torch.equal(got, want)
     assert torch.equal(one.k, two.k) and torch.equal(one.v, two.v)
     reqs = [0, 7, 8, 100, 201, 255]
     ref = oracle_decode(wl, only=[(b, h) for b in reqs for h in range(wl.q_heads)])
     check(got, ref, TOL["e4m3"], "c5 fused sampled")
+    check(want, ref, TOL["e4m3"], "c5 store + decode sampled")
     pk, pv = oracle_pools_after_store(wl)
     _pool_rows_equal_oracle_store(wl, one.k, pk)
     _pool_rows_equal_oracle_store(wl, one.v, pv)
