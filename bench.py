@@ -43,6 +43,7 @@ import json
 import math
 import multiprocessing
 import os
+import re
 import sys
 import time
 
@@ -62,11 +63,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """Source text without comments and blank space, so that a sha of it changes
+    with the code only (the kernels hold no string literals with comment marks)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_sha(*names) -> str:
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sliding_window_attention_swa_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

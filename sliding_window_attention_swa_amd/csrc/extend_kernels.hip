@@ -882,9 +882,10 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
 //     wavefront owns RB row blocks, so each K / V fragment it reads from LDS
 //     feeds RB MFMAs (LDS bandwidth per flop falls as 1 / RB);
 //   * the band [first key of the first query, last query] is walked in blocks
-//     of 64 keys, double-buffered in LDS: while block j is computed the rows
+//     of 64 keys through three LDS stages: while block j is computed the rows
 //     of block j + 1 are in flight in registers and the slots of block j + 2
-//     are read; one workgroup barrier per block;
+//     are read, and the odd wavefronts still read block j - 1's V rows; one
+//     workgroup barrier per block;
 //   * online softmax in base 2 that rescales lazily: the running max of a row
 //     moves only when a block's max exceeds it by more than 8, so a row's
 //     weights stay below 2^8 (exact in bf16 up to its relative precision) and,
