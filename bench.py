@@ -56,7 +56,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 SIMDS = 1024                 # 256 CUs x 4 SIMDs
 METRIC = "SWA decode HBM GB/s & tokens/s; windowed prefill TFLOP/s (% of MI355X peak)"
-SWEEP_WINDOWS = (512, 1024, 4096)
+SWEEP_WINDOWS = (512, 1024, 4096)   # prefill window sweep on the C3 shape
+DECODE_WINDOWS = (1023, 4095)       # long-window decode on the C2 batch
 
 
 def log(msg):
@@ -249,7 +250,7 @@ def run_cpu_baselines(names, hosts):
                 step_s, sample = cpu_mixed_step(pool, nw, _HOST["c4"])
                 out[name] = cpu_baseline_entry(round(h["step_bytes"] / step_s / 1e9, 6), "GB/s", nw, sample)
                 out[name]["tokens_per_s"] = round(h["st"].batch / step_s, 4)
-            elif name in ("c1", "c2", "c5"):
+            elif name in ("c1", "c2", "c5") or name.startswith("c2w_"):
                 wl = h["wl"]
                 units, secs = cpu_decode_layer(pool, nw, name, wl)
                 out[name] = cpu_baseline_entry(round(units * h["layer_bytes"] / secs / 1e9, 6), "GB/s", nw,
@@ -357,6 +358,11 @@ def decode_host(name):
     from sliding_window_attention_swa_amd import workloads as W
     if name == "c2":
         return W.c2_decode_bf16(), 32, "batched SWA decode B=64, T~U[1K,8K], W=128, 64q/8kv, D=128, bf16, page 16"
+    if name.startswith("c2w_"):
+        w = int(name.split("_")[1])
+        return (W.c2_decode_bf16(window=w), 8,
+                f"long-window SWA decode: the B=64 batch of T~U[1K,8K] with W={w}, 64q/8kv, D=128, bf16, page 16, "
+                "split over the window's keys")
     if name == "c5":
         return (W.c5_decode_fp8(), 16,
                 "fp8 KV decode B=256, T~lognormal(16K), W=128, 64q/8kv, D=128, e4m3 K/V, bf16 q, page 64")
@@ -421,6 +427,9 @@ class DecodeBench:
                                 device="cuda")))
         self.sinks = torch.from_numpy(wl.sinks).cuda() if wl.sinks is not None else None
         self.decode_bytes, self.store_bytes, self.translate_bytes, self.fused, self.flops = decode_bytes(wl, out_dtype)
+        # windows past the one-split kernels: the library's plan (split over the window's keys)
+        self.splits, ws = swa.swa_decode_plan(B, Hq, Hkv, D, wl.window, int(wl.seq_lens.max()))
+        self.ws = torch.empty(max(ws // 4, 1), dtype=torch.float32, device="cuda") if ws > 0 else None
         self.step_bytes = self.translate_bytes + layers * (self.store_bytes + self.decode_bytes)
 
     def step(self):
@@ -440,7 +449,8 @@ class DecodeBench:
                                  ly["new_v"], sinks=self.sinks, slot_table=self.table, table_indptr=self.indptr)
         else:
             swa.swa_decode(ly["q"], ly["kv"], self.index, wl.window, ly["out"], sinks=self.sinks,
-                           slot_table=self.table, table_indptr=self.indptr)
+                           slot_table=self.table, table_indptr=self.indptr, num_splits=self.splits,
+                           workspace=self.ws)
 
     def dominant(self):
         """Back-to-back decode launches only (one per layer; with the store fused
@@ -464,10 +474,12 @@ def run_decode_gpu(args, torch, swa, name, wl, layers, desc, cpu):
         value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5), dtype={"c5": "bf16 q / e4m3 kv",
                                                                             "c1": "f32"}.get(name, "bf16"),
         config={"workload": desc, "global_batch": int(wl.batch), "layers_per_step": layers, "window": wl.window,
-                "max_seq_len": int(wl.seq_lens.max())},
+                "max_seq_len": int(wl.seq_lens.max()), "num_splits": bench.splits},
         tokens_per_s=round(wl.batch / (ms * 1e-3), 1),
         layer_tokens_per_s=round(wl.batch * layers / (ms * 1e-3), 1),
-        roofline=dict(kernel="swa_decode_store (store fused)" if bench.fused else "swa_decode", bound="hbm",
+        roofline=dict(kernel="swa_decode_store (store fused)" if bench.fused else
+                      "swa_decode (split over the window's keys: stream + merge)" if wl.window > 255 else "swa_decode",
+                      bound="hbm",
                       achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=traffic_from_profile(f"swa_decode_{name}", DECODE_SRC),
@@ -838,10 +850,12 @@ def run_evict_workload(args, torch, swa, W):
     # of calling the eviction when nothing is due (skipped in profiling runs)
     noop = None if args.skip_noop else time_replays(torch, g, 20) / bench.copies
     # algorithmic bytes of one call: per released position its req_to_token
-    # entry (4 B) and its mapping entry read and cleared (8 + 8 B); per released
-    # page one int64 report; per request req_pool_idx, pre_lens and evicted_lens
-    # read (12 B) and evicted_lens written (4 B); the count (8 B).
-    nbytes = positions * 20 + pages * 8 + eb.batch * 16 + 8
+    # entry (4 B) and its mapping entry cleared (8 B); per candidate (the range's
+    # first position and each page start: here every one reports a page) its
+    # mapping entry read (8 B) and the int64 report; per request req_pool_idx,
+    # pre_lens and evicted_lens read (12 B) and evicted_lens written (4 B); the
+    # count (8 B).
+    nbytes = positions * 12 + pages * 16 + eb.batch * 16 + 8
     value = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] evict {ms * 1e3:.2f} us per call, {positions} positions, {pages} pages; "
         f"no-op call {'-' if noop is None else f'{noop * 1e3:.2f}'} us")
@@ -966,7 +980,7 @@ def host_inputs(names):
         if n == "c4":
             st = W.c4_mixed_step()
             hosts[n] = dict(st=st, step_bytes=mixed_bytes(st)[2])
-        elif n in ("c1", "c2", "c5"):
+        elif n in ("c1", "c2", "c5") or n.startswith("c2w_"):
             wl, layers, desc = decode_host(n)
             out_dtype = "f32" if wl.q_dtype == "f32" else "bf16"
             dec, store, translate, fused, _ = decode_bytes(wl, out_dtype)
@@ -1001,13 +1015,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "c1", "c2", "c3", "c3w", "c4", "c5", "evict", "alloc", "unified"])
+                    choices=["all", "c1", "c2", "c2w", "c3", "c3w", "c4", "c5", "evict", "alloc", "unified"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-noop", action="store_true",
                     help="evict: skip timing the calls that release nothing (for profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a copy kernel of known size (counter calibration)")
-    ap.add_argument("--window", type=int, default=None, help="c3w: one window of the sweep only")
+    ap.add_argument("--window", type=int, default=None, help="c2w / c3w: one window of the sweep only")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1017,7 +1031,10 @@ def main():
     if args.copy_probe:
         names = []
     elif args.workload == "all":
-        names = ["c4", "c2", "c5", "c3"] + [f"c3w_{w}" for w in SWEEP_WINDOWS] + ["c1"]
+        names = (["c4", "c2", "c5"] + [f"c2w_{w}" for w in DECODE_WINDOWS] + ["c3"]
+                 + [f"c3w_{w}" for w in SWEEP_WINDOWS] + ["c1"])
+    elif args.workload == "c2w":
+        names = [f"c2w_{w}" for w in ((args.window,) if args.window else DECODE_WINDOWS)]
     elif args.workload == "c3w":
         names = [f"c3w_{w}" for w in ((args.window,) if args.window else SWEEP_WINDOWS)]
     elif args.workload in ("c1", "c2", "c3", "c4", "c5"):
@@ -1047,7 +1064,7 @@ def main():
         h = hosts[n]
         if n == "c4":
             results[n] = run_mixed_gpu(args, torch, swa, h["st"], cpu.get(n))
-        elif n in ("c1", "c2", "c5"):
+        elif n in ("c1", "c2", "c5") or n.startswith("c2w_"):
             results[n] = run_decode_gpu(args, torch, swa, n, h["wl"], h["layers"], h["desc"], cpu.get(n))
         else:
             results[n] = run_extend_gpu(args, torch, swa, n, h["wl"], cpu.get(n))

@@ -159,8 +159,9 @@ __global__ void __launch_bounds__(kThreads) evict_scan_kernel(EvictParams p) {
 
 // Apply: one workgroup per (request, chunk).  Three memory phases: the
 // independent per-block values (range, chunk base, request row, the earlier
-// requests' counts), then the chunk's req_to_token entries, then their mapping
-// entries; one barrier ranks the reports and sums the counts together.
+// requests' counts), then the chunk's req_to_token entries, then the mapping
+// entries of its candidates; one barrier ranks the reports and sums the counts
+// together.
 __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
   __shared__ int32_t cnt[kApplyPerThread * 4];
   __shared__ int64_t red[4];
@@ -193,18 +194,22 @@ __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
     const int64_t j0 = c_lo + ps * kPass;
     int32_t full[kApplyPerThread];
     int64_t slot[kApplyPerThread];
-    bool flag[kApplyPerThread];
+    bool flag[kApplyPerThread], clear[kApplyPerThread];
 #pragma unroll
     for (int i = 0; i < kApplyPerThread; ++i) {
       const int64_t j = j0 + i * kThreads + threadIdx.x;
       full[i] = (rows_ok && j < c_hi) ? p.r2t[row * p.r2t_stride + j] : -1;
     }
+    // Only a candidate's mapping value is read (it may report its page); every
+    // other position's entry is cleared without being read: a value that is
+    // already 0 stays 0 and reports nothing either way.  Full slot 0 (padding)
+    // and the trailing sentinel are never written.
 #pragma unroll
     for (int i = 0; i < kApplyPerThread; ++i) {
-      const bool ok = full[i] >= 0 && full[i] < p.map_len - 1;
-      slot[i] = ok ? p.map[full[i]] : 0;
       const int64_t j = j0 + i * kThreads + threadIdx.x;
-      flag[i] = slot[i] > 0 && (j == lo || j % p.page == 0);
+      clear[i] = full[i] > 0 && full[i] < p.map_len - 1;
+      slot[i] = clear[i] && (j == lo || j % p.page == 0) ? p.map[full[i]] : 0;
+      flag[i] = slot[i] > 0;
     }
     // ranks of the reports in position order, and (first pass) the counts' sum,
     // behind one barrier
@@ -239,7 +244,7 @@ __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
         const int64_t at = out + r + __popcll(mask[i] & ((1ull << lane) - 1ull));
         if (at < p.capacity) p.freed_pages[at] = slot[i] / p.page;
       }
-      if (slot[i] > 0) p.map[full[i]] = 0;
+      if (clear[i]) p.map[full[i]] = 0;
     }
     run += acc;
     if (ps + 1 < n_pass) __syncthreads();  // cnt is reused by the next pass

@@ -281,11 +281,14 @@ def c1_decode_f32(seed=SEED_BASE + 1) -> Workload:
                            slack_pages=512, swa_tokens=512)
 
 
-def c2_decode_bf16(seed=SEED_BASE + 2, batch=64, q_heads=64, kv_heads=8) -> Workload:
+def c2_decode_bf16(seed=SEED_BASE + 2, batch=64, q_heads=64, kv_heads=8, window=128) -> Workload:
     """Batched SWA decode: B = 64, T ~ U[1024, 8192], W = 128, 64 q / 8 kv heads,
-    D = 128, bf16, P = 16, out-of-window pages tombstoned, ratio 0.8."""
+    D = 128, bf16, P = 16, out-of-window pages tombstoned, ratio 0.8.  Other
+    windows give the same batch with a longer window (1023 and 4095 keys: the
+    long-window layers, split over their keys)."""
     lens = np.random.default_rng(np.random.SeedSequence(seed).spawn(8)[0]).integers(1024, 8193, size=batch)
-    return decode_workload("c2_decode_bf16_B64", seed, lens, q_heads, kv_heads, 128, 16, "bf16", "bf16", ratio=0.8,
+    name = "c2_decode_bf16_B64" + ("" if window == 128 else f"_W{window}")
+    return decode_workload(name, seed, lens, q_heads, kv_heads, window, 16, "bf16", "bf16", ratio=0.8,
                            with_store=True)
 
 
