@@ -895,6 +895,11 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
 //     band, so they meet in one L2.
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;                                  // keys per band block
+// The A operand of all ones (bf16 1.0): an MFMA of it with a block's packed
+// weights P^T gives each query's sum of those weights in every output row, so
+// the normaliser is summed on the matrix cores from exactly the weights that
+// enter P.V, and the VALU (the busier pipe here) does not add them.
+constexpr bf16x8_t kOnes = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
 constexpr int kBandStage = kBK * (kKRow + kVRow);        // elements of one LDS stage (K rows, then V rows)
 constexpr int32_t kBandMinWindow = 256;                  // windows at least this long use the band kernel
 constexpr float kRescaleSlack = 8.f;                     // log2 of the largest weight before a rescale
@@ -956,7 +961,7 @@ struct BandStage {
 template <int RB, int NW, bool PRECISE>
 __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx &c, uint16_t *lds,
                                             const bf16x8_t (&qop)[RB][4], const int32_t (&q_of)[RB],
-                                            f32x4_t (&acc)[RB][8], float (&m_run)[RB], float (&l_run)[RB]) {
+                                            f32x4_t (&acc)[RB][8], float (&m_run)[RB], f32x4_t (&l_acc)[RB]) {
   constexpr int kPasses = BandStage<NW>::kPasses;
   constexpr int kRowsPerPass = BandStage<NW>::kRowsPerPass;
   const int32_t lane = threadIdx.x & 63;
@@ -967,31 +972,61 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
   const int32_t W = p.window;
   const bool lag = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) != 0;  // wave-uniform
 
-  // slots of block j for this thread's rows (rows past the band read slot 0 and are zeroed)
+  // Slots of block j for this thread's rows.  Band key k (position kj0 + k) is
+  // entry k - lo of sbase when lo <= k < lo + span; every other row (past the
+  // band, or outside the key source) loads the first entry instead, an
+  // unconditional in-bounds read, and its row is zeroed or masked later.  A
+  // band with no source entry at all reads nothing and takes slot 0.
+  const int64_t rel0 = static_cast<int64_t>(c.kj0) - c.ks.pos_base;  // source index of band key 0
+  const int64_t lo64 = rel0 < 0 ? -rel0 : 0;
+  const int64_t hi64 = c.ks.hi - rel0 < c.nkeys ? c.ks.hi - rel0 : c.nkeys;
+  const bool has_src = hi64 > lo64;  // workgroup-uniform
+  const int32_t lo = static_cast<int32_t>(lo64);
+  const uint32_t span = has_src ? static_cast<uint32_t>(hi64 - lo64) : 0u;
+  const int32_t *sbase = has_src ? c.ks.src + (rel0 + lo64) : c.ks.src;
   auto block_slots = [&](int32_t j, int32_t (&sl)[kPasses]) {
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-      const int32_t k = kBK * j + srow + kRowsPerPass * ps;
-      sl[ps] = (j < c.nblk && k < c.nkeys) ? slot_at(c.ks, static_cast<int64_t>(c.kj0) + k) : 0;
+      const int32_t k = kBK * j + srow + kRowsPerPass * ps - lo;
+      sl[ps] = has_src ? sbase[static_cast<uint32_t>(k) < span ? k : 0] : 0;
     }
   };
+  // This thread's 16 bytes of kv head c.g in a token row: row s starts s *
+  // row_elems elements past the head's base (one 32 x 32 -> 64-bit multiply-add
+  // per slot; a slot outside the pool reads row 0).
+  const uint16_t *kbase = p.k + c.g * kD + 8 * spiece;
+  const uint16_t *vbase = p.v + c.g * kD + 8 * spiece;
+  const uint32_t row_elems = static_cast<uint32_t>(p.kv_heads) * kD;
+  // every int32 slot in [0, rows) is below this bound and every negative one is not
+  const uint32_t nrows = p.rows < (int64_t(1) << 31) ? static_cast<uint32_t>(p.rows) : 0x80000000u;
   auto block_fetch = [&](const int32_t (&sl)[kPasses], uint4 (&kv)[kPasses], uint4 (&vv)[kPasses]) {
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-      const int64_t s = (sl[ps] < 0 || sl[ps] >= p.rows) ? 0 : static_cast<int64_t>(sl[ps]);
-      const int64_t off = row_elem(s, p.kv_heads, c.g, kD) + 8 * spiece;
-      kv[ps] = *reinterpret_cast<const uint4 *>(p.k + off);
-      vv[ps] = *reinterpret_cast<const uint4 *>(p.v + off);
+      const uint32_t su = static_cast<uint32_t>(sl[ps]);
+      const uint64_t off = static_cast<uint64_t>(su < nrows ? su : 0u) * row_elems;
+      kv[ps] = *reinterpret_cast<const uint4 *>(kbase + off);
+      vv[ps] = *reinterpret_cast<const uint4 *>(vbase + off);
     }
   };
+  // Rows past the band (only in a tile's last block) hold slot 0's row and are
+  // written as zeros; every other block is written as loaded.
   auto block_put = [&](int32_t j, uint16_t *stage, const uint4 (&kv)[kPasses], const uint4 (&vv)[kPasses]) {
+    if (kBK * (j + 1) <= c.nkeys) {  // workgroup-uniform
 #pragma unroll
-    for (int ps = 0; ps < kPasses; ++ps) {
-      const int32_t row = srow + kRowsPerPass * ps;
-      const bool ok = kBK * j + row < c.nkeys;
-      *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = ok ? kv[ps] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) =
-          ok ? vv[ps] : make_uint4(0, 0, 0, 0);
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const int32_t row = srow + kRowsPerPass * ps;
+        *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = kv[ps];
+        *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) = vv[ps];
+      }
+    } else {
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const int32_t row = srow + kRowsPerPass * ps;
+        const bool ok = kBK * j + row < c.nkeys;
+        *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = ok ? kv[ps] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) =
+            ok ? vv[ps] : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
@@ -1087,7 +1122,7 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
         const float m_new = fmaxf(m_run[i], mx[i]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
         m_run[i] = m_new;
-        l_run[i] *= alpha;
+        l_acc[i] *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[i][n] *= alpha;
       }
@@ -1103,8 +1138,8 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
         const f32x4_t &e0 = s[i][2 * u], &e1 = s[i][2 * u + 1];
         const uint32_t u4[4] = {pack_bf16x2_hw(e0[0], e0[1]), pack_bf16x2_hw(e0[2], e0[3]),
                                 pack_bf16x2_hw(e1[0], e1[1]), pack_bf16x2_hw(e1[2], e1[3])};
-        l_run[i] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[i]))));
         __builtin_memcpy(&pop[i][u], u4, 16);
+        l_acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pop[i][u], l_acc[i], 0, 0, 0);
         if constexpr (PRECISE) {
           const float ev[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
           uint32_t r4[4];
@@ -1113,8 +1148,8 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
             const float h0 = __uint_as_float(u4[k] << 16), h1 = __uint_as_float(u4[k] & 0xFFFF0000u);
             r4[k] = pack_bf16x2_hw(ev[2 * k] - h0, ev[2 * k + 1] - h1);
           }
-          l_run[i] = bf16x2_acc(r4[3], bf16x2_acc(r4[2], bf16x2_acc(r4[1], bf16x2_acc(r4[0], l_run[i]))));
           __builtin_memcpy(&plo[i][u], r4, 16);
+          l_acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, plo[i][u], l_acc[i], 0, 0, 0);
         }
       }
     }
@@ -1195,24 +1230,28 @@ __global__ void __launch_bounds__(NW * 64, WGS) band_kernel(ExtendParams p) {
     for (int i = 0; i < RB; ++i)
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[RB], l_run[RB];
+    float m_run[RB];
+    f32x4_t l_acc[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       m_run[i] = kNegBig;
-      l_run[i] = 0.f;
+      l_acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     if (c.nblk > 0) {
       // queries at positions below kPreciseBelow see fewer keys than that (W >= 256)
       if (c.i0 < kPreciseBelow)
-        band_blocks<RB, NW, true>(p, c, lds, qop, q_of, acc, m_run, l_run);
+        band_blocks<RB, NW, true>(p, c, lds, qop, q_of, acc, m_run, l_acc);
       else
-        band_blocks<RB, NW, false>(p, c, lds, qop, q_of, acc, m_run, l_run);
+        band_blocks<RB, NW, false>(p, c, lds, qop, q_of, acc, m_run, l_acc);
     }
     // ---- sink once, normalise, store the valid query rows
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       typename HeadOut<OUT_BF16>::type o;
-      finish_head<OUT_BF16>(p, acc[i], m_run[i], l_run[i], sink2[i], o);
+      // every lane of query kr holds the whole row sum: a quarter from each of the
+      // four lanes that finish_head adds (exact: scaling by 1/4 and adding four
+      // equal values round nothing)
+      finish_head<OUT_BF16>(p, acc[i], m_run[i], 0.25f * l_acc[i][0], sink2[i], o);
       const int32_t qi = qi0[i] + kr;
       if (qi < qrows.n) write_head<OUT_BF16>(p, o, bt.hq0 + hh[i], qrows.qo0 + qi);
     }
