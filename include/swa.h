@@ -407,7 +407,7 @@ swa_status_t swa_ring_locs(const swa_index_t *idx, int64_t ring_rows, const int3
  *   pre_lens, evicted_lens, protected_lens  device int32 [batch]
  *                (evicted_lens read and updated in place).
  *   workspace    device, swa_evict_workspace_bytes(batch, r2t_stride, page)
- *                bytes, 4-aligned; overwritten.
+ *                bytes, 8-aligned; overwritten.
  * Ranges of different requests must not share full slots (a shared prefix is
  * protected).  Positions or slots outside their tables release nothing.
  * Errors: SWA_E_ARG (null or inconsistent arguments, window < 0, mode not 0/1,

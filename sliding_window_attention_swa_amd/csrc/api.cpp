@@ -688,8 +688,8 @@ swa_status_t swa_alloc_decode(int32_t batch, int32_t page_size, const int32_t *s
 
 size_t swa_evict_workspace_bytes(int32_t batch, int64_t r2t_stride, int32_t page_size) {
   if (batch <= 0 || r2t_stride < 1 || page_size < 1) return 0;
-  return static_cast<size_t>(batch) * static_cast<size_t>(3 + swa::evict_chunks(r2t_stride, page_size)) *
-         sizeof(int32_t);
+  return static_cast<size_t>(swa::evict_cand_offset(batch, r2t_stride, page_size)) +
+         static_cast<size_t>(batch) * static_cast<size_t>(swa::evict_cands(r2t_stride, page_size)) * sizeof(int64_t);
 }
 
 swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32_t *pre_lens,
@@ -707,7 +707,7 @@ swa_status_t swa_evict(const swa_index_t *idx, int64_t *full_to_swa, const int32
   if (idx->batch > 0 && swa::evict_chunks(idx->r2t_stride, idx->page_size) > 65535) return SWA_E_SHAPE;
   if (idx->batch > 0 &&
       (!workspace || workspace_bytes < swa_evict_workspace_bytes(idx->batch, idx->r2t_stride, idx->page_size) ||
-       (reinterpret_cast<uintptr_t>(workspace) & 3u)))
+       (reinterpret_cast<uintptr_t>(workspace) & 7u)))
     return SWA_E_WORKSPACE;
   return from_hip(swa::launch_evict(*idx, full_to_swa, pre_lens, protected_lens, evicted_lens, window, mode,
                                     interval, freed_pages, freed_capacity, freed_count,

@@ -179,7 +179,16 @@ __host__ __device__ inline int64_t evict_chunks(int64_t r2t_stride, int32_t page
   return (r2t_stride + c - 1) / c;
 }
 
-// workspace: int32 [batch] counts, [batch][2] ranges, [batch][evict_chunks] bases
+// Candidates of one request's range (its first position and each page start in
+// it): at most this many for a req_to_token row of r2t_stride positions.
+__host__ __device__ inline int64_t evict_cands(int64_t r2t_stride, int32_t page) { return r2t_stride / page + 2; }
+// Byte offset of the candidates' mapping values in the workspace (8-aligned).
+__host__ __device__ inline int64_t evict_cand_offset(int32_t batch, int64_t r2t_stride, int32_t page) {
+  return (static_cast<int64_t>(batch) * (3 + evict_chunks(r2t_stride, page)) * 4 + 7) / 8 * 8;
+}
+
+// workspace: int32 [batch] counts, [batch][2] ranges, [batch][evict_chunks] bases,
+// then (8-aligned) int64 [batch][evict_cands] the candidates' mapping values
 hipError_t launch_evict(const swa_index_t &idx, int64_t *full_to_swa, const int32_t *pre_lens,
                         const int32_t *protected_lens, int32_t *evicted_lens, int32_t window, int32_t radix,
                         int32_t interval, int64_t *freed_pages, int64_t capacity, int64_t *freed_count,

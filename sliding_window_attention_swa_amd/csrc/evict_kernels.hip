@@ -13,9 +13,9 @@
 // position, or a position that starts a page), so the report order is fixed by
 // those candidates alone.  Two launches:
 //   scan:  one workgroup per request walks its candidates (about 1/page of the
-//          range), counts the reports, records for every chunk of the range the
-//          number of reports before it, stores the range and advances the
-//          evicted length;
+//          range), keeps each candidate's mapping value for the apply, counts
+//          the reports, records for every chunk of the range the number of
+//          reports before it, stores the range and advances the evicted length;
 //   apply: one workgroup per (request, chunk of about 2048 positions) clears
 //          the chunk's mapping entries and writes its reports at
 //          (reports of earlier requests) + (reports of earlier chunks) + rank.
@@ -54,7 +54,16 @@ struct EvictParams {
   int32_t *counts;  // [batch] reports per request
   int32_t *range;   // [batch][2] lo, hi (hi <= lo: nothing released)
   int32_t *base;    // [batch][nchunk] reports of the request before each chunk
+  int64_t *cand;    // [batch][ncand] each candidate's mapping value (0: reports nothing)
+  int64_t ncand;    // candidates per request row at most
+  int32_t page_shift;  // log2(page) for a power-of-two page, else -1
 };
+
+// Page of position j (positions are below 2^31, as the int32 lengths and
+// ranges already require).
+__device__ __forceinline__ uint32_t page_of(const EvictParams &p, uint32_t j) {
+  return p.page_shift >= 0 ? j >> p.page_shift : j / static_cast<uint32_t>(p.page);
+}
 
 // The range [lo, hi) request b releases; hi is the new evicted length when the
 // range is not empty.  Positions at or beyond the row length are never read.
@@ -135,14 +144,19 @@ __global__ void __launch_bounds__(kThreads) evict_scan_kernel(EvictParams p) {
       if (c < n_cand) load_position(p, row, j[i], full, slot[i]);
       flag[i] = slot[i] > 0;
     }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {  // the apply reads these instead of the mapping
+      const int64_t c = c0 + i * kThreads + threadIdx.x;
+      if (c < n_cand) p.cand[static_cast<int64_t>(b) * p.ncand + c] = slot[i];
+    }
     int32_t rank[kPerThread], n;
     block_ranks(flag, rank, n, cnt);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int64_t c = c0 + i * kThreads + threadIdx.x;
       // the chunk's first candidate records the reports before the chunk
-      if (c < n_cand && (c == 0 || j[i] % p.chunk == 0)) {
-        const int64_t k = j[i] / p.chunk;
+      const uint32_t ju = static_cast<uint32_t>(j[i]), k = ju / static_cast<uint32_t>(p.chunk);
+      if (c < n_cand && (c == 0 || k * static_cast<uint32_t>(p.chunk) == ju)) {
         if (k < p.nchunk) p.base[static_cast<int64_t>(b) * p.nchunk + k] = run + rank[i];
       }
     }
@@ -157,11 +171,11 @@ __global__ void __launch_bounds__(kThreads) evict_scan_kernel(EvictParams p) {
   }
 }
 
-// Apply: one workgroup per (request, chunk).  Three memory phases: the
+// Apply: one workgroup per (request, chunk).  Two memory phases: the
 // independent per-block values (range, chunk base, request row, the earlier
-// requests' counts), then the chunk's req_to_token entries, then the mapping
-// entries of its candidates; one barrier ranks the reports and sums the counts
-// together.
+// requests' counts), then the chunk's req_to_token entries together with its
+// candidates' mapping values as the scan read them; one barrier ranks the
+// reports and sums the counts together.  The mapping itself is only written.
 __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
   __shared__ int32_t cnt[kApplyPerThread * 4];
   __shared__ int64_t red[4];
@@ -188,6 +202,8 @@ __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
   // block (0, 0) makes one pass even with nothing of its own, to write the total
   const int64_t n_pass = live ? (c_hi - c_lo + kPass - 1) / kPass : 1;
   const bool rows_ok = row >= 0 && row < p.r2t_rows;
+  const uint32_t lo_page = page_of(p, static_cast<uint32_t>(lo));
+  const int64_t *cand = p.cand + static_cast<int64_t>(b) * p.ncand;
 
   int64_t run = 0;
   for (int64_t ps = 0; ps < n_pass; ++ps) {  // workgroup-uniform trip count
@@ -200,15 +216,22 @@ __global__ void __launch_bounds__(kThreads) evict_apply_kernel(EvictParams p) {
       const int64_t j = j0 + i * kThreads + threadIdx.x;
       full[i] = (rows_ok && j < c_hi) ? p.r2t[row * p.r2t_stride + j] : -1;
     }
-    // Only a candidate's mapping value is read (it may report its page); every
-    // other position's entry is cleared without being read: a value that is
+    // A candidate's mapping value comes from the scan: candidate 0 is lo, then
+    // one per page start, so a page start's candidate is its page minus lo's.
+    // Every position's entry is cleared without being read: a value that is
     // already 0 stays 0 and reports nothing either way.  Full slot 0 (padding)
     // and the trailing sentinel are never written.
 #pragma unroll
     for (int i = 0; i < kApplyPerThread; ++i) {
       const int64_t j = j0 + i * kThreads + threadIdx.x;
+      const uint32_t ju = static_cast<uint32_t>(j);
+      const uint32_t pj = page_of(p, ju);
+      const bool is_cand = j < c_hi && (j == lo || pj * static_cast<uint32_t>(p.page) == ju);
+      slot[i] = is_cand ? cand[pj - lo_page] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kApplyPerThread; ++i) {
       clear[i] = full[i] > 0 && full[i] < p.map_len - 1;
-      slot[i] = clear[i] && (j == lo || j % p.page == 0) ? p.map[full[i]] : 0;
       flag[i] = slot[i] > 0;
     }
     // ranks of the reports in position order, and (first pass) the counts' sum,
@@ -286,6 +309,10 @@ hipError_t launch_evict(const swa_index_t &idx, int64_t *full_to_swa, const int3
   p.counts = workspace;
   p.range = workspace + idx.batch;
   p.base = workspace + 3 * static_cast<int64_t>(idx.batch);
+  p.ncand = evict_cands(idx.r2t_stride, idx.page_size);
+  p.page_shift = (idx.page_size & (idx.page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(idx.page_size)) : -1;
+  p.cand = reinterpret_cast<int64_t *>(reinterpret_cast<char *>(workspace) +
+                                       evict_cand_offset(idx.batch, idx.r2t_stride, idx.page_size));
   hipLaunchKernelGGL(evict_scan_kernel, dim3(static_cast<uint32_t>(idx.batch)), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

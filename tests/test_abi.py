@@ -250,10 +250,11 @@ def test_decode_store_argument_errors(swa):
 def test_evict_argument_errors(swa):
     lib, E = swa.lib, swa
     ix = index(swa)
-    # int32 counts, ranges (2) and one base per chunk of >= 2048 positions starting at page boundaries
-    assert lib.swa_evict_workspace_bytes(5, 4096, 16) == 5 * (3 + 2) * 4
-    assert lib.swa_evict_workspace_bytes(2, 100, 3) == 2 * (3 + 1) * 4      # chunk 2049
-    assert lib.swa_evict_workspace_bytes(1, 4097, 4096) == 1 * (3 + 2) * 4  # chunk 4096
+    # int32 counts, ranges (2) and one base per chunk of >= 2048 positions starting at page boundaries,
+    # rounded up to 8 bytes, then one int64 per candidate: stride // page + 2 per request
+    assert lib.swa_evict_workspace_bytes(5, 4096, 16) == 104 + 5 * (4096 // 16 + 2) * 8   # 100 -> 104
+    assert lib.swa_evict_workspace_bytes(2, 100, 3) == 32 + 2 * (100 // 3 + 2) * 8       # chunk 2049
+    assert lib.swa_evict_workspace_bytes(1, 4097, 4096) == 24 + 1 * (4097 // 4096 + 2) * 8  # chunk 4096; 20 -> 24
     assert lib.swa_evict_workspace_bytes(0, 4096, 16) == 0
     need = lib.swa_evict_workspace_bytes(2, 100, 16)
 
@@ -273,6 +274,7 @@ def test_evict_argument_errors(swa):
     assert ev(pages=None) == E.SWA_E_ARG                # a capacity with no buffer
     assert ev(ws=None) == E.SWA_E_WORKSPACE
     assert ev(ws_bytes=need - 4) == E.SWA_E_WORKSPACE
+    assert ev(ws=FAKE + 4) == E.SWA_E_WORKSPACE  # int64 values need 8-byte alignment
     assert ev(ws=FAKE + 2) == E.SWA_E_WORKSPACE         # misaligned
     short_map = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, None, 1, 2, 16)
     assert ev(ix=short_map) == E.SWA_E_ARG              # a mapping needs its sentinel entry
