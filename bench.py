@@ -996,6 +996,63 @@ def host_inputs(names):
     return hosts
 
 
+def measure_probes(torch, swa):
+    """The practical ceilings next to the published peaks (include/swa_probe.h):
+    one streaming read of 2 GiB with 16-byte loads (best over grids of 1,024 to
+    4,096 workgroups) and a loop of nothing but bf16 MFMAs (two, four or eight
+    wavefronts per SIMD), each the best of five timed launches."""
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return min(ms)
+
+    nbytes = 2 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    read = {}
+    for grid in (1024, 2048, 4096):
+        out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        read[grid] = nbytes / (best_ms(lambda: swa.swa_probe_read(buf, out, grid)) * 1e-3) / 1e9
+    del buf, out
+    mfma, iters = {}, 4096
+    for grid in (512, 1024, 2048):
+        out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        flops = grid * 4 * iters * 8 * 16384
+        mfma[grid] = flops / (best_ms(lambda: swa.swa_probe_mfma(out, grid, iters)) * 1e-3) / 1e12
+    torch.cuda.empty_cache()
+    g_read, g_mfma = max(read, key=read.get), max(mfma, key=mfma.get)
+    log(f"[bench] probes: read {read[g_read]:.1f} GB/s (grid {g_read}), bf16 MFMA {mfma[g_mfma]:.1f} TFLOP/s "
+        f"(grid {g_mfma})")
+    return dict(hbm_read_gbs=round(read[g_read], 1), hbm_read_frac_of_peak=round(read[g_read] / HBM_PEAK_GBS, 4),
+                mfma_bf16_tflops=round(mfma[g_mfma], 1),
+                mfma_frac_of_peak=round(mfma[g_mfma] / BF16_PEAK_TFLOPS, 4),
+                read="swa_probe_read: one pass over 2 GiB, 16-byte loads, grid-stride",
+                mfma="swa_probe_mfma: 8 independent v_mfma_f32_16x16x32_bf16 chains per wavefront")
+
+
+def against_probes(res, probes):
+    """Each roofline also as a fraction of the probe that bounds it."""
+    roof = res.get("roofline")
+    if not roof or not probes:
+        return
+    if roof.get("unit") == "GB/s":
+        roof["frac_of_probe"] = round(roof["achieved"] / probes["hbm_read_gbs"], 4)
+    elif roof.get("unit") == "TFLOP/s":
+        roof["frac_of_probe"] = round(roof["achieved"] / probes["mfma_bf16_tflops"], 4)
+    if "tflops" in roof and roof.get("achieved_gbs"):  # an extend: the attainable roofline of the probes
+        intensity = roof["tflops"] * 1e3 / roof["achieved_gbs"]  # FLOP per byte
+        att = min(probes["mfma_bf16_tflops"], intensity * probes["hbm_read_gbs"] / 1e3)
+        roof["attainable_tflops_of_probes"] = round(att, 1)
+        roof["frac_of_attainable_of_probes"] = round(roof["tflops"] / att, 4)
+
+
 def contract_line(args, res, name):
     """The one JSON line of the benchmark contract around a workload result."""
     line = dict(metric=METRIC, value=res["value"], unit=res["unit"], n_gpus=1, steps=res.get("steps", args.steps),
@@ -1054,9 +1111,14 @@ def main():
     if args.copy_probe:
         print(json.dumps(copy_probe(torch)), flush=True)
         return
+    probes = measure_probes(torch, swa)
     if args.workload in ("evict", "alloc", "unified"):
         fn = {"evict": run_evict_workload, "alloc": run_alloc_workload, "unified": run_unified_workload}
-        print(json.dumps(contract_line(args, fn[args.workload](args, torch, swa, W), args.workload)), flush=True)
+        res = fn[args.workload](args, torch, swa, W)
+        against_probes(res, probes)
+        line = contract_line(args, res, args.workload)
+        line["probes"] = probes
+        print(json.dumps(line), flush=True)
         return
 
     results = {}
@@ -1068,8 +1130,11 @@ def main():
             results[n] = run_decode_gpu(args, torch, swa, n, h["wl"], h["layers"], h["desc"], cpu.get(n))
         else:
             results[n] = run_extend_gpu(args, torch, swa, n, h["wl"], cpu.get(n))
+    for r in results.values():
+        against_probes(r, probes)
     head = names[0]
     line = contract_line(args, results[head], head)
+    line["probes"] = probes
     if len(names) > 1:
         line["sub_results"] = {n: results[n] for n in names[1:]}
     print(json.dumps(line), flush=True)

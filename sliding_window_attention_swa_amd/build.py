@@ -34,7 +34,11 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["api.cpp", "index_kernels.hip", "store_kernels.hip", "decode_kernels.hip", "extend_kernels.hip",
-           "validate_kernels.hip", "evict_kernels.hip", "alloc_kernels.hip"]
+           "validate_kernels.hip", "evict_kernels.hip", "alloc_kernels.hip", "probe_kernels.hip"]
+# Per-source extra flags.  The MFMA probe's accumulators stay in VGPRs: in the
+# AGPR form the compiler rotates the loop-carried accumulators through
+# v_accvgpr moves every iteration, and the probe would time those moves.
+EXTRA = {"probe_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -48,7 +52,7 @@ def _compile(src: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *lang, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *lang, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                      if "packed-fp32-ops" not in line)  # host pass does not know the GPU feature

@@ -24,14 +24,16 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so"
 SWA_OK, SWA_E_ARG, SWA_E_DTYPE, SWA_E_SHAPE, SWA_E_NOSPACE, SWA_E_WORKSPACE, SWA_E_HIP = 0, -1, -2, -3, -4, -5, -6
 SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 
-# every symbol include/swa.h declares
+# every symbol include/swa.h and include/swa_probe.h declare
 EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_kv_store", "swa_decode_plan",
            "swa_decode", "swa_decode_store", "swa_extend", "swa_validate_workspace_bytes", "swa_validate",
            "swa_evict_workspace_bytes", "swa_evict", "swa_alloc_pages_needed", "swa_alloc_extend",
            "swa_alloc_decode", "swa_unified_pool_bytes", "swa_unified_layer_views", "swa_translate_kernel_ids",
            "swa_translate_window_unified", "swa_translate_window_chunked", "swa_extend_chunked",
            "swa_translate_window_ring", "swa_ring_locs", "swa_decode_workspace_bytes", "swa_decode_step",
-           "swa_decode_step_workspace_bytes", "swa_decode_noalloc", "swa_status_string")
+           "swa_decode_step_workspace_bytes", "swa_decode_noalloc", "swa_status_string",
+           # include/swa_probe.h: measurement probes for the benchmark
+           "swa_probe_read", "swa_probe_mfma")
 
 
 class SwaError(RuntimeError):
@@ -131,6 +133,8 @@ _sig = {
     "swa_decode_step": (_i32, [ctypes.POINTER(DecodeStepStruct), ctypes.POINTER(IndexStruct), _i64, _p, _p, _i64, _p,
                                _sz, _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
+    "swa_probe_read": (_i32, [_p, _sz, _p, _i32, _p]),
+    "swa_probe_mfma": (_i32, [_p, _i32, _i32, _p]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(lib, _name)
@@ -625,3 +629,18 @@ def swa_ring_locs(req_pool_idx: torch.Tensor, seq_lens: torch.Tensor, request_sl
     ix = _ring_index(req_pool_idx, seq_lens, request_slots, 1)
     _check(lib.swa_ring_locs(ctypes.byref(ix), ring_rows, _ptr(prefix_lens, torch.int32, "prefix_lens"),
                              _ptr(out, torch.int64, "out"), out.numel(), _stream(stream)), "swa_ring_locs")
+
+
+def swa_probe_read(buf: torch.Tensor, out: torch.Tensor, grid: int, stream=None):
+    """One streaming read of `buf` (16-aligned, a multiple of 16 bytes); out holds grid * 256 floats."""
+    if out.numel() < grid * 256:
+        raise ValueError("out needs grid * 256 floats")
+    _check(lib.swa_probe_read(_ptr(buf, name="buf"), buf.numel() * buf.element_size(),
+                              _ptr(out, torch.float32, "out"), grid, _stream(stream)), "swa_probe_read")
+
+
+def swa_probe_mfma(out: torch.Tensor, grid: int, iters: int, stream=None):
+    """grid * 4 * iters * 8 bf16 MFMAs of 16,384 FLOPs; out holds grid * 256 floats."""
+    if out.numel() < grid * 256:
+        raise ValueError("out needs grid * 256 floats")
+    _check(lib.swa_probe_mfma(_ptr(out, torch.float32, "out"), grid, iters, _stream(stream)), "swa_probe_mfma")

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "swa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("swa.h", "swa_probe.h")]
 
 
 @pytest.fixture(scope="module")
@@ -19,16 +19,22 @@ def swa():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_header_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(os.path.basename(h) for h in HEADERS)
 
 
 def test_header_symbols_exported(swa):
     names = declared_functions()
     assert len(names) >= 8
     for n in names:
-        assert hasattr(swa.lib, n), f"{n} declared in swa.h but not exported"
+        assert hasattr(swa.lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(swa.EXPORTS)
 
 
@@ -495,3 +501,17 @@ def test_decode_noalloc_host_checks(swa):
     big = swa.IndexStruct(FAKE, 3, 100, FAKE, FAKE, None, 0, 1024, 16)
     assert nd(ix=big, splits=8) == E.SWA_E_WORKSPACE       # 1024 x 64 x 8 partials
     assert nd(ix=index(swa, batch=0, map_ptr=None)) == E.SWA_OK   # empty batch: nothing launched
+
+
+def test_probe_argument_errors(swa):
+    lib, E = swa.lib, swa
+    assert lib.swa_probe_read(None, 1024, FAKE, 8, None) == E.SWA_E_ARG
+    assert lib.swa_probe_read(FAKE, 1024, None, 8, None) == E.SWA_E_ARG
+    assert lib.swa_probe_read(FAKE, 0, FAKE, 8, None) == E.SWA_E_ARG
+    assert lib.swa_probe_read(FAKE, 1000, FAKE, 8, None) == E.SWA_E_ARG       # not a multiple of 16
+    assert lib.swa_probe_read(FAKE + 8, 1024, FAKE, 8, None) == E.SWA_E_ARG   # not 16-aligned
+    assert lib.swa_probe_read(FAKE, 1024, FAKE, 0, None) == E.SWA_E_ARG
+    assert lib.swa_probe_read(FAKE, 1024, FAKE, 65536, None) == E.SWA_E_ARG
+    assert lib.swa_probe_mfma(None, 8, 1, None) == E.SWA_E_ARG
+    assert lib.swa_probe_mfma(FAKE, 0, 1, None) == E.SWA_E_ARG
+    assert lib.swa_probe_mfma(FAKE, 8, 0, None) == E.SWA_E_ARG
