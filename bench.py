@@ -998,9 +998,10 @@ def host_inputs(names):
 
 def measure_probes(torch, swa):
     """The practical ceilings next to the published peaks (include/swa_probe.h):
-    one streaming read of 2 GiB with 16-byte loads (best over grids of 1,024 to
-    4,096 workgroups) and a loop of nothing but bf16 MFMAs (two, four or eight
-    wavefronts per SIMD), each the best of five timed launches."""
+    one streaming read of 2 GiB and one copy of 1 GiB with 16-byte accesses
+    (best over grids of 1,024 to 4,096 workgroups) and a loop of nothing but
+    bf16 MFMAs (two, four or eight wavefronts per SIMD), each the best of five
+    timed launches."""
     def best_ms(fn, reps=5):
         fn()
         torch.cuda.synchronize()
@@ -1021,19 +1022,28 @@ def measure_probes(torch, swa):
         out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
         read[grid] = nbytes / (best_ms(lambda: swa.swa_probe_read(buf, out, grid)) * 1e-3) / 1e9
     del buf, out
+    half = nbytes // 2  # 1 GiB read and 1 GiB written
+    src = torch.zeros(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(half, dtype=torch.uint8, device="cuda")
+    copy = {}
+    for grid in (1024, 2048, 4096):
+        copy[grid] = 2 * half / (best_ms(lambda: swa.swa_probe_copy(src, dst, grid)) * 1e-3) / 1e9
+    del src, dst
     mfma, iters = {}, 4096
     for grid in (512, 1024, 2048):
         out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
         flops = grid * 4 * iters * 8 * 16384
         mfma[grid] = flops / (best_ms(lambda: swa.swa_probe_mfma(out, grid, iters)) * 1e-3) / 1e12
     torch.cuda.empty_cache()
-    g_read, g_mfma = max(read, key=read.get), max(mfma, key=mfma.get)
-    log(f"[bench] probes: read {read[g_read]:.1f} GB/s (grid {g_read}), bf16 MFMA {mfma[g_mfma]:.1f} TFLOP/s "
-        f"(grid {g_mfma})")
+    g_read, g_copy, g_mfma = max(read, key=read.get), max(copy, key=copy.get), max(mfma, key=mfma.get)
+    log(f"[bench] probes: read {read[g_read]:.1f} GB/s (grid {g_read}), copy {copy[g_copy]:.1f} GB/s read + written "
+        f"(grid {g_copy}), bf16 MFMA {mfma[g_mfma]:.1f} TFLOP/s (grid {g_mfma})")
     return dict(hbm_read_gbs=round(read[g_read], 1), hbm_read_frac_of_peak=round(read[g_read] / HBM_PEAK_GBS, 4),
+                hbm_copy_gbs=round(copy[g_copy], 1), hbm_copy_frac_of_peak=round(copy[g_copy] / HBM_PEAK_GBS, 4),
                 mfma_bf16_tflops=round(mfma[g_mfma], 1),
                 mfma_frac_of_peak=round(mfma[g_mfma] / BF16_PEAK_TFLOPS, 4),
                 read="swa_probe_read: one pass over 2 GiB, 16-byte loads, grid-stride",
+                copy="swa_probe_copy: 1 GiB read and 1 GiB written, 16-byte loads and stores, grid-stride",
                 mfma="swa_probe_mfma: 8 independent v_mfma_f32_16x16x32_bf16 chains per wavefront")
 
 
@@ -1044,6 +1054,7 @@ def against_probes(res, probes):
         return
     if roof.get("unit") == "GB/s":
         roof["frac_of_probe"] = round(roof["achieved"] / probes["hbm_read_gbs"], 4)
+        roof["frac_of_copy_probe"] = round(roof["achieved"] / probes["hbm_copy_gbs"], 4)
     elif roof.get("unit") == "TFLOP/s":
         roof["frac_of_probe"] = round(roof["achieved"] / probes["mfma_bf16_tflops"], 4)
     if "tflops" in roof and roof.get("achieved_gbs"):  # an extend: the attainable roofline of the probes

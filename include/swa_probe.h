@@ -3,8 +3,9 @@
  * Not part of the attention path.  They give the practical ceilings that the
  * benchmark reports beside the published MI355X peaks: what a plain streaming
  * read reaches on the HBM, and what a loop of nothing but bf16 MFMAs reaches on
- * the matrix cores.  Each result of the benchmark is then also stated as a
- * fraction of the probe that bounds it.
+ * the matrix cores, and what a plain copy (as many bytes written as read)
+ * reaches.  Each result of the benchmark is then also stated as a fraction of
+ * the probe that bounds it.
  *
  * All pointers are device pointers owned by the caller.  Argument errors are
  * returned before anything is enqueued; a failed launch returns SWA_E_HIP.
@@ -25,6 +26,15 @@ extern "C" {
  *   grid   1 .. 65,535 workgroups.
  * Errors: SWA_E_ARG. */
 swa_status_t swa_probe_read(const void *buf, size_t bytes, float *out, int32_t grid, hipStream_t stream);
+
+/* Copy `bytes` bytes from src to dst with 16-byte loads and stores (a
+ * grid-stride loop over `grid` workgroups of 256 threads): `bytes` read and
+ * `bytes` written, the traffic mix of a kernel that streams one tensor in and
+ * another out.
+ *   src, dst  device, 16-aligned, not overlapping; bytes > 0 and a multiple of 16.
+ *   grid      1 .. 65,535 workgroups.
+ * Errors: SWA_E_ARG. */
+swa_status_t swa_probe_copy(const void *src, void *dst, size_t bytes, int32_t grid, hipStream_t stream);
 
 /* `grid` workgroups of 256 threads each run `iters` rounds of eight independent
  * v_mfma_f32_16x16x32_bf16 per wavefront (16,384 FLOPs each, so a launch does

@@ -1,5 +1,6 @@
-// Measurement probes: the practical HBM read ceiling and the practical bf16
-// MFMA ceiling of the GPU the benchmark runs on (declared in swa_probe.h).
+// Measurement probes: the practical HBM read and copy ceilings and the
+// practical bf16 MFMA ceiling of the GPU the benchmark runs on (declared in
+// swa_probe.h).
 #include "common.hpp"
 #include "swa_probe.h"
 
@@ -14,6 +15,13 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const uint4 *__restrict
     s += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
   }
   out[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = s;
+}
+
+// Grid-stride copy with 16-byte loads and stores.
+__global__ void __launch_bounds__(256) probe_copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                         size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
 // Eight independent accumulator chains per wavefront keep the matrix core
@@ -51,6 +59,16 @@ extern "C" swa_status_t swa_probe_read(const void *buf, size_t bytes, float *out
     return SWA_E_ARG;
   hipLaunchKernelGGL(probe_read_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
                      static_cast<const uint4 *>(buf), bytes / 16, out);
+  return from_launch();
+}
+
+extern "C" swa_status_t swa_probe_copy(const void *src, void *dst, size_t bytes, int32_t grid, hipStream_t stream) {
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if (!src || !dst || bytes == 0 || (bytes & 15u) || (s & 15u) || (d & 15u) || grid < 1 || grid > 65535 ||
+      (s < d + bytes && d < s + bytes))
+    return SWA_E_ARG;
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+                     static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
   return from_launch();
 }
 

@@ -33,7 +33,7 @@ EXPORTS = ("swa_pool_config", "swa_translate_loc", "swa_translate_window", "swa_
            "swa_translate_window_ring", "swa_ring_locs", "swa_decode_workspace_bytes", "swa_decode_step",
            "swa_decode_step_workspace_bytes", "swa_decode_noalloc", "swa_status_string",
            # include/swa_probe.h: measurement probes for the benchmark
-           "swa_probe_read", "swa_probe_mfma")
+           "swa_probe_read", "swa_probe_copy", "swa_probe_mfma")
 
 
 class SwaError(RuntimeError):
@@ -134,6 +134,7 @@ _sig = {
                                _sz, _p]),
     "swa_status_string": (ctypes.c_char_p, [_i32]),
     "swa_probe_read": (_i32, [_p, _sz, _p, _i32, _p]),
+    "swa_probe_copy": (_i32, [_p, _p, _sz, _i32, _p]),
     "swa_probe_mfma": (_i32, [_p, _i32, _i32, _p]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -637,6 +638,15 @@ def swa_probe_read(buf: torch.Tensor, out: torch.Tensor, grid: int, stream=None)
         raise ValueError("out needs grid * 256 floats")
     _check(lib.swa_probe_read(_ptr(buf, name="buf"), buf.numel() * buf.element_size(),
                               _ptr(out, torch.float32, "out"), grid, _stream(stream)), "swa_probe_read")
+
+
+def swa_probe_copy(src: torch.Tensor, dst: torch.Tensor, grid: int, stream=None):
+    """One copy of src into dst (same byte size, 16-aligned, not overlapping)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(lib.swa_probe_copy(_ptr(src, name="src"), _ptr(dst, name="dst"), nbytes, grid, _stream(stream)),
+           "swa_probe_copy")
 
 
 def swa_probe_mfma(out: torch.Tensor, grid: int, iters: int, stream=None):

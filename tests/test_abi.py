@@ -512,6 +512,13 @@ def test_probe_argument_errors(swa):
     assert lib.swa_probe_read(FAKE + 8, 1024, FAKE, 8, None) == E.SWA_E_ARG   # not 16-aligned
     assert lib.swa_probe_read(FAKE, 1024, FAKE, 0, None) == E.SWA_E_ARG
     assert lib.swa_probe_read(FAKE, 1024, FAKE, 65536, None) == E.SWA_E_ARG
+    assert lib.swa_probe_copy(None, FAKE, 1024, 8, None) == E.SWA_E_ARG
+    assert lib.swa_probe_copy(FAKE, None, 1024, 8, None) == E.SWA_E_ARG
+    assert lib.swa_probe_copy(FAKE, FAKE + 512, 1024, 8, None) == E.SWA_E_ARG   # overlapping
+    assert lib.swa_probe_copy(FAKE + 1024, FAKE, 1024 + 16, 8, None) == E.SWA_E_ARG  # overlapping the other way
+    assert lib.swa_probe_copy(FAKE, FAKE + 4096, 1000, 8, None) == E.SWA_E_ARG  # not a multiple of 16
+    assert lib.swa_probe_copy(FAKE + 8, FAKE + 4096, 1024, 8, None) == E.SWA_E_ARG
+    assert lib.swa_probe_copy(FAKE, FAKE + 4096, 1024, 0, None) == E.SWA_E_ARG
     assert lib.swa_probe_mfma(None, 8, 1, None) == E.SWA_E_ARG
     assert lib.swa_probe_mfma(FAKE, 0, 1, None) == E.SWA_E_ARG
     assert lib.swa_probe_mfma(FAKE, 8, 0, None) == E.SWA_E_ARG

@@ -37,3 +37,14 @@ def test_probe_mfma_repeatable():
     torch.cuda.synchronize()
     assert torch.isfinite(a).all() and (a > 0).all()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("grid", [1, 5, 64])
+def test_probe_copy_copies_every_byte(grid):
+    from sliding_window_attention_swa_amd import swa
+    src = torch.randint(0, 256, (16 * 1003,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(16 * 1003 + 64, dtype=torch.uint8, device="cuda")
+    swa.swa_probe_copy(src, dst[:src.numel()], grid)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:src.numel()], src)
+    assert int(dst[src.numel():].count_nonzero()) == 0  # nothing written past the end
