@@ -1,6 +1,7 @@
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|c1|c2|c3|c3w|c4|c5|evict|alloc|unified]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload all|c1|c2|c2w|c3|c3w|c4|c5|evict|alloc|unified] [--window W]
 
 Default (all): one JSON line whose headline is the largest single-GPU
 configuration, the long-context mixed-layer decode step (B = 32, T = 32K, 48
@@ -16,11 +17,16 @@ own roofline and CPU baseline:
          page 16, with the new token's store fused (32 layers per step)
     c5   fp8-KV SWA decode, B = 256, lognormal T (median 16K), e4m3 K/V, page 64,
          translate + store + decode (16 layers per step)
+    c2w  the c2 batch with W = 1023 and 4095 (long windows, split over their keys;
+         8 layers per step)
     c3   chunked-prefill extend, B = 4, prefix 8K + chunk 2K, W = 128, page 64,
          store + extend (4 layers per step): TFLOP/s, fraction of MFMA peak and of
          the attainable roofline
     c3w  the c3 shape with W = 512, 1024, 4096 (compute-bound windows)
     c1   one f32 request, T = 512, W = 128 (latency)
+Before the workloads, three probes of the library (include/swa_probe.h) measure
+the practical ceilings, a streaming read, a copy and a bf16 MFMA loop, and every
+roofline is also stated as a fraction of them (`probes`, `frac_of_probe`).
 Every step is captured once as a HIP graph and replayed; inputs are resident in
 HBM before the timed region.  `value` is algorithmic HBM bytes of the whole step
 per second.  Each `roofline` is its dominant kernel, timed live with HIP events
