@@ -40,6 +40,7 @@ struct AllocParams {
   int64_t *out_swa;
   int64_t capacity;  // entries of out_full / out_swa
   int64_t *new_pages;
+  int32_t page_shift;  // log2(page) for a power-of-two page, else -1
 };
 
 __device__ __forceinline__ int64_t ceil_page(int64_t x, int32_t page) { return (x + page - 1) / page; }
@@ -73,10 +74,17 @@ __device__ __forceinline__ void block_sum2(int64_t &a, int64_t &c, int64_t *red)
   c = red[4] + red[5] + red[6] + red[7];
 }
 
-// One workgroup per request.
+// gridDim.y workgroups per request, striding over its new positions
+// (positions are below 2^31: the lengths are int32).
 __global__ void __launch_bounds__(kThreads) alloc_extend_kernel(AllocParams p) {
   __shared__ int64_t red[8];
   const int32_t b = blockIdx.x;
+  const int32_t c = blockIdx.y;
+  {
+    int64_t pre, seq;
+    lens_of(p, b, pre, seq);
+    if (c > 0 && static_cast<int64_t>(c) * kThreads >= seq - pre) return;  // workgroup-uniform: nothing here
+  }
   // where this request's outputs and new pages start: the earlier requests' totals
   int64_t out_start = 0, page_start = 0;
   for (int32_t i = threadIdx.x; i < b; i += kThreads) {
@@ -89,7 +97,7 @@ __global__ void __launch_bounds__(kThreads) alloc_extend_kernel(AllocParams p) {
 
   int64_t pre, seq;
   lens_of(p, b, pre, seq);
-  if (b == p.batch - 1 && threadIdx.x == 0 && p.new_pages)
+  if (b == p.batch - 1 && c == 0 && threadIdx.x == 0 && p.new_pages)
     *p.new_pages = page_start + ceil_page(seq, p.page) - ceil_page(pre, p.page);
   const int64_t n = seq - pre;
   if (n == 0) return;
@@ -98,15 +106,18 @@ __global__ void __launch_bounds__(kThreads) alloc_extend_kernel(AllocParams p) {
   // the SWA side continues from the mapped last_loc; -1 (no prefix) stays -1
   const int64_t last_swa = (paired && last >= 0 && last < p.map_len - 1) ? p.map[last] : -1;
   const int64_t first_new = ceil_page(pre, p.page) * p.page;  // first position on a new page
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+  const uint32_t pg = static_cast<uint32_t>(p.page);
+  for (int64_t i = static_cast<int64_t>(c) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.y) * kThreads) {
     const int64_t j = pre + i;
     int64_t full, swa_slot = 0;
     if (j < first_new) {
       full = last + 1 + i;
       swa_slot = last_swa + 1 + i;
     } else {
-      const int64_t q = page_start + (j - first_new) / p.page;
-      const int64_t off = j % p.page;
+      const uint32_t d = static_cast<uint32_t>(j - first_new), ju = static_cast<uint32_t>(j);
+      const int64_t q = page_start + (p.page_shift >= 0 ? d >> p.page_shift : d / pg);
+      const int64_t off = p.page_shift >= 0 ? ju & (pg - 1) : ju % pg;
       full = page_at(p.free_full, p.n_free_full, q) * p.page + off;
       if (paired) swa_slot = page_at(p.free_swa, p.n_free_swa, q) * p.page + off;
     }
@@ -195,11 +206,16 @@ hipError_t launch_alloc(const AllocArgs &a, hipStream_t stream) {
   p.out_swa = a.out_swa;
   p.capacity = a.capacity;
   p.new_pages = a.new_pages;
+  p.page_shift = (a.page_size & (a.page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(a.page_size)) : -1;
   if (a.decode) {
     const uint32_t blocks = static_cast<uint32_t>((a.batch + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(alloc_decode_kernel, dim3(blocks), dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(alloc_extend_kernel, dim3(static_cast<uint32_t>(a.batch)), dim3(kThreads), 0, stream, p);
+    // about 2,048 workgroups in all (at least one and at most 16 per request)
+    int64_t split = (2048 + a.batch - 1) / a.batch;
+    split = split < 1 ? 1 : split > 16 ? 16 : split;
+    hipLaunchKernelGGL(alloc_extend_kernel, dim3(static_cast<uint32_t>(a.batch), static_cast<uint32_t>(split)),
+                       dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
