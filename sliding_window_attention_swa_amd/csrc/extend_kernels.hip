@@ -1104,7 +1104,10 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
     // normaliser sums the same rounded weights; PRECISE adds each weight's
     // rounding remainder as a second bf16 term, so a query's few weights carry
     // 16 significant bits)
-    float mx[RB];
+    // A row's max is the largest of its four lanes' maxima, so a wavefront
+    // whose lanes all stay within the slack has no row that grew: the
+    // cross-lane max is only taken in the (rare) rescale.
+    float ml[RB];
     bool grow = false;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -1113,13 +1116,13 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, s[i][kt][r]);
-      mx[i] = wave_max_q(m) * p.scale2;
-      grow = grow || mx[i] > m_run[i] + kRescaleSlack;
+      ml[i] = m;
+      grow = grow || m * p.scale2 > m_run[i] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
-        const float m_new = fmaxf(m_run[i], mx[i]);
+        const float m_new = fmaxf(m_run[i], wave_max_q(ml[i]) * p.scale2);
         const float alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
         m_run[i] = m_new;
         l_acc[i] *= alpha;
