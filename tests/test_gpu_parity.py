@@ -586,6 +586,8 @@ EXTEND_CASES = {
     "g4_empty_first": ([64, 0, 500], [0, 0, 200], 8, 2, 128, 16, False),
     "g8_one_token": ([0], [1], 16, 2, 128, 16, True),
     "g8_w255": ([100, 400], [300, 70], 16, 2, 255, 16, True),
+    # W = 128 stretches of 1, 2, 3, 4 and 5 steady tiles (whole pairs, an odd last tile)
+    "g8_w128_stretches": ([200, 300, 150, 400, 129], [16, 32, 48, 64, 80], 16, 2, 128, 16, True),
     # long bands (W >= 256 and W = -1): the 256-row tiles of the band kernel
     "g8_w256": ([0, 300, 1000], [500, 40, 129], 16, 2, 256, 16, True),
     "g8_w512": ([0, 600, 1500], [700, 300, 64], 16, 2, 512, 16, True),
