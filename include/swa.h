@@ -192,6 +192,10 @@ size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_d
  * (SWA_F32, or SWA_BF16 = the f32 result rounded to nearest even).
  * Supported: head_dim 128; q_dtype f32 with f32 K/V; q_dtype bf16 with bf16 or
  * e4m3 K/V; q_heads / kv_heads in {1, 2, 4, 8, 16}.
+ * Precision: with bf16 or e4m3 K/V, P.V runs in f16 (weights rounded to f16,
+ * V converted to f16, fp32 accumulation), so bf16 V values must satisfy
+ * |v| <= 65504 (larger ones overflow to inf; e4m3 codes always fit).  The
+ * result is not checked: an out-of-range V gives inf/NaN outputs, no error.
  * num_splits and workspace come from swa_decode_plan for the same shape.
  * An empty batch (idx->batch == 0) launches nothing and returns SWA_OK after
  * the same argument checks; q, out and the workspace may then be NULL. */
@@ -325,7 +329,8 @@ swa_status_t swa_decode_step(const swa_decode_step_t *step, const swa_index_t *i
  * and out, i.e. qo_indptr[batch].  Keys come from the window table built by
  * swa_translate_window(prefix_lens) when table_indptr is given, else from
  * req_to_token directly.  Supported: head_dim 128, bf16 q with bf16 K/V,
- * q_heads / kv_heads in {1, 2, 4, 8, 16}.  Requests with no new tokens
+ * q_heads / kv_heads in {1, 2, 4, 8, 16}.  P.V runs in f16 as in swa_decode,
+ * so V values must satisfy |v| <= 65504 (not checked).  Requests with no new tokens
  * (qo_indptr[b] == qo_indptr[b+1]) contribute nothing; an empty batch or
  * total_q == 0 launches nothing, and q and out may then be NULL. */
 swa_status_t swa_extend(const void *q, int32_t q_dtype, int32_t q_heads, const int32_t *qo_indptr,

@@ -46,20 +46,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return u;
 }
 
-// acc + both bf16 values of a packed pair, in f32.  The softmax weights that
-// enter P.V are rounded to bf16; summing the same rounded weights for the
-// normaliser makes the output an exact convex combination of V rows (plus the
-// sink), so the rounding only perturbs relative weights: a query with few keys,
-// whose output is as large as a V row, then carries no more error than one
-// with many.  One dot product against (1, 1) (v_dot2c_f32_bf16; the products
-// are exact).
-__device__ __forceinline__ float bf16x2_acc(uint32_t u, float acc) {
-  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-  bf16x2_v a, ones;
-  const uint32_t one2 = 0x3F803F80u;
+// The P.V product of the MFMA attention kernels runs in IEEE binary16 (f16):
+// the softmax weights are rounded to f16 (11 significant bits, against 8 for
+// bf16) and the V rows are staged as f16, which holds every bf16 value in
+// [2^-14, 65504] exactly (smaller values to within 2^-25; larger ones
+// overflow to inf, so V must stay inside f16's range).  A query whose output
+// is dominated by a few keys is as large as a V row while the output's RMS is
+// that of an average over the window; with bf16 weights the rounding of the
+// few large weights alone could then reach 2% of the RMS, with f16 about 0.3%.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));   // MFMA f16 operand
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4v_t __attribute__((ext_vector_type(4)));
+
+// Two floats -> two f16 (round to nearest even) in one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2_hw(float lo, float hi) {
+  f32x2v_t x = {lo, hi};
+  f16x2v_t r = __builtin_convertvector(x, f16x2v_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
+// acc + both f16 values of a packed pair, in f32 (v_dot2c_f32_f16 against
+// (1, 1); the products are exact): the normaliser sums the same rounded
+// weights that enter P.V, so the output is an exact convex combination of the
+// staged V rows (plus the sink).
+__device__ __forceinline__ float f16x2_acc(uint32_t u, float acc) {
+  f16x2v_t a, ones;
+  const uint32_t one2 = 0x3C003C00u;
   __builtin_memcpy(&a, &u, 4);
   __builtin_memcpy(&ones, &one2, 4);
-  return __builtin_amdgcn_fdot2_f32_bf16(a, ones, acc, false);
+  return __builtin_amdgcn_fdot2(a, ones, acc, false);
+}
+
+// Eight bf16 (a 16-byte piece of a row) -> eight f16 in the same order.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4 &x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2_hw(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xFFFF0000u));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// c + A B on the f16 matrix cores (16x16x32), operands carried as 8 x 16 bits.
+__device__ __forceinline__ f32x4_t mfma_f16(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
+  f16x8_t x, y;
+  __builtin_memcpy(&x, &a, 16);
+  __builtin_memcpy(&y, &b, 16);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
 }
 
 // Reductions over the four 16-lane rows of a wavefront (lanes l, l^16, l^32,

@@ -22,8 +22,9 @@
 //   * online softmax in base 2; the sink enters exactly once, where the final
 //     normalisation happens.
 //
-// bf16 / e4m3 K/V path: S^T = K Q^T and O^T = V^T P^T on the CDNA4 matrix
-// cores (v_mfma_f32_16x16x32_bf16).  With keys as the M dimension of the
+// bf16 / e4m3 K/V path: S^T = K Q^T (v_mfma_f32_16x16x32_bf16) and
+// O^T = V^T P^T (v_mfma_f32_16x16x32_f16, P rounded to f16) on the CDNA4
+// matrix cores.  With keys as the M dimension of the
 // first product, its accumulator layout (lane = head column, 4 keys per lane)
 // is exactly the B-operand layout the second product needs for P^T, so P
 // never leaves registers.  The head dimension is permuted identically in Q and
@@ -31,9 +32,10 @@
 // groups of a key read neighbouring 16-byte pieces).  V is staged through LDS
 // (whole rows per load instruction, padded LDS rows, conflict-free transposed
 // reads with ds_read_b64_tr_b16) because the key index must be the per-lane
-// contraction index of the second product.  e4m3 bytes are widened to bf16
-// exactly with v_cvt_scalef32_pk_bf16_fp8; the per-tensor scales are folded
-// into the logit scale and the output.
+// contraction index of the second product; it is converted to f16 on the way
+// (exact for bf16 values of magnitude 2^-14 .. 65504).  e4m3 K bytes are
+// widened to bf16 and e4m3 V bytes to f16, both exactly; the per-tensor scales
+// are folded into the logit scale and the output.
 //
 // f32 path: plain VALU; 16 keys per wavefront step, 4 lanes per key row.
 #include <mutex>
@@ -299,14 +301,15 @@ __device__ __forceinline__ void load_v(const DecodeParams &p, int32_t slot, int3
   }
 }
 
-// 16 e4m3 bytes -> 16 bf16 (exact).
-__device__ __forceinline__ void fp8x16_to_bf16(const uint4 &x, uint4 (&out)[2]) {
+// 16 e4m3 bytes -> 16 f16 (exact: every e4m3 value, subnormals included, is
+// an f16 normal).
+__device__ __forceinline__ void fp8x16_to_f16(const uint4 &x, uint4 (&out)[2]) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
   uint32_t u[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-    bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+    f16x2v_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+    f16x2v_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
     __builtin_memcpy(&u[2 * i], &a, 4);
     __builtin_memcpy(&u[2 * i + 1], &c, 4);
   }
@@ -372,8 +375,9 @@ __device__ __forceinline__ void new_pieces(const uint4 (&kn_raw)[4], const uint4
   }
 }
 
-// One block's V rows into its 16-row LDS tile (bf16, kSVRow stride); rows of
-// keys at or past k_end are written as zeros (their slots may hold anything).
+// One block's V rows into its 16-row LDS tile as f16 (the P.V operand type;
+// kSVRow stride); rows of keys at or past k_end are written as zeros (their
+// slots may hold anything).
 template <typename KV>
 __device__ __forceinline__ void v_to_lds(const uint4 (&raw)[Layout<KV>::kVLoads], uint16_t *tile, int32_t lane,
                                          int32_t key_base, int32_t k_end) {
@@ -383,10 +387,10 @@ __device__ __forceinline__ void v_to_lds(const uint4 (&raw)[Layout<KV>::kVLoads]
     const bool ok = key_base + key < k_end;
     uint4 *d = reinterpret_cast<uint4 *>(tile + key * kSVRow + Layout<KV>::v_off(lane));
     if constexpr (sizeof(KV) == 2) {
-      d[0] = ok ? raw[j] : make_uint4(0, 0, 0, 0);
+      d[0] = ok ? bf16x8_to_f16x8(raw[j]) : make_uint4(0, 0, 0, 0);
     } else {
       uint4 w2[2];
-      fp8x16_to_bf16(raw[j], w2);
+      fp8x16_to_f16(raw[j], w2);
       d[0] = ok ? w2[0] : make_uint4(0, 0, 0, 0);
       d[1] = ok ? w2[1] : make_uint4(0, 0, 0, 0);
     }
@@ -404,7 +408,7 @@ __device__ __forceinline__ void pv_pair(const uint16_t *pair, int32_t kr, int32_
     const i16x4_t lo = lds_read_tr16(vrow + 16 * c);
     const i16x4_t hi = SECOND ? lds_read_tr16(vrow + 16 * kSVRow + 16 * c) : i16x4_t{0, 0, 0, 0};
     const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[c], 0, 0, 0);
+    acc[c] = mfma_f16(vop, pop, acc[c]);
   }
 }
 
@@ -413,9 +417,15 @@ __device__ __forceinline__ void pv_pair(const uint16_t *pair, int32_t kr, int32_
 __device__ __forceinline__ void pv_single(const uint16_t *blk, int32_t kr, int32_t lq, const i16x4_t &pop,
                                           f32x4_t (&acc)[8]) {
   const uint16_t *vrow = blk + (4 * lq + (kr >> 2)) * kSVRow + 4 * (kr & 3);
+  f16x4v_t b;
+  __builtin_memcpy(&b, &pop, 8);
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(vrow + 16 * c), pop, acc[c], 0, 0, 0);
+  for (int c = 0; c < 8; ++c) {
+    const i16x4_t v = lds_read_tr16(vrow + 16 * c);
+    f16x4v_t a;
+    __builtin_memcpy(&a, &v, 8);
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc[c], 0, 0, 0);
+  }
 }
 
 // Streaming kernel (long key ranges: full layers, split-K).  Each wavefront
@@ -483,10 +493,10 @@ __device__ __forceinline__ void stream_compute(const DecodeParams &p, const Stre
   for (int c = 0; c < 8; ++c) acc[c] *= alpha;
   bf16x8_t pop;
   {
-    uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
-                      pack_bf16x2_hw(pv[6], pv[7])};
+    uint32_t u4[4] = {pack_f16x2_hw(pv[0], pv[1]), pack_f16x2_hw(pv[2], pv[3]), pack_f16x2_hw(pv[4], pv[5]),
+                      pack_f16x2_hw(pv[6], pv[7])};
     // the normaliser sums the rounded weights that enter P.V
-    l_run = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run * alpha))));
+    l_run = f16x2_acc(u4[3], f16x2_acc(u4[2], f16x2_acc(u4[1], f16x2_acc(u4[0], l_run * alpha))));
     __builtin_memcpy(&pop, u4, 16);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's V rows are in LDS
@@ -785,10 +795,10 @@ __global__ void __launch_bounds__(kWinWaves * 64) decode_window_kernel(DecodePar
         pv[4 + r] =
             (2 * u2 + 1 < MAXB) ? __builtin_amdgcn_exp2f(sc[(2 * u2 + 1) < MAXB ? 2 * u2 + 1 : 0][r] - m_run) : 0.f;
       }
-      uint32_t u4[4] = {pack_bf16x2_hw(pv[0], pv[1]), pack_bf16x2_hw(pv[2], pv[3]), pack_bf16x2_hw(pv[4], pv[5]),
-                        pack_bf16x2_hw(pv[6], pv[7])};
+      uint32_t u4[4] = {pack_f16x2_hw(pv[0], pv[1]), pack_f16x2_hw(pv[2], pv[3]), pack_f16x2_hw(pv[4], pv[5]),
+                        pack_f16x2_hw(pv[6], pv[7])};
       // the normaliser sums the rounded weights that enter P.V
-      l_run = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run))));
+      l_run = f16x2_acc(u4[3], f16x2_acc(u4[2], f16x2_acc(u4[1], f16x2_acc(u4[0], l_run))));
       __builtin_memcpy(&pop[u2], u4, 16);
     }
     // ---- O^T = V^T P^T over block pairs (2u2, 2u2+1), each pair's V rows
@@ -963,9 +973,9 @@ __global__ void __launch_bounds__(256, 2) decode_wave_kernel(DecodeParams p) {
   uint16_t *vt = vtiles + w * 16 * kSVRow;
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
-    uint32_t u2[2] = {pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[u][0] - m_run), __builtin_amdgcn_exp2f(sc[u][1] - m_run)),
-                      pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[u][2] - m_run), __builtin_amdgcn_exp2f(sc[u][3] - m_run))};
-    l_run = bf16x2_acc(u2[1], bf16x2_acc(u2[0], l_run));  // the normaliser sums the rounded weights
+    uint32_t u2[2] = {pack_f16x2_hw(__builtin_amdgcn_exp2f(sc[u][0] - m_run), __builtin_amdgcn_exp2f(sc[u][1] - m_run)),
+                      pack_f16x2_hw(__builtin_amdgcn_exp2f(sc[u][2] - m_run), __builtin_amdgcn_exp2f(sc[u][3] - m_run))};
+    l_run = f16x2_acc(u2[1], f16x2_acc(u2[0], l_run));  // the normaliser sums the rounded weights
     i16x4_t pop;
     __builtin_memcpy(&pop, u2, 8);
     v_to_lds<KV>(vraw[u], vt, lane, 16 * u, n);

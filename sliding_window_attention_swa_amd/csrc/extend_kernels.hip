@@ -12,8 +12,9 @@
 //     G = 16 is split into two groups of 8 (eight heads fill the four
 //     wavefronts at two heads each; four each would spill registers); the key
 //     range of a tile is only its band [i0 - W, i0 + 15];
-//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32
-//     accumulation; P is rounded to bf16 for the second product and never leaves
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 and O^T = V^T P^T on
+//     v_mfma_f32_16x16x32_f16, both with fp32 accumulation; P is rounded to f16
+//     (V is staged as f16, exact for bf16 values in f16's range) and never leaves
 //     registers (the first product's accumulator layout is the second's B
 //     operand layout); the V^T operand is read from a row-major LDS tile with
 //     gfx950's transposing ds_read_b64_tr_b16; online softmax in base 2;
@@ -226,11 +227,13 @@ __device__ __forceinline__ void fetch_piece(const ExtendParams &p, int32_t slot,
   v = *reinterpret_cast<const uint4 *>(p.v + off);
 }
 
+// K rows are staged as bf16 (the operand of QK^T), V rows as f16 (the operand
+// of the f16 P.V product).
 __device__ __forceinline__ void put_piece(uint16_t *ktile, uint16_t *vtile, int32_t row, const uint4 &k,
                                           const uint4 &v) {
   const int32_t piece = threadIdx.x & 15;
   *reinterpret_cast<uint4 *>(ktile + row * kKRow + 8 * piece) = k;
-  *reinterpret_cast<uint4 *>(vtile + row * kVRow + 8 * piece) = v;
+  *reinterpret_cast<uint4 *>(vtile + row * kVRow + 8 * piece) = bf16x8_to_f16x8(v);
 }
 
 // Steady tiles read the band from the ring: band block j lives in ring slot
@@ -279,7 +282,7 @@ __device__ __forceinline__ void head_scores(const uint16_t *ktile, const int32_t
 }
 
 // One head's softmax numerators: pw holds the weights 2^(s - m), rounded to
-// bf16 and packed in pairs (keys 4lq + {0,1} and 4lq + {2,3} of each block), m
+// f16 and packed in pairs (keys 4lq + {0,1} and 4lq + {2,3} of each block), m
 // the band's max and l the sum of the rounded weights (the weights that enter
 // P.V), taken block by block.  The whole band at once: no rescaling.  Packing
 // here halves the registers the weights hold while P.V runs.
@@ -298,9 +301,9 @@ __device__ __forceinline__ void head_weights(float scale2, const f32x4_t (&s)[kK
     float e[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[j][r], scale2, -m_new));
-    pw[j][0] = pack_bf16x2_hw(e[0], e[1]);
-    pw[j][1] = pack_bf16x2_hw(e[2], e[3]);
-    l = bf16x2_acc(pw[j][1], bf16x2_acc(pw[j][0], l));
+    pw[j][0] = pack_f16x2_hw(e[0], e[1]);
+    pw[j][1] = pack_f16x2_hw(e[2], e[3]);
+    l = f16x2_acc(pw[j][1], f16x2_acc(pw[j][0], l));
   }
   l_run = l;
 }
@@ -337,7 +340,7 @@ __device__ __forceinline__ void head_pv(const uint16_t *vtile, const int32_t (&s
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const bf16x8_t vop = __builtin_shufflevector(lo[n], hi[n], 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, u == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[n], 0, 0, 0);
+      acc[n] = mfma_f16(vop, pop, u == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[n]);
     }
   }
 }
@@ -460,11 +463,11 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
           const int kb1 = (2 * u + 1) < kKB ? 2 * u + 1 : 2 * u;
-          uint32_t u4[4] = {pack_bf16x2_hw(sacc[m][2 * u][0], sacc[m][2 * u][1]),
-                            pack_bf16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
-                            second ? pack_bf16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
-                            second ? pack_bf16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
-          l_run[m] = bf16x2_acc(u4[3], bf16x2_acc(u4[2], bf16x2_acc(u4[1], bf16x2_acc(u4[0], l_run[m]))));
+          uint32_t u4[4] = {pack_f16x2_hw(sacc[m][2 * u][0], sacc[m][2 * u][1]),
+                            pack_f16x2_hw(sacc[m][2 * u][2], sacc[m][2 * u][3]),
+                            second ? pack_f16x2_hw(sacc[m][kb1][0], sacc[m][kb1][1]) : 0u,
+                            second ? pack_f16x2_hw(sacc[m][kb1][2], sacc[m][kb1][3]) : 0u};
+          l_run[m] = f16x2_acc(u4[3], f16x2_acc(u4[2], f16x2_acc(u4[1], f16x2_acc(u4[0], l_run[m]))));
           __builtin_memcpy(&pop[m], u4, 16);
         }
         // the pair's transposed reads go out before its MFMAs, so their LDS
@@ -480,7 +483,7 @@ __device__ void tile_general(const ExtendParams &p, const KeySrc &ks, const Tile
           bf16x8_t vop = {lo[n][0], lo[n][1], lo[n][2], lo[n][3], hi[n][0], hi[n][1], hi[n][2], hi[n][3]};
 #pragma unroll
           for (int m = 0; m < MB; ++m)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[m], acc[m][n], 0, 0, 0);
+            acc[m][n] = mfma_f16(vop, pop[m], acc[m][n]);
         }
       }
     }
@@ -888,22 +891,21 @@ hipError_t launch_mb(const ExtendParams &p, uint32_t grid, bool out_bf16, hipStr
 //     workgroup barrier per block;
 //   * online softmax in base 2 that rescales lazily: the running max of a row
 //     moves only when a block's max exceeds it by more than 8, so a row's
-//     weights stay below 2^8 (exact in bf16 up to its relative precision) and,
+//     weights stay below 2^8 (well inside f16's range) and,
 //     past the first blocks, the accumulators are almost never rescaled;
 //   * tiles are numbered (request, kv head, tile, q-head group) and dealt to
 //     the XCDs in contiguous ranges: neighbouring tiles share most of their
 //     band, so they meet in one L2.
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;                                  // keys per band block
-// The A operand of all ones (bf16 1.0): an MFMA of it with a block's packed
+// The A operand of all ones (f16 1.0): an MFMA of it with a block's packed
 // weights P^T gives each query's sum of those weights in every output row, so
 // the normaliser is summed on the matrix cores from exactly the weights that
 // enter P.V, and the VALU (the busier pipe here) does not add them.
-constexpr bf16x8_t kOnes = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
+constexpr bf16x8_t kOnes = {0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x3C00};
 constexpr int kBandStage = kBK * (kKRow + kVRow);        // elements of one LDS stage (K rows, then V rows)
 constexpr int32_t kBandMinWindow = 256;                  // windows at least this long use the band kernel
 constexpr float kRescaleSlack = 8.f;                     // log2 of the largest weight before a rescale
-constexpr int32_t kPreciseBelow = 128;                   // tiles with queries before this position: two-term weights
 
 struct BandTile {
   int32_t b, g, hq0, tile;  // request, kv head, first q head of the group, tile of the request
@@ -948,7 +950,7 @@ struct BandStage {
 
 // The band's blocks for this wave's RB row blocks (query positions q_of[i] +
 // kr): S^T = K Q^T, masks on edge blocks, softmax with lazy rescaling, O^T +=
-// V^T P^T.  PRECISE: each weight also enters its bf16 rounding remainder.
+// V^T P^T (weights and V rows in f16).
 //
 // Two wavefronts share each SIMD.  The odd wavefronts run one block behind in
 // their P.V: in the iteration of block j they first do P.V of block j - 1, then
@@ -958,7 +960,7 @@ struct BandStage {
 // 1139 us with no wavefront behind, and 1208 us with the upper four behind
 // (waves 2k and 2k + 1 appear to share a SIMD).  That P.V reads the V rows of
 // block j - 1 while block j + 1 is written, hence three LDS stages.
-template <int RB, int NW, bool PRECISE>
+template <int RB, int NW>
 __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx &c, uint16_t *lds,
                                             const bf16x8_t (&qop)[RB][4], const int32_t (&q_of)[RB],
                                             f32x4_t (&acc)[RB][8], float (&m_run)[RB], f32x4_t (&l_acc)[RB]) {
@@ -1016,7 +1018,7 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
       for (int ps = 0; ps < kPasses; ++ps) {
         const int32_t row = srow + kRowsPerPass * ps;
         *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = kv[ps];
-        *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) = vv[ps];
+        *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) = bf16x8_to_f16x8(vv[ps]);
       }
     } else {
 #pragma unroll
@@ -1025,13 +1027,13 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
         const bool ok = kBK * j + row < c.nkeys;
         *reinterpret_cast<uint4 *>(stage + row * kKRow + 8 * spiece) = ok ? kv[ps] : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4 *>(stage + kBK * kKRow + row * kVRow + 8 * spiece) =
-            ok ? vv[ps] : make_uint4(0, 0, 0, 0);
+            ok ? bf16x8_to_f16x8(vv[ps]) : make_uint4(0, 0, 0, 0);
       }
     }
   };
   const int32_t voff = (4 * lq + (kr >> 2)) * kVRow + 4 * (kr & 3);
   // O^T += V^T P^T over the key-tile pairs (0, 1) and (2, 3) of the block whose V rows are at vt
-  auto pv = [&](const uint16_t *vt, const bf16x8_t (&pop)[RB][2], const bf16x8_t (&plo)[RB][2]) {
+  auto pv = [&](const uint16_t *vt, const bf16x8_t (&pop)[RB][2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint16_t *va = vt + (32 * u) * kVRow + voff;
@@ -1043,8 +1045,7 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
         const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
-          acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i][u], acc[i][n], 0, 0, 0);
-          if constexpr (PRECISE) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[i][u], acc[i][n], 0, 0, 0);
+          acc[i][n] = mfma_f16(vop, pop[i][u], acc[i][n]);
         }
       }
     }
@@ -1052,7 +1053,7 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
 
   int32_t sl[kPasses];
   uint4 kv[kPasses], vv[kPasses];
-  bf16x8_t pop[RB][2], plo[RB][2];  // the weights of the last softmax (the lagging half's next P.V)
+  bf16x8_t pop[RB][2];  // the weights of the last softmax (the lagging half's next P.V)
   block_slots(0, sl);
   block_fetch(sl, kv, vv);
   block_slots(1, sl);
@@ -1067,7 +1068,7 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
       block_slots(j + 2, sl);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (lag && j > 0) pv(prev + kBK * kKRow, pop, plo);  // the lagging half: P.V of block j - 1
+    if (lag && j > 0) pv(prev + kBK * kKRow, pop);  // the lagging half: P.V of block j - 1
     const uint16_t *vt_base = cur + kBK * kKRow;
     const int32_t kb = c.kj0 + kBK * j;  // position of the block's first key
     // ---- S^T = K Q^T: key tile kt (16 keys), lane holds keys 4lq..4lq+3 of query kr
@@ -1100,10 +1101,8 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
           }
       }
     }
-    // ---- softmax: block max per row, lazy rescale, weights packed to bf16 (the
-    // normaliser sums the same rounded weights; PRECISE adds each weight's
-    // rounding remainder as a second bf16 term, so a query's few weights carry
-    // 16 significant bits)
+    // ---- softmax: block max per row, lazy rescale, weights packed to f16 (the
+    // normaliser sums the same rounded weights)
     // A row's max is the largest of its four lanes' maxima, so a wavefront
     // whose lanes all stay within the slack has no row that grew: the
     // cross-lane max is only taken in the (rare) rescale.
@@ -1139,24 +1138,13 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const f32x4_t &e0 = s[i][2 * u], &e1 = s[i][2 * u + 1];
-        const uint32_t u4[4] = {pack_bf16x2_hw(e0[0], e0[1]), pack_bf16x2_hw(e0[2], e0[3]),
-                                pack_bf16x2_hw(e1[0], e1[1]), pack_bf16x2_hw(e1[2], e1[3])};
+        const uint32_t u4[4] = {pack_f16x2_hw(e0[0], e0[1]), pack_f16x2_hw(e0[2], e0[3]),
+                                pack_f16x2_hw(e1[0], e1[1]), pack_f16x2_hw(e1[2], e1[3])};
         __builtin_memcpy(&pop[i][u], u4, 16);
-        l_acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pop[i][u], l_acc[i], 0, 0, 0);
-        if constexpr (PRECISE) {
-          const float ev[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
-          uint32_t r4[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float h0 = __uint_as_float(u4[k] << 16), h1 = __uint_as_float(u4[k] & 0xFFFF0000u);
-            r4[k] = pack_bf16x2_hw(ev[2 * k] - h0, ev[2 * k + 1] - h1);
-          }
-          __builtin_memcpy(&plo[i][u], r4, 16);
-          l_acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, plo[i][u], l_acc[i], 0, 0, 0);
-        }
+        l_acc[i] = mfma_f16(kOnes, pop[i][u], l_acc[i]);
       }
     }
-    if (!lag) pv(vt_base, pop, plo);  // the leading half: P.V of block j now
+    if (!lag) pv(vt_base, pop);  // the leading half: P.V of block j now
     if (more) block_put(j + 1, next, kv, vv);
     lds_barrier();
     uint16_t *t = prev;
@@ -1164,7 +1152,7 @@ __device__ __forceinline__ void band_blocks(const ExtendParams &p, const BandCtx
     cur = next;
     next = t;
   }
-  if (lag) pv(prev + kBK * kKRow, pop, plo);  // the last block's P.V (its stage is not rewritten before a barrier)
+  if (lag) pv(prev + kBK * kKRow, pop);  // the last block's P.V (its stage is not rewritten before a barrier)
 }
 
 // A tile is RB * NW row blocks of 16 q rows (heads x queries); WGS
@@ -1241,11 +1229,7 @@ __global__ void __launch_bounds__(NW * 64, WGS) band_kernel(ExtendParams p) {
       l_acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     if (c.nblk > 0) {
-      // queries at positions below kPreciseBelow see fewer keys than that (W >= 256)
-      if (c.i0 < kPreciseBelow)
-        band_blocks<RB, NW, true>(p, c, lds, qop, q_of, acc, m_run, l_acc);
-      else
-        band_blocks<RB, NW, false>(p, c, lds, qop, q_of, acc, m_run, l_acc);
+      band_blocks<RB, NW>(p, c, lds, qop, q_of, acc, m_run, l_acc);
     }
     // ---- sink once, normalise, store the valid query rows
 #pragma unroll
