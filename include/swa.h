@@ -194,8 +194,9 @@ size_t swa_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_d
  * e4m3 K/V; q_heads / kv_heads in {1, 2, 4, 8, 16}.
  * Precision: with bf16 or e4m3 K/V, P.V runs in f16 (weights rounded to f16,
  * V converted to f16, fp32 accumulation), so bf16 V values must satisfy
- * |v| <= 65504 (larger ones overflow to inf; e4m3 codes always fit).  The
- * result is not checked: an out-of-range V gives inf/NaN outputs, no error.
+ * |v| <= 65504 (larger ones overflow to inf; e4m3 codes always fit); values
+ * below 2^-14 in magnitude become f16 subnormals, accurate to 2^-25.  V is
+ * not checked: an out-of-range V gives inf/NaN outputs, no error.
  * num_splits and workspace come from swa_decode_plan for the same shape.
  * An empty batch (idx->batch == 0) launches nothing and returns SWA_OK after
  * the same argument checks; q, out and the workspace may then be NULL. */

@@ -636,6 +636,55 @@ def test_extend_small(name):
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
+def scale_v_bf16(wl, log2_scale, extremes=False):
+    """V rows (pool rows and the new tokens' rows) times 2^log2_scale, which is
+    exact in bf16 while no value leaves its normal range.  extremes: dims 0-3 of
+    every new V row become +-65280 (the largest bf16 value that f16 holds) and
+    +-2^-14 (f16's smallest normal)."""
+    def scaled(bits):
+        return WL.to_store(codecs.bf16_bits_to_f64(bits) * 2.0 ** log2_scale, "bf16")
+    wl.pool_v = WL.SparsePool(*wl.pool_v.shape, "bf16", wl.pool_v.used_rows, scaled(wl.pool_v.values))
+    nv = scaled(wl.new_v)
+    if extremes:
+        nv[..., :4] = WL.to_store(np.array([65280.0, -65280.0, 2.0 ** -14, -(2.0 ** -14)]), "bf16")
+    wl.new_v = nv
+
+
+V_RANGE_SCALES = [(13, True), (-10, False)]  # |v| up to 65280 / about 1e-3 with ~5% f16 subnormals
+
+
+@pytest.mark.parametrize("window", [128, 1023])
+@pytest.mark.parametrize("log2_scale,extremes", V_RANGE_SCALES)
+def test_decode_v_range_edges(window, log2_scale, extremes):
+    """P.V runs in f16: bf16 V converts exactly up to 65504 and keeps 2^-25
+    absolute accuracy below 2^-14.  V at both ends of that range stays within
+    the bf16 tolerance, on the window kernel (W = 128, fused store too) and on
+    the split-K stream kernel (W = 1023)."""
+    say(f"decode V range W={window} scale 2^{log2_scale}")
+    wl = WL.decode_workload(f"vrange_{window}", 41 + window, [1, 130, 700, 2000, 3000], 16, 2, window, 16, "bf16",
+                            "bf16", with_store=True)
+    scale_v_bf16(wl, log2_scale, extremes)
+    ref = oracle_decode(wl)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    check(run_decode(dw, "f32"), ref, TOL["bf16"], f"decode W={window} V x 2^{log2_scale}")
+    if window == 128:
+        check(run_decode_store(DeviceWorkload(wl), "f32"), ref, TOL["bf16"], f"fused decode V x 2^{log2_scale}")
+
+
+@pytest.mark.parametrize("window", [128, 512])
+@pytest.mark.parametrize("log2_scale,extremes", V_RANGE_SCALES)
+def test_extend_v_range_edges(window, log2_scale, extremes):
+    """As test_decode_v_range_edges for extend: the W = 128 ring path and the
+    band kernel (W = 512)."""
+    say(f"extend V range W={window} scale 2^{log2_scale}")
+    wl = WL.extend_workload(f"vrange_{window}", 43 + window, [0, 300, 700], [40, 100, 64], 16, 2, window, 16)
+    scale_v_bf16(wl, log2_scale, extremes)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    check(run_extend(dw, "f32"), oracle_extend(wl), TOL["bf16"], f"extend W={window} V x 2^{log2_scale}")
+
+
 def test_extend_bad_qo_indptr_stays_in_bounds():
     """qo_indptr entries outside [0, total_q] or out of order: every request's
     rows are clamped into [0, total_q], so nothing outside `out` is written,
