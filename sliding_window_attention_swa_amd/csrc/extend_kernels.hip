@@ -942,6 +942,24 @@ struct BandCtx {
   int32_t nblk;    // 64-key blocks
 };
 
+// Per-request fields of the band kernel, read once per workgroup into LDS (for
+// batches of up to kBandTabReqs requests and up to kBandTabHeads q heads), so
+// that a tile's context is found with LDS reads instead of a walk over the
+// batch's qo_indptr (one dependent global round trip per request) followed by
+// the request's own lengths and table range.
+constexpr int kBandTabReqs = 1024;
+constexpr int kBandTabHeads = 256;
+struct BandReq {
+  int64_t src_off;    // key source: entry 0 is src_off past the window table (or req_to_token)
+  int64_t src_hi;     // entries in the key source
+  int32_t pos_base;   // position of entry 0
+  int32_t qo0, n;     // query rows
+  int32_t prefix;     // cached positions
+  int32_t seq;        // sequence length, clamped to the req_to_token stride
+  int32_t tiles;      // tiles of the request (all kv heads and q-head groups)
+  int32_t tile0;      // tiles of the requests before it
+};
+
 template <int NW>
 struct BandStage {
   static constexpr int kRowsPerPass = NW * 64 / 16;   // 16 threads per 256-byte row
@@ -1161,6 +1179,9 @@ template <int RB, int NW, int WGS, bool OUT_BF16>
 __global__ void __launch_bounds__(NW * 64, WGS) band_kernel(ExtendParams p) {
   constexpr int kRowBlocks = RB * NW;
   __shared__ __attribute__((aligned(16))) uint16_t lds[3 * kBandStage];
+  __shared__ BandReq reqs[kBandTabReqs];
+  __shared__ float sinks_tab[kBandTabHeads];
+  __shared__ int32_t total_tab;
   const int32_t lane = threadIdx.x & 63;
   const int32_t w = threadIdx.x >> 6;
   const int32_t kr = lane & 15;
@@ -1169,22 +1190,105 @@ __global__ void __launch_bounds__(NW * 64, WGS) band_kernel(ExtendParams p) {
   const int32_t nsub = TQ / 16;                  // 16-query sub-blocks per head
   const int32_t W = p.window;
 
+  const bool tab = p.batch <= kBandTabReqs && p.q_heads <= kBandTabHeads;  // uniform
   int32_t total = 0;
-  for (int32_t b = 0; b < p.batch; ++b) total += (new_count(p, b) + TQ - 1) / TQ * p.kv_heads * p.halves;
+  if (tab) {
+    for (int32_t b = threadIdx.x; b < p.batch; b += NW * 64) {
+      BandReq rq;
+      const QoRows qrows = qo_rows(p, b);
+      rq.qo0 = qrows.qo0;
+      rq.n = qrows.n;
+      rq.seq = p.seq_lens[b];
+      if (rq.seq > p.r2t_stride) rq.seq = static_cast<int32_t>(p.r2t_stride);
+      rq.prefix = p.prefix_lens[b];
+      const KeySrc ks = key_src<false>(p, b, rq.prefix);
+      rq.src_off = ks.src - (p.indptr ? p.table : p.r2t);
+      rq.src_hi = ks.hi;
+      rq.pos_base = ks.pos_base;
+      rq.tiles = (rq.n + TQ - 1) / TQ * p.kv_heads * p.halves;
+      reqs[b] = rq;
+    }
+    for (int32_t h = threadIdx.x; h < p.q_heads; h += NW * 64) sinks_tab[h] = p.sinks ? p.sinks[h] * kLog2e : 0.f;
+    __syncthreads();
+    if (w == 0) {  // exclusive prefix of the tile counts, 64 requests at a time
+      int32_t run = 0;
+      for (int32_t base = 0; base < p.batch; base += 64) {
+        const int32_t b = base + lane;
+        const int32_t cnt = b < p.batch ? reqs[b].tiles : 0;
+        int32_t inc = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int32_t y = __shfl_up(inc, d);
+          if (lane >= d) inc += y;
+        }
+        if (b < p.batch) reqs[b].tile0 = run + inc - cnt;
+        run += __shfl(inc, 63);
+      }
+      if (lane == 0) total_tab = run;
+    }
+    __syncthreads();
+    total = total_tab;
+  } else {
+    for (int32_t b = 0; b < p.batch; ++b) total += (new_count(p, b) + TQ - 1) / TQ * p.kv_heads * p.halves;
+  }
   const int32_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
   const int32_t x = blockIdx.x % 8;
   const int32_t t_lo = static_cast<int32_t>(static_cast<int64_t>(total) * x / 8);
   const int32_t t_hi = static_cast<int32_t>(static_cast<int64_t>(total) * (x + 1) / 8);
 
+  int32_t b_from = 0;  // a workgroup's tiles increase, so their requests do too
   for (int32_t t = t_lo + static_cast<int32_t>(blockIdx.x / 8); t < t_hi; t += per_xcd) {
-    const BandTile bt = band_tile(p, TQ, t);
-    if (bt.b < 0) break;
-    const QoRows qrows = qo_rows(p, bt.b);
-    int32_t seq = p.seq_lens[bt.b];
-    if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
-    const int32_t prefix = p.prefix_lens[bt.b];
+    BandTile bt;
+    QoRows qrows;
+    int32_t seq, prefix;
     BandCtx c;
-    c.ks = key_src<false>(p, bt.b, prefix);
+    if (tab) {
+      // the request holding tile t: the first from b_from whose tiles end past t
+      int32_t b = -1;
+      for (int32_t base = b_from; base < p.batch; base += 64) {
+        const int32_t bb = base + lane;
+        const bool hit = bb < p.batch && reqs[bb].tile0 + reqs[bb].tiles > t;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+        if (m != 0) {
+          b = base + static_cast<int32_t>(__builtin_ctzll(m));
+          break;
+        }
+      }
+      if (b < 0) break;
+      b_from = b;
+      const BandReq &rq = reqs[b];
+      const int32_t ntile = __builtin_amdgcn_readfirstlane((rq.n + TQ - 1) / TQ);
+      int32_t tl = __builtin_amdgcn_readfirstlane(t - rq.tile0);
+      const int32_t half = tl % p.halves;
+      tl /= p.halves;
+      bt.b = b;
+      bt.g = tl / ntile;
+      bt.tile = tl % ntile;
+      bt.hq0 = bt.g * p.group + half * p.ghead;
+      qrows.qo0 = __builtin_amdgcn_readfirstlane(rq.qo0);
+      qrows.n = __builtin_amdgcn_readfirstlane(rq.n);
+      seq = __builtin_amdgcn_readfirstlane(rq.seq);
+      prefix = __builtin_amdgcn_readfirstlane(rq.prefix);
+      // 64-bit fields made wave-uniform half by half; the source pointer is
+      // rebuilt from a kernel argument so that it stays a global pointer
+      auto uni64 = [](int64_t v) {
+        const uint64_t u = static_cast<uint64_t>(v);
+        return static_cast<int64_t>(
+            (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32))) << 32) |
+            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u))));
+      };
+      c.ks.src = (p.indptr ? p.table : p.r2t) + uni64(rq.src_off);
+      c.ks.hi = uni64(rq.src_hi);
+      c.ks.pos_base = __builtin_amdgcn_readfirstlane(rq.pos_base);
+    } else {
+      bt = band_tile(p, TQ, t);
+      if (bt.b < 0) break;
+      qrows = qo_rows(p, bt.b);
+      seq = p.seq_lens[bt.b];
+      if (seq > p.r2t_stride) seq = static_cast<int32_t>(p.r2t_stride);
+      prefix = p.prefix_lens[bt.b];
+      c.ks = key_src<false>(p, bt.b, prefix);
+    }
     c.g = bt.g;
     c.i0 = prefix + bt.tile * TQ;
     c.i_last = c.i0 + TQ - 1;
@@ -1213,7 +1317,7 @@ __global__ void __launch_bounds__(NW * 64, WGS) band_kernel(ExtendParams p) {
         const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 32 * cc);
         __builtin_memcpy(&qop[i][cc], &raw, 16);
       }
-      sink2[i] = p.sinks ? p.sinks[bt.hq0 + hh[i]] * kLog2e : 0.f;
+      sink2[i] = tab ? sinks_tab[bt.hq0 + hh[i]] : (p.sinks ? p.sinks[bt.hq0 + hh[i]] * kLog2e : 0.f);
     }
 
     f32x4_t acc[RB][8];
