@@ -636,6 +636,26 @@ def test_extend_small(name):
     assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
 
 
+def test_extend_band_batch_past_request_table():
+    """The long-window (band) kernel reads each request's lengths, rows and key
+    source into a per-workgroup table for batches of up to 1024 requests; a
+    larger batch walks the batch in global memory instead.  1030 requests with
+    1-3 new tokens each at W = 300 take that path, checked in full against the
+    oracle."""
+    say("extend band, 1030 requests (no request table)")
+    rng = np.random.default_rng(5)
+    B = 1030
+    pre = rng.integers(0, 400, size=B).tolist()
+    chunk = rng.integers(1, 4, size=B).tolist()
+    wl = WL.extend_workload("band_big_batch", 61, pre, chunk, 16, 2, 300, 16)
+    dw = DeviceWorkload(wl)
+    run_store(dw)
+    out = run_extend(dw, "f32")
+    check(out, oracle_extend(wl), TOL["bf16"], "band, 1030 requests")
+    out_bf = run_extend(dw, "bf16")
+    assert np.array_equal(device_to_bits(out_bf), bf16_of(out))
+
+
 def scale_v_bf16(wl, log2_scale, extremes=False):
     """V rows (pool rows and the new tokens' rows) times 2^log2_scale, which is
     exact in bf16 while no value leaves its normal range.  extremes: dims 0-3 of
