@@ -53,7 +53,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
 // overflow to inf, so V must stay inside f16's range).  A query whose output
 // is dominated by a few keys is as large as a V row while the output's RMS is
 // that of an average over the window; with bf16 weights the rounding of the
-// few large weights alone could then reach 2% of the RMS, with f16 about 0.3%.
+// few large weights alone could then reach 2% of the RMS, with f16 it stays
+// below 0.5%.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));   // MFMA f16 operand
 typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4v_t __attribute__((ext_vector_type(4)));
